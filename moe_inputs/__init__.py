@@ -1,0 +1,247 @@
+"""Seeded synthetic inputs for the sparse Mixture-of-Experts layer forward pass.
+
+This module is shared by the HIP path's tests/benchmark and by the oracle's tests. It therefore
+holds only random draws, the encoders that put those draws into their storage formats (bf16 bits,
+OCP e4m3 weight codes with per-row fp32 scales) and the layer shapes. It holds none of the layer's
+own arithmetic: no router, no top-k, no expert MLP, no activation quantisation. The two
+router biases that need a calibrated popularity profile are read from text fixtures written by
+``tests/golden/make_bias.py``.
+
+Shapes follow the Nemotron 3 pages: a learned router picks k of E routable experts (6 of 128 in
+Nano, MarkTechPost article on Nemotron 3, "Hybrid Mamba Transformer MoE architecture"); LatentMoE
+runs E' = E*H/l experts with k' = k*H/l in a latent width l (Nemotron 3 white paper summary,
+section 2.2 and the speed-read equation).
+
+Random recipe (one ``numpy.random.SeedSequence`` per tensor, per expert for expert weights):
+  x ~ N(0, 1)                                    tag 1
+  W_r ~ N(0, 1/H)                                tag 2
+  b ~ U(-0.1, 0.1) or a stored fixture           tag 3
+  W_up[e] ~ N(0, 1/D),  W_down[e] ~ N(0, 1/I)    tags 4, 5 (sequence [seed, tag, e])
+  Ws_up ~ N(0, 1/H),    Ws_down ~ N(0, 1/I_s)    tags 6, 7
+  W_in ~ N(0, 1/H),     W_out ~ N(0, 1/l)        tags 8, 9
+Draws are fp32, then rounded to nearest-even bf16 (bf16 layers) or quantised per output row to
+e4m3 with scale = row amax / 448 (fp8 expert weights).
+"""
+from __future__ import annotations
+
+import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+__all__ = [
+    "LayerConfig", "CONFIGS", "TAGS", "make_layer", "f32_to_bf16_bits", "bf16_bits_to_f32",
+    "encode_e4m3", "decode_e4m3", "quantize_rows_e4m3", "golden_dir", "read_bias_fixture",
+]
+
+TAGS = dict(x=1, W_r=2, b=3, W_up=4, W_down=5, Ws_up=6, Ws_down=7, W_in=8, W_out=9, rank=10)
+
+_GOLDEN = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "tests", "golden")
+
+
+def golden_dir() -> str:
+    return _GOLDEN
+
+
+@dataclasses.dataclass(frozen=True)
+class LayerConfig:
+    name: str
+    T: int
+    H: int
+    E: int
+    k: int
+    I: int
+    I_shared: int = 0
+    latent: int = 0              # 0: plain MoE; else the latent width l
+    act_dtype: str = "bf16"      # x, W_r, shared expert, W_in / W_out: "f32" | "bf16"
+    expert_dtype: str = "bf16"   # W_up / W_down: "f32" | "bf16" | "e4m3"
+    bias: str = "uniform"        # "uniform" or a fixture file name under tests/golden
+    description: str = ""
+
+    @property
+    def D(self) -> int:
+        """Width the routed experts read and write: H, or l for LatentMoE."""
+        return self.latent if self.latent else self.H
+
+    @property
+    def P(self) -> int:
+        return self.T * self.k
+
+    def with_T(self, T: int) -> "LayerConfig":
+        return dataclasses.replace(self, T=T)
+
+
+CONFIGS = {
+    "tiny_f32": LayerConfig(
+        "tiny_f32", T=64, H=256, E=16, k=2, I=128, act_dtype="f32", expert_dtype="f32",
+        description="tiny MoE layer, fp32, T=64 H=256 E=16 k=2 I=128, no shared expert"),
+    "nano_decode_bf16": LayerConfig(
+        "nano_decode_bf16", T=64, H=2688, E=128, k=6, I=1856, I_shared=3712,
+        description="Nano-shaped decode step, bf16, T=64, 6 of 128 experts + shared expert"),
+    "nano_prefill_bf16": LayerConfig(
+        "nano_prefill_bf16", T=8192, H=2688, E=128, k=6, I=1856, I_shared=3712,
+        bias="bias_nano_prefill_zipf.txt",
+        description="Nano-shaped prefill, bf16, T=8192, Zipf(1.1) expert popularity"),
+    "latent_bf16": LayerConfig(
+        "latent_bf16", T=4096, H=4096, E=512, k=24, I=512, latent=1024,
+        description="LatentMoE, bf16, T=4096 H=4096 l=1024 E'=512 k'=24 I=512"),
+    "nano_fp8": LayerConfig(
+        "nano_fp8", T=16384, H=2688, E=128, k=6, I=1856, I_shared=3712, expert_dtype="e4m3",
+        bias="bias_nano_fp8_imbalance.txt",
+        description="Nano-shaped, e4m3 expert weights, T=16384, heavy expert imbalance"),
+}
+
+
+# ----------------------------------------------------------------------------- format encoders
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 values to the nearest bf16 (ties to even); returns the uint16 bit patterns."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(u: np.ndarray) -> np.ndarray:
+    return (np.asarray(u, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    """OCP E4M3 (fn variant): bias 7, no infinities, S.1111.111 is NaN, max 448."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int32)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    v = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    v = np.where((e == 15) & (m == 7), np.nan, v)
+    return s * v
+
+
+def encode_e4m3(v: np.ndarray) -> np.ndarray:
+    """Nearest (ties to even), saturating at +-448, OCP E4M3 codes of finite values."""
+    v = np.asarray(v, dtype=np.float64)
+    neg = np.signbit(v)
+    a = np.minimum(np.abs(v), 448.0)
+    _, ex = np.frexp(a)                         # a = f * 2**ex with f in [0.5, 1)
+    e = np.maximum(ex - 1, -6)                  # unbiased exponent; subnormals share 2**-6
+    q = np.rint(a / np.exp2(e - 3.0))           # 3 mantissa bits: quantum 2**(e-3)
+    val = np.minimum(q * np.exp2(e - 3.0), 448.0)
+    _, ex2 = np.frexp(val)
+    e2 = ex2 - 1
+    normal = val >= 2.0 ** -6
+    ef = np.where(normal, e2 + 7, 0)
+    mf = np.where(normal, val / np.exp2(e2 - 3.0) - 8.0, val / 2.0 ** -9)
+    mf = np.where(val == 0, 0, mf)
+    ef = np.where(val == 0, 0, ef)
+    code = (ef.astype(np.int32) << 3) | np.rint(mf).astype(np.int32)
+    return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def quantize_rows_e4m3(w: np.ndarray):
+    """Per-row (output channel) e4m3 codes with fp32 scale = row amax / 448 (1 for a zero row)."""
+    w = np.asarray(w, dtype=np.float32)
+    amax = np.abs(w).max(axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    v = (w / scale[..., None]).astype(np.float32)
+    return encode_e4m3(v), scale
+
+
+# ----------------------------------------------------------------------------- draws
+
+def _rng(*key):
+    return np.random.default_rng(np.random.SeedSequence(list(key)))
+
+
+def _normal(key, shape, fan_in):
+    a = _rng(*key).standard_normal(shape, dtype=np.float32)
+    a *= np.float32(1.0 / np.sqrt(fan_in))
+    return a
+
+
+def _store(a: np.ndarray, dtype: str):
+    """fp32 draw -> (storage array, per-row scales or None)."""
+    if dtype == "f32":
+        return a, None
+    if dtype == "bf16":
+        return f32_to_bf16_bits(a), None
+    if dtype == "e4m3":
+        return quantize_rows_e4m3(a)
+    raise ValueError(dtype)
+
+
+def read_bias_fixture(fname: str, E: int) -> np.ndarray:
+    vals = []
+    with open(os.path.join(_GOLDEN, fname)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                vals.append(float.fromhex(line))
+    b = np.array(vals, dtype=np.float64)
+    if b.shape != (E,):
+        raise ValueError(f"{fname}: expected {E} values, found {b.shape[0]}")
+    out = b.astype(np.float32)
+    if not np.array_equal(out.astype(np.float64), b):
+        raise ValueError(f"{fname}: values are not exact fp32")
+    return out
+
+
+_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def _expert_stack(seed, tag, E, rows, cols, fan_in, dtype):
+    """[E, rows, cols] weights, one seed sequence per expert, drawn in a thread pool."""
+    item = {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8}[dtype]
+    out = np.empty((E, rows, cols), dtype=item)
+    scales = np.empty((E, rows), dtype=np.float32) if dtype == "e4m3" else None
+
+    def one(e):
+        st, sc = _store(_normal((seed, tag, e), (rows, cols), fan_in), dtype)
+        out[e] = st
+        if scales is not None:
+            scales[e] = sc
+
+    with ThreadPoolExecutor(_THREADS) as ex:
+        list(ex.map(one, range(E)))
+    return out, scales
+
+
+def make_layer(cfg: LayerConfig, seed: int = 0, tensors=None) -> dict:
+    """All inputs of one layer call, in storage formats.
+
+    Returns a dict with numpy arrays: x [T,H], W_r [E,H], b [E] fp32, W_up [E,I,D],
+    W_down [E,D,I] (+ s_up [E,I], s_down [E,D] for e4m3), Ws_up [I_s,H], Ws_down [H,I_s],
+    W_in [l,H], W_out [H,l]. fp32 tensors are float32, bf16 tensors are uint16 bit patterns,
+    e4m3 tensors are uint8 codes. ``tensors`` restricts which entries are drawn.
+    """
+    want = (lambda n: True) if tensors is None else (lambda n: n in tensors)
+    T, H, E, I, D, Is, L = cfg.T, cfg.H, cfg.E, cfg.I, cfg.D, cfg.I_shared, cfg.latent
+    ad = cfg.act_dtype
+    out = {"config": cfg, "seed": seed}
+    if want("x"):
+        out["x"] = _store(_normal((seed, TAGS["x"]), (T, H), 1.0), ad)[0]
+    if want("W_r"):
+        out["W_r"] = _store(_normal((seed, TAGS["W_r"]), (E, H), H), ad)[0]
+    if want("b"):
+        if cfg.bias == "uniform":
+            out["b"] = _rng(seed, TAGS["b"]).uniform(-0.1, 0.1, E).astype(np.float32)
+        else:
+            out["b"] = read_bias_fixture(cfg.bias, E)
+    if want("W_up"):
+        out["W_up"], out["s_up"] = _expert_stack(seed, TAGS["W_up"], E, I, D, D, cfg.expert_dtype)
+    if want("W_down"):
+        out["W_down"], out["s_down"] = _expert_stack(seed, TAGS["W_down"], E, D, I, I,
+                                                     cfg.expert_dtype)
+    if Is and want("Ws_up"):
+        out["Ws_up"] = _store(_normal((seed, TAGS["Ws_up"]), (Is, H), H), ad)[0]
+    if Is and want("Ws_down"):
+        out["Ws_down"] = _store(_normal((seed, TAGS["Ws_down"]), (H, Is), Is), ad)[0]
+    if L and want("W_in"):
+        out["W_in"] = _store(_normal((seed, TAGS["W_in"]), (L, H), H), ad)[0]
+    if L and want("W_out"):
+        out["W_out"] = _store(_normal((seed, TAGS["W_out"]), (H, L), L), ad)[0]
+    return out
+
+
+def expert_rank_permutation(seed: int, E: int) -> np.ndarray:
+    """Which expert holds popularity rank r (rank 0 = most popular) in the skewed profiles."""
+    return _rng(seed, TAGS["rank"]).permutation(E)

@@ -1,0 +1,223 @@
+"""Python face of the double-precision MoE-layer oracle (``moe_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the CPU-baseline leg of the
+benchmark, never by the HIP library or its binding. It marshals numpy arrays (in their storage
+formats, as produced by ``moe_inputs``) into the C structs and back; all arithmetic is in the C
+file, single-threaded, in double precision.
+
+Parity status: every function here is pinned by the CPU tests in ``tests/test_oracle_pins.py``
+against brute force, closed forms, library routines or invariants; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "_moe_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+F32, BF16, E4M3, F64 = 0, 1, 2, 3
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain IEEE semantics: no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O3", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+                               "-ffp-contract=off", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class OrcMat(C.Structure):
+    _fields_ = [("data", C.c_void_p), ("scale", C.c_void_p), ("dtype", C.c_int32),
+                ("pad_", C.c_int32), ("cols", C.c_int64)]
+
+
+class OrcLayer(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("T", "H", "E", "k", "I", "I_shared", "latent",
+                                         "fp8_emulate")] + \
+               [("x", OrcMat), ("W_r", OrcMat), ("b", C.c_void_p), ("W_up", OrcMat),
+                ("W_down", OrcMat), ("Ws_up", OrcMat), ("Ws_down", OrcMat), ("W_in", OrcMat),
+                ("W_out", OrcMat)]
+
+
+def lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            L = C.CDLL(build())
+            i32p, f64p, f32p = (np.ctypeslib.ndpointer(np.int32, flags="C"),
+                                np.ctypeslib.ndpointer(np.float64, flags="C"),
+                                np.ctypeslib.ndpointer(np.float32, flags="C"))
+            L.orc_bf16_to_f64.restype = C.c_double
+            L.orc_bf16_to_f64.argtypes = [C.c_uint16]
+            L.orc_e4m3_to_f64.restype = C.c_double
+            L.orc_e4m3_to_f64.argtypes = [C.c_uint8]
+            L.orc_f64_to_e4m3.restype = C.c_uint8
+            L.orc_f64_to_e4m3.argtypes = [C.c_double]
+            L.orc_logits.argtypes = [C.POINTER(OrcLayer), C.c_void_p, C.c_int32, f64p]
+            L.orc_route.argtypes = [f64p, f32p, C.c_int32, C.c_int32, C.c_int32, i32p, f64p,
+                                    f64p]
+            L.orc_route_f32.argtypes = [f32p, f32p, C.c_int32, C.c_int32, C.c_int32, i32p, f64p,
+                                        f64p]
+            L.orc_dispatch.argtypes = [i32p, C.c_int32, C.c_int32, C.c_int32, i32p, i32p, i32p,
+                                       i32p]
+            L.orc_forward_tokens.argtypes = [C.POINTER(OrcLayer), C.c_void_p, C.c_int32, i32p,
+                                             f64p, f64p, f64p]
+            L.orc_bias_update.argtypes = [f64p, i32p, f64p, C.c_int32, C.c_double]
+            _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != 0:
+        raise ValueError(f"oracle call failed with code {rc}")
+
+
+_DT = {np.dtype(np.float32): F32, np.dtype(np.uint16): BF16, np.dtype(np.uint8): E4M3,
+       np.dtype(np.float64): F64}
+
+
+def _mat(a, scale=None, keep=None):
+    if a is None:
+        return OrcMat()
+    a = np.ascontiguousarray(a)
+    m = OrcMat()
+    m.data = a.ctypes.data
+    m.dtype = _DT[a.dtype]
+    m.cols = a.shape[-1]
+    if m.dtype == E4M3:
+        if scale is None:
+            raise ValueError("e4m3 matrix needs its per-row scales")
+        scale = np.ascontiguousarray(scale, dtype=np.float32)
+        m.scale = scale.ctypes.data
+        keep.append(scale)
+    keep.append(a)
+    return m
+
+
+def layer(inp: dict, fp8_emulate: bool = False):
+    """Build the C layer struct from a ``moe_inputs.make_layer`` dict. Returns (struct, keepalive)."""
+    cfg = inp["config"]
+    keep = []
+    L = OrcLayer()
+    L.T, L.H, L.E, L.k, L.I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
+    L.I_shared, L.latent, L.fp8_emulate = cfg.I_shared, cfg.latent, int(fp8_emulate)
+    L.x = _mat(inp.get("x"), keep=keep)
+    L.W_r = _mat(inp.get("W_r"), keep=keep)
+    b = np.ascontiguousarray(inp["b"], dtype=np.float32) if "b" in inp else None
+    if b is not None:
+        keep.append(b)
+        L.b = b.ctypes.data
+    L.W_up = _mat(inp.get("W_up"), inp.get("s_up"), keep)
+    L.W_down = _mat(inp.get("W_down"), inp.get("s_down"), keep)
+    L.Ws_up = _mat(inp.get("Ws_up"), keep=keep)
+    L.Ws_down = _mat(inp.get("Ws_down"), keep=keep)
+    L.W_in = _mat(inp.get("W_in"), keep=keep)
+    L.W_out = _mat(inp.get("W_out"), keep=keep)
+    return L, keep
+
+
+def _tokens(tokens):
+    if tokens is None:
+        return None, 0, None
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    return t.ctypes.data, t.shape[0], t
+
+
+def logits(inp: dict, tokens=None) -> np.ndarray:
+    """Router logits in double for the listed tokens (all if None): [n, E]."""
+    L, keep = layer(inp)
+    p, n, tk = _tokens(tokens)
+    n = n if tokens is not None else inp["config"].T
+    z = np.zeros((n, inp["config"].E), dtype=np.float64)
+    _check(lib().orc_logits(C.byref(L), p, n, z))
+    return z
+
+
+def route(z: np.ndarray, b: np.ndarray, k: int):
+    """Double-precision routing: (idx [T,k] int32, gates [T,k], margin [T])."""
+    z = np.ascontiguousarray(z, dtype=np.float64)
+    T, E = z.shape
+    idx = np.zeros((T, k), np.int32)
+    g = np.zeros((T, k), np.float64)
+    m = np.zeros(T, np.float64)
+    _check(lib().orc_route(z, np.ascontiguousarray(b, np.float32), T, E, k, idx, g, m))
+    return idx, g, m
+
+
+def route_f32(z32: np.ndarray, b: np.ndarray, k: int):
+    """Routing from fp32 logits, decisions taken on fp32-rounded scores and keys."""
+    z32 = np.ascontiguousarray(z32, dtype=np.float32)
+    T, E = z32.shape
+    idx = np.zeros((T, k), np.int32)
+    g = np.zeros((T, k), np.float64)
+    m = np.zeros(T, np.float64)
+    _check(lib().orc_route_f32(z32, np.ascontiguousarray(b, np.float32), T, E, k, idx, g, m))
+    return idx, g, m
+
+
+def dispatch(idx: np.ndarray, E: int):
+    """(counts [E], offsets [E+1], perm [T*k], pos [T,k]) -- all int32."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    T, k = idx.shape
+    counts = np.zeros(E, np.int32)
+    offsets = np.zeros(E + 1, np.int32)
+    perm = np.zeros(T * k, np.int32)
+    pos = np.zeros((T, k), np.int32)
+    _check(lib().orc_dispatch(idx, T, E, k, counts, offsets, perm, pos))
+    return counts, offsets, perm, pos
+
+
+def forward_tokens(inp: dict, idx: np.ndarray, gates: np.ndarray, tokens=None,
+                   fp8_emulate: bool = False) -> np.ndarray:
+    """Layer output in double for the listed tokens (all if None) given their routing rows."""
+    cfg = inp["config"]
+    L, keep = layer(inp, fp8_emulate)
+    p, n, tk = _tokens(tokens)
+    n = n if tokens is not None else cfg.T
+    idx = np.ascontiguousarray(idx, dtype=np.int32).reshape(n, cfg.k)
+    gates = np.ascontiguousarray(gates, dtype=np.float64).reshape(n, cfg.k)
+    y = np.zeros((n, cfg.H), np.float64)
+    work = np.zeros(2 * cfg.D + max(cfg.I, cfg.I_shared), np.float64)
+    _check(lib().orc_forward_tokens(C.byref(L), p, n, idx, gates, y, work))
+    return y
+
+
+def forward(inp: dict, tokens=None, fp8_emulate: bool = False) -> dict:
+    """Route and run the listed tokens (all if None). Returns logits, idx, gates, margin, y."""
+    z = logits(inp, tokens)
+    idx, g, m = route(z, inp["b"], inp["config"].k)
+    y = forward_tokens(inp, idx, g, tokens, fp8_emulate)
+    return dict(logits=z, idx=idx, gates=g, margin=m, y=y)
+
+
+def bias_update(b: np.ndarray, counts: np.ndarray, target: np.ndarray, gamma: float) -> np.ndarray:
+    """One aux-loss-free sign step of the routing bias toward per-expert target loads."""
+    b = np.array(b, dtype=np.float64, copy=True)
+    _check(lib().orc_bias_update(b, np.ascontiguousarray(counts, np.int32),
+                                 np.ascontiguousarray(target, np.float64), b.shape[0], gamma))
+    return b
+
+
+def bf16_to_f64(u) -> np.ndarray:
+    f = lib().orc_bf16_to_f64
+    return np.array([f(int(v)) for v in np.ravel(u)], dtype=np.float64).reshape(np.shape(u))
+
+
+def e4m3_to_f64(c) -> np.ndarray:
+    f = lib().orc_e4m3_to_f64
+    return np.array([f(int(v)) for v in np.ravel(c)], dtype=np.float64).reshape(np.shape(c))
+
+
+def f64_to_e4m3(v) -> np.ndarray:
+    f = lib().orc_f64_to_e4m3
+    return np.array([f(float(x)) for x in np.ravel(v)], dtype=np.uint8).reshape(np.shape(v))

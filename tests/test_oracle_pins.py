@@ -1,0 +1,328 @@
+"""Pins of the double-precision oracle to things other than itself (CPU only).
+
+Each test ties one oracle function to brute force on tiny inputs, a closed form, a special case
+that reduces to a library routine (numpy matmul / stable sort, torch's float8 and bfloat16
+casts), or an invariant of the layer. Together they are chosen so that a plausible slip anywhere
+in the oracle (a dropped term, a wrong sign or index, a transposed operand, biased gates, softmax
+for sigmoid, an unstable dispatch) fails at least one of them.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+from oracle import oracle as O
+
+
+def cfg(**kw):
+    base = dict(name="pin", T=8, H=32, E=4, k=2, I=16, act_dtype="f32", expert_dtype="f32")
+    base.update(kw)
+    return mi.LayerConfig(**base)
+
+
+def dense_mlp(x, W_up, W_down):
+    """Textbook squared-ReLU MLP through numpy matmul: W_down relu(W_up x)^2, rows of x."""
+    a = x @ W_up.T
+    return (np.maximum(a, 0.0) ** 2) @ W_down.T
+
+
+def f64(inp, name):
+    a = inp[name]
+    if a.dtype == np.uint16:
+        return mi.bf16_bits_to_f32(a).astype(np.float64)
+    if a.dtype == np.uint8:
+        scale = inp["s_up" if name == "W_up" else "s_down"]
+        vals = torch.from_numpy(a).view(torch.float8_e4m3fn).double().numpy()
+        return vals * scale[..., None].astype(np.float64)
+    return a.astype(np.float64)
+
+
+# ----------------------------------------------------------------------------- formats
+
+def test_e4m3_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = O.e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan) and nan.sum() == 2   # S.1111.111 only
+    assert np.array_equal(mine[~nan], ref[~nan])
+    assert O.e4m3_to_f64(np.array([0x7E]))[0] == 448.0
+    assert O.e4m3_to_f64(np.array([0x01]))[0] == 2.0 ** -9
+
+
+def test_e4m3_encode_roundtrip_and_ties_even():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    assert np.array_equal(O.f64_to_e4m3(O.e4m3_to_f64(codes)), codes)
+    # midpoints between neighbouring positive codes go to the even mantissa
+    vals = O.e4m3_to_f64(np.arange(0, 0x7E, dtype=np.uint8))
+    mids = (vals[:-1] + vals[1:]) / 2
+    got = O.f64_to_e4m3(mids)
+    want = torch.from_numpy(mids.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert np.array_equal(got, want.numpy())
+    assert np.all(got % 2 == 0)
+    # saturation beyond the largest finite value
+    assert O.f64_to_e4m3(np.array([470.0, 1e6, -1e6])).tolist() == [0x7E, 0x7E, 0xFE]
+
+
+def test_e4m3_encode_random_matches_torch_and_generator():
+    rng = np.random.default_rng(1)
+    v = (rng.standard_normal(4000) * np.exp2(rng.integers(-12, 8, 4000))).astype(np.float32)
+    v = np.clip(v, -448, 448)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.f64_to_e4m3(v.astype(np.float64)), ref)
+    assert np.array_equal(mi.encode_e4m3(v), ref)
+
+
+def test_bf16_decode_and_generator_rounding_match_torch():
+    rng = np.random.default_rng(2)
+    v = (rng.standard_normal(5000) * np.exp2(rng.integers(-30, 30, 5000))).astype(np.float32)
+    bits = mi.f32_to_bf16_bits(v)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bits, ref)
+    assert np.array_equal(O.bf16_to_f64(bits[:500]),
+                          torch.from_numpy(ref[:500].view(np.int16)).view(torch.bfloat16)
+                          .double().numpy())
+
+
+# ----------------------------------------------------------------------------- routing
+
+def brute_route(key, s, k):
+    order = np.lexsort((np.arange(key.shape[0]), -key))   # key descending, index ascending
+    sel = order[:k]
+    margin = key[order[k - 1]] - key[order[k]] if k < key.shape[0] else np.inf
+    return sel, s[sel] / s[sel].sum(), margin
+
+
+@pytest.mark.parametrize("T,E,k", [(7, 5, 2), (16, 16, 2), (9, 12, 12), (5, 33, 6), (3, 64, 24)])
+def test_route_matches_brute_force(T, E, k):
+    rng = np.random.default_rng(T * 100 + E)
+    z = rng.standard_normal((T, E))
+    b = rng.uniform(-0.1, 0.1, E).astype(np.float32)
+    z[0, :3] = z[0, 3]            # exact ties in logits
+    idx, g, m = O.route(z, b, k)
+    for t in range(T):
+        s = 1.0 / (1.0 + np.exp(-z[t]))
+        sel, gg, mm = brute_route(s + b.astype(np.float64), s, k)
+        assert idx[t].tolist() == sel.tolist()
+        np.testing.assert_allclose(g[t], gg, rtol=1e-15, atol=0)
+        assert m[t] == mm
+
+
+def test_route_f32_matches_brute_force_in_binary32():
+    rng = np.random.default_rng(3)
+    T, E, k = 40, 128, 6
+    z = rng.standard_normal((T, E)).astype(np.float32)
+    b = rng.uniform(-0.1, 0.1, E).astype(np.float32)
+    z[1, :] = z[1, 0]
+    b[:8] = b[0]
+    idx, g, m = O.route_f32(z, b, k)
+    for t in range(T):
+        s32 = (1.0 / (1.0 + np.exp(-z[t].astype(np.float64)))).astype(np.float32)
+        key32 = s32 + b                     # numpy binary32 add
+        sel, gg, _ = brute_route(key32.astype(np.float64), s32.astype(np.float64), k)
+        assert idx[t].tolist() == sel.tolist()
+        np.testing.assert_allclose(g[t], gg, rtol=1e-15)
+
+
+def test_route_exact_ties_take_lowest_index():
+    E, k = 10, 4
+    z = np.zeros((1, E))
+    b = np.zeros(E, np.float32)
+    idx, g, m = O.route(z, b, k)
+    assert idx[0].tolist() == [0, 1, 2, 3] and m[0] == 0.0
+    np.testing.assert_array_equal(g[0], np.full(k, 0.25))
+
+
+def test_route_forced_by_bias_and_gates_ignore_bias():
+    # sigma(log 3) = 3/4 and sigma(0) = 1/2: closed-form gates 0.6 / 0.4 (softmax would be 3/4, 1/4)
+    E, k = 6, 2
+    z = np.zeros((1, E))
+    z[0, 4] = np.log(3.0)
+    b = np.zeros(E, np.float32)
+    b[[1, 4]] = 4.0                     # scores are in (0, 1): +4 forces experts 1 and 4
+    idx, g, _ = O.route(z, b, k)
+    assert idx[0].tolist() == [4, 1]
+    np.testing.assert_allclose(g[0], [0.6, 0.4], rtol=1e-14)
+    b2 = b.copy()
+    b2[1] = 5.0                        # expert 1 now first by key; gates still unbiased
+    idx2, g2, _ = O.route(z, b2, k)
+    assert idx2[0].tolist() == [1, 4]
+    np.testing.assert_allclose(g2[0], [0.4, 0.6], rtol=1e-14)
+
+
+def test_route_invariant_to_common_bias_shift():
+    rng = np.random.default_rng(4)
+    T, E, k = 50, 32, 4
+    z = rng.standard_normal((T, E))
+    b = (rng.integers(-100, 100, E) / 1024.0).astype(np.float32)
+    i1, g1, _ = O.route(z, b, k)
+    i2, g2, _ = O.route(z, (b + np.float32(0.5)).astype(np.float32), k)
+    assert np.array_equal(i1, i2)
+    np.testing.assert_array_equal(g1, g2)
+    np.testing.assert_allclose(g1.sum(1), 1.0, rtol=0, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------- dispatch
+
+@pytest.mark.parametrize("T,E,k", [(1, 4, 1), (37, 8, 3), (64, 16, 2), (200, 128, 6)])
+def test_dispatch_matches_stable_sort(T, E, k):
+    rng = np.random.default_rng(T + E)
+    idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    counts, offsets, perm, pos = O.dispatch(idx, E)
+    order = np.argsort(idx.ravel(), kind="stable")          # pairs grouped by expert, in order
+    assert np.array_equal(counts, np.bincount(idx.ravel(), minlength=E))
+    assert offsets[0] == 0 and offsets[-1] == T * k
+    assert np.array_equal(np.diff(offsets), counts)
+    assert np.array_equal(perm, order // k)
+    inv = np.empty(T * k, np.int64)
+    inv[order] = np.arange(T * k)
+    assert np.array_equal(pos.ravel(), inv)
+    for e in range(E):                                       # stable: tokens ascend in an expert
+        seg = perm[offsets[e]:offsets[e + 1]]
+        assert np.all(np.diff(seg) > 0)
+
+
+# ----------------------------------------------------------------------------- layer math
+
+def test_single_expert_is_dense_squared_relu_mlp():
+    c = cfg(E=1, k=1, T=5, H=48, I=24)
+    inp = mi.make_layer(c, seed=7)
+    r = O.forward(inp)
+    assert np.all(r["idx"] == 0) and np.all(r["gates"] == 1.0)
+    want = dense_mlp(f64(inp, "x"), f64(inp, "W_up")[0], f64(inp, "W_down")[0])
+    np.testing.assert_allclose(r["y"], want, rtol=1e-12, atol=1e-13)
+
+
+def test_all_experts_with_zero_router_is_uniform_average():
+    c = cfg(E=5, k=5, T=6, H=40, I=20)
+    inp = mi.make_layer(c, seed=8)
+    inp["W_r"] = np.zeros_like(inp["W_r"])
+    inp["b"] = np.zeros_like(inp["b"])
+    r = O.forward(inp)
+    assert np.array_equal(r["idx"], np.tile(np.arange(5), (6, 1)))
+    np.testing.assert_allclose(r["gates"], 0.2, rtol=1e-15)
+    x, Wu, Wd = f64(inp, "x"), f64(inp, "W_up"), f64(inp, "W_down")
+    want = sum(dense_mlp(x, Wu[e], Wd[e]) for e in range(5)) / 5
+    np.testing.assert_allclose(r["y"], want, rtol=1e-12, atol=1e-13)
+
+
+def test_two_expert_gates_weight_each_output():
+    # E=2, k=2, logits (0, log 3) via the router: y = 0.4 f0(x) + 0.6 f1(x)  (closed-form gates)
+    c = cfg(E=2, k=2, T=1, H=16, I=8)
+    inp = mi.make_layer(c, seed=9)
+    x = np.zeros((1, 16), np.float32)
+    x[0, 0] = 1.0
+    Wr = np.zeros((2, 16), np.float32)
+    Wr[1, 0] = np.float32(np.log(3.0))
+    inp["x"], inp["W_r"], inp["b"] = x, Wr, np.zeros(2, np.float32)
+    r = O.forward(inp)
+    s1 = 1 / (1 + np.exp(-np.float64(np.float32(np.log(3.0)))))
+    g = np.array([s1, 0.5]) / (s1 + 0.5)
+    assert r["idx"][0].tolist() == [1, 0]
+    Wu, Wd = f64(inp, "W_up"), f64(inp, "W_down")
+    want = g[0] * dense_mlp(x.astype(np.float64), Wu[1], Wd[1]) + \
+        g[1] * dense_mlp(x.astype(np.float64), Wu[0], Wd[0])
+    np.testing.assert_allclose(r["y"], want, rtol=1e-13)
+
+
+def test_shared_expert_alone_is_dense_mlp():
+    c = cfg(E=4, k=2, T=5, H=32, I=16, I_shared=24)
+    inp = mi.make_layer(c, seed=10)
+    inp["W_down"] = np.zeros_like(inp["W_down"])
+    r = O.forward(inp)
+    want = dense_mlp(f64(inp, "x"), f64(inp, "Ws_up"), f64(inp, "Ws_down"))
+    np.testing.assert_allclose(r["y"], want, rtol=1e-12, atol=1e-13)
+
+
+def test_zero_input_gives_zero_and_doubling_input_quadruples_output():
+    c = cfg(E=6, k=3, T=7, H=32, I=16, I_shared=8)
+    inp = mi.make_layer(c, seed=11)
+    inp["W_r"] = np.zeros_like(inp["W_r"])        # routing then does not depend on x
+    r1 = O.forward(inp)
+    inp2 = dict(inp, x=(inp["x"] * 2).astype(np.float32))
+    r2 = O.forward(inp2)
+    assert np.array_equal(r2["y"], 4.0 * r1["y"])     # powers of two: exact
+    inp0 = dict(inp, x=np.zeros_like(inp["x"]))
+    assert np.all(O.forward(inp0)["y"] == 0.0)
+
+
+def test_token_permutation_equivariance():
+    c = cfg(E=8, k=3, T=12, H=32, I=16, I_shared=8, act_dtype="bf16", expert_dtype="bf16")
+    inp = mi.make_layer(c, seed=12)
+    perm = np.random.default_rng(0).permutation(12)
+    r = O.forward(inp)
+    rp = O.forward(dict(inp, x=inp["x"][perm]))
+    assert np.array_equal(rp["y"], r["y"][perm])
+    assert np.array_equal(rp["idx"], r["idx"][perm])
+
+
+def test_latent_with_identity_projections_is_plain_moe():
+    c = cfg(E=8, k=3, T=6, H=32, I=16, act_dtype="bf16", expert_dtype="bf16")
+    inp = mi.make_layer(c, seed=13)
+    cl = dataclasses.replace(c, latent=32)
+    eye = mi.f32_to_bf16_bits(np.eye(32, dtype=np.float32))
+    inpl = dict(inp, config=cl, W_in=eye, W_out=eye)
+    assert np.array_equal(O.forward(inpl)["y"], O.forward(inp)["y"])
+
+
+def test_latent_single_expert_is_projected_dense_mlp():
+    c = cfg(E=1, k=1, T=4, H=48, I=8, latent=16)
+    inp = mi.make_layer(c, seed=14)
+    r = O.forward(inp)
+    x, Win, Wout = f64(inp, "x"), f64(inp, "W_in"), f64(inp, "W_out")
+    want = dense_mlp(x @ Win.T, f64(inp, "W_up")[0], f64(inp, "W_down")[0]) @ Wout.T
+    np.testing.assert_allclose(r["y"], want, rtol=1e-12, atol=1e-13)
+
+
+def test_latent_scaling_of_expert_count_and_top_k():
+    # E' = E*H/l and k' = k*H/l (Nemotron 3 white paper, section 2.2); Table 1 trained k'=22.
+    golden = {}
+    with open(mi.golden_dir() + "/latent_scaling.txt") as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                key, val = line.split("=")
+                golden[key.strip()] = int(val)
+    H, l, E, k = golden["H"], golden["l"], golden["E"], golden["k"]
+    assert E * H // l == golden["E_latent"]
+    c = mi.CONFIGS["latent_bf16"]
+    assert (c.H, c.latent, c.E) == (H, l, golden["E_latent"]) and c.k == k * H // l
+
+
+def test_fp8_experts_use_dequantised_weights_exactly():
+    c = cfg(E=1, k=1, T=4, H=64, I=32, act_dtype="bf16", expert_dtype="e4m3")
+    inp = mi.make_layer(c, seed=15)
+    r = O.forward(inp)
+    want = dense_mlp(f64(inp, "x"), f64(inp, "W_up")[0], f64(inp, "W_down")[0])
+    np.testing.assert_allclose(r["y"], want, rtol=1e-12, atol=1e-13)
+
+
+def test_fp8_emulation_quantises_activation_rows():
+    # E=1, k=1: x and h rows quantised per row (scale amax/448, codes via torch's e4m3 cast),
+    # h rounded to bf16 first; the rest is numpy matmul.
+    c = cfg(E=1, k=1, T=6, H=64, I=32, act_dtype="bf16", expert_dtype="e4m3")
+    inp = mi.make_layer(c, seed=16)
+    r = O.forward_tokens(inp, np.zeros((6, 1), np.int32), np.ones((6, 1)), fp8_emulate=True)
+
+    def q(rows):
+        rows32 = rows.astype(np.float32)
+        amax = np.abs(rows32).max(1)
+        sc = np.where(amax > 0, amax / np.float32(448), np.float32(1)).astype(np.float32)
+        v = torch.from_numpy((rows32 / sc[:, None]).astype(np.float32))
+        return v.to(torch.float8_e4m3fn).double().numpy() * sc[:, None].astype(np.float64)
+
+    x = q(f64(inp, "x"))
+    h = np.maximum(x @ f64(inp, "W_up")[0].T, 0) ** 2
+    h = torch.from_numpy(h).float().to(torch.bfloat16).double().numpy()
+    want = q(h) @ f64(inp, "W_down")[0].T
+    np.testing.assert_allclose(r, want, rtol=1e-12, atol=1e-13)
+
+
+def test_bias_update_sign_rule():
+    b = np.array([0.0, 0.5, -0.5, 1.0])
+    counts = np.array([10, 3, 7, 7], np.int32)
+    target = np.array([5.0, 5.0, 7.0, 9.0])
+    nb = O.bias_update(b, counts, target, 0.25)
+    np.testing.assert_array_equal(nb, [-0.25, 0.75, -0.5, 1.25])
