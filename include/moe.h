@@ -1,0 +1,149 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts layer forward library
+ * (libmoe_mi355x.so).
+ *
+ * The layer is the MoE block of the Nemotron 3 hybrid Mamba-Transformer stack, which takes the
+ * place of the FFN: a learned router sends every token to k of E routable experts (6 of 128 in
+ * Nano) ["NVIDIA AI发布了Nemotron 3：一款混合Mamba Transformer MoE堆栈", section
+ * "混合Mamba Transformer MoE架构"], expert selection is balanced aux-loss-free in the DeepSeek
+ * style ["Nemotron 3 Nano：開放高效的 MoE 混合 Mamba-Transformer 智能體推理模型", section 2.2],
+ * and the selected experts' outputs are combined with the router's weights ["Nemotron 3 Nano:
+ * Open, Efficient Mixture-of-Experts Hybrid Mamba-Transformer Model for Agentic Reasoning",
+ * section "技术框架"]. LatentMoE projects tokens from H to a latent width l, runs
+ * E' = E*H/l experts with k' = k*H/l there and projects back, while router and shared expert stay
+ * in H ["NVIDIA Nemotron 3: Efficient and Open Intelligence", section 2.2 and Figure 3b].
+ *
+ * What one call computes, per token t (x_t is row t of x):
+ *   logits  z = x_t W_r^T                                   (fp32 accumulation)
+ *   scores  s = sigmoid(z)                                  (fp32, evaluated in double, rounded)
+ *   keys    s + b  -> idx = k largest keys, descending; equal keys: lower expert index first
+ *   gates   g_j = s[idx_j] / sum_j s[idx_j]                 (unbiased scores, sum 1)
+ *   u       = x_t, or x_t W_in^T rounded to bf16 (LatentMoE)
+ *   expert  f_e(u) = relu(u W_up[e]^T)^2 W_down[e]^T        (squared-ReLU, no gate, no bias)
+ *   routed  r = sum_j g_j f_{idx_j}(u)                      (fixed j order: deterministic)
+ *   y_t     = r, or r W_out^T (LatentMoE);  y_t += relu(x_t Ws_up^T)^2 Ws_down^T if I_shared > 0
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers to row-major, contiguous arrays, 16-byte aligned, owned
+ *     by the caller. The library never allocates, frees or synchronises on the call path; scratch
+ *     comes from the caller's workspace (size from moe_workspace_size).
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null stream).
+ *   - Return value: MOE_OK (0) or a negative moe_status; nothing is launched on an error found
+ *     before launch. MOE_ERR_HIP reports a failed launch (hipGetLastError after enqueueing).
+ *   - Thread safety: stateless apart from a per-device properties cache; concurrent calls on
+ *     different streams need different workspaces and outputs.
+ *   - Dimension rules: H, I, I_shared and latent are multiples of 16; 1 <= k <= E <= 1024,
+ *     k <= 64; T >= 0 (T == 0 is a no-op that returns MOE_OK).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_F32 = 0,      /* IEEE binary32 */
+  MOE_BF16 = 1,     /* bfloat16 */
+  MOE_FP8_E4M3 = 2  /* OCP 8-bit E4M3 (fn: max 448, no inf), expert weights only */
+} moe_dtype_t;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,  /* null required pointer, misaligned pointer, bad dimension */
+  MOE_ERR_UNSUPPORTED = -2,  /* dtype / shape / path combination not provided */
+  MOE_ERR_WORKSPACE = -3,    /* workspace missing or smaller than moe_workspace_size */
+  MOE_ERR_HIP = -4           /* a HIP launch failed */
+} moe_status;
+
+/* desc.flags */
+#define MOE_PATH_AUTO 0u         /* stream path when the mean expert load T*k/E is <= 8 */
+#define MOE_PATH_GROUPED 1u      /* grouped MFMA GEMMs with a device-built tile list (prefill) */
+#define MOE_PATH_STREAM 2u       /* read each touched expert's weights once (decode; bf16 only) */
+#define MOE_PATH_MASK 3u
+#define MOE_ROUTING_GIVEN 4u     /* routing->idx and routing->gates are INPUTS: skip the router */
+
+typedef struct {
+  int32_t T;           /* tokens */
+  int32_t H;           /* hidden width */
+  int32_t E;           /* routed experts (E' for LatentMoE) */
+  int32_t k;           /* experts per token (k' for LatentMoE) */
+  int32_t I;           /* expert inner width */
+  int32_t I_shared;    /* shared-expert inner width; 0 = no shared expert */
+  int32_t latent;      /* 0 = plain MoE; else the latent width l (latent_moe_forward only) */
+  moe_dtype_t act_dtype;    /* x, y, W_r, shared expert, W_in, W_out: MOE_F32 or MOE_BF16 */
+  moe_dtype_t expert_dtype; /* W_up, W_down: act_dtype, or MOE_FP8_E4M3 with act MOE_BF16 */
+  uint32_t flags;
+} moe_desc_t;
+
+/* D below is the width the routed experts read and write: H, or latent for LatentMoE. */
+typedef struct {
+  const void *x;        /* [T, H]  act_dtype */
+  const void *W_r;      /* [E, H]  act_dtype (router / gating network, always in H) */
+  const float *b;       /* [E]     fp32 selection bias (enters the keys, never the gates) */
+  const void *W_up;     /* [E, I, D] expert_dtype */
+  const void *W_down;   /* [E, D, I] expert_dtype */
+  const float *s_up;    /* [E, I] fp32 per-output-channel scales (MOE_FP8_E4M3 only) */
+  const float *s_down;  /* [E, D] fp32 per-output-channel scales (MOE_FP8_E4M3 only) */
+  const void *Ws_up;    /* [I_shared, H] act_dtype, or NULL when I_shared == 0 */
+  const void *Ws_down;  /* [H, I_shared] act_dtype, or NULL when I_shared == 0 */
+  const void *W_in;     /* [latent, H] act_dtype (LatentMoE only) */
+  const void *W_out;    /* [H, latent] act_dtype (LatentMoE only) */
+} moe_weights_t;
+
+/* Optional routing record. Any non-NULL member is written (or, for idx and gates under
+ * MOE_ROUTING_GIVEN, read) by the layer call. */
+typedef struct {
+  int32_t *idx;      /* [T, k]  selected experts, descending key order */
+  float *gates;      /* [T, k]  gate weights */
+  int32_t *counts;   /* [E]     pairs per expert */
+  int32_t *offsets;  /* [E + 1] exclusive prefix sum of counts, offsets[E] = T*k */
+  int32_t *perm;     /* [T*k]   token of each pair, grouped by expert, tokens ascending */
+  int32_t *pos;      /* [T, k]  row of pair (t, j) in that grouped order (inverse of perm) */
+  float *logits;     /* [T, E]  router logits */
+} moe_routing_t;
+
+/* Bytes of workspace moe_layer_forward / latent_moe_forward need for this descriptor (the path
+ * is resolved from desc->flags exactly as the forward call resolves it). */
+int32_t moe_workspace_size(const moe_desc_t *desc, size_t *bytes);
+
+/* Plain MoE layer forward (desc->latent must be 0). y: [T, H] act_dtype.
+ * routing may be NULL unless MOE_ROUTING_GIVEN is set. */
+int32_t moe_layer_forward(const moe_desc_t *desc, const moe_weights_t *w, void *y, void *ws,
+                          size_t ws_bytes, moe_routing_t *routing, void *stream);
+
+/* LatentMoE layer forward (desc->latent = l > 0, W_in and W_out required): experts run in the
+ * latent width, their gated sum is projected back with W_out, and the shared expert (if any) is
+ * added in H. y: [T, H] act_dtype. */
+int32_t latent_moe_forward(const moe_desc_t *desc, const moe_weights_t *w, void *y, void *ws,
+                           size_t ws_bytes, moe_routing_t *routing, void *stream);
+
+/* Router alone (steps logits -> scores -> top-k -> gates). If `logits` is non-NULL it is used as
+ * the fp32 router logits [T, E] and x / W_r are ignored; otherwise logits are computed from
+ * x [T, H] and W_r [E, H] (dtype `dt`) into `logits_out` [T, E], which is then required.
+ * Writes idx [T, k] and gates [T, k]. */
+int32_t moe_route(const float *logits, const void *x, const void *W_r, const float *b, int32_t T,
+                  int32_t H, int32_t E, int32_t k, moe_dtype_t dt, int32_t *idx, float *gates,
+                  float *logits_out, void *stream);
+
+/* Workspace bytes moe_dispatch needs. */
+int32_t moe_dispatch_workspace_size(int32_t T, int32_t E, int32_t k, size_t *bytes);
+
+/* Dispatch alone: from idx [T, k] (values in [0, E), distinct per token) build counts [E],
+ * offsets [E + 1], perm [T*k] and pos [T, k] as described in moe_routing_t. The order is stable
+ * and deterministic (no atomics decide it). */
+int32_t moe_dispatch(const int32_t *idx, int32_t T, int32_t E, int32_t k, int32_t *counts,
+                     int32_t *offsets, int32_t *perm, int32_t *pos, void *ws, size_t ws_bytes,
+                     void *stream);
+
+/* Static text for a status code. */
+const char *moe_status_str(int32_t code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

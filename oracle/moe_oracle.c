@@ -196,6 +196,27 @@ int orc_route_f32(const float *z, const float *b, int32_t T, int32_t E, int32_t 
   return ORC_OK;
 }
 
+/* Gates of a given selection (the gate step alone): g_j = s[idx_j] / sum_j s[idx_j] with
+ * s = 1 / (1 + exp(-z)) in double. Used when a selection inside the near-tie band is taken from
+ * elsewhere and the layer output is recomputed for it. */
+int orc_gates_for(const double *z, const int32_t *idx, int32_t T, int32_t E, int32_t k,
+                  double *gates) {
+  if (!z || !idx || !gates || E < 1 || k < 1 || k > E) return ORC_EINVAL;
+  for (int32_t t = 0; t < T; ++t) {
+    double sum = 0.0;
+    for (int32_t j = 0; j < k; ++j) {
+      int32_t e = idx[(int64_t)t * k + j];
+      if (e < 0 || e >= E) return ORC_EINVAL;
+      sum += 1.0 / (1.0 + exp(-z[(int64_t)t * E + e]));
+    }
+    for (int32_t j = 0; j < k; ++j) {
+      int32_t e = idx[(int64_t)t * k + j];
+      gates[(int64_t)t * k + j] = (1.0 / (1.0 + exp(-z[(int64_t)t * E + e]))) / sum;
+    }
+  }
+  return ORC_OK;
+}
+
 /* ------------------------------------------------------------------ dispatch */
 
 /* Group the T*k (token, slot) pairs by expert, tokens ascending inside an expert:

@@ -68,6 +68,7 @@ def lib():
                                     f64p]
             L.orc_route_f32.argtypes = [f32p, f32p, C.c_int32, C.c_int32, C.c_int32, i32p, f64p,
                                         f64p]
+            L.orc_gates_for.argtypes = [f64p, i32p, C.c_int32, C.c_int32, C.c_int32, f64p]
             L.orc_dispatch.argtypes = [i32p, C.c_int32, C.c_int32, C.c_int32, i32p, i32p, i32p,
                                        i32p]
             L.orc_forward_tokens.argtypes = [C.POINTER(OrcLayer), C.c_void_p, C.c_int32, i32p,
@@ -163,6 +164,16 @@ def route_f32(z32: np.ndarray, b: np.ndarray, k: int):
     m = np.zeros(T, np.float64)
     _check(lib().orc_route_f32(z32, np.ascontiguousarray(b, np.float32), T, E, k, idx, g, m))
     return idx, g, m
+
+
+def gates_for(z: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Gate weights of a given selection idx [T,k] from double logits z [T,E]."""
+    z = np.ascontiguousarray(z, dtype=np.float64)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    T, E = z.shape
+    g = np.zeros(idx.shape, np.float64)
+    _check(lib().orc_gates_for(z, idx, T, E, idx.shape[1], g))
+    return g
 
 
 def dispatch(idx: np.ndarray, E: int):

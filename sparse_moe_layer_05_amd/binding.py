@@ -1,0 +1,230 @@
+"""ctypes binding of libmoe_mi355x.so (the gfx950 MoE layer library).
+
+Argument marshalling only: torch tensors supply device memory and the current stream; every step
+of the layer runs in the library's HIP kernels. The library must have been built
+(``python -m sparse_moe_layer_05_amd.build``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import threading
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
+
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+PATH_AUTO, PATH_GROUPED, PATH_STREAM, ROUTING_GIVEN = 0, 1, 2, 4
+_PATHS = {"auto": PATH_AUTO, "grouped": PATH_GROUPED, "stream": PATH_STREAM}
+
+EXPORTS = ("moe_workspace_size", "moe_layer_forward", "latent_moe_forward", "moe_route",
+           "moe_dispatch_workspace_size", "moe_dispatch", "moe_status_str")
+
+
+class MoeDesc(C.Structure):
+    _fields_ = [("T", C.c_int32), ("H", C.c_int32), ("E", C.c_int32), ("k", C.c_int32),
+                ("I", C.c_int32), ("I_shared", C.c_int32), ("latent", C.c_int32),
+                ("act_dtype", C.c_int32), ("expert_dtype", C.c_int32), ("flags", C.c_uint32)]
+
+
+class MoeWeights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("x", "W_r", "b", "W_up", "W_down", "s_up", "s_down",
+                                          "Ws_up", "Ws_down", "W_in", "W_out")]
+
+
+class MoeRouting(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("idx", "gates", "counts", "offsets", "perm", "pos",
+                                          "logits")]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {status_str(code)} ({code})")
+        self.code = code
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load the library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                                   "(run python -m sparse_moe_layer_05_amd.build)")
+            L = C.CDLL(LIB_PATH)
+            vp, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
+            L.moe_workspace_size.argtypes = [C.POINTER(MoeDesc), C.POINTER(sz)]
+            for fn in (L.moe_layer_forward, L.latent_moe_forward):
+                fn.argtypes = [C.POINTER(MoeDesc), C.POINTER(MoeWeights), vp, vp, sz,
+                               C.POINTER(MoeRouting), vp]
+            L.moe_route.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+            L.moe_dispatch_workspace_size.argtypes = [i32, i32, i32, C.POINTER(sz)]
+            L.moe_dispatch.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+            L.moe_status_str.argtypes = [i32]
+            L.moe_status_str.restype = C.c_char_p
+            for name in EXPORTS:
+                if name != "moe_status_str":
+                    getattr(L, name).restype = C.c_int32
+            _lib = L
+    return _lib
+
+
+def status_str(code: int) -> str:
+    return lib().moe_status_str(code).decode()
+
+
+def _check(rc: int, where: str):
+    if rc != MOE_OK:
+        raise MoeError(rc, where)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return MOE_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def make_desc(x, W_r, W_up, k, Ws_up=None, W_in=None, path="auto", routing_given=False):
+    T, H = x.shape
+    E, I = W_up.shape[0], W_up.shape[1]
+    d = MoeDesc()
+    d.T, d.H, d.E, d.k, d.I = T, H, E, k, I
+    d.I_shared = Ws_up.shape[0] if Ws_up is not None else 0
+    d.latent = W_in.shape[0] if W_in is not None else 0
+    d.act_dtype = _dtype_code(x)
+    d.expert_dtype = _dtype_code(W_up)
+    d.flags = _PATHS[path] | (ROUTING_GIVEN if routing_given else 0)
+    return d
+
+
+def workspace_size(desc: MoeDesc) -> int:
+    n = C.c_size_t(0)
+    _check(lib().moe_workspace_size(C.byref(desc), C.byref(n)), "moe_workspace_size")
+    return n.value
+
+
+def alloc_routing(T: int, E: int, k: int, device) -> dict:
+    i32 = dict(dtype=torch.int32, device=device)
+    return dict(idx=torch.empty((T, k), **i32), gates=torch.empty((T, k), dtype=torch.float32,
+                                                                  device=device),
+                counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
+                perm=torch.empty(T * k, **i32), pos=torch.empty((T, k), **i32),
+                logits=torch.empty((T, E), dtype=torch.float32, device=device))
+
+
+class Layer:
+    """One layer call prepared once (descriptor, weights struct, workspace, outputs), so that a
+    benchmark loop or a graph capture can replay ``__call__`` without any allocation."""
+
+    def __init__(self, x, W_r, b, W_up, W_down, k, *, s_up=None, s_down=None, Ws_up=None,
+                 Ws_down=None, W_in=None, W_out=None, path="auto", routing=None,
+                 routing_given=False, out=None):
+        self.desc = make_desc(x, W_r, W_up, k, Ws_up, W_in, path, routing_given)
+        w = MoeWeights()
+        w.x, w.W_r, w.b, w.W_up, w.W_down = _p(x), _p(W_r), _p(b), _p(W_up), _p(W_down)
+        w.s_up, w.s_down = _p(s_up), _p(s_down)
+        w.Ws_up, w.Ws_down, w.W_in, w.W_out = _p(Ws_up), _p(Ws_down), _p(W_in), _p(W_out)
+        self.w = w
+        self._keep = [x, W_r, b, W_up, W_down, s_up, s_down, Ws_up, Ws_down, W_in, W_out]
+        self.y = out if out is not None else torch.empty_like(x)
+        self.ws_bytes = workspace_size(self.desc)
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=x.device)
+        self.routing = routing
+        self.r = None
+        if routing is not None:
+            r = MoeRouting()
+            for name, _ in MoeRouting._fields_:
+                setattr(r, name, _p(routing.get(name)))
+            self.r = r
+        self.fn = lib().latent_moe_forward if self.desc.latent else lib().moe_layer_forward
+
+    def __call__(self, stream=None):
+        rc = self.fn(C.byref(self.desc), C.byref(self.w), _p(self.y), _p(self.ws), self.ws_bytes,
+                     C.byref(self.r) if self.r is not None else None, _stream(stream))
+        _check(rc, "latent_moe_forward" if self.desc.latent else "moe_layer_forward")
+        return self.y
+
+
+def layer_forward(x, W_r, b, W_up, W_down, k, **kw):
+    """y = MoE layer (or LatentMoE when W_in / W_out are given) of x; see moe.h."""
+    return Layer(x, W_r, b, W_up, W_down, k, **kw)()
+
+
+def route(b, k, *, logits=None, x=None, W_r=None, stream=None):
+    """Router alone. Returns (idx, gates, logits)."""
+    src = logits if logits is not None else x
+    T = src.shape[0]
+    E = b.shape[0]
+    dev = src.device
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    lo = None
+    H, dt = 0, MOE_F32
+    if logits is None:
+        H = x.shape[1]
+        dt = _dtype_code(x)
+        lo = torch.empty((T, E), dtype=torch.float32, device=dev)
+    rc = lib().moe_route(_p(logits), _p(x), _p(W_r), _p(b), T, H, E, k, dt, _p(idx), _p(gates),
+                         _p(lo), _stream(stream))
+    _check(rc, "moe_route")
+    return idx, gates, (logits if logits is not None else lo)
+
+
+def dispatch(idx, E, stream=None):
+    """(counts, offsets, perm, pos) of idx [T, k]."""
+    T, k = idx.shape
+    dev = idx.device
+    n = C.c_size_t(0)
+    _check(lib().moe_dispatch_workspace_size(T, E, k, C.byref(n)), "moe_dispatch_workspace_size")
+    ws = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    pos = torch.empty((T, k), dtype=torch.int32, device=dev)
+    rc = lib().moe_dispatch(_p(idx), T, E, k, _p(counts), _p(offsets), _p(perm), _p(pos), _p(ws),
+                            n.value, _stream(stream))
+    _check(rc, "moe_dispatch")
+    return counts, offsets, perm, pos
+
+
+def to_device(inp: dict, device="cuda") -> dict:
+    """numpy arrays of a ``moe_inputs.make_layer`` dict -> torch tensors on ``device``
+    (uint16 bf16 bit patterns become torch.bfloat16; e4m3 codes stay uint8)."""
+    import numpy as np
+    out = {}
+    for name, a in inp.items():
+        if isinstance(a, np.ndarray):
+            t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 \
+                else torch.from_numpy(a)
+            out[name] = t.to(device)
+    return out
+
+
+def layer_from(dev: dict, k: int, **kw) -> Layer:
+    """A Layer over a ``to_device`` dict."""
+    return Layer(dev["x"], dev["W_r"], dev["b"], dev["W_up"], dev["W_down"], k,
+                 s_up=dev.get("s_up"), s_down=dev.get("s_down"), Ws_up=dev.get("Ws_up"),
+                 Ws_down=dev.get("Ws_down"), W_in=dev.get("W_in"), W_out=dev.get("W_out"), **kw)

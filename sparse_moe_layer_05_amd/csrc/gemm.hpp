@@ -1,0 +1,75 @@
+// Parameters and launchers of the tiled GEMM family used by the MoE layer:
+//   C[m, n] = epilogue( sum_k A[m, k] * B[n, k] )      (both operands K-contiguous)
+// A holds activations (token rows, optionally gathered through an index list), B holds weights
+// stored [G][N][K] (one [N][K] panel per expert). Grouped launches walk a device-built list of
+// (expert, M-tile) pairs, so no host round trip is needed to learn the per-expert token counts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum class Elt : int { F32 = 0, BF16 = 1, FP8 = 2 };
+
+enum class Epi : int {
+  Store = 0,        // C = acc
+  SqRelu = 1,       // C = relu(acc)^2
+  SqReluAmax = 2,   // C = relu(acc)^2 (bf16) and row_amax[row] = max over the row (bit-pattern max)
+  Combine = 3       // C[t] = acc + sum_j gates[t, j] * Y[pos[t, j]]   (rows are tokens)
+};
+
+struct GemmParams {
+  // A operand: rows of K elements (a_elt); row r of group g is a_gather[offs[g] + r] when
+  // a_gather is set, else offs[g] + r. With a_quant the bf16 rows are quantised to e4m3 on load
+  // with per-row scale row_amax[out row] / 448.
+  const void* A = nullptr;
+  int64_t lda = 0;  // elements
+  const int32_t* a_gather = nullptr;
+  const float* a_scale = nullptr;  // fp8 A: scale per *source* row (token)
+  int a_quant = 0;
+  // B operand: [G][N][K], b_gstride elements between experts; fp8: per-channel scales [G][N]
+  const void* B = nullptr;
+  int64_t ldb = 0;
+  int64_t b_gstride = 0;
+  const float* b_scale = nullptr;
+  // Optional second K segment for dense launches: acc += A2[m, :] . B2[n, :]
+  const void* A2 = nullptr;
+  int64_t lda2 = 0;
+  const void* B2 = nullptr;
+  int64_t ldb2 = 0;
+  int K2 = 0;
+  // Output
+  void* C = nullptr;
+  int64_t ldc = 0;
+  int M = 0, N = 0, K = 0;
+  // Grouping (both null for a dense launch of M rows)
+  const int32_t* offs = nullptr;      // [G + 1] row offsets
+  const int32_t* mt_start = nullptr;  // [G + 1] prefix of ceil(rows_g / BM)
+  int G = 0;
+  // Epilogue inputs
+  float* row_amax = nullptr;          // SqReluAmax output / a_quant input, indexed by out row
+  const float* gates = nullptr;       // Combine: [M, topk]
+  const int32_t* pos = nullptr;       // Combine: [M, topk]
+  int topk = 0;
+  const void* Y = nullptr;            // Combine: rows of N, y_elt
+  int64_t ldy = 0;
+};
+
+struct GemmKind {
+  Elt ab;      // element type of A and B as fed to the matrix cores (F32: vector ALU path)
+  Elt out;     // C element type
+  Epi epi;
+  Elt y = Elt::BF16;  // Combine: element type of Y
+};
+
+// Tile height of the grouped launches; the dispatch step builds mt_start with it.
+constexpr int kGroupBM = 128;
+
+// Upper bound of M-tiles over all groups for P routed rows in G groups (each group wastes < 1).
+inline int max_group_mtiles(int P, int G, int BM) { return (P + G * (BM - 1)) / BM; }
+
+hipError_t launch_gemm(const GemmKind& kind, const GemmParams& p, int max_mtiles,
+                       hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,69 @@
+// Launchers of the non-GEMM kernels of the MoE layer (routing, dispatch, combine, fp8
+// activation quantisation, decode-path expert streaming).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm.hpp"
+
+namespace moe {
+
+constexpr int kDispatchChunk = 256;  // tokens per dispatch workgroup
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 64;
+
+// logits [T, E] fp32 -> idx [T, k] (descending key, lower index on ties), gates [T, k].
+hipError_t launch_topk(const float* logits, const float* b, int T, int E, int k, int32_t* idx,
+                       float* gates, hipStream_t s);
+
+// Dispatch scratch: chunk_counts and chunk_base, each [ceil(T / 256), E] int32.
+inline size_t dispatch_scratch_ints(int T, int E) {
+  return 2 * (size_t)((T + kDispatchChunk - 1) / kDispatchChunk) * (size_t)E;
+}
+
+// idx [T, k] -> counts [E], offsets [E + 1], perm [T*k], pos [T, k]; optionally the prefix of
+// ceil(counts / bm) M-tiles (mt_start [E + 1], for grouped GEMMs) and zeroes zero_rows[r] for
+// every written pair row r. Pairs with an out-of-range or repeated expert are dropped (pos = -1).
+hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int32_t* counts,
+                           int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* scratch,
+                           int bm, int32_t* mt_start, float* zero_rows, hipStream_t s);
+
+// out[t] = S[t] (optional, same element type as Y) + sum_j gates[t, j] * Y[pos[t, j]], in fixed
+// j order, rounded once to out_elt.
+hipError_t launch_combine(const void* Y, Elt y_elt, int64_t ldy, const void* S, int64_t lds,
+                          const int32_t* pos, const float* gates, int T, int D, int k, void* out,
+                          Elt out_elt, int64_t ldo, hipStream_t s);
+
+// Per-row e4m3 quantisation of bf16 rows: scale[t] = amax / 448 (1 for a zero row),
+// q[t, :] = e4m3(x / scale).
+hipError_t launch_quant_rows(const uint16_t* x, int64_t ldx, int T, int H, uint8_t* q,
+                             float* scale, hipStream_t s);
+
+// Decode path: every routed group g (expert) with rows offs[g] .. offs[g+1] and, optionally, the
+// shared expert (rows 0 .. Ts-1 of As) stream their weight matrix [N][K] from HBM exactly once:
+//   out[r, n] = act( sum_k A[src(r), k] * W[g][n, k] )
+// act = bf16(relu(acc)^2) for the up projection, fp32 acc for the down projection.
+struct StreamParams {
+  // routed experts
+  const uint16_t* A = nullptr;        // activation rows (bf16), lda elements apart
+  int64_t lda = 0;
+  const int32_t* gather = nullptr;    // source row of pair row r = gather[r] (nullptr: r)
+  const int32_t* offs = nullptr;      // [E + 1]
+  int E = 0;
+  const uint16_t* W = nullptr;        // [E][N][K]
+  int N = 0, K = 0;
+  void* out = nullptr;                // pair rows, ldo elements apart
+  int64_t ldo = 0;
+  // shared expert (Ws == nullptr: none)
+  const uint16_t* As = nullptr;
+  int64_t lda_s = 0;
+  const uint16_t* Ws = nullptr;       // [Ns][Ks]
+  int Ns = 0, Ks = 0, Ts = 0;
+  void* out_s = nullptr;
+  int64_t ldo_s = 0;
+  int sqrelu_bf16 = 0;                // 1: bf16(relu(acc)^2); 0: fp32 acc
+};
+hipError_t launch_stream(const StreamParams& p, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,336 @@
+// Router top-k, dispatch, combine and fp8 activation quantisation for the MoE layer (gfx950).
+//
+// Routing follows the Nemotron 3 MoE layer: the router picks k of E experts per token
+// ("NVIDIA AI发布了Nemotron 3：一款混合Mamba Transformer MoE堆栈", section
+// "混合Mamba Transformer MoE架构") with an aux-loss-free per-expert bias that only steers the
+// selection ("Nemotron 3 Nano：開放高效的 MoE 混合 Mamba-Transformer 智能體推理模型", section
+// 2.2); sigmoid scores renormalised over the selected experts are the gate weights.
+#include "common.hpp"
+#include "kernels.hpp"
+
+#include <math.h>
+
+namespace moe {
+namespace {
+
+// ------------------------------------------------------------------------------------ top-k
+// One wave per token. Lane l holds experts l, l + 64, ...; k rounds of a wave-wide arg-max
+// over (key desc, expert asc) by butterfly shuffles, the winner's owner lane retiring it.
+// s = fp32(1 / (1 + exp(-z))) is evaluated in double so that the rounded score does not depend
+// on a particular single-precision exp; key = s + b is one binary32 addition.
+template <int NPER>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
+                                                   const float* __restrict__ bias, int T, int E,
+                                                   int k, int32_t* __restrict__ idx,
+                                                   float* __restrict__ gates) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float key[NPER], sc[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) {
+      const float z = logits[(int64_t)t * E + e];
+      const float s = (float)(1.0 / (1.0 + exp(-(double)z)));
+      sc[i] = s;
+      key[i] = s + bias[e];
+    } else {
+      sc[i] = 0.f;
+      key[i] = -INFINITY;
+    }
+  }
+  uint32_t taken = 0;
+  float sum = 0.f, mine = 0.f;
+  for (int j = 0; j < k; ++j) {
+    float bk = -INFINITY, bs = 0.f;
+    int be = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+      const int e = lane + 64 * i;
+      const bool free = !((taken >> i) & 1u) && e < E;
+      if (free && (key[i] > bk || (key[i] == bk && e < be))) {
+        bk = key[i];
+        be = e;
+        bs = sc[i];
+      }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const float ok = __shfl_xor(bk, m);
+      const int oe = __shfl_xor(be, m);
+      const float os = __shfl_xor(bs, m);
+      if (ok > bk || (ok == bk && oe < be)) {
+        bk = ok;
+        be = oe;
+        bs = os;
+      }
+    }
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    sum += bs;                       // same order j = 0..k-1 on every lane: deterministic
+    if (lane == j) mine = bs;
+    if (lane == 0) idx[(int64_t)t * k + j] = be;
+  }
+  if (lane < k) gates[(int64_t)t * k + lane] = mine / sum;
+}
+
+// --------------------------------------------------------------------------------- dispatch
+// Tokens are cut into chunks of 256 (one workgroup each). Inside a chunk, an LDS bitmask per
+// expert records which of the 256 tokens chose it; the popcount of the bits below a token is
+// its stable rank inside the chunk, and chunk bases from a prefix over chunks make the global
+// order "experts ascending, tokens ascending" without any order-deciding atomics.
+__device__ __forceinline__ uint32_t build_masks(const int32_t* __restrict__ idx, int T, int E,
+                                                int k, uint32_t* mask, int t, int tid) {
+  for (int i = tid; i < E * 8; i += kDispatchChunk) mask[i] = 0;
+  __syncthreads();
+  uint32_t valid = 0;  // bit j: pair (t, j) is kept
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(int64_t)t * k + j];
+      if ((unsigned)e < (unsigned)E) {
+        const uint32_t bit = 1u << (tid & 31);
+        const uint32_t old = atomicOr(&mask[e * 8 + (tid >> 5)], bit);
+        if (!(old & bit)) valid |= 1u << j;  // a repeated expert in one token is dropped
+      }
+    }
+  }
+  __syncthreads();
+  return valid;
+}
+
+__global__ __launch_bounds__(kDispatchChunk) void dispatch_count(const int32_t* __restrict__ idx,
+                                                                 int T, int E, int k,
+                                                                 int32_t* __restrict__ ccount) {
+  extern __shared__ uint32_t mask[];
+  const int tid = threadIdx.x, c = blockIdx.x;
+  build_masks(idx, T, E, k, mask, c * kDispatchChunk + tid, tid);
+  for (int e = tid; e < E; e += kDispatchChunk) {
+    int n = 0;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) n += __popc(mask[e * 8 + w]);
+    ccount[(int64_t)c * E + e] = n;
+  }
+}
+
+// One workgroup of 1024 threads, thread e = expert e.
+__global__ __launch_bounds__(1024) void dispatch_scan(const int32_t* __restrict__ ccount,
+                                                      int nchunks, int E, int bm,
+                                                      int32_t* __restrict__ cbase,
+                                                      int32_t* __restrict__ counts,
+                                                      int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ mt_start) {
+  __shared__ int32_t s_a[1024], s_b[1024];
+  const int e = threadIdx.x;
+  int tot = 0;
+  if (e < E)
+    for (int c = 0; c < nchunks; ++c) tot += ccount[(int64_t)c * E + e];
+  const int mt = bm > 0 ? (tot + bm - 1) / bm : 0;
+  s_a[e] = e < E ? tot : 0;
+  s_b[e] = e < E ? mt : 0;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {  // inclusive Hillis-Steele scan
+    const int va = e >= d ? s_a[e - d] : 0, vb = e >= d ? s_b[e - d] : 0;
+    __syncthreads();
+    s_a[e] += va;
+    s_b[e] += vb;
+    __syncthreads();
+  }
+  if (e < E) {
+    const int ex = s_a[e] - tot;
+    counts[e] = tot;
+    offsets[e] = ex;
+    if (e == E - 1) offsets[E] = s_a[e];
+    if (mt_start) {
+      mt_start[e] = s_b[e] - mt;
+      if (e == E - 1) mt_start[E] = s_b[e];
+    }
+    int run = ex;
+    for (int c = 0; c < nchunks; ++c) {
+      cbase[(int64_t)c * E + e] = run;
+      run += ccount[(int64_t)c * E + e];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kDispatchChunk) void dispatch_scatter(
+    const int32_t* __restrict__ idx, int T, int E, int k, const int32_t* __restrict__ cbase,
+    int32_t* __restrict__ perm, int32_t* __restrict__ pos, float* __restrict__ zero_rows) {
+  extern __shared__ uint32_t mask[];
+  const int tid = threadIdx.x, c = blockIdx.x, t = c * kDispatchChunk + tid;
+  const uint32_t valid = build_masks(idx, T, E, k, mask, t, tid);
+  if (t >= T) return;
+  const int w = tid >> 5;
+  const uint32_t below = (1u << (tid & 31)) - 1u;
+  for (int j = 0; j < k; ++j) {
+    if (!((valid >> j) & 1u)) {
+      pos[(int64_t)t * k + j] = -1;
+      continue;
+    }
+    const int e = idx[(int64_t)t * k + j];
+    int rank = __popc(mask[e * 8 + w] & below);
+    for (int q = 0; q < w; ++q) rank += __popc(mask[e * 8 + q]);
+    const int r = cbase[(int64_t)c * E + e] + rank;
+    perm[r] = t;
+    pos[(int64_t)t * k + j] = r;
+    if (zero_rows) zero_rows[r] = 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------------- combine
+// One workgroup per token; each thread owns 8 consecutive columns (one 16-byte bf16 load or two
+// fp32 loads per source row). Sum order: S first, then j = 0..k-1.
+template <Elt YT, Elt OT>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y, int64_t ldy,
+                                                      const void* __restrict__ S, int64_t lds,
+                                                      const int32_t* __restrict__ pos,
+                                                      const float* __restrict__ gates, int T,
+                                                      int D, int k, void* __restrict__ out,
+                                                      int64_t ldo) {
+  const int t = blockIdx.x;
+  for (int c = threadIdx.x * 8; c < D; c += blockDim.x * 8) {
+    float acc[8];
+    auto load8 = [&](const void* base, int64_t row, int64_t ld, float* v) {
+      if constexpr (YT == Elt::BF16) {
+        const uint4 q = *(const uint4*)((const uint16_t*)base + row * ld + c);
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFF);
+          v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+        }
+      } else {
+        const float4 a = *(const float4*)((const float*)base + row * ld + c);
+        const float4 b = *(const float4*)((const float*)base + row * ld + c + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+      }
+    };
+    if (S) {
+      load8(S, t, lds, acc);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    }
+    for (int j = 0; j < k; ++j) {
+      const int r = pos[(int64_t)t * k + j];
+      if (r < 0) continue;
+      const float g = gates[(int64_t)t * k + j];
+      float v[8];
+      load8(Y, r, ldy, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+    }
+    if constexpr (OT == Elt::BF16) {
+      uint4 q;
+      q.x = pack_bf16x2(acc[0], acc[1]);
+      q.y = pack_bf16x2(acc[2], acc[3]);
+      q.z = pack_bf16x2(acc[4], acc[5]);
+      q.w = pack_bf16x2(acc[6], acc[7]);
+      *(uint4*)((uint16_t*)out + (int64_t)t * ldo + c) = q;
+    } else {
+      float* o = (float*)out + (int64_t)t * ldo + c;
+      *(float4*)o = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      *(float4*)(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+  }
+}
+
+// -------------------------------------------------------------------------------- quantise
+// One workgroup per row: amax by wave shuffles + LDS, then e4m3 codes of x / scale.
+__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x,
+                                                         int64_t ldx, int H,
+                                                         uint8_t* __restrict__ q,
+                                                         float* __restrict__ scale) {
+  __shared__ float s_max[4];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const uint16_t* row = x + (int64_t)t * ldx;
+  float m = 0.f;
+  for (int c = tid * 8; c < H; c += 256 * 8) {
+    const uint4 v = *(const uint4*)(row + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m = fmaxf(m, fabsf(bf16_bits_to_f32(w[i] & 0xFFFF)));
+      m = fmaxf(m, fabsf(bf16_bits_to_f32(w[i] >> 16)));
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((tid & 63) == 0) s_max[tid >> 6] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+  const float s = amax > 0.f ? amax / 448.f : 1.f;
+  if (tid == 0) scale[t] = s;
+  for (int c = tid * 8; c < H; c += 256 * 8) {
+    const uint4 v = *(const uint4*)(row + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float f0 = bf16_bits_to_f32(w[2 * h] & 0xFFFF) / s;
+      const float f1 = bf16_bits_to_f32(w[2 * h] >> 16) / s;
+      const float f2 = bf16_bits_to_f32(w[2 * h + 1] & 0xFFFF) / s;
+      const float f3 = bf16_bits_to_f32(w[2 * h + 1] >> 16) / s;
+      o[h] = cvt_fp8x2(f0, f1) | (cvt_fp8x2(f2, f3) << 16);
+    }
+    *(uint2*)(q + (int64_t)t * H + c) = make_uint2(o[0], o[1]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_topk(const float* logits, const float* b, int T, int E, int k, int32_t* idx,
+                       float* gates, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const dim3 grid((T + 3) / 4), block(256);
+  if (E <= 64) hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, logits, b, T, E, k, idx, gates);
+  else if (E <= 128) hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, logits, b, T, E, k, idx, gates);
+  else if (E <= 256) hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, logits, b, T, E, k, idx, gates);
+  else if (E <= 512) hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, logits, b, T, E, k, idx, gates);
+  else hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, logits, b, T, E, k, idx, gates);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int32_t* counts,
+                           int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* scratch,
+                           int bm, int32_t* mt_start, float* zero_rows, hipStream_t s) {
+  const int nch = (T + kDispatchChunk - 1) / kDispatchChunk;
+  int32_t* ccount = scratch;
+  int32_t* cbase = scratch + (size_t)nch * E;
+  const size_t lds = (size_t)E * 8 * sizeof(uint32_t);
+  if (nch > 0)
+    hipLaunchKernelGGL(dispatch_count, dim3(nch), dim3(kDispatchChunk), lds, s, idx, T, E, k,
+                       ccount);
+  hipLaunchKernelGGL(dispatch_scan, dim3(1), dim3(1024), 0, s, ccount, nch, E, bm, cbase, counts,
+                     offsets, mt_start);
+  if (nch > 0)
+    hipLaunchKernelGGL(dispatch_scatter, dim3(nch), dim3(kDispatchChunk), lds, s, idx, T, E, k,
+                       cbase, perm, pos, zero_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const void* Y, Elt y_elt, int64_t ldy, const void* S, int64_t lds,
+                          const int32_t* pos, const float* gates, int T, int D, int k, void* out,
+                          Elt out_elt, int64_t ldo, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const int threads = D / 8 >= 256 ? 256 : ((D / 8 + 63) / 64) * 64;
+  const dim3 grid(T), block(threads);
+  if (y_elt == Elt::BF16 && out_elt == Elt::BF16)
+    hipLaunchKernelGGL((combine_kernel<Elt::BF16, Elt::BF16>), grid, block, 0, s, Y, ldy, S, lds, pos, gates, T, D, k, out, ldo);
+  else if (y_elt == Elt::F32 && out_elt == Elt::BF16)
+    hipLaunchKernelGGL((combine_kernel<Elt::F32, Elt::BF16>), grid, block, 0, s, Y, ldy, S, lds, pos, gates, T, D, k, out, ldo);
+  else if (y_elt == Elt::F32 && out_elt == Elt::F32)
+    hipLaunchKernelGGL((combine_kernel<Elt::F32, Elt::F32>), grid, block, 0, s, Y, ldy, S, lds, pos, gates, T, D, k, out, ldo);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(const uint16_t* x, int64_t ldx, int T, int H, uint8_t* q,
+                             float* scale, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_rows_kernel, dim3(T), dim3(256), 0, s, x, ldx, H, q, scale);
+  return hipGetLastError();
+}
+
+}  // namespace moe

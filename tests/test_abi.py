@@ -1,0 +1,125 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol include/moe.h declares, and
+rejects bad arguments before it launches anything (no GPU is touched by these calls)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import sparse_moe_layer_05_amd as moe
+from sparse_moe_layer_05_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = C.c_void_p(0x10000)    # aligned, never dereferenced: validation fails or returns first
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    return set(re.findall(r"^(?:int32_t|const char \*)\s*(\w+)\(", text, re.M))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert names == set(B.EXPORTS)
+    L = moe.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def desc(**kw):
+    d = B.MoeDesc()
+    base = dict(T=64, H=256, E=16, k=2, I=128, I_shared=0, latent=0, act_dtype=1,
+                expert_dtype=1, flags=0)
+    base.update(kw)
+    for k_, v in base.items():
+        setattr(d, k_, v)
+    return d
+
+
+def ws_size(d):
+    n = C.c_size_t(0)
+    rc = moe.lib().moe_workspace_size(C.byref(d), C.byref(n))
+    return rc, n.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=0), B.MOE_ERR_INVALID_ARG), (dict(k=17), B.MOE_ERR_INVALID_ARG),
+    (dict(k=65, E=128), B.MOE_ERR_INVALID_ARG), (dict(E=0), B.MOE_ERR_INVALID_ARG),
+    (dict(E=1025, k=2), B.MOE_ERR_INVALID_ARG), (dict(T=-1), B.MOE_ERR_INVALID_ARG),
+    (dict(H=250), B.MOE_ERR_INVALID_ARG), (dict(I=100), B.MOE_ERR_INVALID_ARG),
+    (dict(I_shared=8), B.MOE_ERR_INVALID_ARG), (dict(latent=40), B.MOE_ERR_INVALID_ARG),
+    (dict(act_dtype=2), B.MOE_ERR_UNSUPPORTED), (dict(act_dtype=0, expert_dtype=2),
+                                                  B.MOE_ERR_UNSUPPORTED),
+    (dict(act_dtype=0, expert_dtype=1), B.MOE_ERR_UNSUPPORTED),
+    (dict(expert_dtype=2, flags=B.PATH_STREAM), B.MOE_ERR_UNSUPPORTED),
+    (dict(act_dtype=0, expert_dtype=0, flags=B.PATH_STREAM), B.MOE_ERR_UNSUPPORTED),
+    (dict(flags=3), B.MOE_ERR_INVALID_ARG), (dict(flags=64), B.MOE_ERR_INVALID_ARG),
+])
+def test_descriptor_validation(kw, code):
+    assert ws_size(desc(**kw))[0] == code
+
+
+def test_workspace_grows_with_tokens_and_path():
+    a = ws_size(desc(T=64))[1]
+    b = ws_size(desc(T=640))[1]
+    assert 0 < a < b
+    s = ws_size(desc(T=64, flags=B.PATH_STREAM))[1]
+    g = ws_size(desc(T=64, flags=B.PATH_GROUPED))[1]
+    assert s > 0 and g > 0
+    assert ws_size(desc(T=0))[0] == 0
+
+
+def forward(d, w=None, y=FAKE, ws=FAKE, ws_bytes=1 << 40, r=None, latent=False):
+    if w is None:
+        w = B.MoeWeights()
+        for n, _ in B.MoeWeights._fields_:
+            setattr(w, n, FAKE.value)
+    fn = moe.lib().latent_moe_forward if latent else moe.lib().moe_layer_forward
+    return fn(C.byref(d), C.byref(w), y, ws, ws_bytes, C.byref(r) if r else None, None)
+
+
+def test_forward_argument_errors_are_reported_before_launch():
+    assert forward(desc(k=0)) == B.MOE_ERR_INVALID_ARG
+    assert forward(desc(), y=None) == B.MOE_ERR_INVALID_ARG
+    assert forward(desc(), y=C.c_void_p(0x10004)) == B.MOE_ERR_INVALID_ARG   # misaligned
+    assert forward(desc(), ws=None) == B.MOE_ERR_WORKSPACE
+    assert forward(desc(), ws_bytes=16) == B.MOE_ERR_WORKSPACE
+    assert forward(desc(latent=64)) == B.MOE_ERR_INVALID_ARG                # latent via plain call
+    assert forward(desc(), latent=True) == B.MOE_ERR_INVALID_ARG            # plain via latent call
+    w = B.MoeWeights()
+    for n, _ in B.MoeWeights._fields_:
+        setattr(w, n, FAKE.value)
+    w.W_up = None
+    assert forward(desc(), w=w) == B.MOE_ERR_INVALID_ARG
+    w.W_up = FAKE.value
+    w.Ws_up = None
+    assert forward(desc(I_shared=64), w=w) == B.MOE_ERR_INVALID_ARG
+    w.Ws_up = FAKE.value
+    w.s_up = None
+    assert forward(desc(expert_dtype=2), w=w) == B.MOE_ERR_INVALID_ARG
+    assert forward(desc(flags=B.ROUTING_GIVEN)) == B.MOE_ERR_INVALID_ARG   # given but no record
+    assert forward(desc(T=0)) == B.MOE_OK                                 # empty: no-op
+
+
+def test_route_and_dispatch_argument_errors():
+    L = moe.lib()
+    assert L.moe_route(None, FAKE, FAKE, FAKE, 4, 64, 8, 0, 1, FAKE, FAKE, FAKE, None) == \
+        B.MOE_ERR_INVALID_ARG
+    assert L.moe_route(None, FAKE, FAKE, FAKE, 4, 64, 8, 2, 1, FAKE, FAKE, None, None) == \
+        B.MOE_ERR_INVALID_ARG                                    # x given but no logits_out
+    assert L.moe_route(None, FAKE, FAKE, FAKE, 4, 64, 8, 2, 2, FAKE, FAKE, FAKE, None) == \
+        B.MOE_ERR_UNSUPPORTED
+    assert L.moe_route(FAKE, None, None, FAKE, 0, 0, 8, 2, 0, FAKE, FAKE, None, None) == B.MOE_OK
+    n = C.c_size_t(0)
+    assert L.moe_dispatch_workspace_size(300, 16, 2, C.byref(n)) == B.MOE_OK
+    assert n.value == 2 * 2 * 16 * 4                             # two [ceil(300/256), E] int tables
+    assert L.moe_dispatch(FAKE, 300, 16, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None) == \
+        B.MOE_ERR_WORKSPACE
+    assert L.moe_dispatch(FAKE, 300, 16, 17, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == \
+        B.MOE_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4):
+        assert moe.status_str(code) and moe.status_str(code) != "unknown status"
+    assert moe.status_str(7) == "unknown status"

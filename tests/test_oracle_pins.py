@@ -152,6 +152,15 @@ def test_route_forced_by_bias_and_gates_ignore_bias():
     np.testing.assert_allclose(g2[0], [0.4, 0.6], rtol=1e-14)
 
 
+def test_gates_for_a_given_selection():
+    # sigma(log 3) = 3/4, sigma(0) = 1/2: selection [4, 0] -> 0.6, 0.4 whatever the bias says
+    z = np.zeros((1, 6))
+    z[0, 4] = np.log(3.0)
+    np.testing.assert_allclose(O.gates_for(z, np.array([[4, 0]])), [[0.6, 0.4]], rtol=1e-14)
+    np.testing.assert_allclose(O.gates_for(z, np.array([[0, 4]])), [[0.4, 0.6]], rtol=1e-14)
+    np.testing.assert_allclose(O.gates_for(z, np.array([[1, 2, 3]])), [[1 / 3] * 3], rtol=1e-15)
+
+
 def test_route_invariant_to_common_bias_shift():
     rng = np.random.default_rng(4)
     T, E, k = 50, 32, 4
