@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""MoE-layer forward benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--also NAME,...] [--graph]
+
+A step is one full layer call (router GEMM, top-k, dispatch, expert GEMMs / weight streaming,
+shared expert, combine) over one batch of seeded synthetic tokens already resident in HBM.
+Prints one JSON line: tokens/s, the dominant kernel's roofline fraction (HIP events around that
+kernel's launches during the timed region, against algorithmic bytes or flops), and the
+double-precision oracle timed on a bounded token sample on the host as the CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s, Nano shape (T=64 decode, T=8192 prefill); % roofline"
+PEAK_HBM = 8.0e12            # B/s, MI355X HBM3E
+PEAK_MFMA = {"bf16": 2.5e15, "fp8": 5.0e15, "f32": 157.3e12}   # dense FLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="nano_decode_bf16")
+    ap.add_argument("--also", default="nano_prefill_bf16",
+                    help="comma-separated extra workloads reported under 'also' ('' for none)")
+    ap.add_argument("--path", default="auto", choices=["auto", "grouped", "stream"])
+    ap.add_argument("--graph", action="store_true", help="replay the step as a captured graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0: auto)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run one device copy of MIB MiB (a known-size reference for "
+                         "hardware byte counters)")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ algorithmic work per launch
+
+def work_of(name, cfg, counts, stream=False):
+    """(flops, bytes) one launch of trace span `name` must do for layer `cfg`; expert weights of
+    the touched experts counted once, activations counted once in and once out."""
+    T, H, E, k, I, Is, L = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared, cfg.latent
+    D, P = cfg.D, cfg.T * cfg.k
+    ea = 4 if cfg.act_dtype == "f32" else 2
+    ew = {"f32": 4, "bf16": 2, "e4m3": 1}[cfg.expert_dtype]
+    touched = int(np.count_nonzero(counts))
+    role = name.split(":")[1]
+    if role == "router":
+        return 2 * T * E * H, T * H * ea + E * H * ea + T * E * 4
+    if role == "up":       # stream: routed up (+ shared up)
+        f = 2 * P * I * D + (2 * T * Is * H if Is and not L else 0)
+        b = touched * I * D * ew + T * D * ea + P * I * 2
+        if Is and not L:
+            b += Is * H * ea + T * Is * 2
+        return f, b
+    if role == "down":     # stream: routed down (+ shared down), fp32 outputs
+        f = 2 * P * D * I + (2 * T * H * Is if Is and not L else 0)
+        b = touched * D * I * ew + P * I * 2 + P * D * 4
+        if Is and not L:
+            b += H * Is * ea + T * Is * 2 + T * H * 4
+        return f, b
+    if role == "routed_up":
+        scales = touched * I * 4 if ew == 1 else 0
+        return 2 * P * I * D, touched * I * D * ew + scales + T * D * (1 if ew == 1 else ea) + P * I * 2
+    if role == "routed_down":
+        scales = touched * D * 4 if ew == 1 else 0
+        return 2 * P * D * I, touched * D * I * ew + scales + P * I * 2 + P * D * ea
+    if role == "shared_up":
+        return 2 * T * Is * H, Is * H * ea + T * H * ea + T * Is * ea
+    if role == "shared_down":
+        return 2 * T * H * Is, H * Is * ea + T * Is * ea + T * H * 4
+    if role == "latent_in":
+        return 2 * T * L * H, L * H * ea + T * H * ea + T * L * ea
+    if role == "latent_out":
+        f = 2 * T * H * L + (2 * T * H * Is if Is else 0)
+        return f, H * L * ea + T * L * ea + T * H * ea + (H * Is * ea + T * Is * ea if Is else 0)
+    if role in ("y", "z"):
+        yb = 4 if stream else ea
+        s_in = T * H * 4 if (Is and not L and role == "y") else 0
+        return 2 * P * D, P * D * yb + s_in + T * D * ea
+    if role == "x":
+        return 0, T * D * ea + T * D
+    return 0, 0
+
+
+def kernel_of(span):
+    return span.split(":")[0]
+
+
+def mfma_dtype(kernel, cfg):
+    if "fp8" in kernel:
+        return "fp8"
+    return "f32" if cfg.act_dtype == "f32" else "bf16"
+
+
+# ------------------------------------------------------------------ one workload
+
+def prepare(name, moe, mi, torch, path, shared=None):
+    cfg = mi.CONFIGS[name]
+    if shared is not None and shared["cfg"].H == cfg.H and shared["cfg"].E == cfg.E and \
+            shared["cfg"].I == cfg.I and shared["cfg"].expert_dtype == cfg.expert_dtype and \
+            shared["cfg"].I_shared == cfg.I_shared and not cfg.latent:
+        inp = mi.make_layer(cfg, 0, tensors={"x", "b"})       # same seeded weights: reuse them
+        dev = dict(shared["dev"])
+        dev.update(moe.to_device(inp))
+        inp = dict(shared["inp"], **{k_: v for k_, v in inp.items()})
+    else:
+        inp = mi.make_layer(cfg, 0)
+        dev = moe.to_device(inp)
+    rt = moe.alloc_routing(cfg.T, cfg.E, cfg.k, "cuda")
+    layer = moe.layer_from(dev, cfg.k, path=path, routing=rt)
+    return dict(cfg=cfg, inp=inp, dev=dev, rt=rt, layer=layer)
+
+
+def measure(w, moe, torch, steps, warmup, graph):
+    cfg, layer = w["cfg"], w["layer"]
+    stream = torch.cuda.current_stream()
+    for _ in range(max(warmup, 1)):
+        layer()
+    torch.cuda.synchronize()
+    counts = w["rt"]["counts"].cpu().numpy()
+
+    # traced pass over a few steps: per-span durations, to find the dominant kernel
+    spans_per_step = 16
+    moe.binding.trace_enable(4 * spans_per_step)
+    for _ in range(3):
+        layer()
+    torch.cuda.synchronize()
+    recs = moe.binding.trace_records()
+    moe.binding.trace_disable()
+    per_kernel = {}
+    for n, ms in recs:
+        per_kernel.setdefault(kernel_of(n), 0.0)
+        per_kernel[kernel_of(n)] += ms
+    dominant = max(per_kernel, key=per_kernel.get)
+    dispatch_launch = None
+    runner = layer
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            layer()                                 # warm the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            layer()
+        torch.cuda.synchronize()
+        runner = g.replay
+        for _ in range(max(warmup, 1)):
+            runner()
+        torch.cuda.synchronize()
+
+    # timed region: K steps; events bracket the dominant kernel's launches (eager mode)
+    if not graph:
+        moe.binding.trace_enable(steps * 4, dominant + ":")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        runner()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    if not graph:
+        krec = moe.binding.trace_records()
+        moe.binding.trace_disable()
+    else:
+        # graph replays cannot carry the event records: time the kernel in an eager pass
+        moe.binding.trace_enable(steps * 4, dominant + ":")
+        for _ in range(steps):
+            layer()
+        torch.cuda.synchronize()
+        krec = moe.binding.trace_records()
+        moe.binding.trace_disable()
+    ms_step = elapsed * 1e3 / steps
+    stream_path = any(kernel_of(n) == "stream" for n, _ in recs)
+    flops = sum(work_of(n, cfg, counts, stream_path)[0] for n, _ in krec)
+    bts = sum(work_of(n, cfg, counts, stream_path)[1] for n, _ in krec)
+    kms = sum(ms for _, ms in krec)
+    nlaunch = len(krec)
+    dt = mfma_dtype(dominant, cfg)
+    ridge = PEAK_MFMA[dt] / PEAK_HBM
+    ai = flops / max(bts, 1)
+    if ai < ridge:
+        bound, achieved, peak, unit = "hbm", bts / (kms * 1e-3) / 1e9, PEAK_HBM / 1e9, "GB/s"
+    else:
+        bound, achieved = "mfma", flops / (kms * 1e-3) / 1e12
+        peak, unit = PEAK_MFMA[dt] / 1e12, "TFLOP/s"
+    roof = dict(bound=bound, achieved=round(achieved, 1), peak=peak, unit=unit,
+                frac=round(achieved / peak, 4), traffic=None, kernel=dominant,
+                launches=nlaunch, avg_launch_us=round(kms * 1e3 / max(nlaunch, 1), 2),
+                algorithmic_flops_per_launch=int(flops / max(nlaunch, 1)),
+                algorithmic_bytes_per_launch=int(bts / max(nlaunch, 1)))
+    breakdown = {k_: round(v * 1e3 / 3, 2) for k_, v in sorted(per_kernel.items(),
+                                                              key=lambda kv: -kv[1])}
+    return dict(ms_per_step=ms_step, tokens_per_s=cfg.T / (ms_step * 1e-3), roofline=roof,
+                kernel_us_per_step=breakdown, touched_experts=int(np.count_nonzero(counts)))
+
+
+def cpu_baseline(w, n_tokens):
+    from oracle import oracle as O
+    cfg, inp = w["cfg"], w["inp"]
+    toks = np.linspace(0, cfg.T - 1, n_tokens).astype(np.int32)
+    O.build()
+    t0 = time.perf_counter()
+    O.forward(inp, toks)
+    dt = time.perf_counter() - t0
+    return dict(value=round(n_tokens / dt, 3), unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{n_tokens} of the {cfg.T} tokens of {cfg.name} (router over all E, "
+                       f"k experts and the shared expert per token), double precision, one "
+                       f"thread, {dt:.1f} s")
+
+
+def describe(cfg):
+    return dict(workload=cfg.name, description=cfg.description, T=cfg.T, H=cfg.H, E=cfg.E,
+                k=cfg.k, I=cfg.I, I_shared=cfg.I_shared, latent=cfg.latent,
+                act_dtype=cfg.act_dtype, expert_dtype=cfg.expert_dtype)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import moe_inputs as mi
+    import sparse_moe_layer_05_amd as moe
+
+    torch.cuda.set_device(0)
+    moe.lib()
+    main_w = prepare(args.config, moe, mi, torch, args.path)
+    res = measure(main_w, moe, torch, args.steps, args.warmup, args.graph)
+    cfg = main_w["cfg"]
+    out = {
+        "metric": METRIC, "value": round(res["tokens_per_s"], 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "e4m3+bf16" if cfg.expert_dtype == "e4m3" else cfg.act_dtype,
+        "data": "synthetic", "config": describe(cfg), "roofline": res["roofline"],
+    }
+    extra = {}
+    for name in [n for n in args.also.split(",") if n and n != args.config]:
+        w = prepare(name, moe, mi, torch, args.path, shared=main_w)
+        r = measure(w, moe, torch, args.steps, args.warmup, args.graph)
+        extra[name] = dict(tokens_per_s=round(r["tokens_per_s"], 1),
+                           ms_per_step=round(r["ms_per_step"], 4), roofline=r["roofline"],
+                           kernel_us_per_step=r["kernel_us_per_step"])
+        del w
+        torch.cuda.empty_cache()
+    out["kernel_us_per_step"] = res["kernel_us_per_step"]
+    out["touched_experts"] = res["touched_experts"]
+    if extra:
+        out["also"] = extra
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = n
+        del src, dst
+    if not args.no_cpu_baseline:
+        n = args.cpu_tokens or max(4, min(cfg.T, int(12.0 / per_token_seconds(cfg))))
+        out["cpu_baseline"] = cpu_baseline(main_w, n)
+    print(json.dumps(out), flush=True)
+
+
+def per_token_seconds(cfg):
+    """Rough oracle cost per token (for a ~12 s CPU sample): ~4 ns per multiply-add."""
+    D = cfg.D
+    macs = cfg.E * cfg.H + cfg.k * 2 * cfg.I * D + 2 * cfg.I_shared * cfg.H
+    if cfg.latent:
+        macs += 2 * cfg.latent * cfg.H
+    return macs * 4e-9
+
+
+if __name__ == "__main__":
+    main()

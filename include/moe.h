@@ -142,6 +142,18 @@ int32_t moe_dispatch(const int32_t *idx, int32_t T, int32_t E, int32_t k, int32_
 /* Static text for a status code. */
 const char *moe_status_str(int32_t code);
 
+/* ---- Diagnostics: per-launch timing with HIP events (process-wide; not for concurrent calls).
+ * moe_trace_enable(capacity, filter) creates 2*capacity events up front (its only allocation;
+ * capacity 0 disables tracing and destroys them). While enabled, every kernel launch of a layer
+ * call whose trace name starts with `filter` (NULL or "" = all) is bracketed by two events
+ * recorded on the call's stream, until `capacity` launches are recorded. Trace names are
+ * "<kernel>:<role>", e.g. "stream:up", "gemm_bf16_sqrelu:routed_up", "dispatch:all".
+ * After synchronising the stream, moe_trace_read(i, name, ms) returns record i. */
+int32_t moe_trace_enable(int32_t capacity, const char *filter);
+int32_t moe_trace_count(void);
+int32_t moe_trace_read(int32_t i, const char **name, float *ms);
+void moe_trace_reset(void);
+
 #ifdef __cplusplus
 }
 #endif

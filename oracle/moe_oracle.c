@@ -246,9 +246,10 @@ int orc_dispatch(const int32_t *idx, int32_t T, int32_t E, int32_t k, int32_t *c
 
 /* ------------------------------------------------------------------ fp8 activation emulation */
 
-/* Per-row e4m3 quantisation of an activation row as the fp8 path performs it: scale =
- * fp32(amax / 448) (1 for an all-zero row), code = e4m3(fp32(v / scale)), value = code * scale.
- * Replaces v in place with the dequantised value. Used only in the emulation mode. */
+/* Per-row e4m3 quantisation of an activation row as the fp8 path performs it: the row's scale is
+ * fp32(amax / 448) (1 for an all-zero row); codes are e4m3(fp32(v * fp32(448 / amax))), i.e. the
+ * row is multiplied by the rounded reciprocal of the scale; value = code * scale. Replaces v in
+ * place with the dequantised value. Used only in the emulation mode. */
 static void quant_row_e4m3(double *v, int64_t n) {
   float amax = 0.0f;
   for (int64_t i = 0; i < n; ++i) {
@@ -256,8 +257,9 @@ static void quant_row_e4m3(double *v, int64_t n) {
     if (a > amax) amax = a;
   }
   volatile float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+  volatile float inv = amax > 0.0f ? 448.0f / amax : 1.0f;
   for (int64_t i = 0; i < n; ++i) {
-    volatile float q = (float)v[i] / scale;
+    volatile float q = (float)v[i] * inv;
     v[i] = orc_e4m3_to_f64(orc_f64_to_e4m3((double)q)) * (double)scale;
   }
 }

@@ -20,7 +20,8 @@ PATH_AUTO, PATH_GROUPED, PATH_STREAM, ROUTING_GIVEN = 0, 1, 2, 4
 _PATHS = {"auto": PATH_AUTO, "grouped": PATH_GROUPED, "stream": PATH_STREAM}
 
 EXPORTS = ("moe_workspace_size", "moe_layer_forward", "latent_moe_forward", "moe_route",
-           "moe_dispatch_workspace_size", "moe_dispatch", "moe_status_str")
+           "moe_dispatch_workspace_size", "moe_dispatch", "moe_status_str", "moe_trace_enable",
+           "moe_trace_count", "moe_trace_read", "moe_trace_reset")
 
 
 class MoeDesc(C.Structure):
@@ -67,10 +68,14 @@ def lib() -> C.CDLL:
             L.moe_dispatch_workspace_size.argtypes = [i32, i32, i32, C.POINTER(sz)]
             L.moe_dispatch.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
             L.moe_status_str.argtypes = [i32]
-            L.moe_status_str.restype = C.c_char_p
+            L.moe_trace_enable.argtypes = [i32, C.c_char_p]
+            L.moe_trace_count.argtypes = []
+            L.moe_trace_read.argtypes = [i32, C.POINTER(C.c_char_p), C.POINTER(C.c_float)]
+            L.moe_trace_reset.argtypes = []
             for name in EXPORTS:
-                if name != "moe_status_str":
-                    getattr(L, name).restype = C.c_int32
+                getattr(L, name).restype = C.c_int32
+            L.moe_status_str.restype = C.c_char_p
+            L.moe_trace_reset.restype = None
             _lib = L
     return _lib
 
@@ -208,6 +213,29 @@ def dispatch(idx, E, stream=None):
                             n.value, _stream(stream))
     _check(rc, "moe_dispatch")
     return counts, offsets, perm, pos
+
+
+def trace_enable(capacity: int, prefix: str = "") -> None:
+    """Record HIP events around every launch whose trace name starts with `prefix`."""
+    _check(lib().moe_trace_enable(capacity, prefix.encode()), "moe_trace_enable")
+
+
+def trace_disable() -> None:
+    _check(lib().moe_trace_enable(0, None), "moe_trace_enable")
+
+
+def trace_reset() -> None:
+    lib().moe_trace_reset()
+
+
+def trace_records() -> list:
+    """[(name, ms)] of the recorded launches (synchronise the stream first)."""
+    out = []
+    for i in range(lib().moe_trace_count()):
+        name, ms = C.c_char_p(), C.c_float()
+        _check(lib().moe_trace_read(i, C.byref(name), C.byref(ms)), "moe_trace_read")
+        out.append((name.value.decode(), ms.value))
+    return out
 
 
 def to_device(inp: dict, device="cuda") -> dict:

@@ -2,23 +2,31 @@
 // projections (grouped, A rows gathered through the dispatch permutation), the shared expert,
 // and the LatentMoE projections.
 //
-// bf16 / fp8 tiles run on the matrix cores: v_mfma_f32_32x32x16_bf16 and
-// v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3, unit scales). A workgroup of 4 waves owns a BM x BN
-// output tile, each wave a (BM/2) x (BN/2) quarter. Every K-step stages a 128-byte slab of each
-// A and B row in LDS (64 bf16 or 128 e4m3 values), double buffered, with the 16-byte chunk index
-// XOR-swizzled by (row / 2) % 8 so that fragment reads of 16 consecutive rows hit 16 distinct
-// 16-byte bank groups. fp32 layers use a vector-ALU variant with the same parameters.
+// bf16 / e4m3 tiles run on the matrix cores (v_mfma_f32_32x32x16_bf16,
+// v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales). A workgroup of WGM x WGN waves owns a
+// BM x BN output tile. Each K-step stages a 128-byte slab of every A and B row in LDS (64 bf16
+// or 128 e4m3 values). Slabs are filled
+// by global_load_lds_dwordx4 (global memory straight to LDS, no register staging): one
+// instruction fills 8 rows x 128 bytes, lane l landing at byte 16*l. The 16-byte chunk order
+// inside a row is XOR-swizzled by (row / 2) % 8 by choosing which global chunk each lane
+// fetches, so the fragment reads of 16 consecutive rows touch 16 distinct 16-byte bank groups.
+// In a final partial K-step, lanes whose chunk lies beyond K fetch an in-row chunk and their
+// slots are zeroed once the stage has landed. NS stages are in flight: K-step ks + NS - 1 is
+// loaded while K-step ks is multiplied.
+// The epilogue stages each wave's accumulators through LDS in 16-row strips so that every lane
+// finishes 8 consecutive columns of a row with 16-byte loads and stores.
+// fp32 layers use a vector-ALU kernel with the same parameters.
 #include "common.hpp"
 #include "gemm.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kSlab = 128;  // bytes of one row per K-step
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kSlab + ((chunk ^ ((row >> 1) & 7)) << 4);
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int slot(int row, int chunk) {
+  return row * kSlab + ((chunk ^ swz(row)) << 4);
 }
 
 template <Elt E> struct EltBytes { static constexpr int v = E == Elt::F32 ? 4 : (E == Elt::BF16 ? 2 : 1); };
@@ -43,8 +51,7 @@ __device__ __forceinline__ bool tile_of(const GemmParams& p, int& g, int& row0, 
     const int local = L - p.mt_start[g] * nN;
     n0 = (local / mt_g) * BN;          // a group's tiles: N-major, M fastest (weight panel reuse)
     const int mt = local % mt_g;
-    const int gr0 = p.offs[g];
-    row0 = gr0 + mt * BM;
+    row0 = p.offs[g] + mt * BM;
     rows = min(BM, p.offs[g + 1] - row0);
   } else {
     const int nM = cdiv(p.M, BM);
@@ -62,134 +69,122 @@ __device__ __forceinline__ bool tile_of(const GemmParams& p, int& g, int& row0, 
   return rows > 0;
 }
 
+__device__ __forceinline__ void unpack8(const uint4 q, float* v) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFF);
+    v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+  }
+}
+
 // -------------------------------------------------------------------------------------------
 // Matrix-core kernel (bf16 or e4m3 operands, fp32 accumulation).
 // -------------------------------------------------------------------------------------------
-template <int BM, int BN, Elt AB, Elt OUT, Epi EPI, bool AQ, Elt YT>
-__global__ __launch_bounds__(kThreads) void gemm_mfma(GemmParams p) {
+template <int BM, int BN, int WGM, int WGN, int NS, Elt AB, Elt OUT, Epi EPI>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
   static_assert(AB == Elt::BF16 || AB == Elt::FP8, "matrix-core path");
-  static_assert(!AQ || AB == Elt::FP8, "quantise-on-load feeds e4m3 tiles");
+  static_assert(NS >= 2, "at least double buffering");
+  if (p.ksplit > 1) {  // this workgroup's K slice (dense Store launches)
+    const int k0 = blockIdx.y * p.kchunk;
+    p.K = min(p.kchunk, p.K - k0);
+    p.A = (const uint8_t*)p.A + (int64_t)k0 * EltBytes<AB>::v;
+    p.B = (const uint8_t*)p.B + (int64_t)k0 * EltBytes<AB>::v;
+    p.C = (uint8_t*)p.C + (int64_t)blockIdx.y * p.M * p.ldc * EltBytes<OUT>::v;
+  }
+  constexpr int NW = WGM * WGN;
   constexpr int EB = EltBytes<AB>::v;
-  constexpr int WM = BM / 2, WN = BN / 2, MB = WM / 32, NB = WN / 32;
-  constexpr int A_CH = BM * 8 / kThreads;      // 16-byte chunks per thread per K-step (A)
-  constexpr int AQ_CH = BM * 16 / kThreads;    // bf16 source chunks per thread (quantised A)
-  constexpr int B_CH = BN * 8 / kThreads;
-  static_assert(A_CH >= 1 && B_CH >= 1 && MB >= 1 && NB >= 1, "tile too small");
+  constexpr int WM = BM / WGM, WN = BN / WGN, MB = WM / 32, NB = WN / 32;
+  constexpr int A_GRP = BM / (8 * NW), B_GRP = BN / (8 * NW);  // 1-KB groups per wave
+  constexpr int STAGE = (BM + BN) * kSlab;
+  constexpr int EPW = WN + 4;                                   // epilogue strip row (floats)
+  static_assert(A_GRP >= 1 && B_GRP >= 1 && MB >= 1 && NB >= 1, "tile too small");
+  static_assert(NW * 16 * EPW * 4 <= NS * STAGE, "epilogue strips must fit in the stages");
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (BM + BN) * kSlab];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
 
   int g, row0, rows, n0;
   if (!tile_of<BM, BN>(p, g, row0, rows, n0)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int lrow = lane >> 3, lpos = lane & 7;
 
-  // Source rows of this thread's A chunks (clamped into the tile; extra rows are never stored).
-  const uint8_t* a_row[AQ ? AQ_CH : A_CH];
-  float a_sc[AQ ? AQ_CH : 1];
-  if constexpr (!AQ) {
+  // Per-lane global sources, as 32-bit byte offsets from wave-uniform bases. Lane (lrow, lpos)
+  // of 1-KB group q fills LDS row q*8 + lrow, slot lpos, which holds global chunk lpos ^ swz(row).
+  const uint8_t* abase = (const uint8_t*)p.A;
+  const uint8_t* bbase = (const uint8_t*)p.B + (int64_t)g * p.b_gstride * EB;
+  uint32_t oa[A_GRP], ob[B_GRP];
+  // This lane's chunk byte offset. Its rows (wave + NW*i)*8 + lrow differ by multiples of 16
+  // across groups (NW is even) and swz has period 16, so one offset serves every group.
+  static_assert(NW % 2 == 0, "an even wave count keeps the swizzle constant across groups");
+  const int cofs = (lpos ^ swz(wave * 8 + lrow)) << 4;
+  auto set_sources = [&](bool seg2) {
+    if (seg2) {
+      abase = (const uint8_t*)p.A2;
+      bbase = (const uint8_t*)p.B2;
+    }
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      const int r = (tid >> 3) + i * (kThreads / 8);
+    for (int i = 0; i < A_GRP; ++i) {
+      const int r = (wave + NW * i) * 8 + lrow;
       const int rr = r < rows ? r : 0;
-      const int64_t src = p.a_gather ? p.a_gather[row0 + rr] : (int64_t)(row0 + rr);
-      a_row[i] = (const uint8_t*)p.A + src * p.lda * EB;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < AQ_CH; ++i) {
-      const int r = (tid >> 4) + i * (kThreads / 16);
-      const int rr = r < rows ? r : 0;
-      a_row[i] = (const uint8_t*)p.A + (int64_t)(row0 + rr) * p.lda * 2;
-      const float amax = p.row_amax[row0 + rr];
-      a_sc[i] = amax > 0.f ? amax / 448.f : 1.f;   // the per-row scale; codes = h / scale
-    }
-  }
-  const uint8_t* b_row[B_CH];
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int n = n0 + (tid >> 3) + i * (kThreads / 8);
-    const int nn = n < p.N ? n : p.N - 1;
-    b_row[i] = (const uint8_t*)p.B + ((int64_t)g * p.b_gstride + (int64_t)nn * p.ldb) * EB;
-  }
-
-  const int kb1 = p.K * EB;                         // bytes of K in segment 1
-  const int nk1 = cdiv(kb1, kSlab);
-  const int kb2 = p.K2 * EB;
-  const int nk = nk1 + cdiv(kb2, kSlab);
-
-  uint4 ra[AQ ? AQ_CH : A_CH], rb[B_CH];
-
-  auto load = [&](int ks) {
-    const bool seg2 = ks >= nk1;
-    const int kb = (seg2 ? ks - nk1 : ks) * kSlab;
-    const int klim = seg2 ? kb2 : kb1;
-    if constexpr (!AQ) {
-#pragma unroll
-      for (int i = 0; i < A_CH; ++i) {
-        const int off = kb + ((tid & 7) << 4);
-        const uint8_t* base = a_row[i];
-        if (seg2) {
-          const int r = (tid >> 3) + i * (kThreads / 8);
-          const int rr = r < rows ? r : 0;
-          base = (const uint8_t*)p.A2 + (int64_t)(row0 + rr) * p.lda2 * EB;
-        }
-        ra[i] = off < klim ? *(const uint4*)(base + off) : make_uint4(0, 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < AQ_CH; ++i) {
-        const int off = 2 * kb + ((tid & 15) << 4);  // bf16 source bytes
-        ra[i] = off < 2 * klim ? *(const uint4*)(a_row[i] + off) : make_uint4(0, 0, 0, 0);
-      }
+      int64_t src = row0 + rr;
+      if (!seg2 && p.a_gather) src = p.a_gather[row0 + rr];
+      oa[i] = (uint32_t)(src * (seg2 ? p.lda2 : p.lda) * EB);
     }
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      const int off = kb + ((tid & 7) << 4);
-      const uint8_t* base = b_row[i];
-      if (seg2) {
-        const int n = n0 + (tid >> 3) + i * (kThreads / 8);
-        const int nn = n < p.N ? n : p.N - 1;
-        base = (const uint8_t*)p.B2 + (int64_t)nn * p.ldb2 * EB;
-      }
-      rb[i] = off < klim ? *(const uint4*)(base + off) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < B_GRP; ++i) {
+      const int r = (wave + NW * i) * 8 + lrow;
+      const int n = n0 + r < p.N ? n0 + r : p.N - 1;
+      ob[i] = (uint32_t)((int64_t)n * (seg2 ? p.ldb2 : p.ldb) * EB);
     }
   };
 
-  auto store = [&](int buf) {
-    uint8_t* As = smem + buf * (BM + BN) * kSlab;
-    uint8_t* Bs = As + BM * kSlab;
-    if constexpr (!AQ) {
+  const int kb1 = p.K * EB, kb2 = p.K2 * EB;   // K bytes per segment
+  const int nk1 = cdiv(kb1, kSlab);
+  const int nk = nk1 + cdiv(kb2, kSlab);
+  // Bytes of K-step ks that lie inside K when the step is partial, else 0.
+  auto tail_of = [&](int ks) {
+    const bool seg2 = ks >= nk1;
+    const int kb = (seg2 ? ks - nk1 : ks) * kSlab;
+    const int klim = seg2 ? kb2 : kb1;
+    return kb + kSlab <= klim ? 0 : klim - kb;
+  };
+
+  // Issue the loads of K-step ks into stage `st`, straight to LDS. Lanes whose chunk lies beyond
+  // K fetch chunk 0 of the same row instead; fix_tail() zeroes those slots once they landed.
+  auto issue = [&](int ks, uint8_t* st) {
+    const bool seg2 = ks >= nk1;
+    if (ks == nk1 && nk1 > 0 && kb2 > 0) set_sources(true);
+    const int kb = (seg2 ? ks - nk1 : ks) * kSlab;
+    const int klim = seg2 ? kb2 : kb1;
+    const int cuse = (kb + cofs < klim) ? cofs : 0;
 #pragma unroll
-      for (int i = 0; i < A_CH; ++i) {
-        const int r = (tid >> 3) + i * (kThreads / 8);
-        *(uint4*)(As + swz(r, tid & 7)) = ra[i];
-      }
-    } else {
+    for (int i = 0; i < A_GRP; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(abase + oa[i] + kb + cuse),
+          (__attribute__((address_space(3))) void*)(st + (wave + NW * i) * 1024), 16, 0, 0);
+    uint8_t* sb = st + BM * kSlab;
 #pragma unroll
-      for (int i = 0; i < AQ_CH; ++i) {
-        const int r = (tid >> 4) + i * (kThreads / 16);
-        const int q = tid & 15;  // bf16 chunk: elements 8q .. 8q+7 -> fp8 bytes 8q .. 8q+7
-        const float s = a_sc[i];
-        const uint4 v = ra[i];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        uint32_t c[2];
+    for (int i = 0; i < B_GRP; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(bbase + ob[i] + kb + cuse),
+          (__attribute__((address_space(3))) void*)(sb + (wave + NW * i) * 1024), 16, 0, 0);
+  };
+
+  // Zero the slots of a partial K-step that lie beyond K (after the stage has landed).
+  auto fix_tail = [&](int ks, uint8_t* st) {
+    const int tl = tail_of(ks);
+    if (tl == 0) return;  // uniform across the workgroup
+    if (cofs >= tl) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const float f0 = bf16_bits_to_f32(w[2 * h] & 0xFFFF) / s;
-          const float f1 = bf16_bits_to_f32(w[2 * h] >> 16) / s;
-          const float f2 = bf16_bits_to_f32(w[2 * h + 1] & 0xFFFF) / s;
-          const float f3 = bf16_bits_to_f32(w[2 * h + 1] >> 16) / s;
-          c[h] = cvt_fp8x2(f0, f1) | (cvt_fp8x2(f2, f3) << 16);
-        }
-        *(uint2*)(As + swz(r, q >> 1) + ((q & 1) << 3)) = make_uint2(c[0], c[1]);
-      }
+      for (int i = 0; i < A_GRP; ++i)
+        *(uint4*)(st + (wave + NW * i) * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < B_GRP; ++i)
+        *(uint4*)(st + BM * kSlab + (wave + NW * i) * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      const int r = (tid >> 3) + i * (kThreads / 8);
-      *(uint4*)(Bs + swz(r, tid & 7)) = rb[i];
-    }
+    __syncthreads();
   };
 
   f32x16_t acc[MB][NB];
@@ -200,124 +195,151 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma(GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto compute = [&](int buf) {
-    const uint8_t* As = smem + buf * (BM + BN) * kSlab;
+  // One K-step on the matrix cores. Fragments of k-sub s+1 are read from LDS while the MFMAs
+  // of k-sub s issue; scheduling fences keep the compiler from hoisting further reads (which
+  // would only add registers).
+  auto compute = [&](const uint8_t* As) {
     const uint8_t* Bs = As + BM * kSlab;
     if constexpr (AB == Elt::BF16) {
+      bf16x8_t a[2][MB], b[2][NB];
+      auto rd = [&](int s, int buf) {
+        const int ch = 2 * s + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < MB; ++i) a[buf][i] = *(const bf16x8_t*)(As + slot(wm * WM + i * 32 + (lane & 31), ch));
+#pragma unroll
+        for (int j = 0; j < NB; ++j) b[buf][j] = *(const bf16x8_t*)(Bs + slot(wn * WN + j * 32 + (lane & 31), ch));
+      };
+      rd(0, 0);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int ch = 2 * s + (lane >> 5);
-        bf16x8_t a[MB], b[NB];
-#pragma unroll
-        for (int i = 0; i < MB; ++i) a[i] = *(const bf16x8_t*)(As + swz(wm * WM + i * 32 + (lane & 31), ch));
-#pragma unroll
-        for (int j = 0; j < NB; ++j) b[j] = *(const bf16x8_t*)(Bs + swz(wn * WN + j * 32 + (lane & 31), ch));
+        if (s < 3) rd(s + 1, (s + 1) & 1);
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
           for (int j = 0; j < NB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      i32x8_t a[2][MB], b[2][NB];
+      auto rd = [&](int s, int buf) {
         const int ch = 4 * s + 2 * (lane >> 5);
-        i32x8_t a[MB], b[NB];
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
           const int r = wm * WM + i * 32 + (lane & 31);
-          const i32x4_t lo = *(const i32x4_t*)(As + swz(r, ch));
-          const i32x4_t hi = *(const i32x4_t*)(As + swz(r, ch + 1));
-          a[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          const i32x4_t lo = *(const i32x4_t*)(As + slot(r, ch));
+          const i32x4_t hi = *(const i32x4_t*)(As + slot(r, ch + 1));
+          a[buf][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           const int r = wn * WN + j * 32 + (lane & 31);
-          const i32x4_t lo = *(const i32x4_t*)(Bs + swz(r, ch));
-          const i32x4_t hi = *(const i32x4_t*)(Bs + swz(r, ch + 1));
-          b[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          const i32x4_t lo = *(const i32x4_t*)(Bs + slot(r, ch));
+          const i32x4_t hi = *(const i32x4_t*)(Bs + slot(r, ch + 1));
+          b[buf][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
+      };
+      rd(0, 0);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (s < 1) rd(s + 1, (s + 1) & 1);
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
           for (int j = 0; j < NB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j],
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[s & 1][i], b[s & 1][j], acc[i][j],
                                                                          0, 0, 0, 127, 0, 127);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
 
-  if (nk > 0) {
-    load(0);
-    store(0);
+  // Pipeline: K-step ks + NS - 1 is issued while K-step ks is computed. Before computing ks a
+  // wave waits until at most (stages issued after ks) x (loads per stage) of its own loads are
+  // still in flight, then the barrier makes every wave's slab visible and frees stage ks - 1.
+  constexpr int PER = A_GRP + B_GRP;
+  auto wait_ahead = [&](int ahead) {
+    // s_waitcnt vmcnt(ahead * PER), other counters untouched
+#define MOE_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)))
+    if constexpr (NS >= 4) { if (ahead >= 2) { MOE_VMCNT(2 * PER); return; } }
+    if constexpr (NS >= 3) { if (ahead >= 1) { MOE_VMCNT(PER); return; } }
+    MOE_VMCNT(0);
+#undef MOE_VMCNT
+  };
+  static_assert((NS - 2) * PER < 64, "vmcnt range");
+
+  set_sources(false);
+#pragma unroll
+  for (int q = 0; q < NS - 1; ++q)
+    if (q < nk) issue(q, smem + q * STAGE);
+  for (int ks = 0; ks < nk; ++ks) {
+    wait_ahead(min(NS - 2, nk - 1 - ks));
     __syncthreads();
-    for (int ks = 0; ks < nk; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < nk) load(ks + 1);
-      compute(cur);
-      if (ks + 1 < nk) store(cur ^ 1);
-      __syncthreads();
-    }
+    uint8_t* cur = smem + (ks % NS) * STAGE;
+    fix_tail(ks, cur);
+    if (ks + NS - 1 < nk) issue(ks + NS - 1, smem + ((ks + NS - 1) % NS) * STAGE);
+    compute(cur);
   }
+  __syncthreads();  // every wave is done with the stages: the epilogue reuses them
 
   // ---------------------------------------------------------------- epilogue
-  // acc[i][j][r] is C[wm*WM + i*32 + (r/4)*8 + (lane/32)*4 + r%4][wn*WN + j*32 + lane%32]
-  const int colL = lane & 31;
+  // acc[i][j][r] is C[wm*WM + i*32 + (r/4)*8 + (lane/32)*4 + r%4][wn*WN + j*32 + lane%32].
+  // Strip h of m-block i (rows 16h .. 16h+15, registers 8h .. 8h+7) goes through LDS; then lane
+  // l finishes items l, l + 64, ... where item = (row in strip) * (WN/8) + column group.
+  float* ep = (float*)smem + wave * 16 * EPW;
+  constexpr int CG = WN / 8;             // 8-column groups per strip row
+  constexpr int ITEMS = 16 * CG / 64;    // items per lane per strip
+  static_assert((16 * CG) % 64 == 0, "strip must split evenly over the wave");
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rl = wm * WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-      const bool rok = rl < rows;
-      const int row = row0 + (rok ? rl : 0);
-      float rs = 1.f;
-      if constexpr (AB == Elt::FP8) {
-        if constexpr (AQ) {
-          const float amax = p.row_amax[row];
-          rs = amax > 0.f ? amax / 448.f : 1.f;
-        } else {
-          const int64_t src = p.a_gather ? p.a_gather[row] : (int64_t)row;
-          rs = p.a_scale[src];
-        }
-      }
-      float rmax = 0.f;
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int n = n0 + wn * WN + j * 32 + colL;
-        const bool ok = rok && n < p.N;
-        float v = acc[i][j][r];
-        if constexpr (AB == Elt::FP8) v *= rs * p.b_scale[(int64_t)g * p.N + (n < p.N ? n : 0)];
-        if constexpr (EPI == Epi::SqRelu || EPI == Epi::SqReluAmax) v = sqrelu(v);
-        if constexpr (EPI == Epi::Combine) {
-          if (ok) {
-            for (int jj = 0; jj < p.topk; ++jj) {
-              const int64_t q = (int64_t)row * p.topk + jj;
-              const float gte = p.gates[q];
-              const int64_t yr = p.pos[q];
-              if (yr < 0) continue;  // dropped pair
-              float yv;
-              if constexpr (YT == Elt::BF16)
-                yv = bf16_bits_to_f32(((const uint16_t*)p.Y)[yr * p.ldy + n]);
-              else
-                yv = ((const float*)p.Y)[yr * p.ldy + n];
-              v += gte * yv;
-            }
-          }
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          const int r = 8 * h + rr;
+          const int srow = (rr >> 2) * 8 + (lane >> 5) * 4 + (rr & 3);
+          ep[srow * EPW + j * 32 + (lane & 31)] = acc[i][j][r];
         }
+#pragma unroll
+      for (int it = 0; it < ITEMS; ++it) {
+        const int item = it * 64 + lane;
+        const int srow = item / CG, cg = item % CG;
+        const int rl = wm * WM + i * 32 + h * 16 + srow;
+        const int col = n0 + wn * WN + cg * 8;
+        const bool ok = rl < rows && col < p.N;
+        const int row = row0 + (rl < rows ? rl : 0);
+        float v[8];
+        const float4 lo = *(const float4*)(ep + srow * EPW + cg * 8);
+        const float4 hi = *(const float4*)(ep + srow * EPW + cg * 8 + 4);
+        v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+        v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
         if (ok) {
+          if constexpr (AB == Elt::FP8) {
+            const int64_t src = p.a_gather ? p.a_gather[row] : (int64_t)row;
+            const float rs = p.a_scale[src];
+            const float* bs = p.b_scale + (int64_t)g * p.N + col;
+            const float4 s0 = *(const float4*)bs, s1 = *(const float4*)(bs + 4);
+            const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] *= rs * sc[q];
+          }
+          if constexpr (EPI == Epi::SqRelu) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = sqrelu(v[q]);
+          }
           if constexpr (OUT == Elt::BF16) {
-            const uint32_t hb = f32_to_bf16_bits(v);
-            ((uint16_t*)p.C)[(int64_t)row * p.ldc + n] = (uint16_t)hb;
-            if constexpr (EPI == Epi::SqReluAmax) rmax = fmaxf(rmax, bf16_bits_to_f32(hb));
+            uint32_t w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+            *(uint4*)((uint16_t*)p.C + (int64_t)row * p.ldc + col) = make_uint4(w[0], w[1], w[2], w[3]);
           } else {
-            ((float*)p.C)[(int64_t)row * p.ldc + n] = v;
+            float* o = (float*)p.C + (int64_t)row * p.ldc + col;
+            *(float4*)o = make_float4(v[0], v[1], v[2], v[3]);
+            *(float4*)(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
           }
         }
-      }
-      if constexpr (EPI == Epi::SqReluAmax) {
-#pragma unroll
-        for (int m = 1; m < 32; m <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, m, 32));
-        if (colL == 0 && rok) atomicMax((unsigned int*)&p.row_amax[row], __float_as_uint(rmax));
       }
     }
   }
@@ -327,7 +349,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma(GemmParams p) {
 // Vector-ALU kernel for fp32 layers: 64 x 64 tile, each thread a 4 x 4 block, K-steps of 16.
 // -------------------------------------------------------------------------------------------
 template <Epi EPI>
-__global__ __launch_bounds__(kThreads) void gemm_f32(GemmParams p) {
+__global__ __launch_bounds__(256) void gemm_f32(GemmParams p) {
   constexpr int BM = 64, BN = 64, BK = 16;
   __shared__ float As[BK][BM + 4];
   __shared__ float Bs[BK][BN + 4];
@@ -335,8 +357,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32(GemmParams p) {
   if (!tile_of<BM, BN>(p, g, row0, rows, n0)) return;
   const int tid = threadIdx.x;
   const int tr = tid / 16, tc = tid % 16;  // thread's 4 x 4 block: rows tr*4.., cols tc*4..
-  // loader: 64 rows x 16 k = 1024 values = 4 per thread; thread loads row lr, k lk..lk+3
-  const int lr = tid >> 2, lk = (tid & 3) * 4;
+  const int lr = tid >> 2, lk = (tid & 3) * 4;  // loader: row lr, k lk .. lk+3
   const int rr = lr < rows ? lr : 0;
   const int64_t asrc = p.a_gather ? p.a_gather[row0 + rr] : (int64_t)(row0 + rr);
   const int nn = n0 + lr < p.N ? n0 + lr : p.N - 1;
@@ -379,72 +400,72 @@ __global__ __launch_bounds__(kThreads) void gemm_f32(GemmParams p) {
       if (n >= p.N) continue;
       float v = acc[x][y];
       if constexpr (EPI == Epi::SqRelu) v = sqrelu(v);
-      if constexpr (EPI == Epi::Combine) {
-        for (int jj = 0; jj < p.topk; ++jj) {
-          const int64_t q = (int64_t)row * p.topk + jj;
-          const int64_t yr = p.pos[q];
-          if (yr < 0) continue;  // dropped pair
-          v += p.gates[q] * ((const float*)p.Y)[yr * p.ldy + n];
-        }
-      }
       ((float*)p.C)[(int64_t)row * p.ldc + n] = v;
     }
   }
 }
 
-template <int BM, int BN, Elt AB, Elt OUT, Epi EPI, bool AQ, Elt YT>
-hipError_t run_mfma(const GemmParams& p, int max_mtiles, hipStream_t s) {
-  const int tiles = max_mtiles * cdiv(p.N, BN);
-  const int grid = cdiv(tiles, kXcds) * kXcds;
+template <int BM, int BN, int WGM, int WGN, int NS, Elt AB, Elt OUT, Epi EPI>
+hipError_t run_mfma(const GemmParams& p, int mtiles, hipStream_t s) {
+  const int tiles = mtiles * cdiv(p.N, BN);
   if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_mfma<BM, BN, AB, OUT, EPI, AQ, YT>), dim3(grid), dim3(kThreads), 0, s, p);
+  const int grid = cdiv(tiles, kXcds) * kXcds;
+  hipLaunchKernelGGL((gemm_mfma<BM, BN, WGM, WGN, NS, AB, OUT, EPI>), dim3(grid, p.ksplit),
+                     dim3(64 * WGM * WGN), 0, s, p);
   return hipGetLastError();
 }
 
 template <Epi EPI>
-hipError_t run_f32(const GemmParams& p, int max_mtiles, hipStream_t s) {
-  const int tiles = max_mtiles * cdiv(p.N, 64);
-  const int grid = cdiv(tiles, kXcds) * kXcds;
+hipError_t run_f32(const GemmParams& p, int mtiles, hipStream_t s) {
+  const int tiles = mtiles * cdiv(p.N, 64);
   if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_f32<EPI>), dim3(grid), dim3(kThreads), 0, s, p);
+  const int grid = cdiv(tiles, kXcds) * kXcds;
+  hipLaunchKernelGGL((gemm_f32<EPI>), dim3(grid), dim3(256), 0, s, p);
   return hipGetLastError();
+}
+
+// Dense bf16 launch: 256 x 256 tiles on 8 waves when there are enough of them to fill the chip,
+// 128 x 128 tiles on 4 waves (two workgroups per CU) otherwise.
+template <Elt OUT, Epi EPI>
+hipError_t run_dense_bf16(const GemmParams& p, hipStream_t s) {
+  if (p.ksplit == 1 && cdiv(p.M, 256) * cdiv(p.N, 256) >= 192)
+    return run_mfma<256, 256, 2, 4, 2, Elt::BF16, OUT, EPI>(p, cdiv(p.M, 256), s);
+  return run_mfma<128, 128, 2, 2, 2, Elt::BF16, OUT, EPI>(p, cdiv(p.M, 128), s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const GemmKind& k, const GemmParams& p, int max_mtiles, hipStream_t s) {
-  constexpr int BM = kGroupBM;
-  // Dense launches (no group list) size their own M-tile count from M. Grouped fp32 launches
-  // use 64-row tiles, so their group list must have been built with bm = 64.
+  // Grouped launches (mt_start set) walk M-tiles of kGroupBM rows (64 for fp32 layers): the
+  // dispatch step built mt_start with that height.
+  const bool grouped = p.mt_start != nullptr;
   if (k.ab == Elt::F32) {
-    const int mt = p.mt_start ? max_mtiles : cdiv(p.M, 64);
+    const int mt = grouped ? max_mtiles : cdiv(p.M, 64);
     switch (k.epi) {
       case Epi::Store: return run_f32<Epi::Store>(p, mt, s);
       case Epi::SqRelu: return run_f32<Epi::SqRelu>(p, mt, s);
-      case Epi::Combine: return run_f32<Epi::Combine>(p, mt, s);
       default: return hipErrorInvalidValue;
     }
   }
-  const int mt = p.mt_start ? max_mtiles : cdiv(p.M, BM);
+  constexpr int GB = kGroupBM;
   if (k.ab == Elt::BF16) {
-    if (k.out == Elt::F32 && k.epi == Epi::Store)
-      return run_mfma<BM, 128, Elt::BF16, Elt::F32, Epi::Store, false, Elt::BF16>(p, mt, s);
-    if (k.out == Elt::BF16 && k.epi == Epi::Store)
-      return run_mfma<BM, 128, Elt::BF16, Elt::BF16, Epi::Store, false, Elt::BF16>(p, mt, s);
-    if (k.out == Elt::BF16 && k.epi == Epi::SqRelu)
-      return run_mfma<BM, 128, Elt::BF16, Elt::BF16, Epi::SqRelu, false, Elt::BF16>(p, mt, s);
-    if (k.out == Elt::BF16 && k.epi == Epi::Combine && k.y == Elt::BF16)
-      return run_mfma<BM, 128, Elt::BF16, Elt::BF16, Epi::Combine, false, Elt::BF16>(p, mt, s);
-    if (k.out == Elt::BF16 && k.epi == Epi::Combine && k.y == Elt::F32)
-      return run_mfma<BM, 128, Elt::BF16, Elt::BF16, Epi::Combine, false, Elt::F32>(p, mt, s);
+    if (grouped) {
+      if (k.out == Elt::BF16 && k.epi == Epi::SqRelu)
+        return run_mfma<GB, 256, 2, 4, 3, Elt::BF16, Elt::BF16, Epi::SqRelu>(p, max_mtiles, s);
+      if (k.out == Elt::BF16 && k.epi == Epi::Store)
+        return run_mfma<GB, 256, 2, 4, 3, Elt::BF16, Elt::BF16, Epi::Store>(p, max_mtiles, s);
+      return hipErrorInvalidValue;
+    }
+    if (k.out == Elt::F32 && k.epi == Epi::Store) return run_dense_bf16<Elt::F32, Epi::Store>(p, s);
+    if (k.out == Elt::BF16 && k.epi == Epi::Store) return run_dense_bf16<Elt::BF16, Epi::Store>(p, s);
+    if (k.out == Elt::BF16 && k.epi == Epi::SqRelu) return run_dense_bf16<Elt::BF16, Epi::SqRelu>(p, s);
     return hipErrorInvalidValue;
   }
-  if (k.ab == Elt::FP8) {
-    if (k.out == Elt::BF16 && k.epi == Epi::SqReluAmax && !p.a_quant)
-      return run_mfma<BM, 128, Elt::FP8, Elt::BF16, Epi::SqReluAmax, false, Elt::BF16>(p, mt, s);
-    if (k.out == Elt::BF16 && k.epi == Epi::Store && p.a_quant)
-      return run_mfma<BM, 128, Elt::FP8, Elt::BF16, Epi::Store, true, Elt::BF16>(p, mt, s);
-    return hipErrorInvalidValue;
+  if (k.ab == Elt::FP8 && grouped && k.out == Elt::BF16) {
+    if (k.epi == Epi::SqRelu)
+      return run_mfma<GB, 256, 2, 4, 3, Elt::FP8, Elt::BF16, Epi::SqRelu>(p, max_mtiles, s);
+    if (k.epi == Epi::Store)
+      return run_mfma<GB, 256, 2, 4, 3, Elt::FP8, Elt::BF16, Epi::Store>(p, max_mtiles, s);
   }
   return hipErrorInvalidValue;
 }

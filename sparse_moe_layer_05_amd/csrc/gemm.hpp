@@ -14,20 +14,16 @@ enum class Elt : int { F32 = 0, BF16 = 1, FP8 = 2 };
 
 enum class Epi : int {
   Store = 0,        // C = acc
-  SqRelu = 1,       // C = relu(acc)^2
-  SqReluAmax = 2,   // C = relu(acc)^2 (bf16) and row_amax[row] = max over the row (bit-pattern max)
-  Combine = 3       // C[t] = acc + sum_j gates[t, j] * Y[pos[t, j]]   (rows are tokens)
+  SqRelu = 1        // C = relu(acc)^2
 };
 
 struct GemmParams {
-  // A operand: rows of K elements (a_elt); row r of group g is a_gather[offs[g] + r] when
-  // a_gather is set, else offs[g] + r. With a_quant the bf16 rows are quantised to e4m3 on load
-  // with per-row scale row_amax[out row] / 448.
+  // A operand: rows of K elements; row r of group g is a_gather[offs[g] + r] when a_gather is
+  // set, else offs[g] + r.
   const void* A = nullptr;
   int64_t lda = 0;  // elements
   const int32_t* a_gather = nullptr;
-  const float* a_scale = nullptr;  // fp8 A: scale per *source* row (token)
-  int a_quant = 0;
+  const float* a_scale = nullptr;  // e4m3 A: dequantisation scale per *source* row
   // B operand: [G][N][K], b_gstride elements between experts; fp8: per-channel scales [G][N]
   const void* B = nullptr;
   int64_t ldb = 0;
@@ -43,24 +39,20 @@ struct GemmParams {
   void* C = nullptr;
   int64_t ldc = 0;
   int M = 0, N = 0, K = 0;
+  // Split-K (dense launches only): slice y of ksplit covers K columns [y*kchunk, (y+1)*kchunk)
+  // and writes its partial product to C + y * M * ldc (Store epilogue).
+  int ksplit = 1;
+  int kchunk = 0;
   // Grouping (both null for a dense launch of M rows)
   const int32_t* offs = nullptr;      // [G + 1] row offsets
   const int32_t* mt_start = nullptr;  // [G + 1] prefix of ceil(rows_g / BM)
   int G = 0;
-  // Epilogue inputs
-  float* row_amax = nullptr;          // SqReluAmax output / a_quant input, indexed by out row
-  const float* gates = nullptr;       // Combine: [M, topk]
-  const int32_t* pos = nullptr;       // Combine: [M, topk]
-  int topk = 0;
-  const void* Y = nullptr;            // Combine: rows of N, y_elt
-  int64_t ldy = 0;
 };
 
 struct GemmKind {
   Elt ab;      // element type of A and B as fed to the matrix cores (F32: vector ALU path)
   Elt out;     // C element type
   Epi epi;
-  Elt y = Elt::BF16;  // Combine: element type of Y
 };
 
 // Tile height of the grouped launches; the dispatch step builds mt_start with it.

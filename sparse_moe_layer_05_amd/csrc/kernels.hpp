@@ -14,29 +14,47 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxK = 64;
 
 // logits [T, E] fp32 -> idx [T, k] (descending key, lower index on ties), gates [T, k].
-hipError_t launch_topk(const float* logits, const float* b, int T, int E, int k, int32_t* idx,
-                       float* gates, hipStream_t s);
+// With nsplit > 1, `logits` holds nsplit partial sums [nsplit][T][E] that are added in slice
+// order first (and written to logits_out when it is not null).
+hipError_t launch_topk(const float* logits, int nsplit, const float* b, int T, int E, int k,
+                       int32_t* idx, float* gates, float* logits_out, hipStream_t s);
+
+// Router K-split for small T: number of K slices (and the slice width) that give the dense
+// router GEMM about one workgroup per CU.
+void router_split(int T, int E, int H, int* nsplit, int* kchunk);
 
 // Dispatch scratch: chunk_counts and chunk_base, each [ceil(T / 256), E] int32.
 inline size_t dispatch_scratch_ints(int T, int E) {
   return 2 * (size_t)((T + kDispatchChunk - 1) / kDispatchChunk) * (size_t)E;
 }
 
+// Extra dispatch products for the decode path: touched experts split by load into "narrow"
+// (1 .. kNarrowMax pairs) and "wide" (more) lists, both ascending, their lengths, and work
+// counters that the streaming kernels claim units from (cleared here).
+constexpr int kNarrowMax = 16;
+struct DispatchExtras {
+  int32_t* narrow = nullptr;    // [E]
+  int32_t* wide = nullptr;      // [E]
+  int32_t* n_lists = nullptr;   // [2]: number of narrow experts, number of wide experts
+  int32_t* counters = nullptr;  // [ncounters], set to 0
+  int ncounters = 0;
+};
+
 // idx [T, k] -> counts [E], offsets [E + 1], perm [T*k], pos [T, k]; optionally the prefix of
-// ceil(counts / bm) M-tiles (mt_start [E + 1], for grouped GEMMs) and zeroes zero_rows[r] for
-// every written pair row r. Pairs with an out-of-range or repeated expert are dropped (pos = -1).
+// ceil(counts / bm) M-tiles (mt_start [E + 1], for grouped GEMMs) and the decode extras.
+// Pairs with an out-of-range or repeated expert are dropped (pos = -1).
 hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* scratch,
-                           int bm, int32_t* mt_start, float* zero_rows, hipStream_t s);
+                           int bm, int32_t* mt_start, const DispatchExtras& ex, hipStream_t s);
 
-// out[t] = S[t] (optional, same element type as Y) + sum_j gates[t, j] * Y[pos[t, j]], in fixed
-// j order, rounded once to out_elt.
-hipError_t launch_combine(const void* Y, Elt y_elt, int64_t ldy, const void* S, int64_t lds,
+// out[t] = S[t] (optional, fp32) + sum_j gates[t, j] * Y[pos[t, j]], in fixed j order, rounded
+// once to out_elt.
+hipError_t launch_combine(const void* Y, Elt y_elt, int64_t ldy, const float* S, int64_t lds,
                           const int32_t* pos, const float* gates, int T, int D, int k, void* out,
                           Elt out_elt, int64_t ldo, hipStream_t s);
 
 // Per-row e4m3 quantisation of bf16 rows: scale[t] = amax / 448 (1 for a zero row),
-// q[t, :] = e4m3(x / scale).
+// q[t, :] = e4m3(x * fp32(448 / amax)).
 hipError_t launch_quant_rows(const uint16_t* x, int64_t ldx, int T, int H, uint8_t* q,
                              float* scale, hipStream_t s);
 
@@ -63,6 +81,13 @@ struct StreamParams {
   void* out_s = nullptr;
   int64_t ldo_s = 0;
   int sqrelu_bf16 = 0;                // 1: bf16(relu(acc)^2); 0: fp32 acc
+  // work lists from the dispatch step; units are claimed through counter[0] (phase 1: shared
+  // expert and wide experts) and counter[1] (phase 2: narrow experts), both zero on entry
+  const int32_t* narrow = nullptr;
+  const int32_t* wide = nullptr;
+  const int32_t* n_narrow = nullptr;
+  const int32_t* n_wide = nullptr;
+  int32_t* counter = nullptr;
 };
 hipError_t launch_stream(const StreamParams& p, hipStream_t s);
 

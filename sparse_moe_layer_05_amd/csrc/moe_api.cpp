@@ -19,7 +19,10 @@ struct Plan {
   Elt act = Elt::BF16, ex = Elt::BF16;
   int T = 0, H = 0, E = 0, k = 0, I = 0, Is = 0, L = 0, D = 0, P = 0, bm = 0;
   size_t logits = 0, idx = 0, gates = 0, counts = 0, offsets = 0, perm = 0, pos = 0;
-  size_t dscratch = 0, mt_start = 0, xq = 0, sx = 0, hmax = 0, xl = 0, z = 0, h = 0, hs = 0;
+  size_t zpart = 0, touched = 0, wcount = 0;  // router K-slices, touched experts, work counters
+  size_t S = 0;                               // shared-expert output [T, H] fp32 (grouped path)
+  int nsplit = 1, kchunk = 0;
+  size_t dscratch = 0, mt_start = 0, xq = 0, sx = 0, hq = 0, sh = 0, xl = 0, z = 0, h = 0, hs = 0;
   size_t Y = 0, total = 0;
 };
 
@@ -64,7 +67,11 @@ int32_t make_plan(const moe_desc_t* d, bool latent_call, Plan* pl) {
     return at;
   };
   const size_t P = (size_t)p.P, Tz = (size_t)p.T, Ez = (size_t)p.E;
+  if (p.act == Elt::BF16) router_split(p.T, p.E, p.H, &p.nsplit, &p.kchunk);
   p.logits = take(Tz * Ez * 4);
+  if (p.nsplit > 1) p.zpart = take((size_t)p.nsplit * Tz * Ez * 4);
+  p.touched = take((2 * Ez + 2) * 4);  // narrow list, wide list, their two lengths
+  p.wcount = take(4 * 4);
   p.idx = take(P * 4);
   p.gates = take(P * 4);
   p.counts = take(Ez * 4);
@@ -76,7 +83,8 @@ int32_t make_plan(const moe_desc_t* d, bool latent_call, Plan* pl) {
   if (fp8) {
     p.xq = take(Tz * (size_t)p.D);
     p.sx = take(Tz * 4);
-    p.hmax = take(P * 4);
+    p.hq = take(P * (size_t)p.I);
+    p.sh = take(P * 4);
   }
   if (p.L) {
     p.xl = take(Tz * (size_t)p.L * ea);
@@ -84,6 +92,7 @@ int32_t make_plan(const moe_desc_t* d, bool latent_call, Plan* pl) {
   }
   p.h = take(P * (size_t)p.I * ea);
   if (p.Is) p.hs = take(Tz * (size_t)p.Is * ea);
+  if (p.Is && !p.L && p.path == MOE_PATH_GROUPED) p.S = take(Tz * (size_t)p.H * 4);
   if (p.path == MOE_PATH_STREAM) {
     const size_t rows = P + ((p.Is && !p.L) ? Tz : 0);
     p.Y = take(rows * (size_t)p.D * 4);
@@ -96,6 +105,33 @@ int32_t make_plan(const moe_desc_t* d, bool latent_call, Plan* pl) {
 }
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// ---------------------------------------------------------------- launch trace (diagnostics)
+struct Trace {
+  int cap = 0, n = 0;
+  hipEvent_t* ev = nullptr;
+  const char** names = nullptr;
+  char filter[64] = {0};
+};
+Trace g_trace;
+
+// Brackets the launches made during its lifetime with two events on `s`.
+struct TraceSpan {
+  int slot = -1;
+  hipStream_t s;
+  TraceSpan(const char* name, hipStream_t st) : s(st) {
+    if (g_trace.n >= g_trace.cap) return;
+    if (strncmp(name, g_trace.filter, strlen(g_trace.filter)) != 0) return;
+    slot = g_trace.n++;
+    g_trace.names[slot] = name;
+    (void)hipEventRecord(g_trace.ev[2 * slot], s);
+  }
+  ~TraceSpan() {
+    if (slot >= 0) (void)hipEventRecord(g_trace.ev[2 * slot + 1], s);
+  }
+};
+
+#define MOE_SPAN(name) TraceSpan span_##__LINE__(name, s)
 
 #define MOE_TRY(expr)                                   \
   do {                                                  \
@@ -152,7 +188,6 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
   int32_t* pos = pick(r ? r->pos : (int32_t*)nullptr, pl.pos);
   int32_t* dscr = (int32_t*)(base + pl.dscratch);
   int32_t* mt_start = (int32_t*)(base + pl.mt_start);
-  float* hmax = fp8 ? (float*)(base + pl.hmax) : nullptr;
   void* h = base + pl.h;
   void* hs = pl.Is ? base + pl.hs : nullptr;
   void* Y = base + pl.Y;
@@ -161,17 +196,44 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
 
   // (1) router: logits = x W_r^T, then top-k and gates
   if (!given) {
-    MOE_TRY(dense(act, Elt::F32, Epi::Store, w->x, H, w->W_r, H, logits, E, T, E, H, s));
-    MOE_TRY(launch_topk(logits, w->b, T, E, k, idx, gates, s));
+    float* zsrc = pl.nsplit > 1 ? (float*)(base + pl.zpart) : logits;
+    {
+      MOE_SPAN(act == Elt::F32 ? "gemm_f32_store:router" : "gemm_bf16_f32out:router");
+      GemmParams g;
+      g.A = w->x; g.lda = H; g.B = w->W_r; g.ldb = H; g.C = zsrc; g.ldc = E;
+      g.M = T; g.N = E; g.K = H; g.ksplit = pl.nsplit; g.kchunk = pl.kchunk;
+      MOE_TRY(launch_gemm(GemmKind{act, Elt::F32, Epi::Store}, g, 0, s));
+    }
+    {
+      MOE_SPAN("topk:router");
+      MOE_TRY(launch_topk(zsrc, pl.nsplit, w->b, T, E, k, idx, gates,
+                          pl.nsplit > 1 ? logits : nullptr, s));
+    }
   }
   // (2) dispatch: counts, offsets, stable permutation, inverse positions, M-tile prefix
-  MOE_TRY(launch_dispatch(idx, T, E, k, counts, offsets, perm, pos, dscr,
-                          stream_path ? 0 : pl.bm, stream_path ? nullptr : mt_start, hmax, s));
+  int32_t* touched = (int32_t*)(base + pl.touched);
+  int32_t* wcount = (int32_t*)(base + pl.wcount);
+  {
+    MOE_SPAN("dispatch:all");
+    DispatchExtras ex;
+    if (stream_path) {
+      ex.narrow = touched;
+      ex.wide = touched + E;
+      ex.n_lists = touched + 2 * E;
+      ex.counters = wcount;
+      ex.ncounters = 4;
+    }
+    MOE_TRY(launch_dispatch(idx, T, E, k, counts, offsets, perm, pos, dscr,
+                            stream_path ? 0 : pl.bm, stream_path ? nullptr : mt_start, ex, s));
+  }
   // (3) routed experts read x, or its projection into the latent width
   const void* xin = w->x;
   if (L) {
     void* xl = base + pl.xl;
-    MOE_TRY(dense(act, act, Epi::Store, w->x, H, w->W_in, H, xl, L, T, L, H, s));
+    {
+      MOE_SPAN(act == Elt::F32 ? "gemm_f32_store:latent_in" : "gemm_bf16_store:latent_in");
+      MOE_TRY(dense(act, act, Epi::Store, w->x, H, w->W_in, H, xl, L, T, L, H, s));
+    }
     xin = xl;
   }
   // (4) routed experts (+ the shared expert on the stream path of a plain layer)
@@ -187,7 +249,12 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
       up.Ns = Is; up.Ks = H; up.Ts = T; up.out_s = hs; up.ldo_s = Is;
     }
     up.sqrelu_bf16 = 1;
-    MOE_TRY(launch_stream(up, s));
+    up.narrow = touched; up.wide = touched + E; up.n_narrow = touched + 2 * E;
+    up.n_wide = touched + 2 * E + 1; up.counter = wcount;
+    {
+      MOE_SPAN("stream:up");
+      MOE_TRY(launch_stream(up, s));
+    }
     StreamParams dn;
     dn.A = (const uint16_t*)h; dn.lda = I; dn.offs = offsets; dn.E = E;
     dn.W = (const uint16_t*)w->W_down; dn.N = D; dn.K = I; dn.out = Y; dn.ldo = D;
@@ -196,7 +263,12 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
       dn.Ns = H; dn.Ks = Is; dn.Ts = T; dn.out_s = (float*)Y + (size_t)P * D; dn.ldo_s = D;
     }
     dn.sqrelu_bf16 = 0;
-    MOE_TRY(launch_stream(dn, s));
+    dn.narrow = touched; dn.wide = touched + E; dn.n_narrow = touched + 2 * E;
+    dn.n_wide = touched + 2 * E + 1; dn.counter = wcount + 2;
+    {
+      MOE_SPAN("stream:down");
+      MOE_TRY(launch_stream(dn, s));
+    }
   } else {
     const int max_mt = max_group_mtiles(P, E, pl.bm);
     GemmParams up;
@@ -210,40 +282,78 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
     dn.C = Y; dn.ldc = D; dn.N = D; dn.K = I;
     dn.offs = offsets; dn.mt_start = mt_start; dn.G = E;
     if (fp8) {
+      // e4m3 expert weights: the expert input rows and the h rows are quantised per row to
+      // e4m3 (scale = row amax / 448) and both projections run on fp8 matrix cores.
       uint8_t* xq = base + pl.xq;
       float* sx = (float*)(base + pl.sx);
-      MOE_TRY(launch_quant_rows((const uint16_t*)xin, D, T, D, xq, sx, s));
-      up.A = xq; up.a_scale = sx; up.b_scale = w->s_up; up.row_amax = hmax;
-      MOE_TRY(launch_gemm(GemmKind{Elt::FP8, Elt::BF16, Epi::SqReluAmax}, up, max_mt, s));
-      dn.a_quant = 1; dn.row_amax = hmax; dn.b_scale = w->s_down;
-      MOE_TRY(launch_gemm(GemmKind{Elt::FP8, Elt::BF16, Epi::Store}, dn, max_mt, s));
+      uint8_t* hq = base + pl.hq;
+      float* sh = (float*)(base + pl.sh);
+      {
+        MOE_SPAN("quant_rows:x");
+        MOE_TRY(launch_quant_rows((const uint16_t*)xin, D, T, D, xq, sx, s));
+      }
+      up.A = xq; up.a_scale = sx; up.b_scale = w->s_up;
+      {
+        MOE_SPAN("gemm_fp8_sqrelu:routed_up");
+        MOE_TRY(launch_gemm(GemmKind{Elt::FP8, Elt::BF16, Epi::SqRelu}, up, max_mt, s));
+      }
+      {
+        MOE_SPAN("quant_rows:h");
+        MOE_TRY(launch_quant_rows((const uint16_t*)h, I, P, I, hq, sh, s));
+      }
+      dn.A = hq; dn.a_scale = sh; dn.b_scale = w->s_down;
+      {
+        MOE_SPAN("gemm_fp8_store:routed_down");
+        MOE_TRY(launch_gemm(GemmKind{Elt::FP8, Elt::BF16, Epi::Store}, dn, max_mt, s));
+      }
     } else {
       up.A = xin;
-      MOE_TRY(launch_gemm(GemmKind{act, act, Epi::SqRelu}, up, max_mt, s));
-      MOE_TRY(launch_gemm(GemmKind{act, act, Epi::Store}, dn, max_mt, s));
+      {
+        MOE_SPAN(act == Elt::F32 ? "gemm_f32_sqrelu:routed_up" : "gemm_bf16_sqrelu:routed_up");
+        MOE_TRY(launch_gemm(GemmKind{act, act, Epi::SqRelu}, up, max_mt, s));
+      }
+      {
+        MOE_SPAN(act == Elt::F32 ? "gemm_f32_store:routed_down" : "gemm_bf16_store:routed_down");
+        MOE_TRY(launch_gemm(GemmKind{act, act, Epi::Store}, dn, max_mt, s));
+      }
     }
   }
   // (5) combine (+ shared expert) and, for LatentMoE, the projection back to H
   if (!L) {
+    const float* S = nullptr;
     if (Is && !stream_path) {
-      MOE_TRY(dense(act, act, Epi::SqRelu, w->x, H, w->Ws_up, H, hs, Is, T, Is, H, s));
-      GemmParams g;
-      g.A = hs; g.lda = Is; g.B = w->Ws_down; g.ldb = Is; g.C = y; g.ldc = H;
-      g.M = T; g.N = H; g.K = Is;
-      g.gates = gates; g.pos = pos; g.topk = k; g.Y = Y; g.ldy = D;
-      MOE_TRY(launch_gemm(GemmKind{act, act, Epi::Combine, y_elt}, g, 0, s));
-    } else {
-      const void* S = (Is && stream_path) ? (const void*)((float*)Y + (size_t)P * D) : nullptr;
-      MOE_TRY(launch_combine(Y, y_elt, D, S, D, pos, gates, T, D, k, y, act, H, s));
+      // shared expert in H (always on, weight 1): S = relu(x Ws_up^T)^2 Ws_down^T in fp32
+      float* Sw = (float*)(base + pl.S);
+      {
+        MOE_SPAN(act == Elt::F32 ? "gemm_f32_sqrelu:shared_up" : "gemm_bf16_sqrelu:shared_up");
+        MOE_TRY(dense(act, act, Epi::SqRelu, w->x, H, w->Ws_up, H, hs, Is, T, Is, H, s));
+      }
+      {
+        MOE_SPAN(act == Elt::F32 ? "gemm_f32_store:shared_down" : "gemm_bf16_f32out:shared_down");
+        MOE_TRY(dense(act, Elt::F32, Epi::Store, hs, Is, w->Ws_down, Is, Sw, H, T, H, Is, s));
+      }
+      S = Sw;
+    } else if (Is && stream_path) {
+      S = (const float*)Y + (size_t)P * D;
     }
+    MOE_SPAN("combine:y");
+    MOE_TRY(launch_combine(Y, y_elt, D, S, H, pos, gates, T, D, k, y, act, H, s));
   } else {
     void* z = base + pl.z;
-    MOE_TRY(launch_combine(Y, y_elt, D, nullptr, 0, pos, gates, T, L, k, z, act, L, s));
+    {
+      MOE_SPAN("combine:z");
+      MOE_TRY(launch_combine(Y, y_elt, D, nullptr, 0, pos, gates, T, L, k, z, act, L, s));
+    }
     if (Is) {
-      MOE_TRY(dense(act, act, Epi::SqRelu, w->x, H, w->Ws_up, H, hs, Is, T, Is, H, s));
+      {
+        MOE_SPAN(act == Elt::F32 ? "gemm_f32_sqrelu:shared_up" : "gemm_bf16_sqrelu:shared_up");
+        MOE_TRY(dense(act, act, Epi::SqRelu, w->x, H, w->Ws_up, H, hs, Is, T, Is, H, s));
+      }
+      MOE_SPAN(act == Elt::F32 ? "gemm_f32_store:latent_out" : "gemm_bf16_store:latent_out");
       MOE_TRY(dense(act, act, Epi::Store, z, L, w->W_out, L, y, H, T, H, L, s, hs, Is,
                     w->Ws_down, Is, Is));
     } else {
+      MOE_SPAN(act == Elt::F32 ? "gemm_f32_store:latent_out" : "gemm_bf16_store:latent_out");
       MOE_TRY(dense(act, act, Epi::Store, z, L, w->W_out, L, y, H, T, H, L, s));
     }
   }
@@ -290,7 +400,7 @@ int32_t moe_route(const float* logits, const void* x, const void* W_r, const flo
     MOE_TRY(dense(e, Elt::F32, Epi::Store, x, H, W_r, H, logits_out, E, T, E, H, s));
     logits = logits_out;
   }
-  MOE_TRY(launch_topk(logits, b, T, E, k, idx, gates, s));
+  MOE_TRY(launch_topk(logits, 1, b, T, E, k, idx, gates, nullptr, s));
   return MOE_OK;
 }
 
@@ -310,9 +420,43 @@ int32_t moe_dispatch(const int32_t* idx, int32_t T, int32_t E, int32_t k, int32_
   if (!idx || !counts || !offsets || !perm || !pos) return MOE_ERR_INVALID_ARG;
   if (need && (!ws || ws_bytes < need || !aligned16(ws))) return MOE_ERR_WORKSPACE;
   MOE_TRY(launch_dispatch(idx, T, E, k, counts, offsets, perm, pos, (int32_t*)ws, 0, nullptr,
-                          nullptr, (hipStream_t)stream));
+                          DispatchExtras(), (hipStream_t)stream));
   return MOE_OK;
 }
+
+int32_t moe_trace_enable(int32_t capacity, const char* filter) {
+  if (capacity < 0) return MOE_ERR_INVALID_ARG;
+  if (filter && strlen(filter) >= sizeof(g_trace.filter)) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < 2 * g_trace.cap; ++i) (void)hipEventDestroy(g_trace.ev[i]);
+  delete[] g_trace.ev;
+  delete[] g_trace.names;
+  g_trace = Trace();
+  if (capacity == 0) return MOE_OK;
+  g_trace.ev = new hipEvent_t[2 * (size_t)capacity];
+  g_trace.names = new const char*[capacity];
+  for (int i = 0; i < 2 * capacity; ++i) {
+    if (hipEventCreate(&g_trace.ev[i]) != hipSuccess) {
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(g_trace.ev[j]);
+      delete[] g_trace.ev;
+      delete[] g_trace.names;
+      g_trace = Trace();
+      return MOE_ERR_HIP;
+    }
+  }
+  g_trace.cap = capacity;
+  if (filter) strcpy(g_trace.filter, filter);
+  return MOE_OK;
+}
+
+int32_t moe_trace_count(void) { return g_trace.n; }
+
+int32_t moe_trace_read(int32_t i, const char** name, float* ms) {
+  if (i < 0 || i >= g_trace.n || !name || !ms) return MOE_ERR_INVALID_ARG;
+  *name = g_trace.names[i];
+  return hip_status(hipEventElapsedTime(ms, g_trace.ev[2 * i], g_trace.ev[2 * i + 1]));
+}
+
+void moe_trace_reset(void) { g_trace.n = 0; }
 
 const char* moe_status_str(int32_t code) {
   switch (code) {

@@ -10,6 +10,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace moe {
 namespace {
 
@@ -19,10 +21,11 @@ namespace {
 // s = fp32(1 / (1 + exp(-z))) is evaluated in double so that the rounded score does not depend
 // on a particular single-precision exp; key = s + b is one binary32 addition.
 template <int NPER>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int nsplit,
                                                    const float* __restrict__ bias, int T, int E,
                                                    int k, int32_t* __restrict__ idx,
-                                                   float* __restrict__ gates) {
+                                                   float* __restrict__ gates,
+                                                   float* __restrict__ logits_out) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -31,7 +34,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   for (int i = 0; i < NPER; ++i) {
     const int e = lane + 64 * i;
     if (e < E) {
-      const float z = logits[(int64_t)t * E + e];
+      float z = logits[(int64_t)t * E + e];
+#pragma unroll 8
+      for (int q = 1; q < nsplit; ++q) z += logits[((int64_t)q * T + t) * E + e];  // slice order
+      if (logits_out) logits_out[(int64_t)t * E + e] = z;
       const float s = (float)(1.0 / (1.0 + exp(-(double)z)));
       sc[i] = s;
       key[i] = s + bias[e];
@@ -79,18 +85,18 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 // expert records which of the 256 tokens chose it; the popcount of the bits below a token is
 // its stable rank inside the chunk, and chunk bases from a prefix over chunks make the global
 // order "experts ascending, tokens ascending" without any order-deciding atomics.
-__device__ __forceinline__ uint32_t build_masks(const int32_t* __restrict__ idx, int T, int E,
+__device__ __forceinline__ uint64_t build_masks(const int32_t* __restrict__ idx, int T, int E,
                                                 int k, uint32_t* mask, int t, int tid) {
   for (int i = tid; i < E * 8; i += kDispatchChunk) mask[i] = 0;
   __syncthreads();
-  uint32_t valid = 0;  // bit j: pair (t, j) is kept
+  uint64_t valid = 0;  // bit j: pair (t, j) is kept (k <= 64)
   if (t < T) {
     for (int j = 0; j < k; ++j) {
       const int e = idx[(int64_t)t * k + j];
       if ((unsigned)e < (unsigned)E) {
         const uint32_t bit = 1u << (tid & 31);
         const uint32_t old = atomicOr(&mask[e * 8 + (tid >> 5)], bit);
-        if (!(old & bit)) valid |= 1u << j;  // a repeated expert in one token is dropped
+        if (!(old & bit)) valid |= 1ull << j;  // a repeated expert in one token is dropped
       }
     }
   }
@@ -112,39 +118,69 @@ __global__ __launch_bounds__(kDispatchChunk) void dispatch_count(const int32_t* 
   }
 }
 
+// Block-wide inclusive scans (Hillis-Steele) of four per-thread values over 1024 threads.
+__device__ __forceinline__ void scan4(int32_t (*s)[1024], int e) {
+  for (int d = 1; d < 1024; d <<= 1) {
+    int v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = e >= d ? s[q][e - d] : 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s[q][e] += v[q];
+    __syncthreads();
+  }
+}
+
+// Per-expert totals -> counts, offsets, M-tile prefix, narrow / wide lists; thread e = expert e.
+// s[0..3] end as the inclusive scans of counts, M-tiles, narrow flags and wide flags.
+__device__ __forceinline__ void dispatch_totals(int e, int E, int tot, int bm,
+                                                int32_t (*s)[1024], int32_t* counts,
+                                                int32_t* offsets, int32_t* mt_start,
+                                                const DispatchExtras& ex) {
+  const int mt = bm > 0 ? (tot + bm - 1) / bm : 0;
+  const bool in = e < E;
+  const int nar = in && tot > 0 && tot <= kNarrowMax;
+  const int wid = in && tot > kNarrowMax;
+  s[0][e] = in ? tot : 0;
+  s[1][e] = in ? mt : 0;
+  s[2][e] = nar;
+  s[3][e] = wid;
+  __syncthreads();
+  scan4(s, e);
+  if (in) {
+    counts[e] = tot;
+    offsets[e] = s[0][e] - tot;
+    if (e == E - 1) offsets[E] = s[0][e];
+    if (mt_start) {
+      mt_start[e] = s[1][e] - mt;
+      if (e == E - 1) mt_start[E] = s[1][e];
+    }
+    if (ex.narrow && nar) ex.narrow[s[2][e] - 1] = e;
+    if (ex.wide && wid) ex.wide[s[3][e] - 1] = e;
+    if (ex.n_lists && e == E - 1) {
+      ex.n_lists[0] = s[2][e];
+      ex.n_lists[1] = s[3][e];
+    }
+  }
+  if (e < ex.ncounters) ex.counters[e] = 0;
+}
+
 // One workgroup of 1024 threads, thread e = expert e.
 __global__ __launch_bounds__(1024) void dispatch_scan(const int32_t* __restrict__ ccount,
                                                       int nchunks, int E, int bm,
                                                       int32_t* __restrict__ cbase,
                                                       int32_t* __restrict__ counts,
                                                       int32_t* __restrict__ offsets,
-                                                      int32_t* __restrict__ mt_start) {
-  __shared__ int32_t s_a[1024], s_b[1024];
+                                                      int32_t* __restrict__ mt_start,
+                                                      DispatchExtras ex) {
+  __shared__ int32_t s[4][1024];
   const int e = threadIdx.x;
   int tot = 0;
   if (e < E)
     for (int c = 0; c < nchunks; ++c) tot += ccount[(int64_t)c * E + e];
-  const int mt = bm > 0 ? (tot + bm - 1) / bm : 0;
-  s_a[e] = e < E ? tot : 0;
-  s_b[e] = e < E ? mt : 0;
-  __syncthreads();
-  for (int d = 1; d < 1024; d <<= 1) {  // inclusive Hillis-Steele scan
-    const int va = e >= d ? s_a[e - d] : 0, vb = e >= d ? s_b[e - d] : 0;
-    __syncthreads();
-    s_a[e] += va;
-    s_b[e] += vb;
-    __syncthreads();
-  }
+  dispatch_totals(e, E, tot, bm, s, counts, offsets, mt_start, ex);
   if (e < E) {
-    const int ex = s_a[e] - tot;
-    counts[e] = tot;
-    offsets[e] = ex;
-    if (e == E - 1) offsets[E] = s_a[e];
-    if (mt_start) {
-      mt_start[e] = s_b[e] - mt;
-      if (e == E - 1) mt_start[E] = s_b[e];
-    }
-    int run = ex;
+    int run = s[0][e] - tot;
     for (int c = 0; c < nchunks; ++c) {
       cbase[(int64_t)c * E + e] = run;
       run += ccount[(int64_t)c * E + e];
@@ -152,17 +188,71 @@ __global__ __launch_bounds__(1024) void dispatch_scan(const int32_t* __restrict_
   }
 }
 
+// All of dispatch in one workgroup when T fits one chunk (T <= 256): masks, totals, scatter.
+__global__ __launch_bounds__(1024) void dispatch_small(const int32_t* __restrict__ idx, int T,
+                                                       int E, int k, int bm,
+                                                       int32_t* __restrict__ counts,
+                                                       int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ perm,
+                                                       int32_t* __restrict__ pos,
+                                                       int32_t* __restrict__ mt_start,
+                                                       DispatchExtras ex) {
+  __shared__ uint32_t mask[kMaxE * 8];
+  __shared__ int32_t s[4][1024];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < E * 8; i += 1024) mask[i] = 0;
+  __syncthreads();
+  uint64_t valid = 0;
+  if (tid < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(int64_t)tid * k + j];
+      if ((unsigned)e < (unsigned)E) {
+        const uint32_t bit = 1u << (tid & 31);
+        const uint32_t old = atomicOr(&mask[e * 8 + (tid >> 5)], bit);
+        if (!(old & bit)) valid |= 1ull << j;
+      }
+    }
+  }
+  __syncthreads();
+  int tot = 0;
+  if (tid < E)
+#pragma unroll
+    for (int w = 0; w < 8; ++w) tot += __popc(mask[tid * 8 + w]);
+  dispatch_totals(tid, E, tot, bm, s, counts, offsets, mt_start, ex);
+  // s[0][e] - count[e] is the base of expert e; counts are re-derived from the masks below.
+  if (tid < T) {
+    const int w = tid >> 5;
+    const uint32_t below = (1u << (tid & 31)) - 1u;
+    for (int j = 0; j < k; ++j) {
+      if (!((valid >> j) & 1ull)) {
+        pos[(int64_t)tid * k + j] = -1;
+        continue;
+      }
+      const int e = idx[(int64_t)tid * k + j];
+      int cnt = 0, rank = __popc(mask[e * 8 + w] & below);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        cnt += __popc(mask[e * 8 + q]);
+        if (q < w) rank += __popc(mask[e * 8 + q]);
+      }
+      const int r = s[0][e] - cnt + rank;
+      perm[r] = tid;
+      pos[(int64_t)tid * k + j] = r;
+    }
+  }
+}
+
 __global__ __launch_bounds__(kDispatchChunk) void dispatch_scatter(
     const int32_t* __restrict__ idx, int T, int E, int k, const int32_t* __restrict__ cbase,
-    int32_t* __restrict__ perm, int32_t* __restrict__ pos, float* __restrict__ zero_rows) {
+    int32_t* __restrict__ perm, int32_t* __restrict__ pos) {
   extern __shared__ uint32_t mask[];
   const int tid = threadIdx.x, c = blockIdx.x, t = c * kDispatchChunk + tid;
-  const uint32_t valid = build_masks(idx, T, E, k, mask, t, tid);
+  const uint64_t valid = build_masks(idx, T, E, k, mask, t, tid);
   if (t >= T) return;
   const int w = tid >> 5;
   const uint32_t below = (1u << (tid & 31)) - 1u;
   for (int j = 0; j < k; ++j) {
-    if (!((valid >> j) & 1u)) {
+    if (!((valid >> j) & 1ull)) {
       pos[(int64_t)t * k + j] = -1;
       continue;
     }
@@ -172,16 +262,15 @@ __global__ __launch_bounds__(kDispatchChunk) void dispatch_scatter(
     const int r = cbase[(int64_t)c * E + e] + rank;
     perm[r] = t;
     pos[(int64_t)t * k + j] = r;
-    if (zero_rows) zero_rows[r] = 0.f;
   }
 }
 
 // ---------------------------------------------------------------------------------- combine
 // One workgroup per token; each thread owns 8 consecutive columns (one 16-byte bf16 load or two
-// fp32 loads per source row). Sum order: S first, then j = 0..k-1.
+// fp32 loads per source row). Sum order: S (fp32) first, then j = 0..k-1.
 template <Elt YT, Elt OT>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y, int64_t ldy,
-                                                      const void* __restrict__ S, int64_t lds,
+                                                      const float* __restrict__ S, int64_t lds,
                                                       const int32_t* __restrict__ pos,
                                                       const float* __restrict__ gates, int T,
                                                       int D, int k, void* __restrict__ out,
@@ -206,7 +295,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y
       }
     };
     if (S) {
-      load8(S, t, lds, acc);
+      const float4 a = *(const float4*)(S + t * lds + c);
+      const float4 b = *(const float4*)(S + t * lds + c + 4);
+      acc[0] = a.x; acc[1] = a.y; acc[2] = a.z; acc[3] = a.w;
+      acc[4] = b.x; acc[5] = b.y; acc[6] = b.z; acc[7] = b.w;
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = 0.f;
@@ -236,7 +328,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y
 }
 
 // -------------------------------------------------------------------------------- quantise
-// One workgroup per row: amax by wave shuffles + LDS, then e4m3 codes of x / scale.
+// One workgroup per row: amax by wave shuffles + LDS, then e4m3 codes of x * (448 / amax).
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x,
                                                          int64_t ldx, int H,
                                                          uint8_t* __restrict__ q,
@@ -259,18 +351,18 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
   if ((tid & 63) == 0) s_max[tid >> 6] = m;
   __syncthreads();
   const float amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
-  const float s = amax > 0.f ? amax / 448.f : 1.f;
-  if (tid == 0) scale[t] = s;
+  const float inv = amax > 0.f ? 448.f / amax : 1.f;   // codes = e4m3(x * inv)
+  if (tid == 0) scale[t] = amax > 0.f ? amax / 448.f : 1.f;
   for (int c = tid * 8; c < H; c += 256 * 8) {
     const uint4 v = *(const uint4*)(row + c);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t o[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const float f0 = bf16_bits_to_f32(w[2 * h] & 0xFFFF) / s;
-      const float f1 = bf16_bits_to_f32(w[2 * h] >> 16) / s;
-      const float f2 = bf16_bits_to_f32(w[2 * h + 1] & 0xFFFF) / s;
-      const float f3 = bf16_bits_to_f32(w[2 * h + 1] >> 16) / s;
+      const float f0 = bf16_bits_to_f32(w[2 * h] & 0xFFFF) * inv;
+      const float f1 = bf16_bits_to_f32(w[2 * h] >> 16) * inv;
+      const float f2 = bf16_bits_to_f32(w[2 * h + 1] & 0xFFFF) * inv;
+      const float f3 = bf16_bits_to_f32(w[2 * h + 1] >> 16) * inv;
       o[h] = cvt_fp8x2(f0, f1) | (cvt_fp8x2(f2, f3) << 16);
     }
     *(uint2*)(q + (int64_t)t * H + c) = make_uint2(o[0], o[1]);
@@ -279,37 +371,51 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
 
 }  // namespace
 
-hipError_t launch_topk(const float* logits, const float* b, int T, int E, int k, int32_t* idx,
-                       float* gates, hipStream_t s) {
+hipError_t launch_topk(const float* logits, int nsplit, const float* b, int T, int E, int k,
+                       int32_t* idx, float* gates, float* logits_out, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const dim3 grid((T + 3) / 4), block(256);
-  if (E <= 64) hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, logits, b, T, E, k, idx, gates);
-  else if (E <= 128) hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, logits, b, T, E, k, idx, gates);
-  else if (E <= 256) hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, logits, b, T, E, k, idx, gates);
-  else if (E <= 512) hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, logits, b, T, E, k, idx, gates);
-  else hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, logits, b, T, E, k, idx, gates);
+#define MOE_TOPK(NPER) hipLaunchKernelGGL(topk_kernel<NPER>, grid, block, 0, s, logits, nsplit, b, \
+                                          T, E, k, idx, gates, logits_out)
+  if (E <= 64) MOE_TOPK(1);
+  else if (E <= 128) MOE_TOPK(2);
+  else if (E <= 256) MOE_TOPK(4);
+  else if (E <= 512) MOE_TOPK(8);
+  else MOE_TOPK(16);
+#undef MOE_TOPK
   return hipGetLastError();
+}
+
+void router_split(int T, int E, int H, int* nsplit, int* kchunk) {
+  const int tiles = cdiv(T, 128) * cdiv(E, 128);
+  const int n = (tiles == 0 || tiles >= 128) ? 1 : std::max(1, std::min(256 / tiles, H / 128));
+  const int chunk = cdiv(cdiv(H, n), 64) * 64;   // whole 64-wide K-steps per slice
+  *kchunk = chunk;
+  *nsplit = cdiv(H, chunk);
 }
 
 hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* scratch,
-                           int bm, int32_t* mt_start, float* zero_rows, hipStream_t s) {
+                           int bm, int32_t* mt_start, const DispatchExtras& ex, hipStream_t s) {
   const int nch = (T + kDispatchChunk - 1) / kDispatchChunk;
+  if (nch <= 1) {
+    hipLaunchKernelGGL(dispatch_small, dim3(1), dim3(1024), 0, s, idx, T, E, k, bm, counts,
+                       offsets, perm, pos, mt_start, ex);
+    return hipGetLastError();
+  }
   int32_t* ccount = scratch;
   int32_t* cbase = scratch + (size_t)nch * E;
   const size_t lds = (size_t)E * 8 * sizeof(uint32_t);
-  if (nch > 0)
-    hipLaunchKernelGGL(dispatch_count, dim3(nch), dim3(kDispatchChunk), lds, s, idx, T, E, k,
-                       ccount);
+  hipLaunchKernelGGL(dispatch_count, dim3(nch), dim3(kDispatchChunk), lds, s, idx, T, E, k,
+                     ccount);
   hipLaunchKernelGGL(dispatch_scan, dim3(1), dim3(1024), 0, s, ccount, nch, E, bm, cbase, counts,
-                     offsets, mt_start);
-  if (nch > 0)
-    hipLaunchKernelGGL(dispatch_scatter, dim3(nch), dim3(kDispatchChunk), lds, s, idx, T, E, k,
-                       cbase, perm, pos, zero_rows);
+                     offsets, mt_start, ex);
+  hipLaunchKernelGGL(dispatch_scatter, dim3(nch), dim3(kDispatchChunk), lds, s, idx, T, E, k,
+                     cbase, perm, pos);
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const void* Y, Elt y_elt, int64_t ldy, const void* S, int64_t lds,
+hipError_t launch_combine(const void* Y, Elt y_elt, int64_t ldy, const float* S, int64_t lds,
                           const int32_t* pos, const float* gates, int T, int D, int k, void* out,
                           Elt out_elt, int64_t ldo, hipStream_t s) {
   if (T <= 0) return hipSuccess;

@@ -15,7 +15,7 @@ FAKE = C.c_void_p(0x10000)    # aligned, never dereferenced: validation fails or
 
 def declared_symbols():
     text = open(os.path.join(ROOT, "include", "moe.h")).read()
-    return set(re.findall(r"^(?:int32_t|const char \*)\s*(\w+)\(", text, re.M))
+    return set(re.findall(r"^(?:int32_t|const char \*|void)\s*(\w+)\(", text, re.M))
 
 
 def test_library_exports_every_declared_symbol():

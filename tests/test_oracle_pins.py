@@ -309,8 +309,8 @@ def test_fp8_experts_use_dequantised_weights_exactly():
 
 
 def test_fp8_emulation_quantises_activation_rows():
-    # E=1, k=1: x and h rows quantised per row (scale amax/448, codes via torch's e4m3 cast),
-    # h rounded to bf16 first; the rest is numpy matmul.
+    # E=1, k=1: x and h rows quantised per row (scale amax/448, codes = torch's e4m3 cast of
+    # the row times fp32(448/amax)), h rounded to bf16 first; the rest is numpy matmul.
     c = cfg(E=1, k=1, T=6, H=64, I=32, act_dtype="bf16", expert_dtype="e4m3")
     inp = mi.make_layer(c, seed=16)
     r = O.forward_tokens(inp, np.zeros((6, 1), np.int32), np.ones((6, 1)), fp8_emulate=True)
@@ -319,7 +319,8 @@ def test_fp8_emulation_quantises_activation_rows():
         rows32 = rows.astype(np.float32)
         amax = np.abs(rows32).max(1)
         sc = np.where(amax > 0, amax / np.float32(448), np.float32(1)).astype(np.float32)
-        v = torch.from_numpy((rows32 / sc[:, None]).astype(np.float32))
+        inv = np.where(amax > 0, np.float32(448) / amax, np.float32(1)).astype(np.float32)
+        v = torch.from_numpy((rows32 * inv[:, None]).astype(np.float32))
         return v.to(torch.float8_e4m3fn).double().numpy() * sc[:, None].astype(np.float64)
 
     x = q(f64(inp, "x"))
