@@ -28,17 +28,17 @@ inline size_t dispatch_scratch_ints(int T, int E) {
   return 2 * (size_t)((T + kDispatchChunk - 1) / kDispatchChunk) * (size_t)E;
 }
 
-// Extra dispatch products for the decode path: touched experts split by load into "narrow"
-// (1 .. kNarrowMax pairs) and "wide" (more) lists, both ascending, their lengths, and work
-// counters that the streaming kernels claim units from (cleared here).
-constexpr int kNarrowMax = 16;
+// Extra dispatch product for the decode path: the touched experts cut into slices of at most
+// kSliceRows consecutive pair rows, ascending by expert then row. Slice i covers pair rows
+// slice_r[i] .. min(slice_r[i] + kSliceRows, offsets[slice_e[i] + 1]) - 1 of expert slice_e[i].
+// Each array holds at most E + T*k / kSliceRows entries.
+constexpr int kSliceRows = 16;
 struct DispatchExtras {
-  int32_t* narrow = nullptr;    // [E]
-  int32_t* wide = nullptr;      // [E]
-  int32_t* n_lists = nullptr;   // [2]: number of narrow experts, number of wide experts
-  int32_t* counters = nullptr;  // [ncounters], set to 0
-  int ncounters = 0;
+  int32_t* slice_e = nullptr;   // expert of each slice
+  int32_t* slice_r = nullptr;   // first pair row of each slice
+  int32_t* n_slices = nullptr;  // [1]: number of slices
 };
+inline int max_slices(int P, int E) { return E + P / kSliceRows; }
 
 // idx [T, k] -> counts [E], offsets [E + 1], perm [T*k], pos [T, k]; optionally the prefix of
 // ceil(counts / bm) M-tiles (mt_start [E + 1], for grouped GEMMs) and the decode extras.
@@ -81,13 +81,10 @@ struct StreamParams {
   void* out_s = nullptr;
   int64_t ldo_s = 0;
   int sqrelu_bf16 = 0;                // 1: bf16(relu(acc)^2); 0: fp32 acc
-  // work lists from the dispatch step; units are claimed through counter[0] (phase 1: shared
-  // expert and wide experts) and counter[1] (phase 2: narrow experts), both zero on entry
-  const int32_t* narrow = nullptr;
-  const int32_t* wide = nullptr;
-  const int32_t* n_narrow = nullptr;
-  const int32_t* n_wide = nullptr;
-  int32_t* counter = nullptr;
+  // slices of the routed experts from the dispatch step (see DispatchExtras)
+  const int32_t* slice_e = nullptr;
+  const int32_t* slice_r = nullptr;
+  const int32_t* n_slices = nullptr;
 };
 hipError_t launch_stream(const StreamParams& p, hipStream_t s);
 

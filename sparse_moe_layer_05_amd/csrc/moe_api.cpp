@@ -19,7 +19,7 @@ struct Plan {
   Elt act = Elt::BF16, ex = Elt::BF16;
   int T = 0, H = 0, E = 0, k = 0, I = 0, Is = 0, L = 0, D = 0, P = 0, bm = 0;
   size_t logits = 0, idx = 0, gates = 0, counts = 0, offsets = 0, perm = 0, pos = 0;
-  size_t zpart = 0, touched = 0, wcount = 0;  // router K-slices, touched experts, work counters
+  size_t zpart = 0, slices = 0;  // router K-slices, decode slices of the touched experts
   size_t S = 0;                               // shared-expert output [T, H] fp32 (grouped path)
   int nsplit = 1, kchunk = 0;
   size_t dscratch = 0, mt_start = 0, xq = 0, sx = 0, hq = 0, sh = 0, xl = 0, z = 0, h = 0, hs = 0;
@@ -70,8 +70,7 @@ int32_t make_plan(const moe_desc_t* d, bool latent_call, Plan* pl) {
   if (p.act == Elt::BF16) router_split(p.T, p.E, p.H, &p.nsplit, &p.kchunk);
   p.logits = take(Tz * Ez * 4);
   if (p.nsplit > 1) p.zpart = take((size_t)p.nsplit * Tz * Ez * 4);
-  p.touched = take((2 * Ez + 2) * 4);  // narrow list, wide list, their two lengths
-  p.wcount = take(4 * 4);
+  p.slices = take((2 * (size_t)max_slices(p.P, p.E) + 1) * 4);  // decode slices, their count
   p.idx = take(P * 4);
   p.gates = take(P * 4);
   p.counts = take(Ez * 4);
@@ -211,17 +210,15 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
     }
   }
   // (2) dispatch: counts, offsets, stable permutation, inverse positions, M-tile prefix
-  int32_t* touched = (int32_t*)(base + pl.touched);
-  int32_t* wcount = (int32_t*)(base + pl.wcount);
+  int32_t* slices = (int32_t*)(base + pl.slices);
+  const int max_sl = max_slices(P, E);
   {
     MOE_SPAN("dispatch:all");
     DispatchExtras ex;
     if (stream_path) {
-      ex.narrow = touched;
-      ex.wide = touched + E;
-      ex.n_lists = touched + 2 * E;
-      ex.counters = wcount;
-      ex.ncounters = 4;
+      ex.slice_e = slices;
+      ex.slice_r = slices + max_sl;
+      ex.n_slices = slices + 2 * max_sl;
     }
     MOE_TRY(launch_dispatch(idx, T, E, k, counts, offsets, perm, pos, dscr,
                             stream_path ? 0 : pl.bm, stream_path ? nullptr : mt_start, ex, s));
@@ -249,8 +246,7 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
       up.Ns = Is; up.Ks = H; up.Ts = T; up.out_s = hs; up.ldo_s = Is;
     }
     up.sqrelu_bf16 = 1;
-    up.narrow = touched; up.wide = touched + E; up.n_narrow = touched + 2 * E;
-    up.n_wide = touched + 2 * E + 1; up.counter = wcount;
+    up.slice_e = slices; up.slice_r = slices + max_sl; up.n_slices = slices + 2 * max_sl;
     {
       MOE_SPAN("stream:up");
       MOE_TRY(launch_stream(up, s));
@@ -263,8 +259,7 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
       dn.Ns = H; dn.Ks = Is; dn.Ts = T; dn.out_s = (float*)Y + (size_t)P * D; dn.ldo_s = D;
     }
     dn.sqrelu_bf16 = 0;
-    dn.narrow = touched; dn.wide = touched + E; dn.n_narrow = touched + 2 * E;
-    dn.n_wide = touched + 2 * E + 1; dn.counter = wcount + 2;
+    dn.slice_e = slices; dn.slice_r = slices + max_sl; dn.n_slices = slices + 2 * max_sl;
     {
       MOE_SPAN("stream:down");
       MOE_TRY(launch_stream(dn, s));

@@ -131,38 +131,39 @@ __device__ __forceinline__ void scan4(int32_t (*s)[1024], int e) {
   }
 }
 
-// Per-expert totals -> counts, offsets, M-tile prefix, narrow / wide lists; thread e = expert e.
-// s[0..3] end as the inclusive scans of counts, M-tiles, narrow flags and wide flags.
+// Per-expert totals -> counts, offsets, M-tile prefix, decode slices; thread e = expert e.
+// s[0..2] end as the inclusive scans of counts, M-tiles and slices (s[3] is unused).
 __device__ __forceinline__ void dispatch_totals(int e, int E, int tot, int bm,
                                                 int32_t (*s)[1024], int32_t* counts,
                                                 int32_t* offsets, int32_t* mt_start,
                                                 const DispatchExtras& ex) {
   const int mt = bm > 0 ? (tot + bm - 1) / bm : 0;
   const bool in = e < E;
-  const int nar = in && tot > 0 && tot <= kNarrowMax;
-  const int wid = in && tot > kNarrowMax;
+  const int ns = in ? (tot + kSliceRows - 1) / kSliceRows : 0;
   s[0][e] = in ? tot : 0;
   s[1][e] = in ? mt : 0;
-  s[2][e] = nar;
-  s[3][e] = wid;
+  s[2][e] = ns;
+  s[3][e] = 0;
   __syncthreads();
   scan4(s, e);
   if (in) {
+    const int base = s[0][e] - tot;
     counts[e] = tot;
-    offsets[e] = s[0][e] - tot;
+    offsets[e] = base;
     if (e == E - 1) offsets[E] = s[0][e];
     if (mt_start) {
       mt_start[e] = s[1][e] - mt;
       if (e == E - 1) mt_start[E] = s[1][e];
     }
-    if (ex.narrow && nar) ex.narrow[s[2][e] - 1] = e;
-    if (ex.wide && wid) ex.wide[s[3][e] - 1] = e;
-    if (ex.n_lists && e == E - 1) {
-      ex.n_lists[0] = s[2][e];
-      ex.n_lists[1] = s[3][e];
+    if (ex.slice_e) {
+      const int first = s[2][e] - ns;
+      for (int j = 0; j < ns; ++j) {
+        ex.slice_e[first + j] = e;
+        ex.slice_r[first + j] = base + j * kSliceRows;
+      }
+      if (e == E - 1) ex.n_slices[0] = s[2][e];
     }
   }
-  if (e < ex.ncounters) ex.counters[e] = 0;
 }
 
 // One workgroup of 1024 threads, thread e = expert e.

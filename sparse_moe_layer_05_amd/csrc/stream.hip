@@ -1,19 +1,21 @@
 // Decode path of the MoE layer on gfx950. With tens of tokens, reading the touched experts'
 // weights dominates and the layer is HBM-bound ("NVIDIA Nemotron 3: Efficient and Open
 // Intelligence", section 2.2, latency-oriented deployment), so each touched expert's weight
-// matrix is read from HBM exactly once.
+// matrix is read from HBM once.
 //
-// Work comes in units of 16 weight rows. A persistent grid of 1024 waves (one per SIMD) claims
-// units from device counters that the dispatch step cleared, in two phases:
-//   1. "wide" units: the shared expert's blocks and the blocks of experts with more than 16
-//      tokens, up to 64 tokens per pass (four 16-token slices);
-//   2. "narrow" units: the blocks of experts with at most 16 tokens. This is the bulk of the
-//      bytes, so loads are double buffered in registers with a one-unit lookahead: while the
-//      last k batch of a unit is multiplied, the first batch of the next claimed unit is in
-//      flight.
-// Inside a unit the weights are the matrix-core "A" operand and the tokens the "B" operand of
-// v_mfma_f32_16x16x32_bf16: lane l loads 16 bytes of weight row (l % 16) at k offset
-// 8 * (l / 16) of each 32-wide k step straight from HBM into registers (no LDS).
+// Work comes in units of 16 weight rows against one slice of at most 16 tokens of one expert
+// (the shared expert's tokens are cut into slices the same way). All units cost about the same,
+// so a persistent grid of 1024 waves (one per SIMD) deals them out round robin: unit j goes to
+// wave j mod 1024, and no wave holds more than one unit more than any other. Waves are numbered
+// die by die and units ordered row block first, slice second, so the slices that share weight
+// rows run at the same time on neighbouring waves of one die: the weights come from HBM once
+// and from that die's L2 for the other slices.
+//
+// Loads are double buffered in registers with a one-unit lookahead: while a unit streams, the
+// next one is resolved, and its first k batch is in flight while the current unit's last batch
+// is multiplied. Inside a unit the weights are the matrix-core "A" operand and the tokens the
+// "B" operand of v_mfma_f32_16x16x32_bf16: lane l loads 16 bytes of weight row (l % 16) at k
+// offset 8 * (l / 16) of each 32-wide k step straight from HBM into registers (no LDS).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -22,17 +24,15 @@ namespace {
 
 constexpr int kUnitRows = 16;
 constexpr int kStreamWaves = 1024;  // 4 per CU, one per SIMD
-constexpr int UN = 16;              // narrow units: 32-wide k steps per load batch
-constexpr int UW = 4;               // wide units: k steps per batch
-constexpr int NSW = 4;              // wide units: 16-token slices per pass
+constexpr int UN = 6;               // 32-wide k steps per load batch
+
+// Unit lookups are wave-uniform: reading them through the constant address space makes them
+// scalar loads, which are counted apart from the vector loads, so a lookup never waits for the
+// weight loads in flight (vector loads complete in issue order).
+typedef const __attribute__((address_space(4))) int32_t* scalar_ptr;
+__device__ __forceinline__ int sload(const int32_t* p, int i) { return ((scalar_ptr)p)[i]; }
 
 __device__ __forceinline__ bf16x8_t ld16(const uint16_t* p) { return *(const bf16x8_t*)p; }
-
-__device__ __forceinline__ int claim(int32_t* counter, int lane) {
-  int u = 0;
-  if (lane == 0) u = atomicAdd(counter, 1);
-  return __shfl(u, 0);
-}
 
 // One lane's part of a 16 x 16 output block: 4 consecutive columns n .. n+3 of row orow.
 __device__ __forceinline__ void store_block(const f32x4_t v, void* out, int64_t ldo,
@@ -46,160 +46,174 @@ __device__ __forceinline__ void store_block(const f32x4_t v, void* out, int64_t 
   }
 }
 
-// Wide unit: rows n0 .. n0+15 of W ([N][K]) against rows [row_begin, row_begin + nrows) of the
-// activations, 64 tokens per pass.
-__device__ void wide_unit(const uint16_t* __restrict__ A, int64_t lda,
-                          const int32_t* __restrict__ gather, int row_begin, int nrows,
-                          const uint16_t* __restrict__ W, int N, int K, int n0, void* out,
-                          int64_t ldo, bool sq, int lane) {
-  const uint16_t* wrow = W + (int64_t)min(n0 + (lane & 15), N - 1) * K;
+// A unit resolved to this lane's pointers. Pointers include the lane's k offset within a
+// 32-wide step.
+struct Unit {
+  const uint16_t* w;  // this lane's weight row
+  const uint16_t* a;  // this lane's token row
+  void* out;
+  int64_t ldo;
+  int64_t orow;       // output row of this lane's token
+  int n;              // first of this lane's 4 output columns
+  int N, K;           // weight rows and columns of the expert
+  int nrows;          // tokens of the slice
+};
+
+// Streams the units this wave is dealt: first, first + nwaves, ... below total;
+// resolve(u, unit) fills a unit.
+//
+// Each k batch covers U steps of 32 columns; the loads of the following batch (of this unit or,
+// after its last batch, of the next unit) are in flight while a batch is multiplied. The two
+// register sets swap roles between consecutive batches and are never copied (a copy would wait
+// for the loads in flight). kFull (every K >= 32*U): the last batch of a unit is moved back to
+// end exactly at K and the weight chunks it shares with the batch before are zeroed, so every
+// load of a batch is one base address plus an immediate offset and every batch issues the same
+// number of loads, which lets the compiler wait for exactly the batch it multiplies. !kFull:
+// loads of the last batch past K are clamped into the row and zeroed.
+template <int U, bool kFull, class Resolve>
+__device__ void stream_units(int first, int total, int nwaves, int lane, bool sq,
+                             Resolve resolve) {
   const int kq = (lane >> 4) * 8;
-  for (int t0 = 0; t0 < nrows; t0 += 16 * NSW) {
-    const int ns = min(NSW, cdiv(nrows - t0, 16));
-    const uint16_t* arow[NSW];
+  const int tr = lane & 15;
+  if (first >= total) return;
+  Unit cur, nxt;
+  int u = first;
+  resolve(u, cur);
+  int un = u + nwaves < total ? u + nwaves : -1;
+  if (un >= 0) resolve(un, nxt);
+
+  auto nbat_of = [&](int K) { return cdiv(K, 32 * U); };
+  auto kbase = [&](int K, int b) { return kFull ? min(b * 32 * U, K - 32 * U) : b * 32 * U; };
+  // loads of batch b of unit s, or of batch 0 of unit o when other is set (chosen field by
+  // field: choosing a whole unit would put both in memory)
+  auto issue = [&](const Unit& s, const Unit& o, bool other, int b, bf16x8_t* wf,
+                   bf16x8_t* xf) {
+    const int K = other ? o.K : s.K;
+    const uint16_t* w = other ? o.w : s.w;
+    const uint16_t* a = other ? o.a : s.a;
+    const int kb = kbase(K, b);
 #pragma unroll
-    for (int s = 0; s < NSW; ++s) {
-      const int tr = min(t0 + s * 16 + (lane & 15), nrows - 1);
-      const int64_t src = gather ? gather[row_begin + tr] : (int64_t)(row_begin + tr);
-      arow[s] = A + src * lda;
+    for (int q = 0; q < U; ++q) {
+      const int kk = kFull ? kb + q * 32 : min(kb + q * 32, K - 8 - kq);
+      wf[q] = ld16(w + kk);
+      xf[q] = ld16(a + kk);
     }
-    f32x4_t acc[NSW];
+  };
+  // last batch b: zero the weight chunks that an earlier batch already covered, or that lie
+  // past K
+  auto mask = [&](int K, int b, bf16x8_t* wf) {
+    const int kb = kbase(K, b);
 #pragma unroll
-    for (int s = 0; s < NSW; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < K; k0 += 32 * UW) {
-      bf16x8_t wf[UW], xf[UW][NSW];
-#pragma unroll
-      for (int u = 0; u < UW; ++u) {
-        const int kk = k0 + u * 32 + kq;
-        const bool ok = kk < K;
-        wf[u] = ok ? ld16(wrow + kk) : bf16x8_t{};
-#pragma unroll
-        for (int s = 0; s < NSW; ++s)
-          if (s < ns) xf[u][s] = ok ? ld16(arow[s] + kk) : bf16x8_t{};
-      }
-#pragma unroll
-      for (int u = 0; u < UW; ++u)
-#pragma unroll
-        for (int s = 0; s < NSW; ++s)
-          if (s < ns) acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], xf[u][s], acc[s], 0, 0, 0);
+    for (int q = 0; q < U; ++q) {
+      const bool drop = kFull ? kb + q * 32 + kq < b * 32 * U : kb + q * 32 + kq >= K;
+      if (drop) wf[q] = bf16x8_t{};
     }
-    // acc[s][r] = out[token t0 + s*16 + lane%16][n0 + (lane/16)*4 + r]
-    const int n = n0 + (lane >> 4) * 4;
+  };
+
+  bf16x8_t w0[U], w1[U], x0[U], x1[U];
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int b = 0, nbat = nbat_of(cur.K);
+  // One k batch: put the following batch in flight into (wnxt, xnxt), multiply (wcur, xcur).
+  // After a wave's last unit the following batch re-reads the unit's first one (unused) so that
+  // the load count stays the same. Returns false once the wave is done.
+  auto step = [&](bf16x8_t* wcur, bf16x8_t* xcur, bf16x8_t* wnxt, bf16x8_t* xnxt) {
+    const bool last = b + 1 == nbat;
+    issue(cur, nxt, last && un >= 0, last ? 0 : b + 1, wnxt, xnxt);
+    if (last) mask(cur.K, b, wcur);
 #pragma unroll
-    for (int s = 0; s < NSW; ++s) {
-      const int tr = t0 + s * 16 + (lane & 15);
-      if (s < ns && tr < nrows && n < N) store_block(acc[s], out, ldo, row_begin + tr, n, sq);
+    for (int q = 0; q < U; ++q)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wcur[q], xcur[q], acc, 0, 0, 0);
+    if (!last) {
+      ++b;
+      return true;
     }
+    // unit done: acc[r] = out[token tr][n + r]; lanes holding a real token store
+    if (tr < cur.nrows && cur.n < cur.N) store_block(acc, cur.out, cur.ldo, cur.orow, cur.n, sq);
+    acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (un < 0) return false;
+    cur = nxt;
+    u = un;
+    b = 0;
+    nbat = nbat_of(cur.K);
+    un = u + nwaves < total ? u + nwaves : -1;
+    if (un >= 0) resolve(un, nxt);
+    return true;
+  };
+  issue(cur, cur, false, 0, w0, x0);
+  for (;;) {
+    if (!step(w0, x0, w1, x1)) break;
+    if (!step(w1, x1, w0, x0)) break;
   }
 }
 
-// A narrow unit resolved to this lane's pointers: 16 weight rows, up to 16 token rows.
-struct Narrow {
-  const uint16_t* w;   // this lane's weight row
-  const uint16_t* a;   // this lane's token row
-  int64_t orow;        // output row of this lane's token
-  int n;               // first of this lane's 4 output columns
-  int nrows, tr;       // tokens of the unit, this lane's token index
-  int nbat;            // load batches over K
-};
-
 __global__ __launch_bounds__(256, 1) void stream_kernel(StreamParams p) {
   const int lane = threadIdx.x & 63;
-  const bool sq = p.sqrelu_bf16;
-  const int nbr = cdiv(p.N, kUnitRows);
-
-  // ---- phase 1: wide units (shared expert blocks, then blocks of experts with > 16 tokens)
-  {
-    const int nbs = p.Ws ? cdiv(p.Ns, kUnitRows) : 0;
-    const int total = nbs + *p.n_wide * nbr;
-    for (;;) {
-      const int u = claim(p.counter, lane);
-      if (u >= total) break;  // every wave leaves once the list is exhausted
-      if (u < nbs) {
-        wide_unit(p.As, p.lda_s, nullptr, 0, p.Ts, p.Ws, p.Ns, p.Ks, u * kUnitRows, p.out_s,
-                  p.ldo_s, sq, lane);
-      } else {
-        const int v = u - nbs;
-        const int g = p.wide[v / nbr];
-        const int rb0 = p.offs[g];
-        wide_unit(p.A, p.lda, p.gather, rb0, p.offs[g + 1] - rb0, p.W + (int64_t)g * p.N * p.K,
-                  p.N, p.K, (v % nbr) * kUnitRows, p.out, p.ldo, sq, lane);
-      }
-    }
-  }
-
-  // ---- phase 2: narrow units, double-buffered loads with a one-unit lookahead
-  const int total = *p.n_narrow * nbr;
+  const int tr = lane & 15;
   const int kq = (lane >> 4) * 8;
-  auto resolve = [&](int u, Narrow& s) {
-    const int g = p.narrow[u / nbr];
-    const int n0 = (u % nbr) * kUnitRows;
-    const int rb0 = p.offs[g];
-    s.nrows = p.offs[g + 1] - rb0;
-    s.tr = lane & 15;
-    const int tr = min(s.tr, s.nrows - 1);
-    s.a = p.A + (int64_t)(p.gather ? p.gather[rb0 + tr] : rb0 + tr) * p.lda;
-    s.w = p.W + (int64_t)g * p.N * p.K + (int64_t)min(n0 + (lane & 15), p.N - 1) * p.K;
-    s.orow = rb0 + s.tr;
-    s.n = n0 + (lane >> 4) * 4;
-    s.nbat = cdiv(p.K, 32 * UN);
-  };
-  auto issue = [&](const Narrow& s, int b, bf16x8_t* wf, bf16x8_t* xf) {
-#pragma unroll
-    for (int q = 0; q < UN; ++q) {
-      const int kk = b * 32 * UN + q * 32 + kq;
-      const bool ok = kk < p.K;
-      wf[q] = ok ? ld16(s.w + kk) : bf16x8_t{};
-      xf[q] = ok ? ld16(s.a + kk) : bf16x8_t{};
-    }
-  };
+  const int nwaves = gridDim.x * 4;
+  // waves numbered die by die: consecutive numbers share a CU, then a die
+  const int wave = xcd_logical_block(blockIdx.x, gridDim.x) * 4 +
+                   __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  Narrow cur, nxt;
-  bf16x8_t wc[UN], xc[UN], wn[UN], xn[UN];
-  int u = claim(p.counter + 1, lane);
-  if (u >= total) return;
-  resolve(u, cur);
-  issue(cur, 0, wc, xc);
-  int b = 0;
-  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (;;) {
-    bool more = true, fresh = false;
-    if (b + 1 < cur.nbat) {
-      issue(cur, b + 1, wn, xn);
+  // units [0, nsh): the shared expert, block-major over its token slices;
+  // units [nsh, nsh + nrt): the routed experts, block-major over the dispatch slices
+  const int nss = p.Ws ? cdiv(p.Ts, kSliceRows) : 0;
+  const int nsh = nss ? cdiv(p.Ns, kUnitRows) * nss : 0;
+  const int nsl = sload(p.n_slices, 0);
+  const int nrt = cdiv(p.N, kUnitRows) * nsl;
+  auto resolve = [&](int u, Unit& s) {
+    int n0, src;
+    if (u < nsh) {
+      n0 = (u / nss) * kUnitRows;
+      const int r0 = (u % nss) * kSliceRows;
+      s.nrows = min(p.Ts - r0, kSliceRows);
+      s.orow = r0 + tr;
+      src = r0 + min(tr, s.nrows - 1);
+      s.a = p.As + (int64_t)src * p.lda_s + kq;
+      s.w = p.Ws + (int64_t)min(n0 + tr, p.Ns - 1) * p.Ks + kq;
+      s.out = p.out_s;
+      s.ldo = p.ldo_s;
+      s.N = p.Ns;
+      s.K = p.Ks;
     } else {
-      const int un = claim(p.counter + 1, lane);
-      if (un < total) {
-        resolve(un, nxt);
-        issue(nxt, 0, wn, xn);
-        fresh = true;
-      } else {
-        more = false;  // the list is exhausted: this is the wave's last batch
+      const int v = u - nsh;
+      const int i = v % nsl;
+      n0 = (v / nsl) * kUnitRows;
+      const int g = sload(p.slice_e, i);
+      const int r0 = sload(p.slice_r, i);
+      s.nrows = min(sload(p.offs, g + 1) - r0, kSliceRows);
+      s.orow = r0 + tr;
+      src = r0 + min(tr, s.nrows - 1);
+      if (p.gather) {
+        // the slice's token rows as scalar loads; each lane keeps its own
+        int row = 0;
+#pragma unroll
+        for (int j = 0; j < kSliceRows; ++j) {
+          const int r = sload(p.gather, r0 + min(j, s.nrows - 1));
+          if (tr == j) row = r;
+        }
+        src = row;
       }
+      s.a = p.A + (int64_t)src * p.lda + kq;
+      s.w = p.W + (int64_t)g * p.N * p.K + (int64_t)min(n0 + tr, p.N - 1) * p.K + kq;
+      s.out = p.out;
+      s.ldo = p.ldo;
+      s.N = p.N;
+      s.K = p.K;
     }
-#pragma unroll
-    for (int q = 0; q < UN; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wc[q], xc[q], acc, 0, 0, 0);
-    if (b + 1 == cur.nbat) {  // unit done: lanes holding a real token store their 4 columns
-      if (cur.tr < cur.nrows && cur.n < p.N) store_block(acc, p.out, p.ldo, cur.orow, cur.n, sq);
-      acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    if (!more) break;
-#pragma unroll
-    for (int q = 0; q < UN; ++q) {
-      wc[q] = wn[q];
-      xc[q] = xn[q];
-    }
-    if (fresh) {
-      cur = nxt;
-      b = 0;
-    } else {
-      ++b;
-    }
-  }
+    s.n = n0 + (lane >> 4) * 4;
+  };
+  const bool sq = p.sqrelu_bf16;
+  if (min(p.K, nss ? p.Ks : p.K) >= 32 * UN)
+    stream_units<UN, true>(wave, nsh + nrt, nwaves, lane, sq, resolve);
+  else
+    stream_units<UN, false>(wave, nsh + nrt, nwaves, lane, sq, resolve);
 }
 
 }  // namespace
 
 hipError_t launch_stream(const StreamParams& p, hipStream_t s) {
+  static_assert(kStreamWaves / 4 % kXcds == 0, "the wave numbering needs whole dies");
   hipLaunchKernelGGL(stream_kernel, dim3(kStreamWaves / 4), dim3(256), 0, s, p);
   return hipGetLastError();
 }
