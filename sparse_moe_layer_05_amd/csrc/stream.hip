@@ -7,9 +7,8 @@
 // (the shared expert's tokens are cut into slices the same way). All units cost about the same,
 // so a persistent grid of 1024 waves (one per SIMD) deals them out round robin: unit j goes to
 // wave j mod 1024, and no wave holds more than one unit more than any other. Waves are numbered
-// die by die and units ordered row block first, slice second, so the slices that share weight
-// rows run at the same time on neighbouring waves of one die: the weights come from HBM once
-// and from that die's L2 for the other slices.
+// die by die, so units with neighbouring numbers run at the same time on one die: the slices of
+// one expert that share weight rows take the rows from HBM once and from that die's L2 after.
 //
 // Loads are double buffered in registers with a one-unit lookahead: while a unit streams, the
 // next one is resolved, and its first k batch is in flight while the current unit's last batch
@@ -155,12 +154,15 @@ __global__ __launch_bounds__(256, 1) void stream_kernel(StreamParams p) {
   const int wave = xcd_logical_block(blockIdx.x, gridDim.x) * 4 +
                    __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  // units [0, nsh): the shared expert, block-major over its token slices;
-  // units [nsh, nsh + nrt): the routed experts, block-major over the dispatch slices
+  // units [0, nsh): the shared expert, row block major, its token slices minor (slices that
+  // share weight rows run side by side and share them through L2);
+  // units [nsh, nsh + nrt): the routed slices, slice major, row block minor (neighbouring waves
+  // stream neighbouring rows of one expert's matrix)
   const int nss = p.Ws ? cdiv(p.Ts, kSliceRows) : 0;
   const int nsh = nss ? cdiv(p.Ns, kUnitRows) * nss : 0;
   const int nsl = sload(p.n_slices, 0);
-  const int nrt = cdiv(p.N, kUnitRows) * nsl;
+  const int nbr = cdiv(p.N, kUnitRows);
+  const int nrt = nbr * nsl;
   auto resolve = [&](int u, Unit& s) {
     int n0, src;
     if (u < nsh) {
@@ -177,8 +179,8 @@ __global__ __launch_bounds__(256, 1) void stream_kernel(StreamParams p) {
       s.K = p.Ks;
     } else {
       const int v = u - nsh;
-      const int i = v % nsl;
-      n0 = (v / nsl) * kUnitRows;
+      const int i = v / nbr;
+      n0 = (v % nbr) * kUnitRows;
       const int g = sload(p.slice_e, i);
       const int r0 = sload(p.slice_r, i);
       s.nrows = min(sload(p.offs, g + 1) - r0, kSliceRows);
