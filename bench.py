@@ -195,15 +195,39 @@ def measure(w, moe, torch, steps, warmup, graph):
     else:
         bound, achieved = "mfma", flops / (kms * 1e-3) / 1e12
         peak, unit = PEAK_MFMA[dt] / 1e12, "TFLOP/s"
+    traffic = measured_traffic(cfg.name, dominant)
     roof = dict(bound=bound, achieved=round(achieved, 1), peak=peak, unit=unit,
-                frac=round(achieved / peak, 4), traffic=None, kernel=dominant,
+                frac=round(achieved / peak, 4), traffic=traffic, kernel=dominant,
                 launches=nlaunch, avg_launch_us=round(kms * 1e3 / max(nlaunch, 1), 2),
                 algorithmic_flops_per_launch=int(flops / max(nlaunch, 1)),
                 algorithmic_bytes_per_launch=int(bts / max(nlaunch, 1)))
+    if traffic:
+        roof["traffic_over_algorithmic_bytes"] = round(traffic / max(bts / max(nlaunch, 1), 1), 3)
     breakdown = {k_: round(v * 1e3 / 3, 2) for k_, v in sorted(per_kernel.items(),
                                                               key=lambda kv: -kv[1])}
     return dict(ms_per_step=ms_step, tokens_per_s=cfg.T / (ms_step * 1e-3), roofline=roof,
                 kernel_us_per_step=breakdown, touched_experts=int(np.count_nonzero(counts)))
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` on `workload` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE passes (profiles/traffic.json, copy-calibrated), or None when there is no entry or
+    the kernel's sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        ent = json.load(f)["entries"].get(f"{workload}/{kernel}")
+    if ent is None:
+        return None
+    h = hashlib.sha256()
+    for src in ent["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest()[:16] != ent["sha"]:
+        return None
+    return int(ent["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(w, n_tokens):
