@@ -16,6 +16,8 @@
 // The epilogue stages each wave's accumulators through LDS in 16-row strips so that every lane
 // finishes 8 consecutive columns of a row with 16-byte loads and stores.
 // fp32 layers use a vector-ALU kernel with the same parameters.
+#include <cmath>
+
 #include "common.hpp"
 #include "gemm.hpp"
 
@@ -424,12 +426,26 @@ hipError_t run_f32(const GemmParams& p, int mtiles, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Dense bf16 launch: 256 x 256 tiles on 8 waves when there are enough of them to fill the chip,
-// 128 x 128 tiles on 4 waves (two workgroups per CU) otherwise.
+// Dense bf16 launch. Candidate tiles (measured on the chip, random bf16 data): 256 x 256 on 4
+// waves (one workgroup per CU, the best per-tile rate), 128 x 192 and 128 x 128 on 4 waves (two
+// workgroups per CU). The estimate charges every round of resident workgroups in full, so it
+// picks the tile that wastes least of the last round.
 template <Elt OUT, Epi EPI>
 hipError_t run_dense_bf16(const GemmParams& p, hipStream_t s) {
-  if (p.ksplit == 1 && cdiv(p.M, 256) * cdiv(p.N, 256) >= 192)
-    return run_mfma<256, 256, 2, 4, 2, Elt::BF16, OUT, EPI>(p, cdiv(p.M, 256), s);
+  if (p.ksplit > 1) return run_mfma<128, 128, 2, 2, 2, Elt::BF16, OUT, EPI>(p, cdiv(p.M, 128), s);
+  struct Cand { int bm, bn, wg; double rate; };   // rate: relative throughput per CU
+  constexpr Cand cands[3] = {{256, 256, 1, 1.13}, {128, 192, 2, 1.01}, {128, 128, 2, 0.95}};
+  int best = 0;
+  double best_t = 1e300;
+  for (int i = 0; i < 3; ++i) {
+    const Cand& c = cands[i];
+    const double tiles = (double)cdiv(p.M, c.bm) * cdiv(p.N, c.bn);
+    const double rounds = std::ceil(tiles / (256.0 * c.wg));
+    const double t = rounds * c.wg * c.bm * c.bn / c.rate;
+    if (t < best_t) { best_t = t; best = i; }
+  }
+  if (best == 0) return run_mfma<256, 256, 2, 2, 2, Elt::BF16, OUT, EPI>(p, cdiv(p.M, 256), s);
+  if (best == 1) return run_mfma<128, 192, 2, 2, 2, Elt::BF16, OUT, EPI>(p, cdiv(p.M, 128), s);
   return run_mfma<128, 128, 2, 2, 2, Elt::BF16, OUT, EPI>(p, cdiv(p.M, 128), s);
 }
 
@@ -450,10 +466,11 @@ hipError_t launch_gemm(const GemmKind& k, const GemmParams& p, int max_mtiles, h
   constexpr int GB = kGroupBM;
   if (k.ab == Elt::BF16) {
     if (grouped) {
+      // 128 x 192 tiles on 4 waves, two workgroups per CU: the fastest routed shape measured
       if (k.out == Elt::BF16 && k.epi == Epi::SqRelu)
-        return run_mfma<GB, 256, 2, 4, 3, Elt::BF16, Elt::BF16, Epi::SqRelu>(p, max_mtiles, s);
+        return run_mfma<GB, 192, 2, 2, 2, Elt::BF16, Elt::BF16, Epi::SqRelu>(p, max_mtiles, s);
       if (k.out == Elt::BF16 && k.epi == Epi::Store)
-        return run_mfma<GB, 256, 2, 4, 3, Elt::BF16, Elt::BF16, Epi::Store>(p, max_mtiles, s);
+        return run_mfma<GB, 192, 2, 2, 2, Elt::BF16, Elt::BF16, Epi::Store>(p, max_mtiles, s);
       return hipErrorInvalidValue;
     }
     if (k.out == Elt::F32 && k.epi == Epi::Store) return run_dense_bf16<Elt::F32, Epi::Store>(p, s);
