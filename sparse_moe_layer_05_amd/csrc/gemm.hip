@@ -24,11 +24,15 @@
 namespace moe {
 namespace {
 
-constexpr int kSlab = 128;  // bytes of one row per K-step
-
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int slot(int row, int chunk) {
-  return row * kSlab + ((chunk ^ swz(row)) << 4);
+// A K-step stages SL bytes of every operand row (SL = 128 or 64). The 16-byte chunks of a row
+// are XOR-swizzled so that the fragment reads of 16 consecutive rows at one chunk index hit 16
+// distinct 16-byte bank groups: rows of 128 bytes swizzle by (row / 2) % 8, rows of 64 bytes by
+// (row / 4) % 4.
+template <int SL> __device__ __forceinline__ int swz(int row) {
+  return SL == 128 ? (row >> 1) & 7 : (row >> 2) & 3;
+}
+template <int SL> __device__ __forceinline__ int slot(int row, int chunk) {
+  return row * SL + ((chunk ^ swz<SL>(row)) << 4);
 }
 
 template <Elt E> struct EltBytes { static constexpr int v = E == Elt::F32 ? 4 : (E == Elt::BF16 ? 2 : 1); };
@@ -83,10 +87,11 @@ __device__ __forceinline__ void unpack8(const uint4 q, float* v) {
 // -------------------------------------------------------------------------------------------
 // Matrix-core kernel (bf16 or e4m3 operands, fp32 accumulation).
 // -------------------------------------------------------------------------------------------
-template <int BM, int BN, int WGM, int WGN, int NS, Elt AB, Elt OUT, Epi EPI>
+template <int BM, int BN, int WGM, int WGN, int NS, Elt AB, Elt OUT, Epi EPI, int SL = 128>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
   static_assert(AB == Elt::BF16 || AB == Elt::FP8, "matrix-core path");
   static_assert(NS >= 2, "at least double buffering");
+  static_assert(SL == 128 || SL == 64, "64- or 128-byte K-steps");
   if (p.ksplit > 1) {  // this workgroup's K slice (dense Store launches)
     const int k0 = blockIdx.y * p.kchunk;
     p.K = min(p.kchunk, p.K - k0);
@@ -97,8 +102,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
   constexpr int NW = WGM * WGN;
   constexpr int EB = EltBytes<AB>::v;
   constexpr int WM = BM / WGM, WN = BN / WGN, MB = WM / 32, NB = WN / 32;
-  constexpr int A_GRP = BM / (8 * NW), B_GRP = BN / (8 * NW);  // 1-KB groups per wave
-  constexpr int STAGE = (BM + BN) * kSlab;
+  constexpr int RPI = 1024 / SL, LPR = SL / 16;  // rows per 1-KB load, lanes per row
+  constexpr int A_GRP = BM / (RPI * NW), B_GRP = BN / (RPI * NW);  // 1-KB loads per wave
+  constexpr int STAGE = (BM + BN) * SL;
   constexpr int EPW = WN + 4;                                   // epilogue strip row (floats)
   static_assert(A_GRP >= 1 && B_GRP >= 1 && MB >= 1 && NB >= 1, "tile too small");
   static_assert(NW * 16 * EPW * 4 <= NS * STAGE, "epilogue strips must fit in the stages");
@@ -110,17 +116,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
-  const int lrow = lane >> 3, lpos = lane & 7;
+  const int lrow = lane / LPR, lpos = lane % LPR;
 
   // Per-lane global sources, as 32-bit byte offsets from wave-uniform bases. Lane (lrow, lpos)
-  // of 1-KB group q fills LDS row q*8 + lrow, slot lpos, which holds global chunk lpos ^ swz(row).
+  // of 1-KB group q fills LDS row q*RPI + lrow, slot lpos, which holds global chunk
+  // lpos ^ swz(row).
   const uint8_t* abase = (const uint8_t*)p.A;
   const uint8_t* bbase = (const uint8_t*)p.B + (int64_t)g * p.b_gstride * EB;
   uint32_t oa[A_GRP], ob[B_GRP];
-  // This lane's chunk byte offset. Its rows (wave + NW*i)*8 + lrow differ by multiples of 16
-  // across groups (NW is even) and swz has period 16, so one offset serves every group.
-  static_assert(NW % 2 == 0, "an even wave count keeps the swizzle constant across groups");
-  const int cofs = (lpos ^ swz(wave * 8 + lrow)) << 4;
+  // This lane's chunk byte offset. 128-byte rows: the lane's rows (wave + NW*i)*8 + lrow differ
+  // by multiples of 16 across groups (NW is even) and swz has period 16. 64-byte rows: swz of
+  // row q*16 + lrow depends on lrow only. Either way one offset serves every group.
+  static_assert(SL == 64 || NW % 2 == 0, "an even wave count keeps the swizzle constant");
+  const int cofs = (lpos ^ swz<SL>(wave * RPI + lrow)) << 4;
   auto set_sources = [&](bool seg2) {
     if (seg2) {
       abase = (const uint8_t*)p.A2;
@@ -128,7 +136,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
     }
 #pragma unroll
     for (int i = 0; i < A_GRP; ++i) {
-      const int r = (wave + NW * i) * 8 + lrow;
+      const int r = (wave + NW * i) * RPI + lrow;
       const int rr = r < rows ? r : 0;
       int64_t src = row0 + rr;
       if (!seg2 && p.a_gather) src = p.a_gather[row0 + rr];
@@ -136,21 +144,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
     }
 #pragma unroll
     for (int i = 0; i < B_GRP; ++i) {
-      const int r = (wave + NW * i) * 8 + lrow;
+      const int r = (wave + NW * i) * RPI + lrow;
       const int n = n0 + r < p.N ? n0 + r : p.N - 1;
       ob[i] = (uint32_t)((int64_t)n * (seg2 ? p.ldb2 : p.ldb) * EB);
     }
   };
 
   const int kb1 = p.K * EB, kb2 = p.K2 * EB;   // K bytes per segment
-  const int nk1 = cdiv(kb1, kSlab);
-  const int nk = nk1 + cdiv(kb2, kSlab);
+  const int nk1 = cdiv(kb1, SL);
+  const int nk = nk1 + cdiv(kb2, SL);
   // Bytes of K-step ks that lie inside K when the step is partial, else 0.
   auto tail_of = [&](int ks) {
     const bool seg2 = ks >= nk1;
-    const int kb = (seg2 ? ks - nk1 : ks) * kSlab;
+    const int kb = (seg2 ? ks - nk1 : ks) * SL;
     const int klim = seg2 ? kb2 : kb1;
-    return kb + kSlab <= klim ? 0 : klim - kb;
+    return kb + SL <= klim ? 0 : klim - kb;
   };
 
   // Issue the loads of K-step ks into stage `st`, straight to LDS. Lanes whose chunk lies beyond
@@ -158,7 +166,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
   auto issue = [&](int ks, uint8_t* st) {
     const bool seg2 = ks >= nk1;
     if (ks == nk1 && nk1 > 0 && kb2 > 0) set_sources(true);
-    const int kb = (seg2 ? ks - nk1 : ks) * kSlab;
+    const int kb = (seg2 ? ks - nk1 : ks) * SL;
     const int klim = seg2 ? kb2 : kb1;
     const int cuse = (kb + cofs < klim) ? cofs : 0;
 #pragma unroll
@@ -166,7 +174,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
       __builtin_amdgcn_global_load_lds(
           (const void*)(abase + oa[i] + kb + cuse),
           (__attribute__((address_space(3))) void*)(st + (wave + NW * i) * 1024), 16, 0, 0);
-    uint8_t* sb = st + BM * kSlab;
+    uint8_t* sb = st + BM * SL;
 #pragma unroll
     for (int i = 0; i < B_GRP; ++i)
       __builtin_amdgcn_global_load_lds(
@@ -184,7 +192,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
         *(uint4*)(st + (wave + NW * i) * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < B_GRP; ++i)
-        *(uint4*)(st + BM * kSlab + (wave + NW * i) * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+        *(uint4*)(st + BM * SL + (wave + NW * i) * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
     }
     __syncthreads();
   };
@@ -201,20 +209,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
   // of k-sub s issue; scheduling fences keep the compiler from hoisting further reads (which
   // would only add registers).
   auto compute = [&](const uint8_t* As) {
-    const uint8_t* Bs = As + BM * kSlab;
+    const uint8_t* Bs = As + BM * SL;
     if constexpr (AB == Elt::BF16) {
       bf16x8_t a[2][MB], b[2][NB];
       auto rd = [&](int s, int buf) {
         const int ch = 2 * s + (lane >> 5);
 #pragma unroll
-        for (int i = 0; i < MB; ++i) a[buf][i] = *(const bf16x8_t*)(As + slot(wm * WM + i * 32 + (lane & 31), ch));
+        for (int i = 0; i < MB; ++i) a[buf][i] = *(const bf16x8_t*)(As + slot<SL>(wm * WM + i * 32 + (lane & 31), ch));
 #pragma unroll
-        for (int j = 0; j < NB; ++j) b[buf][j] = *(const bf16x8_t*)(Bs + slot(wn * WN + j * 32 + (lane & 31), ch));
+        for (int j = 0; j < NB; ++j) b[buf][j] = *(const bf16x8_t*)(Bs + slot<SL>(wn * WN + j * 32 + (lane & 31), ch));
       };
       rd(0, 0);
+      constexpr int NSUB = SL / 32;  // 16-element k-subs per K-step
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (s < 3) rd(s + 1, (s + 1) & 1);
+      for (int s = 0; s < NSUB; ++s) {
+        if (s < NSUB - 1) rd(s + 1, (s + 1) & 1);
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -229,22 +238,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
           const int r = wm * WM + i * 32 + (lane & 31);
-          const i32x4_t lo = *(const i32x4_t*)(As + slot(r, ch));
-          const i32x4_t hi = *(const i32x4_t*)(As + slot(r, ch + 1));
+          const i32x4_t lo = *(const i32x4_t*)(As + slot<SL>(r, ch));
+          const i32x4_t hi = *(const i32x4_t*)(As + slot<SL>(r, ch + 1));
           a[buf][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           const int r = wn * WN + j * 32 + (lane & 31);
-          const i32x4_t lo = *(const i32x4_t*)(Bs + slot(r, ch));
-          const i32x4_t hi = *(const i32x4_t*)(Bs + slot(r, ch + 1));
+          const i32x4_t lo = *(const i32x4_t*)(Bs + slot<SL>(r, ch));
+          const i32x4_t hi = *(const i32x4_t*)(Bs + slot<SL>(r, ch + 1));
           b[buf][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
       };
       rd(0, 0);
+      constexpr int NSUB = SL / 64;  // 64-element k-subs per K-step
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        if (s < 1) rd(s + 1, (s + 1) & 1);
+      for (int s = 0; s < NSUB; ++s) {
+        if (s < NSUB - 1) rd(s + 1, (s + 1) & 1);
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -407,12 +417,12 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmParams p) {
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int NS, Elt AB, Elt OUT, Epi EPI>
+template <int BM, int BN, int WGM, int WGN, int NS, Elt AB, Elt OUT, Epi EPI, int SL = 128>
 hipError_t run_mfma(const GemmParams& p, int mtiles, hipStream_t s) {
   const int tiles = mtiles * cdiv(p.N, BN);
   if (tiles <= 0) return hipSuccess;
   const int grid = cdiv(tiles, kXcds) * kXcds;
-  hipLaunchKernelGGL((gemm_mfma<BM, BN, WGM, WGN, NS, AB, OUT, EPI>), dim3(grid, p.ksplit),
+  hipLaunchKernelGGL((gemm_mfma<BM, BN, WGM, WGN, NS, AB, OUT, EPI, SL>), dim3(grid, p.ksplit),
                      dim3(64 * WGM * WGN), 0, s, p);
   return hipGetLastError();
 }
@@ -479,10 +489,11 @@ hipError_t launch_gemm(const GemmKind& k, const GemmParams& p, int max_mtiles, h
     return hipErrorInvalidValue;
   }
   if (k.ab == Elt::FP8 && grouped && k.out == Elt::BF16) {
+    // the same 128 x 192 / 4-wave shape measured fastest for e4m3 as for bf16
     if (k.epi == Epi::SqRelu)
-      return run_mfma<GB, 256, 2, 4, 3, Elt::FP8, Elt::BF16, Epi::SqRelu>(p, max_mtiles, s);
+      return run_mfma<GB, 192, 2, 2, 2, Elt::FP8, Elt::BF16, Epi::SqRelu>(p, max_mtiles, s);
     if (k.epi == Epi::Store)
-      return run_mfma<GB, 256, 2, 4, 3, Elt::FP8, Elt::BF16, Epi::Store>(p, max_mtiles, s);
+      return run_mfma<GB, 192, 2, 2, 2, Elt::FP8, Elt::BF16, Epi::Store>(p, max_mtiles, s);
   }
   return hipErrorInvalidValue;
 }
