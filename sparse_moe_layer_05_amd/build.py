@@ -44,7 +44,10 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(len(SOURCES)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = OUT + f".tmp{os.getpid()}"
-    res = subprocess.run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp],
+    # -z defs: every symbol must resolve at link time (a kernel whose host stub failed to
+    # instantiate would otherwise only surface when the library is loaded or called)
+    res = subprocess.run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-Wl,-z,defs", *objs,
+                          "-o", tmp],
                          capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")

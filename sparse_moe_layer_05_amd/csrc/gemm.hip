@@ -4,15 +4,16 @@
 //
 // bf16 / e4m3 tiles run on the matrix cores (v_mfma_f32_32x32x16_bf16,
 // v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales). A workgroup of WGM x WGN waves owns a
-// BM x BN output tile. Each K-step stages a 128-byte slab of every A and B row in LDS (64 bf16
-// or 128 e4m3 values). Slabs are filled
-// by global_load_lds_dwordx4 (global memory straight to LDS, no register staging): one
-// instruction fills 8 rows x 128 bytes, lane l landing at byte 16*l. The 16-byte chunk order
-// inside a row is XOR-swizzled by (row / 2) % 8 by choosing which global chunk each lane
-// fetches, so the fragment reads of 16 consecutive rows touch 16 distinct 16-byte bank groups.
-// In a final partial K-step, lanes whose chunk lies beyond K fetch an in-row chunk and their
-// slots are zeroed once the stage has landed. NS stages are in flight: K-step ks + NS - 1 is
-// loaded while K-step ks is multiplied.
+// BM x BN output tile. Each K-step stages an SL-byte slab of every A and B row in LDS (SL = 128:
+// 64 bf16 or 128 e4m3 values). Slabs are filled by buffer_load_dwordx4 ... lds (global memory
+// straight to LDS, no register staging): one instruction fills 1 KB (8 rows x 128 bytes), lane l
+// landing at byte 16*l. Operands are addressed through buffer resources that span exactly their
+// extent: a per-lane 32-bit row offset plus the K-step offset as a scalar. The 16-byte chunk
+// order inside a row is XOR-swizzled by choosing which global chunk each lane fetches, so the
+// fragment reads of 16 consecutive rows touch 16 distinct 16-byte bank groups. In a final
+// partial K-step, lanes whose chunk lies beyond K skip the access and their slots are zeroed
+// once the stage has landed. NS stages are in flight: K-step ks + NS - 1 is loaded while K-step
+// ks is multiplied.
 // The epilogue stages each wave's accumulators through LDS in 16-row strips so that every lane
 // finishes 8 consecutive columns of a row with 16-byte loads and stores.
 // fp32 layers use a vector-ALU kernel with the same parameters.
@@ -33,6 +34,13 @@ template <int SL> __device__ __forceinline__ int swz(int row) {
 }
 template <int SL> __device__ __forceinline__ int slot(int row, int chunk) {
   return row * SL + ((chunk ^ swz<SL>(row)) << 4);
+}
+
+// A raw buffer resource over [base, base + bytes): loads at per-lane offsets beyond it return
+// zeros without touching memory. bytes is clamped to the 32-bit range of the descriptor.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(uint32_t)n, 0x00020000);
 }
 
 template <Elt E> struct EltBytes { static constexpr int v = E == Elt::F32 ? 4 : (E == Elt::BF16 ? 2 : 1); };
@@ -92,11 +100,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
   static_assert(AB == Elt::BF16 || AB == Elt::FP8, "matrix-core path");
   static_assert(NS >= 2, "at least double buffering");
   static_assert(SL == 128 || SL == 64, "64- or 128-byte K-steps");
+  int64_t kshift = 0;  // bytes the operand bases moved by for a K slice
   if (p.ksplit > 1) {  // this workgroup's K slice (dense Store launches)
     const int k0 = blockIdx.y * p.kchunk;
     p.K = min(p.kchunk, p.K - k0);
-    p.A = (const uint8_t*)p.A + (int64_t)k0 * EltBytes<AB>::v;
-    p.B = (const uint8_t*)p.B + (int64_t)k0 * EltBytes<AB>::v;
+    kshift = (int64_t)k0 * EltBytes<AB>::v;
+    p.A = (const uint8_t*)p.A + kshift;
+    p.B = (const uint8_t*)p.B + kshift;
     p.C = (uint8_t*)p.C + (int64_t)blockIdx.y * p.M * p.ldc * EltBytes<OUT>::v;
   }
   constexpr int NW = WGM * WGN;
@@ -114,15 +124,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
   int g, row0, rows, n0;
   if (!tile_of<BM, BN>(p, g, row0, rows, n0)) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
   const int lrow = lane / LPR, lpos = lane % LPR;
 
-  // Per-lane global sources, as 32-bit byte offsets from wave-uniform bases. Lane (lrow, lpos)
-  // of 1-KB group q fills LDS row q*RPI + lrow, slot lpos, which holds global chunk
-  // lpos ^ swz(row).
-  const uint8_t* abase = (const uint8_t*)p.A;
-  const uint8_t* bbase = (const uint8_t*)p.B + (int64_t)g * p.b_gstride * EB;
+  // Operands are read through buffer resources that span exactly their extent in memory, so a
+  // read past the end returns zeros instead of touching other memory. Per lane a 32-bit byte
+  // offset (row start + this lane's chunk); the K-step offset is a scalar added by the load.
+  // Lane (lrow, lpos) of 1-KB group q fills LDS row q*RPI + lrow, slot lpos, which holds global
+  // chunk lpos ^ swz(row).
+  __amdgpu_buffer_rsrc_t ra = rsrc(p.A, (int64_t)p.a_rows * p.lda * EB - kshift);
+  __amdgpu_buffer_rsrc_t rb = rsrc((const uint8_t*)p.B + (int64_t)g * p.b_gstride * EB,
+                                   (int64_t)p.N * p.ldb * EB - kshift);
   uint32_t oa[A_GRP], ob[B_GRP];
   // This lane's chunk byte offset. 128-byte rows: the lane's rows (wave + NW*i)*8 + lrow differ
   // by multiples of 16 across groups (NW is even) and swz has period 16. 64-byte rows: swz of
@@ -131,8 +145,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
   const int cofs = (lpos ^ swz<SL>(wave * RPI + lrow)) << 4;
   auto set_sources = [&](bool seg2) {
     if (seg2) {
-      abase = (const uint8_t*)p.A2;
-      bbase = (const uint8_t*)p.B2;
+      ra = rsrc(p.A2, (int64_t)p.a2_rows * p.lda2 * EB);
+      rb = rsrc(p.B2, (int64_t)p.N * p.ldb2 * EB);
     }
 #pragma unroll
     for (int i = 0; i < A_GRP; ++i) {
@@ -140,13 +154,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
       const int rr = r < rows ? r : 0;
       int64_t src = row0 + rr;
       if (!seg2 && p.a_gather) src = p.a_gather[row0 + rr];
-      oa[i] = (uint32_t)(src * (seg2 ? p.lda2 : p.lda) * EB);
+      oa[i] = (uint32_t)(src * (seg2 ? p.lda2 : p.lda) * EB) + cofs;
     }
 #pragma unroll
     for (int i = 0; i < B_GRP; ++i) {
       const int r = (wave + NW * i) * RPI + lrow;
       const int n = n0 + r < p.N ? n0 + r : p.N - 1;
-      ob[i] = (uint32_t)((int64_t)n * (seg2 ? p.ldb2 : p.ldb) * EB);
+      ob[i] = (uint32_t)((int64_t)n * (seg2 ? p.ldb2 : p.ldb) * EB) + cofs;
     }
   };
 
@@ -161,25 +175,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
     return kb + SL <= klim ? 0 : klim - kb;
   };
 
-  // Issue the loads of K-step ks into stage `st`, straight to LDS. Lanes whose chunk lies beyond
-  // K fetch chunk 0 of the same row instead; fix_tail() zeroes those slots once they landed.
+  // Issue the loads of K-step ks into stage `st`, straight to LDS. In a partial K-step, lanes
+  // whose chunk lies beyond K take a per-lane offset outside the buffer (the hardware range
+  // check then skips the access); fix_tail() zeroes their slots once the stage has landed.
   auto issue = [&](int ks, uint8_t* st) {
     const bool seg2 = ks >= nk1;
     if (ks == nk1 && nk1 > 0 && kb2 > 0) set_sources(true);
     const int kb = (seg2 ? ks - nk1 : ks) * SL;
-    const int klim = seg2 ? kb2 : kb1;
-    const int cuse = (kb + cofs < klim) ? cofs : 0;
-#pragma unroll
-    for (int i = 0; i < A_GRP; ++i)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(abase + oa[i] + kb + cuse),
-          (__attribute__((address_space(3))) void*)(st + (wave + NW * i) * 1024), 16, 0, 0);
+    const int tl = tail_of(ks);
+    const bool live = tl == 0 || cofs < tl;
     uint8_t* sb = st + BM * SL;
 #pragma unroll
+    for (int i = 0; i < A_GRP; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (__attribute__((address_space(3))) void*)(st + (wave + NW * i) * 1024), 16,
+          (int)(live ? oa[i] : 0xFFFFFFF0u), kb, 0, 0);
+#pragma unroll
     for (int i = 0; i < B_GRP; ++i)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(bbase + ob[i] + kb + cuse),
-          (__attribute__((address_space(3))) void*)(sb + (wave + NW * i) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, (__attribute__((address_space(3))) void*)(sb + (wave + NW * i) * 1024), 16,
+          (int)(live ? ob[i] : 0xFFFFFFF0u), kb, 0, 0);
   };
 
   // Zero the slots of a partial K-step that lie beyond K (after the stage has landed).
@@ -436,22 +451,21 @@ hipError_t run_f32(const GemmParams& p, int mtiles, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Dense bf16 launch. Candidate tiles (measured on the chip, random bf16 data): 256 x 256 on 4
-// waves (one workgroup per CU, the best per-tile rate), 128 x 192 and 128 x 128 on 4 waves (two
-// workgroups per CU). The estimate charges every round of resident workgroups in full, so it
-// picks the tile that wastes least of the last round.
+// Dense bf16 launch. Candidate tiles (rates measured on the chip with random bf16 data):
+// 256 x 256 on 4 waves (one workgroup per CU), 128 x 192 and 128 x 128 on 4 waves (two
+// workgroups per CU). The estimate charges each CU for the whole tiles it receives, so it picks
+// the tile that balances best over the 256 CUs.
 template <Elt OUT, Epi EPI>
 hipError_t run_dense_bf16(const GemmParams& p, hipStream_t s) {
   if (p.ksplit > 1) return run_mfma<128, 128, 2, 2, 2, Elt::BF16, OUT, EPI>(p, cdiv(p.M, 128), s);
-  struct Cand { int bm, bn, wg; double rate; };   // rate: relative throughput per CU
-  constexpr Cand cands[3] = {{256, 256, 1, 1.13}, {128, 192, 2, 1.01}, {128, 128, 2, 0.95}};
+  struct Cand { int bm, bn; double rate; };   // rate: relative throughput per CU
+  constexpr Cand cands[3] = {{256, 256, 1.03}, {128, 192, 1.0}, {128, 128, 0.94}};
   int best = 0;
   double best_t = 1e300;
   for (int i = 0; i < 3; ++i) {
     const Cand& c = cands[i];
     const double tiles = (double)cdiv(p.M, c.bm) * cdiv(p.N, c.bn);
-    const double rounds = std::ceil(tiles / (256.0 * c.wg));
-    const double t = rounds * c.wg * c.bm * c.bn / c.rate;
+    const double t = std::ceil(tiles / 256.0) * c.bm * c.bn / c.rate;
     if (t < best_t) { best_t = t; best = i; }
   }
   if (best == 0) return run_mfma<256, 256, 2, 2, 2, Elt::BF16, OUT, EPI>(p, cdiv(p.M, 256), s);

@@ -22,6 +22,7 @@ struct GemmParams {
   // set, else offs[g] + r.
   const void* A = nullptr;
   int64_t lda = 0;  // elements
+  int a_rows = 0;   // rows of A that may be read (the extent of the operand in memory)
   const int32_t* a_gather = nullptr;
   const float* a_scale = nullptr;  // e4m3 A: dequantisation scale per *source* row
   // B operand: [G][N][K], b_gstride elements between experts; fp8: per-channel scales [G][N]
@@ -32,6 +33,7 @@ struct GemmParams {
   // Optional second K segment for dense launches: acc += A2[m, :] . B2[n, :]
   const void* A2 = nullptr;
   int64_t lda2 = 0;
+  int a2_rows = 0;
   const void* B2 = nullptr;
   int64_t ldb2 = 0;
   int K2 = 0;

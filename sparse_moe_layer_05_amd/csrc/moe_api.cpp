@@ -144,9 +144,9 @@ hipError_t dense(Elt ab, Elt out, Epi epi, const void* A, int64_t lda, const voi
                  const void* A2 = nullptr, int64_t lda2 = 0, const void* B2 = nullptr,
                  int64_t ldb2 = 0, int K2 = 0) {
   GemmParams g;
-  g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc;
+  g.A = A; g.lda = lda; g.a_rows = M; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc;
   g.M = M; g.N = N; g.K = K;
-  g.A2 = A2; g.lda2 = lda2; g.B2 = B2; g.ldb2 = ldb2; g.K2 = K2;
+  g.A2 = A2; g.lda2 = lda2; g.a2_rows = M; g.B2 = B2; g.ldb2 = ldb2; g.K2 = K2;
   return launch_gemm(GemmKind{ab, out, epi}, g, 0, s);
 }
 
@@ -199,7 +199,7 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
     {
       MOE_SPAN(act == Elt::F32 ? "gemm_f32_store:router" : "gemm_bf16_f32out:router");
       GemmParams g;
-      g.A = w->x; g.lda = H; g.B = w->W_r; g.ldb = H; g.C = zsrc; g.ldc = E;
+      g.A = w->x; g.lda = H; g.a_rows = T; g.B = w->W_r; g.ldb = H; g.C = zsrc; g.ldc = E;
       g.M = T; g.N = E; g.K = H; g.ksplit = pl.nsplit; g.kchunk = pl.kchunk;
       MOE_TRY(launch_gemm(GemmKind{act, Elt::F32, Epi::Store}, g, 0, s));
     }
@@ -267,12 +267,12 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
   } else {
     const int max_mt = max_group_mtiles(P, E, pl.bm);
     GemmParams up;
-    up.lda = D; up.a_gather = perm;
+    up.lda = D; up.a_rows = T; up.a_gather = perm;
     up.B = w->W_up; up.ldb = D; up.b_gstride = (int64_t)I * D;
     up.C = h; up.ldc = I; up.N = I; up.K = D;
     up.offs = offsets; up.mt_start = mt_start; up.G = E;
     GemmParams dn;
-    dn.A = h; dn.lda = I;
+    dn.A = h; dn.lda = I; dn.a_rows = P;
     dn.B = w->W_down; dn.ldb = I; dn.b_gstride = (int64_t)D * I;
     dn.C = Y; dn.ldc = D; dn.N = D; dn.K = I;
     dn.offs = offsets; dn.mt_start = mt_start; dn.G = E;
