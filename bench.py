@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="nano_decode_bf16")
-    ap.add_argument("--also", default="nano_prefill_bf16",
+    ap.add_argument("--also", default="nano_prefill_bf16,latent_decode_bf16",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--path", default="auto", choices=["auto", "grouped", "stream"])
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured graph")

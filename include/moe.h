@@ -140,6 +140,17 @@ int32_t moe_dispatch(const int32_t *idx, int32_t T, int32_t E, int32_t k, int32_
                      void *stream);
 
 /* Static text for a status code. */
+/* Aux-loss-free load balancing step ("Nemotron 3 Nano：開放高效的 MoE 混合 Mamba-Transformer
+ * 智能體推理模型", section 2.2, training hyper-parameters: DeepSeek's auxiliary-loss-free
+ * balancing). The routing bias of every expert moves by a fixed step toward its target load:
+ *   b[e] <- fp32(b[e] + gamma * sign(target[e] - counts[e]))        (sign(0) = 0)
+ * counts [E] int32 (device): pairs routed to each expert, e.g. moe_routing_t.counts of a forward
+ * call. target [E] fp32 (device) or NULL for the mean load sum(counts) / E (compared exactly in
+ * integers). b [E] fp32 (device) is updated in place. Only the bias changes: gates never use it.
+ * Errors: MOE_ERR_INVALID_ARG for E < 1 or a NULL counts / b. Asynchronous on `stream`. */
+int32_t moe_bias_update(const int32_t *counts, const float *target, int32_t E, float gamma,
+                        float *b, void *stream);
+
 const char *moe_status_str(int32_t code);
 
 /* ---- Diagnostics: per-launch timing with HIP events (process-wide; not for concurrent calls).

@@ -4,8 +4,8 @@ The layer runs in hand-written HIP kernels behind the C ABI declared in include/
 (libmoe_mi355x.so, built in-tree by ``python -m sparse_moe_layer_05_amd.build``). This package
 is its thin Python binding: torch provides device memory and streams.
 """
-from .binding import (Layer, MoeError, alloc_routing, dispatch, layer_forward, layer_from, lib,
-                      route, status_str, to_device, workspace_size)
+from .binding import (Layer, MoeError, alloc_routing, bias_update, dispatch, layer_forward,
+                      layer_from, lib, route, status_str, to_device, workspace_size)
 
-__all__ = ["Layer", "MoeError", "alloc_routing", "dispatch", "layer_forward", "layer_from", "lib",
-           "route", "status_str", "to_device", "workspace_size"]
+__all__ = ["Layer", "MoeError", "alloc_routing", "bias_update", "dispatch", "layer_forward",
+           "layer_from", "lib", "route", "status_str", "to_device", "workspace_size"]

@@ -20,7 +20,8 @@ PATH_AUTO, PATH_GROUPED, PATH_STREAM, ROUTING_GIVEN = 0, 1, 2, 4
 _PATHS = {"auto": PATH_AUTO, "grouped": PATH_GROUPED, "stream": PATH_STREAM}
 
 EXPORTS = ("moe_workspace_size", "moe_layer_forward", "latent_moe_forward", "moe_route",
-           "moe_dispatch_workspace_size", "moe_dispatch", "moe_status_str", "moe_trace_enable",
+           "moe_dispatch_workspace_size", "moe_dispatch", "moe_bias_update", "moe_status_str",
+           "moe_trace_enable",
            "moe_trace_count", "moe_trace_read", "moe_trace_reset")
 
 
@@ -67,6 +68,7 @@ def lib() -> C.CDLL:
             L.moe_route.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
             L.moe_dispatch_workspace_size.argtypes = [i32, i32, i32, C.POINTER(sz)]
             L.moe_dispatch.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+            L.moe_bias_update.argtypes = [vp, vp, i32, C.c_float, vp, vp]
             L.moe_status_str.argtypes = [i32]
             L.moe_trace_enable.argtypes = [i32, C.c_char_p]
             L.moe_trace_count.argtypes = []
@@ -213,6 +215,14 @@ def dispatch(idx, E, stream=None):
                             n.value, _stream(stream))
     _check(rc, "moe_dispatch")
     return counts, offsets, perm, pos
+
+
+def bias_update(counts, b, gamma: float, target=None, stream=None) -> None:
+    """In place: b[e] += gamma * sign(target[e] - counts[e]) (target None: the mean load)."""
+    E = b.numel()
+    rc = lib().moe_bias_update(_p(counts), _p(target) if target is not None else None, E,
+                               float(gamma), _p(b), _stream(stream))
+    _check(rc, "moe_bias_update")
 
 
 def trace_enable(capacity: int, prefix: str = "") -> None:

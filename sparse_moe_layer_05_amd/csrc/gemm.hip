@@ -183,18 +183,31 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
     if (ks == nk1 && nk1 > 0 && kb2 > 0) set_sources(true);
     const int kb = (seg2 ? ks - nk1 : ks) * SL;
     const int tl = tail_of(ks);
-    const bool live = tl == 0 || cofs < tl;
     uint8_t* sb = st + BM * SL;
+    if (tl == 0) {  // every K-step but a partial last one (uniform branch)
 #pragma unroll
-    for (int i = 0; i < A_GRP; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (__attribute__((address_space(3))) void*)(st + (wave + NW * i) * 1024), 16,
-          (int)(live ? oa[i] : 0xFFFFFFF0u), kb, 0, 0);
+      for (int i = 0; i < A_GRP; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (__attribute__((address_space(3))) void*)(st + (wave + NW * i) * 1024), 16,
+            (int)oa[i], kb, 0, 0);
 #pragma unroll
-    for (int i = 0; i < B_GRP; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb, (__attribute__((address_space(3))) void*)(sb + (wave + NW * i) * 1024), 16,
-          (int)(live ? ob[i] : 0xFFFFFFF0u), kb, 0, 0);
+      for (int i = 0; i < B_GRP; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (__attribute__((address_space(3))) void*)(sb + (wave + NW * i) * 1024), 16,
+            (int)ob[i], kb, 0, 0);
+    } else {
+      const bool live = cofs < tl;
+#pragma unroll
+      for (int i = 0; i < A_GRP; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (__attribute__((address_space(3))) void*)(st + (wave + NW * i) * 1024), 16,
+            (int)(live ? oa[i] : 0xFFFFFFF0u), kb, 0, 0);
+#pragma unroll
+      for (int i = 0; i < B_GRP; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (__attribute__((address_space(3))) void*)(sb + (wave + NW * i) * 1024), 16,
+            (int)(live ? ob[i] : 0xFFFFFFF0u), kb, 0, 0);
+    }
   };
 
   // Zero the slots of a partial K-step that lie beyond K (after the stage has landed).

@@ -58,6 +58,13 @@ hipError_t launch_combine(const void* Y, Elt y_elt, int64_t ldy, const float* S,
 hipError_t launch_quant_rows(const uint16_t* x, int64_t ldx, int T, int H, uint8_t* q,
                              float* scale, hipStream_t s);
 
+// Aux-loss-free bias step: b[e] += gamma * sign(target[e] - counts[e]) in fp32; target NULL means
+// the mean load, compared exactly as sign(sum(counts) - E * counts[e]).
+hipError_t launch_bias_update(const int32_t* counts, const float* target, int E, float gamma,
+                              float* b, hipStream_t s);
+
+enum StreamStore : int { kStoreF32 = 0, kStoreSqRelu = 1, kStoreBF16 = 2 };
+
 // Decode path: every routed group g (expert) with rows offs[g] .. offs[g+1] and, optionally, the
 // shared expert (rows 0 .. Ts-1 of As) stream their weight matrix [N][K] from HBM exactly once:
 //   out[r, n] = act( sum_k A[src(r), k] * W[g][n, k] )
@@ -80,8 +87,10 @@ struct StreamParams {
   int Ns = 0, Ks = 0, Ts = 0;
   void* out_s = nullptr;
   int64_t ldo_s = 0;
-  int sqrelu_bf16 = 0;                // 1: bf16(relu(acc)^2); 0: fp32 acc
-  // slices of the routed experts from the dispatch step (see DispatchExtras)
+  int store = 0;                      // kStoreF32: fp32 acc; kStoreSqRelu: bf16(relu(acc)^2);
+                                      // kStoreBF16: bf16(acc)
+  // slices of the routed experts from the dispatch step (see DispatchExtras); n_slices NULL:
+  // no routed units (a dense weight-streaming product through the shared slot alone)
   const int32_t* slice_e = nullptr;
   const int32_t* slice_r = nullptr;
   const int32_t* n_slices = nullptr;

@@ -150,6 +150,17 @@ hipError_t dense(Elt ab, Elt out, Epi epi, const void* A, int64_t lda, const voi
   return launch_gemm(GemmKind{ab, out, epi}, g, 0, s);
 }
 
+// Dense bf16 product with few rows, out[t, n] = A[t, :] . W[n, :] for t < T, through the
+// weight-streaming kernel (its shared-expert slot alone): W is read from HBM once, spread over
+// every SIMD, where a tiled GEMM would leave most CUs idle at this M.
+hipError_t stream_dense(const void* A, int64_t lda, const void* W, int N, int K, int T, void* out,
+                        int64_t ldo, int store, hipStream_t s) {
+  StreamParams p;
+  p.As = (const uint16_t*)A; p.lda_s = lda; p.Ws = (const uint16_t*)W; p.Ns = N; p.Ks = K;
+  p.Ts = T; p.out_s = out; p.ldo_s = ldo; p.store = store;
+  return launch_stream(p, s);
+}
+
 int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, size_t ws_bytes,
                 moe_routing_t* r, void* stream, bool latent_call) {
   Plan pl;
@@ -227,7 +238,10 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
   const void* xin = w->x;
   if (L) {
     void* xl = base + pl.xl;
-    {
+    if (stream_path) {
+      MOE_SPAN("stream:latent_in");
+      MOE_TRY(stream_dense(w->x, H, w->W_in, L, H, T, xl, L, kStoreBF16, s));
+    } else {
       MOE_SPAN(act == Elt::F32 ? "gemm_f32_store:latent_in" : "gemm_bf16_store:latent_in");
       MOE_TRY(dense(act, act, Epi::Store, w->x, H, w->W_in, H, xl, L, T, L, H, s));
     }
@@ -245,7 +259,7 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
       up.As = (const uint16_t*)w->x; up.lda_s = H; up.Ws = (const uint16_t*)w->Ws_up;
       up.Ns = Is; up.Ks = H; up.Ts = T; up.out_s = hs; up.ldo_s = Is;
     }
-    up.sqrelu_bf16 = 1;
+    up.store = kStoreSqRelu;
     up.slice_e = slices; up.slice_r = slices + max_sl; up.n_slices = slices + 2 * max_sl;
     {
       MOE_SPAN("stream:up");
@@ -258,7 +272,7 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
       dn.As = (const uint16_t*)hs; dn.lda_s = Is; dn.Ws = (const uint16_t*)w->Ws_down;
       dn.Ns = H; dn.Ks = Is; dn.Ts = T; dn.out_s = (float*)Y + (size_t)P * D; dn.ldo_s = D;
     }
-    dn.sqrelu_bf16 = 0;
+    dn.store = kStoreF32;
     dn.slice_e = slices; dn.slice_r = slices + max_sl; dn.n_slices = slices + 2 * max_sl;
     {
       MOE_SPAN("stream:down");
@@ -347,6 +361,9 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
       MOE_SPAN(act == Elt::F32 ? "gemm_f32_store:latent_out" : "gemm_bf16_store:latent_out");
       MOE_TRY(dense(act, act, Epi::Store, z, L, w->W_out, L, y, H, T, H, L, s, hs, Is,
                     w->Ws_down, Is, Is));
+    } else if (stream_path) {
+      MOE_SPAN("stream:latent_out");
+      MOE_TRY(stream_dense(z, L, w->W_out, H, L, T, y, H, kStoreBF16, s));
     } else {
       MOE_SPAN(act == Elt::F32 ? "gemm_f32_store:latent_out" : "gemm_bf16_store:latent_out");
       MOE_TRY(dense(act, act, Epi::Store, z, L, w->W_out, L, y, H, T, H, L, s));
@@ -417,6 +434,12 @@ int32_t moe_dispatch(const int32_t* idx, int32_t T, int32_t E, int32_t k, int32_
   MOE_TRY(launch_dispatch(idx, T, E, k, counts, offsets, perm, pos, (int32_t*)ws, 0, nullptr,
                           DispatchExtras(), (hipStream_t)stream));
   return MOE_OK;
+}
+
+int32_t moe_bias_update(const int32_t* counts, const float* target, int32_t E, float gamma,
+                        float* b, void* stream) {
+  if (E < 1 || !counts || !b) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_bias_update(counts, target, E, gamma, b, (hipStream_t)stream));
 }
 
 int32_t moe_trace_enable(int32_t capacity, const char* filter) {

@@ -29,14 +29,30 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  float key[NPER], sc[NPER];
+  float key[NPER], sc[NPER], zs[NPER];
+  // K-slice partials (split-K router), summed in slice order; the loads of one slice for all of
+  // this lane's experts are independent, so they are issued together
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int e = lane + 64 * i;
+    zs[i] = e < E ? logits[(int64_t)t * E + e] : 0.f;
+  }
+#pragma unroll 4
+  for (int q = 1; q < nsplit; ++q) {
+    float v[NPER];
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+      const int e = lane + 64 * i;
+      v[i] = e < E ? logits[((int64_t)q * T + t) * E + e] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) zs[i] += v[i];
+  }
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
     const int e = lane + 64 * i;
     if (e < E) {
-      float z = logits[(int64_t)t * E + e];
-#pragma unroll 8
-      for (int q = 1; q < nsplit; ++q) z += logits[((int64_t)q * T + t) * E + e];  // slice order
+      const float z = zs[i];
       if (logits_out) logits_out[(int64_t)t * E + e] = z;
       const float s = (float)(1.0 / (1.0 + exp(-(double)z)));
       sc[i] = s;
@@ -370,6 +386,34 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
   }
 }
 
+// One workgroup; thread e handles expert e (loops for E > 1024). The mean-load comparison is done
+// in integers: sign(sum/E - c) = sign(sum - E*c).
+__global__ __launch_bounds__(1024) void bias_update_kernel(const int32_t* __restrict__ counts,
+                                                           const float* __restrict__ target,
+                                                           int E, float gamma,
+                                                           float* __restrict__ b) {
+  __shared__ long long total;
+  if (!target) {
+    long long part = 0;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) part += counts[e];
+    if (threadIdx.x == 0) total = 0;
+    __syncthreads();
+    atomicAdd((unsigned long long*)&total, (unsigned long long)part);  // exact: integer sum
+    __syncthreads();
+  }
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int sgn;
+    if (target) {
+      const float d = target[e] - (float)counts[e];
+      sgn = (d > 0.f) - (d < 0.f);
+    } else {
+      const long long d = total - (long long)E * counts[e];
+      sgn = (d > 0) - (d < 0);
+    }
+    if (sgn) b[e] = b[e] + (sgn > 0 ? gamma : -gamma);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_topk(const float* logits, int nsplit, const float* b, int T, int E, int k,
@@ -440,4 +484,11 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t ldx, int T, int H, uint8
   return hipGetLastError();
 }
 
+hipError_t launch_bias_update(const int32_t* counts, const float* target, int E, float gamma,
+                              float* b, hipStream_t s) {
+  hipLaunchKernelGGL(bias_update_kernel, dim3(1), dim3(1024), 0, s, counts, target, E, gamma, b);
+  return hipGetLastError();
+}
+
 }  // namespace moe
+

@@ -35,13 +35,14 @@ __device__ __forceinline__ bf16x8_t ld16(const uint16_t* p) { return *(const bf1
 
 // One lane's part of a 16 x 16 output block: 4 consecutive columns n .. n+3 of row orow.
 __device__ __forceinline__ void store_block(const f32x4_t v, void* out, int64_t ldo,
-                                            int64_t orow, int n, bool sq) {
-  if (sq) {
-    const uint2 q = make_uint2(pack_bf16x2(sqrelu(v[0]), sqrelu(v[1])),
-                               pack_bf16x2(sqrelu(v[2]), sqrelu(v[3])));
-    *(uint2*)((uint16_t*)out + orow * ldo + n) = q;
-  } else {
+                                            int64_t orow, int n, int mode) {
+  if (mode == kStoreF32) {
     *(float4*)((float*)out + orow * ldo + n) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    const bool sq = mode == kStoreSqRelu;
+    const uint2 q = make_uint2(pack_bf16x2(sq ? sqrelu(v[0]) : v[0], sq ? sqrelu(v[1]) : v[1]),
+                               pack_bf16x2(sq ? sqrelu(v[2]) : v[2], sq ? sqrelu(v[3]) : v[3]));
+    *(uint2*)((uint16_t*)out + orow * ldo + n) = q;
   }
 }
 
@@ -70,7 +71,7 @@ struct Unit {
 // number of loads, which lets the compiler wait for exactly the batch it multiplies. !kFull:
 // loads of the last batch past K are clamped into the row and zeroed.
 template <int U, bool kFull, class Resolve>
-__device__ void stream_units(int first, int total, int nwaves, int lane, bool sq,
+__device__ void stream_units(int first, int total, int nwaves, int lane, int mode,
                              Resolve resolve) {
   const int kq = (lane >> 4) * 8;
   const int tr = lane & 15;
@@ -127,7 +128,7 @@ __device__ void stream_units(int first, int total, int nwaves, int lane, bool sq
       return true;
     }
     // unit done: acc[r] = out[token tr][n + r]; lanes holding a real token store
-    if (tr < cur.nrows && cur.n < cur.N) store_block(acc, cur.out, cur.ldo, cur.orow, cur.n, sq);
+    if (tr < cur.nrows && cur.n < cur.N) store_block(acc, cur.out, cur.ldo, cur.orow, cur.n, mode);
     acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (un < 0) return false;
     cur = nxt;
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(256, 1) void stream_kernel(StreamParams p) {
   // stream neighbouring rows of one expert's matrix)
   const int nss = p.Ws ? cdiv(p.Ts, kSliceRows) : 0;
   const int nsh = nss ? cdiv(p.Ns, kUnitRows) * nss : 0;
-  const int nsl = sload(p.n_slices, 0);
+  const int nsl = p.n_slices ? sload(p.n_slices, 0) : 0;
   const int nbr = cdiv(p.N, kUnitRows);
   const int nrt = nbr * nsl;
   auto resolve = [&](int u, Unit& s) {
@@ -205,11 +206,12 @@ __global__ __launch_bounds__(256, 1) void stream_kernel(StreamParams p) {
     }
     s.n = n0 + (lane >> 4) * 4;
   };
-  const bool sq = p.sqrelu_bf16;
-  if (min(p.K, nss ? p.Ks : p.K) >= 32 * UN)
-    stream_units<UN, true>(wave, nsh + nrt, nwaves, lane, sq, resolve);
+  // the shifted-last-batch path needs every unit's K to span at least one batch
+  const bool full = (nrt == 0 || p.K >= 32 * UN) && (nsh == 0 || p.Ks >= 32 * UN);
+  if (full)
+    stream_units<UN, true>(wave, nsh + nrt, nwaves, lane, p.store, resolve);
   else
-    stream_units<UN, false>(wave, nsh + nrt, nwaves, lane, sq, resolve);
+    stream_units<UN, false>(wave, nsh + nrt, nwaves, lane, p.store, resolve);
 }
 
 }  // namespace

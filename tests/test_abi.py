@@ -101,6 +101,13 @@ def test_forward_argument_errors_are_reported_before_launch():
     assert forward(desc(T=0)) == B.MOE_OK                                 # empty: no-op
 
 
+def test_bias_update_argument_errors():
+    L = moe.lib()
+    assert L.moe_bias_update(FAKE, None, 0, 1e-3, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_bias_update(None, None, 8, 1e-3, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_bias_update(FAKE, None, 8, 1e-3, None, None) == B.MOE_ERR_INVALID_ARG
+
+
 def test_route_and_dispatch_argument_errors():
     L = moe.lib()
     assert L.moe_route(None, FAKE, FAKE, FAKE, 4, 64, 8, 0, 1, FAKE, FAKE, FAKE, None) == \

@@ -143,6 +143,16 @@ def test_nano_decode_full_oracle_both_paths():
         assert err <= 5e-3
 
 
+@pytest.mark.parametrize("name", ["latent_decode_bf16", "latent_decode_k22_bf16"])
+def test_latent_decode_full_oracle_both_paths(name):
+    # LatentMoE in the latency regime: 64 tokens, E'=512, k'=24 (and the k'=22 variant); the
+    # automatic path is the weight-streaming one, checked on every token beside the grouped one
+    inp = mi.make_layer(mi.CONFIGS[name], seed=0)
+    ya, _ = check_full(inp, "auto")
+    yg, _ = check_full(inp, "grouped")
+    assert rel_frob(ya, yg) < 5e-3
+
+
 def test_routing_given_matches_oracle_on_its_own_selection():
     cfg = SMALL["bf16_ragged"]
     inp = mi.make_layer(cfg, seed=3)
@@ -258,6 +268,46 @@ def test_latent_identity_projection_equals_plain_layer():
     inl = dict(inp, config=dataclasses.replace(cfg, latent=cfg.H), W_in=eye, W_out=eye)
     yl, _ = run(inl, "grouped")
     assert np.array_equal(yl, yp)
+
+
+@pytest.mark.parametrize("E,with_target", [(1, False), (128, False), (128, True), (512, True),
+                                           (1500, False)])
+def test_bias_update_is_bit_exact(E, with_target):
+    # the sign rule in fp32 against the oracle's fp64 step rounded once to fp32 (one fp32 add is
+    # correctly rounded, so the two agree bit for bit)
+    rng = np.random.default_rng(E + with_target)
+    counts = rng.integers(0, 400, E).astype(np.int32)
+    counts[: E // 4] = int(counts.sum()) // E            # some experts exactly at the mean load
+    b = (rng.standard_normal(E) * 0.1).astype(np.float32)
+    gamma = np.float32(1e-3)
+    target = (rng.integers(0, 400, E).astype(np.float32) if with_target else
+              np.full(E, counts.sum() / E))
+    if with_target:
+        target[: E // 8] = counts[: E // 8]              # exact ties: no step
+    want = O.bias_update(b.astype(np.float64), counts, target.astype(np.float64),
+                         float(gamma)).astype(np.float32)
+    bd = torch.from_numpy(b).cuda()
+    moe.bias_update(torch.from_numpy(counts).cuda(), bd, float(gamma),
+                    torch.from_numpy(target.astype(np.float32)).cuda() if with_target else None)
+    torch.cuda.synchronize()
+    assert np.array_equal(bd.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+def test_bias_update_from_a_forward_pass_moves_load_toward_the_mean():
+    # counts straight from the layer's dispatch: overloaded experts step down, idle ones up
+    cfg = mi.CONFIGS["nano_decode_bf16"]
+    inp = mi.make_layer(cfg, seed=0)
+    _, rt = run(inp, "auto")
+    counts = rt["counts"]
+    b = inp["b"].astype(np.float32).copy()
+    bd = torch.from_numpy(b).cuda()
+    moe.bias_update(torch.from_numpy(counts).cuda(), bd, 1e-3)
+    torch.cuda.synchronize()
+    nb = bd.cpu().numpy()
+    mean = counts.sum() / cfg.E
+    assert np.all(nb[counts > mean] < b[counts > mean])
+    assert np.all(nb[counts < mean] > b[counts < mean])
+    assert np.array_equal(nb[counts == mean], b[counts == mean])
 
 
 def test_zero_tokens_is_a_no_op():
