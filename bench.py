@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="nano_decode_bf16")
-    ap.add_argument("--also", default="nano_prefill_bf16,latent_decode_bf16",
+    ap.add_argument("--also", default="nano_prefill_bf16,latent_decode_bf16,nano_fp8_decode",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--path", default="auto", choices=["auto", "grouped", "stream"])
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured graph")
@@ -75,7 +75,8 @@ def work_of(name, cfg, counts, stream=False):
         return 2 * P * I * D, touched * I * D * ew + scales + T * D * (1 if ew == 1 else ea) + P * I * 2
     if role == "routed_down":
         scales = touched * D * 4 if ew == 1 else 0
-        return 2 * P * D * I, touched * D * I * ew + scales + P * I * 2 + P * D * ea
+        h_in = P * I * (1 if ew == 1 else 2)
+        return 2 * P * D * I, touched * D * I * ew + scales + h_in + P * D * (4 if stream else ea)
     if role == "shared_up":
         return 2 * T * Is * H, Is * H * ea + T * H * ea + T * Is * ea
     if role == "shared_down":

@@ -92,6 +92,9 @@ CONFIGS = {
     "latent_decode_k22_bf16": LayerConfig(
         "latent_decode_k22_bf16", T=64, H=4096, E=512, k=22, I=512, latent=1024,
         description="LatentMoE decode step with the k'=22 of the published comparison"),
+    "nano_fp8_decode": LayerConfig(
+        "nano_fp8_decode", T=64, H=2688, E=128, k=6, I=1856, I_shared=3712, expert_dtype="e4m3",
+        description="Nano-shaped decode step, e4m3 expert weights, T=64"),
     "nano_fp8": LayerConfig(
         "nano_fp8", T=16384, H=2688, E=128, k=6, I=1856, I_shared=3712, expert_dtype="e4m3",
         bias="bias_nano_fp8_imbalance.txt",

@@ -70,20 +70,23 @@ enum StreamStore : int { kStoreF32 = 0, kStoreSqRelu = 1, kStoreBF16 = 2 };
 //   out[r, n] = act( sum_k A[src(r), k] * W[g][n, k] )
 // act = bf16(relu(acc)^2) for the up projection, fp32 acc for the down projection.
 struct StreamParams {
+  int fp8 = 0;                        // 1: routed operands are e4m3 codes (no shared slot)
   // routed experts
-  const uint16_t* A = nullptr;        // activation rows (bf16), lda elements apart
+  const void* A = nullptr;            // activation rows (bf16 or e4m3), lda elements apart
   int64_t lda = 0;
+  const float* a_scale = nullptr;     // e4m3: dequantisation scale per source row
   const int32_t* gather = nullptr;    // source row of pair row r = gather[r] (nullptr: r)
   const int32_t* offs = nullptr;      // [E + 1]
   int E = 0;
-  const uint16_t* W = nullptr;        // [E][N][K]
+  const void* W = nullptr;            // [E][N][K]
+  const float* w_scale = nullptr;     // e4m3: per output channel [E][N]
   int N = 0, K = 0;
   void* out = nullptr;                // pair rows, ldo elements apart
   int64_t ldo = 0;
   // shared expert (Ws == nullptr: none)
-  const uint16_t* As = nullptr;
+  const void* As = nullptr;           // bf16
   int64_t lda_s = 0;
-  const uint16_t* Ws = nullptr;       // [Ns][Ks]
+  const void* Ws = nullptr;           // [Ns][Ks] bf16
   int Ns = 0, Ks = 0, Ts = 0;
   void* out_s = nullptr;
   int64_t ldo_s = 0;

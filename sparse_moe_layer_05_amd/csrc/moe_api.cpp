@@ -47,7 +47,8 @@ int32_t make_plan(const moe_desc_t* d, bool latent_call, Plan* pl) {
   p.T = (int)T; p.H = (int)H; p.E = (int)E; p.k = (int)k; p.I = (int)I; p.Is = (int)Is;
   p.L = (int)L; p.D = L ? (int)L : (int)H; p.P = (int)(T * k);
   const uint32_t path = d->flags & MOE_PATH_MASK;
-  const bool stream_ok = p.act == Elt::BF16 && p.ex == Elt::BF16;
+  // the decode path streams bf16 experts, and e4m3 experts of a plain (non-latent) layer
+  const bool stream_ok = p.act == Elt::BF16 && (p.ex == Elt::BF16 || (p.ex == Elt::FP8 && !p.L));
   if (path == MOE_PATH_AUTO)
     p.path = (stream_ok && (int64_t)p.P <= 8 * E) ? MOE_PATH_STREAM : MOE_PATH_GROUPED;
   else if (path == MOE_PATH_STREAM)
@@ -249,14 +250,59 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
   }
   // (4) routed experts (+ the shared expert on the stream path of a plain layer)
   Elt y_elt = act;
-  if (stream_path) {
+  if (stream_path && fp8) {
+    // e4m3 experts: expert inputs and the h rows quantised per row, routed units on the e4m3
+    // streaming kernel; the bf16 shared expert streams in launches of its own
+    y_elt = Elt::F32;
+    uint8_t* xq = base + pl.xq;
+    float* sx = (float*)(base + pl.sx);
+    uint8_t* hq = base + pl.hq;
+    float* sh = (float*)(base + pl.sh);
+    {
+      MOE_SPAN("quant_rows:x");
+      MOE_TRY(launch_quant_rows((const uint16_t*)xin, D, T, D, xq, sx, s));
+    }
+    StreamParams up;
+    up.fp8 = 1;
+    up.A = xq; up.lda = D; up.a_scale = sx; up.gather = perm; up.offs = offsets; up.E = E;
+    up.W = w->W_up; up.w_scale = w->s_up; up.N = I; up.K = D; up.out = h; up.ldo = I;
+    up.store = kStoreSqRelu;
+    up.slice_e = slices; up.slice_r = slices + max_sl; up.n_slices = slices + 2 * max_sl;
+    {
+      MOE_SPAN("stream:routed_up");
+      MOE_TRY(launch_stream(up, s));
+    }
+    if (Is) {
+      MOE_SPAN("stream:shared_up");
+      MOE_TRY(stream_dense(w->x, H, w->Ws_up, Is, H, T, hs, Is, kStoreSqRelu, s));
+    }
+    {
+      MOE_SPAN("quant_rows:h");
+      MOE_TRY(launch_quant_rows((const uint16_t*)h, I, P, I, hq, sh, s));
+    }
+    StreamParams dn;
+    dn.fp8 = 1;
+    dn.A = hq; dn.lda = I; dn.a_scale = sh; dn.offs = offsets; dn.E = E;
+    dn.W = w->W_down; dn.w_scale = w->s_down; dn.N = D; dn.K = I; dn.out = Y; dn.ldo = D;
+    dn.store = kStoreF32;
+    dn.slice_e = slices; dn.slice_r = slices + max_sl; dn.n_slices = slices + 2 * max_sl;
+    {
+      MOE_SPAN("stream:routed_down");
+      MOE_TRY(launch_stream(dn, s));
+    }
+    if (Is) {
+      MOE_SPAN("stream:shared_down");
+      MOE_TRY(stream_dense(hs, Is, w->Ws_down, H, Is, T, (float*)Y + (size_t)P * D, D, kStoreF32,
+                           s));
+    }
+  } else if (stream_path) {
     y_elt = Elt::F32;
     const bool sh = Is && !L;
     StreamParams up;
-    up.A = (const uint16_t*)xin; up.lda = D; up.gather = perm; up.offs = offsets; up.E = E;
-    up.W = (const uint16_t*)w->W_up; up.N = I; up.K = D; up.out = h; up.ldo = I;
+    up.A = xin; up.lda = D; up.gather = perm; up.offs = offsets; up.E = E;
+    up.W = w->W_up; up.N = I; up.K = D; up.out = h; up.ldo = I;
     if (sh) {
-      up.As = (const uint16_t*)w->x; up.lda_s = H; up.Ws = (const uint16_t*)w->Ws_up;
+      up.As = w->x; up.lda_s = H; up.Ws = w->Ws_up;
       up.Ns = Is; up.Ks = H; up.Ts = T; up.out_s = hs; up.ldo_s = Is;
     }
     up.store = kStoreSqRelu;
@@ -266,10 +312,10 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
       MOE_TRY(launch_stream(up, s));
     }
     StreamParams dn;
-    dn.A = (const uint16_t*)h; dn.lda = I; dn.offs = offsets; dn.E = E;
-    dn.W = (const uint16_t*)w->W_down; dn.N = D; dn.K = I; dn.out = Y; dn.ldo = D;
+    dn.A = h; dn.lda = I; dn.offs = offsets; dn.E = E;
+    dn.W = w->W_down; dn.N = D; dn.K = I; dn.out = Y; dn.ldo = D;
     if (sh) {
-      dn.As = (const uint16_t*)hs; dn.lda_s = Is; dn.Ws = (const uint16_t*)w->Ws_down;
+      dn.As = hs; dn.lda_s = Is; dn.Ws = w->Ws_down;
       dn.Ns = H; dn.Ks = Is; dn.Ts = T; dn.out_s = (float*)Y + (size_t)P * D; dn.ldo_s = D;
     }
     dn.store = kStoreF32;

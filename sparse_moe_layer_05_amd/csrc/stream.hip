@@ -13,8 +13,11 @@
 // Loads are double buffered in registers with a one-unit lookahead: while a unit streams, the
 // next one is resolved, and its first k batch is in flight while the current unit's last batch
 // is multiplied. Inside a unit the weights are the matrix-core "A" operand and the tokens the
-// "B" operand of v_mfma_f32_16x16x32_bf16: lane l loads 16 bytes of weight row (l % 16) at k
-// offset 8 * (l / 16) of each 32-wide k step straight from HBM into registers (no LDS).
+// "B" operand, loaded straight from HBM into registers (no LDS): bf16 through
+// v_mfma_f32_16x16x32_bf16, or e4m3 expert weights with e4m3 token rows through
+// v_mfma_scale_f32_16x16x128_f8f6f4 (per-channel and per-token scales applied to the result,
+// as in "Nemotron 3 Nano：開放高效的 MoE 混合 Mamba-Transformer 智能體推理模型", section 4,
+// FP8 expert weights).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -23,15 +26,12 @@ namespace {
 
 constexpr int kUnitRows = 16;
 constexpr int kStreamWaves = 1024;  // 4 per CU, one per SIMD
-constexpr int UN = 6;               // 32-wide k steps per load batch
 
 // Unit lookups are wave-uniform: reading them through the constant address space makes them
 // scalar loads, which are counted apart from the vector loads, so a lookup never waits for the
 // weight loads in flight (vector loads complete in issue order).
 typedef const __attribute__((address_space(4))) int32_t* scalar_ptr;
 __device__ __forceinline__ int sload(const int32_t* p, int i) { return ((scalar_ptr)p)[i]; }
-
-__device__ __forceinline__ bf16x8_t ld16(const uint16_t* p) { return *(const bf16x8_t*)p; }
 
 // One lane's part of a 16 x 16 output block: 4 consecutive columns n .. n+3 of row orow.
 __device__ __forceinline__ void store_block(const f32x4_t v, void* out, int64_t ldo,
@@ -46,34 +46,50 @@ __device__ __forceinline__ void store_block(const f32x4_t v, void* out, int64_t 
   }
 }
 
-// A unit resolved to this lane's pointers. Pointers include the lane's k offset within a
-// 32-wide step.
+// Operand element types: bf16 (v_mfma_f32_16x16x32_bf16, 32 elements = 64 bytes per k step)
+// and OCP e4m3 (v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales, 128 elements = 128
+// bytes per k step). Lane l holds 16 (bf16) or 32 (e4m3) consecutive bytes of row l % 16 at byte
+// (l / 16) * LB of each step, for weights and tokens alike; the result register r of lane l is
+// out[weight row (l / 16) * 4 + r][token l % 16].
+template <Elt T> struct Fmt;
+template <> struct Fmt<Elt::BF16> {
+  static constexpr int SB = 64, LB = 16, U = 6;  // step bytes, lane bytes, steps per batch
+};
+template <> struct Fmt<Elt::FP8> {
+  static constexpr int SB = 128, LB = 32, U = 3;
+};
+
+// A unit resolved to this lane's pointers. Pointers include the lane's byte offset within a k
+// step.
 struct Unit {
-  const uint16_t* w;  // this lane's weight row
-  const uint16_t* a;  // this lane's token row
+  const uint8_t* w;   // this lane's weight row
+  const uint8_t* a;   // this lane's token row
   void* out;
   int64_t ldo;
   int64_t orow;       // output row of this lane's token
   int n;              // first of this lane's 4 output columns
-  int N, K;           // weight rows and columns of the expert
+  int N, KB;          // weight rows of the expert, bytes of a row (K * element size)
   int nrows;          // tokens of the slice
+  float asc;          // e4m3: this lane's token scale
+  const float* wsc;   // e4m3: scales of this lane's 4 output channels
 };
 
 // Streams the units this wave is dealt: first, first + nwaves, ... below total;
 // resolve(u, unit) fills a unit.
 //
-// Each k batch covers U steps of 32 columns; the loads of the following batch (of this unit or,
-// after its last batch, of the next unit) are in flight while a batch is multiplied. The two
-// register sets swap roles between consecutive batches and are never copied (a copy would wait
-// for the loads in flight). kFull (every K >= 32*U): the last batch of a unit is moved back to
+// Each k batch covers U steps; the loads of the following batch (of this unit or, after its last
+// batch, of the next unit) are in flight while a batch is multiplied. The two register sets swap
+// roles between consecutive batches and are never copied (a copy would wait for the loads in
+// flight). kFull (every row spans at least one batch): the last batch of a unit is moved back to
 // end exactly at K and the weight chunks it shares with the batch before are zeroed, so every
 // load of a batch is one base address plus an immediate offset and every batch issues the same
 // number of loads, which lets the compiler wait for exactly the batch it multiplies. !kFull:
 // loads of the last batch past K are clamped into the row and zeroed.
-template <int U, bool kFull, class Resolve>
+template <Elt T, bool kFull, class Resolve>
 __device__ void stream_units(int first, int total, int nwaves, int lane, int mode,
                              Resolve resolve) {
-  const int kq = (lane >> 4) * 8;
+  constexpr int SB = Fmt<T>::SB, LB = Fmt<T>::LB, U = Fmt<T>::U, C = LB / 16, BB = U * SB;
+  const int lb = (lane >> 4) * LB;  // this lane's byte offset within a step
   const int tr = lane & 15;
   if (first >= total) return;
   Unit cur, nxt;
@@ -82,59 +98,85 @@ __device__ void stream_units(int first, int total, int nwaves, int lane, int mod
   int un = u + nwaves < total ? u + nwaves : -1;
   if (un >= 0) resolve(un, nxt);
 
-  auto nbat_of = [&](int K) { return cdiv(K, 32 * U); };
-  auto kbase = [&](int K, int b) { return kFull ? min(b * 32 * U, K - 32 * U) : b * 32 * U; };
+  auto nbat_of = [&](int KB) { return cdiv(KB, BB); };
+  auto kbase = [&](int KB, int b) { return kFull ? min(b * BB, KB - BB) : b * BB; };
   // loads of batch b of unit s, or of batch 0 of unit o when other is set (chosen field by
   // field: choosing a whole unit would put both in memory)
-  auto issue = [&](const Unit& s, const Unit& o, bool other, int b, bf16x8_t* wf,
-                   bf16x8_t* xf) {
-    const int K = other ? o.K : s.K;
-    const uint16_t* w = other ? o.w : s.w;
-    const uint16_t* a = other ? o.a : s.a;
-    const int kb = kbase(K, b);
+  auto issue = [&](const Unit& s, const Unit& o, bool other, int b, uint4* wf, uint4* xf) {
+    const int KB = other ? o.KB : s.KB;
+    const uint8_t* w = other ? o.w : s.w;
+    const uint8_t* a = other ? o.a : s.a;
+    const int kb = kbase(KB, b);
 #pragma unroll
-    for (int q = 0; q < U; ++q) {
-      const int kk = kFull ? kb + q * 32 : min(kb + q * 32, K - 8 - kq);
-      wf[q] = ld16(w + kk);
-      xf[q] = ld16(a + kk);
-    }
+    for (int q = 0; q < U; ++q)
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int off = kFull ? kb + q * SB + c * 16 : min(kb + q * SB + c * 16, KB - 16 - lb);
+        wf[q * C + c] = *(const uint4*)(w + off);
+        xf[q * C + c] = *(const uint4*)(a + off);
+      }
   };
   // last batch b: zero the weight chunks that an earlier batch already covered, or that lie
   // past K
-  auto mask = [&](int K, int b, bf16x8_t* wf) {
-    const int kb = kbase(K, b);
+  auto mask = [&](int KB, int b, uint4* wf) {
+    const int kb = kbase(KB, b);
 #pragma unroll
-    for (int q = 0; q < U; ++q) {
-      const bool drop = kFull ? kb + q * 32 + kq < b * 32 * U : kb + q * 32 + kq >= K;
-      if (drop) wf[q] = bf16x8_t{};
+    for (int q = 0; q < U; ++q)
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int at = kb + q * SB + lb + c * 16;
+        const bool drop = kFull ? at < b * BB : at >= KB;
+        if (drop) wf[q * C + c] = make_uint4(0, 0, 0, 0);
+      }
+  };
+  auto mfma = [&](const uint4* wf, const uint4* xf, int q, f32x4_t acc) {
+    if constexpr (T == Elt::BF16) {
+      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wf[q]),
+                                                    __builtin_bit_cast(bf16x8_t, xf[q]), acc,
+                                                    0, 0, 0);
+    } else {
+      const uint4 w0 = wf[2 * q], w1 = wf[2 * q + 1], x0 = xf[2 * q], x1 = xf[2 * q + 1];
+      const i32x8_t wa = {(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w,
+                          (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+      const i32x8_t xa = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                          (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa, xa, acc, 0, 0, 0, 127, 0, 127);
     }
   };
 
-  bf16x8_t w0[U], w1[U], x0[U], x1[U];
+  uint4 w0[U * C], w1[U * C], x0[U * C], x1[U * C];
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  int b = 0, nbat = nbat_of(cur.K);
+  int b = 0, nbat = nbat_of(cur.KB);
   // One k batch: put the following batch in flight into (wnxt, xnxt), multiply (wcur, xcur).
   // After a wave's last unit the following batch re-reads the unit's first one (unused) so that
   // the load count stays the same. Returns false once the wave is done.
-  auto step = [&](bf16x8_t* wcur, bf16x8_t* xcur, bf16x8_t* wnxt, bf16x8_t* xnxt) {
+  auto step = [&](uint4* wcur, uint4* xcur, uint4* wnxt, uint4* xnxt) {
     const bool last = b + 1 == nbat;
     issue(cur, nxt, last && un >= 0, last ? 0 : b + 1, wnxt, xnxt);
-    if (last) mask(cur.K, b, wcur);
+    if (last) mask(cur.KB, b, wcur);
 #pragma unroll
-    for (int q = 0; q < U; ++q)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wcur[q], xcur[q], acc, 0, 0, 0);
+    for (int q = 0; q < U; ++q) acc = mfma(wcur, xcur, q, acc);
     if (!last) {
       ++b;
       return true;
     }
     // unit done: acc[r] = out[token tr][n + r]; lanes holding a real token store
-    if (tr < cur.nrows && cur.n < cur.N) store_block(acc, cur.out, cur.ldo, cur.orow, cur.n, mode);
+    if (tr < cur.nrows && cur.n < cur.N) {
+      if constexpr (T == Elt::FP8) {
+        const float4 sc = *(const float4*)cur.wsc;
+        acc[0] *= cur.asc * sc.x;
+        acc[1] *= cur.asc * sc.y;
+        acc[2] *= cur.asc * sc.z;
+        acc[3] *= cur.asc * sc.w;
+      }
+      store_block(acc, cur.out, cur.ldo, cur.orow, cur.n, mode);
+    }
     acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (un < 0) return false;
     cur = nxt;
     u = un;
     b = 0;
-    nbat = nbat_of(cur.K);
+    nbat = nbat_of(cur.KB);
     un = u + nwaves < total ? u + nwaves : -1;
     if (un >= 0) resolve(un, nxt);
     return true;
@@ -146,10 +188,13 @@ __device__ void stream_units(int first, int total, int nwaves, int lane, int mod
   }
 }
 
+template <Elt T>
 __global__ __launch_bounds__(256, 1) void stream_kernel(StreamParams p) {
+  constexpr int EB = T == Elt::FP8 ? 1 : 2;
+  constexpr int LB = Fmt<T>::LB;
   const int lane = threadIdx.x & 63;
   const int tr = lane & 15;
-  const int kq = (lane >> 4) * 8;
+  const int lb = (lane >> 4) * LB;
   const int nwaves = gridDim.x * 4;
   // waves numbered die by die: consecutive numbers share a CU, then a die
   const int wave = xcd_logical_block(blockIdx.x, gridDim.x) * 4 +
@@ -164,6 +209,10 @@ __global__ __launch_bounds__(256, 1) void stream_kernel(StreamParams p) {
   const int nsl = p.n_slices ? sload(p.n_slices, 0) : 0;
   const int nbr = cdiv(p.N, kUnitRows);
   const int nrt = nbr * nsl;
+  const uint8_t* As = (const uint8_t*)p.As;
+  const uint8_t* Ws = (const uint8_t*)p.Ws;
+  const uint8_t* A = (const uint8_t*)p.A;
+  const uint8_t* W = (const uint8_t*)p.W;
   auto resolve = [&](int u, Unit& s) {
     int n0, src;
     if (u < nsh) {
@@ -172,12 +221,14 @@ __global__ __launch_bounds__(256, 1) void stream_kernel(StreamParams p) {
       s.nrows = min(p.Ts - r0, kSliceRows);
       s.orow = r0 + tr;
       src = r0 + min(tr, s.nrows - 1);
-      s.a = p.As + (int64_t)src * p.lda_s + kq;
-      s.w = p.Ws + (int64_t)min(n0 + tr, p.Ns - 1) * p.Ks + kq;
+      s.a = As + (int64_t)src * p.lda_s * EB + lb;
+      s.w = Ws + (int64_t)min(n0 + tr, p.Ns - 1) * p.Ks * EB + lb;
       s.out = p.out_s;
       s.ldo = p.ldo_s;
       s.N = p.Ns;
-      s.K = p.Ks;
+      s.KB = p.Ks * EB;
+      s.asc = 1.f;
+      s.wsc = nullptr;
     } else {
       const int v = u - nsh;
       const int i = v / nbr;
@@ -197,28 +248,38 @@ __global__ __launch_bounds__(256, 1) void stream_kernel(StreamParams p) {
         }
         src = row;
       }
-      s.a = p.A + (int64_t)src * p.lda + kq;
-      s.w = p.W + (int64_t)g * p.N * p.K + (int64_t)min(n0 + tr, p.N - 1) * p.K + kq;
+      s.a = A + (int64_t)src * p.lda * EB + lb;
+      s.w = W + ((int64_t)g * p.N + min(n0 + tr, p.N - 1)) * p.K * EB + lb;
       s.out = p.out;
       s.ldo = p.ldo;
       s.N = p.N;
-      s.K = p.K;
+      s.KB = p.K * EB;
+      s.asc = p.a_scale ? p.a_scale[src] : 1.f;
+      s.wsc = p.w_scale ? p.w_scale + (int64_t)g * p.N + min(n0 + (lane >> 4) * 4, p.N - 4)
+                        : nullptr;
     }
     s.n = n0 + (lane >> 4) * 4;
   };
-  // the shifted-last-batch path needs every unit's K to span at least one batch
-  const bool full = (nrt == 0 || p.K >= 32 * UN) && (nsh == 0 || p.Ks >= 32 * UN);
+  // the shifted-last-batch path needs every unit's row to span at least one batch
+  constexpr int BB = Fmt<T>::U * Fmt<T>::SB;
+  const bool full = (nrt == 0 || p.K * EB >= BB) && (nsh == 0 || p.Ks * EB >= BB);
   if (full)
-    stream_units<UN, true>(wave, nsh + nrt, nwaves, lane, p.store, resolve);
+    stream_units<T, true>(wave, nsh + nrt, nwaves, lane, p.store, resolve);
   else
-    stream_units<UN, false>(wave, nsh + nrt, nwaves, lane, p.store, resolve);
+    stream_units<T, false>(wave, nsh + nrt, nwaves, lane, p.store, resolve);
 }
 
 }  // namespace
 
 hipError_t launch_stream(const StreamParams& p, hipStream_t s) {
   static_assert(kStreamWaves / 4 % kXcds == 0, "the wave numbering needs whole dies");
-  hipLaunchKernelGGL(stream_kernel, dim3(kStreamWaves / 4), dim3(256), 0, s, p);
+  if (p.fp8) {
+    // e4m3 launches carry routed units only, with both scale sets
+    if (p.Ws || !p.a_scale || !p.w_scale) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(stream_kernel<Elt::FP8>, dim3(kStreamWaves / 4), dim3(256), 0, s, p);
+  } else {
+    hipLaunchKernelGGL(stream_kernel<Elt::BF16>, dim3(kStreamWaves / 4), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 

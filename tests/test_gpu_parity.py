@@ -163,13 +163,32 @@ def test_routing_given_matches_oracle_on_its_own_selection():
         assert rel_frob(y, ref["y"]) <= 5e-3
 
 
-def test_fp8_small_against_emulating_oracle():
+@pytest.mark.parametrize("path", ["grouped", "stream"])
+def test_fp8_small_against_emulating_oracle(path):
+    # K of 256 and 128 bytes: shorter than one e4m3 streaming batch (the clamped-tail path)
     inp = mi.make_layer(SMALL["fp8_small"], seed=4)
-    y, rt = run(inp)
+    y, rt = run(inp, path)
     ref, _ = reference(inp, rt["idx"], fp8_emulate=True)
     err = rel_frob(y, ref["y"])
-    say(f"[gpu] fp8 small vs emulating oracle: {err:.3e}")
+    say(f"[gpu] fp8 small ({path}) vs emulating oracle: {err:.3e}")
     assert err <= 5e-3
+
+
+def test_fp8_decode_full_oracle_both_paths():
+    # Nano-shaped e4m3 experts at T=64: the automatic path streams the e4m3 weights; every token
+    # against the exact oracle (3e-2) and against the oracle emulating the activation rounding
+    inp = mi.make_layer(mi.CONFIGS["nano_fp8_decode"], seed=0)
+    dev = moe.to_device(inp)
+    ys = {}
+    for path in ("auto", "grouped"):
+        y, rt = run(inp, path, dev=dev)
+        ref, nswap = reference(inp, rt["idx"])
+        refe, _ = reference(inp, rt["idx"], fp8_emulate=True)
+        err, erre = rel_frob(y, ref["y"]), rel_frob(y, refe["y"])
+        say(f"[gpu] fp8 decode {path}: {err:.3e} exact, {erre:.3e} emulating, swaps {nswap}")
+        assert err <= 3e-2 and erre <= 5e-3
+        ys[path] = y
+    assert rel_frob(ys["auto"], ys["grouped"]) < 5e-3
 
 
 # --------------------------------------------------------------------- routing and dispatch
