@@ -58,16 +58,20 @@ def work_of(name, cfg, counts, stream=False):
     role = name.split(":")[1]
     if role == "router":
         return 2 * T * E * H, T * H * ea + E * H * ea + T * E * 4
-    if role == "up":       # stream: routed up (+ shared up)
-        f = 2 * P * I * D + (2 * T * Is * H if Is and not L else 0)
-        b = touched * I * D * ew + T * D * ea + P * I * 2
-        if Is and not L:
+    # stream launches: routed projection, plus the shared expert's on a bf16 plain layer
+    sh = bool(Is and not L and ew != 1)
+    if role == "up":
+        scales = touched * I * 4 if ew == 1 else 0
+        f = 2 * P * I * D + (2 * T * Is * H if sh else 0)
+        b = touched * I * D * ew + scales + T * D * (1 if ew == 1 else ea) + P * I * 2
+        if sh:
             b += Is * H * ea + T * Is * 2
         return f, b
-    if role == "down":     # stream: routed down (+ shared down), fp32 outputs
-        f = 2 * P * D * I + (2 * T * H * Is if Is and not L else 0)
-        b = touched * D * I * ew + P * I * 2 + P * D * 4
-        if Is and not L:
+    if role == "down":     # fp32 outputs
+        scales = touched * D * 4 if ew == 1 else 0
+        f = 2 * P * D * I + (2 * T * H * Is if sh else 0)
+        b = touched * D * I * ew + scales + P * I * (1 if ew == 1 else 2) + P * D * 4
+        if sh:
             b += H * Is * ea + T * Is * 2 + T * H * 4
         return f, b
     if role == "routed_up":
@@ -79,7 +83,7 @@ def work_of(name, cfg, counts, stream=False):
         return 2 * P * D * I, touched * D * I * ew + scales + h_in + P * D * (4 if stream else ea)
     if role == "shared_up":
         return 2 * T * Is * H, Is * H * ea + T * H * ea + T * Is * ea
-    if role == "shared_down":
+    if role == "shared_down":  # fp32 output
         return 2 * T * H * Is, H * Is * ea + T * Is * ea + T * H * 4
     if role == "latent_in":
         return 2 * T * L * H, L * H * ea + T * H * ea + T * L * ea

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe.h"
 #include "kernels.hpp"
 
@@ -106,6 +108,40 @@ int32_t make_plan(const moe_desc_t* d, bool latent_call, Plan* pl) {
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Per device: a second stream (default priority) and two events, made on first use and kept for
+// the life of the process. The decode path forks the shared expert onto it: that work does not
+// depend on routing, so it overlaps the router, top-k, dispatch and the routed experts, and is
+// joined back before the combine (a fork / join that stream capture also records).
+struct Side {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+Side g_side[kMaxDevices];
+std::mutex g_side_mu;
+
+hipError_t side_of(Side** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  Side& sd = g_side[dev];
+  if (!sd.s) {
+    Side n;
+    if ((e = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming)) != hipSuccess) {
+      if (n.fork) (void)hipEventDestroy(n.fork);
+      (void)hipStreamDestroy(n.s);
+      return e;
+    }
+    sd = n;
+  }
+  *out = &sd;
+  return hipSuccess;
+}
+
 // ---------------------------------------------------------------- launch trace (diagnostics)
 struct Trace {
   int cap = 0, n = 0;
@@ -132,6 +168,7 @@ struct TraceSpan {
 };
 
 #define MOE_SPAN(name) TraceSpan span_##__LINE__(name, s)
+#define MOE_SPAN_ON(name, st) TraceSpan span_##__LINE__(name, st)
 
 #define MOE_TRY(expr)                                   \
   do {                                                  \
@@ -205,6 +242,27 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
   const Elt act = pl.act;
   const bool stream_path = pl.path == MOE_PATH_STREAM;
 
+  // (0) decode path of a plain e4m3 layer: the bf16 shared expert (weight 1, every token,
+  // independent of routing) cannot share the e4m3 launches, so it streams on the side stream
+  // while the routed work proceeds on `s`. (A bf16 layer deals its shared-expert units out in
+  // the routed launches instead, which measured faster there.)
+  Side* side = nullptr;
+  if (stream_path && fp8 && Is && !L) {
+    MOE_TRY(side_of(&side));
+    MOE_TRY(hipEventRecord(side->fork, s));
+    MOE_TRY(hipStreamWaitEvent(side->s, side->fork, 0));
+    {
+      MOE_SPAN_ON("stream:shared_up", side->s);
+      MOE_TRY(stream_dense(w->x, H, w->Ws_up, Is, H, T, hs, Is, kStoreSqRelu, side->s));
+    }
+    {
+      MOE_SPAN_ON("stream:shared_down", side->s);
+      MOE_TRY(stream_dense(hs, Is, w->Ws_down, H, Is, T, (float*)Y + (size_t)P * D, D, kStoreF32,
+                           side->s));
+    }
+    MOE_TRY(hipEventRecord(side->join, side->s));
+  }
+
   // (1) router: logits = x W_r^T, then top-k and gates
   if (!given) {
     float* zsrc = pl.nsplit > 1 ? (float*)(base + pl.zpart) : logits;
@@ -269,12 +327,8 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
     up.store = kStoreSqRelu;
     up.slice_e = slices; up.slice_r = slices + max_sl; up.n_slices = slices + 2 * max_sl;
     {
-      MOE_SPAN("stream:routed_up");
+      MOE_SPAN("stream:up");
       MOE_TRY(launch_stream(up, s));
-    }
-    if (Is) {
-      MOE_SPAN("stream:shared_up");
-      MOE_TRY(stream_dense(w->x, H, w->Ws_up, Is, H, T, hs, Is, kStoreSqRelu, s));
     }
     {
       MOE_SPAN("quant_rows:h");
@@ -287,13 +341,8 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
     dn.store = kStoreF32;
     dn.slice_e = slices; dn.slice_r = slices + max_sl; dn.n_slices = slices + 2 * max_sl;
     {
-      MOE_SPAN("stream:routed_down");
+      MOE_SPAN("stream:down");
       MOE_TRY(launch_stream(dn, s));
-    }
-    if (Is) {
-      MOE_SPAN("stream:shared_down");
-      MOE_TRY(stream_dense(hs, Is, w->Ws_down, H, Is, T, (float*)Y + (size_t)P * D, D, kStoreF32,
-                           s));
     }
   } else if (stream_path) {
     y_elt = Elt::F32;
@@ -301,7 +350,7 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
     StreamParams up;
     up.A = xin; up.lda = D; up.gather = perm; up.offs = offsets; up.E = E;
     up.W = w->W_up; up.N = I; up.K = D; up.out = h; up.ldo = I;
-    if (sh) {
+    if (sh) {  // the shared expert's units share the launch with the routed ones
       up.As = w->x; up.lda_s = H; up.Ws = w->Ws_up;
       up.Ns = Is; up.Ks = H; up.Ts = T; up.out_s = hs; up.ldo_s = Is;
     }
@@ -390,6 +439,7 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
       S = Sw;
     } else if (Is && stream_path) {
       S = (const float*)Y + (size_t)P * D;
+      if (side) MOE_TRY(hipStreamWaitEvent(s, side->join, 0));  // shared rows of Y are written
     }
     MOE_SPAN("combine:y");
     MOE_TRY(launch_combine(Y, y_elt, D, S, H, pos, gates, T, D, k, y, act, H, s));

@@ -188,25 +188,24 @@ __device__ void stream_units(int first, int total, int nwaves, int lane, int mod
   }
 }
 
+// The units of one launch that this wave streams with operands of type T: the shared expert's
+// (shared_part, bf16 only) and the routed experts' (routed_part).
 template <Elt T>
-__global__ __launch_bounds__(256, 1) void stream_kernel(StreamParams p) {
+__device__ void run_units(const StreamParams& p, int wave, int nwaves, bool shared_part,
+                          bool routed_part) {
   constexpr int EB = T == Elt::FP8 ? 1 : 2;
   constexpr int LB = Fmt<T>::LB;
   const int lane = threadIdx.x & 63;
   const int tr = lane & 15;
   const int lb = (lane >> 4) * LB;
-  const int nwaves = gridDim.x * 4;
-  // waves numbered die by die: consecutive numbers share a CU, then a die
-  const int wave = xcd_logical_block(blockIdx.x, gridDim.x) * 4 +
-                   __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   // units [0, nsh): the shared expert, row block major, its token slices minor (slices that
   // share weight rows run side by side and share them through L2);
   // units [nsh, nsh + nrt): the routed slices, slice major, row block minor (neighbouring waves
   // stream neighbouring rows of one expert's matrix)
-  const int nss = p.Ws ? cdiv(p.Ts, kSliceRows) : 0;
+  const int nss = p.Ws && shared_part ? cdiv(p.Ts, kSliceRows) : 0;
   const int nsh = nss ? cdiv(p.Ns, kUnitRows) * nss : 0;
-  const int nsl = p.n_slices ? sload(p.n_slices, 0) : 0;
+  const int nsl = p.n_slices && routed_part ? sload(p.n_slices, 0) : 0;
   const int nbr = cdiv(p.N, kUnitRows);
   const int nrt = nbr * nsl;
   const uint8_t* As = (const uint8_t*)p.As;
@@ -267,6 +266,16 @@ __global__ __launch_bounds__(256, 1) void stream_kernel(StreamParams p) {
     stream_units<T, true>(wave, nsh + nrt, nwaves, lane, p.store, resolve);
   else
     stream_units<T, false>(wave, nsh + nrt, nwaves, lane, p.store, resolve);
+}
+
+// One launch: every wave streams its share of the units (the shared expert's first, bf16 only,
+// then the routed experts').
+template <Elt T>
+__global__ __launch_bounds__(256, 1) void stream_kernel(StreamParams p) {
+  // waves numbered die by die: consecutive numbers share a CU, then a die
+  const int wave = xcd_logical_block(blockIdx.x, gridDim.x) * 4 +
+                   __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  run_units<T>(p, wave, gridDim.x * 4, T == Elt::BF16, true);
 }
 
 }  // namespace

@@ -179,16 +179,16 @@ def test_fp8_decode_full_oracle_both_paths():
     # against the exact oracle (3e-2) and against the oracle emulating the activation rounding
     inp = mi.make_layer(mi.CONFIGS["nano_fp8_decode"], seed=0)
     dev = moe.to_device(inp)
-    ys = {}
-    for path in ("auto", "grouped"):
-        y, rt = run(inp, path, dev=dev)
-        ref, nswap = reference(inp, rt["idx"])
-        refe, _ = reference(inp, rt["idx"], fp8_emulate=True)
+    ya, rta = run(inp, "auto", dev=dev)
+    yg, rtg = run(inp, "grouped", dev=dev)
+    assert np.array_equal(rta["idx"], rtg["idx"])      # one router for both paths
+    ref, nswap = reference(inp, rta["idx"])
+    refe, _ = reference(inp, rta["idx"], fp8_emulate=True)
+    for path, y in (("auto", ya), ("grouped", yg)):
         err, erre = rel_frob(y, ref["y"]), rel_frob(y, refe["y"])
         say(f"[gpu] fp8 decode {path}: {err:.3e} exact, {erre:.3e} emulating, swaps {nswap}")
         assert err <= 3e-2 and erre <= 5e-3
-        ys[path] = y
-    assert rel_frob(ys["auto"], ys["grouped"]) < 5e-3
+    assert rel_frob(ya, yg) < 5e-3
 
 
 # --------------------------------------------------------------------- routing and dispatch
