@@ -104,7 +104,7 @@ def kernel_of(span):
 
 
 def mfma_dtype(kernel, cfg):
-    if "fp8" in kernel:
+    if "fp8" in kernel or "e4m3" in kernel:
         return "fp8"
     return "f32" if cfg.act_dtype == "f32" else "bf16"
 

@@ -327,7 +327,7 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
     up.store = kStoreSqRelu;
     up.slice_e = slices; up.slice_r = slices + max_sl; up.n_slices = slices + 2 * max_sl;
     {
-      MOE_SPAN("stream:up");
+      MOE_SPAN("stream_e4m3:up");
       MOE_TRY(launch_stream(up, s));
     }
     {
@@ -341,7 +341,7 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
     dn.store = kStoreF32;
     dn.slice_e = slices; dn.slice_r = slices + max_sl; dn.n_slices = slices + 2 * max_sl;
     {
-      MOE_SPAN("stream:down");
+      MOE_SPAN("stream_e4m3:down");
       MOE_TRY(launch_stream(dn, s));
     }
   } else if (stream_path) {
