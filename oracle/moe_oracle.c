@@ -21,7 +21,9 @@
  *         Agentic Reasoning", section "技术框架": router -> selected experts -> weighted combination.
  *  [N3W]  "NVIDIA Nemotron 3: Efficient and Open Intelligence", section 2.2 (LatentMoE, Figure 3b,
  *         Table 1) and the speed-read equation E' = E*H/l, k' = k*H/l; section 2.4 (latent
- *         projections kept in BF16).
+ *         projections kept in BF16; NVFP4 micro-block scaling with E2M1 elements, whose native
+ *         gfx950 counterpart, the OCP microscaling formats MXFP4 / MXFP8, is what the block-scaled
+ *         expert weights here use).
  * Where the pages leave a step open, the reading taken is stated at the function.
  */
 #include <math.h>
@@ -29,14 +31,17 @@
 #include <stdint.h>
 #include <string.h>
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_E4M3 = 2, ORC_F64 = 3 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_E4M3 = 2, ORC_F64 = 3, ORC_MXFP4 = 4, ORC_MXFP8 = 5 };
 enum { ORC_OK = 0, ORC_EINVAL = -1 };
 
-/* A row-major matrix view [rows][cols] in its storage format. For e4m3 the value of element
- * (r, c) is decode(code) * scale[r] (one fp32 scale per row, i.e. per output channel). */
+/* A row-major matrix view [rows][cols] in its storage format (cols counts elements).
+ *   e4m3:   value (r, c) = e4m3(code[r][c]) * scale[r], one fp32 scale per row (output channel);
+ *   MXFP8:  value (r, c) = e4m3(code[r][c]) * e8m0(scale[r][c / 32]), uint8 block scales;
+ *   MXFP4:  value (r, c) = e2m1(nibble c of row r) * e8m0(scale[r][c / 32]); a row holds cols / 2
+ *           bytes, element 2i in the low nibble of byte i and element 2i + 1 in the high one. */
 typedef struct {
   const void *data;
-  const float *scale;
+  const void *scale;
   int32_t dtype;
   int32_t pad_;
   int64_t cols;
@@ -93,12 +98,32 @@ uint8_t orc_f64_to_e4m3(double v) {
   return sign | (uint8_t)(((e + 7) << 3) | mant);
 }
 
+/* OCP E2M1 (MX spec, FP4): 1 sign, 2 exponent (bias 1) and 1 mantissa bit; exponent field 0
+ * holds the subnormal m * 0.5; no infinities or NaN; largest magnitude 6. */
+double orc_e2m1_to_f64(uint8_t c) {
+  int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+  double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return s ? -v : v;
+}
+
+/* OCP E8M0 block scale: 2^(code - 127); code 255 is NaN. */
+double orc_e8m0_to_f64(uint8_t c) { return c == 255 ? NAN : ldexp(1.0, (int)c - 127); }
+
 static double at(const orc_mat *m, int64_t r, int64_t c) {
   int64_t i = r * m->cols + c;
   switch (m->dtype) {
     case ORC_F32: return (double)((const float *)m->data)[i];
     case ORC_BF16: return orc_bf16_to_f64(((const uint16_t *)m->data)[i]);
-    case ORC_E4M3: return orc_e4m3_to_f64(((const uint8_t *)m->data)[i]) * (double)m->scale[r];
+    case ORC_E4M3:
+      return orc_e4m3_to_f64(((const uint8_t *)m->data)[i]) * (double)((const float *)m->scale)[r];
+    case ORC_MXFP8:
+      return orc_e4m3_to_f64(((const uint8_t *)m->data)[i]) *
+             orc_e8m0_to_f64(((const uint8_t *)m->scale)[r * (m->cols / 32) + c / 32]);
+    case ORC_MXFP4: {
+      const uint8_t byte = ((const uint8_t *)m->data)[r * (m->cols / 2) + c / 2];
+      return orc_e2m1_to_f64((uint8_t)(c % 2 ? byte >> 4 : byte & 15)) *
+             orc_e8m0_to_f64(((const uint8_t *)m->scale)[r * (m->cols / 32) + c / 32]);
+    }
     default: return ((const double *)m->data)[i];
   }
 }
@@ -284,14 +309,16 @@ static double sqrelu(double a) { return a > 0.0 ? a * a : 0.0; }
  *   y_t    = W_out acc (LatentMoE) or acc;
  *   y_t   += Ws_down relu(Ws_up x_t)^2 when a shared expert is present; it is always on, outside
  *            the gate normalisation, and reads the H-wide token [N3W 2.2].
- * With fp8_emulate (e4m3 experts only) u and each h row are quantised per row to e4m3 first,
- * h after rounding to bf16, which is where the fp8 path stores it. */
+ * With fp8_emulate (8-bit or block-scaled expert weights only: e4m3, MXFP8, MXFP4) u and each h
+ * row are quantised per row to e4m3 first, h after rounding to bf16, which is where those paths
+ * store it. */
 int orc_forward_tokens(const orc_layer *L, const int32_t *tokens, int32_t n, const int32_t *idx,
                        const double *gates, double *y, double *work) {
   if (!L || !idx || !gates || !y || !work) return ORC_EINVAL;
   const int32_t H = L->H, I = L->I, Is = L->I_shared, Lw = L->latent;
   const int32_t D = Lw ? Lw : H;
-  const int emulate = L->fp8_emulate && L->W_up.dtype == ORC_E4M3;
+  const int emulate = L->fp8_emulate && (L->W_up.dtype == ORC_E4M3 ||
+                                         L->W_up.dtype == ORC_MXFP8 || L->W_up.dtype == ORC_MXFP4);
   /* work holds u[D], acc[D], h[max(I, I_s)] */
   double *u = work, *acc = work + D, *h = work + 2 * (int64_t)D;
   int32_t cnt = tokens ? n : L->T;

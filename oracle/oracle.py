@@ -23,7 +23,7 @@ _LIB = os.path.join(_HERE, "_moe_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
-F32, BF16, E4M3, F64 = 0, 1, 2, 3
+F32, BF16, E4M3, F64, MXFP4, MXFP8 = 0, 1, 2, 3, 4, 5
 
 
 def build(force: bool = False) -> str:
@@ -63,6 +63,10 @@ def lib():
             L.orc_e4m3_to_f64.argtypes = [C.c_uint8]
             L.orc_f64_to_e4m3.restype = C.c_uint8
             L.orc_f64_to_e4m3.argtypes = [C.c_double]
+            L.orc_e2m1_to_f64.restype = C.c_double
+            L.orc_e2m1_to_f64.argtypes = [C.c_uint8]
+            L.orc_e8m0_to_f64.restype = C.c_double
+            L.orc_e8m0_to_f64.argtypes = [C.c_uint8]
             L.orc_logits.argtypes = [C.POINTER(OrcLayer), C.c_void_p, C.c_int32, f64p]
             L.orc_route.argtypes = [f64p, f32p, C.c_int32, C.c_int32, C.c_int32, i32p, f64p,
                                     f64p]
@@ -87,20 +91,36 @@ _DT = {np.dtype(np.float32): F32, np.dtype(np.uint16): BF16, np.dtype(np.uint8):
        np.dtype(np.float64): F64}
 
 
-def _mat(a, scale=None, keep=None):
+_BLOCK_FORMATS = {"mxfp4": MXFP4, "mxfp8": MXFP8}
+
+
+def _mat(a, scale=None, keep=None, fmt=None):
+    """View of one matrix in its storage format. ``fmt`` names a block-scaled format ("mxfp4":
+    two E2M1 codes per byte, "mxfp8": e4m3 codes; uint8 E8M0 scales per 32 columns); otherwise
+    the format follows the array's dtype (uint8 = e4m3 with fp32 per-row scales)."""
     if a is None:
         return OrcMat()
     a = np.ascontiguousarray(a)
     m = OrcMat()
     m.data = a.ctypes.data
-    m.dtype = _DT[a.dtype]
-    m.cols = a.shape[-1]
-    if m.dtype == E4M3:
-        if scale is None:
-            raise ValueError("e4m3 matrix needs its per-row scales")
-        scale = np.ascontiguousarray(scale, dtype=np.float32)
+    if fmt in _BLOCK_FORMATS:
+        m.dtype = _BLOCK_FORMATS[fmt]
+        m.cols = a.shape[-1] * (2 if fmt == "mxfp4" else 1)
+        if scale is None or np.asarray(scale).dtype != np.uint8 or \
+                np.asarray(scale).shape[-1] * 32 != m.cols:
+            raise ValueError(f"{fmt} matrix needs uint8 E8M0 scales, one per 32 columns")
+        scale = np.ascontiguousarray(scale)
         m.scale = scale.ctypes.data
         keep.append(scale)
+    else:
+        m.dtype = _DT[a.dtype]
+        m.cols = a.shape[-1]
+        if m.dtype == E4M3:
+            if scale is None:
+                raise ValueError("e4m3 matrix needs its per-row scales")
+            scale = np.ascontiguousarray(scale, dtype=np.float32)
+            m.scale = scale.ctypes.data
+            keep.append(scale)
     keep.append(a)
     return m
 
@@ -118,8 +138,9 @@ def layer(inp: dict, fp8_emulate: bool = False):
     if b is not None:
         keep.append(b)
         L.b = b.ctypes.data
-    L.W_up = _mat(inp.get("W_up"), inp.get("s_up"), keep)
-    L.W_down = _mat(inp.get("W_down"), inp.get("s_down"), keep)
+    fmt = cfg.expert_dtype
+    L.W_up = _mat(inp.get("W_up"), inp.get("s_up"), keep, fmt)
+    L.W_down = _mat(inp.get("W_down"), inp.get("s_down"), keep, fmt)
     L.Ws_up = _mat(inp.get("Ws_up"), keep=keep)
     L.Ws_down = _mat(inp.get("Ws_down"), keep=keep)
     L.W_in = _mat(inp.get("W_in"), keep=keep)
@@ -226,6 +247,16 @@ def bf16_to_f64(u) -> np.ndarray:
 
 def e4m3_to_f64(c) -> np.ndarray:
     f = lib().orc_e4m3_to_f64
+    return np.array([f(int(v)) for v in np.ravel(c)], dtype=np.float64).reshape(np.shape(c))
+
+
+def e2m1_to_f64(c) -> np.ndarray:
+    f = lib().orc_e2m1_to_f64
+    return np.array([f(int(v)) for v in np.ravel(c)], dtype=np.float64).reshape(np.shape(c))
+
+
+def e8m0_to_f64(c) -> np.ndarray:
+    f = lib().orc_e8m0_to_f64
     return np.array([f(int(v)) for v in np.ravel(c)], dtype=np.float64).reshape(np.shape(c))
 
 

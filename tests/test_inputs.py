@@ -1,5 +1,6 @@
 """CPU checks of the seeded input generator and of the calibrated bias fixtures."""
 import numpy as np
+import torch
 
 import moe_inputs as mi
 from oracle import oracle as O
@@ -64,3 +65,62 @@ def test_imbalance_bias_fixture_subset():
     mean = sub.T * sub.k / c.E
     assert np.all(counts[:4] > 8 * mean) and np.all(counts[:4] < 12 * mean)
     assert np.sum(counts == 0) >= 8
+
+
+def _spec_e2m1():
+    vals = []
+    with open(f"{mi.golden_dir()}/e2m1_values.txt") as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                vals.append(float.fromhex(line))
+    return np.array(vals)
+
+
+def test_mx_block_scale_is_floor_log2_amax_minus_emax():
+    rng = np.random.default_rng(5)
+    w = rng.standard_normal((7, 96)) * np.exp2(rng.integers(-20, 20, (7, 1)))
+    w[3, 32:64] = 0.0                                             # an all-zero block
+    for fmt, emax in (("mxfp4", 2), ("mxfp8", 8)):
+        _, sc = mi.quantize_blocks_mx(w, fmt)
+        amax = np.abs(w.reshape(7, 3, 32)).max(-1)
+        want = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1))) - emax + 127, 0)
+        assert np.array_equal(sc, want.astype(np.uint8)), fmt
+
+
+def test_mxfp8_elements_are_torch_e4m3_of_the_scaled_block():
+    rng = np.random.default_rng(6)
+    w = (rng.standard_normal((5, 64)) * np.exp2(rng.integers(-8, 8, (5, 64)))).astype(np.float32)
+    codes, sc = mi.quantize_blocks_mx(w, "mxfp8")
+    x = np.repeat(np.exp2(sc.astype(np.float64) - 127), 32, axis=-1)
+    v = np.clip(w / x, -448, 448).astype(np.float32)               # exact: x is a power of two
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref)
+
+
+def test_mxfp4_elements_are_nearest_spec_values_ties_even_and_packed_low_first():
+    spec = _spec_e2m1()
+    rng = np.random.default_rng(7)
+    w = rng.standard_normal((4, 128)) * 3.0
+    # plant exact midpoints of the E2M1 grid (times the block scale) and out-of-range values
+    mags = spec[:8]
+    w[0, :7] = (mags[:-1] + mags[1:]) / 2
+    w[0, 7] = 6.0                                                  # amax of the block: scale 2^0
+    w[1, :3] = [7.9, -7.0, 6.5]                                    # saturate at +-6 times the scale
+    codes, sc = mi.quantize_blocks_mx(w, "mxfp4")
+    x = np.repeat(np.exp2(sc.astype(np.float64) - 127), 32, axis=-1)
+    q = w / x
+    # brute force: nearest magnitude on the spec grid; on a tie the even code (mantissa bit 0)
+    d = np.abs(np.abs(q)[..., None] - mags)
+    best = d.min(-1, keepdims=True)
+    cand = np.where(d == best, np.arange(8), 99)
+    even = np.where(cand % 2 == 0, cand, 99).min(-1)
+    mag_code = np.where(even < 99, even, cand.min(-1))
+    want = (mag_code | np.where(np.signbit(q), 8, 0)).astype(np.uint8)
+    assert np.array_equal(codes & 0xF, want[:, 0::2]) and np.array_equal(codes >> 4, want[:, 1::2])
+    assert sc[0, 0] == 127
+    assert mi.decode_blocks_mx(codes, sc, "mxfp4")[0, :8].tolist() == \
+        [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, 6.0]
+    # a zero block: scale code 0 and zero codes
+    z, zs = mi.quantize_blocks_mx(np.zeros((1, 32)), "mxfp4")
+    assert zs.tolist() == [[0]] and not z.any()

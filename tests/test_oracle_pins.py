@@ -30,6 +30,10 @@ def dense_mlp(x, W_up, W_down):
 
 def f64(inp, name):
     a = inp[name]
+    fmt = inp["config"].expert_dtype
+    if name in ("W_up", "W_down") and fmt in mi.BLOCK_FORMATS:
+        # the generator's own decoder (written apart from the oracle's)
+        return mi.decode_blocks_mx(a, inp["s_up" if name == "W_up" else "s_down"], fmt)
     if a.dtype == np.uint16:
         return mi.bf16_bits_to_f32(a).astype(np.float64)
     if a.dtype == np.uint8:
@@ -84,6 +88,34 @@ def test_bf16_decode_and_generator_rounding_match_torch():
     assert np.array_equal(O.bf16_to_f64(bits[:500]),
                           torch.from_numpy(ref[:500].view(np.int16)).view(torch.bfloat16)
                           .double().numpy())
+
+
+def read_e2m1_table():
+    vals = []
+    with open(f"{mi.golden_dir()}/e2m1_values.txt") as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                vals.append(float.fromhex(line))
+    assert len(vals) == 16
+    return np.array(vals)
+
+
+def test_e2m1_decode_matches_the_spec_table():
+    table = read_e2m1_table()
+    codes = np.arange(16, dtype=np.uint8)
+    for dec in (O.e2m1_to_f64(codes), mi.decode_e2m1(codes)):
+        assert np.array_equal(dec, table)
+        assert np.array_equal(np.signbit(dec), np.signbit(table))   # 0x8 is -0
+
+
+def test_e8m0_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).double().numpy()
+    for dec in (O.e8m0_to_f64(codes), mi.decode_e8m0(codes)):
+        assert np.isnan(dec[255]) and np.isnan(ref[255])
+        assert np.array_equal(dec[:255], ref[:255])
+    assert O.e8m0_to_f64(np.array([127]))[0] == 1.0
 
 
 # ----------------------------------------------------------------------------- routing
@@ -328,6 +360,50 @@ def test_fp8_emulation_quantises_activation_rows():
     h = torch.from_numpy(h).float().to(torch.bfloat16).double().numpy()
     want = q(h) @ f64(inp, "W_down")[0].T
     np.testing.assert_allclose(r, want, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+@pytest.mark.parametrize("E,k", [(1, 1), (5, 2)])
+def test_block_scaled_experts_use_decoded_weights_exactly(fmt, E, k):
+    # Every selected expert is a squared-ReLU MLP over the block-decoded weights: checked with
+    # numpy matmul on the generator's decoder, per token and selected expert; several experts
+    # check the expert stride of packed codes and of the block scales.
+    c = cfg(E=E, k=k, T=5, H=96, I=64, act_dtype="bf16", expert_dtype=fmt)
+    inp = mi.make_layer(c, seed=17)
+    rng = np.random.default_rng(3)
+    for name in ("s_up", "s_down"):   # spread the block scales over 13 binades
+        inp[name] = (inp[name] + rng.integers(-6, 7, inp[name].shape)).astype(np.uint8)
+    assert len(np.unique(inp["s_up"])) > 8
+    r = O.forward(inp)
+    x, Wu, Wd = f64(inp, "x"), f64(inp, "W_up"), f64(inp, "W_down")
+    want = np.zeros((c.T, c.H))
+    for t in range(c.T):
+        for j in range(k):
+            e = r["idx"][t, j]
+            want[t] += r["gates"][t, j] * dense_mlp(x[t:t + 1], Wu[e], Wd[e])[0]
+    np.testing.assert_allclose(r["y"], want, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+def test_block_scaled_emulation_quantises_activation_rows(fmt):
+    # Block-scaled expert weights take the activation rows through the same per-row e4m3
+    # quantisation as e4m3 weights. With one block scale 2^-5 throughout, the same weights are
+    # an e4m3 layer exactly (element codes as e4m3 codes, row scales 2^-5), which must give the
+    # same emulated output bit for bit. (Block-scale indexing is pinned by the test above.)
+    c = cfg(E=1, k=1, T=6, H=64, I=32, act_dtype="bf16", expert_dtype=fmt)
+    inp = mi.make_layer(c, seed=18)
+    twin = dict(inp, config=dataclasses.replace(c, expert_dtype="e4m3"))
+    for w, sc in (("W_up", "s_up"), ("W_down", "s_down")):
+        inp[sc] = np.full_like(inp[sc], 127 - 5)
+        elements = mi.decode_blocks_mx(inp[w], np.full_like(inp[sc], 127), fmt)
+        twin[w] = mi.encode_e4m3(elements)
+        assert np.array_equal(mi.decode_e4m3(twin[w]), elements)
+        twin[sc] = np.full(elements.shape[:-1], 2.0 ** -5, np.float32)
+    one = (np.zeros((6, 1), np.int32), np.ones((6, 1)))
+    a = O.forward_tokens(inp, *one, fp8_emulate=True)
+    b = O.forward_tokens(twin, *one, fp8_emulate=True)
+    assert np.array_equal(a, b)
+    assert not np.array_equal(a, O.forward_tokens(inp, *one))   # emulation did change it
 
 
 def test_bias_update_sign_rule():
