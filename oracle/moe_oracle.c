@@ -311,7 +311,7 @@ static double sqrelu(double a) { return a > 0.0 ? a * a : 0.0; }
  *            the gate normalisation, and reads the H-wide token [N3W 2.2].
  * With fp8_emulate (8-bit or block-scaled expert weights only: e4m3, MXFP8, MXFP4) u and each h
  * row are quantised per row to e4m3 first, h after rounding to bf16, which is where those paths
- * store it. */
+ * store it; so is the LatentMoE projection u of a bf16 layer. */
 int orc_forward_tokens(const orc_layer *L, const int32_t *tokens, int32_t n, const int32_t *idx,
                        const double *gates, double *y, double *work) {
   if (!L || !idx || !gates || !y || !work) return ORC_EINVAL;
@@ -335,7 +335,11 @@ int orc_forward_tokens(const orc_layer *L, const int32_t *tokens, int32_t n, con
       }
       acc[d] = 0.0;
     }
-    if (emulate) quant_row_e4m3(u, D);
+    if (emulate) {
+      if (Lw && L->x.dtype == ORC_BF16)
+        for (int32_t d = 0; d < D; ++d) u[d] = round_bf16(u[d]);
+      quant_row_e4m3(u, D);
+    }
     for (int32_t j = 0; j < L->k; ++j) {
       int32_t e = idx[(int64_t)a * L->k + j];
       double g = gates[(int64_t)a * L->k + j];

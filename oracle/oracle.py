@@ -224,8 +224,19 @@ def forward_tokens(inp: dict, idx: np.ndarray, gates: np.ndarray, tokens=None,
     return y
 
 
-def forward(inp: dict, tokens=None, fp8_emulate: bool = False) -> dict:
-    """Route and run the listed tokens (all if None). Returns logits, idx, gates, margin, y."""
+def forward(inp: dict, tokens=None, fp8_emulate: bool = False, threads: int = 1) -> dict:
+    """Route and run the listed tokens (all if None). Returns logits, idx, gates, margin, y.
+
+    ``threads`` > 1 hands disjoint groups of tokens to that many threads (the C calls release
+    the interpreter lock); every token is computed exactly as in a single call."""
+    if threads > 1:
+        t = np.arange(inp["config"].T) if tokens is None else np.asarray(tokens, dtype=np.int32)
+        groups = [g for g in np.array_split(t, min(threads, max(1, len(t)))) if len(g)]
+        if len(groups) > 1:
+            from concurrent.futures import ThreadPoolExecutor
+            with ThreadPoolExecutor(len(groups)) as ex:
+                parts = list(ex.map(lambda g: forward(inp, g, fp8_emulate), groups))
+            return {k: np.concatenate([p[k] for p in parts]) for k in parts[0]}
     z = logits(inp, tokens)
     idx, g, m = route(z, inp["b"], inp["config"].k)
     y = forward_tokens(inp, idx, g, tokens, fp8_emulate)

@@ -362,6 +362,30 @@ def test_fp8_emulation_quantises_activation_rows():
     np.testing.assert_allclose(r, want, rtol=1e-12, atol=1e-13)
 
 
+def test_fp8_emulation_of_a_latent_layer_rounds_the_projection_to_bf16():
+    # LatentMoE with e4m3 experts: the projection u = W_in x is rounded to bf16 (where a bf16
+    # layer keeps it), then quantised per row like x; E=1, k=1, no shared expert; numpy matmul.
+    c = cfg(E=1, k=1, T=5, H=64, I=32, latent=48, act_dtype="bf16", expert_dtype="e4m3")
+    inp = mi.make_layer(c, seed=19)
+    r = O.forward_tokens(inp, np.zeros((5, 1), np.int32), np.ones((5, 1)), fp8_emulate=True)
+
+    def bf16(a):
+        return torch.from_numpy(a).float().to(torch.bfloat16).double().numpy()
+
+    def q(rows):
+        rows32 = rows.astype(np.float32)
+        amax = np.abs(rows32).max(1)
+        sc = (amax / np.float32(448)).astype(np.float32)
+        inv = (np.float32(448) / amax).astype(np.float32)
+        v = torch.from_numpy((rows32 * inv[:, None]).astype(np.float32))
+        return v.to(torch.float8_e4m3fn).double().numpy() * sc[:, None].astype(np.float64)
+
+    u = q(bf16(f64(inp, "x") @ f64(inp, "W_in").T))
+    h = q(bf16(np.maximum(u @ f64(inp, "W_up")[0].T, 0) ** 2))
+    want = (h @ f64(inp, "W_down")[0].T) @ f64(inp, "W_out").T
+    np.testing.assert_allclose(r, want, rtol=1e-12, atol=1e-13)
+
+
 @pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
 @pytest.mark.parametrize("E,k", [(1, 1), (5, 2)])
 def test_block_scaled_experts_use_decoded_weights_exactly(fmt, E, k):
