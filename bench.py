@@ -33,7 +33,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="nano_decode_bf16")
-    ap.add_argument("--also", default="nano_prefill_bf16,latent_decode_bf16,nano_fp8_decode",
+    ap.add_argument("--also", default="nano_prefill_bf16,latent_decode_bf16,nano_fp8_decode,"
+                                      "nano_mxfp4_decode,nano_mxfp8_decode,latent_mxfp4_decode",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--path", default="auto", choices=["auto", "grouped", "stream"])
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured graph")
@@ -53,34 +54,41 @@ def work_of(name, cfg, counts, stream=False):
     T, H, E, k, I, Is, L = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared, cfg.latent
     D, P = cfg.D, cfg.T * cfg.k
     ea = 4 if cfg.act_dtype == "f32" else 2
-    ew = {"f32": 4, "bf16": 2, "e4m3": 1}[cfg.expert_dtype]
+    # weight bytes per element; 8-bit and 4-bit experts meet e4m3 token rows
+    ew = {"f32": 4, "bf16": 2, "e4m3": 1, "mxfp8": 1, "mxfp4": 0.5}[cfg.expert_dtype]
+    narrow = cfg.expert_dtype in ("e4m3", "mxfp4", "mxfp8")
+    mx = cfg.expert_dtype in ("mxfp4", "mxfp8")
     touched = int(np.count_nonzero(counts))
+
+    def scales(rows, K):   # e4m3: fp32 per output channel; MX: one E8M0 byte per 32 along K
+        if mx:
+            return touched * rows * (K // 32)
+        return touched * rows * 4 if narrow else 0
+
     role = name.split(":")[1]
     if role == "router":
         return 2 * T * E * H, T * H * ea + E * H * ea + T * E * 4
     # stream launches: routed projection, plus the shared expert's on a bf16 plain layer
-    sh = bool(Is and not L and ew != 1)
+    sh = bool(Is and not L and not narrow)
     if role == "up":
-        scales = touched * I * 4 if ew == 1 else 0
         f = 2 * P * I * D + (2 * T * Is * H if sh else 0)
-        b = touched * I * D * ew + scales + T * D * (1 if ew == 1 else ea) + P * I * 2
+        b = touched * I * D * ew + scales(I, D) + T * D * (1 if narrow else ea) + P * I * 2
         if sh:
             b += Is * H * ea + T * Is * 2
-        return f, b
+        return f, int(b)
     if role == "down":     # fp32 outputs
-        scales = touched * D * 4 if ew == 1 else 0
         f = 2 * P * D * I + (2 * T * H * Is if sh else 0)
-        b = touched * D * I * ew + scales + P * I * (1 if ew == 1 else 2) + P * D * 4
+        b = touched * D * I * ew + scales(D, I) + P * I * (1 if narrow else 2) + P * D * 4
         if sh:
             b += H * Is * ea + T * Is * 2 + T * H * 4
-        return f, b
+        return f, int(b)
     if role == "routed_up":
-        scales = touched * I * 4 if ew == 1 else 0
-        return 2 * P * I * D, touched * I * D * ew + scales + T * D * (1 if ew == 1 else ea) + P * I * 2
+        return 2 * P * I * D, int(touched * I * D * ew + scales(I, D) +
+                                  T * D * (1 if narrow else ea) + P * I * 2)
     if role == "routed_down":
-        scales = touched * D * 4 if ew == 1 else 0
-        h_in = P * I * (1 if ew == 1 else 2)
-        return 2 * P * D * I, touched * D * I * ew + scales + h_in + P * D * (4 if stream else ea)
+        h_in = P * I * (1 if narrow else 2)
+        return 2 * P * D * I, int(touched * D * I * ew + scales(D, I) + h_in +
+                                  P * D * (4 if stream else ea))
     if role == "shared_up":
         return 2 * T * Is * H, Is * H * ea + T * H * ea + T * Is * ea
     if role == "shared_down":  # fp32 output
@@ -104,7 +112,8 @@ def kernel_of(span):
 
 
 def mfma_dtype(kernel, cfg):
-    if "fp8" in kernel or "e4m3" in kernel:
+    # the block-scaled kernels multiply MXFP4 / MXFP8 weights by e4m3 tokens: fp8 rate
+    if "fp8" in kernel or "e4m3" in kernel or "mxfp" in kernel:
         return "fp8"
     return "f32" if cfg.act_dtype == "f32" else "bf16"
 
@@ -249,6 +258,13 @@ def cpu_baseline(w, n_tokens):
                        f"thread, {dt:.1f} s")
 
 
+def dtype_of(cfg):
+    """Arithmetic types of the path: bf16, or the expert-weight format with bf16 activations."""
+    if cfg.expert_dtype in ("e4m3", "mxfp4", "mxfp8"):
+        return f"{cfg.expert_dtype}+bf16"
+    return cfg.act_dtype
+
+
 def describe(cfg):
     return dict(workload=cfg.name, description=cfg.description, T=cfg.T, H=cfg.H, E=cfg.E,
                 k=cfg.k, I=cfg.I, I_shared=cfg.I_shared, latent=cfg.latent,
@@ -276,14 +292,14 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(res["ms_per_step"], 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": "e4m3+bf16" if cfg.expert_dtype == "e4m3" else cfg.act_dtype,
+        "dtype": dtype_of(cfg),
         "data": "synthetic", "config": describe(cfg), "roofline": res["roofline"],
     }
     extra = {}
     for name in [n for n in args.also.split(",") if n and n != args.config]:
         w = prepare(name, moe, mi, torch, args.path, shared=main_w)
         r = measure(w, moe, torch, args.steps, args.warmup, args.graph)
-        extra[name] = dict(tokens_per_s=round(r["tokens_per_s"], 1),
+        extra[name] = dict(tokens_per_s=round(r["tokens_per_s"], 1), dtype=dtype_of(w["cfg"]),
                            ms_per_step=round(r["ms_per_step"], 4), roofline=r["roofline"],
                            kernel_us_per_step=r["kernel_us_per_step"])
         del w

@@ -33,7 +33,14 @@
  *   - Thread safety: stateless apart from a per-device properties cache; concurrent calls on
  *     different streams need different workspaces and outputs.
  *   - Dimension rules: H, I, I_shared and latent are multiples of 16; 1 <= k <= E <= 1024,
- *     k <= 64; T >= 0 (T == 0 is a no-op that returns MOE_OK).
+ *     k <= 64; T >= 0 (T == 0 is a no-op that returns MOE_OK). MOE_MXFP4 / MOE_MXFP8 experts
+ *     also need D (H, or latent) and I to be multiples of 32 (else MOE_ERR_INVALID_ARG).
+ *   - Expert weights of 8 or 4 bits (MOE_FP8_E4M3, MOE_MXFP4, MOE_MXFP8): the expert input rows
+ *     and the rows of h = relu(u W_up^T)^2 (rounded to bf16) are quantised per row to e4m3 with
+ *     scale amax / 448 before they meet the weights, as in "Nemotron 3 Nano：開放高效的 MoE 混合
+ *     Mamba-Transformer 智能體推理模型", section 4 (FP8 expert weights). MOE_MXFP4 / MOE_MXFP8
+ *     run on the decode (stream) path only, whatever T is; MOE_PATH_GROUPED is unsupported for
+ *     them.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -45,10 +52,20 @@
 extern "C" {
 #endif
 
+/* Expert-weight formats beyond the activation type (expert weights only, with MOE_BF16
+ * activations). MOE_MXFP4 / MOE_MXFP8 are the OCP Microscaling (MX v1.0) formats: blocks of 32
+ * consecutive elements along K (the input width of each projection) share one E8M0 scale
+ * 2^(code - 127); the elements are E2M1 (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives;
+ * two per byte, element 2i in the low nibble of byte i) or E4M3. They are the gfx950-native
+ * counterpart of the micro-block scaled FP4 of "NVIDIA Nemotron 3: Efficient and Open
+ * Intelligence", section 2.4. Scale code 255 (NaN) is not supported: a block carrying it makes
+ * its outputs undefined. */
 typedef enum {
   MOE_F32 = 0,      /* IEEE binary32 */
   MOE_BF16 = 1,     /* bfloat16 */
-  MOE_FP8_E4M3 = 2  /* OCP 8-bit E4M3 (fn: max 448, no inf), expert weights only */
+  MOE_FP8_E4M3 = 2, /* OCP 8-bit E4M3 (fn: max 448, no inf) with fp32 per-output-channel scales */
+  MOE_MXFP4 = 3,    /* OCP MXFP4: E2M1 elements, E8M0 scale per 32 along K */
+  MOE_MXFP8 = 4     /* OCP MXFP8: E4M3 elements, E8M0 scale per 32 along K */
 } moe_dtype_t;
 
 typedef enum {
@@ -60,9 +77,11 @@ typedef enum {
 } moe_status;
 
 /* desc.flags */
-#define MOE_PATH_AUTO 0u         /* stream path when the mean expert load T*k/E is <= 8 */
+#define MOE_PATH_AUTO 0u         /* stream path when the mean expert load T*k/E is <= 8, or for
+                                    MXFP4 / MXFP8 experts */
 #define MOE_PATH_GROUPED 1u      /* grouped MFMA GEMMs with a device-built tile list (prefill) */
-#define MOE_PATH_STREAM 2u       /* read each touched expert's weights once (decode; bf16 only) */
+#define MOE_PATH_STREAM 2u       /* read each touched expert's weights once (decode): bf16,
+                                    MXFP4 and MXFP8 experts, e4m3 experts without latent */
 #define MOE_PATH_MASK 3u
 #define MOE_ROUTING_GIVEN 4u     /* routing->idx and routing->gates are INPUTS: skip the router */
 
@@ -84,10 +103,12 @@ typedef struct {
   const void *x;        /* [T, H]  act_dtype */
   const void *W_r;      /* [E, H]  act_dtype (router / gating network, always in H) */
   const float *b;       /* [E]     fp32 selection bias (enters the keys, never the gates) */
-  const void *W_up;     /* [E, I, D] expert_dtype */
-  const void *W_down;   /* [E, D, I] expert_dtype */
-  const float *s_up;    /* [E, I] fp32 per-output-channel scales (MOE_FP8_E4M3 only) */
-  const float *s_down;  /* [E, D] fp32 per-output-channel scales (MOE_FP8_E4M3 only) */
+  const void *W_up;     /* [E, I, D] expert_dtype (MOE_MXFP4: [E, I, D / 2] bytes) */
+  const void *W_down;   /* [E, D, I] expert_dtype (MOE_MXFP4: [E, D, I / 2] bytes) */
+  const void *s_up;     /* MOE_FP8_E4M3: [E, I] fp32 per-output-channel scales;
+                           MOE_MXFP4 / MOE_MXFP8: [E, I, D / 32] uint8 E8M0 block scales;
+                           otherwise unused */
+  const void *s_down;   /* MOE_FP8_E4M3: [E, D] fp32; MOE_MXFP4 / MOE_MXFP8: [E, D, I / 32] uint8 */
   const void *Ws_up;    /* [I_shared, H] act_dtype, or NULL when I_shared == 0 */
   const void *Ws_down;  /* [H, I_shared] act_dtype, or NULL when I_shared == 0 */
   const void *W_in;     /* [latent, H] act_dtype (LatentMoE only) */

@@ -14,7 +14,9 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 
-MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4, MOE_MXFP8 = 0, 1, 2, 3, 4
+_EXPERT_DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_FP8_E4M3, "mxfp4": MOE_MXFP4,
+                  "mxfp8": MOE_MXFP8}
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 PATH_AUTO, PATH_GROUPED, PATH_STREAM, ROUTING_GIVEN = 0, 1, 2, 4
 _PATHS = {"auto": PATH_AUTO, "grouped": PATH_GROUPED, "stream": PATH_STREAM}
@@ -114,7 +116,21 @@ def _stream(stream):
     return C.c_void_p(s.cuda_stream)
 
 
-def make_desc(x, W_r, W_up, k, Ws_up=None, W_in=None, path="auto", routing_given=False):
+def expert_dtype_code(x, W_up, s_up=None, W_in=None, expert_dtype=None) -> int:
+    """moe_dtype_t of the expert weights: given by name, or read off the tensors (float / bf16
+    weights: their dtype; uint8 codes with fp32 scales: e4m3; with uint8 block scales: MXFP8,
+    or MXFP4 when a row holds half as many bytes as the expert input width)."""
+    if expert_dtype is not None:
+        return _EXPERT_DTYPES[expert_dtype]
+    if W_up.dtype in (torch.uint8, torch.float8_e4m3fn) and s_up is not None \
+            and s_up.dtype == torch.uint8:
+        D = W_in.shape[0] if W_in is not None else x.shape[1]
+        return MOE_MXFP4 if 2 * W_up.shape[-1] == D else MOE_MXFP8
+    return _dtype_code(W_up)
+
+
+def make_desc(x, W_r, W_up, k, Ws_up=None, W_in=None, path="auto", routing_given=False,
+              s_up=None, expert_dtype=None):
     T, H = x.shape
     E, I = W_up.shape[0], W_up.shape[1]
     d = MoeDesc()
@@ -122,7 +138,7 @@ def make_desc(x, W_r, W_up, k, Ws_up=None, W_in=None, path="auto", routing_given
     d.I_shared = Ws_up.shape[0] if Ws_up is not None else 0
     d.latent = W_in.shape[0] if W_in is not None else 0
     d.act_dtype = _dtype_code(x)
-    d.expert_dtype = _dtype_code(W_up)
+    d.expert_dtype = expert_dtype_code(x, W_up, s_up, W_in, expert_dtype)
     d.flags = _PATHS[path] | (ROUTING_GIVEN if routing_given else 0)
     return d
 
@@ -148,8 +164,9 @@ class Layer:
 
     def __init__(self, x, W_r, b, W_up, W_down, k, *, s_up=None, s_down=None, Ws_up=None,
                  Ws_down=None, W_in=None, W_out=None, path="auto", routing=None,
-                 routing_given=False, out=None):
-        self.desc = make_desc(x, W_r, W_up, k, Ws_up, W_in, path, routing_given)
+                 routing_given=False, out=None, expert_dtype=None):
+        self.desc = make_desc(x, W_r, W_up, k, Ws_up, W_in, path, routing_given, s_up,
+                              expert_dtype)
         w = MoeWeights()
         w.x, w.W_r, w.b, w.W_up, w.W_down = _p(x), _p(W_r), _p(b), _p(W_up), _p(W_down)
         w.s_up, w.s_down = _p(s_up), _p(s_down)
@@ -250,7 +267,7 @@ def trace_records() -> list:
 
 def to_device(inp: dict, device="cuda") -> dict:
     """numpy arrays of a ``moe_inputs.make_layer`` dict -> torch tensors on ``device``
-    (uint16 bf16 bit patterns become torch.bfloat16; e4m3 codes stay uint8)."""
+    (uint16 bf16 bit patterns become torch.bfloat16; e4m3, E2M1 and E8M0 codes stay uint8)."""
     import numpy as np
     out = {}
     for name, a in inp.items():

@@ -10,7 +10,9 @@
 
 namespace moe {
 
-enum class Elt : int { F32 = 0, BF16 = 1, FP8 = 2 };
+// FP8 is OCP e4m3. MXFP4 / MXFP8 are OCP microscaling weight formats (E2M1 or E4M3 elements,
+// one E8M0 scale per 32 consecutive K elements); only the decode streaming kernel reads them.
+enum class Elt : int { F32 = 0, BF16 = 1, FP8 = 2, MXFP4 = 3, MXFP8 = 4 };
 
 enum class Epi : int {
   Store = 0,        // C = acc

@@ -70,16 +70,19 @@ enum StreamStore : int { kStoreF32 = 0, kStoreSqRelu = 1, kStoreBF16 = 2 };
 //   out[r, n] = act( sum_k A[src(r), k] * W[g][n, k] )
 // act = bf16(relu(acc)^2) for the up projection, fp32 acc for the down projection.
 struct StreamParams {
-  int fp8 = 0;                        // 1: routed operands are e4m3 codes (no shared slot)
+  // routed weight format: BF16 (bf16 tokens), or FP8 / MXFP4 / MXFP8 (e4m3 token codes with a
+  // scale per source row; no shared slot)
+  Elt wt = Elt::BF16;
   // routed experts
   const void* A = nullptr;            // activation rows (bf16 or e4m3), lda elements apart
   int64_t lda = 0;
-  const float* a_scale = nullptr;     // e4m3: dequantisation scale per source row
+  const float* a_scale = nullptr;     // e4m3 tokens: dequantisation scale per source row
   const int32_t* gather = nullptr;    // source row of pair row r = gather[r] (nullptr: r)
   const int32_t* offs = nullptr;      // [E + 1]
   int E = 0;
-  const void* W = nullptr;            // [E][N][K]
-  const float* w_scale = nullptr;     // e4m3: per output channel [E][N]
+  const void* W = nullptr;            // [E][N][K] (MXFP4: [E][N][K / 2] bytes)
+  const float* w_scale = nullptr;     // FP8: per output channel [E][N]
+  const uint8_t* w_mx = nullptr;      // MXFP4 / MXFP8: E8M0 block scales [E][N][K / 32]
   int N = 0, K = 0;
   void* out = nullptr;                // pair rows, ldo elements apart
   int64_t ldo = 0;

@@ -40,23 +40,31 @@ int32_t make_plan(const moe_desc_t* d, bool latent_call, Plan* pl) {
   if (T * k > INT32_MAX / 2 || T * (H > L ? H : L) > ((int64_t)1 << 40)) return MOE_ERR_INVALID_ARG;
   if (d->act_dtype != MOE_F32 && d->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   const bool fp8 = d->expert_dtype == MOE_FP8_E4M3;
-  if (!fp8 && d->expert_dtype != d->act_dtype) return MOE_ERR_UNSUPPORTED;
-  if (fp8 && d->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  const bool mx = d->expert_dtype == MOE_MXFP4 || d->expert_dtype == MOE_MXFP8;
+  if (!fp8 && !mx && d->expert_dtype != d->act_dtype) return MOE_ERR_UNSUPPORTED;
+  if ((fp8 || mx) && d->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  // block-scaled rows are whole 32-element blocks, in both projections
+  const int64_t Dw = L ? L : H;
+  if (mx && (Dw % 32 || I % 32)) return MOE_ERR_INVALID_ARG;
   if (d->flags & ~(MOE_PATH_MASK | MOE_ROUTING_GIVEN)) return MOE_ERR_INVALID_ARG;
   Plan p;
   p.act = d->act_dtype == MOE_F32 ? Elt::F32 : Elt::BF16;
-  p.ex = fp8 ? Elt::FP8 : p.act;
+  p.ex = fp8 ? Elt::FP8
+             : d->expert_dtype == MOE_MXFP4 ? Elt::MXFP4
+             : d->expert_dtype == MOE_MXFP8 ? Elt::MXFP8 : p.act;
   p.T = (int)T; p.H = (int)H; p.E = (int)E; p.k = (int)k; p.I = (int)I; p.Is = (int)Is;
   p.L = (int)L; p.D = L ? (int)L : (int)H; p.P = (int)(T * k);
   const uint32_t path = d->flags & MOE_PATH_MASK;
-  // the decode path streams bf16 experts, and e4m3 experts of a plain (non-latent) layer
-  const bool stream_ok = p.act == Elt::BF16 && (p.ex == Elt::BF16 || (p.ex == Elt::FP8 && !p.L));
+  // the decode path streams bf16 experts, e4m3 experts of a plain (non-latent) layer, and
+  // block-scaled experts, which have no other path
+  const bool stream_ok =
+      p.act == Elt::BF16 && (p.ex == Elt::BF16 || (p.ex == Elt::FP8 && !p.L) || mx);
   if (path == MOE_PATH_AUTO)
-    p.path = (stream_ok && (int64_t)p.P <= 8 * E) ? MOE_PATH_STREAM : MOE_PATH_GROUPED;
+    p.path = (stream_ok && ((int64_t)p.P <= 8 * E || mx)) ? MOE_PATH_STREAM : MOE_PATH_GROUPED;
   else if (path == MOE_PATH_STREAM)
     p.path = stream_ok ? MOE_PATH_STREAM : -1;
   else if (path == MOE_PATH_GROUPED)
-    p.path = MOE_PATH_GROUPED;
+    p.path = mx ? -1 : MOE_PATH_GROUPED;
   else
     return MOE_ERR_INVALID_ARG;
   if (p.path < 0) return MOE_ERR_UNSUPPORTED;
@@ -82,7 +90,7 @@ int32_t make_plan(const moe_desc_t* d, bool latent_call, Plan* pl) {
   p.pos = take(P * 4);
   p.dscratch = take(dispatch_scratch_ints(p.T, p.E) * 4);
   p.mt_start = take((Ez + 1) * 4);
-  if (fp8) {
+  if (fp8 || mx) {  // per-row e4m3 copies of the expert inputs and of h
     p.xq = take(Tz * (size_t)p.D);
     p.sx = take(Tz * 4);
     p.hq = take(P * (size_t)p.I);
@@ -207,9 +215,10 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
   if (pl.T == 0) return MOE_OK;  // empty batch: nothing to read or write
   if (!w || !y) return MOE_ERR_INVALID_ARG;
   const bool given = d->flags & MOE_ROUTING_GIVEN;
-  const bool fp8 = pl.ex == Elt::FP8;
+  // 8-bit or 4-bit expert weights: e4m3 with per-channel scales, or MXFP4 / MXFP8 blocks
+  const bool narrow = pl.ex == Elt::FP8 || pl.ex == Elt::MXFP4 || pl.ex == Elt::MXFP8;
   if (!w->x || !w->b || !w->W_up || !w->W_down || (!given && !w->W_r)) return MOE_ERR_INVALID_ARG;
-  if (fp8 && (!w->s_up || !w->s_down)) return MOE_ERR_INVALID_ARG;
+  if (narrow && (!w->s_up || !w->s_down)) return MOE_ERR_INVALID_ARG;
   if (pl.Is && (!w->Ws_up || !w->Ws_down)) return MOE_ERR_INVALID_ARG;
   if (pl.L && (!w->W_in || !w->W_out)) return MOE_ERR_INVALID_ARG;
   if (given && (!r || !r->idx || !r->gates)) return MOE_ERR_INVALID_ARG;
@@ -242,12 +251,12 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
   const Elt act = pl.act;
   const bool stream_path = pl.path == MOE_PATH_STREAM;
 
-  // (0) decode path of a plain e4m3 layer: the bf16 shared expert (weight 1, every token,
-  // independent of routing) cannot share the e4m3 launches, so it streams on the side stream
-  // while the routed work proceeds on `s`. (A bf16 layer deals its shared-expert units out in
-  // the routed launches instead, which measured faster there.)
+  // (0) decode path of a plain layer with 8-bit or 4-bit experts: the bf16 shared expert
+  // (weight 1, every token, independent of routing) cannot share the narrow launches, so it
+  // streams on the side stream while the routed work proceeds on `s`. (A bf16 layer deals its
+  // shared-expert units out in the routed launches instead, which measured faster there.)
   Side* side = nullptr;
-  if (stream_path && fp8 && Is && !L) {
+  if (stream_path && narrow && Is && !L) {
     MOE_TRY(side_of(&side));
     MOE_TRY(hipEventRecord(side->fork, s));
     MOE_TRY(hipStreamWaitEvent(side->s, side->fork, 0));
@@ -308,26 +317,38 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
   }
   // (4) routed experts (+ the shared expert on the stream path of a plain layer)
   Elt y_elt = act;
-  if (stream_path && fp8) {
-    // e4m3 experts: expert inputs and the h rows quantised per row, routed units on the e4m3
-    // streaming kernel; the bf16 shared expert streams in launches of its own
+  if (stream_path && narrow) {
+    // 8-bit / 4-bit experts: expert inputs and the h rows quantised per row to e4m3, routed
+    // units on the narrow streaming kernel; the bf16 shared expert streams in launches of its
+    // own
     y_elt = Elt::F32;
     uint8_t* xq = base + pl.xq;
     float* sx = (float*)(base + pl.sx);
     uint8_t* hq = base + pl.hq;
     float* sh = (float*)(base + pl.sh);
+    const bool mx = pl.ex != Elt::FP8;
+    const char* up_name = pl.ex == Elt::FP8     ? "stream_e4m3:up"
+                          : pl.ex == Elt::MXFP4 ? "stream_mxfp4:up"
+                                                : "stream_mxfp8:up";
+    const char* dn_name = pl.ex == Elt::FP8     ? "stream_e4m3:down"
+                          : pl.ex == Elt::MXFP4 ? "stream_mxfp4:down"
+                                                : "stream_mxfp8:down";
     {
       MOE_SPAN("quant_rows:x");
       MOE_TRY(launch_quant_rows((const uint16_t*)xin, D, T, D, xq, sx, s));
     }
     StreamParams up;
-    up.fp8 = 1;
+    up.wt = pl.ex;
     up.A = xq; up.lda = D; up.a_scale = sx; up.gather = perm; up.offs = offsets; up.E = E;
-    up.W = w->W_up; up.w_scale = w->s_up; up.N = I; up.K = D; up.out = h; up.ldo = I;
+    up.W = w->W_up; up.N = I; up.K = D; up.out = h; up.ldo = I;
+    if (mx)
+      up.w_mx = (const uint8_t*)w->s_up;
+    else
+      up.w_scale = (const float*)w->s_up;
     up.store = kStoreSqRelu;
     up.slice_e = slices; up.slice_r = slices + max_sl; up.n_slices = slices + 2 * max_sl;
     {
-      MOE_SPAN("stream_e4m3:up");
+      MOE_SPAN(up_name);
       MOE_TRY(launch_stream(up, s));
     }
     {
@@ -335,13 +356,17 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
       MOE_TRY(launch_quant_rows((const uint16_t*)h, I, P, I, hq, sh, s));
     }
     StreamParams dn;
-    dn.fp8 = 1;
+    dn.wt = pl.ex;
     dn.A = hq; dn.lda = I; dn.a_scale = sh; dn.offs = offsets; dn.E = E;
-    dn.W = w->W_down; dn.w_scale = w->s_down; dn.N = D; dn.K = I; dn.out = Y; dn.ldo = D;
+    dn.W = w->W_down; dn.N = D; dn.K = I; dn.out = Y; dn.ldo = D;
+    if (mx)
+      dn.w_mx = (const uint8_t*)w->s_down;
+    else
+      dn.w_scale = (const float*)w->s_down;
     dn.store = kStoreF32;
     dn.slice_e = slices; dn.slice_r = slices + max_sl; dn.n_slices = slices + 2 * max_sl;
     {
-      MOE_SPAN("stream_e4m3:down");
+      MOE_SPAN(dn_name);
       MOE_TRY(launch_stream(dn, s));
     }
   } else if (stream_path) {
@@ -385,7 +410,7 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
     dn.B = w->W_down; dn.ldb = I; dn.b_gstride = (int64_t)D * I;
     dn.C = Y; dn.ldc = D; dn.N = D; dn.K = I;
     dn.offs = offsets; dn.mt_start = mt_start; dn.G = E;
-    if (fp8) {
+    if (pl.ex == Elt::FP8) {
       // e4m3 expert weights: the expert input rows and the h rows are quantised per row to
       // e4m3 (scale = row amax / 448) and both projections run on fp8 matrix cores.
       uint8_t* xq = base + pl.xq;
@@ -396,7 +421,7 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
         MOE_SPAN("quant_rows:x");
         MOE_TRY(launch_quant_rows((const uint16_t*)xin, D, T, D, xq, sx, s));
       }
-      up.A = xq; up.a_scale = sx; up.b_scale = w->s_up;
+      up.A = xq; up.a_scale = sx; up.b_scale = (const float*)w->s_up;
       {
         MOE_SPAN("gemm_fp8_sqrelu:routed_up");
         MOE_TRY(launch_gemm(GemmKind{Elt::FP8, Elt::BF16, Epi::SqRelu}, up, max_mt, s));
@@ -405,7 +430,7 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
         MOE_SPAN("quant_rows:h");
         MOE_TRY(launch_quant_rows((const uint16_t*)h, I, P, I, hq, sh, s));
       }
-      dn.A = hq; dn.a_scale = sh; dn.b_scale = w->s_down;
+      dn.A = hq; dn.a_scale = sh; dn.b_scale = (const float*)w->s_down;
       {
         MOE_SPAN("gemm_fp8_store:routed_down");
         MOE_TRY(launch_gemm(GemmKind{Elt::FP8, Elt::BF16, Epi::Store}, dn, max_mt, s));

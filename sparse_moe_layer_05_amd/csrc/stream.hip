@@ -14,10 +14,13 @@
 // next one is resolved, and its first k batch is in flight while the current unit's last batch
 // is multiplied. Inside a unit the weights are the matrix-core "A" operand and the tokens the
 // "B" operand, loaded straight from HBM into registers (no LDS): bf16 through
-// v_mfma_f32_16x16x32_bf16, or e4m3 expert weights with e4m3 token rows through
-// v_mfma_scale_f32_16x16x128_f8f6f4 (per-channel and per-token scales applied to the result,
-// as in "Nemotron 3 Nano：開放高效的 MoE 混合 Mamba-Transformer 智能體推理模型", section 4,
-// FP8 expert weights).
+// v_mfma_f32_16x16x32_bf16, or 8-bit / 4-bit expert weights with e4m3 token rows through
+// v_mfma_scale_f32_16x16x128_f8f6f4: e4m3 weights with per-channel scales applied to the result
+// ("Nemotron 3 Nano：開放高效的 MoE 混合 Mamba-Transformer 智能體推理模型", section 4, FP8 expert
+// weights), or OCP microscaling MXFP4 (E2M1) / MXFP8 (E4M3) weights whose E8M0 block scales the
+// matrix core applies itself (the native gfx950 counterpart of the micro-block scaled FP4 in
+// "NVIDIA Nemotron 3: Efficient and Open Intelligence", section 2.4). Token scales are applied
+// to the result.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -46,32 +49,65 @@ __device__ __forceinline__ void store_block(const f32x4_t v, void* out, int64_t 
   }
 }
 
-// Operand element types: bf16 (v_mfma_f32_16x16x32_bf16, 32 elements = 64 bytes per k step)
-// and OCP e4m3 (v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales, 128 elements = 128
-// bytes per k step). Lane l holds 16 (bf16) or 32 (e4m3) consecutive bytes of row l % 16 at byte
-// (l / 16) * LB of each step, for weights and tokens alike; the result register r of lane l is
-// out[weight row (l / 16) * 4 + r][token l % 16].
+// Operand layouts. A k step is KS elements, one matrix-core instruction. In every step lane l
+// holds weight row l % 16 and token row l % 16; the result register r of lane l is
+// out[weight row (l / 16) * 4 + r][token l % 16]. With g = l / 16, the bytes a lane loads in a
+// step are CW (weights) or CA (tokens) 16-byte chunks at byte LW * g + c * CWS, or
+// LA * g + c * CAS, from the step's start:
+//  - bf16 (16x16x32 bf16): 8 elements 8g .. 8g + 7 of the step, one chunk;
+//  - e4m3 x e4m3 with unit block scales (16x16x128): the lane's 32 bytes 32g .. 32g + 31; any
+//    order of k serves as long as both operands use it;
+//  - with real block scales the matrix core's own order of k matters. It takes an e4m3
+//    operand's k as 16g .. 16g + 15 and 64 + 16g .. 64 + 16g + 15 (two chunks 64 bytes apart),
+//    an E2M1 operand's k as 32g .. 32g + 31 (one chunk of 16 bytes, element 2i in the low
+//    nibble of byte i), and the E8M0 scale a lane passes as covering k 32g .. 32g + 31 of its
+//    row. So MXFP4 / MXFP8 weights and the e4m3 tokens they meet are loaded in that order.
 template <Elt T> struct Fmt;
+// R: blocks of 16 weight rows per unit, sharing the unit's token loads.
 template <> struct Fmt<Elt::BF16> {
-  static constexpr int SB = 64, LB = 16, U = 6;  // step bytes, lane bytes, steps per batch
+  static constexpr int KS = 32, U = 6, R = 1;    // elements per step, steps per batch
+  static constexpr int WH = 4, AB = 2;           // weight half-bytes / token bytes per element
+  static constexpr int CW = 1, LW = 16, CWS = 0;
+  static constexpr int CA = 1, LA = 16, CAS = 0;
 };
 template <> struct Fmt<Elt::FP8> {
-  static constexpr int SB = 128, LB = 32, U = 3;
+  static constexpr int KS = 128, U = 3, R = 1;
+  static constexpr int WH = 2, AB = 1;
+  static constexpr int CW = 2, LW = 32, CWS = 16;
+  static constexpr int CA = 2, LA = 32, CAS = 16;
 };
+// 4-bit weights: a 16-row unit would carry half the bytes of an 8-bit one for the same fixed
+// cost per unit and twice as many token bytes per weight byte; two row blocks restore both.
+// (Block-scaled widths are multiples of 32, so both row blocks are always whole.)
+template <> struct Fmt<Elt::MXFP4> {
+  static constexpr int KS = 128, U = 8, R = 2;
+  static constexpr int WH = 1, AB = 1;
+  static constexpr int CW = 1, LW = 16, CWS = 0;
+  static constexpr int CA = 2, LA = 16, CAS = 64;
+};
+template <> struct Fmt<Elt::MXFP8> {
+  static constexpr int KS = 128, U = 4, R = 1;
+  static constexpr int WH = 2, AB = 1;
+  static constexpr int CW = 2, LW = 16, CWS = 64;
+  static constexpr int CA = 2, LA = 16, CAS = 64;
+};
+template <Elt T> constexpr bool kBlockScaled = T == Elt::MXFP4 || T == Elt::MXFP8;
+constexpr int kMxBlock = 32;  // elements per E8M0 scale
 
 // A unit resolved to this lane's pointers. Pointers include the lane's byte offset within a k
 // step.
 struct Unit {
   const uint8_t* w;   // this lane's weight row
   const uint8_t* a;   // this lane's token row
+  const uint8_t* wx;  // MXFP4 / MXFP8: E8M0 scales of this lane's weight row, from block g
   void* out;
   int64_t ldo;
   int64_t orow;       // output row of this lane's token
-  int n;              // first of this lane's 4 output columns
-  int N, KB;          // weight rows of the expert, bytes of a row (K * element size)
+  int n;              // first of this lane's 4 output columns (row block r: n + 16 r)
+  int N, K;           // weight rows of the expert, elements of a row
   int nrows;          // tokens of the slice
-  float asc;          // e4m3: this lane's token scale
-  const float* wsc;   // e4m3: scales of this lane's 4 output channels
+  float asc;          // e4m3 tokens: this lane's token scale
+  const float* wsc;   // FP8: scales of this lane's 4 output channels
 };
 
 // Streams the units this wave is dealt: first, first + nwaves, ... below total;
@@ -88,8 +124,12 @@ struct Unit {
 template <Elt T, bool kFull, class Resolve>
 __device__ void stream_units(int first, int total, int nwaves, int lane, int mode,
                              Resolve resolve) {
-  constexpr int SB = Fmt<T>::SB, LB = Fmt<T>::LB, U = Fmt<T>::U, C = LB / 16, BB = U * SB;
-  const int lb = (lane >> 4) * LB;  // this lane's byte offset within a step
+  using F = Fmt<T>;
+  constexpr int KS = F::KS, U = F::U, R = F::R, CW = F::CW, CA = F::CA, BK = U * KS;
+  constexpr int SW = KS * F::WH / 2, SA = KS * F::AB;  // bytes of a step
+  constexpr bool kMx = kBlockScaled<T>;
+  const int g = lane >> 4;
+  const int lbw = g * F::LW, lba = g * F::LA;  // this lane's byte offsets within a step
   const int tr = lane & 15;
   if (first >= total) return;
   Unit cur, nxt;
@@ -98,106 +138,153 @@ __device__ void stream_units(int first, int total, int nwaves, int lane, int mod
   int un = u + nwaves < total ? u + nwaves : -1;
   if (un >= 0) resolve(un, nxt);
 
-  auto nbat_of = [&](int KB) { return cdiv(KB, BB); };
-  auto kbase = [&](int KB, int b) { return kFull ? min(b * BB, KB - BB) : b * BB; };
+  auto nbat_of = [&](int K) { return cdiv(K, BK); };
+  auto kbase = [&](int K, int b) { return kFull ? min(b * BK, K - BK) : b * BK; };
   // loads of batch b of unit s, or of batch 0 of unit o when other is set (chosen field by
   // field: choosing a whole unit would put both in memory)
-  auto issue = [&](const Unit& s, const Unit& o, bool other, int b, uint4* wf, uint4* xf) {
-    const int KB = other ? o.KB : s.KB;
+  auto issue = [&](const Unit& s, const Unit& o, bool other, int b, uint4* wf, uint4* xf,
+                   int* sf) {
+    const int K = other ? o.K : s.K;
     const uint8_t* w = other ? o.w : s.w;
     const uint8_t* a = other ? o.a : s.a;
-    const int kb = kbase(KB, b);
+    const int kb = kbase(K, b);
+    const int kbw = kb * F::WH / 2, kba = kb * F::AB;
+    const int KBw = K * F::WH / 2, KBa = K * F::AB;
 #pragma unroll
-    for (int q = 0; q < U; ++q)
+    for (int q = 0; q < U; ++q) {
 #pragma unroll
-      for (int c = 0; c < C; ++c) {
-        const int off = kFull ? kb + q * SB + c * 16 : min(kb + q * SB + c * 16, KB - 16 - lb);
-        wf[q * C + c] = *(const uint4*)(w + off);
-        xf[q * C + c] = *(const uint4*)(a + off);
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < CW; ++c) {
+          const int off = kbw + q * SW + c * F::CWS;
+          wf[(q * R + r) * CW + c] = *(const uint4*)(w + (int64_t)r * kUnitRows * KBw +
+                                                     (kFull ? off : min(off, KBw - 16 - lbw)));
+        }
+#pragma unroll
+      for (int c = 0; c < CA; ++c) {
+        const int off = kba + q * SA + c * F::CAS;
+        xf[q * CA + c] = *(const uint4*)(a + (kFull ? off : min(off, KBa - 16 - lba)));
       }
+      if constexpr (kMx) {
+        const uint8_t* wx = other ? o.wx : s.wx;
+        const int blk = kb / kMxBlock + q * (KS / kMxBlock);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          sf[q * R + r] = wx[r * kUnitRows * (K / kMxBlock) +
+                             (kFull ? blk : min(blk, K / kMxBlock - 1 - g))];
+      }
+    }
   };
   // last batch b: zero the weight chunks that an earlier batch already covered, or that lie
   // past K
-  auto mask = [&](int KB, int b, uint4* wf) {
-    const int kb = kbase(KB, b);
+  auto mask = [&](int K, int b, uint4* wf) {
+    const int kb = kbase(K, b);
 #pragma unroll
     for (int q = 0; q < U; ++q)
 #pragma unroll
-      for (int c = 0; c < C; ++c) {
-        const int at = kb + q * SB + lb + c * 16;
-        const bool drop = kFull ? at < b * BB : at >= KB;
-        if (drop) wf[q * C + c] = make_uint4(0, 0, 0, 0);
+      for (int c = 0; c < CW; ++c) {
+        const int at = kb + q * KS + (lbw + c * F::CWS) * 2 / F::WH;  // first element
+        const bool drop = kFull ? at < b * BK : at >= K;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          if (drop) wf[(q * R + r) * CW + c] = make_uint4(0, 0, 0, 0);
       }
   };
-  auto mfma = [&](const uint4* wf, const uint4* xf, int q, f32x4_t acc) {
+  auto cat8 = [](uint4 p, uint4 q) {
+    return i32x8_t{(int)p.x, (int)p.y, (int)p.z, (int)p.w, (int)q.x, (int)q.y, (int)q.z,
+                   (int)q.w};
+  };
+  // step q of row block r
+  auto mfma = [&](const uint4* wf, const uint4* xf, const int* sf, int q, int r, f32x4_t acc) {
+    const int i = q * R + r;
     if constexpr (T == Elt::BF16) {
-      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wf[q]),
+      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wf[i]),
                                                     __builtin_bit_cast(bf16x8_t, xf[q]), acc,
                                                     0, 0, 0);
+    } else if constexpr (T == Elt::FP8) {
+      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          cat8(wf[2 * i], wf[2 * i + 1]), cat8(xf[2 * q], xf[2 * q + 1]), acc, 0, 0, 0, 127, 0,
+          127);
+    } else if constexpr (T == Elt::MXFP8) {
+      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          cat8(wf[2 * i], wf[2 * i + 1]), cat8(xf[2 * q], xf[2 * q + 1]), acc, 0, 0, 0, sf[i],
+          0, 127);
     } else {
-      const uint4 w0 = wf[2 * q], w1 = wf[2 * q + 1], x0 = xf[2 * q], x1 = xf[2 * q + 1];
-      const i32x8_t wa = {(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w,
-                          (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
-      const i32x8_t xa = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                          (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa, xa, acc, 0, 0, 0, 127, 0, 127);
+      // E2M1 weights (format 4) fill the operand's first four registers
+      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          cat8(wf[i], make_uint4(0, 0, 0, 0)), cat8(xf[2 * q], xf[2 * q + 1]), acc, 4, 0, 0,
+          sf[i], 0, 127);
     }
   };
 
-  uint4 w0[U * C], w1[U * C], x0[U * C], x1[U * C];
-  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  int b = 0, nbat = nbat_of(cur.KB);
-  // One k batch: put the following batch in flight into (wnxt, xnxt), multiply (wcur, xcur).
-  // After a wave's last unit the following batch re-reads the unit's first one (unused) so that
-  // the load count stays the same. Returns false once the wave is done.
-  auto step = [&](uint4* wcur, uint4* xcur, uint4* wnxt, uint4* xnxt) {
-    const bool last = b + 1 == nbat;
-    issue(cur, nxt, last && un >= 0, last ? 0 : b + 1, wnxt, xnxt);
-    if (last) mask(cur.KB, b, wcur);
+  uint4 w0[U * R * CW], w1[U * R * CW], x0[U * CA], x1[U * CA];
+  int s0[U * R], s1[U * R];
+  f32x4_t acc[R];
 #pragma unroll
-    for (int q = 0; q < U; ++q) acc = mfma(wcur, xcur, q, acc);
+  for (int r = 0; r < R; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int b = 0, nbat = nbat_of(cur.K);
+  // One k batch: put the following batch in flight into (wnxt, xnxt, snxt), multiply the
+  // current one. After a wave's last unit the following batch re-reads the unit's first one
+  // (unused) so that the load count stays the same. Returns false once the wave is done.
+  auto step = [&](uint4* wcur, uint4* xcur, int* scur, uint4* wnxt, uint4* xnxt, int* snxt) {
+    const bool last = b + 1 == nbat;
+    issue(cur, nxt, last && un >= 0, last ? 0 : b + 1, wnxt, xnxt, snxt);
+    if (last) mask(cur.K, b, wcur);
+#pragma unroll
+    for (int q = 0; q < U; ++q)
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = mfma(wcur, xcur, scur, q, r, acc[r]);
     if (!last) {
       ++b;
       return true;
     }
-    // unit done: acc[r] = out[token tr][n + r]; lanes holding a real token store
-    if (tr < cur.nrows && cur.n < cur.N) {
-      if constexpr (T == Elt::FP8) {
-        const float4 sc = *(const float4*)cur.wsc;
-        acc[0] *= cur.asc * sc.x;
-        acc[1] *= cur.asc * sc.y;
-        acc[2] *= cur.asc * sc.z;
-        acc[3] *= cur.asc * sc.w;
+    // unit done: acc[r][i] = out[token tr][n + 16 r + i]; lanes holding a real token store
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      f32x4_t v = acc[r];
+      if (tr < cur.nrows && cur.n + kUnitRows * r < cur.N) {
+        if constexpr (T == Elt::FP8) {
+          const float4 sc = *(const float4*)cur.wsc;
+          v[0] *= cur.asc * sc.x;
+          v[1] *= cur.asc * sc.y;
+          v[2] *= cur.asc * sc.z;
+          v[3] *= cur.asc * sc.w;
+        } else if constexpr (kMx) {
+          v[0] *= cur.asc;
+          v[1] *= cur.asc;
+          v[2] *= cur.asc;
+          v[3] *= cur.asc;
+        }
+        store_block(v, cur.out, cur.ldo, cur.orow, cur.n + kUnitRows * r, mode);
       }
-      store_block(acc, cur.out, cur.ldo, cur.orow, cur.n, mode);
+      acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (un < 0) return false;
     cur = nxt;
     u = un;
     b = 0;
-    nbat = nbat_of(cur.KB);
+    nbat = nbat_of(cur.K);
     un = u + nwaves < total ? u + nwaves : -1;
     if (un >= 0) resolve(un, nxt);
     return true;
   };
-  issue(cur, cur, false, 0, w0, x0);
+  issue(cur, cur, false, 0, w0, x0, s0);
   for (;;) {
-    if (!step(w0, x0, w1, x1)) break;
-    if (!step(w1, x1, w0, x0)) break;
+    if (!step(w0, x0, s0, w1, x1, s1)) break;
+    if (!step(w1, x1, s1, w0, x0, s0)) break;
   }
 }
 
-// The units of one launch that this wave streams with operands of type T: the shared expert's
+// The units of one launch that this wave streams with weights of type T: the shared expert's
 // (shared_part, bf16 only) and the routed experts' (routed_part).
 template <Elt T>
 __device__ void run_units(const StreamParams& p, int wave, int nwaves, bool shared_part,
                           bool routed_part) {
-  constexpr int EB = T == Elt::FP8 ? 1 : 2;
-  constexpr int LB = Fmt<T>::LB;
+  using F = Fmt<T>;
   const int lane = threadIdx.x & 63;
   const int tr = lane & 15;
-  const int lb = (lane >> 4) * LB;
+  const int g = lane >> 4;
+  const int lbw = g * F::LW, lba = g * F::LA;
 
   // units [0, nsh): the shared expert, row block major, its token slices minor (slices that
   // share weight rows run side by side and share them through L2);
@@ -206,7 +293,7 @@ __device__ void run_units(const StreamParams& p, int wave, int nwaves, bool shar
   const int nss = p.Ws && shared_part ? cdiv(p.Ts, kSliceRows) : 0;
   const int nsh = nss ? cdiv(p.Ns, kUnitRows) * nss : 0;
   const int nsl = p.n_slices && routed_part ? sload(p.n_slices, 0) : 0;
-  const int nbr = cdiv(p.N, kUnitRows);
+  const int nbr = cdiv(p.N, kUnitRows * F::R);
   const int nrt = nbr * nsl;
   const uint8_t* As = (const uint8_t*)p.As;
   const uint8_t* Ws = (const uint8_t*)p.Ws;
@@ -214,27 +301,28 @@ __device__ void run_units(const StreamParams& p, int wave, int nwaves, bool shar
   const uint8_t* W = (const uint8_t*)p.W;
   auto resolve = [&](int u, Unit& s) {
     int n0, src;
-    if (u < nsh) {
+    if (u < nsh) {  // bf16 shared expert (only with T == BF16)
       n0 = (u / nss) * kUnitRows;
       const int r0 = (u % nss) * kSliceRows;
       s.nrows = min(p.Ts - r0, kSliceRows);
       s.orow = r0 + tr;
       src = r0 + min(tr, s.nrows - 1);
-      s.a = As + (int64_t)src * p.lda_s * EB + lb;
-      s.w = Ws + (int64_t)min(n0 + tr, p.Ns - 1) * p.Ks * EB + lb;
+      s.a = As + (int64_t)src * p.lda_s * F::AB + lba;
+      s.w = Ws + (int64_t)min(n0 + tr, p.Ns - 1) * p.Ks * F::WH / 2 + lbw;
+      s.wx = nullptr;
       s.out = p.out_s;
       s.ldo = p.ldo_s;
       s.N = p.Ns;
-      s.KB = p.Ks * EB;
+      s.K = p.Ks;
       s.asc = 1.f;
       s.wsc = nullptr;
     } else {
       const int v = u - nsh;
       const int i = v / nbr;
-      n0 = (v % nbr) * kUnitRows;
-      const int g = sload(p.slice_e, i);
+      n0 = (v % nbr) * kUnitRows * F::R;
+      const int e = sload(p.slice_e, i);
       const int r0 = sload(p.slice_r, i);
-      s.nrows = min(sload(p.offs, g + 1) - r0, kSliceRows);
+      s.nrows = min(sload(p.offs, e + 1) - r0, kSliceRows);
       s.orow = r0 + tr;
       src = r0 + min(tr, s.nrows - 1);
       if (p.gather) {
@@ -247,21 +335,22 @@ __device__ void run_units(const StreamParams& p, int wave, int nwaves, bool shar
         }
         src = row;
       }
-      s.a = A + (int64_t)src * p.lda * EB + lb;
-      s.w = W + ((int64_t)g * p.N + min(n0 + tr, p.N - 1)) * p.K * EB + lb;
+      const int64_t wrow = (int64_t)e * p.N + min(n0 + tr, p.N - 1);
+      s.a = A + (int64_t)src * p.lda * F::AB + lba;
+      s.w = W + wrow * p.K * F::WH / 2 + lbw;
+      s.wx = kBlockScaled<T> ? p.w_mx + wrow * (p.K / kMxBlock) + g : nullptr;
       s.out = p.out;
       s.ldo = p.ldo;
       s.N = p.N;
-      s.KB = p.K * EB;
+      s.K = p.K;
       s.asc = p.a_scale ? p.a_scale[src] : 1.f;
-      s.wsc = p.w_scale ? p.w_scale + (int64_t)g * p.N + min(n0 + (lane >> 4) * 4, p.N - 4)
-                        : nullptr;
+      s.wsc = p.w_scale ? p.w_scale + (int64_t)e * p.N + min(n0 + g * 4, p.N - 4) : nullptr;
     }
-    s.n = n0 + (lane >> 4) * 4;
+    s.n = n0 + g * 4;
   };
   // the shifted-last-batch path needs every unit's row to span at least one batch
-  constexpr int BB = Fmt<T>::U * Fmt<T>::SB;
-  const bool full = (nrt == 0 || p.K * EB >= BB) && (nsh == 0 || p.Ks * EB >= BB);
+  constexpr int BK = F::U * F::KS;
+  const bool full = (nrt == 0 || p.K >= BK) && (nsh == 0 || p.Ks >= BK);
   if (full)
     stream_units<T, true>(wave, nsh + nrt, nwaves, lane, p.store, resolve);
   else
@@ -282,12 +371,31 @@ __global__ __launch_bounds__(256, 1) void stream_kernel(StreamParams p) {
 
 hipError_t launch_stream(const StreamParams& p, hipStream_t s) {
   static_assert(kStreamWaves / 4 % kXcds == 0, "the wave numbering needs whole dies");
-  if (p.fp8) {
-    // e4m3 launches carry routed units only, with both scale sets
-    if (p.Ws || !p.a_scale || !p.w_scale) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(stream_kernel<Elt::FP8>, dim3(kStreamWaves / 4), dim3(256), 0, s, p);
-  } else {
-    hipLaunchKernelGGL(stream_kernel<Elt::BF16>, dim3(kStreamWaves / 4), dim3(256), 0, s, p);
+  const dim3 grid(kStreamWaves / 4), block(256);
+  // 8-bit and 4-bit launches carry routed units only, with their scales
+  const bool narrow = p.wt != Elt::BF16;
+  if (narrow && (p.Ws || !p.a_scale)) return hipErrorInvalidValue;
+  switch (p.wt) {
+    case Elt::BF16:
+      hipLaunchKernelGGL(stream_kernel<Elt::BF16>, grid, block, 0, s, p);
+      break;
+    case Elt::FP8:
+      if (!p.w_scale) return hipErrorInvalidValue;
+      hipLaunchKernelGGL(stream_kernel<Elt::FP8>, grid, block, 0, s, p);
+      break;
+    case Elt::MXFP4:
+    case Elt::MXFP8:
+      // block scales cover 32 elements; a unit's row blocks must lie inside the matrix
+      if (!p.w_mx || p.K % kMxBlock) return hipErrorInvalidValue;
+      if (p.N % (kUnitRows * (p.wt == Elt::MXFP4 ? Fmt<Elt::MXFP4>::R : Fmt<Elt::MXFP8>::R)))
+        return hipErrorInvalidValue;
+      if (p.wt == Elt::MXFP4)
+        hipLaunchKernelGGL(stream_kernel<Elt::MXFP4>, grid, block, 0, s, p);
+      else
+        hipLaunchKernelGGL(stream_kernel<Elt::MXFP8>, grid, block, 0, s, p);
+      break;
+    default:
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

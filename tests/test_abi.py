@@ -55,6 +55,16 @@ def ws_size(d):
     (dict(expert_dtype=2, latent=64, flags=B.PATH_STREAM), B.MOE_ERR_UNSUPPORTED),
     (dict(act_dtype=0, expert_dtype=0, flags=B.PATH_STREAM), B.MOE_ERR_UNSUPPORTED),
     (dict(flags=3), B.MOE_ERR_INVALID_ARG), (dict(flags=64), B.MOE_ERR_INVALID_ARG),
+    # block-scaled experts: bf16 activations, whole 32-blocks, decode path only
+    (dict(expert_dtype=B.MOE_MXFP4, flags=B.PATH_STREAM), B.MOE_OK),
+    (dict(expert_dtype=B.MOE_MXFP8), B.MOE_OK),
+    (dict(expert_dtype=B.MOE_MXFP4, latent=64, flags=B.PATH_STREAM), B.MOE_OK),
+    (dict(expert_dtype=B.MOE_MXFP4, flags=B.PATH_GROUPED), B.MOE_ERR_UNSUPPORTED),
+    (dict(expert_dtype=B.MOE_MXFP8, act_dtype=0), B.MOE_ERR_UNSUPPORTED),
+    (dict(expert_dtype=B.MOE_MXFP4, I=144), B.MOE_ERR_INVALID_ARG),
+    (dict(expert_dtype=B.MOE_MXFP8, H=272), B.MOE_ERR_INVALID_ARG),
+    (dict(expert_dtype=B.MOE_MXFP4, latent=48), B.MOE_ERR_INVALID_ARG),
+    (dict(expert_dtype=5), B.MOE_ERR_UNSUPPORTED),
 ])
 def test_descriptor_validation(kw, code):
     assert ws_size(desc(**kw))[0] == code
@@ -68,6 +78,10 @@ def test_workspace_grows_with_tokens_and_path():
     g = ws_size(desc(T=64, flags=B.PATH_GROUPED))[1]
     assert s > 0 and g > 0
     assert ws_size(desc(T=0))[0] == 0
+    # block-scaled experts take the stream path whatever the load
+    for dt in (B.MOE_MXFP4, B.MOE_MXFP8):
+        big = dict(T=6400, expert_dtype=dt)
+        assert ws_size(desc(**big)) == ws_size(desc(**big, flags=B.PATH_STREAM))
 
 
 def forward(d, w=None, y=FAKE, ws=FAKE, ws_bytes=1 << 40, r=None, latent=False):
@@ -98,6 +112,7 @@ def test_forward_argument_errors_are_reported_before_launch():
     w.Ws_up = FAKE.value
     w.s_up = None
     assert forward(desc(expert_dtype=2), w=w) == B.MOE_ERR_INVALID_ARG
+    assert forward(desc(expert_dtype=B.MOE_MXFP4), w=w) == B.MOE_ERR_INVALID_ARG
     assert forward(desc(flags=B.ROUTING_GIVEN)) == B.MOE_ERR_INVALID_ARG   # given but no record
     assert forward(desc(T=0)) == B.MOE_OK                                 # empty: no-op
 
