@@ -122,7 +122,7 @@ int32_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP
 // joined back before the combine (a fork / join that stream capture also records).
 struct Side {
   hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, ready = nullptr;  // ready: expert inputs quantised
 };
 constexpr int kMaxDevices = 64;
 Side g_side[kMaxDevices];
@@ -139,8 +139,10 @@ hipError_t side_of(Side** out) {
     Side n;
     if ((e = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking)) != hipSuccess) return e;
     if ((e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming)) != hipSuccess) {
+        (e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&n.ready, hipEventDisableTiming)) != hipSuccess) {
       if (n.fork) (void)hipEventDestroy(n.fork);
+      if (n.join) (void)hipEventDestroy(n.join);
       (void)hipStreamDestroy(n.s);
       return e;
     }
@@ -254,12 +256,19 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
   // (0) decode path of a plain layer with 8-bit or 4-bit experts: the bf16 shared expert
   // (weight 1, every token, independent of routing) cannot share the narrow launches, so it
   // streams on the side stream while the routed work proceeds on `s`. (A bf16 layer deals its
-  // shared-expert units out in the routed launches instead, which measured faster there.)
+  // shared-expert units out in the routed launches instead, which measured faster there.) The
+  // per-row e4m3 copy of x does not depend on routing either: it runs first on the side stream.
   Side* side = nullptr;
   if (stream_path && narrow && Is && !L) {
     MOE_TRY(side_of(&side));
     MOE_TRY(hipEventRecord(side->fork, s));
     MOE_TRY(hipStreamWaitEvent(side->s, side->fork, 0));
+    {
+      MOE_SPAN_ON("quant_rows:x", side->s);
+      MOE_TRY(launch_quant_rows((const uint16_t*)w->x, H, T, H, base + pl.xq,
+                                (float*)(base + pl.sx), side->s));
+    }
+    MOE_TRY(hipEventRecord(side->ready, side->s));
     {
       MOE_SPAN_ON("stream:shared_up", side->s);
       MOE_TRY(stream_dense(w->x, H, w->Ws_up, Is, H, T, hs, Is, kStoreSqRelu, side->s));
@@ -333,7 +342,9 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
     const char* dn_name = pl.ex == Elt::FP8     ? "stream_e4m3:down"
                           : pl.ex == Elt::MXFP4 ? "stream_mxfp4:down"
                                                 : "stream_mxfp8:down";
-    {
+    if (side) {
+      MOE_TRY(hipStreamWaitEvent(s, side->ready, 0));  // quantised on the side stream
+    } else {
       MOE_SPAN("quant_rows:x");
       MOE_TRY(launch_quant_rows((const uint16_t*)xin, D, T, D, xq, sx, s));
     }

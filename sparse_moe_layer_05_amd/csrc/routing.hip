@@ -16,22 +16,92 @@ namespace moe {
 namespace {
 
 // ------------------------------------------------------------------------------------ top-k
-// One wave per token. Lane l holds experts l, l + 64, ...; k rounds of a wave-wide arg-max
-// over (key desc, expert asc) by butterfly shuffles, the winner's owner lane retiring it.
-// s = fp32(1 / (1 + exp(-z))) is evaluated in double so that the rounded score does not depend
-// on a particular single-precision exp; key = s + b is one binary32 addition.
+// Wave-wide max / min by DPP row shifts and row broadcasts (lane 63 ends with the result over
+// all 64 lanes), then read back from lane 63 as a wave-uniform value. A lane whose DPP source
+// is outside its row (or whose row is masked off) combines with the identity.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_max_step(float v) {
+  const float o = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY),
+                                                             __float_as_int(v), CTRL, ROWS, 0xf,
+                                                             false));
+  return fmaxf(v, o);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_min_step(int v) {
+  return min(v, __builtin_amdgcn_update_dpp(0x7FFFFFFF, v, CTRL, ROWS, 0xf, false));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = dpp_max_step<0x111, 0xf>(v);  // row_shr:1
+  v = dpp_max_step<0x112, 0xf>(v);  // row_shr:2
+  v = dpp_max_step<0x114, 0xf>(v);  // row_shr:4
+  v = dpp_max_step<0x118, 0xf>(v);  // row_shr:8: lane 15 of each row holds the row's max
+  v = dpp_max_step<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ int wave_min(int v) {
+  v = dpp_min_step<0x111, 0xf>(v);
+  v = dpp_min_step<0x112, 0xf>(v);
+  v = dpp_min_step<0x114, 0xf>(v);
+  v = dpp_min_step<0x118, 0xf>(v);
+  v = dpp_min_step<0x142, 0xa>(v);
+  v = dpp_min_step<0x143, 0xc>(v);
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// k rounds of selection over the keys of one token; lane l holds experts l, l + 64, ... Each
+// round takes the largest free key (a wave max), then the lowest expert holding it (a wave
+// min: equal keys go to the lower index), and reads that expert's score from its lane. Writes
+// the k experts (descending key) and their gates (scores renormalised over the selection).
 template <int NPER>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int nsplit,
-                                                   const float* __restrict__ bias, int T, int E,
-                                                   int k, int32_t* __restrict__ idx,
-                                                   float* __restrict__ gates,
-                                                   float* __restrict__ logits_out) {
+__device__ __forceinline__ void select_topk(const float* key, const float* sc, int lane, int E,
+                                            int k, int32_t* __restrict__ idx_t,
+                                            float* __restrict__ gates_t) {
+  uint32_t taken = 0;
+  float sum = 0.f, mine = 0.f;
+  for (int j = 0; j < k; ++j) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+      const bool free = !((taken >> i) & 1u) && lane + 64 * i < E;
+      if (free) m = fmaxf(m, key[i]);
+    }
+    m = wave_max(m);
+    int c = 0x7FFFFFFF;
+    float cs = 0.f;
+#pragma unroll
+    for (int i = NPER - 1; i >= 0; --i) {  // descending i: the lowest matching expert wins
+      const int e = lane + 64 * i;
+      const bool free = !((taken >> i) & 1u) && e < E;
+      if (free && key[i] == m) {
+        c = e;
+        cs = sc[i];
+      }
+    }
+    const int be = wave_min(c);
+    const float bs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), be & 63));
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    sum += bs;                       // same order j = 0..k-1 on every lane: deterministic
+    if (lane == j) mine = bs;
+    if (lane == 0) idx_t[j] = be;
+  }
+  if (lane < k) gates_t[lane] = mine / sum;
+}
+
+// One wave per token, four tokens per workgroup (many tokens): lane l holds experts l, l + 64, ...
+// and adds the K-slice partials of a split router in slice order; scores, keys and selection as
+// in topk_kernel.
+template <int NPER>
+__global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict__ logits,
+                                                        int nsplit, const float* __restrict__ bias,
+                                                        int T, int E, int k,
+                                                        int32_t* __restrict__ idx,
+                                                        float* __restrict__ gates,
+                                                        float* __restrict__ logits_out) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  float key[NPER], sc[NPER], zs[NPER];
-  // K-slice partials (split-K router), summed in slice order; the loads of one slice for all of
-  // this lane's experts are independent, so they are issued together
+  float zs[NPER], key[NPER], sc[NPER];
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
     const int e = lane + 64 * i;
@@ -52,9 +122,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   for (int i = 0; i < NPER; ++i) {
     const int e = lane + 64 * i;
     if (e < E) {
-      const float z = zs[i];
-      if (logits_out) logits_out[(int64_t)t * E + e] = z;
-      const float s = (float)(1.0 / (1.0 + exp(-(double)z)));
+      if (logits_out) logits_out[(int64_t)t * E + e] = zs[i];
+      const float s = (float)(1.0 / (1.0 + exp(-(double)zs[i])));
       sc[i] = s;
       key[i] = s + bias[e];
     } else {
@@ -62,38 +131,73 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
       key[i] = -INFINITY;
     }
   }
-  uint32_t taken = 0;
-  float sum = 0.f, mine = 0.f;
-  for (int j = 0; j < k; ++j) {
-    float bk = -INFINITY, bs = 0.f;
-    int be = 0x7FFFFFFF;
+  select_topk<NPER>(key, sc, lane, E, k, idx + (int64_t)t * k, gates + (int64_t)t * k);
+}
+
+// One workgroup of 256 threads per token. Phase 1: thread i owns experts i, i + 256, ... (EPT of
+// them): it adds the nsplit K-slice partials of the split-K router in slice order (the loads of
+// up to 16 slices of all its experts are issued together), then forms the score and the key.
+// s = fp32(1 / (1 + exp(-z))) is evaluated in double so that the rounded score does not depend
+// on a particular single-precision exp; key = s + b is one binary32 addition. Phase 2: wave 0
+// selects; lane l holds experts l, l + 64, ... and k rounds of a wave-wide arg-max over
+// (key desc, expert asc) by butterfly shuffles retire one winner each.
+template <int NPER>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int nsplit,
+                                                   const float* __restrict__ bias, int T, int E,
+                                                   int k, int32_t* __restrict__ idx,
+                                                   float* __restrict__ gates,
+                                                   float* __restrict__ logits_out) {
+  constexpr int EPT = NPER >= 4 ? NPER / 4 : 1;  // experts per thread in phase 1
+  constexpr int SLAB = 16;                        // K slices whose loads are in flight together
+  __shared__ float key_l[64 * NPER], sc_l[64 * NPER];
+  const int tid = threadIdx.x;
+  const int t = blockIdx.x;
+  float z[EPT];
 #pragma unroll
-    for (int i = 0; i < NPER; ++i) {
-      const int e = lane + 64 * i;
-      const bool free = !((taken >> i) & 1u) && e < E;
-      if (free && (key[i] > bk || (key[i] == bk && e < be))) {
-        bk = key[i];
-        be = e;
-        bs = sc[i];
-      }
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ok = __shfl_xor(bk, m);
-      const int oe = __shfl_xor(be, m);
-      const float os = __shfl_xor(bs, m);
-      if (ok > bk || (ok == bk && oe < be)) {
-        bk = ok;
-        be = oe;
-        bs = os;
-      }
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    sum += bs;                       // same order j = 0..k-1 on every lane: deterministic
-    if (lane == j) mine = bs;
-    if (lane == 0) idx[(int64_t)t * k + j] = be;
+  for (int i = 0; i < EPT; ++i) {
+    const int e = tid + 256 * i;
+    z[i] = e < E ? logits[(int64_t)t * E + e] : 0.f;
   }
-  if (lane < k) gates[(int64_t)t * k + lane] = mine / sum;
+  for (int q0 = 1; q0 < nsplit; q0 += SLAB) {
+    float v[EPT][SLAB];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i)
+#pragma unroll
+      for (int q = 0; q < SLAB; ++q) {
+        const int e = tid + 256 * i;
+        v[i][q] = e < E && q0 + q < nsplit ? logits[((int64_t)(q0 + q) * T + t) * E + e] : 0.f;
+      }
+#pragma unroll
+    for (int i = 0; i < EPT; ++i)
+#pragma unroll
+      for (int q = 0; q < SLAB; ++q)
+        if (q0 + q < nsplit) z[i] += v[i][q];
+  }
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int e = tid + 256 * i;
+    if (e < 64 * NPER) {
+      if (e < E) {
+        if (logits_out) logits_out[(int64_t)t * E + e] = z[i];
+        const float sg = (float)(1.0 / (1.0 + exp(-(double)z[i])));
+        sc_l[e] = sg;
+        key_l[e] = sg + bias[e];
+      } else {
+        sc_l[e] = 0.f;
+        key_l[e] = -INFINITY;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid >= 64) return;
+  const int lane = tid;
+  float key[NPER], sc[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    key[i] = key_l[lane + 64 * i];
+    sc[i] = sc_l[lane + 64 * i];
+  }
+  select_topk<NPER>(key, sc, lane, E, k, idx + (int64_t)t * k, gates + (int64_t)t * k);
 }
 
 // --------------------------------------------------------------------------------- dispatch
@@ -134,17 +238,48 @@ __global__ __launch_bounds__(kDispatchChunk) void dispatch_count(const int32_t* 
   }
 }
 
-// Block-wide inclusive scans (Hillis-Steele) of four per-thread values over 1024 threads.
+// Block-wide inclusive scans of four per-thread values over 1024 threads (16 waves): wave scans
+// by shuffles, wave 0 scans the 16 wave totals, and each wave adds the totals before it.
 __device__ __forceinline__ void scan4(int32_t (*s)[1024], int e) {
-  for (int d = 1; d < 1024; d <<= 1) {
-    int v[4];
+  __shared__ int32_t wt[16][4];
+  const int lane = e & 63, w = e >> 6;
+  int v[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = e >= d ? s[q][e - d] : 0;
-    __syncthreads();
+  for (int q = 0; q < 4; ++q) v[q] = s[q][e];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) s[q][e] += v[q];
-    __syncthreads();
+  for (int d = 1; d < 64; d <<= 1)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int o = __shfl_up(v[q], d);
+      if (lane >= d) v[q] += o;
+    }
+  if (lane == 63)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wt[w][q] = v[q];
+  __syncthreads();
+  // wave 0: inclusive scan of the wave totals (lanes 16 g + i all hold total i; each group of
+  // 16 lanes scans its own copy)
+  int u[4] = {0, 0, 0, 0}, own[4] = {0, 0, 0, 0};
+  if (w == 0) {
+    const int i = lane & 15;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) own[q] = u[q] = wt[i][q];
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int o = __shfl_up(u[q], d);
+        if (i >= d) u[q] += o;
+      }
   }
+  __syncthreads();
+  if (w == 0 && lane < 16)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wt[lane][q] = u[q] - own[q];  // totals of the waves before
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) s[q][e] = v[q] + wt[w][q];
+  __syncthreads();
 }
 
 // Per-expert totals -> counts, offsets, M-tile prefix, decode slices; thread e = expert e.
@@ -206,6 +341,10 @@ __global__ __launch_bounds__(1024) void dispatch_scan(const int32_t* __restrict_
 }
 
 // All of dispatch in one workgroup when T fits one chunk (T <= 256): masks, totals, scatter.
+// Work is spread over the T*k (token, slot) pairs, thread i taking pairs i, i + 1024, ... (at
+// most 16). A pair is kept when its expert is in range and no earlier slot of the same token
+// chose that expert (the first occurrence wins, decided without atomics).
+constexpr int kSmallPairs = 16;   // pairs per thread: T*k <= 256*64
 __global__ __launch_bounds__(1024) void dispatch_small(const int32_t* __restrict__ idx, int T,
                                                        int E, int k, int bm,
                                                        int32_t* __restrict__ counts,
@@ -217,19 +356,33 @@ __global__ __launch_bounds__(1024) void dispatch_small(const int32_t* __restrict
   __shared__ uint32_t mask[kMaxE * 8];
   __shared__ int32_t s[4][1024];
   const int tid = threadIdx.x;
+  const int P = T * k;
   for (int i = tid; i < E * 8; i += 1024) mask[i] = 0;
-  __syncthreads();
-  uint64_t valid = 0;
-  if (tid < T) {
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[(int64_t)tid * k + j];
-      if ((unsigned)e < (unsigned)E) {
-        const uint32_t bit = 1u << (tid & 31);
-        const uint32_t old = atomicOr(&mask[e * 8 + (tid >> 5)], bit);
-        if (!(old & bit)) valid |= 1ull << j;
-      }
+  int ex_of[kSmallPairs];
+  uint32_t keep = 0;
+#pragma unroll
+  for (int c = 0; c < kSmallPairs; ++c) {
+    const int pr = tid + 1024 * c;
+    ex_of[c] = pr < P ? idx[pr] : -1;
+  }
+#pragma unroll
+  for (int c = 0; c < kSmallPairs; ++c) {
+    const int pr = tid + 1024 * c;
+    const int e = ex_of[c];
+    if (pr < P && (unsigned)e < (unsigned)E) {
+      const int t = pr / k, j = pr - t * k;
+      bool dup = false;  // independent loads, no early exit
+      for (int jj = 0; jj < j; ++jj) dup |= idx[(int64_t)t * k + jj] == e;
+      if (!dup) keep |= 1u << c;
     }
   }
+  __syncthreads();  // mask cleared
+#pragma unroll
+  for (int c = 0; c < kSmallPairs; ++c)
+    if ((keep >> c) & 1u) {
+      const int t = (tid + 1024 * c) / k;
+      atomicOr(&mask[ex_of[c] * 8 + (t >> 5)], 1u << (t & 31));
+    }
   __syncthreads();
   int tot = 0;
   if (tid < E)
@@ -237,25 +390,26 @@ __global__ __launch_bounds__(1024) void dispatch_small(const int32_t* __restrict
     for (int w = 0; w < 8; ++w) tot += __popc(mask[tid * 8 + w]);
   dispatch_totals(tid, E, tot, bm, s, counts, offsets, mt_start, ex);
   // s[0][e] - count[e] is the base of expert e; counts are re-derived from the masks below.
-  if (tid < T) {
-    const int w = tid >> 5;
-    const uint32_t below = (1u << (tid & 31)) - 1u;
-    for (int j = 0; j < k; ++j) {
-      if (!((valid >> j) & 1ull)) {
-        pos[(int64_t)tid * k + j] = -1;
-        continue;
-      }
-      const int e = idx[(int64_t)tid * k + j];
-      int cnt = 0, rank = __popc(mask[e * 8 + w] & below);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        cnt += __popc(mask[e * 8 + q]);
-        if (q < w) rank += __popc(mask[e * 8 + q]);
-      }
-      const int r = s[0][e] - cnt + rank;
-      perm[r] = tid;
-      pos[(int64_t)tid * k + j] = r;
+  for (int c = 0; c < kSmallPairs; ++c) {
+    const int pr = tid + 1024 * c;
+    if (pr >= P) continue;
+    if (!((keep >> c) & 1u)) {
+      pos[pr] = -1;
+      continue;
     }
+    const int e = ex_of[c];
+    const int t = pr / k, w = t >> 5;
+    const uint32_t below = (1u << (t & 31)) - 1u;
+    int cnt = 0, rank = __popc(mask[e * 8 + w] & below);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      cnt += __popc(mask[e * 8 + q]);
+      if (q < w) rank += __popc(mask[e * 8 + q]);
+    }
+    const int r = s[0][e] - cnt + rank;
+    perm[r] = t;
+    pos[pr] = r;
   }
 }
 
@@ -292,8 +446,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y
                                                       const float* __restrict__ gates, int T,
                                                       int D, int k, void* __restrict__ out,
                                                       int64_t ldo) {
+  // workgroup (t, y) covers columns [y * cpb, (y + 1) * cpb) of token t, cpb = D / gridDim.y
+  // rounded up to whole 8-column groups of the block
   const int t = blockIdx.x;
-  for (int c = threadIdx.x * 8; c < D; c += blockDim.x * 8) {
+  const int cpb = cdiv(cdiv(D, gridDim.y), 8) * 8;
+  const int cend = min(D, (int)(blockIdx.y + 1) * cpb);
+  for (int c = blockIdx.y * cpb + threadIdx.x * 8; c < cend; c += blockDim.x * 8) {
     float acc[8];
     auto load8 = [&](const void* base, int64_t row, int64_t ld, float* v) {
       if constexpr (YT == Elt::BF16) {
@@ -345,7 +503,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y
 }
 
 // -------------------------------------------------------------------------------- quantise
-// One workgroup per row: amax by wave shuffles + LDS, then e4m3 codes of x * (448 / amax).
+// One workgroup per row: amax by wave shuffles + LDS, then e4m3 codes of x * (448 / amax). A row
+// of up to 256 * 8 * kQuantRegs elements is read once and kept in registers; longer rows are
+// read a second time for the codes.
+constexpr int kQuantRegs = 4;
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x,
                                                          int64_t ldx, int H,
                                                          uint8_t* __restrict__ q,
@@ -353,16 +514,24 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
   __shared__ float s_max[4];
   const int t = blockIdx.x, tid = threadIdx.x;
   const uint16_t* row = x + (int64_t)t * ldx;
+  uint4 keep[kQuantRegs];
   float m = 0.f;
-  for (int c = tid * 8; c < H; c += 256 * 8) {
-    const uint4 v = *(const uint4*)(row + c);
+  auto amax8 = [&](const uint4 v) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       m = fmaxf(m, fabsf(bf16_bits_to_f32(w[i] & 0xFFFF)));
       m = fmaxf(m, fabsf(bf16_bits_to_f32(w[i] >> 16)));
     }
+  };
+#pragma unroll
+  for (int r = 0; r < kQuantRegs; ++r) {
+    const int c = (r * 256 + tid) * 8;
+    keep[r] = c < H ? *(const uint4*)(row + c) : make_uint4(0, 0, 0, 0);
   }
+#pragma unroll
+  for (int r = 0; r < kQuantRegs; ++r) amax8(keep[r]);
+  for (int c = (kQuantRegs * 256 + tid) * 8; c < H; c += 256 * 8) amax8(*(const uint4*)(row + c));
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   if ((tid & 63) == 0) s_max[tid >> 6] = m;
@@ -370,8 +539,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
   const float amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
   const float inv = amax > 0.f ? 448.f / amax : 1.f;   // codes = e4m3(x * inv)
   if (tid == 0) scale[t] = amax > 0.f ? amax / 448.f : 1.f;
-  for (int c = tid * 8; c < H; c += 256 * 8) {
-    const uint4 v = *(const uint4*)(row + c);
+  auto codes8 = [&](const uint4 v, int c) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t o[2];
 #pragma unroll
@@ -383,7 +551,13 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
       o[h] = cvt_fp8x2(f0, f1) | (cvt_fp8x2(f2, f3) << 16);
     }
     *(uint2*)(q + (int64_t)t * H + c) = make_uint2(o[0], o[1]);
+  };
+#pragma unroll
+  for (int r = 0; r < kQuantRegs; ++r) {
+    const int c = (r * 256 + tid) * 8;
+    if (c < H) codes8(keep[r], c);
   }
+  for (int c = (kQuantRegs * 256 + tid) * 8; c < H; c += 256 * 8) codes8(*(const uint4*)(row + c), c);
 }
 
 // One workgroup; thread e handles expert e (loops for E > 1024). The mean-load comparison is done
@@ -419,9 +593,19 @@ __global__ __launch_bounds__(1024) void bias_update_kernel(const int32_t* __rest
 hipError_t launch_topk(const float* logits, int nsplit, const float* b, int T, int E, int k,
                        int32_t* idx, float* gates, float* logits_out, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  const dim3 grid((T + 3) / 4), block(256);
-#define MOE_TOPK(NPER) hipLaunchKernelGGL(topk_kernel<NPER>, grid, block, 0, s, logits, nsplit, b, \
-                                          T, E, k, idx, gates, logits_out)
+  // few tokens with a split router: a workgroup per token adds the partials; else a wave per
+  // token
+  const bool wg = nsplit > 1 && T < 1024;
+  const dim3 grid(wg ? T : (T + 3) / 4), block(256);
+#define MOE_TOPK(NPER)                                                                         \
+  do {                                                                                         \
+    if (wg)                                                                                    \
+      hipLaunchKernelGGL(topk_kernel<NPER>, grid, block, 0, s, logits, nsplit, b, T, E, k, idx, \
+                         gates, logits_out);                                                   \
+    else                                                                                       \
+      hipLaunchKernelGGL(topk_wave_kernel<NPER>, grid, block, 0, s, logits, nsplit, b, T, E, k, \
+                         idx, gates, logits_out);                                              \
+  } while (0)
   if (E <= 64) MOE_TOPK(1);
   else if (E <= 128) MOE_TOPK(2);
   else if (E <= 256) MOE_TOPK(4);
@@ -464,8 +648,11 @@ hipError_t launch_combine(const void* Y, Elt y_elt, int64_t ldy, const float* S,
                           const int32_t* pos, const float* gates, int T, int D, int k, void* out,
                           Elt out_elt, int64_t ldo, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  const int threads = D / 8 >= 256 ? 256 : ((D / 8 + 63) / 64) * 64;
-  const dim3 grid(T), block(threads);
+  // Many tokens: one workgroup per token. Few tokens (decode): a token's columns are split over
+  // workgroups of one wave, 512 columns each, so that enough of them run at once.
+  const bool few = T < 1024;
+  const int threads = few ? 64 : (D / 8 >= 256 ? 256 : ((D / 8 + 63) / 64) * 64);
+  const dim3 grid(T, few ? cdiv(D, 512) : 1), block(threads);
   if (y_elt == Elt::BF16 && out_elt == Elt::BF16)
     hipLaunchKernelGGL((combine_kernel<Elt::BF16, Elt::BF16>), grid, block, 0, s, Y, ldy, S, lds, pos, gates, T, D, k, out, ldo);
   else if (y_elt == Elt::F32 && out_elt == Elt::BF16)
