@@ -34,7 +34,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="nano_decode_bf16")
     ap.add_argument("--also", default="nano_prefill_bf16,latent_decode_bf16,nano_fp8_decode,"
-                                      "nano_mxfp4_decode,nano_mxfp8_decode,latent_mxfp4_decode",
+                                      "nano_mxfp4_decode,nano_mxfp8_decode,latent_mxfp4_decode,"
+                                      "latent_fp8_decode",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--path", default="auto", choices=["auto", "grouped", "stream"])
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured graph")

@@ -81,7 +81,7 @@ typedef enum {
                                     MXFP4 / MXFP8 experts */
 #define MOE_PATH_GROUPED 1u      /* grouped MFMA GEMMs with a device-built tile list (prefill) */
 #define MOE_PATH_STREAM 2u       /* read each touched expert's weights once (decode): bf16,
-                                    MXFP4 and MXFP8 experts, e4m3 experts without latent */
+                                    e4m3, MXFP4 and MXFP8 experts */
 #define MOE_PATH_MASK 3u
 #define MOE_ROUTING_GIVEN 4u     /* routing->idx and routing->gates are INPUTS: skip the router */
 

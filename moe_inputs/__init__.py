@@ -114,6 +114,9 @@ CONFIGS = {
         "nano_mxfp8_decode", T=64, H=2688, E=128, k=6, I=1856, I_shared=3712,
         expert_dtype="mxfp8",
         description="Nano-shaped decode step, MXFP8 expert weights (E4M3, E8M0 per 32), T=64"),
+    "latent_fp8_decode": LayerConfig(
+        "latent_fp8_decode", T=64, H=4096, E=512, k=24, I=512, latent=1024, expert_dtype="e4m3",
+        description="LatentMoE decode step, e4m3 expert weights, T=64 H=4096 l=1024 E'=512 k'=24"),
     "latent_mxfp4_decode": LayerConfig(
         "latent_mxfp4_decode", T=64, H=4096, E=512, k=24, I=512, latent=1024,
         expert_dtype="mxfp4",

@@ -55,10 +55,8 @@ int32_t make_plan(const moe_desc_t* d, bool latent_call, Plan* pl) {
   p.T = (int)T; p.H = (int)H; p.E = (int)E; p.k = (int)k; p.I = (int)I; p.Is = (int)Is;
   p.L = (int)L; p.D = L ? (int)L : (int)H; p.P = (int)(T * k);
   const uint32_t path = d->flags & MOE_PATH_MASK;
-  // the decode path streams bf16 experts, e4m3 experts of a plain (non-latent) layer, and
-  // block-scaled experts, which have no other path
-  const bool stream_ok =
-      p.act == Elt::BF16 && (p.ex == Elt::BF16 || (p.ex == Elt::FP8 && !p.L) || mx);
+  // the decode path streams bf16, e4m3 and block-scaled experts (the last have no other path)
+  const bool stream_ok = p.act == Elt::BF16 && (p.ex == Elt::BF16 || fp8 || mx);
   if (path == MOE_PATH_AUTO)
     p.path = (stream_ok && ((int64_t)p.P <= 8 * E || mx)) ? MOE_PATH_STREAM : MOE_PATH_GROUPED;
   else if (path == MOE_PATH_STREAM)

@@ -52,7 +52,7 @@ def ws_size(d):
                                                   B.MOE_ERR_UNSUPPORTED),
     (dict(act_dtype=0, expert_dtype=1), B.MOE_ERR_UNSUPPORTED),
     (dict(expert_dtype=2, flags=B.PATH_STREAM), B.MOE_OK),
-    (dict(expert_dtype=2, latent=64, flags=B.PATH_STREAM), B.MOE_ERR_UNSUPPORTED),
+    (dict(expert_dtype=2, latent=64, flags=B.PATH_STREAM), B.MOE_OK),
     (dict(act_dtype=0, expert_dtype=0, flags=B.PATH_STREAM), B.MOE_ERR_UNSUPPORTED),
     (dict(flags=3), B.MOE_ERR_INVALID_ARG), (dict(flags=64), B.MOE_ERR_INVALID_ARG),
     # block-scaled experts: bf16 activations, whole 32-blocks, decode path only

@@ -7,10 +7,10 @@ Bars (from the layer's specification):
     recomputed by the oracle for the selection the GPU made;
   * outputs: relative Frobenius error <= 5e-3 (bf16) and 1e-5 for fp32 layers (fp32
     accumulation over K <= 256: ~sqrt(K) * 2^-24 relative, with margin). With 8-bit or 4-bit
-    experts the expert inputs and h are rounded per row to e4m3, and the bar is <= 5e-3 against
-    the oracle that emulates that rounding; against the oracle without it, <= 3e-2 for e4m3
-    experts (on the e4m3 workloads, which carry a shared expert) and <= 6e-2 for MXFP4 / MXFP8
-    experts on any layer. The 6e-2: a round to nearest e4m3 has relative RMS error
+    experts (e4m3, MXFP4, MXFP8) the expert inputs and h are rounded per row to e4m3, and the
+    bar is <= 5e-3 against the oracle that emulates that rounding; against the oracle without
+    it, <= 3e-2 on layers with a shared expert and <= 6e-2 on layers whose whole output is
+    routed. The 6e-2: a round to nearest e4m3 has relative RMS error
     2^-4 / sqrt(3) * sqrt(E[1/m^2]) ~ 0.0255 for mantissas m uniform in [1, 2); h = a^2 doubles
     the error it inherits from u and adds its own, sqrt((2 * 0.0255)^2 + 0.0255^2) ~ 0.057 on a
     layer with no shared expert, whose routed part is then the whole output (measured between
@@ -33,8 +33,9 @@ import sparse_moe_layer_05_amd as moe  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-5, "bf16": 5e-3, "e4m3": 3e-2, "mxfp4": 6e-2, "mxfp8": 6e-2}
+TOL = {"f32": 1e-5, "bf16": 5e-3}
 NARROW = ("e4m3", "mxfp4", "mxfp8")
+NARROW_TOL = {True: 3e-2, False: 6e-2}     # keyed by "has a shared expert"
 BAND = 1e-4
 THREADS = max(1, min(16, os.cpu_count() or 1))   # oracle threads (tokens are independent)
 
@@ -58,7 +59,9 @@ def rel_frob(a, b):
 
 
 def tol_of(cfg):
-    return TOL[cfg.expert_dtype if cfg.expert_dtype in NARROW else cfg.act_dtype]
+    if cfg.expert_dtype in NARROW:
+        return NARROW_TOL[cfg.I_shared > 0]
+    return TOL[cfg.act_dtype]
 
 
 def run(inp, path="auto", given=None, dev=None):
@@ -134,10 +137,12 @@ SMALL = {
                                  expert_dtype="mxfp8"),
     "latent_mxfp4_small": mi.LayerConfig("latent_mxfp4_small", T=50, H=256, E=32, k=4, I=96,
                                          latent=128, I_shared=64, expert_dtype="mxfp4"),
+    "latent_fp8_small": mi.LayerConfig("latent_fp8_small", T=45, H=256, E=32, k=4, I=96,
+                                       latent=128, expert_dtype="e4m3"),
 }
 MX_ONLY = {"mxfp4_one": dataclasses.replace(SMALL["mxfp4_long"], name="mxfp4_one", T=1)}
 MX_SMALL = ["mxfp4_small", "mxfp8_small", "mxfp4_long", "mxfp8_long", "latent_mxfp4_small",
-            "mxfp4_one"]
+            "mxfp4_one", "latent_fp8_small"]
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -217,11 +222,15 @@ def test_fp8_decode_full_oracle_both_paths():
 
 @pytest.mark.parametrize("spread", [False, True])
 @pytest.mark.parametrize("name", MX_SMALL)
-def test_block_scaled_against_emulating_oracle(name, spread):
-    # MXFP4 / MXFP8 expert weights on the streaming kernel against the oracle that rounds the
-    # activation rows as the kernel does; with `spread` the stored block scales are moved over
-    # 13 binades (still valid MX data), so every block carries its own exponent
-    inp = mi.make_layer({**SMALL, **MX_ONLY}[name], seed=9)
+def test_narrow_small_against_emulating_oracle(name, spread):
+    # MXFP4 / MXFP8 (and LatentMoE e4m3) expert weights on the streaming kernel against the
+    # oracle that rounds the activation rows as the kernel does; with `spread` the stored block
+    # scales are moved over 13 binades (still valid MX data), so every block carries its own
+    # exponent
+    cfg = {**SMALL, **MX_ONLY}[name]
+    if spread and cfg.expert_dtype not in mi.BLOCK_FORMATS:
+        pytest.skip("block scales only")
+    inp = mi.make_layer(cfg, seed=9)
     if spread:
         rng = np.random.default_rng(10)
         for sc in ("s_up", "s_down"):
@@ -233,16 +242,30 @@ def test_block_scaled_against_emulating_oracle(name, spread):
     assert err <= 5e-3
 
 
-@pytest.mark.parametrize("name", ["nano_mxfp4_decode", "nano_mxfp8_decode", "latent_mxfp4_decode"])
-def test_block_scaled_decode_full_oracle(name):
-    # decode-sized layers with MXFP4 / MXFP8 experts, every token: against the exact oracle
-    # (3e-2) and the oracle emulating the activation rounding (5e-3)
+@pytest.mark.parametrize("name", ["nano_mxfp4_decode", "nano_mxfp8_decode", "latent_mxfp4_decode",
+                                  "latent_fp8_decode"])
+def test_narrow_decode_full_oracle(name):
+    # decode-sized layers with MXFP4 / MXFP8 / e4m3 experts (LatentMoE e4m3 included), every
+    # token, on the streaming path: against the exact oracle and the oracle emulating the
+    # activation rounding (5e-3)
     inp = mi.make_layer(mi.CONFIGS[name], seed=0)
     y, rt = check_full(inp, "auto")
     refe, nswap = reference(inp, rt["idx"], fp8_emulate=True)
     erre = rel_frob(y, refe["y"])
     say(f"[gpu]   {name}: {erre:.3e} against the emulating oracle, swaps {nswap}")
     assert erre <= 5e-3
+
+
+def test_latent_fp8_both_paths_against_emulating_oracle():
+    # LatentMoE with e4m3 experts: the projection is rounded to bf16 and quantised per row on
+    # both paths; each path against the emulating oracle
+    inp = mi.make_layer(SMALL["latent_fp8_small"], seed=11)
+    for path in ("stream", "grouped"):
+        y, rt = run(inp, path)
+        ref, nswap = reference(inp, rt["idx"], fp8_emulate=True)
+        err = rel_frob(y, ref["y"])
+        say(f"[gpu] latent e4m3 ({path}) vs emulating oracle: {err:.3e}, swaps {nswap}")
+        assert err <= 5e-3
 
 
 # --------------------------------------------------------------------- routing and dispatch
