@@ -91,8 +91,9 @@ struct StreamParams {
   int64_t lda_s = 0;
   const void* Ws = nullptr;           // [Ns][Ks] bf16
   int Ns = 0, Ks = 0, Ts = 0;
-  void* out_s = nullptr;
+  void* out_s = nullptr;              // ksplit_s > 1: ksplit_s fp32 slabs [Ts][ldo_s]
   int64_t ldo_s = 0;
+  int ksplit_s = 1;                   // K ranges of the shared slot (kStoreF32 only)
   int store = 0;                      // kStoreF32: fp32 acc; kStoreSqRelu: bf16(relu(acc)^2);
                                       // kStoreBF16: bf16(acc)
   // slices of the routed experts from the dispatch step (see DispatchExtras); n_slices NULL:
@@ -102,5 +103,10 @@ struct StreamParams {
   const int32_t* n_slices = nullptr;
 };
 hipError_t launch_stream(const StreamParams& p, hipStream_t s);
+
+// out[t, n] = store(sum over s of part[s][t][n]) for the S fp32 slabs [T][ld] of a split
+// weight-streaming product (slab order), store as in StreamStore.
+hipError_t launch_reduce_slabs(const float* part, int S, int T, int N, int64_t ld, void* out,
+                               int64_t ldo, int mode, hipStream_t s);
 
 }  // namespace moe

@@ -26,6 +26,8 @@ struct Plan {
   int nsplit = 1, kchunk = 0;
   size_t dscratch = 0, mt_start = 0, xq = 0, sx = 0, hq = 0, sh = 0, xl = 0, z = 0, h = 0, hs = 0;
   size_t Y = 0, total = 0;
+  int lsplit = 1;    // K ranges of the streamed projection into the latent width (decode)
+  size_t xpart = 0;  // its fp32 slabs [lsplit][T][L]
 };
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -97,6 +99,15 @@ int32_t make_plan(const moe_desc_t* d, bool latent_call, Plan* pl) {
   if (p.L) {
     p.xl = take(Tz * (size_t)p.L * ea);
     p.z = take(Tz * (size_t)p.L * ea);
+    if (p.path == MOE_PATH_STREAM) {
+      // x W_in^T streams W_in once; with few units (L/16 row blocks x T/16 token slices) each
+      // wave would walk all of H alone, so K is split until about one unit per wave
+      const int64_t units = (int64_t)((p.L + 15) / 16) * ((p.T + 15) / 16);
+      while (units * p.lsplit * 2 <= 1024 && H % (p.lsplit * 2 * 8) == 0 &&
+             H / (p.lsplit * 2) >= 256)
+        p.lsplit *= 2;
+      if (p.lsplit > 1) p.xpart = take((size_t)p.lsplit * Tz * (size_t)p.L * 4);
+    }
   }
   p.h = take(P * (size_t)p.I * ea);
   if (p.Is) p.hs = take(Tz * (size_t)p.Is * ea);
@@ -200,10 +211,10 @@ hipError_t dense(Elt ab, Elt out, Epi epi, const void* A, int64_t lda, const voi
 // weight-streaming kernel (its shared-expert slot alone): W is read from HBM once, spread over
 // every SIMD, where a tiled GEMM would leave most CUs idle at this M.
 hipError_t stream_dense(const void* A, int64_t lda, const void* W, int N, int K, int T, void* out,
-                        int64_t ldo, int store, hipStream_t s) {
+                        int64_t ldo, int store, hipStream_t s, int ksplit = 1) {
   StreamParams p;
   p.As = (const uint16_t*)A; p.lda_s = lda; p.Ws = (const uint16_t*)W; p.Ns = N; p.Ks = K;
-  p.Ts = T; p.out_s = out; p.ldo_s = ldo; p.store = store;
+  p.Ts = T; p.out_s = out; p.ldo_s = ldo; p.store = store; p.ksplit_s = ksplit;
   return launch_stream(p, s);
 }
 
@@ -313,7 +324,15 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
   const void* xin = w->x;
   if (L) {
     void* xl = base + pl.xl;
-    if (stream_path) {
+    if (stream_path && pl.lsplit > 1) {
+      float* part = (float*)(base + pl.xpart);
+      {
+        MOE_SPAN("stream:latent_in");
+        MOE_TRY(stream_dense(w->x, H, w->W_in, L, H, T, part, L, kStoreF32, s, pl.lsplit));
+      }
+      MOE_SPAN("reduce:latent_in");
+      MOE_TRY(launch_reduce_slabs(part, pl.lsplit, T, L, L, xl, L, kStoreBF16, s));
+    } else if (stream_path) {
       MOE_SPAN("stream:latent_in");
       MOE_TRY(stream_dense(w->x, H, w->W_in, L, H, T, xl, L, kStoreBF16, s));
     } else {

@@ -290,7 +290,11 @@ __device__ void run_units(const StreamParams& p, int wave, int nwaves, bool shar
   // share weight rows run side by side and share them through L2);
   // units [nsh, nsh + nrt): the routed slices, slice major, row block minor (neighbouring waves
   // stream neighbouring rows of one expert's matrix)
-  const int nss = p.Ws && shared_part ? cdiv(p.Ts, kSliceRows) : 0;
+  // the shared slot's K may be split in ksplit_s ranges of Kc elements, each written to its own
+  // fp32 slab of the output (summed by a separate reduction)
+  const int nks = p.ksplit_s > 1 ? p.ksplit_s : 1;
+  const int Kc = p.Ks / nks;
+  const int nss = p.Ws && shared_part ? cdiv(p.Ts, kSliceRows) * nks : 0;
   const int nsh = nss ? cdiv(p.Ns, kUnitRows) * nss : 0;
   const int nsl = p.n_slices && routed_part ? sload(p.n_slices, 0) : 0;
   const int nbr = cdiv(p.N, kUnitRows * F::R);
@@ -303,17 +307,18 @@ __device__ void run_units(const StreamParams& p, int wave, int nwaves, bool shar
     int n0, src;
     if (u < nsh) {  // bf16 shared expert (only with T == BF16)
       n0 = (u / nss) * kUnitRows;
-      const int r0 = (u % nss) * kSliceRows;
+      const int ks = (u % nss) % nks;  // K range, fastest
+      const int r0 = (u % nss) / nks * kSliceRows;
       s.nrows = min(p.Ts - r0, kSliceRows);
       s.orow = r0 + tr;
       src = r0 + min(tr, s.nrows - 1);
-      s.a = As + (int64_t)src * p.lda_s * F::AB + lba;
-      s.w = Ws + (int64_t)min(n0 + tr, p.Ns - 1) * p.Ks * F::WH / 2 + lbw;
+      s.a = As + ((int64_t)src * p.lda_s + (int64_t)ks * Kc) * F::AB + lba;
+      s.w = Ws + ((int64_t)min(n0 + tr, p.Ns - 1) * p.Ks + (int64_t)ks * Kc) * F::WH / 2 + lbw;
       s.wx = nullptr;
-      s.out = p.out_s;
+      s.out = nks > 1 ? (void*)((float*)p.out_s + (int64_t)ks * p.Ts * p.ldo_s) : p.out_s;
       s.ldo = p.ldo_s;
       s.N = p.Ns;
-      s.K = p.Ks;
+      s.K = Kc;
       s.asc = 1.f;
       s.wsc = nullptr;
     } else {
@@ -350,7 +355,7 @@ __device__ void run_units(const StreamParams& p, int wave, int nwaves, bool shar
   };
   // the shifted-last-batch path needs every unit's row to span at least one batch
   constexpr int BK = F::U * F::KS;
-  const bool full = (nrt == 0 || p.K >= BK) && (nsh == 0 || p.Ks >= BK);
+  const bool full = (nrt == 0 || p.K >= BK) && (nsh == 0 || Kc >= BK);
   if (full)
     stream_units<T, true>(wave, nsh + nrt, nwaves, lane, p.store, resolve);
   else
@@ -367,7 +372,39 @@ __global__ __launch_bounds__(256, 1) void stream_kernel(StreamParams p) {
   run_units<T>(p, wave, gridDim.x * 4, T == Elt::BF16, true);
 }
 
+// out[t, n] = store(sum_s part[s][t][n]) over the S fp32 slabs of a split shared slot, added in
+// slab order; 8 columns per thread.
+__global__ __launch_bounds__(256) void reduce_slabs_kernel(const float* __restrict__ part, int S,
+                                                           int T, int N, int64_t ld,
+                                                           void* __restrict__ out, int64_t ldo,
+                                                           int mode) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int cg = N / 8;
+  if (i >= (int64_t)T * cg) return;
+  const int t = (int)(i / cg), n = (int)(i % cg) * 8;
+  float4 a = *(const float4*)(part + (int64_t)t * ld + n);
+  float4 b = *(const float4*)(part + (int64_t)t * ld + n + 4);
+  for (int s = 1; s < S; ++s) {
+    const float* q = part + ((int64_t)s * T + t) * ld + n;
+    const float4 c = *(const float4*)q, d = *(const float4*)(q + 4);
+    a.x += c.x; a.y += c.y; a.z += c.z; a.w += c.w;
+    b.x += d.x; b.y += d.y; b.z += d.z; b.w += d.w;
+  }
+  store_block(f32x4_t{a.x, a.y, a.z, a.w}, out, ldo, t, n, mode);
+  store_block(f32x4_t{b.x, b.y, b.z, b.w}, out, ldo, t, n + 4, mode);
+}
+
 }  // namespace
+
+hipError_t launch_reduce_slabs(const float* part, int S, int T, int N, int64_t ld, void* out,
+                               int64_t ldo, int mode, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (N % 8) return hipErrorInvalidValue;
+  const int64_t items = (int64_t)T * (N / 8);
+  hipLaunchKernelGGL(reduce_slabs_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s,
+                     part, S, T, N, ld, out, ldo, mode);
+  return hipGetLastError();
+}
 
 hipError_t launch_stream(const StreamParams& p, hipStream_t s) {
   static_assert(kStreamWaves / 4 % kXcds == 0, "the wave numbering needs whole dies");
@@ -375,6 +412,8 @@ hipError_t launch_stream(const StreamParams& p, hipStream_t s) {
   // 8-bit and 4-bit launches carry routed units only, with their scales
   const bool narrow = p.wt != Elt::BF16;
   if (narrow && (p.Ws || !p.a_scale)) return hipErrorInvalidValue;
+  // a split shared slot writes fp32 slabs of whole 16-byte chunks of K
+  if (p.ksplit_s > 1 && (p.store != kStoreF32 || p.Ks % (p.ksplit_s * 8))) return hipErrorInvalidValue;
   switch (p.wt) {
     case Elt::BF16:
       hipLaunchKernelGGL(stream_kernel<Elt::BF16>, grid, block, 0, s, p);

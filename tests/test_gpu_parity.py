@@ -139,6 +139,9 @@ SMALL = {
                                          latent=128, I_shared=64, expert_dtype="mxfp4"),
     "latent_fp8_small": mi.LayerConfig("latent_fp8_small", T=45, H=256, E=32, k=4, I=96,
                                        latent=128, expert_dtype="e4m3"),
+    # few tokens and a wide H: the streamed projection into the latent width splits K in four
+    "latent_split_small": mi.LayerConfig("latent_split_small", T=20, H=1024, E=16, k=4, I=64,
+                                         latent=64, I_shared=32),
 }
 MX_ONLY = {"mxfp4_one": dataclasses.replace(SMALL["mxfp4_long"], name="mxfp4_one", T=1)}
 MX_SMALL = ["mxfp4_small", "mxfp8_small", "mxfp4_long", "mxfp8_long", "latent_mxfp4_small",
@@ -152,7 +155,7 @@ def test_small_layer_all_tokens(name):
 
 
 @pytest.mark.parametrize("name", ["bf16_ragged", "bf16_no_shared", "latent_small",
-                                  "latent_small_shared"])
+                                  "latent_small_shared", "latent_split_small"])
 def test_stream_and_grouped_paths_agree_with_oracle(name):
     inp = mi.make_layer(SMALL[name], seed=2)
     ys, _ = check_full(inp, "stream")
