@@ -478,14 +478,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     }
-    for (int j = 0; j < k; ++j) {
-      const int r = pos[(int64_t)t * k + j];
-      if (r < 0) continue;
-      const float g = gates[(int64_t)t * k + j];
-      float v[8];
-      load8(Y, r, ldy, v);
+    // rows j0 .. j0+7 are loaded together, then added in j order
+    constexpr int JB = 8;
+    for (int j0 = 0; j0 < k; j0 += JB) {
+      float v[JB][8], g[JB];
+      bool ok[JB];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+      for (int jj = 0; jj < JB; ++jj) {
+        const int j = j0 + jj;
+        const int r = j < k ? pos[(int64_t)t * k + j] : -1;
+        ok[jj] = r >= 0;
+        g[jj] = ok[jj] ? gates[(int64_t)t * k + j] : 0.f;
+        if (ok[jj]) load8(Y, r, ldy, v[jj]);
+      }
+#pragma unroll
+      for (int jj = 0; jj < JB; ++jj)
+        if (ok[jj])
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(g[jj], v[jj][i], acc[i]);
     }
     if constexpr (OT == Elt::BF16) {
       uint4 q;
