@@ -63,30 +63,36 @@ __device__ __forceinline__ void store_block(const f32x4_t v, void* out, int64_t 
 //    nibble of byte i), and the E8M0 scale a lane passes as covering k 32g .. 32g + 31 of its
 //    row. So MXFP4 / MXFP8 weights and the e4m3 tokens they meet are loaded in that order.
 template <Elt T> struct Fmt;
-// R: blocks of 16 weight rows per unit, sharing the unit's token loads.
+// R: blocks of 16 weight rows per unit, sharing the unit's token loads; U(R): steps per batch.
+// bf16 routed launches take two blocks: a unit's token bytes otherwise equal its weight bytes,
+// and two blocks measured 2% faster on the Nano decode step (four slower, from the longer tail
+// of fewer units). Dense launches of the shared slot alone have few units and keep one block.
 template <> struct Fmt<Elt::BF16> {
-  static constexpr int KS = 32, U = 6, R = 1;    // elements per step, steps per batch
+  static constexpr int KS = 32, R = 2;            // elements per step, routed row blocks
+  static constexpr int U(int r) { return r == 1 ? 6 : 4; }
   static constexpr int WH = 4, AB = 2;           // weight half-bytes / token bytes per element
   static constexpr int CW = 1, LW = 16, CWS = 0;
   static constexpr int CA = 1, LA = 16, CAS = 0;
 };
 template <> struct Fmt<Elt::FP8> {
-  static constexpr int KS = 128, U = 3, R = 1;
+  static constexpr int KS = 128, R = 1;
+  static constexpr int U(int) { return 3; }
   static constexpr int WH = 2, AB = 1;
   static constexpr int CW = 2, LW = 32, CWS = 16;
   static constexpr int CA = 2, LA = 32, CAS = 16;
 };
 // 4-bit weights: a 16-row unit would carry half the bytes of an 8-bit one for the same fixed
 // cost per unit and twice as many token bytes per weight byte; two row blocks restore both.
-// (Block-scaled widths are multiples of 32, so both row blocks are always whole.)
 template <> struct Fmt<Elt::MXFP4> {
-  static constexpr int KS = 128, U = 8, R = 2;
+  static constexpr int KS = 128, R = 2;
+  static constexpr int U(int) { return 8; }
   static constexpr int WH = 1, AB = 1;
   static constexpr int CW = 1, LW = 16, CWS = 0;
   static constexpr int CA = 2, LA = 16, CAS = 64;
 };
 template <> struct Fmt<Elt::MXFP8> {
-  static constexpr int KS = 128, U = 4, R = 1;
+  static constexpr int KS = 128, R = 1;
+  static constexpr int U(int) { return 4; }
   static constexpr int WH = 2, AB = 1;
   static constexpr int CW = 2, LW = 16, CWS = 64;
   static constexpr int CA = 2, LA = 16, CAS = 64;
@@ -97,9 +103,11 @@ constexpr int kMxBlock = 32;  // elements per E8M0 scale
 // A unit resolved to this lane's pointers. Pointers include the lane's byte offset within a k
 // step.
 struct Unit {
-  const uint8_t* w;   // this lane's weight row
+  const uint8_t* w;   // this lane's weight row (row block 0)
   const uint8_t* a;   // this lane's token row
   const uint8_t* wx;  // MXFP4 / MXFP8: E8M0 scales of this lane's weight row, from block g
+  int64_t w1;         // bytes from this lane's weight row to its row in block 1, clamped to the
+                      // last row (bf16; block-scaled matrices use a fixed stride)
   void* out;
   int64_t ldo;
   int64_t orow;       // output row of this lane's token
@@ -121,11 +129,11 @@ struct Unit {
 // load of a batch is one base address plus an immediate offset and every batch issues the same
 // number of loads, which lets the compiler wait for exactly the batch it multiplies. !kFull:
 // loads of the last batch past K are clamped into the row and zeroed.
-template <Elt T, bool kFull, class Resolve>
+template <Elt T, int R, bool kFull, class Resolve>
 __device__ void stream_units(int first, int total, int nwaves, int lane, int mode,
                              Resolve resolve) {
   using F = Fmt<T>;
-  constexpr int KS = F::KS, U = F::U, R = F::R, CW = F::CW, CA = F::CA, BK = U * KS;
+  constexpr int KS = F::KS, U = F::U(R), CW = F::CW, CA = F::CA, BK = U * KS;
   constexpr int SW = KS * F::WH / 2, SA = KS * F::AB;  // bytes of a step
   constexpr bool kMx = kBlockScaled<T>;
   const int g = lane >> 4;
@@ -150,6 +158,10 @@ __device__ void stream_units(int first, int total, int nwaves, int lane, int mod
     const int kb = kbase(K, b);
     const int kbw = kb * F::WH / 2, kba = kb * F::AB;
     const int KBw = K * F::WH / 2, KBa = K * F::AB;
+    // block-scaled matrices have whole 32-row blocks: their second block is a fixed stride away
+    // (no per-unit offsets, which keeps the MXFP4 kernel's registers within what lets it share
+    // a SIMD with the dense bf16 launches of the side stream)
+    const int64_t w1 = R == 1 || kMx ? 0 : (other ? o.w1 : s.w1);
 #pragma unroll
     for (int q = 0; q < U; ++q) {
 #pragma unroll
@@ -157,7 +169,8 @@ __device__ void stream_units(int first, int total, int nwaves, int lane, int mod
 #pragma unroll
         for (int c = 0; c < CW; ++c) {
           const int off = kbw + q * SW + c * F::CWS;
-          wf[(q * R + r) * CW + c] = *(const uint4*)(w + (int64_t)r * kUnitRows * KBw +
+          wf[(q * R + r) * CW + c] = *(const uint4*)(w + (kMx ? (int64_t)r * kUnitRows * KBw
+                                                                : r * w1) +
                                                      (kFull ? off : min(off, KBw - 16 - lbw)));
         }
 #pragma unroll
@@ -277,7 +290,7 @@ __device__ void stream_units(int first, int total, int nwaves, int lane, int mod
 
 // The units of one launch that this wave streams with weights of type T: the shared expert's
 // (shared_part, bf16 only) and the routed experts' (routed_part).
-template <Elt T>
+template <Elt T, int R>
 __device__ void run_units(const StreamParams& p, int wave, int nwaves, bool shared_part,
                           bool routed_part) {
   using F = Fmt<T>;
@@ -295,9 +308,9 @@ __device__ void run_units(const StreamParams& p, int wave, int nwaves, bool shar
   const int nks = p.ksplit_s > 1 ? p.ksplit_s : 1;
   const int Kc = p.Ks / nks;
   const int nss = p.Ws && shared_part ? cdiv(p.Ts, kSliceRows) * nks : 0;
-  const int nsh = nss ? cdiv(p.Ns, kUnitRows) * nss : 0;
+  const int nsh = nss ? cdiv(p.Ns, kUnitRows * R) * nss : 0;
   const int nsl = p.n_slices && routed_part ? sload(p.n_slices, 0) : 0;
-  const int nbr = cdiv(p.N, kUnitRows * F::R);
+  const int nbr = cdiv(p.N, kUnitRows * R);
   const int nrt = nbr * nsl;
   const uint8_t* As = (const uint8_t*)p.As;
   const uint8_t* Ws = (const uint8_t*)p.Ws;
@@ -306,7 +319,7 @@ __device__ void run_units(const StreamParams& p, int wave, int nwaves, bool shar
   auto resolve = [&](int u, Unit& s) {
     int n0, src;
     if (u < nsh) {  // bf16 shared expert (only with T == BF16)
-      n0 = (u / nss) * kUnitRows;
+      n0 = (u / nss) * kUnitRows * R;
       const int ks = (u % nss) % nks;  // K range, fastest
       const int r0 = (u % nss) / nks * kSliceRows;
       s.nrows = min(p.Ts - r0, kSliceRows);
@@ -314,6 +327,12 @@ __device__ void run_units(const StreamParams& p, int wave, int nwaves, bool shar
       src = r0 + min(tr, s.nrows - 1);
       s.a = As + ((int64_t)src * p.lda_s + (int64_t)ks * Kc) * F::AB + lba;
       s.w = Ws + ((int64_t)min(n0 + tr, p.Ns - 1) * p.Ks + (int64_t)ks * Kc) * F::WH / 2 + lbw;
+      // full rows of Ks elements apart, also when this unit covers one K range of them
+      if constexpr (R > 1)
+        s.w1 = (int64_t)(min(n0 + kUnitRows + tr, p.Ns - 1) - min(n0 + tr, p.Ns - 1)) * p.Ks *
+               F::WH / 2;
+      else
+        s.w1 = 0;
       s.wx = nullptr;
       s.out = nks > 1 ? (void*)((float*)p.out_s + (int64_t)ks * p.Ts * p.ldo_s) : p.out_s;
       s.ldo = p.ldo_s;
@@ -324,7 +343,7 @@ __device__ void run_units(const StreamParams& p, int wave, int nwaves, bool shar
     } else {
       const int v = u - nsh;
       const int i = v / nbr;
-      n0 = (v % nbr) * kUnitRows * F::R;
+      n0 = (v % nbr) * kUnitRows * R;
       const int e = sload(p.slice_e, i);
       const int r0 = sload(p.slice_r, i);
       s.nrows = min(sload(p.offs, e + 1) - r0, kSliceRows);
@@ -341,6 +360,11 @@ __device__ void run_units(const StreamParams& p, int wave, int nwaves, bool shar
         src = row;
       }
       const int64_t wrow = (int64_t)e * p.N + min(n0 + tr, p.N - 1);
+      if constexpr (R > 1 && !kBlockScaled<T>)
+        s.w1 = (int64_t)(min(n0 + kUnitRows + tr, p.N - 1) - min(n0 + tr, p.N - 1)) * p.K *
+               F::WH / 2;
+      else
+        s.w1 = 0;
       s.a = A + (int64_t)src * p.lda * F::AB + lba;
       s.w = W + wrow * p.K * F::WH / 2 + lbw;
       s.wx = kBlockScaled<T> ? p.w_mx + wrow * (p.K / kMxBlock) + g : nullptr;
@@ -354,22 +378,22 @@ __device__ void run_units(const StreamParams& p, int wave, int nwaves, bool shar
     s.n = n0 + g * 4;
   };
   // the shifted-last-batch path needs every unit's row to span at least one batch
-  constexpr int BK = F::U * F::KS;
+  constexpr int BK = F::U(R) * F::KS;
   const bool full = (nrt == 0 || p.K >= BK) && (nsh == 0 || Kc >= BK);
   if (full)
-    stream_units<T, true>(wave, nsh + nrt, nwaves, lane, p.store, resolve);
+    stream_units<T, R, true>(wave, nsh + nrt, nwaves, lane, p.store, resolve);
   else
-    stream_units<T, false>(wave, nsh + nrt, nwaves, lane, p.store, resolve);
+    stream_units<T, R, false>(wave, nsh + nrt, nwaves, lane, p.store, resolve);
 }
 
 // One launch: every wave streams its share of the units (the shared expert's first, bf16 only,
 // then the routed experts').
-template <Elt T>
+template <Elt T, int R>
 __global__ __launch_bounds__(256, 1) void stream_kernel(StreamParams p) {
   // waves numbered die by die: consecutive numbers share a CU, then a die
   const int wave = xcd_logical_block(blockIdx.x, gridDim.x) * 4 +
                    __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  run_units<T>(p, wave, gridDim.x * 4, T == Elt::BF16, true);
+  run_units<T, R>(p, wave, gridDim.x * 4, T == Elt::BF16, true);
 }
 
 // out[t, n] = store(sum_s part[s][t][n]) over the S fp32 slabs of a split shared slot, added in
@@ -394,6 +418,15 @@ __global__ __launch_bounds__(256) void reduce_slabs_kernel(const float* __restri
   store_block(f32x4_t{b.x, b.y, b.z, b.w}, out, ldo, t, n + 4, mode);
 }
 
+// A dense product through the shared slot alone (bf16, one row block per unit). A wave of it must
+// fit on a SIMD beside a wave of the MXFP4 kernel (152 + 360 of the 512 registers): the bf16
+// shared expert of a layer with narrow experts streams on a side stream next to those launches.
+__global__ __launch_bounds__(256, 1) void stream_dense_kernel(StreamParams p) {
+  const int wave = xcd_logical_block(blockIdx.x, gridDim.x) * 4 +
+                   __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  run_units<Elt::BF16, 1>(p, wave, gridDim.x * 4, true, false);
+}
+
 }  // namespace
 
 hipError_t launch_reduce_slabs(const float* part, int S, int T, int N, int64_t ld, void* out,
@@ -416,11 +449,14 @@ hipError_t launch_stream(const StreamParams& p, hipStream_t s) {
   if (p.ksplit_s > 1 && (p.store != kStoreF32 || p.Ks % (p.ksplit_s * 8))) return hipErrorInvalidValue;
   switch (p.wt) {
     case Elt::BF16:
-      hipLaunchKernelGGL(stream_kernel<Elt::BF16>, grid, block, 0, s, p);
+      if (p.n_slices)  // routed units (and maybe the shared slot's)
+        hipLaunchKernelGGL((stream_kernel<Elt::BF16, Fmt<Elt::BF16>::R>), grid, block, 0, s, p);
+      else             // a dense product through the shared slot alone
+        hipLaunchKernelGGL(stream_dense_kernel, grid, block, 0, s, p);
       break;
     case Elt::FP8:
       if (!p.w_scale) return hipErrorInvalidValue;
-      hipLaunchKernelGGL(stream_kernel<Elt::FP8>, grid, block, 0, s, p);
+      hipLaunchKernelGGL((stream_kernel<Elt::FP8, Fmt<Elt::FP8>::R>), grid, block, 0, s, p);
       break;
     case Elt::MXFP4:
     case Elt::MXFP8:
@@ -429,9 +465,9 @@ hipError_t launch_stream(const StreamParams& p, hipStream_t s) {
       if (p.N % (kUnitRows * (p.wt == Elt::MXFP4 ? Fmt<Elt::MXFP4>::R : Fmt<Elt::MXFP8>::R)))
         return hipErrorInvalidValue;
       if (p.wt == Elt::MXFP4)
-        hipLaunchKernelGGL(stream_kernel<Elt::MXFP4>, grid, block, 0, s, p);
+        hipLaunchKernelGGL((stream_kernel<Elt::MXFP4, Fmt<Elt::MXFP4>::R>), grid, block, 0, s, p);
       else
-        hipLaunchKernelGGL(stream_kernel<Elt::MXFP8>, grid, block, 0, s, p);
+        hipLaunchKernelGGL((stream_kernel<Elt::MXFP8, Fmt<Elt::MXFP8>::R>), grid, block, 0, s, p);
       break;
     default:
       return hipErrorInvalidValue;
