@@ -220,8 +220,51 @@ def measure(w, moe, torch, steps, warmup, graph):
         roof["traffic_over_algorithmic_bytes"] = round(traffic / max(bts / max(nlaunch, 1), 1), 3)
     breakdown = {k_: round(v * 1e3 / 3, 2) for k_, v in sorted(per_kernel.items(),
                                                               key=lambda kv: -kv[1])}
+    # outside the timed region: the distribution of single steps (events on the call's stream,
+    # which also waits for the side stream), and steps after the 256 MB Infinity Cache has been
+    # overwritten by a 512 MB store, so that no weights stay cached between steps
+    dist = step_times(layer, torch, max(steps, 20))
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = step_times(layer, torch, min(max(steps, 10), 30), before=lambda: flush.fill_(1))
+    del flush
+    pct = lambda a, q: round(float(np.percentile(a, q)), 1)
     return dict(ms_per_step=ms_step, tokens_per_s=cfg.T / (ms_step * 1e-3), roofline=roof,
-                kernel_us_per_step=breakdown, touched_experts=int(np.count_nonzero(counts)))
+                kernel_us_per_step=breakdown, touched_experts=int(np.count_nonzero(counts)),
+                step_us=dict(median=pct(dist, 50), p10=pct(dist, 10), p90=pct(dist, 90),
+                             cold_cache_median=pct(cold, 50),
+                             cold_cache_tokens_per_s=round(cfg.T / (np.median(cold) * 1e-6), 1)))
+
+
+def step_times(layer, torch, n, before=None):
+    """Microseconds of n single steps, each bracketed by events on the current stream."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for a, b in ev:
+        if before is not None:
+            before()
+        a.record()
+        layer()
+        b.record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+
+
+def peak_from_clock():
+    """Dense peaks recomputed from the device's reported peak clock and CU count (4096 bf16 and
+    8192 fp8 flops per CU per clock on gfx950), beside the published figures."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return None
+    clk, cus = ctypes.c_int(0), ctypes.c_int(0)
+    if hip.hipDeviceGetAttribute(ctypes.byref(clk), 5, 0) or \
+            hip.hipDeviceGetAttribute(ctypes.byref(cus), 63, 0):   # clock rate (kHz), CU count
+        return None
+    hz = clk.value * 1e3
+    return dict(clock_mhz=round(hz / 1e6), cus=cus.value,
+                bf16_tflops=round(cus.value * 4096 * hz / 1e12, 1),
+                fp8_tflops=round(cus.value * 8192 * hz / 1e12, 1))
 
 
 def measured_traffic(workload, kernel):
@@ -253,7 +296,14 @@ def cpu_baseline(w, n_tokens):
     t0 = time.perf_counter()
     O.forward(inp, toks)
     dt = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return dict(value=round(n_tokens / dt, 3), unit="tokens/s", cores=1, kind="oracle",
+                cpu_model=model, host_cpus=os.cpu_count(),
                 sample=f"{n_tokens} of the {cfg.T} tokens of {cfg.name} (router over all E, "
                        f"k experts and the shared expert per token), double precision, one "
                        f"thread, {dt:.1f} s")
@@ -302,9 +352,11 @@ def main():
         r = measure(w, moe, torch, args.steps, args.warmup, args.graph)
         extra[name] = dict(tokens_per_s=round(r["tokens_per_s"], 1), dtype=dtype_of(w["cfg"]),
                            ms_per_step=round(r["ms_per_step"], 4), roofline=r["roofline"],
-                           kernel_us_per_step=r["kernel_us_per_step"])
+                           step_us=r["step_us"], kernel_us_per_step=r["kernel_us_per_step"])
         del w
         torch.cuda.empty_cache()
+    out["step_us"] = res["step_us"]
+    out["peak_from_clock"] = peak_from_clock()
     out["kernel_us_per_step"] = res["kernel_us_per_step"]
     out["touched_experts"] = res["touched_experts"]
     if extra:
