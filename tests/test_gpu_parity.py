@@ -471,3 +471,33 @@ def test_full_size_layer(name, full_runs):
         erre = rel_frob(y[toks], refe["y"])
         say(f"[gpu]   {name}: vs emulating oracle {erre:.3e}")
         assert erre <= 5e-3
+
+
+@pytest.mark.parametrize("name,path", [("bf16_ragged", "stream"), ("mxfp4_small", "stream"),
+                                       ("fp8_small", "stream"), ("bf16_ragged", "grouped")])
+def test_graph_replay_matches_eager(name, path):
+    # A layer call captured in a graph (side-stream fork and join included) and replayed
+    # several times, with eager work and synchronisation between the replays: every replay
+    # must equal the eager call bit for bit.
+    cfg = SMALL[name]
+    inp = mi.make_layer(cfg, seed=12)
+    dev = moe.to_device(inp)
+    layer = moe.layer_from(dev, cfg.k, path=path)
+    want = layer().clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        layer()
+    torch.cuda.synchronize()
+    for i in range(4):
+        layer.y.zero_()
+        junk = torch.randn(1 << 20, device="cuda") * (i + 1)   # eager work in between
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.y, want), f"replay {i}"
+        del junk
