@@ -117,6 +117,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
   constexpr int STAGE = (BM + BN) * SL;
   constexpr int EPW = WN + 4;                                   // epilogue strip row (floats)
   static_assert(A_GRP >= 1 && B_GRP >= 1 && MB >= 1 && NB >= 1, "tile too small");
+  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0,
+                "every tile row must be covered by the waves' 1-KB loads");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tiles are whole 32 x 32 blocks");
   static_assert(NW * 16 * EPW * 4 <= NS * STAGE, "epilogue strips must fit in the stages");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
