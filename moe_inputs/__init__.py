@@ -46,7 +46,8 @@ __all__ = [
 BLOCK_FORMATS = ("mxfp4", "mxfp8")
 MX_BLOCK = 32
 
-TAGS = dict(x=1, W_r=2, b=3, W_up=4, W_down=5, Ws_up=6, Ws_down=7, W_in=8, W_out=9, rank=10)
+TAGS = dict(x=1, W_r=2, b=3, W_up=4, W_down=5, Ws_up=6, Ws_down=7, W_in=8, W_out=9, rank=10,
+            dy=11)
 
 _GOLDEN = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "tests", "golden")
 
@@ -363,3 +364,9 @@ def make_layer(cfg: LayerConfig, seed: int = 0, tensors=None) -> dict:
 def expert_rank_permutation(seed: int, E: int) -> np.ndarray:
     """Which expert holds popularity rank r (rank 0 = most popular) in the skewed profiles."""
     return _rng(seed, TAGS["rank"]).permutation(E)
+
+
+def make_grad_output(cfg: LayerConfig, seed: int = 0) -> np.ndarray:
+    """Upstream gradient dy [T, H] for the backward pass: N(0, 1) draws stored in the layer's
+    activation format (bf16 bit patterns or fp32)."""
+    return _store(_normal((seed, TAGS["dy"]), (cfg.T, cfg.H), 1.0), cfg.act_dtype)[0]

@@ -29,6 +29,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_E4M3 = 2, ORC_F64 = 3, ORC_MXFP4 = 4, ORC_MXFP8 = 5 };
@@ -398,4 +399,139 @@ int orc_bias_update(double *b, const int32_t *counts, const double *target, int3
     b[e] += gamma * (double)((d > 0.0) - (d < 0.0));
   }
   return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ layer backward */
+
+/* Gradient accumulators of the backward pass, all in double; any pointer may be NULL (that
+ * gradient is skipped). With expert >= 0 the routed weight gradients dW_up / dW_down hold that
+ * one expert only ([I][D] and [D][I]); with expert < 0 they hold the whole stacks ([E*I][D],
+ * [E*D][I]). dW_r is [E][H]; dWs_up [I_s][H]; dWs_down [H][I_s]. */
+typedef struct {
+  double *dW_r, *dW_up, *dW_down, *dWs_up, *dWs_down;
+  int32_t expert;
+  int32_t pad_;
+} orc_grads;
+
+/* Backward pass of the plain MoE layer (no latent projections) for the listed tokens (all T if
+ * tokens is NULL), given the selection idx the forward made (one row of k per listed token) and
+ * the gradient dy of a scalar loss with respect to y (one row of H per listed token).
+ *
+ * The selection is piecewise constant in the inputs, so it is held fixed and the gradient flows
+ * through the gate weights only: with s_j = sigmoid(z_{e_j}), Z = sum_j s_j and g_j = s_j / Z
+ * (the renormalised unbiased scores; the bias steers the choice and gets no gradient, as in
+ * aux-loss-free balancing [N3N 2.2]), the chain rule of the forward written out step by step:
+ *   a = W_up[e] x,  r = max(a, 0),  h = r^2,  Y_j = W_down[e] h,  y += g_j Y_j;
+ *   dY_j = g_j dy,  dg_j = <dy, Y_j>,  dh = W_down[e]^T dY_j,  da = 2 r (.) dh,
+ *   dx += W_up[e]^T da,  dW_down[e] += dY_j h^T,  dW_up[e] += da x^T;
+ *   ds_j = (dg_j - sum_m g_m dg_m) / Z,  dz_{e_j} = ds_j s_j (1 - s_j)  (0 for other experts),
+ *   dx += sum_j dz_{e_j} W_r[e_j],  dW_r[e_j] += dz_{e_j} x;
+ *   shared expert (weight 1): a_s = Ws_up x, r_s = max(a_s, 0), dh_s = Ws_down^T dy,
+ *   da_s = 2 r_s (.) dh_s, dx += Ws_up^T da_s, dWs_down += dy h_s^T, dWs_up += da_s x^T.
+ * The derivative of the squared ReLU is taken as 2 max(a, 0), which is 0 at a = 0.
+ * dx is [n][H] and dz [n][E] per listed token (either may be NULL). */
+int orc_backward_tokens(const orc_layer *L, const int32_t *tokens, int32_t n, const int32_t *idx,
+                        const double *dy, double *dx, double *dz, const orc_grads *G) {
+  if (!L || !idx || !dy || L->latent || L->k < 1 || L->k > ORC_EMAX) return ORC_EINVAL;
+  const int32_t H = L->H, I = L->I, Is = L->I_shared, E = L->E, k = L->k;
+  const int32_t Imax = I > Is ? I : Is;
+  double *r = (double *)malloc(sizeof(double) * (size_t)Imax);
+  double *dh = (double *)malloc(sizeof(double) * (size_t)Imax);
+  double *Y = (double *)malloc(sizeof(double) * (size_t)H);
+  double *gx = (double *)malloc(sizeof(double) * (size_t)H);
+  double s[ORC_EMAX], g[ORC_EMAX], dg[ORC_EMAX];
+  int rc = ORC_OK;
+  if (!r || !dh || !Y || !gx) { rc = ORC_EINVAL; goto done; }
+  int32_t cnt = tokens ? n : L->T;
+  for (int32_t a = 0; a < cnt; ++a) {
+    const int32_t t = tokens ? tokens[a] : a;
+    const int32_t *it = idx + (int64_t)a * k;
+    const double *dyt = dy + (int64_t)a * H;
+    for (int32_t c = 0; c < H; ++c) gx[c] = 0.0;
+    /* gates of the given selection */
+    double Z = 0.0;
+    for (int32_t j = 0; j < k; ++j) {
+      if (it[j] < 0 || it[j] >= E) { rc = ORC_EINVAL; goto done; }
+      double z = 0.0;
+      for (int32_t c = 0; c < H; ++c) z += at(&L->x, t, c) * at(&L->W_r, it[j], c);
+      s[j] = 1.0 / (1.0 + exp(-z));
+      Z += s[j];
+    }
+    for (int32_t j = 0; j < k; ++j) g[j] = s[j] / Z;
+    /* routed experts */
+    for (int32_t j = 0; j < k; ++j) {
+      const int32_t e = it[j];
+      const int want_w = G && (G->expert < 0 || G->expert == e);
+      const int64_t ew = G && G->expert >= 0 ? 0 : e; /* row block of e in the dW arrays */
+      for (int32_t i = 0; i < I; ++i) {
+        double acc = 0.0;
+        for (int32_t c = 0; c < H; ++c) acc += at(&L->W_up, (int64_t)e * I + i, c) * at(&L->x, t, c);
+        r[i] = acc > 0.0 ? acc : 0.0;
+      }
+      dg[j] = 0.0;
+      for (int32_t c = 0; c < H; ++c) {
+        double acc = 0.0;
+        for (int32_t i = 0; i < I; ++i) acc += at(&L->W_down, (int64_t)e * H + c, i) * (r[i] * r[i]);
+        Y[c] = acc;
+        dg[j] += dyt[c] * acc;
+      }
+      for (int32_t i = 0; i < I; ++i) {
+        double acc = 0.0;
+        for (int32_t c = 0; c < H; ++c) acc += at(&L->W_down, (int64_t)e * H + c, i) * (g[j] * dyt[c]);
+        dh[i] = 2.0 * r[i] * acc; /* da */
+      }
+      for (int32_t c = 0; c < H; ++c) {
+        double acc = 0.0;
+        for (int32_t i = 0; i < I; ++i) acc += at(&L->W_up, (int64_t)e * I + i, c) * dh[i];
+        gx[c] += acc;
+      }
+      if (want_w && G->dW_down)
+        for (int32_t c = 0; c < H; ++c)
+          for (int32_t i = 0; i < I; ++i)
+            G->dW_down[(ew * H + c) * I + i] += g[j] * dyt[c] * (r[i] * r[i]);
+      if (want_w && G->dW_up)
+        for (int32_t i = 0; i < I; ++i)
+          for (int32_t c = 0; c < H; ++c)
+            G->dW_up[(ew * I + i) * H + c] += dh[i] * at(&L->x, t, c);
+    }
+    /* router: through the renormalised gates and the sigmoid */
+    double gdg = 0.0;
+    for (int32_t j = 0; j < k; ++j) gdg += g[j] * dg[j];
+    if (dz)
+      for (int32_t e = 0; e < E; ++e) dz[(int64_t)a * E + e] = 0.0;
+    for (int32_t j = 0; j < k; ++j) {
+      const double dzj = (dg[j] - gdg) / Z * s[j] * (1.0 - s[j]);
+      if (dz) dz[(int64_t)a * E + it[j]] = dzj;
+      for (int32_t c = 0; c < H; ++c) gx[c] += dzj * at(&L->W_r, it[j], c);
+      if (G && G->dW_r)
+        for (int32_t c = 0; c < H; ++c) G->dW_r[(int64_t)it[j] * H + c] += dzj * at(&L->x, t, c);
+    }
+    /* shared expert */
+    if (Is) {
+      for (int32_t i = 0; i < Is; ++i) {
+        double acc = 0.0;
+        for (int32_t c = 0; c < H; ++c) acc += at(&L->Ws_up, i, c) * at(&L->x, t, c);
+        r[i] = acc > 0.0 ? acc : 0.0;
+        double d = 0.0;
+        for (int32_t c = 0; c < H; ++c) d += at(&L->Ws_down, c, i) * dyt[c];
+        dh[i] = 2.0 * r[i] * d; /* da_s */
+      }
+      for (int32_t c = 0; c < H; ++c) {
+        double acc = 0.0;
+        for (int32_t i = 0; i < Is; ++i) acc += at(&L->Ws_up, i, c) * dh[i];
+        gx[c] += acc;
+      }
+      if (G && G->dWs_down)
+        for (int32_t c = 0; c < H; ++c)
+          for (int32_t i = 0; i < Is; ++i) G->dWs_down[(int64_t)c * Is + i] += dyt[c] * (r[i] * r[i]);
+      if (G && G->dWs_up)
+        for (int32_t i = 0; i < Is; ++i)
+          for (int32_t c = 0; c < H; ++c) G->dWs_up[(int64_t)i * H + c] += dh[i] * at(&L->x, t, c);
+    }
+    if (dx)
+      for (int32_t c = 0; c < H; ++c) dx[(int64_t)a * H + c] = gx[c];
+  }
+done:
+  free(r); free(dh); free(Y); free(gx);
+  return rc;
 }

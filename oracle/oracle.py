@@ -41,6 +41,12 @@ class OrcMat(C.Structure):
                 ("pad_", C.c_int32), ("cols", C.c_int64)]
 
 
+class OrcGrads(C.Structure):
+    _fields_ = [("dW_r", C.c_void_p), ("dW_up", C.c_void_p), ("dW_down", C.c_void_p),
+                ("dWs_up", C.c_void_p), ("dWs_down", C.c_void_p), ("expert", C.c_int32),
+                ("pad_", C.c_int32)]
+
+
 class OrcLayer(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("T", "H", "E", "k", "I", "I_shared", "latent",
                                          "fp8_emulate")] + \
@@ -78,6 +84,8 @@ def lib():
             L.orc_forward_tokens.argtypes = [C.POINTER(OrcLayer), C.c_void_p, C.c_int32, i32p,
                                              f64p, f64p, f64p]
             L.orc_bias_update.argtypes = [f64p, i32p, f64p, C.c_int32, C.c_double]
+            L.orc_backward_tokens.argtypes = [C.POINTER(OrcLayer), C.c_void_p, C.c_int32, i32p,
+                                              f64p, C.c_void_p, C.c_void_p, C.POINTER(OrcGrads)]
             _lib = L
     return _lib
 
@@ -241,6 +249,56 @@ def forward(inp: dict, tokens=None, fp8_emulate: bool = False, threads: int = 1)
     idx, g, m = route(z, inp["b"], inp["config"].k)
     y = forward_tokens(inp, idx, g, tokens, fp8_emulate)
     return dict(logits=z, idx=idx, gates=g, margin=m, y=y)
+
+
+GRAD_NAMES = ("dx", "dz", "dW_r", "dW_up", "dW_down", "dWs_up", "dWs_down")
+
+
+def backward(inp: dict, idx: np.ndarray, dy: np.ndarray, tokens=None, want=GRAD_NAMES,
+             expert: int = -1, threads: int = 1) -> dict:
+    """Gradients in double of the scalar loss sum_t <dy_t, y_t> for the listed tokens (all if
+    None), holding the selection idx fixed (one row of k per listed token; dy one row of H).
+
+    Returns the requested names of GRAD_NAMES: dx [n, H] and dz [n, E] per listed token; weight
+    gradients summed over the listed tokens, dW_up / dW_down for one expert only when
+    ``expert`` >= 0. ``threads`` > 1 splits the tokens over threads and adds their weight
+    gradients afterwards (float64 sums, so the order of that final addition may differ from a
+    single call in the last bits)."""
+    cfg = inp["config"]
+    if cfg.latent:
+        raise ValueError("the backward oracle covers the plain MoE layer only")
+    t_all = np.arange(cfg.T, dtype=np.int32) if tokens is None else \
+        np.ascontiguousarray(tokens, dtype=np.int32)
+    n = len(t_all)
+    idx = np.ascontiguousarray(idx, dtype=np.int32).reshape(n, cfg.k)
+    dy = np.ascontiguousarray(dy, dtype=np.float64).reshape(n, cfg.H)
+    if threads > 1 and n > 1:
+        groups = [g for g in np.array_split(np.arange(n), min(threads, n)) if len(g)]
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(len(groups)) as ex:
+            parts = list(ex.map(lambda g: backward(inp, idx[g], dy[g], t_all[g], want, expert),
+                                groups))
+        out = {}
+        for k in parts[0]:
+            out[k] = np.concatenate([p[k] for p in parts]) if k in ("dx", "dz") else \
+                sum(p[k] for p in parts)
+        return out
+    H, E, I, Is = cfg.H, cfg.E, cfg.I, cfg.I_shared
+    shapes = {"dx": (n, H), "dz": (n, E), "dW_r": (E, H),
+              "dW_up": (I, H) if expert >= 0 else (E, I, H),
+              "dW_down": (H, I) if expert >= 0 else (E, H, I),
+              "dWs_up": (Is, H), "dWs_down": (H, Is)}
+    out = {k: np.zeros(shapes[k], np.float64) for k in want
+           if k in shapes and not (k.startswith("dWs") and not Is)}
+    G = OrcGrads()
+    for k in ("dW_r", "dW_up", "dW_down", "dWs_up", "dWs_down"):
+        setattr(G, k, out[k].ctypes.data if k in out else None)
+    G.expert = expert
+    L, keep = layer(inp)
+    _check(lib().orc_backward_tokens(C.byref(L), t_all.ctypes.data, n, idx, dy,
+                                     out["dx"].ctypes.data if "dx" in out else None,
+                                     out["dz"].ctypes.data if "dz" in out else None, C.byref(G)))
+    return out
 
 
 def bias_update(b: np.ndarray, counts: np.ndarray, target: np.ndarray, gamma: float) -> np.ndarray:

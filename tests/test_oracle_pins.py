@@ -436,3 +436,139 @@ def test_bias_update_sign_rule():
     target = np.array([5.0, 5.0, 7.0, 9.0])
     nb = O.bias_update(b, counts, target, 0.25)
     np.testing.assert_array_equal(nb, [-0.25, 0.75, -0.5, 1.25])
+
+
+# ----------------------------------------------------------------------------- backward
+
+_WEIGHTS = ("x", "W_r", "W_up", "W_down", "Ws_up", "Ws_down")
+_GRAD_OF = {"x": "dx", "W_r": "dW_r", "W_up": "dW_up", "W_down": "dW_down", "Ws_up": "dWs_up",
+            "Ws_down": "dWs_down"}
+
+
+def f64_layer(seed, T=3, H=8, E=5, k=2, I=6, Is=4):
+    """A tiny layer held in float64 (read exactly by the oracle), with pre-activations kept away
+    from the squared-ReLU's kink so that central differences never straddle it."""
+    c = cfg(T=T, H=H, E=E, k=k, I=I, I_shared=Is)
+    rng = np.random.default_rng(seed)
+    inp = {"config": c, "x": rng.standard_normal((T, H)),
+           "W_r": rng.standard_normal((E, H)) / np.sqrt(H),
+           "b": rng.uniform(-0.1, 0.1, E).astype(np.float32),
+           "W_up": rng.standard_normal((E, I, H)) / np.sqrt(H),
+           "W_down": rng.standard_normal((E, H, I)) / np.sqrt(I)}
+    if Is:
+        inp["Ws_up"] = rng.standard_normal((Is, H)) / np.sqrt(H)
+        inp["Ws_down"] = rng.standard_normal((H, Is)) / np.sqrt(Is)
+    a = np.einsum("eih,th->tei", inp["W_up"], inp["x"])
+    gap = np.abs(a).min()
+    if Is:
+        gap = min(gap, np.abs(inp["x"] @ inp["Ws_up"].T).min())
+    return inp, gap
+
+
+def loss(inp, idx, dy):
+    """Sum_t <dy_t, y_t> with the selection idx held fixed and gates recomputed from the logits."""
+    g = O.gates_for(O.logits(inp), idx)
+    return float(np.sum(O.forward_tokens(inp, idx, g) * dy))
+
+
+def test_backward_matches_central_differences():
+    # Pins every gradient of the backward oracle to the forward oracle alone: each entry of
+    # every input is nudged by +-eps and the change of the loss compared with the gradient.
+    for seed in range(20):
+        inp, gap = f64_layer(seed)
+        if gap > 1e-2:
+            break
+    c = inp["config"]
+    idx, _, margin = O.route(O.logits(inp), inp["b"], c.k)
+    dy = np.random.default_rng(99).standard_normal((c.T, c.H))
+    grads = O.backward(inp, idx, dy)
+    eps = 1e-6
+    for name in _WEIGHTS:
+        arr = inp[name]
+        fd = np.zeros(arr.shape)
+        for i in np.ndindex(arr.shape):
+            keep = arr[i]
+            arr[i] = keep + eps
+            up = loss(inp, idx, dy)
+            arr[i] = keep - eps
+            dn = loss(inp, idx, dy)
+            arr[i] = keep
+            fd[i] = (up - dn) / (2 * eps)
+        got = grads[_GRAD_OF[name]]
+        assert np.allclose(got, fd, rtol=1e-6, atol=1e-8), (name, np.abs(got - fd).max())
+
+
+def torch_layer_loss(t, idx, dy, k):
+    """The layer written with torch float64 ops on CPU (selection fixed) for autograd."""
+    x, W_r, W_up, W_down = t["x"], t["W_r"], t["W_up"], t["W_down"]
+    s = torch.sigmoid(x @ W_r.T)
+    sel = torch.from_numpy(idx.astype(np.int64))
+    ss = torch.gather(s, 1, sel)
+    g = ss / ss.sum(dim=1, keepdim=True)
+    y = torch.zeros_like(x)
+    for j in range(k):
+        e = sel[:, j]
+        a = torch.einsum("tih,th->ti", W_up[e], x)
+        h = torch.relu(a) ** 2
+        y = y + g[:, j:j + 1] * torch.einsum("thi,ti->th", W_down[e], h)
+    if "Ws_up" in t:
+        y = y + (torch.relu(x @ t["Ws_up"].T) ** 2) @ t["Ws_down"].T
+    return (y * torch.from_numpy(dy)).sum()
+
+
+@pytest.mark.parametrize("shared", [0, 24])
+def test_backward_matches_torch_autograd(shared):
+    # bf16-valued inputs (the oracle reads the bit patterns exactly; torch gets the same values
+    # in float64); gradients from torch's reverse-mode differentiation of the layer.
+    c = cfg(T=16, H=32, E=8, k=3, I=16, I_shared=shared, act_dtype="bf16", expert_dtype="bf16")
+    inp = mi.make_layer(c, seed=4)
+    dy64 = mi.bf16_bits_to_f32(mi.make_grad_output(c, seed=4)).astype(np.float64)
+    idx, _, _ = O.route(O.logits(inp), inp["b"], c.k)
+    grads = O.backward(inp, idx, dy64)
+    names = [n for n in _WEIGHTS if n in inp]
+    t = {n: torch.tensor(f64(inp, n), dtype=torch.float64, requires_grad=True) for n in names}
+    L = torch_layer_loss(t, idx, dy64, c.k)
+    auto = torch.autograd.grad(L, [t[n] for n in names])
+    for n, gref in zip(names, auto):
+        got = grads[_GRAD_OF[n]]
+        ref = gref.numpy()
+        assert np.allclose(got, ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max()), n
+    # dz: only the selected experts carry a logit gradient
+    dz = grads["dz"]
+    mask = np.zeros_like(dz, dtype=bool)
+    np.put_along_axis(mask, idx.astype(np.int64), True, axis=1)
+    assert np.all(dz[~mask] == 0.0)
+
+
+def test_backward_expert_filter_and_threads_agree_with_full_call():
+    c = cfg(T=40, H=32, E=6, k=2, I=16, I_shared=8, act_dtype="bf16", expert_dtype="bf16")
+    inp = mi.make_layer(c, seed=2)
+    dy = mi.bf16_bits_to_f32(mi.make_grad_output(c, seed=2)).astype(np.float64)
+    idx, _, _ = O.route(O.logits(inp), inp["b"], c.k)
+    full = O.backward(inp, idx, dy)
+    split = O.backward(inp, idx, dy, threads=4)
+    for n in full:
+        assert np.allclose(split[n], full[n], rtol=1e-12, atol=1e-14), n
+    e = int(idx[0, 0])
+    one = O.backward(inp, idx, dy, want=("dW_up", "dW_down"), expert=e)
+    assert np.array_equal(one["dW_up"], full["dW_up"][e])
+    assert np.array_equal(one["dW_down"], full["dW_down"][e])
+    # tokens that do not route to e contribute nothing to its weight gradients
+    sel = np.where((idx == e).any(axis=1))[0]
+    sub = O.backward(inp, idx[sel], dy[sel], tokens=sel, want=("dW_up", "dW_down"), expert=e)
+    assert np.array_equal(sub["dW_up"], one["dW_up"])
+
+
+def test_backward_is_linear_in_dy_and_zero_input_gives_zero_weight_gradients():
+    c = cfg(T=12, H=32, E=5, k=2, I=16, I_shared=8, act_dtype="bf16", expert_dtype="bf16")
+    inp = mi.make_layer(c, seed=6)
+    idx, _, _ = O.route(O.logits(inp), inp["b"], c.k)
+    dy = mi.bf16_bits_to_f32(mi.make_grad_output(c, seed=6)).astype(np.float64)
+    g1 = O.backward(inp, idx, dy)
+    g2 = O.backward(inp, idx, 2.0 * dy)
+    for n in g1:
+        assert np.array_equal(g2[n], 2.0 * g1[n]), n
+    z = dict(inp, x=np.zeros_like(inp["x"]))
+    g0 = O.backward(z, idx, dy)
+    for n in ("dx", "dz", "dW_r", "dW_up", "dW_down", "dWs_up", "dWs_down"):
+        assert not np.any(g0[n]), n
