@@ -160,7 +160,6 @@ int32_t moe_dispatch(const int32_t *idx, int32_t T, int32_t E, int32_t k, int32_
                      int32_t *offsets, int32_t *perm, int32_t *pos, void *ws, size_t ws_bytes,
                      void *stream);
 
-/* Static text for a status code. */
 /* Aux-loss-free load balancing step ("Nemotron 3 Nano：開放高效的 MoE 混合 Mamba-Transformer
  * 智能體推理模型", section 2.2, training hyper-parameters: DeepSeek's auxiliary-loss-free
  * balancing). The routing bias of every expert moves by a fixed step toward its target load:
@@ -172,6 +171,39 @@ int32_t moe_dispatch(const int32_t *idx, int32_t T, int32_t E, int32_t k, int32_
 int32_t moe_bias_update(const int32_t *counts, const float *target, int32_t E, float gamma,
                         float *b, void *stream);
 
+/* ---- Backward pass (training) of the plain MoE layer.
+ * Gradients of a scalar loss given dy = dLoss/dy [T, H] (device, act dtype), for the forward that
+ * moe_layer_forward computes ("NVIDIA Nemotron 3: Efficient and Open Intelligence", section 2.2;
+ * "Nemotron 3 Nano: Open, Efficient Mixture-of-Experts Hybrid Mamba-Transformer Model for Agentic
+ * Reasoning", section "技术框架"). The top-k selection is piecewise constant, so it is held at the
+ * forward's choice and the gradient reaches the router through the gate weights only:
+ *   g_j = s_j / sum_m s_m with s = sigmoid(x W_r^T) over the selected experts;
+ *   dz_{e_j} = (dg_j - sum_m g_m dg_m) / sum_m s_m * s_j (1 - s_j), dg_j = <dy, Y_j>, where Y_j is
+ *   expert e_j's output. The routing bias b only steers the selection and has no gradient.
+ * The squared ReLU's derivative is 2 relu(a). Every gradient is written (not accumulated) in
+ * fp32, row-major:
+ *   dx [T, H], dW_r [E, H], dW_up [E, I, H], dW_down [E, H, I], dWs_up [I_s, H], dWs_down [H, I_s]
+ *   (the last two only when I_shared > 0; all others are required).
+ * Supported: act_dtype = expert_dtype = MOE_BF16, latent = 0, routing computed inside (flags:
+ * path bits ignored, MOE_ROUTING_GIVEN not accepted) -- else MOE_ERR_UNSUPPORTED. The call
+ * recomputes the forward's routing and expert activations from x (nothing is saved between
+ * calls) and makes transposed copies of the weights in the workspace. Pointers: 16-byte aligned
+ * device memory owned by the caller. Workspace: moe_backward_workspace_size bytes. Asynchronous
+ * on `stream`; nothing is allocated or synchronised. Results are deterministic (no atomics). */
+typedef struct {
+  float *dx;
+  float *dW_r;
+  float *dW_up;
+  float *dW_down;
+  float *dWs_up;
+  float *dWs_down;
+} moe_grads_t;
+
+int32_t moe_backward_workspace_size(const moe_desc_t *desc, size_t *bytes);
+int32_t moe_layer_backward(const moe_desc_t *desc, const moe_weights_t *weights, const void *dy,
+                           moe_grads_t *grads, void *ws, size_t ws_bytes, void *stream);
+
+/* Static text for a status code. */
 const char *moe_status_str(int32_t code);
 
 /* ---- Diagnostics: per-launch timing with HIP events (process-wide; not for concurrent calls).

@@ -22,7 +22,8 @@ PATH_AUTO, PATH_GROUPED, PATH_STREAM, ROUTING_GIVEN = 0, 1, 2, 4
 _PATHS = {"auto": PATH_AUTO, "grouped": PATH_GROUPED, "stream": PATH_STREAM}
 
 EXPORTS = ("moe_workspace_size", "moe_layer_forward", "latent_moe_forward", "moe_route",
-           "moe_dispatch_workspace_size", "moe_dispatch", "moe_bias_update", "moe_status_str",
+           "moe_dispatch_workspace_size", "moe_dispatch", "moe_bias_update",
+           "moe_backward_workspace_size", "moe_layer_backward", "moe_status_str",
            "moe_trace_enable",
            "moe_trace_count", "moe_trace_read", "moe_trace_reset")
 
@@ -41,6 +42,11 @@ class MoeWeights(C.Structure):
 class MoeRouting(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("idx", "gates", "counts", "offsets", "perm", "pos",
                                           "logits")]
+
+
+class MoeGrads(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("dx", "dW_r", "dW_up", "dW_down", "dWs_up",
+                                          "dWs_down")]
 
 
 class MoeError(RuntimeError):
@@ -71,6 +77,9 @@ def lib() -> C.CDLL:
             L.moe_dispatch_workspace_size.argtypes = [i32, i32, i32, C.POINTER(sz)]
             L.moe_dispatch.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
             L.moe_bias_update.argtypes = [vp, vp, i32, C.c_float, vp, vp]
+            L.moe_backward_workspace_size.argtypes = [C.POINTER(MoeDesc), C.POINTER(sz)]
+            L.moe_layer_backward.argtypes = [C.POINTER(MoeDesc), C.POINTER(MoeWeights), vp,
+                                             C.POINTER(MoeGrads), vp, sz, vp]
             L.moe_status_str.argtypes = [i32]
             L.moe_trace_enable.argtypes = [i32, C.c_char_p]
             L.moe_trace_count.argtypes = []
@@ -190,6 +199,48 @@ class Layer:
                      C.byref(self.r) if self.r is not None else None, _stream(stream))
         _check(rc, "latent_moe_forward" if self.desc.latent else "moe_layer_forward")
         return self.y
+
+
+class Backward:
+    """One backward call prepared once (descriptor, weights, gradient outputs in fp32,
+    workspace): ``__call__(dy)`` writes the gradients of sum(dy * y) into ``self.grads``."""
+
+    def __init__(self, x, W_r, b, W_up, W_down, k, *, Ws_up=None, Ws_down=None):
+        self.desc = make_desc(x, W_r, W_up, k, Ws_up)
+        w = MoeWeights()
+        w.x, w.W_r, w.b, w.W_up, w.W_down = _p(x), _p(W_r), _p(b), _p(W_up), _p(W_down)
+        w.Ws_up, w.Ws_down = _p(Ws_up), _p(Ws_down)
+        self.w = w
+        self._keep = [x, W_r, b, W_up, W_down, Ws_up, Ws_down]
+        f32 = dict(dtype=torch.float32, device=x.device)
+        self.grads = {"dx": torch.empty(x.shape, **f32), "dW_r": torch.empty(W_r.shape, **f32),
+                      "dW_up": torch.empty(W_up.shape, **f32),
+                      "dW_down": torch.empty(W_down.shape, **f32)}
+        if Ws_up is not None:
+            self.grads["dWs_up"] = torch.empty(Ws_up.shape, **f32)
+            self.grads["dWs_down"] = torch.empty(Ws_down.shape, **f32)
+        g = MoeGrads()
+        for name, _ in MoeGrads._fields_:
+            setattr(g, name, _p(self.grads.get(name)))
+        self.g = g
+        n = C.c_size_t(0)
+        _check(lib().moe_backward_workspace_size(C.byref(self.desc), C.byref(n)),
+               "moe_backward_workspace_size")
+        self.ws_bytes = n.value
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=x.device)
+
+    def __call__(self, dy, stream=None):
+        rc = lib().moe_layer_backward(C.byref(self.desc), C.byref(self.w), _p(dy),
+                                      C.byref(self.g), _p(self.ws), self.ws_bytes,
+                                      _stream(stream))
+        _check(rc, "moe_layer_backward")
+        return self.grads
+
+
+def backward_from(dev: dict, k: int) -> Backward:
+    """A Backward over a ``to_device`` dict."""
+    return Backward(dev["x"], dev["W_r"], dev["b"], dev["W_up"], dev["W_down"], k,
+                    Ws_up=dev.get("Ws_up"), Ws_down=dev.get("Ws_down"))
 
 
 def layer_forward(x, W_r, b, W_up, W_down, k, **kw):

@@ -1,0 +1,277 @@
+// Non-GEMM kernels of the MoE layer's backward pass (bf16 layers): operand transposes for the
+// data- and weight-gradient products, the gradient through the routing gates, the router weight
+// gradient and the sum that forms dx.
+//
+// The gradient is that of the forward of the Nemotron 3 MoE layer ("NVIDIA Nemotron 3: Efficient
+// and Open Intelligence", section 2.2; "Nemotron 3 Nano: Open, Efficient Mixture-of-Experts
+// Hybrid Mamba-Transformer Model for Agentic Reasoning", section "技术框架") with the top-k
+// selection held fixed: it is piecewise constant, so the gradient reaches the router only
+// through the gate weights g_j = s_j / sum_m s_m, s = sigmoid(logits). The per-expert bias of
+// aux-loss-free balancing ("Nemotron 3 Nano：開放高效的 MoE 混合 Mamba-Transformer 智能體推理模型",
+// section 2.2) only steers the selection and has no gradient.
+#include <cmath>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kTile = 64;  // transpose tile: 64 columns x 64 features of bf16
+
+// Column (pair row r or token) -> source row of the transpose, or -1 for a padding column.
+__device__ __forceinline__ int source_row(const TransposeParams& p, int c) {
+  if (!p.koffs) return c < p.R ? c : -1;
+  int lo = 0, hi = p.G - 1;  // group g holds columns [koffs[g], koffs[g+1])
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.koffs[mid] <= c) lo = mid; else hi = mid - 1;
+  }
+  const int r = p.offs[lo] + (c - p.koffs[lo]);
+  return r < p.offs[lo + 1] ? r : -1;
+}
+
+// dst[d][c] = src[row(c)][d]: 64 x 64 tiles through LDS, 16-byte loads and stores.
+__global__ __launch_bounds__(256) void transpose_kernel(TransposeParams p) {
+  __shared__ uint16_t tile[kTile][kTile + 8];  // [feature][column]; rows of 144 bytes
+  const int ncols = p.koffs ? p.koffs[p.G] : p.ncols;
+  const int c0 = blockIdx.x * kTile, d0 = blockIdx.y * kTile;
+  if (c0 >= ncols) return;
+  const uint16_t* src = p.src + (int64_t)blockIdx.z * p.src_bstride;
+  uint16_t* dst = p.dst + (int64_t)blockIdx.z * p.dst_bstride;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int q = tid + it * 256;
+    const int cl = q >> 3, ch = q & 7;
+    const int c = c0 + cl, d = d0 + ch * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (c < ncols && d < p.Cc) {
+      const int r = source_row(p, c);
+      if (r >= 0) {
+        const int64_t sr = p.gather ? p.gather[r] : r;
+        v = *(const uint4*)(src + sr * p.lds + d);
+      }
+    }
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[ch * 8 + 2 * e][cl] = (uint16_t)(w[e] & 0xFFFF);
+      tile[ch * 8 + 2 * e + 1][cl] = (uint16_t)(w[e] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int q = tid + it * 256;
+    const int dl = q >> 3, ch = q & 7;
+    const int d = d0 + dl, c = c0 + ch * 8;
+    if (d >= p.Cc || c >= ncols) continue;
+    const uint16_t* t = &tile[dl][ch * 8];
+    uint16_t* o = dst + (int64_t)d * p.ldd + c;
+    if (c + 8 <= ncols) {
+      *(uint4*)o = make_uint4(t[0] | ((uint32_t)t[1] << 16), t[2] | ((uint32_t)t[3] << 16),
+                              t[4] | ((uint32_t)t[5] << 16), t[6] | ((uint32_t)t[7] << 16));
+    } else {
+      for (int e = 0; c + e < ncols; ++e) o[e] = t[e];
+    }
+  }
+}
+
+// Padded K offsets of the weight-gradient products: koffs[g + 1] = koffs[g] + roundup(counts[g],
+// 64), so every expert's window of the transposed operands starts on a 128-byte boundary.
+__global__ void pad_offsets_kernel(const int32_t* counts, int G, int32_t* koffs) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int acc = 0;
+  koffs[0] = 0;
+  for (int g = 0; g < G; ++g) {
+    acc += (counts[g] + kTile - 1) / kTile * kTile;
+    koffs[g + 1] = acc;
+  }
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) s += red[w];  // fixed order
+  return s;
+}
+
+// One workgroup per token t. With Y_j the forward's expert output row of pair (t, j):
+//   dg_j = <dy_t, Y_j>,  s_j = sigmoid(logit of e_j),  Z = sum_j s_j,
+//   dz_j = (dg_j - sum_m g_m dg_m) / Z * s_j (1 - s_j),
+//   dYp[pos(t, j)] = bf16(g_j dy_t),  dzp[pos(t, j)] = dz_j.
+__global__ __launch_bounds__(256) void bwd_route_kernel(const uint16_t* dy, const uint16_t* Yp,
+                                                        const float* logits, const int32_t* idx,
+                                                        const float* gates, const int32_t* pos,
+                                                        int H, int E, int k, uint16_t* dYp,
+                                                        float* dzp) {
+  __shared__ float red[4];
+  __shared__ float dg[kMaxK];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const uint16_t* dyt = dy + (int64_t)t * H;
+  const int nch = H / 8;
+  for (int j = 0; j < k; ++j) {
+    const int r = pos[(int64_t)t * k + j];
+    float part = 0.f;
+    if (r >= 0) {
+      const uint16_t* y = Yp + (int64_t)r * H;
+      for (int c = tid; c < nch; c += 256) {
+        const uint4 a = *(const uint4*)(dyt + c * 8), b = *(const uint4*)(y + c * 8);
+        const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          part += bf16_bits_to_f32(wa[e] & 0xFFFF) * bf16_bits_to_f32(wb[e] & 0xFFFF);
+          part += bf16_bits_to_f32(wa[e] >> 16) * bf16_bits_to_f32(wb[e] >> 16);
+        }
+      }
+    }
+    const float s = block_sum(part, red);
+    if (tid == 0) dg[j] = s;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float Z = 0.f, gdg = 0.f;
+    float sj[kMaxK];
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(int64_t)t * k + j];
+      sj[j] = (float)(1.0 / (1.0 + exp(-(double)logits[(int64_t)t * E + e])));
+      Z += sj[j];
+      gdg += gates[(int64_t)t * k + j] * dg[j];
+    }
+    for (int j = 0; j < k; ++j) {
+      const int r = pos[(int64_t)t * k + j];
+      if (r >= 0) dzp[r] = (dg[j] - gdg) / Z * sj[j] * (1.f - sj[j]);
+    }
+  }
+  for (int j = 0; j < k; ++j) {
+    const int r = pos[(int64_t)t * k + j];
+    if (r < 0) continue;
+    const float g = gates[(int64_t)t * k + j];
+    uint16_t* o = dYp + (int64_t)r * H;
+    for (int c = tid; c < nch; c += 256) {
+      const uint4 a = *(const uint4*)(dyt + c * 8);
+      const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = pack_bf16x2(g * bf16_bits_to_f32(wa[e] & 0xFFFF), g * bf16_bits_to_f32(wa[e] >> 16));
+      *(uint4*)(o + c * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+// dW_r[e][h] = sum over expert e's pair rows p (ascending) of dzp[p] * x[perm[p]][h]. Workgroup:
+// 256 columns of one expert; wave w adds rows w, w + 4, ...; the four partial sums are added in
+// wave order.
+__global__ __launch_bounds__(256) void bwd_router_weight_kernel(const float* dzp,
+                                                                const uint16_t* x,
+                                                                const int32_t* perm,
+                                                                const int32_t* offs, int H,
+                                                                float* dWr) {
+  __shared__ float4 part[4][64];
+  const int e = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 256 + lane * 4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (c < H) {
+    for (int p = offs[e] + wave; p < offs[e + 1]; p += 4) {
+      const float z = dzp[p];
+      const uint2 v = *(const uint2*)(x + (int64_t)perm[p] * H + c);
+      acc.x += z * bf16_bits_to_f32(v.x & 0xFFFF);
+      acc.y += z * bf16_bits_to_f32(v.x >> 16);
+      acc.z += z * bf16_bits_to_f32(v.y & 0xFFFF);
+      acc.w += z * bf16_bits_to_f32(v.y >> 16);
+    }
+  }
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0 && c < H) {
+    float4 s = part[0][lane];
+    for (int w = 1; w < 4; ++w) {
+      const float4 q = part[w][lane];
+      s.x += q.x; s.y += q.y; s.z += q.z; s.w += q.w;
+    }
+    *(float4*)(dWr + (int64_t)e * H + c) = s;
+  }
+}
+
+// dx[t] = dxs[t] (shared expert; optional) + sum_j du[pos(t, j)] + sum_j dzp[pos(t, j)] W_r[e_j],
+// added in that fixed order, fp32.
+__global__ __launch_bounds__(256) void bwd_dx_kernel(const float* dxs, const float* du,
+                                                     const float* dzp, const uint16_t* Wr,
+                                                     const int32_t* idx, const int32_t* pos,
+                                                     int H, int k, float* dx) {
+  const int t = blockIdx.x;
+  for (int c = threadIdx.x * 4; c < H; c += 1024) {
+    float4 a = dxs ? *(const float4*)(dxs + (int64_t)t * H + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      const int r = pos[(int64_t)t * k + j];
+      if (r < 0) continue;
+      const float4 u = *(const float4*)(du + (int64_t)r * H + c);
+      a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
+    }
+    for (int j = 0; j < k; ++j) {
+      const int r = pos[(int64_t)t * k + j];
+      if (r < 0) continue;
+      const float z = dzp[r];
+      const uint2 w = *(const uint2*)(Wr + (int64_t)idx[(int64_t)t * k + j] * H + c);
+      a.x += z * bf16_bits_to_f32(w.x & 0xFFFF);
+      a.y += z * bf16_bits_to_f32(w.x >> 16);
+      a.z += z * bf16_bits_to_f32(w.y & 0xFFFF);
+      a.w += z * bf16_bits_to_f32(w.y >> 16);
+    }
+    *(float4*)(dx + (int64_t)t * H + c) = a;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_transpose(const TransposeParams& p, int max_cols, int batch, hipStream_t s) {
+  if (max_cols <= 0 || p.Cc <= 0 || batch <= 0) return hipSuccess;
+  if (p.Cc % 8 || p.lds % 8 || p.ldd % 8 || (p.koffs && (!p.offs || p.G < 1)))
+    return hipErrorInvalidValue;
+  dim3 grid(cdiv(max_cols, kTile), cdiv(p.Cc, kTile), batch);
+  hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_pad_offsets(const int32_t* counts, int G, int32_t* koffs, hipStream_t s) {
+  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(64), 0, s, counts, G, koffs);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_route(const uint16_t* dy, const uint16_t* Yp, const float* logits,
+                            const int32_t* idx, const float* gates, const int32_t* pos, int T,
+                            int H, int E, int k, uint16_t* dYp, float* dzp, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (H % 8 || k > kMaxK) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_route_kernel, dim3(T), dim3(256), 0, s, dy, Yp, logits, idx, gates,
+                     pos, H, E, k, dYp, dzp);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_router_weight(const float* dzp, const uint16_t* x, const int32_t* perm,
+                                    const int32_t* offs, int E, int H, float* dWr,
+                                    hipStream_t s) {
+  if (H % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_router_weight_kernel, dim3(cdiv(H, 256), E), dim3(256), 0, s, dzp, x,
+                     perm, offs, H, dWr);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dx(const float* dxs, const float* du, const float* dzp, const uint16_t* Wr,
+                         const int32_t* idx, const int32_t* pos, int T, int H, int k, float* dx,
+                         hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (H % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_dx_kernel, dim3(T), dim3(256), 0, s, dxs, du, dzp, Wr, idx, pos, H, k,
+                     dx);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -51,6 +51,17 @@ __device__ __forceinline__ bool tile_of(const GemmParams& p, int& g, int& row0, 
                                         int& n0) {
   const int nN = cdiv(p.N, BN);
   const int L = xcd_logical_block(blockIdx.x, gridDim.x);
+  if (p.koffs) {                       // one M x N product per group, M-tiles fastest
+    const int nM = cdiv(p.M, BM);
+    const int per = nM * nN;
+    if (L >= p.G * per) return false;
+    g = L / per;
+    const int local = L - g * per;
+    n0 = (local / nM) * BN;
+    row0 = (local % nM) * BM;
+    rows = min(BM, p.M - row0);
+    return rows > 0;
+  }
   if (p.mt_start) {
     const int total = p.mt_start[p.G] * nN;
     if (L >= total) return false;
@@ -126,6 +137,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
 
   int g, row0, rows, n0;
   if (!tile_of<BM, BN>(p, g, row0, rows, n0)) return;
+  if (p.koffs) {  // this group's K window of both operands, and its output matrix
+    const int k0 = p.koffs[g];
+    p.K = p.koffs[g + 1] - k0;
+    kshift = (int64_t)k0 * EltBytes<AB>::v;
+    p.A = (const uint8_t*)p.A + kshift;
+    p.B = (const uint8_t*)p.B + kshift;
+    p.C = (uint8_t*)p.C + g * p.c_gstride * EltBytes<OUT>::v;
+    g = 0;  // the operands are shared: no per-group B panel
+  }
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -372,15 +392,42 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
 #pragma unroll
             for (int q = 0; q < 8; ++q) v[q] = sqrelu(v[q]);
           }
-          if constexpr (OUT == Elt::BF16) {
+          if constexpr (EPI == Epi::SqReluSave) {  // relu(a) kept for the backward pass
             uint32_t w[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
-            *(uint4*)((uint16_t*)p.C + (int64_t)row * p.ldc + col) = make_uint4(w[0], w[1], w[2], w[3]);
+            for (int q = 0; q < 4; ++q)
+              w[q] = pack_bf16x2(fmaxf(v[2 * q], 0.f), fmaxf(v[2 * q + 1], 0.f));
+            *(uint4*)((uint16_t*)p.C2 + (int64_t)row * p.ldc + col) = make_uint4(w[0], w[1], w[2], w[3]);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = sqrelu(v[q]);
+          }
+          if constexpr (EPI == Epi::DSqRelu) {  // d/da relu(a)^2 = 2 relu(a), relu(a) saved in C2
+            float r[8];
+            unpack8(*(const uint4*)((const uint16_t*)p.C2 + (int64_t)row * p.ldc + col), r);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] *= 2.f * r[q];
+          }
+          // 16-byte stores when the 8 columns lie inside N on an aligned row; else (N or ldc
+          // not a multiple of 8, e.g. router logits of E experts) element by element
+          const bool whole = col + 8 <= p.N && p.ldc % 8 == 0;
+          if constexpr (OUT == Elt::BF16) {
+            uint16_t* o = (uint16_t*)p.C + (int64_t)row * p.ldc + col;
+            if (whole) {
+              uint32_t w[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+              *(uint4*)o = make_uint4(w[0], w[1], w[2], w[3]);
+            } else {
+              for (int q = 0; q < 8 && col + q < p.N; ++q) o[q] = (uint16_t)f32_to_bf16_bits(v[q]);
+            }
           } else {
             float* o = (float*)p.C + (int64_t)row * p.ldc + col;
-            *(float4*)o = make_float4(v[0], v[1], v[2], v[3]);
-            *(float4*)(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+            if (whole) {
+              *(float4*)o = make_float4(v[0], v[1], v[2], v[3]);
+              *(float4*)(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+            } else {
+              for (int q = 0; q < 8 && col + q < p.N; ++q) o[q] = v[q];
+            }
           }
         }
       }
@@ -505,17 +552,36 @@ hipError_t launch_gemm(const GemmKind& k, const GemmParams& p, int max_mtiles, h
   }
   constexpr int GB = kGroupBM;
   if (k.ab == Elt::BF16) {
+    if (p.koffs) {  // weight gradients: one product per group over its K window
+      if (k.out != Elt::F32 || k.epi != Epi::Store || p.ksplit > 1) return hipErrorInvalidValue;
+      return run_mfma<GB, 192, 2, 2, 2, Elt::BF16, Elt::F32, Epi::Store>(
+          p, p.G * cdiv(p.M, GB), s);
+    }
+    if ((k.epi == Epi::SqReluSave || k.epi == Epi::DSqRelu) &&
+        (!p.C2 || k.out != Elt::BF16 || p.N % 8 || p.ldc % 8))
+      return hipErrorInvalidValue;
     if (grouped) {
       // 128 x 192 tiles on 4 waves, two workgroups per CU: the fastest routed shape measured
       if (k.out == Elt::BF16 && k.epi == Epi::SqRelu)
         return run_mfma<GB, 192, 2, 2, 2, Elt::BF16, Elt::BF16, Epi::SqRelu>(p, max_mtiles, s);
       if (k.out == Elt::BF16 && k.epi == Epi::Store)
         return run_mfma<GB, 192, 2, 2, 2, Elt::BF16, Elt::BF16, Epi::Store>(p, max_mtiles, s);
+      if (k.out == Elt::BF16 && k.epi == Epi::SqReluSave)
+        return run_mfma<GB, 192, 2, 2, 2, Elt::BF16, Elt::BF16, Epi::SqReluSave>(p, max_mtiles, s);
+      if (k.out == Elt::BF16 && k.epi == Epi::DSqRelu)
+        return run_mfma<GB, 192, 2, 2, 2, Elt::BF16, Elt::BF16, Epi::DSqRelu>(p, max_mtiles, s);
+      if (k.out == Elt::F32 && k.epi == Epi::Store)
+        return run_mfma<GB, 192, 2, 2, 2, Elt::BF16, Elt::F32, Epi::Store>(p, max_mtiles, s);
       return hipErrorInvalidValue;
     }
     if (k.out == Elt::F32 && k.epi == Epi::Store) return run_dense_bf16<Elt::F32, Epi::Store>(p, s);
     if (k.out == Elt::BF16 && k.epi == Epi::Store) return run_dense_bf16<Elt::BF16, Epi::Store>(p, s);
     if (k.out == Elt::BF16 && k.epi == Epi::SqRelu) return run_dense_bf16<Elt::BF16, Epi::SqRelu>(p, s);
+    if (p.ksplit > 1) return hipErrorInvalidValue;
+    if (k.out == Elt::BF16 && k.epi == Epi::SqReluSave)
+      return run_dense_bf16<Elt::BF16, Epi::SqReluSave>(p, s);
+    if (k.out == Elt::BF16 && k.epi == Epi::DSqRelu)
+      return run_dense_bf16<Elt::BF16, Epi::DSqRelu>(p, s);
     return hipErrorInvalidValue;
   }
   if (k.ab == Elt::FP8 && grouped && k.out == Elt::BF16) {

@@ -16,7 +16,9 @@ enum class Elt : int { F32 = 0, BF16 = 1, FP8 = 2, MXFP4 = 3, MXFP8 = 4 };
 
 enum class Epi : int {
   Store = 0,        // C = acc
-  SqRelu = 1        // C = relu(acc)^2
+  SqRelu = 1,       // C = relu(acc)^2
+  SqReluSave = 2,   // C = relu(acc)^2 and C2 = relu(acc) (the factor the backward pass needs)
+  DSqRelu = 3       // C = acc * 2 * C2: the squared ReLU's derivative at the saved relu(a)
 };
 
 struct GemmParams {
@@ -39,9 +41,10 @@ struct GemmParams {
   const void* B2 = nullptr;
   int64_t ldb2 = 0;
   int K2 = 0;
-  // Output
+  // Output; C2 is the second matrix of the SqReluSave / DSqRelu epilogues (same shape, ldc)
   void* C = nullptr;
   int64_t ldc = 0;
+  void* C2 = nullptr;
   int M = 0, N = 0, K = 0;
   // Split-K (dense launches only): slice y of ksplit covers K columns [y*kchunk, (y+1)*kchunk)
   // and writes its partial product to C + y * M * ldc (Store epilogue).
@@ -51,6 +54,11 @@ struct GemmParams {
   const int32_t* offs = nullptr;      // [G + 1] row offsets
   const int32_t* mt_start = nullptr;  // [G + 1] prefix of ceil(rows_g / BM)
   int G = 0;
+  // K-grouped launches (weight gradients): group g reduces over K columns
+  // [koffs[g], koffs[g + 1]) of both operands (multiples of 64) and writes its M x N product to
+  // C + g * c_gstride. M, N and the operands are shared by the groups; K is unused.
+  const int32_t* koffs = nullptr;
+  int64_t c_gstride = 0;
 };
 
 struct GemmKind {

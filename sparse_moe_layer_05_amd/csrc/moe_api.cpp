@@ -521,6 +521,311 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
   return hip_status(hipGetLastError());
 }
 
+// ---------------------------------------------------------------- backward pass (bf16)
+
+struct BwdPlan {
+  int T = 0, H = 0, E = 0, k = 0, I = 0, Is = 0, P = 0, Ppad = 0, Tpad = 0;
+  int nsplit = 1, kchunk = 0;
+  size_t logits = 0, zpart = 0, idx = 0, gates = 0, counts = 0, offsets = 0, perm = 0, pos = 0;
+  size_t dscratch = 0, mt_start = 0, koffs = 0;
+  size_t r = 0, h = 0, Yp = 0, hs = 0, rs = 0;                 // recomputed forward
+  size_t dYp = 0, dzp = 0, da = 0, du = 0, das = 0, dxs = 0;   // backward intermediates
+  size_t WuT = 0, WdT = 0, WsuT = 0, WsdT = 0;                 // transposed weights
+  size_t dYpT = 0, hT = 0, daT = 0, XpT = 0;                   // [feature][padded pair column]
+  size_t dyT = 0, hsT = 0, dasT = 0, xT = 0;                   // [feature][padded token]
+  size_t total = 0;
+};
+
+int32_t make_bwd_plan(const moe_desc_t* d, BwdPlan* out) {
+  if (d->latent) return MOE_ERR_UNSUPPORTED;  // the LatentMoE backward is not provided
+  Plan fp;
+  moe_desc_t dd = *d;
+  dd.flags = MOE_PATH_GROUPED;
+  int32_t rc = make_plan(&dd, false, &fp);
+  if (rc) return rc;
+  if (d->flags & ~(MOE_PATH_MASK | MOE_ROUTING_GIVEN)) return MOE_ERR_INVALID_ARG;
+  if (d->flags & MOE_ROUTING_GIVEN) return MOE_ERR_UNSUPPORTED;
+  if (d->act_dtype != MOE_BF16 || d->expert_dtype != MOE_BF16 || d->latent) return MOE_ERR_UNSUPPORTED;
+  BwdPlan p;
+  p.T = fp.T; p.H = fp.H; p.E = fp.E; p.k = fp.k; p.I = fp.I; p.Is = fp.Is; p.P = fp.P;
+  p.nsplit = fp.nsplit; p.kchunk = fp.kchunk;
+  // each expert's pair columns start on a multiple of 64 (at most 63 padding columns each);
+  // the row pitch stays a multiple of 64 elements
+  p.Ppad = (p.P + 63) / 64 * 64 + 64 * p.E;
+  p.Tpad = (p.T + 63) / 64 * 64;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += (bytes + kAlign - 1) / kAlign * kAlign;
+    return at;
+  };
+  const size_t T = p.T, H = p.H, E = p.E, I = p.I, Is = p.Is, P = p.P, Pp = p.Ppad, Tp = p.Tpad;
+  p.logits = take(T * E * 4);
+  if (p.nsplit > 1) p.zpart = take((size_t)p.nsplit * T * E * 4);
+  p.idx = take(P * 4);
+  p.gates = take(P * 4);
+  p.counts = take(E * 4);
+  p.offsets = take((E + 1) * 4);
+  p.perm = take(P * 4);
+  p.pos = take(P * 4);
+  p.dscratch = take(dispatch_scratch_ints(p.T, p.E) * 4);
+  p.mt_start = take((E + 1) * 4);
+  p.koffs = take((E + 1) * 4);
+  p.r = take(P * I * 2);
+  p.h = take(P * I * 2);
+  p.Yp = take(P * H * 2);
+  p.dYp = take(P * H * 2);
+  p.dzp = take(P * 4);
+  p.da = take(P * I * 2);
+  p.du = take(P * H * 4);
+  p.WuT = take(E * H * I * 2);
+  p.WdT = take(E * I * H * 2);
+  p.dYpT = take(H * Pp * 2);
+  p.hT = take(I * Pp * 2);
+  p.daT = take(I * Pp * 2);
+  p.XpT = take(H * Pp * 2);
+  if (Is) {
+    p.hs = take(T * Is * 2);
+    p.rs = take(T * Is * 2);
+    p.das = take(T * Is * 2);
+    p.dxs = take(T * H * 4);
+    p.WsuT = take(H * Is * 2);
+    p.WsdT = take(Is * H * 2);
+    p.dyT = take(H * Tp * 2);
+    p.hsT = take(Is * Tp * 2);
+    p.dasT = take(Is * Tp * 2);
+    p.xT = take(H * Tp * 2);
+  }
+  p.total = off;
+  *out = p;
+  return MOE_OK;
+}
+
+// W[b] [rows][cols] -> WT[b] [cols][rows] for `batch` matrices (bf16).
+hipError_t transpose_weights(const void* W, int rows, int cols, int batch, void* WT,
+                             hipStream_t s) {
+  TransposeParams t;
+  t.src = (const uint16_t*)W; t.lds = cols; t.R = rows; t.Cc = cols;
+  t.dst = (uint16_t*)WT; t.ldd = rows; t.ncols = rows;
+  t.src_bstride = (int64_t)rows * cols; t.dst_bstride = (int64_t)rows * cols;
+  return launch_transpose(t, rows, batch, s);
+}
+
+int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, moe_grads_t* gr,
+                 void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!d) return MOE_ERR_INVALID_ARG;
+  BwdPlan pl;
+  int32_t rc = make_bwd_plan(d, &pl);
+  if (rc) return rc;
+  if (pl.T == 0) return MOE_OK;
+  if (!w || !dy || !gr || !w->x || !w->W_r || !w->b || !w->W_up || !w->W_down || !gr->dx ||
+      !gr->dW_r || !gr->dW_up || !gr->dW_down)
+    return MOE_ERR_INVALID_ARG;
+  if (pl.Is && (!w->Ws_up || !w->Ws_down || !gr->dWs_up || !gr->dWs_down))
+    return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {w->x, w->W_r, w->W_up, w->W_down, w->Ws_up, w->Ws_down, dy, gr->dx,
+                        gr->dW_r, gr->dW_up, gr->dW_down, gr->dWs_up, gr->dWs_down};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < pl.total || !aligned16(ws)) return MOE_ERR_WORKSPACE;
+
+  uint8_t* base = (uint8_t*)ws;
+  auto at = [&](size_t off) { return (void*)(base + off); };
+  const int T = pl.T, H = pl.H, E = pl.E, k = pl.k, I = pl.I, Is = pl.Is, P = pl.P;
+  float* logits = (float*)at(pl.logits);
+  int32_t* idx = (int32_t*)at(pl.idx);
+  float* gates = (float*)at(pl.gates);
+  int32_t* counts = (int32_t*)at(pl.counts);
+  int32_t* offsets = (int32_t*)at(pl.offsets);
+  int32_t* perm = (int32_t*)at(pl.perm);
+  int32_t* pos = (int32_t*)at(pl.pos);
+  int32_t* mt_start = (int32_t*)at(pl.mt_start);
+  int32_t* koffs = (int32_t*)at(pl.koffs);
+  const int max_mt = max_group_mtiles(P, E, kGroupBM);
+
+  // (1) forward recompute: routing and dispatch as in the forward call
+  {
+    float* zsrc = pl.nsplit > 1 ? (float*)at(pl.zpart) : logits;
+    {
+      MOE_SPAN("gemm_bf16_f32out:router");
+      GemmParams g;
+      g.A = w->x; g.lda = H; g.a_rows = T; g.B = w->W_r; g.ldb = H; g.C = zsrc; g.ldc = E;
+      g.M = T; g.N = E; g.K = H; g.ksplit = pl.nsplit; g.kchunk = pl.kchunk;
+      MOE_TRY(launch_gemm(GemmKind{Elt::BF16, Elt::F32, Epi::Store}, g, 0, s));
+    }
+    {
+      MOE_SPAN("topk:router");
+      MOE_TRY(launch_topk(zsrc, pl.nsplit, w->b, T, E, k, idx, gates,
+                          pl.nsplit > 1 ? logits : nullptr, s));
+    }
+    MOE_SPAN("dispatch:all");
+    MOE_TRY(launch_dispatch(idx, T, E, k, counts, offsets, perm, pos, (int32_t*)at(pl.dscratch),
+                            kGroupBM, mt_start, DispatchExtras(), s));
+    MOE_TRY(launch_pad_offsets(counts, E, koffs, s));
+  }
+  // expert activations: relu(a) and h = relu(a)^2 per pair row, then the expert outputs Y
+  void* r = at(pl.r);
+  void* h = at(pl.h);
+  void* Yp = at(pl.Yp);
+  {
+    GemmParams up;
+    up.A = w->x; up.lda = H; up.a_rows = T; up.a_gather = perm;
+    up.B = w->W_up; up.ldb = H; up.b_gstride = (int64_t)I * H;
+    up.C = h; up.C2 = r; up.ldc = I; up.N = I; up.K = H;
+    up.offs = offsets; up.mt_start = mt_start; up.G = E;
+    MOE_SPAN("gemm_bf16_sqrelu:bwd_routed_up");
+    MOE_TRY(launch_gemm(GemmKind{Elt::BF16, Elt::BF16, Epi::SqReluSave}, up, max_mt, s));
+  }
+  {
+    GemmParams dn;
+    dn.A = h; dn.lda = I; dn.a_rows = P;
+    dn.B = w->W_down; dn.ldb = I; dn.b_gstride = (int64_t)H * I;
+    dn.C = Yp; dn.ldc = H; dn.N = H; dn.K = I;
+    dn.offs = offsets; dn.mt_start = mt_start; dn.G = E;
+    MOE_SPAN("gemm_bf16_store:bwd_routed_down");
+    MOE_TRY(launch_gemm(GemmKind{Elt::BF16, Elt::BF16, Epi::Store}, dn, max_mt, s));
+  }
+  void* hs = Is ? at(pl.hs) : nullptr;
+  void* rs = Is ? at(pl.rs) : nullptr;
+  if (Is) {
+    GemmParams g;
+    g.A = w->x; g.lda = H; g.a_rows = T; g.B = w->Ws_up; g.ldb = H; g.C = hs; g.C2 = rs;
+    g.ldc = Is; g.M = T; g.N = Is; g.K = H;
+    MOE_SPAN("gemm_bf16_sqrelu:bwd_shared_up");
+    MOE_TRY(launch_gemm(GemmKind{Elt::BF16, Elt::BF16, Epi::SqReluSave}, g, 0, s));
+  }
+
+  // (2) transposed weights for the data-gradient products (C = A . B^T needs K-contiguous B)
+  void* WuT = at(pl.WuT);
+  void* WdT = at(pl.WdT);
+  {
+    MOE_SPAN("transpose:weights");
+    MOE_TRY(transpose_weights(w->W_up, I, H, E, WuT, s));    // [E][I][H] -> [E][H][I]
+    MOE_TRY(transpose_weights(w->W_down, H, I, E, WdT, s));  // [E][H][I] -> [E][I][H]
+    if (Is) {
+      MOE_TRY(transpose_weights(w->Ws_up, Is, H, 1, at(pl.WsuT), s));    // -> [H][I_s]
+      MOE_TRY(transpose_weights(w->Ws_down, H, Is, 1, at(pl.WsdT), s));  // -> [I_s][H]
+    }
+  }
+
+  // (3) gradient through the gates: dY rows (g_j dy_t) and the logit gradient per pair
+  uint16_t* dYp = (uint16_t*)at(pl.dYp);
+  float* dzp = (float*)at(pl.dzp);
+  {
+    MOE_SPAN("bwd_route:gates");
+    MOE_TRY(launch_bwd_route((const uint16_t*)dy, (const uint16_t*)Yp, logits, idx, gates, pos,
+                             T, H, E, k, dYp, dzp, s));
+  }
+  // (4) data gradients: da = (dY W_down[e]) * 2 relu(a), du = da W_up[e]
+  void* da = at(pl.da);
+  float* du = (float*)at(pl.du);
+  {
+    GemmParams g;
+    g.A = dYp; g.lda = H; g.a_rows = P;
+    g.B = WdT; g.ldb = H; g.b_gstride = (int64_t)I * H;
+    g.C = da; g.C2 = r; g.ldc = I; g.N = I; g.K = H;
+    g.offs = offsets; g.mt_start = mt_start; g.G = E;
+    MOE_SPAN("gemm_bf16_dsqrelu:bwd_routed_dgrad_down");
+    MOE_TRY(launch_gemm(GemmKind{Elt::BF16, Elt::BF16, Epi::DSqRelu}, g, max_mt, s));
+  }
+  {
+    GemmParams g;
+    g.A = da; g.lda = I; g.a_rows = P;
+    g.B = WuT; g.ldb = I; g.b_gstride = (int64_t)H * I;
+    g.C = du; g.ldc = H; g.N = H; g.K = I;
+    g.offs = offsets; g.mt_start = mt_start; g.G = E;
+    MOE_SPAN("gemm_bf16_f32out:bwd_routed_dgrad_up");
+    MOE_TRY(launch_gemm(GemmKind{Elt::BF16, Elt::F32, Epi::Store}, g, max_mt, s));
+  }
+  float* dxs = Is ? (float*)at(pl.dxs) : nullptr;
+  void* das = Is ? at(pl.das) : nullptr;
+  if (Is) {
+    {
+      MOE_SPAN("gemm_bf16_dsqrelu:bwd_shared_dgrad_down");
+      GemmParams g;
+      g.A = dy; g.lda = H; g.a_rows = T; g.B = at(pl.WsdT); g.ldb = H; g.C = das; g.C2 = rs;
+      g.ldc = Is; g.M = T; g.N = Is; g.K = H;
+      MOE_TRY(launch_gemm(GemmKind{Elt::BF16, Elt::BF16, Epi::DSqRelu}, g, 0, s));
+    }
+    MOE_SPAN("gemm_bf16_f32out:bwd_shared_dgrad_up");
+    MOE_TRY(dense(Elt::BF16, Elt::F32, Epi::Store, das, Is, at(pl.WsuT), Is, dxs, H, T, H, Is, s));
+  }
+  {
+    MOE_SPAN("bwd_dx:dx");
+    MOE_TRY(launch_bwd_dx(dxs, du, dzp, (const uint16_t*)w->W_r, idx, pos, T, H, k, gr->dx, s));
+  }
+  {
+    MOE_SPAN("bwd_router_weight:dW_r");
+    MOE_TRY(launch_bwd_router_weight(dzp, (const uint16_t*)w->x, perm, offsets, E, H, gr->dW_r,
+                                     s));
+  }
+
+  // (5) routed weight gradients over each expert's own pair rows: operands transposed so that
+  // the pair index is the contiguous K, each expert's window padded to a multiple of 64 columns
+  uint16_t* dYpT = (uint16_t*)at(pl.dYpT);
+  uint16_t* hT = (uint16_t*)at(pl.hT);
+  uint16_t* daT = (uint16_t*)at(pl.daT);
+  uint16_t* XpT = (uint16_t*)at(pl.XpT);
+  {
+    MOE_SPAN("transpose:routed_activations");
+    TransposeParams t;
+    t.offs = offsets; t.koffs = koffs; t.G = E; t.R = P;
+    t.src = dYp; t.lds = H; t.Cc = H; t.dst = dYpT; t.ldd = pl.Ppad;
+    MOE_TRY(launch_transpose(t, pl.Ppad, 1, s));
+    t.src = (const uint16_t*)h; t.lds = I; t.Cc = I; t.dst = hT;
+    MOE_TRY(launch_transpose(t, pl.Ppad, 1, s));
+    t.src = (const uint16_t*)da; t.dst = daT;
+    MOE_TRY(launch_transpose(t, pl.Ppad, 1, s));
+    t.src = (const uint16_t*)w->x; t.lds = H; t.Cc = H; t.gather = perm; t.dst = XpT;
+    MOE_TRY(launch_transpose(t, pl.Ppad, 1, s));
+  }
+  {
+    GemmParams g;  // dW_down[e] [H][I] = dY_e^T h_e
+    g.A = dYpT; g.lda = pl.Ppad; g.a_rows = H; g.B = hT; g.ldb = pl.Ppad;
+    g.C = gr->dW_down; g.ldc = I; g.M = H; g.N = I; g.G = E; g.koffs = koffs;
+    g.c_gstride = (int64_t)H * I;
+    MOE_SPAN("gemm_bf16_f32out:bwd_routed_wgrad_down");
+    MOE_TRY(launch_gemm(GemmKind{Elt::BF16, Elt::F32, Epi::Store}, g, 0, s));
+  }
+  {
+    GemmParams g;  // dW_up[e] [I][H] = da_e^T x_e
+    g.A = daT; g.lda = pl.Ppad; g.a_rows = I; g.B = XpT; g.ldb = pl.Ppad;
+    g.C = gr->dW_up; g.ldc = H; g.M = I; g.N = H; g.G = E; g.koffs = koffs;
+    g.c_gstride = (int64_t)I * H;
+    MOE_SPAN("gemm_bf16_f32out:bwd_routed_wgrad_up");
+    MOE_TRY(launch_gemm(GemmKind{Elt::BF16, Elt::F32, Epi::Store}, g, 0, s));
+  }
+  // (6) shared expert's weight gradients over all tokens (token columns padded with zeros)
+  if (Is) {
+    uint16_t* dyT = (uint16_t*)at(pl.dyT);
+    uint16_t* hsT = (uint16_t*)at(pl.hsT);
+    uint16_t* dasT = (uint16_t*)at(pl.dasT);
+    uint16_t* xT = (uint16_t*)at(pl.xT);
+    {
+      MOE_SPAN("transpose:shared_activations");
+      TransposeParams t;
+      t.R = T; t.ncols = pl.Tpad;
+      t.src = (const uint16_t*)dy; t.lds = H; t.Cc = H; t.dst = dyT; t.ldd = pl.Tpad;
+      MOE_TRY(launch_transpose(t, pl.Tpad, 1, s));
+      t.src = (const uint16_t*)hs; t.lds = Is; t.Cc = Is; t.dst = hsT;
+      MOE_TRY(launch_transpose(t, pl.Tpad, 1, s));
+      t.src = (const uint16_t*)das; t.dst = dasT;
+      MOE_TRY(launch_transpose(t, pl.Tpad, 1, s));
+      t.src = (const uint16_t*)w->x; t.lds = H; t.Cc = H; t.dst = xT;
+      MOE_TRY(launch_transpose(t, pl.Tpad, 1, s));
+    }
+    {
+      MOE_SPAN("gemm_bf16_f32out:bwd_shared_wgrad_down");
+      MOE_TRY(dense(Elt::BF16, Elt::F32, Epi::Store, dyT, pl.Tpad, hsT, pl.Tpad, gr->dWs_down, Is,
+                    H, Is, pl.Tpad, s));
+    }
+    MOE_SPAN("gemm_bf16_f32out:bwd_shared_wgrad_up");
+    MOE_TRY(dense(Elt::BF16, Elt::F32, Epi::Store, dasT, pl.Tpad, xT, pl.Tpad, gr->dWs_up, H, Is,
+                  H, pl.Tpad, s));
+  }
+  return hip_status(hipGetLastError());
+}
+
 }  // namespace
 
 extern "C" {
@@ -624,6 +929,20 @@ int32_t moe_trace_read(int32_t i, const char** name, float* ms) {
 }
 
 void moe_trace_reset(void) { g_trace.n = 0; }
+
+int32_t moe_backward_workspace_size(const moe_desc_t* desc, size_t* bytes) {
+  if (!desc || !bytes) return MOE_ERR_INVALID_ARG;
+  BwdPlan pl;
+  const int32_t rc = make_bwd_plan(desc, &pl);
+  if (rc) return rc;
+  *bytes = pl.total;
+  return MOE_OK;
+}
+
+int32_t moe_layer_backward(const moe_desc_t* desc, const moe_weights_t* w, const void* dy,
+                           moe_grads_t* grads, void* ws, size_t ws_bytes, void* stream) {
+  return backward(desc, w, dy, grads, ws, ws_bytes, (hipStream_t)stream);
+}
 
 const char* moe_status_str(int32_t code) {
   switch (code) {

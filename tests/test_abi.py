@@ -146,3 +146,58 @@ def test_status_strings():
     for code in (0, -1, -2, -3, -4):
         assert moe.status_str(code) and moe.status_str(code) != "unknown status"
     assert moe.status_str(7) == "unknown status"
+
+
+def bwd_ws(d):
+    n = C.c_size_t(0)
+    rc = moe.lib().moe_backward_workspace_size(C.byref(d), C.byref(n))
+    return rc, n.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), B.MOE_OK), (dict(I_shared=64), B.MOE_OK), (dict(T=0), B.MOE_OK),
+    (dict(act_dtype=0, expert_dtype=0), B.MOE_ERR_UNSUPPORTED),     # fp32 layer
+    (dict(expert_dtype=2), B.MOE_ERR_UNSUPPORTED),                  # e4m3 experts
+    (dict(expert_dtype=B.MOE_MXFP4), B.MOE_ERR_UNSUPPORTED),
+    (dict(latent=64), B.MOE_ERR_UNSUPPORTED),
+    (dict(flags=B.ROUTING_GIVEN), B.MOE_ERR_UNSUPPORTED),
+    (dict(flags=64), B.MOE_ERR_INVALID_ARG), (dict(k=0), B.MOE_ERR_INVALID_ARG),
+    (dict(H=250), B.MOE_ERR_INVALID_ARG),
+])
+def test_backward_descriptor_validation(kw, code):
+    assert bwd_ws(desc(**kw))[0] == code
+
+
+def test_backward_workspace_holds_the_transposed_weights():
+    rc, n = bwd_ws(desc(T=64, H=256, E=16, I=128))
+    assert rc == 0 and n > 2 * 16 * 256 * 128 * 2               # both transposed expert stacks
+    assert bwd_ws(desc(T=640))[1] > n
+    assert bwd_ws(desc(I_shared=64))[1] > n
+
+
+def test_backward_argument_errors_are_reported_before_launch():
+    L = moe.lib()
+    w = B.MoeWeights()
+    for n, _ in B.MoeWeights._fields_:
+        setattr(w, n, FAKE.value)
+    g = B.MoeGrads()
+    for n, _ in B.MoeGrads._fields_:
+        setattr(g, n, FAKE.value)
+
+    def call(d=None, w=w, dy=FAKE, g=g, ws=FAKE, ws_bytes=1 << 40):
+        d = d if d is not None else desc()
+        return L.moe_layer_backward(C.byref(d), C.byref(w), dy, C.byref(g) if g else None, ws,
+                                    ws_bytes, None)
+
+    assert call(dy=None) == B.MOE_ERR_INVALID_ARG
+    assert call(g=None) == B.MOE_ERR_INVALID_ARG
+    assert call(dy=C.c_void_p(0x10008)) == B.MOE_ERR_INVALID_ARG      # misaligned
+    assert call(ws=None) == B.MOE_ERR_WORKSPACE
+    assert call(ws_bytes=16) == B.MOE_ERR_WORKSPACE
+    assert call(desc(latent=64)) == B.MOE_ERR_UNSUPPORTED
+    g.dW_up = None
+    assert call() == B.MOE_ERR_INVALID_ARG
+    g.dW_up = FAKE.value
+    g.dWs_up = None
+    assert call(desc(I_shared=64)) == B.MOE_ERR_INVALID_ARG
+    assert call(desc(T=0)) == B.MOE_OK                                 # empty: no-op

@@ -1,0 +1,176 @@
+"""GPU parity of the backward pass (bf16 plain MoE layer) against the double-precision oracle.
+
+Every gradient the HIP path writes is compared with the oracle's on the same seeded inputs and
+the same selection (the GPU's own, checked first against the oracle's routing wherever the
+oracle's k-th / (k+1)-th key margin exceeds 1e-4), as a relative Frobenius error.
+
+Tolerance. The path stores five intermediate tensors in bf16 -- relu(a), h, the expert outputs Y,
+g * dy and da -- and accumulates in fp32. One bf16 rounding has a relative RMS error of about
+2^-9 / sqrt(3) = 1.1e-3. A gradient that passes through two or three of them in sequence (dW_up:
+g*dy and relu(a) into da) lands near sqrt(3) * 1.1e-3 = 2e-3; measured: dx up to 2.9e-3, dW_up
+3.1e-3, dW_down 2.5e-3, the shared expert's 2.4e-3. The router gradient is built from the
+differences dg_j - sum_m g_m dg_m, which cancel, so its relative error is that of dg (Y rounded)
+times the cancellation ratio: measured up to 8.2e-3 on an expert row fed by three tokens. The
+bounds are 1e-2 (about three times the measured expert, shared-expert and dx errors) and 2e-2
+for dW_r.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+from oracle import oracle as O
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+import torch  # noqa: E402
+
+import sparse_moe_layer_05_amd as moe  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+THREADS = max(1, min(16, os.cpu_count() or 1))
+TOL = {"dx": 1e-2, "dW_r": 2e-2, "dW_up": 1e-2, "dW_down": 1e-2, "dWs_up": 1e-2,
+       "dWs_down": 1e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def rel_frob(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    n = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / n) if n > 0 else float(np.linalg.norm(a))
+
+
+CASES = {
+    # ragged everything: T*k odd, H and I not multiples of the 64-wide K-step or the 192-wide
+    # tiles, 24 experts of uneven load
+    "bwd_ragged": mi.LayerConfig("bwd_ragged", T=301, H=272, E=24, k=5, I=144, I_shared=208),
+    "bwd_no_shared": mi.LayerConfig("bwd_no_shared", T=130, H=256, E=8, k=3, I=96),
+    "bwd_one_token": mi.LayerConfig("bwd_one_token", T=1, H=256, E=16, k=4, I=64, I_shared=64),
+    # few experts, many tokens each: per-expert K windows of several 64-column steps
+    "bwd_few_experts": mi.LayerConfig("bwd_few_experts", T=600, H=256, E=4, k=2, I=128,
+                                      I_shared=96),
+    # an expert count that is not a multiple of 8, and experts left without tokens
+    "bwd_e13_sparse": mi.LayerConfig("bwd_e13_sparse", T=3, H=256, E=13, k=2, I=64),
+}
+
+
+def gpu_selection(dev, k):
+    """The selection the GPU makes (the backward recomputes it with the same kernels)."""
+    T, E = dev["x"].shape[0], dev["W_r"].shape[0]
+    routing = moe.alloc_routing(T, E, k, "cuda")
+    moe.layer_from(dev, k, path="grouped", routing=routing)()
+    torch.cuda.synchronize()
+    return routing["idx"].cpu().numpy(), routing["logits"].cpu().numpy()
+
+
+def check_selection(inp, idx_gpu, tokens=None):
+    z = O.logits(inp, tokens)
+    idx_o, _, margin = O.route(z, inp["b"], inp["config"].k)
+    sure = margin >= 1e-4
+    sel = idx_gpu if tokens is None else idx_gpu[tokens]
+    assert np.array_equal(sel[sure], idx_o[sure])
+
+
+def grads_of(dev, k, dy_dev):
+    bw = moe.backward_from(dev, k)
+    g = bw(dy_dev)
+    torch.cuda.synchronize()
+    return {n: t.cpu().numpy() for n, t in g.items()}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_backward_small_against_oracle(name):
+    cfg = CASES[name]
+    say(f"[gpu] backward parity {name}: T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I} "
+        f"I_s={cfg.I_shared}")
+    inp = mi.make_layer(cfg, seed=3)
+    dy = mi.make_grad_output(cfg, seed=3)
+    dev = moe.to_device(inp)
+    dy_dev = moe.to_device({"dy": dy})["dy"]
+    idx, _ = gpu_selection(dev, cfg.k)
+    check_selection(inp, idx)
+    got = grads_of(dev, cfg.k, dy_dev)
+    ref = O.backward(inp, idx, mi.bf16_bits_to_f32(dy).astype(np.float64), threads=THREADS)
+    for n in got:
+        err = rel_frob(got[n], ref[n])
+        say(f"[gpu]   {name} {n}: rel Frobenius {err:.3e}")
+        assert err <= TOL[n], (n, err)
+
+
+def test_backward_is_deterministic_and_linear_in_dy():
+    cfg = CASES["bwd_ragged"]
+    inp = mi.make_layer(cfg, seed=5)
+    dy = mi.make_grad_output(cfg, seed=5)
+    dev = moe.to_device(inp)
+    dy_dev = moe.to_device({"dy": dy})["dy"]
+    bw = moe.backward_from(dev, cfg.k)
+    a = {n: t.clone() for n, t in bw(dy_dev).items()}
+    b = {n: t.clone() for n, t in bw(dy_dev).items()}
+    c = {n: t.clone() for n, t in bw(2 * dy_dev).items()}   # doubling dy is exact in bf16
+    torch.cuda.synchronize()
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
+        assert torch.equal(c[n], 2 * a[n]), n
+
+
+def test_backward_zero_input_gives_zero_expert_weight_gradients():
+    cfg = CASES["bwd_no_shared"]
+    inp = mi.make_layer(cfg, seed=7)
+    inp["x"] = np.zeros_like(inp["x"])
+    dev = moe.to_device(inp)
+    dy_dev = moe.to_device({"dy": mi.make_grad_output(cfg, seed=7)})["dy"]
+    g = grads_of(dev, cfg.k, dy_dev)
+    for n in ("dx", "dW_r", "dW_up", "dW_down"):
+        assert not np.any(g[n]), n
+
+
+@pytest.mark.parametrize("name", ["nano_decode_bf16", "nano_prefill_bf16"])
+def test_backward_full_size(name):
+    # Real Nano shapes. The decode batch (64 tokens) is checked on every token and every
+    # gradient but the routed expert stacks, of which three experts are checked whole. The
+    # prefill batch (8192 tokens) is checked on sampled tokens' dx and on the least-loaded
+    # expert's complete weight and router-row gradients.
+    cfg = mi.CONFIGS[name]
+    say(f"[gpu] backward full size {name}: T={cfg.T}")
+    inp = mi.make_layer(cfg, seed=0)
+    dy = mi.make_grad_output(cfg, seed=0)
+    dy64 = mi.bf16_bits_to_f32(dy).astype(np.float64)
+    dev = moe.to_device(inp)
+    dy_dev = moe.to_device({"dy": dy})["dy"]
+    idx, _ = gpu_selection(dev, cfg.k)
+    got = grads_of(dev, cfg.k, dy_dev)
+    counts = np.bincount(idx.ravel(), minlength=cfg.E)
+    if cfg.T <= 64:
+        check_selection(inp, idx)
+        ref = O.backward(inp, idx, dy64, want=("dx", "dW_r", "dWs_up", "dWs_down"),
+                         threads=THREADS)
+        for n in ref:
+            err = rel_frob(got[n], ref[n])
+            say(f"[gpu]   {name} {n}: rel Frobenius {err:.3e}")
+            assert err <= TOL[n], (n, err)
+        experts = list(np.argsort(-counts)[:2]) + [int(np.flatnonzero(counts)[-1])]
+    else:
+        rng = np.random.default_rng(11)
+        toks = np.sort(rng.choice(cfg.T, 32, replace=False)).astype(np.int32)
+        check_selection(inp, idx, toks)
+        ref = O.backward(inp, idx[toks], dy64[toks], tokens=toks, want=("dx",), threads=THREADS)
+        err = rel_frob(got["dx"][toks], ref["dx"])
+        say(f"[gpu]   {name} dx ({len(toks)} sampled tokens): rel Frobenius {err:.3e}")
+        assert err <= TOL["dx"]
+        experts = [int(np.argmin(np.where(counts > 0, counts, 1 << 30)))]
+    for e in experts:
+        toks = np.flatnonzero((idx == e).any(axis=1)).astype(np.int32)
+        ref = O.backward(inp, idx[toks], dy64[toks], tokens=toks,
+                         want=("dW_r", "dW_up", "dW_down"), expert=int(e), threads=THREADS)
+        for n, g in (("dW_up", got["dW_up"][e]), ("dW_down", got["dW_down"][e]),
+                     ("dW_r", got["dW_r"][e])):
+            r = ref[n][e] if n == "dW_r" else ref[n]
+            err = rel_frob(g, r)
+            say(f"[gpu]   {name} expert {e} ({len(toks)} tokens) {n}: rel Frobenius {err:.3e}")
+            assert err <= TOL[n], (n, e, err)

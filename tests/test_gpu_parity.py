@@ -139,6 +139,10 @@ SMALL = {
                                          latent=128, I_shared=64, expert_dtype="mxfp4"),
     "latent_fp8_small": mi.LayerConfig("latent_fp8_small", T=45, H=256, E=32, k=4, I=96,
                                        latent=128, expert_dtype="e4m3"),
+    # expert counts that are not multiples of 8: router logits rows of E fp32 values, which the
+    # GEMM epilogue then writes element by element (grouped and decode paths)
+    "bf16_e6": mi.LayerConfig("bf16_e6", T=70, H=256, E=6, k=2, I=96, I_shared=64),
+    "bf16_e13": mi.LayerConfig("bf16_e13", T=9, H=256, E=13, k=3, I=64),
     # few tokens and a wide H: the streamed projection into the latent width splits K in four
     "latent_split_small": mi.LayerConfig("latent_split_small", T=20, H=1024, E=16, k=4, I=64,
                                          latent=64, I_shared=32),
@@ -155,7 +159,8 @@ def test_small_layer_all_tokens(name):
 
 
 @pytest.mark.parametrize("name", ["bf16_ragged", "bf16_no_shared", "latent_small",
-                                  "latent_small_shared", "latent_split_small"])
+                                  "latent_small_shared", "latent_split_small", "bf16_e6",
+                                  "bf16_e13"])
 def test_stream_and_grouped_paths_agree_with_oracle(name):
     inp = mi.make_layer(SMALL[name], seed=2)
     ys, _ = check_full(inp, "stream")
