@@ -4,7 +4,9 @@
     python bench.py [--steps K] [--warmup W] [--config NAME] [--also NAME,...] [--graph]
 
 A step is one full layer call (router GEMM, top-k, dispatch, expert GEMMs / weight streaming,
-shared expert, combine) over one batch of seeded synthetic tokens already resident in HBM.
+shared expert, combine) over one batch of seeded synthetic tokens already resident in HBM. A
+workload named "<config>+backward" times the layer's backward pass instead (reported under
+'also').
 Prints one JSON line: tokens/s, the dominant kernel's roofline fraction (HIP events around that
 kernel's launches during the timed region, against algorithmic bytes or flops), and the
 double-precision oracle timed on a bounded token sample on the host as the CPU baseline.
@@ -35,7 +37,7 @@ def parse():
     ap.add_argument("--config", default="nano_decode_bf16")
     ap.add_argument("--also", default="nano_prefill_bf16,latent_decode_bf16,nano_fp8_decode,"
                                       "nano_mxfp4_decode,nano_mxfp8_decode,latent_mxfp4_decode,"
-                                      "latent_fp8_decode",
+                                      "latent_fp8_decode,nano_prefill_bf16+backward",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--path", default="auto", choices=["auto", "grouped", "stream"])
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured graph")
@@ -67,6 +69,9 @@ def work_of(name, cfg, counts, stream=False):
         return touched * rows * 4 if narrow else 0
 
     role = name.split(":")[1]
+    if role.startswith("bwd_") or role in ("weights", "routed_activations",
+                                           "shared_activations", "gates", "dx", "dW_r"):
+        return backward_work(role, cfg, touched)
     if role == "router":
         return 2 * T * E * H, T * H * ea + E * H * ea + T * E * 4
     # stream launches: routed projection, plus the shared expert's on a bf16 plain layer
@@ -108,6 +113,55 @@ def work_of(name, cfg, counts, stream=False):
     return 0, 0
 
 
+def backward_work(role, cfg, touched):
+    """(flops, bytes) of one launch of a backward-pass span (bf16 plain layer): each GEMM's
+    reduction over the real pairs only (per-expert padding adds zeros, not counted), touched
+    expert weights read once, activations in and out once."""
+    T, H, E, k, I, Is = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared
+    P = T * k
+    wt = touched * I * H * 2          # one touched projection stack, bf16
+    gemm = {
+        # forward recompute: relu(a) and h saved, expert outputs Y
+        "bwd_routed_up": (2 * P * I * H, wt + T * H * 2 + 2 * P * I * 2),
+        "bwd_routed_down": (2 * P * H * I, wt + P * I * 2 + P * H * 2),
+        "bwd_shared_up": (2 * T * Is * H, Is * H * 2 + T * H * 2 + 2 * T * Is * 2),
+        # data gradients (transposed weights; the squared ReLU's derivative fused)
+        "bwd_routed_dgrad_down": (2 * P * I * H, wt + P * H * 2 + 2 * P * I * 2),
+        "bwd_routed_dgrad_up": (2 * P * H * I, wt + P * I * 2 + P * H * 4),
+        "bwd_shared_dgrad_down": (2 * T * Is * H, Is * H * 2 + T * H * 2 + 2 * T * Is * 2),
+        "bwd_shared_dgrad_up": (2 * T * H * Is, H * Is * 2 + T * Is * 2 + T * H * 4),
+        # weight gradients over each expert's pairs (fp32 out, every expert's matrix written)
+        "bwd_routed_wgrad_down": (2 * P * H * I, P * H * 2 + P * I * 2 + E * H * I * 4),
+        "bwd_routed_wgrad_up": (2 * P * I * H, P * I * 2 + P * H * 2 + E * I * H * 4),
+        "bwd_shared_wgrad_down": (2 * T * H * Is, T * H * 2 + T * Is * 2 + H * Is * 4),
+        "bwd_shared_wgrad_up": (2 * T * Is * H, T * Is * 2 + T * H * 2 + Is * H * 4),
+    }
+    if role in gemm:
+        f, b = gemm[role]
+        return f, int(b)
+    if role == "weights":             # transposed copies of both stacks (+ shared): read + write
+        return 0, 2 * (2 * E * I * H * 2 + (2 * Is * H * 2 if Is else 0))
+    if role == "routed_activations":  # dY, h, da, gathered x: read and written once each
+        return 0, 2 * (2 * P * H * 2 + 2 * P * I * 2)
+    if role == "shared_activations":
+        return 0, 2 * (2 * T * H * 2 + 2 * T * Is * 2)
+    if role == "gates":               # dy, Y rows in; g*dy rows and dz out
+        return 2 * P * H, T * H * 2 + P * H * 2 + P * H * 2 + P * 4
+    if role == "dx":
+        return P * H * 4, (T * H * 4 if Is else 0) + P * H * 4 + P * H * 2 + T * H * 4
+    if role == "dW_r":
+        return 2 * P * H, P * 4 + P * H * 2 + E * H * 4
+    return 0, 0
+
+
+def backward_flops(cfg):
+    """Algorithmic flops of the backward pass proper: data and weight gradients of the routed and
+    shared experts and of the router (the forward recompute is not counted)."""
+    T, H, E, k, I, Is = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared
+    P = T * k
+    return 4 * 2 * P * I * H + 4 * 2 * T * Is * H + 2 * 2 * P * H + 2 * P * H
+
+
 def kernel_of(span):
     return span.split(":")[0]
 
@@ -122,7 +176,8 @@ def mfma_dtype(kernel, cfg):
 # ------------------------------------------------------------------ one workload
 
 def prepare(name, moe, mi, torch, path, shared=None):
-    cfg = mi.CONFIGS[name]
+    backward = name.endswith("+backward")
+    cfg = mi.CONFIGS[name.split("+")[0]]
     if shared is not None and shared["cfg"].H == cfg.H and shared["cfg"].E == cfg.E and \
             shared["cfg"].I == cfg.I and shared["cfg"].expert_dtype == cfg.expert_dtype and \
             shared["cfg"].I_shared == cfg.I_shared and not cfg.latent:
@@ -134,8 +189,16 @@ def prepare(name, moe, mi, torch, path, shared=None):
         inp = mi.make_layer(cfg, 0)
         dev = moe.to_device(inp)
     rt = moe.alloc_routing(cfg.T, cfg.E, cfg.k, "cuda")
+    if backward:
+        # the backward pass of the layer for a seeded upstream gradient dy; the forward call
+        # records the routing (the same selection the backward recomputes) for the byte counts
+        moe.layer_from(dev, cfg.k, path="grouped", routing=rt)()
+        dy = moe.to_device({"dy": mi.make_grad_output(cfg, 0)})["dy"]
+        bw = moe.backward_from(dev, cfg.k)
+        return dict(cfg=cfg, inp=inp, dev=dev, rt=rt, layer=lambda: bw(dy), backward=True,
+                    name=name)
     layer = moe.layer_from(dev, cfg.k, path=path, routing=rt)
-    return dict(cfg=cfg, inp=inp, dev=dev, rt=rt, layer=layer)
+    return dict(cfg=cfg, inp=inp, dev=dev, rt=rt, layer=layer, name=name)
 
 
 def measure(w, moe, torch, steps, warmup, graph):
@@ -147,7 +210,7 @@ def measure(w, moe, torch, steps, warmup, graph):
     counts = w["rt"]["counts"].cpu().numpy()
 
     # traced pass over a few steps: per-span durations, to find the dominant kernel
-    spans_per_step = 16
+    spans_per_step = 32 if w.get("backward") else 16
     moe.binding.trace_enable(4 * spans_per_step)
     for _ in range(3):
         layer()
@@ -178,7 +241,7 @@ def measure(w, moe, torch, steps, warmup, graph):
 
     # timed region: K steps; events bracket the dominant kernel's launches (eager mode)
     if not graph:
-        moe.binding.trace_enable(steps * 4, dominant + ":")
+        moe.binding.trace_enable(steps * 8, dominant + ":")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -190,7 +253,7 @@ def measure(w, moe, torch, steps, warmup, graph):
         moe.binding.trace_disable()
     else:
         # graph replays cannot carry the event records: time the kernel in an eager pass
-        moe.binding.trace_enable(steps * 4, dominant + ":")
+        moe.binding.trace_enable(steps * 8, dominant + ":")
         for _ in range(steps):
             layer()
         torch.cuda.synchronize()
@@ -210,7 +273,7 @@ def measure(w, moe, torch, steps, warmup, graph):
     else:
         bound, achieved = "mfma", flops / (kms * 1e-3) / 1e12
         peak, unit = PEAK_MFMA[dt] / 1e12, "TFLOP/s"
-    traffic = measured_traffic(cfg.name, dominant)
+    traffic = measured_traffic(w.get("name", cfg.name), dominant)
     roof = dict(bound=bound, achieved=round(achieved, 1), peak=peak, unit=unit,
                 frac=round(achieved / peak, 4), traffic=traffic, kernel=dominant,
                 launches=nlaunch, avg_launch_us=round(kms * 1e3 / max(nlaunch, 1), 2),
@@ -228,6 +291,10 @@ def measure(w, moe, torch, steps, warmup, graph):
     cold = step_times(layer, torch, min(max(steps, 10), 30), before=lambda: flush.fill_(1))
     del flush
     pct = lambda a, q: round(float(np.percentile(a, q)), 1)
+    if w.get("backward"):   # the whole pass against the bf16 peak (recompute not counted)
+        roof["pass_flops"] = backward_flops(cfg)
+        roof["pass_frac_of_bf16_peak"] = round(
+            backward_flops(cfg) / (ms_step * 1e-3) / PEAK_MFMA["bf16"], 4)
     return dict(ms_per_step=ms_step, tokens_per_s=cfg.T / (ms_step * 1e-3), roofline=roof,
                 kernel_us_per_step=breakdown, touched_experts=int(np.count_nonzero(counts)),
                 step_us=dict(median=pct(dist, 50), p10=pct(dist, 10), p90=pct(dist, 90),

@@ -166,20 +166,31 @@ __global__ __launch_bounds__(256) void bwd_route_kernel(const uint16_t* dy, cons
   }
 }
 
-// dW_r[e][h] = sum over expert e's pair rows p (ascending) of dzp[p] * x[perm[p]][h]. Workgroup:
-// 256 columns of one expert; wave w adds rows w, w + 4, ...; the four partial sums are added in
-// wave order.
-__global__ __launch_bounds__(256) void bwd_router_weight_kernel(const float* dzp,
-                                                                const uint16_t* x,
-                                                                const int32_t* perm,
-                                                                const int32_t* offs, int H,
-                                                                float* dWr) {
-  __shared__ float4 part[4][64];
-  const int e = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+// dW_r[e][h] = sum over expert e's pair rows p (ascending) of dzp[p] * x[perm[p]][h], in two
+// passes with a fixed chunking, so that the popular experts' rows are spread over many
+// workgroups and the sum stays deterministic. Expert e's rows are cut into chunks of 64 in
+// order; its chunks are numbered koffs[e] / 64 .. koffs[e + 1] / 64 - 1 (koffs: per-expert
+// offsets padded to multiples of 64). Pass 1: one workgroup per (chunk, 256 columns) writes the
+// chunk's sum; wave w adds rows w, w + 4, ... of the chunk, the four partial sums are added in
+// wave order. Pass 2: dW_r[e] = sum of e's chunk sums in chunk order.
+__global__ __launch_bounds__(256) void router_weight_chunks_kernel(
+    const float* dzp, const uint16_t* x, const int32_t* perm, const int32_t* offs,
+    const int32_t* koffs, int E, int H, float* part) {
+  __shared__ float4 acc_w[4][64];
+  const int q = blockIdx.y;  // chunk
+  if (q * kTile >= koffs[E]) return;
+  int lo = 0, hi = E - 1;    // expert holding chunk q
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (koffs[mid] <= q * kTile) lo = mid; else hi = mid - 1;
+  }
+  const int p0 = offs[lo] + (q * kTile - koffs[lo]);
+  const int p1 = min(p0 + kTile, offs[lo + 1]);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = blockIdx.x * 256 + lane * 4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (c < H) {
-    for (int p = offs[e] + wave; p < offs[e + 1]; p += 4) {
+    for (int p = p0 + wave; p < p1; p += 4) {
       const float z = dzp[p];
       const uint2 v = *(const uint2*)(x + (int64_t)perm[p] * H + c);
       acc.x += z * bf16_bits_to_f32(v.x & 0xFFFF);
@@ -188,16 +199,30 @@ __global__ __launch_bounds__(256) void bwd_router_weight_kernel(const float* dzp
       acc.w += z * bf16_bits_to_f32(v.y >> 16);
     }
   }
-  part[wave][lane] = acc;
+  acc_w[wave][lane] = acc;
   __syncthreads();
   if (wave == 0 && c < H) {
-    float4 s = part[0][lane];
+    float4 t = acc_w[0][lane];
     for (int w = 1; w < 4; ++w) {
-      const float4 q = part[w][lane];
-      s.x += q.x; s.y += q.y; s.z += q.z; s.w += q.w;
+      const float4 u = acc_w[w][lane];
+      t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
     }
-    *(float4*)(dWr + (int64_t)e * H + c) = s;
+    *(float4*)(part + (int64_t)q * H + c) = t;
   }
+}
+
+__global__ __launch_bounds__(256) void router_weight_sum_kernel(const float* part,
+                                                                const int32_t* koffs, int H,
+                                                                float* dWr) {
+  const int e = blockIdx.y;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c >= H) return;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int q = koffs[e] / kTile; q < koffs[e + 1] / kTile; ++q) {
+    const float4 u = *(const float4*)(part + (int64_t)q * H + c);
+    s.x += u.x; s.y += u.y; s.z += u.z; s.w += u.w;
+  }
+  *(float4*)(dWr + (int64_t)e * H + c) = s;
 }
 
 // dx[t] = dxs[t] (shared expert; optional) + sum_j du[pos(t, j)] + sum_j dzp[pos(t, j)] W_r[e_j],
@@ -256,11 +281,14 @@ hipError_t launch_bwd_route(const uint16_t* dy, const uint16_t* Yp, const float*
 }
 
 hipError_t launch_bwd_router_weight(const float* dzp, const uint16_t* x, const int32_t* perm,
-                                    const int32_t* offs, int E, int H, float* dWr,
-                                    hipStream_t s) {
+                                    const int32_t* offs, const int32_t* koffs, int E, int H,
+                                    int max_chunks, float* part, float* dWr, hipStream_t s) {
   if (H % 4) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_router_weight_kernel, dim3(cdiv(H, 256), E), dim3(256), 0, s, dzp, x,
-                     perm, offs, H, dWr);
+  if (max_chunks > 0)
+    hipLaunchKernelGGL(router_weight_chunks_kernel, dim3(cdiv(H, 256), max_chunks), dim3(256), 0,
+                       s, dzp, x, perm, offs, koffs, E, H, part);
+  hipLaunchKernelGGL(router_weight_sum_kernel, dim3(cdiv(H, 1024), E), dim3(256), 0, s, part,
+                     koffs, H, dWr);
   return hipGetLastError();
 }
 

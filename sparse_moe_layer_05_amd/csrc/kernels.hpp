@@ -145,10 +145,12 @@ hipError_t launch_bwd_route(const uint16_t* dy, const uint16_t* Yp, const float*
                             const int32_t* idx, const float* gates, const int32_t* pos, int T,
                             int H, int E, int k, uint16_t* dYp, float* dzp, hipStream_t s);
 
-// dW_r[e] = sum over expert e's pair rows p (ascending) of dzp[p] x[perm[p]], fp32.
+// dW_r[e] = sum over expert e's pair rows p (ascending) of dzp[p] x[perm[p]], fp32: sums of
+// 64-row chunks (numbered by koffs / 64, at most max_chunks of them) into part
+// [max_chunks][H], then each expert's chunk sums in order.
 hipError_t launch_bwd_router_weight(const float* dzp, const uint16_t* x, const int32_t* perm,
-                                    const int32_t* offs, int E, int H, float* dWr,
-                                    hipStream_t s);
+                                    const int32_t* offs, const int32_t* koffs, int E, int H,
+                                    int max_chunks, float* part, float* dWr, hipStream_t s);
 
 // dx[t] = dxs[t] (optional) + sum_j du[pos(t,j)] + sum_j dzp[pos(t,j)] W_r[idx(t,j)], fp32.
 hipError_t launch_bwd_dx(const float* dxs, const float* du, const float* dzp, const uint16_t* Wr,

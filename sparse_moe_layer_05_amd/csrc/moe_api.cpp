@@ -530,6 +530,7 @@ struct BwdPlan {
   size_t dscratch = 0, mt_start = 0, koffs = 0;
   size_t r = 0, h = 0, Yp = 0, hs = 0, rs = 0;                 // recomputed forward
   size_t dYp = 0, dzp = 0, da = 0, du = 0, das = 0, dxs = 0;   // backward intermediates
+  size_t wr_part = 0;                                          // dW_r chunk sums
   size_t WuT = 0, WdT = 0, WsuT = 0, WsdT = 0;                 // transposed weights
   size_t dYpT = 0, hT = 0, daT = 0, XpT = 0;                   // [feature][padded pair column]
   size_t dyT = 0, hsT = 0, dasT = 0, xT = 0;                   // [feature][padded token]
@@ -576,6 +577,7 @@ int32_t make_bwd_plan(const moe_desc_t* d, BwdPlan* out) {
   p.Yp = take(P * H * 2);
   p.dYp = take(P * H * 2);
   p.dzp = take(P * 4);
+  p.wr_part = take((size_t)(p.Ppad / 64) * H * 4);
   p.da = take(P * I * 2);
   p.du = take(P * H * 4);
   p.WuT = take(E * H * I * 2);
@@ -756,8 +758,8 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
   }
   {
     MOE_SPAN("bwd_router_weight:dW_r");
-    MOE_TRY(launch_bwd_router_weight(dzp, (const uint16_t*)w->x, perm, offsets, E, H, gr->dW_r,
-                                     s));
+    MOE_TRY(launch_bwd_router_weight(dzp, (const uint16_t*)w->x, perm, offsets, koffs, E, H,
+                                     pl.Ppad / 64, (float*)at(pl.wr_part), gr->dW_r, s));
   }
 
   // (5) routed weight gradients over each expert's own pair rows: operands transposed so that
