@@ -79,9 +79,17 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeParams p) {
 }
 
 // Padded K offsets of the weight-gradient products: koffs[g + 1] = koffs[g] + roundup(counts[g],
-// 64), so every expert's window of the transposed operands starts on a 128-byte boundary.
-__global__ void pad_offsets_kernel(const int32_t* counts, int G, int32_t* koffs) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+// 64), so every expert's window of the transposed operands starts on a 128-byte boundary; and
+// the experts by descending count (ties: lower index first), the launch order of those products.
+__global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* counts, int G,
+                                                           int32_t* koffs, int32_t* order) {
+  for (int g = threadIdx.x; g < G; g += blockDim.x) {
+    const int c = counts[g];
+    int rank = 0;
+    for (int q = 0; q < G; ++q) rank += counts[q] > c || (counts[q] == c && q < g);
+    order[rank] = g;
+  }
+  if (threadIdx.x != 0) return;
   int acc = 0;
   koffs[0] = 0;
   for (int g = 0; g < G; ++g) {
@@ -265,8 +273,9 @@ hipError_t launch_transpose(const TransposeParams& p, int max_cols, int batch, h
   return hipGetLastError();
 }
 
-hipError_t launch_pad_offsets(const int32_t* counts, int G, int32_t* koffs, hipStream_t s) {
-  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(64), 0, s, counts, G, koffs);
+hipError_t launch_pad_offsets(const int32_t* counts, int G, int32_t* koffs, int32_t* order,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(1024), 0, s, counts, G, koffs, order);
   return hipGetLastError();
 }
 

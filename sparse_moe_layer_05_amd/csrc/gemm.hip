@@ -50,18 +50,25 @@ template <int BM, int BN>
 __device__ __forceinline__ bool tile_of(const GemmParams& p, int& g, int& row0, int& rows,
                                         int& n0) {
   const int nN = cdiv(p.N, BN);
-  const int L = xcd_logical_block(blockIdx.x, gridDim.x);
-  if (p.koffs) {                       // one M x N product per group, M-tiles fastest
+  if (p.koffs) {
+    // One M x N product per group, M-tiles fastest. A tile's cost grows with its group's K (an
+    // expert's token count), so the tiles are dealt round robin over the dies (block b runs on
+    // die b % 8): every expert's tiles spread over all of them. Its operand panels, re-read by
+    // several dies, are served by the shared Infinity Cache. With korder the groups go heaviest
+    // first, so that the longest tiles do not start last.
+    const int L = blockIdx.x;
     const int nM = cdiv(p.M, BM);
     const int per = nM * nN;
     if (L >= p.G * per) return false;
-    g = L / per;
-    const int local = L - g * per;
+    const int slot = L / per;
+    g = p.korder ? p.korder[slot] : slot;
+    const int local = L - slot * per;
     n0 = (local / nM) * BN;
     row0 = (local % nM) * BM;
     rows = min(BM, p.M - row0);
     return rows > 0;
   }
+  const int L = xcd_logical_block(blockIdx.x, gridDim.x);
   if (p.mt_start) {
     const int total = p.mt_start[p.G] * nN;
     if (L >= total) return false;

@@ -59,6 +59,7 @@ struct GemmParams {
   // C + g * c_gstride. M, N and the operands are shared by the groups; K is unused.
   const int32_t* koffs = nullptr;
   int64_t c_gstride = 0;
+  const int32_t* korder = nullptr;  // optional: the groups in launch order (heaviest first)
 };
 
 struct GemmKind {

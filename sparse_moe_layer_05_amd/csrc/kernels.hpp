@@ -135,8 +135,10 @@ struct TransposeParams {
 // max_cols bounds the destination columns (the grid); the kernel reads koffs[G] itself.
 hipError_t launch_transpose(const TransposeParams& p, int max_cols, int batch, hipStream_t s);
 
-// koffs[g + 1] = koffs[g] + roundup(counts[g], 64), koffs[0] = 0.
-hipError_t launch_pad_offsets(const int32_t* counts, int G, int32_t* koffs, hipStream_t s);
+// koffs[g + 1] = koffs[g] + roundup(counts[g], 64), koffs[0] = 0; order = the groups by
+// descending count, ties by index.
+hipError_t launch_pad_offsets(const int32_t* counts, int G, int32_t* koffs, int32_t* order,
+                              hipStream_t s);
 
 // Gradient through the routing gates, per token: dg_j = <dy_t, Yp[pos(t,j)]>,
 // dz_j = (dg_j - sum_m g_m dg_m) / Z * s_j (1 - s_j) with s = sigmoid(logits), Z = sum_j s_j;

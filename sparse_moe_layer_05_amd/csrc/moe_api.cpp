@@ -527,7 +527,7 @@ struct BwdPlan {
   int T = 0, H = 0, E = 0, k = 0, I = 0, Is = 0, P = 0, Ppad = 0, Tpad = 0;
   int nsplit = 1, kchunk = 0;
   size_t logits = 0, zpart = 0, idx = 0, gates = 0, counts = 0, offsets = 0, perm = 0, pos = 0;
-  size_t dscratch = 0, mt_start = 0, koffs = 0;
+  size_t dscratch = 0, mt_start = 0, koffs = 0, korder = 0;
   size_t r = 0, h = 0, Yp = 0, hs = 0, rs = 0;                 // recomputed forward
   size_t dYp = 0, dzp = 0, da = 0, du = 0, das = 0, dxs = 0;   // backward intermediates
   size_t wr_part = 0;                                          // dW_r chunk sums
@@ -572,6 +572,7 @@ int32_t make_bwd_plan(const moe_desc_t* d, BwdPlan* out) {
   p.dscratch = take(dispatch_scratch_ints(p.T, p.E) * 4);
   p.mt_start = take((E + 1) * 4);
   p.koffs = take((E + 1) * 4);
+  p.korder = take(E * 4);
   p.r = take(P * I * 2);
   p.h = take(P * I * 2);
   p.Yp = take(P * H * 2);
@@ -643,6 +644,7 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
   int32_t* pos = (int32_t*)at(pl.pos);
   int32_t* mt_start = (int32_t*)at(pl.mt_start);
   int32_t* koffs = (int32_t*)at(pl.koffs);
+  int32_t* korder = (int32_t*)at(pl.korder);
   const int max_mt = max_group_mtiles(P, E, kGroupBM);
 
   // (1) forward recompute: routing and dispatch as in the forward call
@@ -663,7 +665,7 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
     MOE_SPAN("dispatch:all");
     MOE_TRY(launch_dispatch(idx, T, E, k, counts, offsets, perm, pos, (int32_t*)at(pl.dscratch),
                             kGroupBM, mt_start, DispatchExtras(), s));
-    MOE_TRY(launch_pad_offsets(counts, E, koffs, s));
+    MOE_TRY(launch_pad_offsets(counts, E, koffs, korder, s));
   }
   // expert activations: relu(a) and h = relu(a)^2 per pair row, then the expert outputs Y
   void* r = at(pl.r);
@@ -784,7 +786,7 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
   {
     GemmParams g;  // dW_down[e] [H][I] = dY_e^T h_e
     g.A = dYpT; g.lda = pl.Ppad; g.a_rows = H; g.B = hT; g.ldb = pl.Ppad;
-    g.C = gr->dW_down; g.ldc = I; g.M = H; g.N = I; g.G = E; g.koffs = koffs;
+    g.C = gr->dW_down; g.ldc = I; g.M = H; g.N = I; g.G = E; g.koffs = koffs; g.korder = korder;
     g.c_gstride = (int64_t)H * I;
     MOE_SPAN("gemm_bf16_f32out:bwd_routed_wgrad_down");
     MOE_TRY(launch_gemm(GemmKind{Elt::BF16, Elt::F32, Epi::Store}, g, 0, s));
@@ -792,7 +794,7 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
   {
     GemmParams g;  // dW_up[e] [I][H] = da_e^T x_e
     g.A = daT; g.lda = pl.Ppad; g.a_rows = I; g.B = XpT; g.ldb = pl.Ppad;
-    g.C = gr->dW_up; g.ldc = H; g.M = I; g.N = H; g.G = E; g.koffs = koffs;
+    g.C = gr->dW_up; g.ldc = H; g.M = I; g.N = H; g.G = E; g.koffs = koffs; g.korder = korder;
     g.c_gstride = (int64_t)I * H;
     MOE_SPAN("gemm_bf16_f32out:bwd_routed_wgrad_up");
     MOE_TRY(launch_gemm(GemmKind{Elt::BF16, Elt::F32, Epi::Store}, g, 0, s));
