@@ -190,12 +190,15 @@ def prepare(name, moe, mi, torch, path, shared=None):
         dev = moe.to_device(inp)
     rt = moe.alloc_routing(cfg.T, cfg.E, cfg.k, "cuda")
     if backward:
-        # the backward pass of the layer for a seeded upstream gradient dy; the forward call
-        # records the routing (the same selection the backward recomputes) for the byte counts
+        # the backward pass of the layer for a seeded upstream gradient dy, as a training step
+        # runs it: after moe_layer_forward_train, reading the activations that call saved. The
+        # forward call below records the routing (the same selection) for the byte counts.
         moe.layer_from(dev, cfg.k, path="grouped", routing=rt)()
         dy = moe.to_device({"dy": mi.make_grad_output(cfg, 0)})["dy"]
         bw = moe.backward_from(dev, cfg.k)
-        return dict(cfg=cfg, inp=inp, dev=dev, rt=rt, layer=lambda: bw(dy), backward=True,
+        bw.forward_train()
+        return dict(cfg=cfg, inp=inp, dev=dev, rt=rt, layer=lambda: bw(dy, saved=True),
+                    recompute=lambda: bw(dy), train_forward=bw.forward_train, backward=True,
                     name=name)
     layer = moe.layer_from(dev, cfg.k, path=path, routing=rt)
     return dict(cfg=cfg, inp=inp, dev=dev, rt=rt, layer=layer, name=name)
@@ -291,15 +294,23 @@ def measure(w, moe, torch, steps, warmup, graph):
     cold = step_times(layer, torch, min(max(steps, 10), 30), before=lambda: flush.fill_(1))
     del flush
     pct = lambda a, q: round(float(np.percentile(a, q)), 1)
+    extra = {}
     if w.get("backward"):   # the whole pass against the bf16 peak (recompute not counted)
         roof["pass_flops"] = backward_flops(cfg)
         roof["pass_frac_of_bf16_peak"] = round(
             backward_flops(cfg) / (ms_step * 1e-3) / PEAK_MFMA["bf16"], 4)
+        # the same backward recomputing the routing and expert activations itself, and the
+        # training forward that saves them (median single steps)
+        rec = step_times(w["recompute"], torch, max(steps // 2, 10))
+        fwd = step_times(w["train_forward"], torch, max(steps // 2, 10))
+        extra = dict(backward_recompute_us=round(float(np.median(rec)), 1),
+                     forward_train_us=round(float(np.median(fwd)), 1))
     return dict(ms_per_step=ms_step, tokens_per_s=cfg.T / (ms_step * 1e-3), roofline=roof,
                 kernel_us_per_step=breakdown, touched_experts=int(np.count_nonzero(counts)),
                 step_us=dict(median=pct(dist, 50), p10=pct(dist, 10), p90=pct(dist, 90),
                              cold_cache_median=pct(cold, 50),
-                             cold_cache_tokens_per_s=round(cfg.T / (np.median(cold) * 1e-6), 1)))
+                             cold_cache_tokens_per_s=round(cfg.T / (np.median(cold) * 1e-6), 1),
+                             **extra))
 
 
 def step_times(layer, torch, n, before=None):

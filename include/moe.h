@@ -84,6 +84,8 @@ typedef enum {
                                     e4m3, MXFP4 and MXFP8 experts */
 #define MOE_PATH_MASK 3u
 #define MOE_ROUTING_GIVEN 4u     /* routing->idx and routing->gates are INPUTS: skip the router */
+#define MOE_SAVED_IN_WORKSPACE 8u /* moe_layer_backward only: the workspace holds what
+                                    moe_layer_forward_train saved; skip the recompute */
 
 typedef struct {
   int32_t T;           /* tokens */
@@ -185,11 +187,15 @@ int32_t moe_bias_update(const int32_t *counts, const float *target, int32_t E, f
  *   dx [T, H], dW_r [E, H], dW_up [E, I, H], dW_down [E, H, I], dWs_up [I_s, H], dWs_down [H, I_s]
  *   (the last two only when I_shared > 0; all others are required).
  * Supported: act_dtype = expert_dtype = MOE_BF16, latent = 0, routing computed inside (flags:
- * path bits ignored, MOE_ROUTING_GIVEN not accepted) -- else MOE_ERR_UNSUPPORTED. The call
- * recomputes the forward's routing and expert activations from x (nothing is saved between
- * calls) and makes transposed copies of the weights in the workspace. Pointers: 16-byte aligned
- * device memory owned by the caller. Workspace: moe_backward_workspace_size bytes. Asynchronous
- * on `stream`; nothing is allocated or synchronised. Results are deterministic (no atomics). */
+ * path bits ignored, MOE_ROUTING_GIVEN not accepted) -- else MOE_ERR_UNSUPPORTED. Without
+ * MOE_SAVED_IN_WORKSPACE the call first recomputes the forward's routing and expert activations
+ * from x; with it, it reads them from the workspace, where moe_layer_forward_train (same
+ * descriptor apart from that flag, same weights and x) left them. Either way it makes transposed
+ * copies of the weights in the workspace, and it never overwrites the saved part, so several
+ * backward calls (e.g. for several dy) may follow one moe_layer_forward_train. Pointers: 16-byte
+ * aligned device memory owned by the caller. Workspace: moe_backward_workspace_size bytes.
+ * Asynchronous on `stream`; nothing is allocated or synchronised. Results are deterministic (no
+ * atomics) and identical with or without the saved activations. */
 typedef struct {
   float *dx;
   float *dW_r;
@@ -200,6 +206,12 @@ typedef struct {
 } moe_grads_t;
 
 int32_t moe_backward_workspace_size(const moe_desc_t *desc, size_t *bytes);
+/* Training forward: y [T, H] exactly as moe_layer_forward computes it on MOE_PATH_GROUPED
+ * (bit for bit), keeping the routing and expert activations moe_layer_backward reads in `ws`
+ * (moe_backward_workspace_size bytes). Same support, arguments and errors as moe_layer_backward
+ * (MOE_SAVED_IN_WORKSPACE must not be set). */
+int32_t moe_layer_forward_train(const moe_desc_t *desc, const moe_weights_t *weights, void *y,
+                                void *ws, size_t ws_bytes, void *stream);
 int32_t moe_layer_backward(const moe_desc_t *desc, const moe_weights_t *weights, const void *dy,
                            moe_grads_t *grads, void *ws, size_t ws_bytes, void *stream);
 

@@ -18,12 +18,13 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4, MOE_MXFP8 = 0, 1, 2, 3, 4
 _EXPERT_DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_FP8_E4M3, "mxfp4": MOE_MXFP4,
                   "mxfp8": MOE_MXFP8}
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
-PATH_AUTO, PATH_GROUPED, PATH_STREAM, ROUTING_GIVEN = 0, 1, 2, 4
+PATH_AUTO, PATH_GROUPED, PATH_STREAM, ROUTING_GIVEN, SAVED_IN_WORKSPACE = 0, 1, 2, 4, 8
 _PATHS = {"auto": PATH_AUTO, "grouped": PATH_GROUPED, "stream": PATH_STREAM}
 
 EXPORTS = ("moe_workspace_size", "moe_layer_forward", "latent_moe_forward", "moe_route",
            "moe_dispatch_workspace_size", "moe_dispatch", "moe_bias_update",
-           "moe_backward_workspace_size", "moe_layer_backward", "moe_status_str",
+           "moe_backward_workspace_size", "moe_layer_forward_train", "moe_layer_backward",
+           "moe_status_str",
            "moe_trace_enable",
            "moe_trace_count", "moe_trace_read", "moe_trace_reset")
 
@@ -80,6 +81,8 @@ def lib() -> C.CDLL:
             L.moe_backward_workspace_size.argtypes = [C.POINTER(MoeDesc), C.POINTER(sz)]
             L.moe_layer_backward.argtypes = [C.POINTER(MoeDesc), C.POINTER(MoeWeights), vp,
                                              C.POINTER(MoeGrads), vp, sz, vp]
+            L.moe_layer_forward_train.argtypes = [C.POINTER(MoeDesc), C.POINTER(MoeWeights), vp,
+                                                  vp, sz, vp]
             L.moe_status_str.argtypes = [i32]
             L.moe_trace_enable.argtypes = [i32, C.c_char_p]
             L.moe_trace_count.argtypes = []
@@ -229,10 +232,21 @@ class Backward:
         self.ws_bytes = n.value
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=x.device)
 
-    def __call__(self, dy, stream=None):
-        rc = lib().moe_layer_backward(C.byref(self.desc), C.byref(self.w), _p(dy),
-                                      C.byref(self.g), _p(self.ws), self.ws_bytes,
-                                      _stream(stream))
+    def forward_train(self, y=None, stream=None):
+        """y of the layer (grouped path), keeping what the backward pass reads in the workspace:
+        later calls with ``saved=True`` skip the recompute."""
+        y = y if y is not None else torch.empty_like(self._keep[0])
+        rc = lib().moe_layer_forward_train(C.byref(self.desc), C.byref(self.w), _p(y),
+                                           _p(self.ws), self.ws_bytes, _stream(stream))
+        _check(rc, "moe_layer_forward_train")
+        return y
+
+    def __call__(self, dy, stream=None, saved=False):
+        d = MoeDesc.from_buffer_copy(self.desc)
+        if saved:
+            d.flags |= SAVED_IN_WORKSPACE
+        rc = lib().moe_layer_backward(C.byref(d), C.byref(self.w), _p(dy), C.byref(self.g),
+                                      _p(self.ws), self.ws_bytes, _stream(stream))
         _check(rc, "moe_layer_backward")
         return self.grads
 

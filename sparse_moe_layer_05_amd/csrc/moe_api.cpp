@@ -544,7 +544,8 @@ int32_t make_bwd_plan(const moe_desc_t* d, BwdPlan* out) {
   dd.flags = MOE_PATH_GROUPED;
   int32_t rc = make_plan(&dd, false, &fp);
   if (rc) return rc;
-  if (d->flags & ~(MOE_PATH_MASK | MOE_ROUTING_GIVEN)) return MOE_ERR_INVALID_ARG;
+  if (d->flags & ~(MOE_PATH_MASK | MOE_ROUTING_GIVEN | MOE_SAVED_IN_WORKSPACE))
+    return MOE_ERR_INVALID_ARG;
   if (d->flags & MOE_ROUTING_GIVEN) return MOE_ERR_UNSUPPORTED;
   if (d->act_dtype != MOE_BF16 || d->expert_dtype != MOE_BF16 || d->latent) return MOE_ERR_UNSUPPORTED;
   BwdPlan p;
@@ -614,25 +615,12 @@ hipError_t transpose_weights(const void* W, int rows, int cols, int batch, void*
   return launch_transpose(t, rows, batch, s);
 }
 
-int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, moe_grads_t* gr,
-                 void* ws, size_t ws_bytes, hipStream_t s) {
-  if (!d) return MOE_ERR_INVALID_ARG;
-  BwdPlan pl;
-  int32_t rc = make_bwd_plan(d, &pl);
-  if (rc) return rc;
-  if (pl.T == 0) return MOE_OK;
-  if (!w || !dy || !gr || !w->x || !w->W_r || !w->b || !w->W_up || !w->W_down || !gr->dx ||
-      !gr->dW_r || !gr->dW_up || !gr->dW_down)
-    return MOE_ERR_INVALID_ARG;
-  if (pl.Is && (!w->Ws_up || !w->Ws_down || !gr->dWs_up || !gr->dWs_down))
-    return MOE_ERR_INVALID_ARG;
-  const void* ptrs[] = {w->x, w->W_r, w->W_up, w->W_down, w->Ws_up, w->Ws_down, dy, gr->dx,
-                        gr->dW_r, gr->dW_up, gr->dW_down, gr->dWs_up, gr->dWs_down};
-  for (const void* q : ptrs)
-    if (q && !aligned16(q)) return MOE_ERR_INVALID_ARG;
-  if (!ws || ws_bytes < pl.total || !aligned16(ws)) return MOE_ERR_WORKSPACE;
-
-  uint8_t* base = (uint8_t*)ws;
+// Routing, dispatch and the expert activations the backward pass reads, into the backward
+// workspace: logits, selection and gates, the dispatch arrays and padded K offsets, relu(a) and
+// h = relu(a)^2 per pair row, the expert outputs Y (bf16, pair rows), and for the shared expert
+// relu(a_s) and h_s.
+int32_t bwd_activations(const BwdPlan& pl, const moe_weights_t* w, uint8_t* base,
+                        hipStream_t s) {
   auto at = [&](size_t off) { return (void*)(base + off); };
   const int T = pl.T, H = pl.H, E = pl.E, k = pl.k, I = pl.I, Is = pl.Is, P = pl.P;
   float* logits = (float*)at(pl.logits);
@@ -646,8 +634,7 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
   int32_t* koffs = (int32_t*)at(pl.koffs);
   int32_t* korder = (int32_t*)at(pl.korder);
   const int max_mt = max_group_mtiles(P, E, kGroupBM);
-
-  // (1) forward recompute: routing and dispatch as in the forward call
+  // routing and dispatch as in the forward call
   {
     float* zsrc = pl.nsplit > 1 ? (float*)at(pl.zpart) : logits;
     {
@@ -698,6 +685,52 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
     MOE_SPAN("gemm_bf16_sqrelu:bwd_shared_up");
     MOE_TRY(launch_gemm(GemmKind{Elt::BF16, Elt::BF16, Epi::SqReluSave}, g, 0, s));
   }
+
+  return MOE_OK;
+}
+
+int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, moe_grads_t* gr,
+                 void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!d) return MOE_ERR_INVALID_ARG;
+  BwdPlan pl;
+  int32_t rc = make_bwd_plan(d, &pl);
+  if (rc) return rc;
+  if (pl.T == 0) return MOE_OK;
+  if (!w || !dy || !gr || !w->x || !w->W_r || !w->b || !w->W_up || !w->W_down || !gr->dx ||
+      !gr->dW_r || !gr->dW_up || !gr->dW_down)
+    return MOE_ERR_INVALID_ARG;
+  if (pl.Is && (!w->Ws_up || !w->Ws_down || !gr->dWs_up || !gr->dWs_down))
+    return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {w->x, w->W_r, w->W_up, w->W_down, w->Ws_up, w->Ws_down, dy, gr->dx,
+                        gr->dW_r, gr->dW_up, gr->dW_down, gr->dWs_up, gr->dWs_down};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < pl.total || !aligned16(ws)) return MOE_ERR_WORKSPACE;
+
+  uint8_t* base = (uint8_t*)ws;
+  auto at = [&](size_t off) { return (void*)(base + off); };
+  const int T = pl.T, H = pl.H, E = pl.E, k = pl.k, I = pl.I, Is = pl.Is, P = pl.P;
+  float* logits = (float*)at(pl.logits);
+  int32_t* idx = (int32_t*)at(pl.idx);
+  float* gates = (float*)at(pl.gates);
+  int32_t* counts = (int32_t*)at(pl.counts);
+  int32_t* offsets = (int32_t*)at(pl.offsets);
+  int32_t* perm = (int32_t*)at(pl.perm);
+  int32_t* pos = (int32_t*)at(pl.pos);
+  int32_t* mt_start = (int32_t*)at(pl.mt_start);
+  int32_t* koffs = (int32_t*)at(pl.koffs);
+  int32_t* korder = (int32_t*)at(pl.korder);
+  const int max_mt = max_group_mtiles(P, E, kGroupBM);
+
+  if (!(d->flags & MOE_SAVED_IN_WORKSPACE)) {  // else moe_layer_forward_train left them
+    rc = bwd_activations(pl, w, base, s);
+    if (rc) return rc;
+  }
+  void* r = at(pl.r);
+  void* h = at(pl.h);
+  void* Yp = at(pl.Yp);
+  void* hs = Is ? at(pl.hs) : nullptr;
+  void* rs = Is ? at(pl.rs) : nullptr;
 
   // (2) transposed weights for the data-gradient products (C = A . B^T needs K-contiguous B)
   void* WuT = at(pl.WuT);
@@ -830,6 +863,40 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
   return hip_status(hipGetLastError());
 }
 
+// Forward pass that keeps what the backward pass reads (in the backward workspace layout):
+// routing, dispatch and the expert activations (bwd_activations), then the shared expert's
+// output and the combine exactly as the grouped forward path computes them.
+int32_t forward_train(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws,
+                      size_t ws_bytes, hipStream_t s) {
+  if (!d) return MOE_ERR_INVALID_ARG;
+  if (d->flags & MOE_SAVED_IN_WORKSPACE) return MOE_ERR_INVALID_ARG;
+  BwdPlan pl;
+  int32_t rc = make_bwd_plan(d, &pl);
+  if (rc) return rc;
+  if (pl.T == 0) return MOE_OK;
+  if (!w || !y || !w->x || !w->W_r || !w->b || !w->W_up || !w->W_down) return MOE_ERR_INVALID_ARG;
+  if (pl.Is && (!w->Ws_up || !w->Ws_down)) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {w->x, w->W_r, w->W_up, w->W_down, w->Ws_up, w->Ws_down, y};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < pl.total || !aligned16(ws)) return MOE_ERR_WORKSPACE;
+  uint8_t* base = (uint8_t*)ws;
+  rc = bwd_activations(pl, w, base, s);
+  if (rc) return rc;
+  const int T = pl.T, H = pl.H, k = pl.k, Is = pl.Is;
+  float* S = nullptr;
+  if (Is) {  // shared expert S = h_s Ws_down^T in fp32 (the dx buffer is free until the backward)
+    S = (float*)(base + pl.dxs);
+    MOE_SPAN("gemm_bf16_f32out:shared_down");
+    MOE_TRY(dense(Elt::BF16, Elt::F32, Epi::Store, base + pl.hs, Is, w->Ws_down, Is, S, H, T, H,
+                  Is, s));
+  }
+  MOE_SPAN("combine:y");
+  MOE_TRY(launch_combine(base + pl.Yp, Elt::BF16, H, S, H, (const int32_t*)(base + pl.pos),
+                         (const float*)(base + pl.gates), T, H, k, y, Elt::BF16, H, s));
+  return hip_status(hipGetLastError());
+}
+
 }  // namespace
 
 extern "C" {
@@ -941,6 +1008,11 @@ int32_t moe_backward_workspace_size(const moe_desc_t* desc, size_t* bytes) {
   if (rc) return rc;
   *bytes = pl.total;
   return MOE_OK;
+}
+
+int32_t moe_layer_forward_train(const moe_desc_t* desc, const moe_weights_t* w, void* y,
+                                void* ws, size_t ws_bytes, void* stream) {
+  return forward_train(desc, w, y, ws, ws_bytes, (hipStream_t)stream);
 }
 
 int32_t moe_layer_backward(const moe_desc_t* desc, const moe_weights_t* w, const void* dy,

@@ -201,3 +201,22 @@ def test_backward_argument_errors_are_reported_before_launch():
     g.dWs_up = None
     assert call(desc(I_shared=64)) == B.MOE_ERR_INVALID_ARG
     assert call(desc(T=0)) == B.MOE_OK                                 # empty: no-op
+
+
+def test_training_forward_and_saved_flag_validation():
+    L = moe.lib()
+    assert bwd_ws(desc(flags=B.SAVED_IN_WORKSPACE))[0] == B.MOE_OK
+    assert ws_size(desc(flags=B.SAVED_IN_WORKSPACE))[0] == B.MOE_ERR_INVALID_ARG  # forward: no
+    w = B.MoeWeights()
+    for n, _ in B.MoeWeights._fields_:
+        setattr(w, n, FAKE.value)
+
+    def ft(d=None, y=FAKE, ws=FAKE, ws_bytes=1 << 40):
+        d = d if d is not None else desc()
+        return L.moe_layer_forward_train(C.byref(d), C.byref(w), y, ws, ws_bytes, None)
+
+    assert ft(y=None) == B.MOE_ERR_INVALID_ARG
+    assert ft(desc(flags=B.SAVED_IN_WORKSPACE)) == B.MOE_ERR_INVALID_ARG
+    assert ft(ws_bytes=16) == B.MOE_ERR_WORKSPACE
+    assert ft(desc(latent=64)) == B.MOE_ERR_UNSUPPORTED
+    assert ft(desc(T=0)) == B.MOE_OK

@@ -174,3 +174,26 @@ def test_backward_full_size(name):
             err = rel_frob(g, r)
             say(f"[gpu]   {name} expert {e} ({len(toks)} tokens) {n}: rel Frobenius {err:.3e}")
             assert err <= TOL[n], (n, e, err)
+
+
+@pytest.mark.parametrize("name", ["bwd_ragged", "bwd_e13_sparse"])
+def test_training_forward_and_saved_backward_match_the_plain_calls(name):
+    # moe_layer_forward_train gives the grouped forward's y bit for bit, and a backward that
+    # reads its saved activations gives the recomputing backward's gradients bit for bit, also
+    # when called twice after one training forward.
+    cfg = CASES[name]
+    inp = mi.make_layer(cfg, seed=9)
+    dev = moe.to_device(inp)
+    dy_dev = moe.to_device({"dy": mi.make_grad_output(cfg, seed=9)})["dy"]
+    y_ref = moe.layer_from(dev, cfg.k, path="grouped")().clone()
+    bw = moe.backward_from(dev, cfg.k)
+    plain = {n: t.clone() for n, t in bw(dy_dev).items()}
+    y = bw.forward_train()
+    first = {n: t.clone() for n, t in bw(dy_dev, saved=True).items()}
+    second = {n: t.clone() for n, t in bw(dy_dev, saved=True).items()}
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
+    for n in plain:
+        assert torch.equal(first[n], plain[n]), n
+        assert torch.equal(second[n], plain[n]), n
+
