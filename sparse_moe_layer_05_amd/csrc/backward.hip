@@ -21,14 +21,8 @@ constexpr int kTile = 64;  // transpose tile: 64 columns x 64 features of bf16
 
 // Column (pair row r or token) -> source row of the transpose, or -1 for a padding column.
 __device__ __forceinline__ int source_row(const TransposeParams& p, int c) {
-  if (!p.koffs) return c < p.R ? c : -1;
-  int lo = 0, hi = p.G - 1;  // group g holds columns [koffs[g], koffs[g+1])
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (p.koffs[mid] <= c) lo = mid; else hi = mid - 1;
-  }
-  const int r = p.offs[lo] + (c - p.koffs[lo]);
-  return r < p.offs[lo + 1] ? r : -1;
+  if (p.cmap) return p.cmap[c];
+  return c < p.R ? c : -1;
 }
 
 // dst[d][c] = src[row(c)][d]: 64 x 64 tiles through LDS, 16-byte loads and stores.
@@ -96,6 +90,25 @@ __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* counts
     acc += (counts[g] + kTile - 1) / kTile * kTile;
     koffs[g + 1] = acc;
   }
+}
+
+// Column map of the per-expert padded layout: cmap[c] = the pair row held by column c, or -1
+// for a padding column. Pair row r of expert g (offs[g] <= r < offs[g + 1]) sits in column
+// koffs[g] + r - offs[g].
+__global__ void column_map_fill_kernel(int32_t* cmap, int n) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c < n) cmap[c] = -1;
+}
+__global__ void column_map_kernel(const int32_t* offs, const int32_t* koffs, int G, int P,
+                                  int32_t* cmap) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= P) return;
+  int lo = 0, hi = G - 1;  // expert holding pair row r: offs[g] <= r < offs[g + 1]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (offs[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  cmap[koffs[lo] + r - offs[lo]] = r;
 }
 
 __device__ __forceinline__ float block_sum(float v, float* red) {
@@ -264,9 +277,20 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* dxs, const flo
 
 }  // namespace
 
+hipError_t launch_column_map(const int32_t* offs, const int32_t* koffs, int G, int P,
+                             int max_cols, int32_t* cmap, hipStream_t s) {
+  if (max_cols <= 0) return hipSuccess;
+  hipLaunchKernelGGL(column_map_fill_kernel, dim3(cdiv(max_cols, 256)), dim3(256), 0, s, cmap,
+                     max_cols);
+  if (P > 0)
+    hipLaunchKernelGGL(column_map_kernel, dim3(cdiv(P, 256)), dim3(256), 0, s, offs, koffs, G, P,
+                       cmap);
+  return hipGetLastError();
+}
+
 hipError_t launch_transpose(const TransposeParams& p, int max_cols, int batch, hipStream_t s) {
   if (max_cols <= 0 || p.Cc <= 0 || batch <= 0) return hipSuccess;
-  if (p.Cc % 8 || p.lds % 8 || p.ldd % 8 || (p.koffs && (!p.offs || p.G < 1)))
+  if (p.Cc % 8 || p.lds % 8 || p.ldd % 8 || (p.koffs && (!p.cmap || p.G < 1)))
     return hipErrorInvalidValue;
   dim3 grid(cdiv(max_cols, kTile), cdiv(p.Cc, kTile), batch);
   hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, s, p);

@@ -113,9 +113,8 @@ hipError_t launch_reduce_slabs(const float* part, int S, int T, int N, int64_t l
 
 // dst[d][c] = src[row(c)][d] for features d < Cc (source columns, destination rows) and
 // destination columns c < ncols, bf16. row(c) is gather[r] when gather is set, else r, where
-//   dense map (koffs null): r = c for c < R; columns R .. ncols-1 are written as zeros;
-//   grouped map: column c of group g (koffs[g] <= c < koffs[g + 1]) is pair row
-//                r = offs[g] + c - koffs[g] while that is below offs[g + 1], else a zero column;
+//   dense map (cmap null): r = c for c < R; columns R .. ncols-1 are written as zeros;
+//   grouped map: r = cmap[c] (launch_column_map), a zero column where that is -1;
 //                ncols = koffs[G].
 // Batches (blockIdx.z) step src and dst by their strides. Cc, lds and ldd are multiples of 8.
 struct TransposeParams {
@@ -127,11 +126,15 @@ struct TransposeParams {
   uint16_t* dst = nullptr;
   int64_t ldd = 0;
   int ncols = 0;
-  const int32_t* offs = nullptr;
+  const int32_t* cmap = nullptr;
   const int32_t* koffs = nullptr;
   int G = 0;
   int64_t src_bstride = 0, dst_bstride = 0;
 };
+// cmap[c] for c < max_cols: the pair row in column c of the per-expert padded layout (pair row r
+// of group g, offs[g] <= r < offs[g + 1], in column koffs[g] + r - offs[g]), -1 elsewhere.
+hipError_t launch_column_map(const int32_t* offs, const int32_t* koffs, int G, int P,
+                             int max_cols, int32_t* cmap, hipStream_t s);
 // max_cols bounds the destination columns (the grid); the kernel reads koffs[G] itself.
 hipError_t launch_transpose(const TransposeParams& p, int max_cols, int batch, hipStream_t s);
 

@@ -527,7 +527,7 @@ struct BwdPlan {
   int T = 0, H = 0, E = 0, k = 0, I = 0, Is = 0, P = 0, Ppad = 0, Tpad = 0;
   int nsplit = 1, kchunk = 0;
   size_t logits = 0, zpart = 0, idx = 0, gates = 0, counts = 0, offsets = 0, perm = 0, pos = 0;
-  size_t dscratch = 0, mt_start = 0, koffs = 0, korder = 0;
+  size_t dscratch = 0, mt_start = 0, koffs = 0, korder = 0, cmap = 0;
   size_t r = 0, h = 0, Yp = 0, hs = 0, rs = 0;                 // recomputed forward
   size_t dYp = 0, dzp = 0, da = 0, du = 0, das = 0, dxs = 0;   // backward intermediates
   size_t wr_part = 0;                                          // dW_r chunk sums
@@ -574,6 +574,7 @@ int32_t make_bwd_plan(const moe_desc_t* d, BwdPlan* out) {
   p.mt_start = take((E + 1) * 4);
   p.koffs = take((E + 1) * 4);
   p.korder = take(E * 4);
+  p.cmap = take((size_t)p.Ppad * 4);
   p.r = take(P * I * 2);
   p.h = take(P * I * 2);
   p.Yp = take(P * H * 2);
@@ -653,6 +654,7 @@ int32_t bwd_activations(const BwdPlan& pl, const moe_weights_t* w, uint8_t* base
     MOE_TRY(launch_dispatch(idx, T, E, k, counts, offsets, perm, pos, (int32_t*)at(pl.dscratch),
                             kGroupBM, mt_start, DispatchExtras(), s));
     MOE_TRY(launch_pad_offsets(counts, E, koffs, korder, s));
+    MOE_TRY(launch_column_map(offsets, koffs, E, P, pl.Ppad, (int32_t*)at(pl.cmap), s));
   }
   // expert activations: relu(a) and h = relu(a)^2 per pair row, then the expert outputs Y
   void* r = at(pl.r);
@@ -806,7 +808,7 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
   {
     MOE_SPAN("transpose:routed_activations");
     TransposeParams t;
-    t.offs = offsets; t.koffs = koffs; t.G = E; t.R = P;
+    t.cmap = (const int32_t*)at(pl.cmap); t.koffs = koffs; t.G = E; t.R = P;
     t.src = dYp; t.lds = H; t.Cc = H; t.dst = dYpT; t.ldd = pl.Ppad;
     MOE_TRY(launch_transpose(t, pl.Ppad, 1, s));
     t.src = (const uint16_t*)h; t.lds = I; t.Cc = I; t.dst = hT;
