@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmoe_mi355x.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["gemm.hip", "routing.hip", "stream.hip", "backward.hip", "moe_api.cpp"]
+SOURCES = ["gemm.hip", "gemm_kt.hip", "routing.hip", "stream.hip", "backward.hip", "moe_api.cpp"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
          # packed fp32 VALU ops stay off (hipcc's host pass reports the feature as unknown)
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

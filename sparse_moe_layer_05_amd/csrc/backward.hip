@@ -1,6 +1,6 @@
-// Non-GEMM kernels of the MoE layer's backward pass (bf16 layers): operand transposes for the
-// data- and weight-gradient products, the gradient through the routing gates, the router weight
-// gradient and the sum that forms dx.
+// Non-GEMM kernels of the MoE layer's backward pass (bf16 layers): the padded per-expert offsets
+// and launch order, the gradient through the routing gates, the router weight gradient, the sum
+// that forms dx, and the gather of token rows into pair order.
 //
 // The gradient is that of the forward of the Nemotron 3 MoE layer ("NVIDIA Nemotron 3: Efficient
 // and Open Intelligence", section 2.2; "Nemotron 3 Nano: Open, Efficient Mixture-of-Experts
@@ -11,70 +11,19 @@
 // section 2.2) only steers the selection and has no gradient.
 #include <cmath>
 
+#include "backward.hpp"
 #include "common.hpp"
+
 #include "kernels.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kTile = 64;  // transpose tile: 64 columns x 64 features of bf16
+constexpr int kTile = 64;  // pair rows per chunk of the router weight gradient
 
-// Column (pair row r or token) -> source row of the transpose, or -1 for a padding column.
-__device__ __forceinline__ int source_row(const TransposeParams& p, int c) {
-  if (p.cmap) return p.cmap[c];
-  return c < p.R ? c : -1;
-}
-
-// dst[d][c] = src[row(c)][d]: 64 x 64 tiles through LDS, 16-byte loads and stores.
-__global__ __launch_bounds__(256) void transpose_kernel(TransposeParams p) {
-  __shared__ uint16_t tile[kTile][kTile + 8];  // [feature][column]; rows of 144 bytes
-  const int ncols = p.koffs ? p.koffs[p.G] : p.ncols;
-  const int c0 = blockIdx.x * kTile, d0 = blockIdx.y * kTile;
-  if (c0 >= ncols) return;
-  const uint16_t* src = p.src + (int64_t)blockIdx.z * p.src_bstride;
-  uint16_t* dst = p.dst + (int64_t)blockIdx.z * p.dst_bstride;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int q = tid + it * 256;
-    const int cl = q >> 3, ch = q & 7;
-    const int c = c0 + cl, d = d0 + ch * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (c < ncols && d < p.Cc) {
-      const int r = source_row(p, c);
-      if (r >= 0) {
-        const int64_t sr = p.gather ? p.gather[r] : r;
-        v = *(const uint4*)(src + sr * p.lds + d);
-      }
-    }
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      tile[ch * 8 + 2 * e][cl] = (uint16_t)(w[e] & 0xFFFF);
-      tile[ch * 8 + 2 * e + 1][cl] = (uint16_t)(w[e] >> 16);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int q = tid + it * 256;
-    const int dl = q >> 3, ch = q & 7;
-    const int d = d0 + dl, c = c0 + ch * 8;
-    if (d >= p.Cc || c >= ncols) continue;
-    const uint16_t* t = &tile[dl][ch * 8];
-    uint16_t* o = dst + (int64_t)d * p.ldd + c;
-    if (c + 8 <= ncols) {
-      *(uint4*)o = make_uint4(t[0] | ((uint32_t)t[1] << 16), t[2] | ((uint32_t)t[3] << 16),
-                              t[4] | ((uint32_t)t[5] << 16), t[6] | ((uint32_t)t[7] << 16));
-    } else {
-      for (int e = 0; c + e < ncols; ++e) o[e] = t[e];
-    }
-  }
-}
-
-// Padded K offsets of the weight-gradient products: koffs[g + 1] = koffs[g] + roundup(counts[g],
-// 64), so every expert's window of the transposed operands starts on a 128-byte boundary; and
-// the experts by descending count (ties: lower index first), the launch order of those products.
+// Chunk numbering of the router weight gradient: koffs[g + 1] = koffs[g] + roundup(counts[g],
+// 64), so expert g owns chunks koffs[g] / 64 .. koffs[g + 1] / 64 - 1; and the experts by
+// descending count (ties: lower index first), the launch order of the weight-gradient products.
 __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* counts, int G,
                                                            int32_t* koffs, int32_t* order) {
   for (int g = threadIdx.x; g < G; g += blockDim.x) {
@@ -90,25 +39,6 @@ __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* counts
     acc += (counts[g] + kTile - 1) / kTile * kTile;
     koffs[g + 1] = acc;
   }
-}
-
-// Column map of the per-expert padded layout: cmap[c] = the pair row held by column c, or -1
-// for a padding column. Pair row r of expert g (offs[g] <= r < offs[g + 1]) sits in column
-// koffs[g] + r - offs[g].
-__global__ void column_map_fill_kernel(int32_t* cmap, int n) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c < n) cmap[c] = -1;
-}
-__global__ void column_map_kernel(const int32_t* offs, const int32_t* koffs, int G, int P,
-                                  int32_t* cmap) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= P) return;
-  int lo = 0, hi = G - 1;  // expert holding pair row r: offs[g] <= r < offs[g + 1]
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (offs[mid] <= r) lo = mid; else hi = mid - 1;
-  }
-  cmap[koffs[lo] + r - offs[lo]] = r;
 }
 
 __device__ __forceinline__ float block_sum(float v, float* red) {
@@ -275,25 +205,22 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* dxs, const flo
   }
 }
 
-}  // namespace
-
-hipError_t launch_column_map(const int32_t* offs, const int32_t* koffs, int G, int P,
-                             int max_cols, int32_t* cmap, hipStream_t s) {
-  if (max_cols <= 0) return hipSuccess;
-  hipLaunchKernelGGL(column_map_fill_kernel, dim3(cdiv(max_cols, 256)), dim3(256), 0, s, cmap,
-                     max_cols);
-  if (P > 0)
-    hipLaunchKernelGGL(column_map_kernel, dim3(cdiv(P, 256)), dim3(256), 0, s, offs, koffs, G, P,
-                       cmap);
-  return hipGetLastError();
+// Xp[p] = x[perm[p]]: one workgroup per pair row, 16-byte copies.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* x, const int32_t* perm,
+                                                          int H, uint16_t* Xp) {
+  const int p = blockIdx.x;
+  const uint4* src = (const uint4*)(x + (int64_t)perm[p] * H);
+  uint4* dst = (uint4*)(Xp + (int64_t)p * H);
+  for (int c = threadIdx.x; c < H / 8; c += 256) dst[c] = src[c];
 }
 
-hipError_t launch_transpose(const TransposeParams& p, int max_cols, int batch, hipStream_t s) {
-  if (max_cols <= 0 || p.Cc <= 0 || batch <= 0) return hipSuccess;
-  if (p.Cc % 8 || p.lds % 8 || p.ldd % 8 || (p.koffs && (!p.cmap || p.G < 1)))
-    return hipErrorInvalidValue;
-  dim3 grid(cdiv(max_cols, kTile), cdiv(p.Cc, kTile), batch);
-  hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, s, p);
+}  // namespace
+
+hipError_t launch_gather_rows(const uint16_t* x, const int32_t* perm, int P, int H, uint16_t* Xp,
+                              hipStream_t s) {
+  if (P <= 0) return hipSuccess;
+  if (H % 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(P), dim3(256), 0, s, x, perm, H, Xp);
   return hipGetLastError();
 }
 

@@ -1,0 +1,335 @@
+// Matrix-core GEMM with K-major operands for the backward pass of the MoE layer (declarations
+// and the layout contract in gemm_kt.hpp).
+//
+// Tile 128 x 192 on 4 waves (2 x 2, 64 x 96 per wave, v_mfma_f32_32x32x16_bf16), two workgroups
+// per CU, two LDS stages of 64 k. Both operand layouts are staged by buffer_load ... lds (global
+// to LDS, 1 KB per instruction, lane l landing at byte 16 l):
+//   K-contiguous rows (A[m][k]): 128 bytes of k per row and stage, 16-byte chunks XOR-swizzled by
+//     (row / 2) % 8, fragments read with ds_read_b128 (as in the forward GEMM);
+//   K-major rows (A[k][m], B[k][n]): 64 rows of k per stage, each holding the tile's 128 or 192
+//     contiguous columns, chunks XOR-swizzled by k % 8. A fragment lane needs 8 consecutive k of
+//     one column; gfx950's transposing read ds_read_b64_tr_b16 provides them. Within each group
+//     of 16 lanes, lane j of the group reads 8 bytes at row k0 + j / 4, column c0 + 4 (j % 4),
+//     and receives column c0 + j at rows k0 .. k0 + 3 (the lane layout was checked on the chip);
+//     two such reads give the 8 k values.
+// Rows of k beyond a K window (the last step of a group) are skipped by the loads and zeroed in
+// LDS; columns beyond M or N read a valid column instead (their outputs are never stored).
+#include "common.hpp"
+#include "gemm_kt.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int BM = 128, BN = 192, NW = 4, WGN = 2, WM = 64, WN = 96, MB = 2, NB = 3;
+constexpr int KS = 64;                  // k per stage
+constexpr int SA = BM * KS * 2, SB = BN * KS * 2;
+constexpr int STAGE = SA + SB;          // 40 KB; two stages
+constexpr int EPW = WN + 4;             // epilogue strip row (floats)
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(uint32_t)n, 0x00020000);
+}
+
+__device__ __forceinline__ int swz_mk(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz_km(int k) { return k & 7; }
+
+__device__ __forceinline__ void unpack8(const uint4 q, float* v) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFF);
+    v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+  }
+}
+
+// Byte offset of element (k, col) of a K-major stage with `pitch` bytes per row of k.
+__device__ __forceinline__ int km_addr(int k, int col, int pitch) {
+  return k * pitch + (((col >> 3) ^ swz_km(k)) << 4) + ((col & 7) << 1);
+}
+
+// The 8 consecutive k (k0 .. k0 + 7 of this lane's 16-lane group) of one fragment column from a
+// K-major stage: `col0` is the group's first column (a multiple of 16), `j` the lane in its group.
+__device__ __forceinline__ bf16x8_t km_frag(const uint8_t* st, int pitch, int col0, int k0, int j) {
+  typedef __attribute__((address_space(3))) v4i16_t lds_v4;
+  const int col = col0 + 4 * (j & 3);
+  const uint8_t* p0 = st + km_addr(k0 + (j >> 2), col, pitch);
+  const uint8_t* p1 = st + km_addr(k0 + 4 + (j >> 2), col, pitch);
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(const void*)p0);
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(const void*)p1);
+  const v8i16_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Tile of this workgroup; false when it has none. kwin: the group's K rows [k0, k0 + kc).
+__device__ __forceinline__ bool kt_tile(const KtParams& p, int& g, int& row0, int& rows, int& n0,
+                                        int& k0, int& kc) {
+  const int nN = cdiv(p.N, BN), nM = cdiv(p.M, BM);
+  k0 = 0;
+  kc = p.K;
+  if (p.kgrp) {  // round robin over the dies, heaviest groups first (their tiles cost most)
+    const int L = blockIdx.x, per = nM * nN;
+    if (L >= p.G * per) return false;
+    const int slot = L / per;
+    g = p.korder ? p.korder[slot] : slot;
+    const int local = L - slot * per;
+    n0 = (local / nM) * BN;
+    row0 = (local % nM) * BM;
+    rows = min(BM, p.M - row0);
+    k0 = p.kgrp[g];
+    kc = p.kgrp[g + 1] - k0;
+    return rows > 0;
+  }
+  const int L = xcd_logical_block(blockIdx.x, gridDim.x);
+  if (p.mt_start) {
+    const int total = p.mt_start[p.G] * nN;
+    if (L >= total) return false;
+    const int key = L / nN;
+    int lo = 0, hi = p.G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.mt_start[mid] <= key) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+    const int mt_g = p.mt_start[g + 1] - p.mt_start[g];
+    const int local = L - p.mt_start[g] * nN;
+    n0 = (local / mt_g) * BN;
+    row0 = p.offs[g] + (local % mt_g) * BM;
+    rows = min(BM, p.offs[g + 1] - row0);
+    return rows > 0;
+  }
+  if (L >= nM * nN) return false;
+  constexpr int GM = 8;
+  const int first = (L / (GM * nN)) * GM;
+  const int gm = min(GM, nM - first);
+  const int within = L - first * nN;
+  g = 0;
+  row0 = (first + within % gm) * BM;
+  n0 = (within / gm) * BN;
+  rows = min(BM, p.M - row0);
+  return rows > 0;
+}
+
+template <int TA, int TB, Elt OUT, Epi EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm_kt_kernel(KtParams p) {
+  static_assert(TB == 1, "B is K-major in every backward product");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  int g, row0, rows, n0, k0, kc;
+  if (!kt_tile(p, g, row0, rows, n0, k0, kc)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  constexpr int A_GRP = TA ? BM * KS * 2 / 1024 / NW : BM / (8 * NW);  // 1-KB loads per wave
+  constexpr int B_GRP = BN * KS * 2 / 1024 / NW;
+  constexpr int PA = BM * 2, PB = BN * 2;                             // K-major pitches
+
+  // Operand resources. K-major operands start at the group's first k row and end after its
+  // last, so a load of a row beyond the window reads nothing.
+  const uint8_t* Bg = (const uint8_t*)p.B + (int64_t)g * p.b_gstride * 2;
+  const __amdgpu_buffer_rsrc_t rb =
+      rsrc(Bg + (int64_t)k0 * p.ldb * 2, (int64_t)kc * p.ldb * 2);
+  const __amdgpu_buffer_rsrc_t ra =
+      TA ? rsrc((const uint8_t*)p.A + (int64_t)k0 * p.lda * 2, (int64_t)kc * p.lda * 2)
+         : rsrc(p.A, (int64_t)p.a_rows * p.lda * 2);
+
+  // Per-lane byte offsets (fixed over the K loop) and, for K-major loads, the lane's k row.
+  uint32_t oa[A_GRP], ob[B_GRP];
+  int ka[A_GRP], kb[B_GRP];
+  const int lrow = lane >> 3, lpos = lane & 7;                        // K-contiguous mapping
+  const int cofs = (lpos ^ swz_mk(wave * 8 + lrow)) << 4;
+#pragma unroll
+  for (int i = 0; i < A_GRP; ++i) {
+    if constexpr (TA) {
+      const int byte = (wave + NW * i) * 1024 + lane * 16;
+      const int kr = byte / PA, slot = (byte % PA) >> 4;
+      int col = row0 + (((slot ^ swz_km(kr))) << 3);
+      col = min(col, p.M - 8);
+      ka[i] = kr;
+      oa[i] = (uint32_t)(kr * p.lda * 2 + col * 2);
+    } else {
+      const int r = (wave + NW * i) * 8 + lrow;
+      const int64_t src = row0 + (r < rows ? r : 0);
+      ka[i] = 0;
+      oa[i] = (uint32_t)(src * p.lda * 2) + cofs;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < B_GRP; ++i) {
+    const int byte = (wave + NW * i) * 1024 + lane * 16;
+    const int kr = byte / PB, slot = (byte % PB) >> 4;
+    int col = n0 + ((slot ^ swz_km(kr)) << 3);
+    col = min(col, p.N - 8);
+    kb[i] = kr;
+    ob[i] = (uint32_t)(kr * p.ldb * 2 + col * 2);
+  }
+
+  const int nk = cdiv(kc, KS);
+  // Issue K-step ks into stage st. Dead lanes (k rows beyond the window; for a K-contiguous A,
+  // chunks beyond K) take an offset outside the buffer and are zeroed by fix_tail.
+  auto issue = [&](int ks, uint8_t* st) {
+    const int left = kc - ks * KS;                 // k rows of this step inside the window
+    const int sa = TA ? ks * KS * (int)p.lda * 2 : ks * KS * 2;
+    const int sb = ks * KS * (int)p.ldb * 2;
+#pragma unroll
+    for (int i = 0; i < A_GRP; ++i) {
+      const bool live = TA ? ka[i] < left : cofs < left * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (__attribute__((address_space(3))) void*)(st + (wave + NW * i) * 1024), 16,
+          (int)(live ? oa[i] : 0xFFFFFFF0u), sa, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < B_GRP; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, (__attribute__((address_space(3))) void*)(st + SA + (wave + NW * i) * 1024), 16,
+          (int)(kb[i] < left ? ob[i] : 0xFFFFFFF0u), sb, 0, 0);
+  };
+  auto fix_tail = [&](int ks, uint8_t* st) {
+    const int left = kc - ks * KS;
+    if (left >= KS) return;  // uniform over the workgroup
+#pragma unroll
+    for (int i = 0; i < A_GRP; ++i)
+      if (TA ? ka[i] >= left : cofs >= left * 2)
+        *(uint4*)(st + (wave + NW * i) * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < B_GRP; ++i)
+      if (kb[i] >= left) *(uint4*)(st + SA + (wave + NW * i) * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+  };
+
+  f32x16_t acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int lg = lane >> 4, lj = lane & 15;   // 16-lane group and lane in it (K-major reads)
+  auto compute = [&](const uint8_t* As) {
+    const uint8_t* Bs = As + SA;
+    bf16x8_t a[2][MB], b[2][NB];
+    auto rd = [&](int s, int buf) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        if constexpr (TA) {
+          a[buf][i] = km_frag(As, PA, wm * WM + i * 32 + 16 * (lg & 1), 16 * s + 8 * (lg >> 1), lj);
+        } else {
+          const int r = wm * WM + i * 32 + (lane & 31);
+          const int ch = 2 * s + (lane >> 5);
+          a[buf][i] = *(const bf16x8_t*)(As + r * 128 + ((ch ^ swz_mk(r)) << 4));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        b[buf][j] = km_frag(Bs, PB, wn * WN + j * 32 + 16 * (lg & 1), 16 * s + 8 * (lg >> 1), lj);
+    };
+    rd(0, 0);
+#pragma unroll
+    for (int s = 0; s < KS / 16; ++s) {
+      if (s < KS / 16 - 1) rd(s + 1, (s + 1) & 1);
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Two stages: K-step ks + 1 is loaded while K-step ks is multiplied.
+  if (nk > 0) issue(0, smem);
+  for (int ks = 0; ks < nk; ++ks) {
+    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));  // vmcnt(0)
+    __syncthreads();
+    uint8_t* cur = smem + (ks & 1) * STAGE;
+    fix_tail(ks, cur);
+    if (ks + 1 < nk) issue(ks + 1, smem + ((ks + 1) & 1) * STAGE);
+    compute(cur);
+  }
+  __syncthreads();  // the epilogue reuses the stages
+
+  // Epilogue (as in the forward GEMM): acc[i][j][r] is C[wm*WM + i*32 + (r/4)*8 + (lane/32)*4 +
+  // r%4][wn*WN + j*32 + lane%32]; 16-row strips go through LDS so each lane finishes 8
+  // consecutive columns of a row.
+  uint8_t* Cg = (uint8_t*)p.C + (p.kgrp ? (int64_t)g * p.c_gstride * (OUT == Elt::F32 ? 4 : 2) : 0);
+  float* ep = (float*)smem + wave * 16 * EPW;
+  constexpr int CG = WN / 8, ITEMS = 16 * CG / 64;
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          const int srow = (rr >> 2) * 8 + (lane >> 5) * 4 + (rr & 3);
+          ep[srow * EPW + j * 32 + (lane & 31)] = acc[i][j][8 * h + rr];
+        }
+#pragma unroll
+      for (int it = 0; it < ITEMS; ++it) {
+        const int item = it * 64 + lane;
+        const int srow = item / CG, cg = item % CG;
+        const int rl = wm * WM + i * 32 + h * 16 + srow;
+        const int col = n0 + wn * WN + cg * 8;
+        if (rl < rows && col < p.N) {
+          const int row = row0 + rl;
+          float v[8];
+          const float4 lo = *(const float4*)(ep + srow * EPW + cg * 8);
+          const float4 hi = *(const float4*)(ep + srow * EPW + cg * 8 + 4);
+          v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+          v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+          if constexpr (EPI == Epi::DSqRelu) {  // d/da relu(a)^2 = 2 relu(a), relu(a) in C2
+            float r[8];
+            unpack8(*(const uint4*)((const uint16_t*)p.C2 + (int64_t)row * p.ldc + col), r);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] *= 2.f * r[q];
+          }
+          if constexpr (OUT == Elt::BF16) {
+            uint32_t w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+            *(uint4*)((uint16_t*)Cg + (int64_t)row * p.ldc + col) = make_uint4(w[0], w[1], w[2], w[3]);
+          } else {
+            float* o = (float*)Cg + (int64_t)row * p.ldc + col;
+            *(float4*)o = make_float4(v[0], v[1], v[2], v[3]);
+            *(float4*)(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int TA, int TB, Elt OUT, Epi EPI>
+hipError_t run_kt(const KtParams& p, int mtiles, hipStream_t s) {
+  const int tiles = mtiles * cdiv(p.N, BN);
+  if (tiles <= 0) return hipSuccess;
+  const int grid = cdiv(tiles, kXcds) * kXcds;
+  hipLaunchKernelGGL((gemm_kt_kernel<TA, TB, OUT, EPI>), dim3(grid), dim3(64 * NW), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_kt(int ta, int tb, Elt out, Epi epi, const KtParams& p, int max_mtiles,
+                          hipStream_t s) {
+  if (tb != 1 || p.M <= 0 || p.N <= 0 || p.N % 8 || p.ldc % 8 || p.ldb % 8 ||
+      (ta && (p.M % 8 || p.lda % 8)) || (!ta && p.K % 8))
+    return hipErrorInvalidValue;
+  if (epi == Epi::DSqRelu && (!p.C2 || out != Elt::BF16)) return hipErrorInvalidValue;
+  const int mt = p.kgrp ? p.G * cdiv(p.M, BM) : (p.mt_start ? max_mtiles : cdiv(p.M, BM));
+  if (ta == 0 && out == Elt::BF16 && epi == Epi::DSqRelu && !p.kgrp)
+    return run_kt<0, 1, Elt::BF16, Epi::DSqRelu>(p, mt, s);
+  if (ta == 0 && out == Elt::F32 && epi == Epi::Store && !p.kgrp)
+    return run_kt<0, 1, Elt::F32, Epi::Store>(p, mt, s);
+  if (ta == 1 && out == Elt::F32 && epi == Epi::Store && !p.mt_start)
+    return run_kt<1, 1, Elt::F32, Epi::Store>(p, mt, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

@@ -109,57 +109,4 @@ hipError_t launch_stream(const StreamParams& p, hipStream_t s);
 hipError_t launch_reduce_slabs(const float* part, int S, int T, int N, int64_t ld, void* out,
                                int64_t ldo, int mode, hipStream_t s);
 
-// ------------------------------------------------------------------ backward pass (bf16)
-
-// dst[d][c] = src[row(c)][d] for features d < Cc (source columns, destination rows) and
-// destination columns c < ncols, bf16. row(c) is gather[r] when gather is set, else r, where
-//   dense map (cmap null): r = c for c < R; columns R .. ncols-1 are written as zeros;
-//   grouped map: r = cmap[c] (launch_column_map), a zero column where that is -1;
-//                ncols = koffs[G].
-// Batches (blockIdx.z) step src and dst by their strides. Cc, lds and ldd are multiples of 8.
-struct TransposeParams {
-  const uint16_t* src = nullptr;
-  int64_t lds = 0;
-  const int32_t* gather = nullptr;
-  int R = 0;
-  int Cc = 0;
-  uint16_t* dst = nullptr;
-  int64_t ldd = 0;
-  int ncols = 0;
-  const int32_t* cmap = nullptr;
-  const int32_t* koffs = nullptr;
-  int G = 0;
-  int64_t src_bstride = 0, dst_bstride = 0;
-};
-// cmap[c] for c < max_cols: the pair row in column c of the per-expert padded layout (pair row r
-// of group g, offs[g] <= r < offs[g + 1], in column koffs[g] + r - offs[g]), -1 elsewhere.
-hipError_t launch_column_map(const int32_t* offs, const int32_t* koffs, int G, int P,
-                             int max_cols, int32_t* cmap, hipStream_t s);
-// max_cols bounds the destination columns (the grid); the kernel reads koffs[G] itself.
-hipError_t launch_transpose(const TransposeParams& p, int max_cols, int batch, hipStream_t s);
-
-// koffs[g + 1] = koffs[g] + roundup(counts[g], 64), koffs[0] = 0; order = the groups by
-// descending count, ties by index.
-hipError_t launch_pad_offsets(const int32_t* counts, int G, int32_t* koffs, int32_t* order,
-                              hipStream_t s);
-
-// Gradient through the routing gates, per token: dg_j = <dy_t, Yp[pos(t,j)]>,
-// dz_j = (dg_j - sum_m g_m dg_m) / Z * s_j (1 - s_j) with s = sigmoid(logits), Z = sum_j s_j;
-// writes dYp[pos(t,j)] = bf16(g_j dy_t) and dzp[pos(t,j)] = dz_j.
-hipError_t launch_bwd_route(const uint16_t* dy, const uint16_t* Yp, const float* logits,
-                            const int32_t* idx, const float* gates, const int32_t* pos, int T,
-                            int H, int E, int k, uint16_t* dYp, float* dzp, hipStream_t s);
-
-// dW_r[e] = sum over expert e's pair rows p (ascending) of dzp[p] x[perm[p]], fp32: sums of
-// 64-row chunks (numbered by koffs / 64, at most max_chunks of them) into part
-// [max_chunks][H], then each expert's chunk sums in order.
-hipError_t launch_bwd_router_weight(const float* dzp, const uint16_t* x, const int32_t* perm,
-                                    const int32_t* offs, const int32_t* koffs, int E, int H,
-                                    int max_chunks, float* part, float* dWr, hipStream_t s);
-
-// dx[t] = dxs[t] (optional) + sum_j du[pos(t,j)] + sum_j dzp[pos(t,j)] W_r[idx(t,j)], fp32.
-hipError_t launch_bwd_dx(const float* dxs, const float* du, const float* dzp, const uint16_t* Wr,
-                         const int32_t* idx, const int32_t* pos, int T, int H, int k, float* dx,
-                         hipStream_t s);
-
 }  // namespace moe

@@ -8,6 +8,8 @@
 #include <mutex>
 
 #include "moe.h"
+#include "backward.hpp"
+#include "gemm_kt.hpp"
 #include "kernels.hpp"
 
 using namespace moe;
@@ -527,13 +529,11 @@ struct BwdPlan {
   int T = 0, H = 0, E = 0, k = 0, I = 0, Is = 0, P = 0, Ppad = 0, Tpad = 0;
   int nsplit = 1, kchunk = 0;
   size_t logits = 0, zpart = 0, idx = 0, gates = 0, counts = 0, offsets = 0, perm = 0, pos = 0;
-  size_t dscratch = 0, mt_start = 0, koffs = 0, korder = 0, cmap = 0;
+  size_t dscratch = 0, mt_start = 0, koffs = 0, korder = 0;
   size_t r = 0, h = 0, Yp = 0, hs = 0, rs = 0;                 // recomputed forward
   size_t dYp = 0, dzp = 0, da = 0, du = 0, das = 0, dxs = 0;   // backward intermediates
   size_t wr_part = 0;                                          // dW_r chunk sums
-  size_t WuT = 0, WdT = 0, WsuT = 0, WsdT = 0;                 // transposed weights
-  size_t dYpT = 0, hT = 0, daT = 0, XpT = 0;                   // [feature][padded pair column]
-  size_t dyT = 0, hsT = 0, dasT = 0, xT = 0;                   // [feature][padded token]
+  size_t Xp = 0;                                               // x rows in pair order
   size_t total = 0;
 };
 
@@ -574,7 +574,6 @@ int32_t make_bwd_plan(const moe_desc_t* d, BwdPlan* out) {
   p.mt_start = take((E + 1) * 4);
   p.koffs = take((E + 1) * 4);
   p.korder = take(E * 4);
-  p.cmap = take((size_t)p.Ppad * 4);
   p.r = take(P * I * 2);
   p.h = take(P * I * 2);
   p.Yp = take(P * H * 2);
@@ -583,37 +582,16 @@ int32_t make_bwd_plan(const moe_desc_t* d, BwdPlan* out) {
   p.wr_part = take((size_t)(p.Ppad / 64) * H * 4);
   p.da = take(P * I * 2);
   p.du = take(P * H * 4);
-  p.WuT = take(E * H * I * 2);
-  p.WdT = take(E * I * H * 2);
-  p.dYpT = take(H * Pp * 2);
-  p.hT = take(I * Pp * 2);
-  p.daT = take(I * Pp * 2);
-  p.XpT = take(H * Pp * 2);
+  p.Xp = take(P * H * 2);
   if (Is) {
     p.hs = take(T * Is * 2);
     p.rs = take(T * Is * 2);
     p.das = take(T * Is * 2);
     p.dxs = take(T * H * 4);
-    p.WsuT = take(H * Is * 2);
-    p.WsdT = take(Is * H * 2);
-    p.dyT = take(H * Tp * 2);
-    p.hsT = take(Is * Tp * 2);
-    p.dasT = take(Is * Tp * 2);
-    p.xT = take(H * Tp * 2);
   }
   p.total = off;
   *out = p;
   return MOE_OK;
-}
-
-// W[b] [rows][cols] -> WT[b] [cols][rows] for `batch` matrices (bf16).
-hipError_t transpose_weights(const void* W, int rows, int cols, int batch, void* WT,
-                             hipStream_t s) {
-  TransposeParams t;
-  t.src = (const uint16_t*)W; t.lds = cols; t.R = rows; t.Cc = cols;
-  t.dst = (uint16_t*)WT; t.ldd = rows; t.ncols = rows;
-  t.src_bstride = (int64_t)rows * cols; t.dst_bstride = (int64_t)rows * cols;
-  return launch_transpose(t, rows, batch, s);
 }
 
 // Routing, dispatch and the expert activations the backward pass reads, into the backward
@@ -654,7 +632,6 @@ int32_t bwd_activations(const BwdPlan& pl, const moe_weights_t* w, uint8_t* base
     MOE_TRY(launch_dispatch(idx, T, E, k, counts, offsets, perm, pos, (int32_t*)at(pl.dscratch),
                             kGroupBM, mt_start, DispatchExtras(), s));
     MOE_TRY(launch_pad_offsets(counts, E, koffs, korder, s));
-    MOE_TRY(launch_column_map(offsets, koffs, E, P, pl.Ppad, (int32_t*)at(pl.cmap), s));
   }
   // expert activations: relu(a) and h = relu(a)^2 per pair row, then the expert outputs Y
   void* r = at(pl.r);
@@ -734,20 +711,7 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
   void* hs = Is ? at(pl.hs) : nullptr;
   void* rs = Is ? at(pl.rs) : nullptr;
 
-  // (2) transposed weights for the data-gradient products (C = A . B^T needs K-contiguous B)
-  void* WuT = at(pl.WuT);
-  void* WdT = at(pl.WdT);
-  {
-    MOE_SPAN("transpose:weights");
-    MOE_TRY(transpose_weights(w->W_up, I, H, E, WuT, s));    // [E][I][H] -> [E][H][I]
-    MOE_TRY(transpose_weights(w->W_down, H, I, E, WdT, s));  // [E][H][I] -> [E][I][H]
-    if (Is) {
-      MOE_TRY(transpose_weights(w->Ws_up, Is, H, 1, at(pl.WsuT), s));    // -> [H][I_s]
-      MOE_TRY(transpose_weights(w->Ws_down, H, Is, 1, at(pl.WsdT), s));  // -> [I_s][H]
-    }
-  }
-
-  // (3) gradient through the gates: dY rows (g_j dy_t) and the logit gradient per pair
+  // (2) gradient through the gates: dY rows (g_j dy_t) and the logit gradient per pair
   uint16_t* dYp = (uint16_t*)at(pl.dYp);
   float* dzp = (float*)at(pl.dzp);
   {
@@ -755,39 +719,43 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
     MOE_TRY(launch_bwd_route((const uint16_t*)dy, (const uint16_t*)Yp, logits, idx, gates, pos,
                              T, H, E, k, dYp, dzp, s));
   }
-  // (4) data gradients: da = (dY W_down[e]) * 2 relu(a), du = da W_up[e]
+  // (3) data gradients, reading the weights as stored (K-major for these products):
+  // da = (dY W_down[e]) * 2 relu(a), du = da W_up[e]; the shared expert's pair likewise
   void* da = at(pl.da);
   float* du = (float*)at(pl.du);
   {
-    GemmParams g;
+    KtParams g;
     g.A = dYp; g.lda = H; g.a_rows = P;
-    g.B = WdT; g.ldb = H; g.b_gstride = (int64_t)I * H;
-    g.C = da; g.C2 = r; g.ldc = I; g.N = I; g.K = H;
+    g.B = w->W_down; g.ldb = I; g.b_gstride = (int64_t)H * I;
+    g.C = da; g.C2 = r; g.ldc = I; g.M = P; g.N = I; g.K = H;
     g.offs = offsets; g.mt_start = mt_start; g.G = E;
-    MOE_SPAN("gemm_bf16_dsqrelu:bwd_routed_dgrad_down");
-    MOE_TRY(launch_gemm(GemmKind{Elt::BF16, Elt::BF16, Epi::DSqRelu}, g, max_mt, s));
+    MOE_SPAN("gemm_kt_dsqrelu:bwd_routed_dgrad_down");
+    MOE_TRY(launch_gemm_kt(0, 1, Elt::BF16, Epi::DSqRelu, g, max_mt, s));
   }
   {
-    GemmParams g;
+    KtParams g;
     g.A = da; g.lda = I; g.a_rows = P;
-    g.B = WuT; g.ldb = I; g.b_gstride = (int64_t)H * I;
-    g.C = du; g.ldc = H; g.N = H; g.K = I;
+    g.B = w->W_up; g.ldb = H; g.b_gstride = (int64_t)I * H;
+    g.C = du; g.ldc = H; g.M = P; g.N = H; g.K = I;
     g.offs = offsets; g.mt_start = mt_start; g.G = E;
-    MOE_SPAN("gemm_bf16_f32out:bwd_routed_dgrad_up");
-    MOE_TRY(launch_gemm(GemmKind{Elt::BF16, Elt::F32, Epi::Store}, g, max_mt, s));
+    MOE_SPAN("gemm_kt_f32out:bwd_routed_dgrad_up");
+    MOE_TRY(launch_gemm_kt(0, 1, Elt::F32, Epi::Store, g, max_mt, s));
   }
   float* dxs = Is ? (float*)at(pl.dxs) : nullptr;
   void* das = Is ? at(pl.das) : nullptr;
   if (Is) {
     {
-      MOE_SPAN("gemm_bf16_dsqrelu:bwd_shared_dgrad_down");
-      GemmParams g;
-      g.A = dy; g.lda = H; g.a_rows = T; g.B = at(pl.WsdT); g.ldb = H; g.C = das; g.C2 = rs;
-      g.ldc = Is; g.M = T; g.N = Is; g.K = H;
-      MOE_TRY(launch_gemm(GemmKind{Elt::BF16, Elt::BF16, Epi::DSqRelu}, g, 0, s));
+      MOE_SPAN("gemm_kt_dsqrelu:bwd_shared_dgrad_down");
+      KtParams g;
+      g.A = dy; g.lda = H; g.a_rows = T; g.B = w->Ws_down; g.ldb = Is;
+      g.C = das; g.C2 = rs; g.ldc = Is; g.M = T; g.N = Is; g.K = H;
+      MOE_TRY(launch_gemm_kt(0, 1, Elt::BF16, Epi::DSqRelu, g, 0, s));
     }
-    MOE_SPAN("gemm_bf16_f32out:bwd_shared_dgrad_up");
-    MOE_TRY(dense(Elt::BF16, Elt::F32, Epi::Store, das, Is, at(pl.WsuT), Is, dxs, H, T, H, Is, s));
+    MOE_SPAN("gemm_kt_f32out:bwd_shared_dgrad_up");
+    KtParams g;
+    g.A = das; g.lda = Is; g.a_rows = T; g.B = w->Ws_up; g.ldb = H;
+    g.C = dxs; g.ldc = H; g.M = T; g.N = H; g.K = Is;
+    MOE_TRY(launch_gemm_kt(0, 1, Elt::F32, Epi::Store, g, 0, s));
   }
   {
     MOE_SPAN("bwd_dx:dx");
@@ -799,68 +767,43 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
                                      pl.Ppad / 64, (float*)at(pl.wr_part), gr->dW_r, s));
   }
 
-  // (5) routed weight gradients over each expert's own pair rows: operands transposed so that
-  // the pair index is the contiguous K, each expert's window padded to a multiple of 64 columns
-  uint16_t* dYpT = (uint16_t*)at(pl.dYpT);
-  uint16_t* hT = (uint16_t*)at(pl.hT);
-  uint16_t* daT = (uint16_t*)at(pl.daT);
-  uint16_t* XpT = (uint16_t*)at(pl.XpT);
+  // (4) routed weight gradients, reduced over each expert's own pair rows (the K window
+  // [offsets[e], offsets[e+1]) of the pair-ordered operands, read as stored), heaviest first
+  uint16_t* Xp = (uint16_t*)at(pl.Xp);
   {
-    MOE_SPAN("transpose:routed_activations");
-    TransposeParams t;
-    t.cmap = (const int32_t*)at(pl.cmap); t.koffs = koffs; t.G = E; t.R = P;
-    t.src = dYp; t.lds = H; t.Cc = H; t.dst = dYpT; t.ldd = pl.Ppad;
-    MOE_TRY(launch_transpose(t, pl.Ppad, 1, s));
-    t.src = (const uint16_t*)h; t.lds = I; t.Cc = I; t.dst = hT;
-    MOE_TRY(launch_transpose(t, pl.Ppad, 1, s));
-    t.src = (const uint16_t*)da; t.dst = daT;
-    MOE_TRY(launch_transpose(t, pl.Ppad, 1, s));
-    t.src = (const uint16_t*)w->x; t.lds = H; t.Cc = H; t.gather = perm; t.dst = XpT;
-    MOE_TRY(launch_transpose(t, pl.Ppad, 1, s));
+    MOE_SPAN("gather_rows:x");
+    MOE_TRY(launch_gather_rows((const uint16_t*)w->x, perm, P, H, Xp, s));
   }
   {
-    GemmParams g;  // dW_down[e] [H][I] = dY_e^T h_e
-    g.A = dYpT; g.lda = pl.Ppad; g.a_rows = H; g.B = hT; g.ldb = pl.Ppad;
-    g.C = gr->dW_down; g.ldc = I; g.M = H; g.N = I; g.G = E; g.koffs = koffs; g.korder = korder;
-    g.c_gstride = (int64_t)H * I;
-    MOE_SPAN("gemm_bf16_f32out:bwd_routed_wgrad_down");
-    MOE_TRY(launch_gemm(GemmKind{Elt::BF16, Elt::F32, Epi::Store}, g, 0, s));
+    KtParams g;  // dW_down[e] [H][I] = dY_e^T h_e
+    g.A = dYp; g.lda = H; g.B = h; g.ldb = I;
+    g.C = gr->dW_down; g.ldc = I; g.c_gstride = (int64_t)H * I;
+    g.M = H; g.N = I; g.G = E; g.kgrp = offsets; g.korder = korder;
+    MOE_SPAN("gemm_kt_f32out:bwd_routed_wgrad_down");
+    MOE_TRY(launch_gemm_kt(1, 1, Elt::F32, Epi::Store, g, 0, s));
   }
   {
-    GemmParams g;  // dW_up[e] [I][H] = da_e^T x_e
-    g.A = daT; g.lda = pl.Ppad; g.a_rows = I; g.B = XpT; g.ldb = pl.Ppad;
-    g.C = gr->dW_up; g.ldc = H; g.M = I; g.N = H; g.G = E; g.koffs = koffs; g.korder = korder;
-    g.c_gstride = (int64_t)I * H;
-    MOE_SPAN("gemm_bf16_f32out:bwd_routed_wgrad_up");
-    MOE_TRY(launch_gemm(GemmKind{Elt::BF16, Elt::F32, Epi::Store}, g, 0, s));
+    KtParams g;  // dW_up[e] [I][H] = da_e^T x_e
+    g.A = da; g.lda = I; g.B = Xp; g.ldb = H;
+    g.C = gr->dW_up; g.ldc = H; g.c_gstride = (int64_t)I * H;
+    g.M = I; g.N = H; g.G = E; g.kgrp = offsets; g.korder = korder;
+    MOE_SPAN("gemm_kt_f32out:bwd_routed_wgrad_up");
+    MOE_TRY(launch_gemm_kt(1, 1, Elt::F32, Epi::Store, g, 0, s));
   }
-  // (6) shared expert's weight gradients over all tokens (token columns padded with zeros)
+  // (5) the shared expert's weight gradients over all tokens
   if (Is) {
-    uint16_t* dyT = (uint16_t*)at(pl.dyT);
-    uint16_t* hsT = (uint16_t*)at(pl.hsT);
-    uint16_t* dasT = (uint16_t*)at(pl.dasT);
-    uint16_t* xT = (uint16_t*)at(pl.xT);
     {
-      MOE_SPAN("transpose:shared_activations");
-      TransposeParams t;
-      t.R = T; t.ncols = pl.Tpad;
-      t.src = (const uint16_t*)dy; t.lds = H; t.Cc = H; t.dst = dyT; t.ldd = pl.Tpad;
-      MOE_TRY(launch_transpose(t, pl.Tpad, 1, s));
-      t.src = (const uint16_t*)hs; t.lds = Is; t.Cc = Is; t.dst = hsT;
-      MOE_TRY(launch_transpose(t, pl.Tpad, 1, s));
-      t.src = (const uint16_t*)das; t.dst = dasT;
-      MOE_TRY(launch_transpose(t, pl.Tpad, 1, s));
-      t.src = (const uint16_t*)w->x; t.lds = H; t.Cc = H; t.dst = xT;
-      MOE_TRY(launch_transpose(t, pl.Tpad, 1, s));
+      MOE_SPAN("gemm_kt_f32out:bwd_shared_wgrad_down");
+      KtParams g;  // dWs_down [H][I_s] = dy^T h_s
+      g.A = dy; g.lda = H; g.B = hs; g.ldb = Is;
+      g.C = gr->dWs_down; g.ldc = Is; g.M = H; g.N = Is; g.K = T;
+      MOE_TRY(launch_gemm_kt(1, 1, Elt::F32, Epi::Store, g, 0, s));
     }
-    {
-      MOE_SPAN("gemm_bf16_f32out:bwd_shared_wgrad_down");
-      MOE_TRY(dense(Elt::BF16, Elt::F32, Epi::Store, dyT, pl.Tpad, hsT, pl.Tpad, gr->dWs_down, Is,
-                    H, Is, pl.Tpad, s));
-    }
-    MOE_SPAN("gemm_bf16_f32out:bwd_shared_wgrad_up");
-    MOE_TRY(dense(Elt::BF16, Elt::F32, Epi::Store, dasT, pl.Tpad, xT, pl.Tpad, gr->dWs_up, H, Is,
-                  H, pl.Tpad, s));
+    MOE_SPAN("gemm_kt_f32out:bwd_shared_wgrad_up");
+    KtParams g;  // dWs_up [I_s][H] = da_s^T x
+    g.A = das; g.lda = Is; g.B = w->x; g.ldb = H;
+    g.C = gr->dWs_up; g.ldc = H; g.M = Is; g.N = H; g.K = T;
+    MOE_TRY(launch_gemm_kt(1, 1, Elt::F32, Epi::Store, g, 0, s));
   }
   return hip_status(hipGetLastError());
 }
