@@ -69,8 +69,7 @@ def work_of(name, cfg, counts, stream=False):
         return touched * rows * 4 if narrow else 0
 
     role = name.split(":")[1]
-    if role.startswith("bwd_") or role in ("weights", "routed_activations",
-                                           "shared_activations", "gates", "dx", "dW_r"):
+    if role.startswith("bwd_") or role in ("pairs", "gates", "dx", "dW_r"):
         return backward_work(role, cfg, touched)
     if role == "router":
         return 2 * T * E * H, T * H * ea + E * H * ea + T * E * 4
@@ -125,7 +124,7 @@ def backward_work(role, cfg, touched):
         "bwd_routed_up": (2 * P * I * H, wt + T * H * 2 + 2 * P * I * 2),
         "bwd_routed_down": (2 * P * H * I, wt + P * I * 2 + P * H * 2),
         "bwd_shared_up": (2 * T * Is * H, Is * H * 2 + T * H * 2 + 2 * T * Is * 2),
-        # data gradients (transposed weights; the squared ReLU's derivative fused)
+        # data gradients (weights read as stored; the squared ReLU's derivative fused)
         "bwd_routed_dgrad_down": (2 * P * I * H, wt + P * H * 2 + 2 * P * I * 2),
         "bwd_routed_dgrad_up": (2 * P * H * I, wt + P * I * 2 + P * H * 4),
         "bwd_shared_dgrad_down": (2 * T * Is * H, Is * H * 2 + T * H * 2 + 2 * T * Is * 2),
@@ -139,12 +138,8 @@ def backward_work(role, cfg, touched):
     if role in gemm:
         f, b = gemm[role]
         return f, int(b)
-    if role == "weights":             # transposed copies of both stacks (+ shared): read + write
-        return 0, 2 * (2 * E * I * H * 2 + (2 * Is * H * 2 if Is else 0))
-    if role == "routed_activations":  # dY, h, da, gathered x: read and written once each
-        return 0, 2 * (2 * P * H * 2 + 2 * P * I * 2)
-    if role == "shared_activations":
-        return 0, 2 * (2 * T * H * 2 + 2 * T * Is * 2)
+    if role == "pairs":               # x rows gathered into pair order
+        return 0, 2 * P * H * 2
     if role == "gates":               # dy, Y rows in; g*dy rows and dz out
         return 2 * P * H, T * H * 2 + P * H * 2 + P * H * 2 + P * 4
     if role == "dx":

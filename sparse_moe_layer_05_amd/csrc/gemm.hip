@@ -50,24 +50,6 @@ template <int BM, int BN>
 __device__ __forceinline__ bool tile_of(const GemmParams& p, int& g, int& row0, int& rows,
                                         int& n0) {
   const int nN = cdiv(p.N, BN);
-  if (p.koffs) {
-    // One M x N product per group, M-tiles fastest. A tile's cost grows with its group's K (an
-    // expert's token count), so the tiles are dealt round robin over the dies (block b runs on
-    // die b % 8): every expert's tiles spread over all of them. Its operand panels, re-read by
-    // several dies, are served by the shared Infinity Cache. With korder the groups go heaviest
-    // first, so that the longest tiles do not start last.
-    const int L = blockIdx.x;
-    const int nM = cdiv(p.M, BM);
-    const int per = nM * nN;
-    if (L >= p.G * per) return false;
-    const int slot = L / per;
-    g = p.korder ? p.korder[slot] : slot;
-    const int local = L - slot * per;
-    n0 = (local / nM) * BN;
-    row0 = (local % nM) * BM;
-    rows = min(BM, p.M - row0);
-    return rows > 0;
-  }
   const int L = xcd_logical_block(blockIdx.x, gridDim.x);
   if (p.mt_start) {
     const int total = p.mt_start[p.G] * nN;
@@ -144,15 +126,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
 
   int g, row0, rows, n0;
   if (!tile_of<BM, BN>(p, g, row0, rows, n0)) return;
-  if (p.koffs) {  // this group's K window of both operands, and its output matrix
-    const int k0 = p.koffs[g];
-    p.K = p.koffs[g + 1] - k0;
-    kshift = (int64_t)k0 * EltBytes<AB>::v;
-    p.A = (const uint8_t*)p.A + kshift;
-    p.B = (const uint8_t*)p.B + kshift;
-    p.C = (uint8_t*)p.C + g * p.c_gstride * EltBytes<OUT>::v;
-    g = 0;  // the operands are shared: no per-group B panel
-  }
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -408,12 +381,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
 #pragma unroll
             for (int q = 0; q < 8; ++q) v[q] = sqrelu(v[q]);
           }
-          if constexpr (EPI == Epi::DSqRelu) {  // d/da relu(a)^2 = 2 relu(a), relu(a) saved in C2
-            float r[8];
-            unpack8(*(const uint4*)((const uint16_t*)p.C2 + (int64_t)row * p.ldc + col), r);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] *= 2.f * r[q];
-          }
           // 16-byte stores when the 8 columns lie inside N on an aligned row; else (N or ldc
           // not a multiple of 8, e.g. router logits of E experts) element by element
           const bool whole = col + 8 <= p.N && p.ldc % 8 == 0;
@@ -559,13 +526,7 @@ hipError_t launch_gemm(const GemmKind& k, const GemmParams& p, int max_mtiles, h
   }
   constexpr int GB = kGroupBM;
   if (k.ab == Elt::BF16) {
-    if (p.koffs) {  // weight gradients: one product per group over its K window
-      if (k.out != Elt::F32 || k.epi != Epi::Store || p.ksplit > 1) return hipErrorInvalidValue;
-      return run_mfma<GB, 192, 2, 2, 2, Elt::BF16, Elt::F32, Epi::Store>(
-          p, p.G * cdiv(p.M, GB), s);
-    }
-    if ((k.epi == Epi::SqReluSave || k.epi == Epi::DSqRelu) &&
-        (!p.C2 || k.out != Elt::BF16 || p.N % 8 || p.ldc % 8))
+    if (k.epi == Epi::SqReluSave && (!p.C2 || k.out != Elt::BF16 || p.N % 8 || p.ldc % 8))
       return hipErrorInvalidValue;
     if (grouped) {
       // 128 x 192 tiles on 4 waves, two workgroups per CU: the fastest routed shape measured
@@ -575,10 +536,6 @@ hipError_t launch_gemm(const GemmKind& k, const GemmParams& p, int max_mtiles, h
         return run_mfma<GB, 192, 2, 2, 2, Elt::BF16, Elt::BF16, Epi::Store>(p, max_mtiles, s);
       if (k.out == Elt::BF16 && k.epi == Epi::SqReluSave)
         return run_mfma<GB, 192, 2, 2, 2, Elt::BF16, Elt::BF16, Epi::SqReluSave>(p, max_mtiles, s);
-      if (k.out == Elt::BF16 && k.epi == Epi::DSqRelu)
-        return run_mfma<GB, 192, 2, 2, 2, Elt::BF16, Elt::BF16, Epi::DSqRelu>(p, max_mtiles, s);
-      if (k.out == Elt::F32 && k.epi == Epi::Store)
-        return run_mfma<GB, 192, 2, 2, 2, Elt::BF16, Elt::F32, Epi::Store>(p, max_mtiles, s);
       return hipErrorInvalidValue;
     }
     if (k.out == Elt::F32 && k.epi == Epi::Store) return run_dense_bf16<Elt::F32, Epi::Store>(p, s);
@@ -587,8 +544,6 @@ hipError_t launch_gemm(const GemmKind& k, const GemmParams& p, int max_mtiles, h
     if (p.ksplit > 1) return hipErrorInvalidValue;
     if (k.out == Elt::BF16 && k.epi == Epi::SqReluSave)
       return run_dense_bf16<Elt::BF16, Epi::SqReluSave>(p, s);
-    if (k.out == Elt::BF16 && k.epi == Epi::DSqRelu)
-      return run_dense_bf16<Elt::BF16, Epi::DSqRelu>(p, s);
     return hipErrorInvalidValue;
   }
   if (k.ab == Elt::FP8 && grouped && k.out == Elt::BF16) {

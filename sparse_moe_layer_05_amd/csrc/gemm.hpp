@@ -19,6 +19,7 @@ enum class Epi : int {
   SqRelu = 1,       // C = relu(acc)^2
   SqReluSave = 2,   // C = relu(acc)^2 and C2 = relu(acc) (the factor the backward pass needs)
   DSqRelu = 3       // C = acc * 2 * C2: the squared ReLU's derivative at the saved relu(a)
+                    // (backward products only, gemm_kt.hpp)
 };
 
 struct GemmParams {
@@ -41,7 +42,7 @@ struct GemmParams {
   const void* B2 = nullptr;
   int64_t ldb2 = 0;
   int K2 = 0;
-  // Output; C2 is the second matrix of the SqReluSave / DSqRelu epilogues (same shape, ldc)
+  // Output; C2 is the second matrix of the SqReluSave epilogue (same shape, ldc)
   void* C = nullptr;
   int64_t ldc = 0;
   void* C2 = nullptr;
@@ -54,12 +55,6 @@ struct GemmParams {
   const int32_t* offs = nullptr;      // [G + 1] row offsets
   const int32_t* mt_start = nullptr;  // [G + 1] prefix of ceil(rows_g / BM)
   int G = 0;
-  // K-grouped launches (weight gradients): group g reduces over K columns
-  // [koffs[g], koffs[g + 1]) of both operands (multiples of 64) and writes its M x N product to
-  // C + g * c_gstride. M, N and the operands are shared by the groups; K is unused.
-  const int32_t* koffs = nullptr;
-  int64_t c_gstride = 0;
-  const int32_t* korder = nullptr;  // optional: the groups in launch order (heaviest first)
 };
 
 struct GemmKind {

@@ -771,7 +771,7 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
   // [offsets[e], offsets[e+1]) of the pair-ordered operands, read as stored), heaviest first
   uint16_t* Xp = (uint16_t*)at(pl.Xp);
   {
-    MOE_SPAN("gather_rows:x");
+    MOE_SPAN("gather_rows:pairs");
     MOE_TRY(launch_gather_rows((const uint16_t*)w->x, perm, P, H, Xp, s));
   }
   {
