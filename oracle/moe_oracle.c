@@ -411,11 +411,12 @@ typedef struct {
   double *dW_r, *dW_up, *dW_down, *dWs_up, *dWs_down;
   int32_t expert;
   int32_t pad_;
+  double *dW_in, *dW_out; /* LatentMoE: [l][H] and [H][l] */
 } orc_grads;
 
-/* Backward pass of the plain MoE layer (no latent projections) for the listed tokens (all T if
- * tokens is NULL), given the selection idx the forward made (one row of k per listed token) and
- * the gradient dy of a scalar loss with respect to y (one row of H per listed token).
+/* Backward pass of the MoE layer for the listed tokens (all T if tokens is NULL), given the
+ * selection idx the forward made (one row of k per listed token) and the gradient dy of a scalar
+ * loss with respect to y (one row of H per listed token).
  *
  * The selection is piecewise constant in the inputs, so it is held fixed and the gradient flows
  * through the gate weights only: with s_j = sigmoid(z_{e_j}), Z = sum_j s_j and g_j = s_j / Z
@@ -428,20 +429,29 @@ typedef struct {
  *   dx += sum_j dz_{e_j} W_r[e_j],  dW_r[e_j] += dz_{e_j} x;
  *   shared expert (weight 1): a_s = Ws_up x, r_s = max(a_s, 0), dh_s = Ws_down^T dy,
  *   da_s = 2 r_s (.) dh_s, dx += Ws_up^T da_s, dWs_down += dy h_s^T, dWs_up += da_s x^T.
+ * LatentMoE [N3W 2.2]: the routed experts read u = W_in x and their gated sum acc (width l)
+ * leaves through y = W_out acc, so the experts see dacc = W_out^T dy in place of dy and u in place
+ * of x; dW_out += dy acc^T; their input gradient du reaches x through dx += W_in^T du, and
+ * dW_in += du x^T. The router and the shared expert read x in H as in the plain layer.
  * The derivative of the squared ReLU is taken as 2 max(a, 0), which is 0 at a = 0.
  * dx is [n][H] and dz [n][E] per listed token (either may be NULL). */
 int orc_backward_tokens(const orc_layer *L, const int32_t *tokens, int32_t n, const int32_t *idx,
                         const double *dy, double *dx, double *dz, const orc_grads *G) {
-  if (!L || !idx || !dy || L->latent || L->k < 1 || L->k > ORC_EMAX) return ORC_EINVAL;
-  const int32_t H = L->H, I = L->I, Is = L->I_shared, E = L->E, k = L->k;
+  if (!L || !idx || !dy || L->k < 1 || L->k > ORC_EMAX) return ORC_EINVAL;
+  const int32_t H = L->H, I = L->I, Is = L->I_shared, E = L->E, k = L->k, Lw = L->latent;
+  const int32_t D = Lw ? Lw : H;
   const int32_t Imax = I > Is ? I : Is;
   double *r = (double *)malloc(sizeof(double) * (size_t)Imax);
   double *dh = (double *)malloc(sizeof(double) * (size_t)Imax);
-  double *Y = (double *)malloc(sizeof(double) * (size_t)H);
+  double *Y = (double *)malloc(sizeof(double) * (size_t)D);
   double *gx = (double *)malloc(sizeof(double) * (size_t)H);
+  double *u = (double *)malloc(sizeof(double) * (size_t)D);    /* expert input (x or W_in x) */
+  double *ge = (double *)malloc(sizeof(double) * (size_t)D);   /* gradient reaching the experts */
+  double *gu = (double *)malloc(sizeof(double) * (size_t)D);   /* gradient of u */
+  double *acc = (double *)malloc(sizeof(double) * (size_t)D);  /* latent: gated expert sum */
   double s[ORC_EMAX], g[ORC_EMAX], dg[ORC_EMAX];
   int rc = ORC_OK;
-  if (!r || !dh || !Y || !gx) { rc = ORC_EINVAL; goto done; }
+  if (!r || !dh || !Y || !gx || !u || !ge || !gu || !acc) { rc = ORC_EINVAL; goto done; }
   int32_t cnt = tokens ? n : L->T;
   for (int32_t a = 0; a < cnt; ++a) {
     const int32_t t = tokens ? tokens[a] : a;
@@ -458,41 +468,75 @@ int orc_backward_tokens(const orc_layer *L, const int32_t *tokens, int32_t n, co
       Z += s[j];
     }
     for (int32_t j = 0; j < k; ++j) g[j] = s[j] / Z;
+    /* expert input u and the gradient reaching the experts' gated sum */
+    for (int32_t d = 0; d < D; ++d) {
+      double a = 0.0;
+      if (Lw)
+        for (int32_t c = 0; c < H; ++c) a += at(&L->W_in, d, c) * at(&L->x, t, c);
+      else
+        a = at(&L->x, t, d);
+      u[d] = a;
+      gu[d] = 0.0;
+      acc[d] = 0.0;
+      double e = 0.0;
+      if (Lw)
+        for (int32_t c = 0; c < H; ++c) e += at(&L->W_out, c, d) * dyt[c];
+      else
+        e = dyt[d];
+      ge[d] = e;
+    }
     /* routed experts */
     for (int32_t j = 0; j < k; ++j) {
       const int32_t e = it[j];
       const int want_w = G && (G->expert < 0 || G->expert == e);
       const int64_t ew = G && G->expert >= 0 ? 0 : e; /* row block of e in the dW arrays */
       for (int32_t i = 0; i < I; ++i) {
-        double acc = 0.0;
-        for (int32_t c = 0; c < H; ++c) acc += at(&L->W_up, (int64_t)e * I + i, c) * at(&L->x, t, c);
-        r[i] = acc > 0.0 ? acc : 0.0;
+        double a = 0.0;
+        for (int32_t d = 0; d < D; ++d) a += at(&L->W_up, (int64_t)e * I + i, d) * u[d];
+        r[i] = a > 0.0 ? a : 0.0;
       }
       dg[j] = 0.0;
-      for (int32_t c = 0; c < H; ++c) {
-        double acc = 0.0;
-        for (int32_t i = 0; i < I; ++i) acc += at(&L->W_down, (int64_t)e * H + c, i) * (r[i] * r[i]);
-        Y[c] = acc;
-        dg[j] += dyt[c] * acc;
+      for (int32_t d = 0; d < D; ++d) {
+        double a = 0.0;
+        for (int32_t i = 0; i < I; ++i) a += at(&L->W_down, (int64_t)e * D + d, i) * (r[i] * r[i]);
+        Y[d] = a;
+        acc[d] += g[j] * a;
+        dg[j] += ge[d] * a;
       }
       for (int32_t i = 0; i < I; ++i) {
-        double acc = 0.0;
-        for (int32_t c = 0; c < H; ++c) acc += at(&L->W_down, (int64_t)e * H + c, i) * (g[j] * dyt[c]);
-        dh[i] = 2.0 * r[i] * acc; /* da */
+        double a = 0.0;
+        for (int32_t d = 0; d < D; ++d) a += at(&L->W_down, (int64_t)e * D + d, i) * (g[j] * ge[d]);
+        dh[i] = 2.0 * r[i] * a; /* da */
       }
-      for (int32_t c = 0; c < H; ++c) {
-        double acc = 0.0;
-        for (int32_t i = 0; i < I; ++i) acc += at(&L->W_up, (int64_t)e * I + i, c) * dh[i];
-        gx[c] += acc;
+      for (int32_t d = 0; d < D; ++d) {
+        double a = 0.0;
+        for (int32_t i = 0; i < I; ++i) a += at(&L->W_up, (int64_t)e * I + i, d) * dh[i];
+        gu[d] += a;
       }
       if (want_w && G->dW_down)
-        for (int32_t c = 0; c < H; ++c)
+        for (int32_t d = 0; d < D; ++d)
           for (int32_t i = 0; i < I; ++i)
-            G->dW_down[(ew * H + c) * I + i] += g[j] * dyt[c] * (r[i] * r[i]);
+            G->dW_down[(ew * D + d) * I + i] += g[j] * ge[d] * (r[i] * r[i]);
       if (want_w && G->dW_up)
         for (int32_t i = 0; i < I; ++i)
-          for (int32_t c = 0; c < H; ++c)
-            G->dW_up[(ew * I + i) * H + c] += dh[i] * at(&L->x, t, c);
+          for (int32_t d = 0; d < D; ++d)
+            G->dW_up[(ew * I + i) * D + d] += dh[i] * u[d];
+    }
+    /* back to x: directly, or through the latent projections */
+    if (Lw) {
+      for (int32_t c = 0; c < H; ++c) {
+        double a = 0.0;
+        for (int32_t d = 0; d < D; ++d) a += at(&L->W_in, d, c) * gu[d];
+        gx[c] += a;
+      }
+      if (G && G->dW_in)
+        for (int32_t d = 0; d < D; ++d)
+          for (int32_t c = 0; c < H; ++c) G->dW_in[(int64_t)d * H + c] += gu[d] * at(&L->x, t, c);
+      if (G && G->dW_out)
+        for (int32_t c = 0; c < H; ++c)
+          for (int32_t d = 0; d < D; ++d) G->dW_out[(int64_t)c * D + d] += dyt[c] * acc[d];
+    } else {
+      for (int32_t c = 0; c < H; ++c) gx[c] += gu[c];
     }
     /* router: through the renormalised gates and the sigmoid */
     double gdg = 0.0;
@@ -532,6 +576,6 @@ int orc_backward_tokens(const orc_layer *L, const int32_t *tokens, int32_t n, co
       for (int32_t c = 0; c < H; ++c) dx[(int64_t)a * H + c] = gx[c];
   }
 done:
-  free(r); free(dh); free(Y); free(gx);
+  free(r); free(dh); free(Y); free(gx); free(u); free(ge); free(gu); free(acc);
   return rc;
 }

@@ -44,7 +44,7 @@ class OrcMat(C.Structure):
 class OrcGrads(C.Structure):
     _fields_ = [("dW_r", C.c_void_p), ("dW_up", C.c_void_p), ("dW_down", C.c_void_p),
                 ("dWs_up", C.c_void_p), ("dWs_down", C.c_void_p), ("expert", C.c_int32),
-                ("pad_", C.c_int32)]
+                ("pad_", C.c_int32), ("dW_in", C.c_void_p), ("dW_out", C.c_void_p)]
 
 
 class OrcLayer(C.Structure):
@@ -251,7 +251,7 @@ def forward(inp: dict, tokens=None, fp8_emulate: bool = False, threads: int = 1)
     return dict(logits=z, idx=idx, gates=g, margin=m, y=y)
 
 
-GRAD_NAMES = ("dx", "dz", "dW_r", "dW_up", "dW_down", "dWs_up", "dWs_down")
+GRAD_NAMES = ("dx", "dz", "dW_r", "dW_up", "dW_down", "dWs_up", "dWs_down", "dW_in", "dW_out")
 
 
 def backward(inp: dict, idx: np.ndarray, dy: np.ndarray, tokens=None, want=GRAD_NAMES,
@@ -261,12 +261,10 @@ def backward(inp: dict, idx: np.ndarray, dy: np.ndarray, tokens=None, want=GRAD_
 
     Returns the requested names of GRAD_NAMES: dx [n, H] and dz [n, E] per listed token; weight
     gradients summed over the listed tokens, dW_up / dW_down for one expert only when
-    ``expert`` >= 0. ``threads`` > 1 splits the tokens over threads and adds their weight
+    ``expert`` >= 0; dW_in / dW_out for a LatentMoE layer. ``threads`` > 1 splits the tokens over threads and adds their weight
     gradients afterwards (float64 sums, so the order of that final addition may differ from a
     single call in the last bits)."""
     cfg = inp["config"]
-    if cfg.latent:
-        raise ValueError("the backward oracle covers the plain MoE layer only")
     t_all = np.arange(cfg.T, dtype=np.int32) if tokens is None else \
         np.ascontiguousarray(tokens, dtype=np.int32)
     n = len(t_all)
@@ -283,15 +281,16 @@ def backward(inp: dict, idx: np.ndarray, dy: np.ndarray, tokens=None, want=GRAD_
             out[k] = np.concatenate([p[k] for p in parts]) if k in ("dx", "dz") else \
                 sum(p[k] for p in parts)
         return out
-    H, E, I, Is = cfg.H, cfg.E, cfg.I, cfg.I_shared
+    H, E, I, Is, Lw, D = cfg.H, cfg.E, cfg.I, cfg.I_shared, cfg.latent, cfg.D
     shapes = {"dx": (n, H), "dz": (n, E), "dW_r": (E, H),
-              "dW_up": (I, H) if expert >= 0 else (E, I, H),
-              "dW_down": (H, I) if expert >= 0 else (E, H, I),
-              "dWs_up": (Is, H), "dWs_down": (H, Is)}
+              "dW_up": (I, D) if expert >= 0 else (E, I, D),
+              "dW_down": (D, I) if expert >= 0 else (E, D, I),
+              "dWs_up": (Is, H), "dWs_down": (H, Is), "dW_in": (Lw, H), "dW_out": (H, Lw)}
     out = {k: np.zeros(shapes[k], np.float64) for k in want
-           if k in shapes and not (k.startswith("dWs") and not Is)}
+           if k in shapes and not (k.startswith("dWs") and not Is)
+           and not (k in ("dW_in", "dW_out") and not Lw)}
     G = OrcGrads()
-    for k in ("dW_r", "dW_up", "dW_down", "dWs_up", "dWs_down"):
+    for k in ("dW_r", "dW_up", "dW_down", "dWs_up", "dWs_down", "dW_in", "dW_out"):
         setattr(G, k, out[k].ctypes.data if k in out else None)
     G.expert = expert
     L, keep = layer(inp)

@@ -440,25 +440,31 @@ def test_bias_update_sign_rule():
 
 # ----------------------------------------------------------------------------- backward
 
-_WEIGHTS = ("x", "W_r", "W_up", "W_down", "Ws_up", "Ws_down")
+_WEIGHTS = ("x", "W_r", "W_up", "W_down", "Ws_up", "Ws_down", "W_in", "W_out")
 _GRAD_OF = {"x": "dx", "W_r": "dW_r", "W_up": "dW_up", "W_down": "dW_down", "Ws_up": "dWs_up",
-            "Ws_down": "dWs_down"}
+            "Ws_down": "dWs_down", "W_in": "dW_in", "W_out": "dW_out"}
 
 
-def f64_layer(seed, T=3, H=8, E=5, k=2, I=6, Is=4):
+def f64_layer(seed, T=3, H=8, E=5, k=2, I=6, Is=4, latent=0):
     """A tiny layer held in float64 (read exactly by the oracle), with pre-activations kept away
     from the squared-ReLU's kink so that central differences never straddle it."""
-    c = cfg(T=T, H=H, E=E, k=k, I=I, I_shared=Is)
+    c = cfg(T=T, H=H, E=E, k=k, I=I, I_shared=Is, latent=latent)
+    D = latent or H
     rng = np.random.default_rng(seed)
     inp = {"config": c, "x": rng.standard_normal((T, H)),
            "W_r": rng.standard_normal((E, H)) / np.sqrt(H),
            "b": rng.uniform(-0.1, 0.1, E).astype(np.float32),
-           "W_up": rng.standard_normal((E, I, H)) / np.sqrt(H),
-           "W_down": rng.standard_normal((E, H, I)) / np.sqrt(I)}
+           "W_up": rng.standard_normal((E, I, D)) / np.sqrt(D),
+           "W_down": rng.standard_normal((E, D, I)) / np.sqrt(I)}
     if Is:
         inp["Ws_up"] = rng.standard_normal((Is, H)) / np.sqrt(H)
         inp["Ws_down"] = rng.standard_normal((H, Is)) / np.sqrt(Is)
-    a = np.einsum("eih,th->tei", inp["W_up"], inp["x"])
+    u = inp["x"]
+    if latent:
+        inp["W_in"] = rng.standard_normal((latent, H)) / np.sqrt(H)
+        inp["W_out"] = rng.standard_normal((H, latent)) / np.sqrt(latent)
+        u = inp["x"] @ inp["W_in"].T
+    a = np.einsum("eid,td->tei", inp["W_up"], u)
     gap = np.abs(a).min()
     if Is:
         gap = min(gap, np.abs(inp["x"] @ inp["Ws_up"].T).min())
@@ -471,11 +477,12 @@ def loss(inp, idx, dy):
     return float(np.sum(O.forward_tokens(inp, idx, g) * dy))
 
 
-def test_backward_matches_central_differences():
+@pytest.mark.parametrize("latent", [0, 4])
+def test_backward_matches_central_differences(latent):
     # Pins every gradient of the backward oracle to the forward oracle alone: each entry of
     # every input is nudged by +-eps and the change of the loss compared with the gradient.
     for seed in range(20):
-        inp, gap = f64_layer(seed)
+        inp, gap = f64_layer(seed, latent=latent)
         if gap > 1e-2:
             break
     c = inp["config"]
@@ -483,7 +490,7 @@ def test_backward_matches_central_differences():
     dy = np.random.default_rng(99).standard_normal((c.T, c.H))
     grads = O.backward(inp, idx, dy)
     eps = 1e-6
-    for name in _WEIGHTS:
+    for name in [n for n in _WEIGHTS if n in inp]:
         arr = inp[name]
         fd = np.zeros(arr.shape)
         for i in np.ndindex(arr.shape):
@@ -502,25 +509,29 @@ def torch_layer_loss(t, idx, dy, k):
     """The layer written with torch float64 ops on CPU (selection fixed) for autograd."""
     x, W_r, W_up, W_down = t["x"], t["W_r"], t["W_up"], t["W_down"]
     s = torch.sigmoid(x @ W_r.T)
+    u = x @ t["W_in"].T if "W_in" in t else x
     sel = torch.from_numpy(idx.astype(np.int64))
     ss = torch.gather(s, 1, sel)
     g = ss / ss.sum(dim=1, keepdim=True)
-    y = torch.zeros_like(x)
+    y = torch.zeros_like(u)
     for j in range(k):
         e = sel[:, j]
-        a = torch.einsum("tih,th->ti", W_up[e], x)
+        a = torch.einsum("tid,td->ti", W_up[e], u)
         h = torch.relu(a) ** 2
-        y = y + g[:, j:j + 1] * torch.einsum("thi,ti->th", W_down[e], h)
+        y = y + g[:, j:j + 1] * torch.einsum("tdi,ti->td", W_down[e], h)
+    if "W_out" in t:
+        y = y @ t["W_out"].T
     if "Ws_up" in t:
         y = y + (torch.relu(x @ t["Ws_up"].T) ** 2) @ t["Ws_down"].T
     return (y * torch.from_numpy(dy)).sum()
 
 
-@pytest.mark.parametrize("shared", [0, 24])
-def test_backward_matches_torch_autograd(shared):
+@pytest.mark.parametrize("shared,latent", [(0, 0), (24, 0), (24, 16)])
+def test_backward_matches_torch_autograd(shared, latent):
     # bf16-valued inputs (the oracle reads the bit patterns exactly; torch gets the same values
     # in float64); gradients from torch's reverse-mode differentiation of the layer.
-    c = cfg(T=16, H=32, E=8, k=3, I=16, I_shared=shared, act_dtype="bf16", expert_dtype="bf16")
+    c = cfg(T=16, H=32, E=8, k=3, I=16, I_shared=shared, latent=latent, act_dtype="bf16",
+            expert_dtype="bf16")
     inp = mi.make_layer(c, seed=4)
     dy64 = mi.bf16_bits_to_f32(mi.make_grad_output(c, seed=4)).astype(np.float64)
     idx, _, _ = O.route(O.logits(inp), inp["b"], c.k)
@@ -572,3 +583,20 @@ def test_backward_is_linear_in_dy_and_zero_input_gives_zero_weight_gradients():
     g0 = O.backward(z, idx, dy)
     for n in ("dx", "dz", "dW_r", "dW_up", "dW_down", "dWs_up", "dWs_down"):
         assert not np.any(g0[n]), n
+
+
+def test_latent_backward_with_identity_projections_is_the_plain_backward():
+    # l = H with W_in = W_out = I: the LatentMoE layer is the plain layer, and so are all its
+    # gradients (dW_in and dW_out themselves are pinned by the difference and autograd tests).
+    c = cfg(T=10, H=16, E=6, k=2, I=8, I_shared=8, act_dtype="f32", expert_dtype="f32")
+    plain = mi.make_layer(c, seed=8)
+    cl = dataclasses.replace(c, latent=16)
+    lat = dict(plain, config=cl, W_in=np.eye(16, dtype=np.float32),
+               W_out=np.eye(16, dtype=np.float32))
+    idx, _, _ = O.route(O.logits(plain), plain["b"], c.k)
+    dy = np.random.default_rng(8).standard_normal((c.T, c.H))
+    gp = O.backward(plain, idx, dy)
+    gl = O.backward(lat, idx, dy)
+    for n in ("dx", "dz", "dW_r", "dW_up", "dW_down", "dWs_up", "dWs_down"):
+        assert np.allclose(gl[n], gp[n], rtol=1e-12, atol=1e-14), n
+
