@@ -37,7 +37,8 @@ def parse():
     ap.add_argument("--config", default="nano_decode_bf16")
     ap.add_argument("--also", default="nano_prefill_bf16,latent_decode_bf16,nano_fp8_decode,"
                                       "nano_mxfp4_decode,nano_mxfp8_decode,latent_mxfp4_decode,"
-                                      "latent_fp8_decode,nano_prefill_bf16+backward",
+                                      "latent_fp8_decode,nano_prefill_bf16+backward,"
+                                      "latent_bf16+backward",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--path", default="auto", choices=["auto", "grouped", "stream"])
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured graph")
@@ -69,7 +70,7 @@ def work_of(name, cfg, counts, stream=False):
         return touched * rows * 4 if narrow else 0
 
     role = name.split(":")[1]
-    if role.startswith("bwd_") or role in ("pairs", "gates", "dx", "dW_r"):
+    if role.startswith("bwd_") or role in ("pairs", "gates", "du", "dx", "dW_r"):
         return backward_work(role, cfg, touched)
     if role == "router":
         return 2 * T * E * H, T * H * ea + E * H * ea + T * E * 4
@@ -116,45 +117,57 @@ def backward_work(role, cfg, touched):
     """(flops, bytes) of one launch of a backward-pass span (bf16 plain layer): each GEMM's
     reduction over the real pairs only (per-expert padding adds zeros, not counted), touched
     expert weights read once, activations in and out once."""
-    T, H, E, k, I, Is = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared
+    T, H, E, k, I, Is, L = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared, cfg.latent
     P = T * k
-    wt = touched * I * H * 2          # one touched projection stack, bf16
+    D = L or H                        # the experts' width
+    wt = touched * I * D * 2          # one touched projection stack, bf16
+    H0 = H
+    H = D                             # routed products below run in the experts' width
     gemm = {
         # forward recompute: relu(a) and h saved, expert outputs Y
         "bwd_routed_up": (2 * P * I * H, wt + T * H * 2 + 2 * P * I * 2),
         "bwd_routed_down": (2 * P * H * I, wt + P * I * 2 + P * H * 2),
-        "bwd_shared_up": (2 * T * Is * H, Is * H * 2 + T * H * 2 + 2 * T * Is * 2),
+        "bwd_shared_up": (2 * T * Is * H0, Is * H0 * 2 + T * H0 * 2 + 2 * T * Is * 2),
         # data gradients (weights read as stored; the squared ReLU's derivative fused)
         "bwd_routed_dgrad_down": (2 * P * I * H, wt + P * H * 2 + 2 * P * I * 2),
         "bwd_routed_dgrad_up": (2 * P * H * I, wt + P * I * 2 + P * H * 4),
-        "bwd_shared_dgrad_down": (2 * T * Is * H, Is * H * 2 + T * H * 2 + 2 * T * Is * 2),
-        "bwd_shared_dgrad_up": (2 * T * H * Is, H * Is * 2 + T * Is * 2 + T * H * 4),
+        "bwd_shared_dgrad_down": (2 * T * Is * H0, Is * H0 * 2 + T * H0 * 2 + 2 * T * Is * 2),
+        "bwd_shared_dgrad_up": (2 * T * H0 * Is, H0 * Is * 2 + T * Is * 2 + T * H0 * 4),
         # weight gradients over each expert's pairs (fp32 out, every expert's matrix written)
         "bwd_routed_wgrad_down": (2 * P * H * I, P * H * 2 + P * I * 2 + E * H * I * 4),
         "bwd_routed_wgrad_up": (2 * P * I * H, P * I * 2 + P * H * 2 + E * I * H * 4),
-        "bwd_shared_wgrad_down": (2 * T * H * Is, T * H * 2 + T * Is * 2 + H * Is * 4),
-        "bwd_shared_wgrad_up": (2 * T * Is * H, T * Is * 2 + T * H * 2 + Is * H * 4),
+        "bwd_shared_wgrad_down": (2 * T * H0 * Is, T * H0 * 2 + T * Is * 2 + H0 * Is * 4),
+        "bwd_shared_wgrad_up": (2 * T * Is * H0, T * Is * 2 + T * H0 * 2 + Is * H0 * 4),
+        # LatentMoE projections: dz = dy W_out, dW_out = dy^T z, dx += du W_in, dW_in = du^T x
+        "bwd_latent_out_dgrad": (2 * T * L * H0, T * H0 * 2 + H0 * L * 2 + T * L * 2),
+        "bwd_latent_out_wgrad": (2 * H0 * L * T, T * H0 * 2 + T * L * 2 + H0 * L * 4),
+        "bwd_latent_in_dgrad": (2 * T * H0 * L, T * L * 2 + L * H0 * 2 + T * H0 * 4),
+        "bwd_latent_in_wgrad": (2 * L * H0 * T, T * L * 2 + T * H0 * 2 + L * H0 * 4),
     }
     if role in gemm:
         f, b = gemm[role]
         return f, int(b)
-    if role == "pairs":               # x rows gathered into pair order
-        return 0, 2 * P * H * 2
+    if role == "pairs":               # expert inputs gathered into pair order
+        return 0, 2 * P * D * 2
     if role == "gates":               # dy, Y rows in; g*dy rows and dz out
-        return 2 * P * H, T * H * 2 + P * H * 2 + P * H * 2 + P * 4
+        return 2 * P * D, T * D * 2 + P * D * 2 + P * D * 2 + P * 4
+    if role == "du":                  # pair rows summed per token (LatentMoE)
+        return P * D, P * D * 4 + T * D * 2
     if role == "dx":
-        return P * H * 4, (T * H * 4 if Is else 0) + P * H * 4 + P * H * 2 + T * H * 4
+        return P * H0 * 4, (T * H0 * 4 if Is else 0) + (T * H0 * 4 if L else P * H0 * 4) + \
+            P * H0 * 2 + T * H0 * 4
     if role == "dW_r":
-        return 2 * P * H, P * 4 + P * H * 2 + E * H * 4
+        return 2 * P * H0, P * 4 + P * H0 * 2 + E * H0 * 4
     return 0, 0
 
 
 def backward_flops(cfg):
     """Algorithmic flops of the backward pass proper: data and weight gradients of the routed and
-    shared experts and of the router (the forward recompute is not counted)."""
-    T, H, E, k, I, Is = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared
-    P = T * k
-    return 4 * 2 * P * I * H + 4 * 2 * T * Is * H + 2 * 2 * P * H + 2 * P * H
+    shared experts, of the LatentMoE projections and of the router (the forward recompute is not
+    counted)."""
+    T, H, E, k, I, Is, L = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared, cfg.latent
+    P, D = T * k, cfg.D
+    return 4 * 2 * P * I * D + 4 * 2 * T * Is * H + 4 * 2 * T * L * H + 2 * 2 * P * H + 2 * P * D
 
 
 def kernel_of(span):

@@ -173,20 +173,23 @@ int32_t moe_dispatch(const int32_t *idx, int32_t T, int32_t E, int32_t k, int32_
 int32_t moe_bias_update(const int32_t *counts, const float *target, int32_t E, float gamma,
                         float *b, void *stream);
 
-/* ---- Backward pass (training) of the plain MoE layer.
+/* ---- Backward pass (training) of the MoE layer and of LatentMoE.
  * Gradients of a scalar loss given dy = dLoss/dy [T, H] (device, act dtype), for the forward that
- * moe_layer_forward computes ("NVIDIA Nemotron 3: Efficient and Open Intelligence", section 2.2;
- * "Nemotron 3 Nano: Open, Efficient Mixture-of-Experts Hybrid Mamba-Transformer Model for Agentic
- * Reasoning", section "技术框架"). The top-k selection is piecewise constant, so it is held at the
- * forward's choice and the gradient reaches the router through the gate weights only:
+ * moe_layer_forward / latent_moe_forward compute ("NVIDIA Nemotron 3: Efficient and Open
+ * Intelligence", section 2.2; "Nemotron 3 Nano: Open, Efficient Mixture-of-Experts Hybrid
+ * Mamba-Transformer Model for Agentic Reasoning", section "技术框架"). The top-k selection is
+ * piecewise constant, so it is held at the forward's choice and the gradient reaches the router
+ * through the gate weights only:
  *   g_j = s_j / sum_m s_m with s = sigmoid(x W_r^T) over the selected experts;
- *   dz_{e_j} = (dg_j - sum_m g_m dg_m) / sum_m s_m * s_j (1 - s_j), dg_j = <dy, Y_j>, where Y_j is
- *   expert e_j's output. The routing bias b only steers the selection and has no gradient.
+ *   dz_{e_j} = (dg_j - sum_m g_m dg_m) / sum_m s_m * s_j (1 - s_j), dg_j = <dY, Y_j>, where Y_j is
+ *   expert e_j's output and dY the gradient reaching the experts' gated sum (dy, or for LatentMoE
+ *   dy W_out, rounded to bf16). The routing bias b only steers the selection: no gradient.
  * The squared ReLU's derivative is 2 relu(a). Every gradient is written (not accumulated) in
- * fp32, row-major:
- *   dx [T, H], dW_r [E, H], dW_up [E, I, H], dW_down [E, H, I], dWs_up [I_s, H], dWs_down [H, I_s]
- *   (the last two only when I_shared > 0; all others are required).
- * Supported: act_dtype = expert_dtype = MOE_BF16, latent = 0, routing computed inside (flags:
+ * fp32, row-major, with D = H (or latent):
+ *   dx [T, H], dW_r [E, H], dW_up [E, I, D], dW_down [E, D, I], dWs_up [I_s, H], dWs_down [H, I_s]
+ *   (when I_shared > 0), dW_in [latent, H] and dW_out [H, latent] (LatentMoE); all required when
+ *   they apply.
+ * Supported: act_dtype = expert_dtype = MOE_BF16, routing computed inside (flags:
  * path bits ignored, MOE_ROUTING_GIVEN not accepted) -- else MOE_ERR_UNSUPPORTED. Without
  * MOE_SAVED_IN_WORKSPACE the call first recomputes the forward's routing and expert activations
  * from x; with it, it reads them from the workspace, where moe_layer_forward_train (same
@@ -203,13 +206,15 @@ typedef struct {
   float *dW_down;
   float *dWs_up;
   float *dWs_down;
+  float *dW_in;     /* LatentMoE only: [latent, H] */
+  float *dW_out;    /* LatentMoE only: [H, latent] */
 } moe_grads_t;
 
 int32_t moe_backward_workspace_size(const moe_desc_t *desc, size_t *bytes);
-/* Training forward: y [T, H] exactly as moe_layer_forward computes it on MOE_PATH_GROUPED
- * (bit for bit), keeping the routing and expert activations moe_layer_backward reads in `ws`
- * (moe_backward_workspace_size bytes). Same support, arguments and errors as moe_layer_backward
- * (MOE_SAVED_IN_WORKSPACE must not be set). */
+/* Training forward: y [T, H] exactly as moe_layer_forward (latent_moe_forward when latent > 0)
+ * computes it on MOE_PATH_GROUPED (bit for bit), keeping the routing and expert activations
+ * moe_layer_backward reads in `ws` (moe_backward_workspace_size bytes). Same support, arguments
+ * and errors as moe_layer_backward (MOE_SAVED_IN_WORKSPACE must not be set). */
 int32_t moe_layer_forward_train(const moe_desc_t *desc, const moe_weights_t *weights, void *y,
                                 void *ws, size_t ws_bytes, void *stream);
 int32_t moe_layer_backward(const moe_desc_t *desc, const moe_weights_t *weights, const void *dy,

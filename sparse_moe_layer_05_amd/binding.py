@@ -47,7 +47,7 @@ class MoeRouting(C.Structure):
 
 class MoeGrads(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("dx", "dW_r", "dW_up", "dW_down", "dWs_up",
-                                          "dWs_down")]
+                                          "dWs_down", "dW_in", "dW_out")]
 
 
 class MoeError(RuntimeError):
@@ -208,13 +208,14 @@ class Backward:
     """One backward call prepared once (descriptor, weights, gradient outputs in fp32,
     workspace): ``__call__(dy)`` writes the gradients of sum(dy * y) into ``self.grads``."""
 
-    def __init__(self, x, W_r, b, W_up, W_down, k, *, Ws_up=None, Ws_down=None):
-        self.desc = make_desc(x, W_r, W_up, k, Ws_up)
+    def __init__(self, x, W_r, b, W_up, W_down, k, *, Ws_up=None, Ws_down=None, W_in=None,
+                 W_out=None):
+        self.desc = make_desc(x, W_r, W_up, k, Ws_up, W_in)
         w = MoeWeights()
         w.x, w.W_r, w.b, w.W_up, w.W_down = _p(x), _p(W_r), _p(b), _p(W_up), _p(W_down)
-        w.Ws_up, w.Ws_down = _p(Ws_up), _p(Ws_down)
+        w.Ws_up, w.Ws_down, w.W_in, w.W_out = _p(Ws_up), _p(Ws_down), _p(W_in), _p(W_out)
         self.w = w
-        self._keep = [x, W_r, b, W_up, W_down, Ws_up, Ws_down]
+        self._keep = [x, W_r, b, W_up, W_down, Ws_up, Ws_down, W_in, W_out]
         f32 = dict(dtype=torch.float32, device=x.device)
         self.grads = {"dx": torch.empty(x.shape, **f32), "dW_r": torch.empty(W_r.shape, **f32),
                       "dW_up": torch.empty(W_up.shape, **f32),
@@ -222,6 +223,9 @@ class Backward:
         if Ws_up is not None:
             self.grads["dWs_up"] = torch.empty(Ws_up.shape, **f32)
             self.grads["dWs_down"] = torch.empty(Ws_down.shape, **f32)
+        if W_in is not None:
+            self.grads["dW_in"] = torch.empty(W_in.shape, **f32)
+            self.grads["dW_out"] = torch.empty(W_out.shape, **f32)
         g = MoeGrads()
         for name, _ in MoeGrads._fields_:
             setattr(g, name, _p(self.grads.get(name)))
@@ -254,7 +258,8 @@ class Backward:
 def backward_from(dev: dict, k: int) -> Backward:
     """A Backward over a ``to_device`` dict."""
     return Backward(dev["x"], dev["W_r"], dev["b"], dev["W_up"], dev["W_down"], k,
-                    Ws_up=dev.get("Ws_up"), Ws_down=dev.get("Ws_down"))
+                    Ws_up=dev.get("Ws_up"), Ws_down=dev.get("Ws_down"), W_in=dev.get("W_in"),
+                    W_out=dev.get("W_out"))
 
 
 def layer_forward(x, W_r, b, W_up, W_down, k, **kw):

@@ -176,20 +176,26 @@ __global__ __launch_bounds__(256) void router_weight_sum_kernel(const float* par
   *(float4*)(dWr + (int64_t)e * H + c) = s;
 }
 
-// dx[t] = dxs[t] (shared expert; optional) + sum_j du[pos(t, j)] + sum_j dzp[pos(t, j)] W_r[e_j],
-// added in that fixed order, fp32.
-__global__ __launch_bounds__(256) void bwd_dx_kernel(const float* dxs, const float* du,
-                                                     const float* dzp, const uint16_t* Wr,
-                                                     const int32_t* idx, const int32_t* pos,
-                                                     int H, int k, float* dx) {
+// dx[t] = dxa[t] + dxb[t] (each optional) + sum_j du[pos(t, j)] (du optional)
+//         + sum_j dzp[pos(t, j)] W_r[e_j], added in that fixed order, fp32.
+__global__ __launch_bounds__(256) void bwd_dx_kernel(const float* dxa, const float* dxb,
+                                                     const float* du, const float* dzp,
+                                                     const uint16_t* Wr, const int32_t* idx,
+                                                     const int32_t* pos, int H, int k, float* dx) {
   const int t = blockIdx.x;
   for (int c = threadIdx.x * 4; c < H; c += 1024) {
-    float4 a = dxs ? *(const float4*)(dxs + (int64_t)t * H + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      const int r = pos[(int64_t)t * k + j];
-      if (r < 0) continue;
-      const float4 u = *(const float4*)(du + (int64_t)r * H + c);
-      a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
+    float4 a = dxa ? *(const float4*)(dxa + (int64_t)t * H + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (dxb) {
+      const float4 q = *(const float4*)(dxb + (int64_t)t * H + c);
+      a.x += q.x; a.y += q.y; a.z += q.z; a.w += q.w;
+    }
+    if (du) {
+      for (int j = 0; j < k; ++j) {
+        const int r = pos[(int64_t)t * k + j];
+        if (r < 0) continue;
+        const float4 u = *(const float4*)(du + (int64_t)r * H + c);
+        a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
+      }
     }
     for (int j = 0; j < k; ++j) {
       const int r = pos[(int64_t)t * k + j];
@@ -202,6 +208,23 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* dxs, const flo
       a.w += z * bf16_bits_to_f32(w.y >> 16);
     }
     *(float4*)(dx + (int64_t)t * H + c) = a;
+  }
+}
+
+// out[t] = bf16(sum_j du[pos(t, j)]) in j order: the gradient of a token's expert input (the
+// LatentMoE projection u), rows of D.
+__global__ __launch_bounds__(256) void pairs_to_tokens_kernel(const float* du, const int32_t* pos,
+                                                              int D, int k, uint16_t* out) {
+  const int t = blockIdx.x;
+  for (int c = threadIdx.x * 4; c < D; c += 1024) {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      const int r = pos[(int64_t)t * k + j];
+      if (r < 0) continue;
+      const float4 u = *(const float4*)(du + (int64_t)r * D + c);
+      a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
+    }
+    *(uint2*)(out + (int64_t)t * D + c) = make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
   }
 }
 
@@ -252,13 +275,21 @@ hipError_t launch_bwd_router_weight(const float* dzp, const uint16_t* x, const i
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dx(const float* dxs, const float* du, const float* dzp, const uint16_t* Wr,
-                         const int32_t* idx, const int32_t* pos, int T, int H, int k, float* dx,
-                         hipStream_t s) {
+hipError_t launch_bwd_dx(const float* dxa, const float* dxb, const float* du, const float* dzp,
+                         const uint16_t* Wr, const int32_t* idx, const int32_t* pos, int T, int H,
+                         int k, float* dx, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (H % 4) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_dx_kernel, dim3(T), dim3(256), 0, s, dxs, du, dzp, Wr, idx, pos, H, k,
-                     dx);
+  hipLaunchKernelGGL(bwd_dx_kernel, dim3(T), dim3(256), 0, s, dxa, dxb, du, dzp, Wr, idx, pos, H,
+                     k, dx);
+  return hipGetLastError();
+}
+
+hipError_t launch_pairs_to_tokens(const float* du, const int32_t* pos, int T, int D, int k,
+                                  uint16_t* out, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (D % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pairs_to_tokens_kernel, dim3(T), dim3(256), 0, s, du, pos, D, k, out);
   return hipGetLastError();
 }
 

@@ -26,10 +26,15 @@ hipError_t launch_bwd_router_weight(const float* dzp, const uint16_t* x, const i
                                     const int32_t* offs, const int32_t* koffs, int E, int H,
                                     int max_chunks, float* part, float* dWr, hipStream_t s);
 
-// dx[t] = dxs[t] (optional) + sum_j du[pos(t,j)] + sum_j dzp[pos(t,j)] W_r[idx(t,j)], fp32.
-hipError_t launch_bwd_dx(const float* dxs, const float* du, const float* dzp, const uint16_t* Wr,
-                         const int32_t* idx, const int32_t* pos, int T, int H, int k, float* dx,
-                         hipStream_t s);
+// dx[t] = dxa[t] + dxb[t] (each optional) + sum_j du[pos(t,j)] (du optional)
+//         + sum_j dzp[pos(t,j)] W_r[idx(t,j)], fp32, in that order.
+hipError_t launch_bwd_dx(const float* dxa, const float* dxb, const float* du, const float* dzp,
+                         const uint16_t* Wr, const int32_t* idx, const int32_t* pos, int T, int H,
+                         int k, float* dx, hipStream_t s);
+
+// out[t] = bf16(sum_j du[pos(t,j)]) for rows of D (fp32 pair rows in, bf16 token rows out).
+hipError_t launch_pairs_to_tokens(const float* du, const int32_t* pos, int T, int D, int k,
+                                  uint16_t* out, hipStream_t s);
 
 // Xp[p] = x[perm[p]] for the P pair rows (bf16 rows of H, H a multiple of 8).
 hipError_t launch_gather_rows(const uint16_t* x, const int32_t* perm, int P, int H, uint16_t* Xp,

@@ -327,6 +327,8 @@ hipError_t launch_gemm_kt(int ta, int tb, Elt out, Epi epi, const KtParams& p, i
     return run_kt<0, 1, Elt::BF16, Epi::DSqRelu>(p, mt, s);
   if (ta == 0 && out == Elt::F32 && epi == Epi::Store && !p.kgrp)
     return run_kt<0, 1, Elt::F32, Epi::Store>(p, mt, s);
+  if (ta == 0 && out == Elt::BF16 && epi == Epi::Store && !p.kgrp)
+    return run_kt<0, 1, Elt::BF16, Epi::Store>(p, mt, s);
   if (ta == 1 && out == Elt::F32 && epi == Epi::Store && !p.mt_start)
     return run_kt<1, 1, Elt::F32, Epi::Store>(p, mt, s);
   return hipErrorInvalidValue;

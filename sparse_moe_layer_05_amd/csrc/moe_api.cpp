@@ -526,42 +526,42 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
 // ---------------------------------------------------------------- backward pass (bf16)
 
 struct BwdPlan {
-  int T = 0, H = 0, E = 0, k = 0, I = 0, Is = 0, P = 0, Ppad = 0, Tpad = 0;
+  int T = 0, H = 0, E = 0, k = 0, I = 0, Is = 0, L = 0, D = 0, P = 0, Ppad = 0;
   int nsplit = 1, kchunk = 0;
   size_t logits = 0, zpart = 0, idx = 0, gates = 0, counts = 0, offsets = 0, perm = 0, pos = 0;
   size_t dscratch = 0, mt_start = 0, koffs = 0, korder = 0;
-  size_t r = 0, h = 0, Yp = 0, hs = 0, rs = 0;                 // recomputed forward
+  size_t r = 0, h = 0, Yp = 0, hs = 0, rs = 0;                 // saved: expert activations
+  size_t u = 0, z = 0;                                         // saved (LatentMoE): x W_in^T, z
   size_t dYp = 0, dzp = 0, da = 0, du = 0, das = 0, dxs = 0;   // backward intermediates
   size_t wr_part = 0;                                          // dW_r chunk sums
-  size_t Xp = 0;                                               // x rows in pair order
+  size_t Xp = 0;                                               // expert inputs in pair order
+  size_t dacc = 0, dut = 0, dxl = 0;                           // LatentMoE: dz, du per token, dx
   size_t total = 0;
 };
 
 int32_t make_bwd_plan(const moe_desc_t* d, BwdPlan* out) {
-  if (d->latent) return MOE_ERR_UNSUPPORTED;  // the LatentMoE backward is not provided
   Plan fp;
   moe_desc_t dd = *d;
   dd.flags = MOE_PATH_GROUPED;
-  int32_t rc = make_plan(&dd, false, &fp);
+  int32_t rc = make_plan(&dd, d->latent > 0, &fp);
   if (rc) return rc;
   if (d->flags & ~(MOE_PATH_MASK | MOE_ROUTING_GIVEN | MOE_SAVED_IN_WORKSPACE))
     return MOE_ERR_INVALID_ARG;
   if (d->flags & MOE_ROUTING_GIVEN) return MOE_ERR_UNSUPPORTED;
-  if (d->act_dtype != MOE_BF16 || d->expert_dtype != MOE_BF16 || d->latent) return MOE_ERR_UNSUPPORTED;
+  if (d->act_dtype != MOE_BF16 || d->expert_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   BwdPlan p;
   p.T = fp.T; p.H = fp.H; p.E = fp.E; p.k = fp.k; p.I = fp.I; p.Is = fp.Is; p.P = fp.P;
+  p.L = fp.L; p.D = fp.D;
   p.nsplit = fp.nsplit; p.kchunk = fp.kchunk;
-  // each expert's pair columns start on a multiple of 64 (at most 63 padding columns each);
-  // the row pitch stays a multiple of 64 elements
+  // dW_r chunks: each expert's pair rows in chunks of 64 (at most 63 padding rows each)
   p.Ppad = (p.P + 63) / 64 * 64 + 64 * p.E;
-  p.Tpad = (p.T + 63) / 64 * 64;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
     off += (bytes + kAlign - 1) / kAlign * kAlign;
     return at;
   };
-  const size_t T = p.T, H = p.H, E = p.E, I = p.I, Is = p.Is, P = p.P, Pp = p.Ppad, Tp = p.Tpad;
+  const size_t T = p.T, H = p.H, E = p.E, I = p.I, Is = p.Is, P = p.P, D = p.D, L = p.L;
   p.logits = take(T * E * 4);
   if (p.nsplit > 1) p.zpart = take((size_t)p.nsplit * T * E * 4);
   p.idx = take(P * 4);
@@ -576,18 +576,29 @@ int32_t make_bwd_plan(const moe_desc_t* d, BwdPlan* out) {
   p.korder = take(E * 4);
   p.r = take(P * I * 2);
   p.h = take(P * I * 2);
-  p.Yp = take(P * H * 2);
-  p.dYp = take(P * H * 2);
-  p.dzp = take(P * 4);
-  p.wr_part = take((size_t)(p.Ppad / 64) * H * 4);
-  p.da = take(P * I * 2);
-  p.du = take(P * H * 4);
-  p.Xp = take(P * H * 2);
+  p.Yp = take(P * D * 2);
+  if (L) {
+    p.u = take(T * L * 2);
+    p.z = take(T * L * 2);
+  }
   if (Is) {
     p.hs = take(T * Is * 2);
     p.rs = take(T * Is * 2);
+  }
+  p.dYp = take(P * D * 2);
+  p.dzp = take(P * 4);
+  p.wr_part = take((size_t)(p.Ppad / 64) * H * 4);
+  p.da = take(P * I * 2);
+  p.du = take(P * D * 4);
+  p.Xp = take(P * D * 2);
+  if (Is) {
     p.das = take(T * Is * 2);
     p.dxs = take(T * H * 4);
+  }
+  if (L) {
+    p.dacc = take(T * L * 2);
+    p.dut = take(T * L * 2);
+    p.dxl = take(T * H * 4);
   }
   p.total = off;
   *out = p;
@@ -595,13 +606,15 @@ int32_t make_bwd_plan(const moe_desc_t* d, BwdPlan* out) {
 }
 
 // Routing, dispatch and the expert activations the backward pass reads, into the backward
-// workspace: logits, selection and gates, the dispatch arrays and padded K offsets, relu(a) and
-// h = relu(a)^2 per pair row, the expert outputs Y (bf16, pair rows), and for the shared expert
-// relu(a_s) and h_s.
+// workspace: logits, selection and gates, the dispatch arrays, the dW_r chunk numbering and the
+// heaviest-first expert order, relu(a) and h = relu(a)^2 per pair row, the expert outputs Y
+// (bf16, pair rows), for LatentMoE the projection u = x W_in^T and the gated sum z, and for the
+// shared expert relu(a_s) and h_s.
 int32_t bwd_activations(const BwdPlan& pl, const moe_weights_t* w, uint8_t* base,
                         hipStream_t s) {
   auto at = [&](size_t off) { return (void*)(base + off); };
-  const int T = pl.T, H = pl.H, E = pl.E, k = pl.k, I = pl.I, Is = pl.Is, P = pl.P;
+  const int T = pl.T, H = pl.H, E = pl.E, k = pl.k, I = pl.I, Is = pl.Is, P = pl.P, L = pl.L,
+            D = pl.D;
   float* logits = (float*)at(pl.logits);
   int32_t* idx = (int32_t*)at(pl.idx);
   float* gates = (float*)at(pl.gates);
@@ -613,7 +626,7 @@ int32_t bwd_activations(const BwdPlan& pl, const moe_weights_t* w, uint8_t* base
   int32_t* koffs = (int32_t*)at(pl.koffs);
   int32_t* korder = (int32_t*)at(pl.korder);
   const int max_mt = max_group_mtiles(P, E, kGroupBM);
-  // routing and dispatch as in the forward call
+  // routing and dispatch as in the forward call (the router reads x in H)
   {
     float* zsrc = pl.nsplit > 1 ? (float*)at(pl.zpart) : logits;
     {
@@ -633,15 +646,22 @@ int32_t bwd_activations(const BwdPlan& pl, const moe_weights_t* w, uint8_t* base
                             kGroupBM, mt_start, DispatchExtras(), s));
     MOE_TRY(launch_pad_offsets(counts, E, koffs, korder, s));
   }
+  // the experts' input: x, or its projection into the latent width
+  const void* xin = w->x;
+  if (L) {
+    MOE_SPAN("gemm_bf16_store:latent_in");
+    MOE_TRY(dense(Elt::BF16, Elt::BF16, Epi::Store, w->x, H, w->W_in, H, at(pl.u), L, T, L, H, s));
+    xin = at(pl.u);
+  }
   // expert activations: relu(a) and h = relu(a)^2 per pair row, then the expert outputs Y
   void* r = at(pl.r);
   void* h = at(pl.h);
   void* Yp = at(pl.Yp);
   {
     GemmParams up;
-    up.A = w->x; up.lda = H; up.a_rows = T; up.a_gather = perm;
-    up.B = w->W_up; up.ldb = H; up.b_gstride = (int64_t)I * H;
-    up.C = h; up.C2 = r; up.ldc = I; up.N = I; up.K = H;
+    up.A = xin; up.lda = D; up.a_rows = T; up.a_gather = perm;
+    up.B = w->W_up; up.ldb = D; up.b_gstride = (int64_t)I * D;
+    up.C = h; up.C2 = r; up.ldc = I; up.N = I; up.K = D;
     up.offs = offsets; up.mt_start = mt_start; up.G = E;
     MOE_SPAN("gemm_bf16_sqrelu:bwd_routed_up");
     MOE_TRY(launch_gemm(GemmKind{Elt::BF16, Elt::BF16, Epi::SqReluSave}, up, max_mt, s));
@@ -649,22 +669,35 @@ int32_t bwd_activations(const BwdPlan& pl, const moe_weights_t* w, uint8_t* base
   {
     GemmParams dn;
     dn.A = h; dn.lda = I; dn.a_rows = P;
-    dn.B = w->W_down; dn.ldb = I; dn.b_gstride = (int64_t)H * I;
-    dn.C = Yp; dn.ldc = H; dn.N = H; dn.K = I;
+    dn.B = w->W_down; dn.ldb = I; dn.b_gstride = (int64_t)D * I;
+    dn.C = Yp; dn.ldc = D; dn.N = D; dn.K = I;
     dn.offs = offsets; dn.mt_start = mt_start; dn.G = E;
     MOE_SPAN("gemm_bf16_store:bwd_routed_down");
     MOE_TRY(launch_gemm(GemmKind{Elt::BF16, Elt::BF16, Epi::Store}, dn, max_mt, s));
   }
-  void* hs = Is ? at(pl.hs) : nullptr;
-  void* rs = Is ? at(pl.rs) : nullptr;
+  if (L) {  // z = sum_j g_j Y_j in the latent width, as the forward combines it
+    MOE_SPAN("combine:z");
+    MOE_TRY(launch_combine(Yp, Elt::BF16, L, nullptr, 0, pos, gates, T, L, k, at(pl.z),
+                           Elt::BF16, L, s));
+  }
   if (Is) {
     GemmParams g;
-    g.A = w->x; g.lda = H; g.a_rows = T; g.B = w->Ws_up; g.ldb = H; g.C = hs; g.C2 = rs;
-    g.ldc = Is; g.M = T; g.N = Is; g.K = H;
+    g.A = w->x; g.lda = H; g.a_rows = T; g.B = w->Ws_up; g.ldb = H; g.C = at(pl.hs);
+    g.C2 = at(pl.rs); g.ldc = Is; g.M = T; g.N = Is; g.K = H;
     MOE_SPAN("gemm_bf16_sqrelu:bwd_shared_up");
     MOE_TRY(launch_gemm(GemmKind{Elt::BF16, Elt::BF16, Epi::SqReluSave}, g, 0, s));
   }
+  return MOE_OK;
+}
 
+int32_t check_bwd_args(const BwdPlan& pl, const moe_weights_t* w) {
+  if (!w || !w->x || !w->W_r || !w->b || !w->W_up || !w->W_down) return MOE_ERR_INVALID_ARG;
+  if (pl.Is && (!w->Ws_up || !w->Ws_down)) return MOE_ERR_INVALID_ARG;
+  if (pl.L && (!w->W_in || !w->W_out)) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {w->x, w->W_r, w->W_up, w->W_down, w->Ws_up, w->Ws_down, w->W_in,
+                        w->W_out};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
@@ -675,24 +708,23 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
   int32_t rc = make_bwd_plan(d, &pl);
   if (rc) return rc;
   if (pl.T == 0) return MOE_OK;
-  if (!w || !dy || !gr || !w->x || !w->W_r || !w->b || !w->W_up || !w->W_down || !gr->dx ||
-      !gr->dW_r || !gr->dW_up || !gr->dW_down)
-    return MOE_ERR_INVALID_ARG;
-  if (pl.Is && (!w->Ws_up || !w->Ws_down || !gr->dWs_up || !gr->dWs_down))
-    return MOE_ERR_INVALID_ARG;
-  const void* ptrs[] = {w->x, w->W_r, w->W_up, w->W_down, w->Ws_up, w->Ws_down, dy, gr->dx,
-                        gr->dW_r, gr->dW_up, gr->dW_down, gr->dWs_up, gr->dWs_down};
+  if ((rc = check_bwd_args(pl, w))) return rc;
+  if (!dy || !gr || !gr->dx || !gr->dW_r || !gr->dW_up || !gr->dW_down) return MOE_ERR_INVALID_ARG;
+  if (pl.Is && (!gr->dWs_up || !gr->dWs_down)) return MOE_ERR_INVALID_ARG;
+  if (pl.L && (!gr->dW_in || !gr->dW_out)) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {dy, gr->dx, gr->dW_r, gr->dW_up, gr->dW_down, gr->dWs_up, gr->dWs_down,
+                        gr->dW_in, gr->dW_out};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return MOE_ERR_INVALID_ARG;
   if (!ws || ws_bytes < pl.total || !aligned16(ws)) return MOE_ERR_WORKSPACE;
 
   uint8_t* base = (uint8_t*)ws;
   auto at = [&](size_t off) { return (void*)(base + off); };
-  const int T = pl.T, H = pl.H, E = pl.E, k = pl.k, I = pl.I, Is = pl.Is, P = pl.P;
+  const int T = pl.T, H = pl.H, E = pl.E, k = pl.k, I = pl.I, Is = pl.Is, P = pl.P, L = pl.L,
+            D = pl.D;
   float* logits = (float*)at(pl.logits);
   int32_t* idx = (int32_t*)at(pl.idx);
   float* gates = (float*)at(pl.gates);
-  int32_t* counts = (int32_t*)at(pl.counts);
   int32_t* offsets = (int32_t*)at(pl.offsets);
   int32_t* perm = (int32_t*)at(pl.perm);
   int32_t* pos = (int32_t*)at(pl.pos);
@@ -711,13 +743,33 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
   void* hs = Is ? at(pl.hs) : nullptr;
   void* rs = Is ? at(pl.rs) : nullptr;
 
+  // (1) LatentMoE: the experts' gated sum z left through y = z W_out^T, so they see
+  // dacc = dy W_out (bf16) in place of dy; dW_out = dy^T z
+  const void* dye = dy;
+  if (L) {
+    {
+      MOE_SPAN("gemm_kt_bf16out:bwd_latent_out_dgrad");
+      KtParams g;
+      g.A = dy; g.lda = H; g.a_rows = T; g.B = w->W_out; g.ldb = L;
+      g.C = at(pl.dacc); g.ldc = L; g.M = T; g.N = L; g.K = H;
+      MOE_TRY(launch_gemm_kt(0, 1, Elt::BF16, Epi::Store, g, 0, s));
+    }
+    {
+      MOE_SPAN("gemm_kt_f32out:bwd_latent_out_wgrad");
+      KtParams g;
+      g.A = dy; g.lda = H; g.B = at(pl.z); g.ldb = L;
+      g.C = gr->dW_out; g.ldc = L; g.M = H; g.N = L; g.K = T;
+      MOE_TRY(launch_gemm_kt(1, 1, Elt::F32, Epi::Store, g, 0, s));
+    }
+    dye = at(pl.dacc);
+  }
   // (2) gradient through the gates: dY rows (g_j dy_t) and the logit gradient per pair
   uint16_t* dYp = (uint16_t*)at(pl.dYp);
   float* dzp = (float*)at(pl.dzp);
   {
     MOE_SPAN("bwd_route:gates");
-    MOE_TRY(launch_bwd_route((const uint16_t*)dy, (const uint16_t*)Yp, logits, idx, gates, pos,
-                             T, H, E, k, dYp, dzp, s));
+    MOE_TRY(launch_bwd_route((const uint16_t*)dye, (const uint16_t*)Yp, logits, idx, gates, pos,
+                             T, D, E, k, dYp, dzp, s));
   }
   // (3) data gradients, reading the weights as stored (K-major for these products):
   // da = (dY W_down[e]) * 2 relu(a), du = da W_up[e]; the shared expert's pair likewise
@@ -725,9 +777,9 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
   float* du = (float*)at(pl.du);
   {
     KtParams g;
-    g.A = dYp; g.lda = H; g.a_rows = P;
-    g.B = w->W_down; g.ldb = I; g.b_gstride = (int64_t)H * I;
-    g.C = da; g.C2 = r; g.ldc = I; g.M = P; g.N = I; g.K = H;
+    g.A = dYp; g.lda = D; g.a_rows = P;
+    g.B = w->W_down; g.ldb = I; g.b_gstride = (int64_t)D * I;
+    g.C = da; g.C2 = r; g.ldc = I; g.M = P; g.N = I; g.K = D;
     g.offs = offsets; g.mt_start = mt_start; g.G = E;
     MOE_SPAN("gemm_kt_dsqrelu:bwd_routed_dgrad_down");
     MOE_TRY(launch_gemm_kt(0, 1, Elt::BF16, Epi::DSqRelu, g, max_mt, s));
@@ -735,8 +787,8 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
   {
     KtParams g;
     g.A = da; g.lda = I; g.a_rows = P;
-    g.B = w->W_up; g.ldb = H; g.b_gstride = (int64_t)I * H;
-    g.C = du; g.ldc = H; g.M = P; g.N = H; g.K = I;
+    g.B = w->W_up; g.ldb = D; g.b_gstride = (int64_t)I * D;
+    g.C = du; g.ldc = D; g.M = P; g.N = D; g.K = I;
     g.offs = offsets; g.mt_start = mt_start; g.G = E;
     MOE_SPAN("gemm_kt_f32out:bwd_routed_dgrad_up");
     MOE_TRY(launch_gemm_kt(0, 1, Elt::F32, Epi::Store, g, max_mt, s));
@@ -757,9 +809,35 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
     g.C = dxs; g.ldc = H; g.M = T; g.N = H; g.K = Is;
     MOE_TRY(launch_gemm_kt(0, 1, Elt::F32, Epi::Store, g, 0, s));
   }
-  {
+  // (4) dx: the experts' input gradient (through W_in for LatentMoE), the shared expert's,
+  // and the router's through the gates
+  if (L) {
+    uint16_t* dut = (uint16_t*)at(pl.dut);
+    {
+      MOE_SPAN("pairs_to_tokens:du");
+      MOE_TRY(launch_pairs_to_tokens(du, pos, T, L, k, dut, s));
+    }
+    {
+      MOE_SPAN("gemm_kt_f32out:bwd_latent_in_dgrad");
+      KtParams g;
+      g.A = dut; g.lda = L; g.a_rows = T; g.B = w->W_in; g.ldb = H;
+      g.C = at(pl.dxl); g.ldc = H; g.M = T; g.N = H; g.K = L;
+      MOE_TRY(launch_gemm_kt(0, 1, Elt::F32, Epi::Store, g, 0, s));
+    }
+    {
+      MOE_SPAN("gemm_kt_f32out:bwd_latent_in_wgrad");
+      KtParams g;  // dW_in [L][H] = du^T x
+      g.A = dut; g.lda = L; g.B = w->x; g.ldb = H;
+      g.C = gr->dW_in; g.ldc = H; g.M = L; g.N = H; g.K = T;
+      MOE_TRY(launch_gemm_kt(1, 1, Elt::F32, Epi::Store, g, 0, s));
+    }
     MOE_SPAN("bwd_dx:dx");
-    MOE_TRY(launch_bwd_dx(dxs, du, dzp, (const uint16_t*)w->W_r, idx, pos, T, H, k, gr->dx, s));
+    MOE_TRY(launch_bwd_dx((const float*)at(pl.dxl), dxs, nullptr, dzp,
+                          (const uint16_t*)w->W_r, idx, pos, T, H, k, gr->dx, s));
+  } else {
+    MOE_SPAN("bwd_dx:dx");
+    MOE_TRY(launch_bwd_dx(dxs, nullptr, du, dzp, (const uint16_t*)w->W_r, idx, pos, T, H, k,
+                          gr->dx, s));
   }
   {
     MOE_SPAN("bwd_router_weight:dW_r");
@@ -767,30 +845,30 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
                                      pl.Ppad / 64, (float*)at(pl.wr_part), gr->dW_r, s));
   }
 
-  // (4) routed weight gradients, reduced over each expert's own pair rows (the K window
+  // (5) routed weight gradients, reduced over each expert's own pair rows (the K window
   // [offsets[e], offsets[e+1]) of the pair-ordered operands, read as stored), heaviest first
   uint16_t* Xp = (uint16_t*)at(pl.Xp);
   {
     MOE_SPAN("gather_rows:pairs");
-    MOE_TRY(launch_gather_rows((const uint16_t*)w->x, perm, P, H, Xp, s));
+    MOE_TRY(launch_gather_rows((const uint16_t*)(L ? at(pl.u) : w->x), perm, P, D, Xp, s));
   }
   {
-    KtParams g;  // dW_down[e] [H][I] = dY_e^T h_e
-    g.A = dYp; g.lda = H; g.B = h; g.ldb = I;
-    g.C = gr->dW_down; g.ldc = I; g.c_gstride = (int64_t)H * I;
-    g.M = H; g.N = I; g.G = E; g.kgrp = offsets; g.korder = korder;
+    KtParams g;  // dW_down[e] [D][I] = dY_e^T h_e
+    g.A = dYp; g.lda = D; g.B = h; g.ldb = I;
+    g.C = gr->dW_down; g.ldc = I; g.c_gstride = (int64_t)D * I;
+    g.M = D; g.N = I; g.G = E; g.kgrp = offsets; g.korder = korder;
     MOE_SPAN("gemm_kt_f32out:bwd_routed_wgrad_down");
     MOE_TRY(launch_gemm_kt(1, 1, Elt::F32, Epi::Store, g, 0, s));
   }
   {
-    KtParams g;  // dW_up[e] [I][H] = da_e^T x_e
-    g.A = da; g.lda = I; g.B = Xp; g.ldb = H;
-    g.C = gr->dW_up; g.ldc = H; g.c_gstride = (int64_t)I * H;
-    g.M = I; g.N = H; g.G = E; g.kgrp = offsets; g.korder = korder;
+    KtParams g;  // dW_up[e] [I][D] = da_e^T (expert input)_e
+    g.A = da; g.lda = I; g.B = Xp; g.ldb = D;
+    g.C = gr->dW_up; g.ldc = D; g.c_gstride = (int64_t)I * D;
+    g.M = I; g.N = D; g.G = E; g.kgrp = offsets; g.korder = korder;
     MOE_SPAN("gemm_kt_f32out:bwd_routed_wgrad_up");
     MOE_TRY(launch_gemm_kt(1, 1, Elt::F32, Epi::Store, g, 0, s));
   }
-  // (5) the shared expert's weight gradients over all tokens
+  // (6) the shared expert's weight gradients over all tokens
   if (Is) {
     {
       MOE_SPAN("gemm_kt_f32out:bwd_shared_wgrad_down");
@@ -809,8 +887,9 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
 }
 
 // Forward pass that keeps what the backward pass reads (in the backward workspace layout):
-// routing, dispatch and the expert activations (bwd_activations), then the shared expert's
-// output and the combine exactly as the grouped forward path computes them.
+// routing, dispatch and the expert activations (bwd_activations), then the output exactly as the
+// grouped forward path computes it: the shared expert and the combine, or for LatentMoE the
+// projection of z back to H with the shared expert as a second K segment.
 int32_t forward_train(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws,
                       size_t ws_bytes, hipStream_t s) {
   if (!d) return MOE_ERR_INVALID_ARG;
@@ -819,16 +898,23 @@ int32_t forward_train(const moe_desc_t* d, const moe_weights_t* w, void* y, void
   int32_t rc = make_bwd_plan(d, &pl);
   if (rc) return rc;
   if (pl.T == 0) return MOE_OK;
-  if (!w || !y || !w->x || !w->W_r || !w->b || !w->W_up || !w->W_down) return MOE_ERR_INVALID_ARG;
-  if (pl.Is && (!w->Ws_up || !w->Ws_down)) return MOE_ERR_INVALID_ARG;
-  const void* ptrs[] = {w->x, w->W_r, w->W_up, w->W_down, w->Ws_up, w->Ws_down, y};
-  for (const void* q : ptrs)
-    if (q && !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  if ((rc = check_bwd_args(pl, w))) return rc;
+  if (!y || !aligned16(y)) return MOE_ERR_INVALID_ARG;
   if (!ws || ws_bytes < pl.total || !aligned16(ws)) return MOE_ERR_WORKSPACE;
   uint8_t* base = (uint8_t*)ws;
   rc = bwd_activations(pl, w, base, s);
   if (rc) return rc;
-  const int T = pl.T, H = pl.H, k = pl.k, Is = pl.Is;
+  const int T = pl.T, H = pl.H, k = pl.k, Is = pl.Is, L = pl.L;
+  if (L) {
+    MOE_SPAN("gemm_bf16_store:latent_out");
+    if (Is)
+      MOE_TRY(dense(Elt::BF16, Elt::BF16, Epi::Store, base + pl.z, L, w->W_out, L, y, H, T, H, L,
+                    s, base + pl.hs, Is, w->Ws_down, Is, Is));
+    else
+      MOE_TRY(dense(Elt::BF16, Elt::BF16, Epi::Store, base + pl.z, L, w->W_out, L, y, H, T, H, L,
+                    s));
+    return hip_status(hipGetLastError());
+  }
   float* S = nullptr;
   if (Is) {  // shared expert S = h_s Ws_down^T in fp32 (the dx buffer is free until the backward)
     S = (float*)(base + pl.dxs);

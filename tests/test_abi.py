@@ -159,7 +159,8 @@ def bwd_ws(d):
     (dict(act_dtype=0, expert_dtype=0), B.MOE_ERR_UNSUPPORTED),     # fp32 layer
     (dict(expert_dtype=2), B.MOE_ERR_UNSUPPORTED),                  # e4m3 experts
     (dict(expert_dtype=B.MOE_MXFP4), B.MOE_ERR_UNSUPPORTED),
-    (dict(latent=64), B.MOE_ERR_UNSUPPORTED),
+    (dict(latent=64), B.MOE_OK), (dict(latent=40), B.MOE_ERR_INVALID_ARG),
+    (dict(latent=64, expert_dtype=2), B.MOE_ERR_UNSUPPORTED),
     (dict(flags=B.ROUTING_GIVEN), B.MOE_ERR_UNSUPPORTED),
     (dict(flags=64), B.MOE_ERR_INVALID_ARG), (dict(k=0), B.MOE_ERR_INVALID_ARG),
     (dict(H=250), B.MOE_ERR_INVALID_ARG),
@@ -198,7 +199,13 @@ def test_backward_argument_errors_are_reported_before_launch():
     assert call(dy=C.c_void_p(0x10008)) == B.MOE_ERR_INVALID_ARG      # misaligned
     assert call(ws=None) == B.MOE_ERR_WORKSPACE
     assert call(ws_bytes=16) == B.MOE_ERR_WORKSPACE
-    assert call(desc(latent=64)) == B.MOE_ERR_UNSUPPORTED
+    g.dW_in = None
+    assert call(desc(latent=64)) == B.MOE_ERR_INVALID_ARG      # dW_in missing
+    g.dW_in = FAKE.value
+    w.W_out = None
+    assert call(desc(latent=64)) == B.MOE_ERR_INVALID_ARG      # W_out missing
+    w.W_out = FAKE.value
+    g.dW_in = None
     g.dW_up = None
     assert call() == B.MOE_ERR_INVALID_ARG
     g.dW_up = FAKE.value
@@ -222,5 +229,5 @@ def test_training_forward_and_saved_flag_validation():
     assert ft(y=None) == B.MOE_ERR_INVALID_ARG
     assert ft(desc(flags=B.SAVED_IN_WORKSPACE)) == B.MOE_ERR_INVALID_ARG
     assert ft(ws_bytes=16) == B.MOE_ERR_WORKSPACE
-    assert ft(desc(latent=64)) == B.MOE_ERR_UNSUPPORTED
+    assert ft(desc(latent=64, expert_dtype=2)) == B.MOE_ERR_UNSUPPORTED
     assert ft(desc(T=0)) == B.MOE_OK
