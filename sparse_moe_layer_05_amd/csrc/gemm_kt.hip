@@ -322,6 +322,13 @@ hipError_t launch_gemm_kt(int ta, int tb, Elt out, Epi epi, const KtParams& p, i
       (ta && (p.M % 8 || p.lda % 8)) || (!ta && p.K % 8))
     return hipErrorInvalidValue;
   if (epi == Epi::DSqRelu && (!p.C2 || out != Elt::BF16)) return hipErrorInvalidValue;
+  // Operand offsets are 32-bit (buffer resources and the per-K-step scalar offset): a K-major
+  // operand's K rows, and a K-contiguous A's rows, must span less than 2 GiB.
+  constexpr int64_t kLim = ((int64_t)1 << 31) - 1;
+  const int64_t krows = p.kgrp ? p.a_rows : p.K;  // K-grouped: the stored rows of both operands
+  if ((int64_t)krows * p.ldb * 2 > kLim || (ta && (int64_t)krows * p.lda * 2 > kLim) ||
+      (!ta && (int64_t)p.a_rows * p.lda * 2 > kLim))
+    return hipErrorInvalidValue;
   const int mt = p.kgrp ? p.G * cdiv(p.M, BM) : (p.mt_start ? max_mtiles : cdiv(p.M, BM));
   if (ta == 0 && out == Elt::BF16 && epi == Epi::DSqRelu && !p.kgrp)
     return run_kt<0, 1, Elt::BF16, Epi::DSqRelu>(p, mt, s);

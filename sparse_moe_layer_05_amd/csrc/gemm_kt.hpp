@@ -25,7 +25,7 @@ struct KtParams {
   int64_t ldc = 0;
   int64_t c_gstride = 0;
   int M = 0, N = 0, K = 0;
-  int a_rows = 0;            // stored rows of A that may be read
+  int a_rows = 0;            // stored rows of A that may be read (K-grouped: rows of A and B)
   // Row-grouped launches (data gradients): group g owns rows [offs[g], offs[g+1]) of A and C
   // (M-tiles from mt_start) and its own B at B + g * b_gstride.
   const int32_t* offs = nullptr;
@@ -42,7 +42,8 @@ struct KtParams {
 //   (0, 1, BF16, Store)                         data gradients (dense or row-grouped)
 //   (1, 1, F32, Store)                          weight gradients (dense or K-grouped)
 // N, ldc and the K-major leading dimensions must be multiples of 8, and so must M when A is
-// K-major and K when it is not. max_mtiles bounds the M-tiles of a row-grouped launch (its grid).
+// K-major and K when it is not; each operand must span less than 2 GiB (32-bit offsets).
+// max_mtiles bounds the M-tiles of a row-grouped launch (its grid).
 hipError_t launch_gemm_kt(int ta, int tb, Elt out, Epi epi, const KtParams& p, int max_mtiles,
                           hipStream_t s);
 

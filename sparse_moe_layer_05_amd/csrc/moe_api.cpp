@@ -854,7 +854,7 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
   }
   {
     KtParams g;  // dW_down[e] [D][I] = dY_e^T h_e
-    g.A = dYp; g.lda = D; g.B = h; g.ldb = I;
+    g.A = dYp; g.lda = D; g.B = h; g.ldb = I; g.a_rows = P;
     g.C = gr->dW_down; g.ldc = I; g.c_gstride = (int64_t)D * I;
     g.M = D; g.N = I; g.G = E; g.kgrp = offsets; g.korder = korder;
     MOE_SPAN("gemm_kt_f32out:bwd_routed_wgrad_down");
@@ -862,7 +862,7 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
   }
   {
     KtParams g;  // dW_up[e] [I][D] = da_e^T (expert input)_e
-    g.A = da; g.lda = I; g.B = Xp; g.ldb = D;
+    g.A = da; g.lda = I; g.B = Xp; g.ldb = D; g.a_rows = P;
     g.C = gr->dW_up; g.ldc = D; g.c_gstride = (int64_t)I * D;
     g.M = I; g.N = D; g.G = E; g.kgrp = offsets; g.korder = korder;
     MOE_SPAN("gemm_kt_f32out:bwd_routed_wgrad_up");
