@@ -83,15 +83,6 @@ __device__ __forceinline__ bool tile_of(const GemmParams& p, int& g, int& row0, 
   return rows > 0;
 }
 
-__device__ __forceinline__ void unpack8(const uint4 q, float* v) {
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFF);
-    v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
-  }
-}
-
 // -------------------------------------------------------------------------------------------
 // Matrix-core kernel (bf16 or e4m3 operands, fp32 accumulation).
 // -------------------------------------------------------------------------------------------
