@@ -59,6 +59,10 @@ CASES = {
                                       I_shared=96),
     # an expert count that is not a multiple of 8, and experts left without tokens
     "bwd_e13_sparse": mi.LayerConfig("bwd_e13_sparse", T=3, H=256, E=13, k=2, I=64),
+    # degenerate routings: every expert selected (k = E), and a single expert (a dense MLP)
+    "bwd_all_experts": mi.LayerConfig("bwd_all_experts", T=20, H=256, E=8, k=8, I=64,
+                                      I_shared=64),
+    "bwd_one_expert": mi.LayerConfig("bwd_one_expert", T=50, H=256, E=1, k=1, I=128),
     # LatentMoE: experts in the latent width, without and with a shared expert
     "bwd_latent": mi.LayerConfig("bwd_latent", T=70, H=256, E=64, k=8, I=64, latent=64),
     "bwd_latent_shared": mi.LayerConfig("bwd_latent_shared", T=33, H=256, E=32, k=4, I=48,
