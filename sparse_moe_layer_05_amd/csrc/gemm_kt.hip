@@ -25,6 +25,7 @@ constexpr int KS = 64;                  // k per stage
 constexpr int SA = BM * KS * 2, SB = BN * KS * 2;
 constexpr int STAGE = SA + SB;          // 40 KB; two stages
 constexpr int EPW = WN + 4;             // epilogue strip row (floats)
+constexpr int kBand = 4;                // N-tiles per band of a K-grouped launch's tile order
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef short v8i16_t __attribute__((ext_vector_type(8)));
@@ -70,14 +71,21 @@ __device__ __forceinline__ bool kt_tile(const KtParams& p, int& g, int& row0, in
   const int nN = cdiv(p.N, BN), nM = cdiv(p.M, BM);
   k0 = 0;
   kc = p.K;
-  if (p.kgrp) {  // round robin over the dies, heaviest groups first (their tiles cost most)
-    const int L = blockIdx.x, per = nM * nN;
-    if (L >= p.G * per) return false;
-    const int slot = L / per;
+  if (p.kgrp) {
+    // Every die takes an equal, compact share of each group's tiles, the groups in launch order
+    // (heaviest first: their tiles cost most). Blocks d, d + 8, d + 16, ... run on die d; its
+    // share of a group is a contiguous run of the group's tiles numbered in bands of kBand
+    // N-tiles, N fastest, so the die's tiles have few A and B slabs between them and share them
+    // through its L2.
+    const int per = nM * nN, cs = cdiv(per, kXcds);
+    const int d = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+    const int slot = j / cs, q = d * cs + j % cs;
+    if (slot >= p.G || q >= per) return false;
     g = p.korder ? p.korder[slot] : slot;
-    const int local = L - slot * per;
-    n0 = (local / nM) * BN;
-    row0 = (local % nM) * BM;
+    const int band = q / (kBand * nM), within = q - band * kBand * nM;
+    const int nb = min(kBand, nN - band * kBand);
+    n0 = (band * kBand + within % nb) * BN;
+    row0 = (within / nb) * BM;
     rows = min(BM, p.M - row0);
     k0 = p.kgrp[g];
     kc = p.kgrp[g + 1] - k0;
@@ -254,11 +262,14 @@ void gemm_kt_kernel(KtParams p) {
   __syncthreads();  // the epilogue reuses the stages
 
   // Epilogue (as in the forward GEMM): acc[i][j][r] is C[wm*WM + i*32 + (r/4)*8 + (lane/32)*4 +
-  // r%4][wn*WN + j*32 + lane%32]; 16-row strips go through LDS so each lane finishes 8
-  // consecutive columns of a row.
+  // r%4][wn*WN + j*32 + lane%32]; 16-row strips go through LDS so each lane finishes CW
+  // consecutive columns of a row: 8 for bf16 outputs, 4 for fp32 (16 bytes either way, so that
+  // consecutive lanes store consecutive 16-byte chunks of a row).
   uint8_t* Cg = (uint8_t*)p.C + (p.kgrp ? (int64_t)g * p.c_gstride * (OUT == Elt::F32 ? 4 : 2) : 0);
   float* ep = (float*)smem + wave * 16 * EPW;
-  constexpr int CG = WN / 8, ITEMS = 16 * CG / 64;
+  constexpr int CW = OUT == Elt::F32 ? 4 : 8;
+  constexpr int CG = WN / CW, ITEMS = 16 * CG / 64;
+  static_assert((16 * CG) % 64 == 0, "strip must split evenly over the wave");
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
 #pragma unroll
@@ -275,29 +286,25 @@ void gemm_kt_kernel(KtParams p) {
         const int item = it * 64 + lane;
         const int srow = item / CG, cg = item % CG;
         const int rl = wm * WM + i * 32 + h * 16 + srow;
-        const int col = n0 + wn * WN + cg * 8;
-        if (rl < rows && col < p.N) {
+        const int col = n0 + wn * WN + cg * CW;
+        if (rl < rows && col < p.N) {  // N % 8 == 0: a group inside N ends inside it
           const int row = row0 + rl;
-          float v[8];
-          const float4 lo = *(const float4*)(ep + srow * EPW + cg * 8);
-          const float4 hi = *(const float4*)(ep + srow * EPW + cg * 8 + 4);
-          v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-          v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-          if constexpr (EPI == Epi::DSqRelu) {  // d/da relu(a)^2 = 2 relu(a), relu(a) in C2
-            float r[8];
-            unpack8(*(const uint4*)((const uint16_t*)p.C2 + (int64_t)row * p.ldc + col), r);
+          const float4 lo = *(const float4*)(ep + srow * EPW + cg * CW);
+          if constexpr (OUT == Elt::F32) {
+            *(float4*)((float*)Cg + (int64_t)row * p.ldc + col) = lo;
+          } else {
+            const float4 hi = *(const float4*)(ep + srow * EPW + cg * CW + 4);
+            float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            if constexpr (EPI == Epi::DSqRelu) {  // d/da relu(a)^2 = 2 relu(a), relu(a) in C2
+              float r[8];
+              unpack8(*(const uint4*)((const uint16_t*)p.C2 + (int64_t)row * p.ldc + col), r);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] *= 2.f * r[q];
-          }
-          if constexpr (OUT == Elt::BF16) {
+              for (int q = 0; q < 8; ++q) v[q] *= 2.f * r[q];
+            }
             uint32_t w[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
             *(uint4*)((uint16_t*)Cg + (int64_t)row * p.ldc + col) = make_uint4(w[0], w[1], w[2], w[3]);
-          } else {
-            float* o = (float*)Cg + (int64_t)row * p.ldc + col;
-            *(float4*)o = make_float4(v[0], v[1], v[2], v[3]);
-            *(float4*)(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
           }
         }
       }
@@ -307,9 +314,11 @@ void gemm_kt_kernel(KtParams p) {
 
 template <int TA, int TB, Elt OUT, Epi EPI>
 hipError_t run_kt(const KtParams& p, int mtiles, hipStream_t s) {
-  const int tiles = mtiles * cdiv(p.N, BN);
+  const int nN = cdiv(p.N, BN), tiles = mtiles * nN;
   if (tiles <= 0) return hipSuccess;
-  const int grid = cdiv(tiles, kXcds) * kXcds;
+  // K-grouped: each die gets ceil(tiles per group / 8) blocks per group (see kt_tile)
+  const int grid = p.kgrp ? p.G * kXcds * cdiv(cdiv(p.M, BM) * nN, kXcds)
+                          : cdiv(tiles, kXcds) * kXcds;
   hipLaunchKernelGGL((gemm_kt_kernel<TA, TB, OUT, EPI>), dim3(grid), dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }
