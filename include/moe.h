@@ -35,6 +35,12 @@
  *   - Dimension rules: H, I, I_shared and latent are multiples of 16; 1 <= k <= E <= 1024,
  *     k <= 64; T >= 0 (T == 0 is a no-op that returns MOE_OK). MOE_MXFP4 / MOE_MXFP8 experts
  *     also need D (H, or latent) and I to be multiples of 32 (else MOE_ERR_INVALID_ARG).
+ *   - Size rule (bf16 activations): the matrix-core GEMMs use 32-bit operand offsets, so each
+ *     of x [T,H], h [T*k,I] (one byte per element for 8- and 4-bit experts, else two), the
+ *     shared expert's [T,I_shared], the latent rows [T,latent] and each weight matrix (W_r, one
+ *     expert's W_up or W_down, Ws_up, Ws_down, W_in, W_out) must span less than 2 GiB; the
+ *     backward pass also needs [T*k, D] in bf16 under 2 GiB. Larger shapes return
+ *     MOE_ERR_INVALID_ARG (split T over several calls).
  *   - Expert weights of 8 or 4 bits (MOE_FP8_E4M3, MOE_MXFP4, MOE_MXFP8): the expert input rows
  *     and the rows of h = relu(u W_up^T)^2 (rounded to bf16) are quantised per row to e4m3 with
  *     scale amax / 448 before they meet the weights, as in "Nemotron 3 Nano：開放高效的 MoE 混合

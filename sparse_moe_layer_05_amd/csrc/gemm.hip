@@ -516,6 +516,13 @@ hipError_t launch_gemm(const GemmKind& k, const GemmParams& p, int max_mtiles, h
     }
   }
   constexpr int GB = kGroupBM;
+  // Operand offsets are 32-bit (buffer resources, per-lane row offsets and the per-K-step
+  // scalar offset): A's rows and one group's B panel must each span less than 2 GiB.
+  constexpr int64_t kLim = ((int64_t)1 << 31) - 1;
+  const int64_t eb = k.ab == Elt::FP8 ? 1 : 2;
+  if ((int64_t)p.a_rows * p.lda * eb > kLim || (int64_t)p.N * p.ldb * eb > kLim ||
+      (p.K2 > 0 && ((int64_t)p.a2_rows * p.lda2 * eb > kLim || (int64_t)p.N * p.ldb2 * eb > kLim)))
+    return hipErrorInvalidValue;
   if (k.ab == Elt::BF16) {
     if (k.epi == Epi::SqReluSave && (!p.C2 || k.out != Elt::BF16 || p.N % 8 || p.ldc % 8))
       return hipErrorInvalidValue;

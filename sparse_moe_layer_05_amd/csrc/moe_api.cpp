@@ -70,6 +70,16 @@ int32_t make_plan(const moe_desc_t* d, bool latent_call, Plan* pl) {
   else
     return MOE_ERR_INVALID_ARG;
   if (p.path < 0) return MOE_ERR_UNSUPPORTED;
+  // The matrix-core GEMMs address each operand through 32-bit buffer offsets: x, the experts'
+  // intermediate rows h, the shared expert's, the latent rows and every weight matrix (of one
+  // expert) must each span less than 2 GiB. (fp32 layers use 64-bit addressing.)
+  if (p.act == Elt::BF16) {
+    constexpr int64_t kOp = ((int64_t)1 << 31) - 1;
+    const int64_t eh = fp8 || mx ? 1 : 2;
+    if (T * H * 2 > kOp || T * k * I * eh > kOp || T * Is * 2 > kOp || T * L * 2 > kOp ||
+        E * H * 2 > kOp || I * Dw * 2 > kOp || Is * H * 2 > kOp || L * H * 2 > kOp)
+      return MOE_ERR_INVALID_ARG;
+  }
   p.bm = p.act == Elt::F32 ? 64 : kGroupBM;
 
   const size_t ea = p.act == Elt::F32 ? 4 : 2;  // activation / intermediate element bytes
@@ -549,6 +559,8 @@ int32_t make_bwd_plan(const moe_desc_t* d, BwdPlan* out) {
     return MOE_ERR_INVALID_ARG;
   if (d->flags & MOE_ROUTING_GIVEN) return MOE_ERR_UNSUPPORTED;
   if (d->act_dtype != MOE_BF16 || d->expert_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  // the pair-ordered rows (g dy, and x or u gathered) are GEMM operands too: under 2 GiB
+  if ((int64_t)fp.P * fp.D * 2 > ((int64_t)1 << 31) - 1) return MOE_ERR_INVALID_ARG;
   BwdPlan p;
   p.T = fp.T; p.H = fp.H; p.E = fp.E; p.k = fp.k; p.I = fp.I; p.Is = fp.Is; p.P = fp.P;
   p.L = fp.L; p.D = fp.D;

@@ -169,6 +169,31 @@ def test_backward_descriptor_validation(kw, code):
     assert bwd_ws(desc(**kw))[0] == code
 
 
+NANO = dict(H=2688, E=128, k=6, I=1856, I_shared=3712)
+
+
+def test_operands_over_2_gib_are_rejected():
+    # The matrix-core GEMMs address operands with 32-bit offsets. At Nano width, 100,000 tokens
+    # give a bf16 h of 100000 * 6 * 1856 * 2 = 2.23e9 bytes, over 2^31 - 1; e4m3 experts keep h
+    # in one byte per element (1.11e9), inside the limit; the fp32 layer's kernels use 64-bit
+    # addressing and take any size.
+    assert ws_size(desc(T=8192, **NANO))[0] == B.MOE_OK
+    assert ws_size(desc(T=100000, **NANO))[0] == B.MOE_ERR_INVALID_ARG
+    assert ws_size(desc(T=100000, expert_dtype=2, **NANO))[0] == B.MOE_OK
+    assert ws_size(desc(T=100000, act_dtype=0, expert_dtype=0, **NANO))[0] == B.MOE_OK
+    # x alone: T * H * 2 over the limit with small experts
+    assert ws_size(desc(T=(1 << 30) // 2688 + 1, H=2688, E=8, k=1, I=16))[0] == \
+        B.MOE_ERR_INVALID_ARG
+    assert ws_size(desc(T=(1 << 30) // 2688, H=2688, E=8, k=1, I=16))[0] == B.MOE_OK
+    # one expert's weight matrix over the limit
+    assert ws_size(desc(T=64, H=32768, E=8, k=2, I=32768 + 16))[0] == B.MOE_ERR_INVALID_ARG
+    # backward: the pair rows [T*k, H] in bf16 (80,000 * 6 * 2688 * 2 = 2.58e9) over the limit
+    # while the forward's h (1.78e9) is inside it
+    assert ws_size(desc(T=80000, **NANO))[0] == B.MOE_OK
+    assert bwd_ws(desc(T=80000, **NANO))[0] == B.MOE_ERR_INVALID_ARG
+    assert bwd_ws(desc(T=8192, **NANO))[0] == B.MOE_OK
+
+
 def test_backward_workspace_holds_no_weight_copies():
     # the weights are read as stored (K-major reads in LDS): the workspace scales with the tokens
     # and holds no copy of the expert stacks
