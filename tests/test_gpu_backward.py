@@ -186,6 +186,49 @@ def test_backward_full_size(name):
             assert err <= TOL[n], (n, e, err)
 
 
+@pytest.mark.parametrize("name", ["nano_prefill_bf16", "latent_bf16"])
+def test_backward_full_size_with_dy_on_sampled_tokens(name):
+    # Real prefill shapes (the launches the bench times) with dy nonzero on 24 sampled tokens
+    # only. With the selection held fixed, a token's contribution to every gradient is zero
+    # when its dy is, so each gradient is a sum over the sampled tokens that the oracle computes
+    # exactly: dx on every token (exactly zero off the sample), dW_r, the shared expert's and
+    # the latent projections' gradients whole, and the expert stacks on the three experts the
+    # sample uses most; every expert the sample does not use gets exactly zero.
+    cfg = mi.CONFIGS[name]
+    say(f"[gpu] backward full size, dy on 24 tokens: {name} T={cfg.T}")
+    inp = mi.make_layer(cfg, seed=0)
+    rng = np.random.default_rng(17)
+    toks = np.sort(rng.choice(cfg.T, 24, replace=False)).astype(np.int32)
+    on = np.zeros(cfg.T, bool)
+    on[toks] = True
+    dy = mi.make_grad_output(cfg, seed=0)
+    dy = np.where(on[:, None], dy, np.zeros_like(dy))        # bf16 bit pattern 0 is +0.0
+    dy64 = mi.bf16_bits_to_f32(dy).astype(np.float64)
+    dev = moe.to_device(inp)
+    dy_dev = moe.to_device({"dy": dy})["dy"]
+    idx, _ = gpu_selection(dev, cfg.k)
+    check_selection(inp, idx, toks)
+    got = grads_of(dev, cfg.k, dy_dev)
+    assert not np.any(got["dx"][~on])
+    ref = O.backward(inp, idx[toks], dy64[toks], tokens=toks,
+                     want=("dx", "dW_r", "dWs_up", "dWs_down", "dW_in", "dW_out"), threads=THREADS)
+    for n in ref:
+        err = rel_frob(got[n][toks] if n == "dx" else got[n], ref[n])
+        say(f"[gpu]   {name} {n}: rel Frobenius {err:.3e}")
+        assert err <= TOL[n], (n, err)
+    used = np.bincount(idx[toks].ravel(), minlength=cfg.E)
+    unused = np.flatnonzero(used == 0)
+    assert not np.any(got["dW_up"][unused]) and not np.any(got["dW_down"][unused])
+    for e in np.argsort(-used, kind="stable")[:3]:
+        mine = toks[(idx[toks] == e).any(axis=1)]
+        r = O.backward(inp, idx[mine], dy64[mine], tokens=mine, want=("dW_up", "dW_down"),
+                       expert=int(e), threads=THREADS)
+        for n in ("dW_up", "dW_down"):
+            err = rel_frob(got[n][e], r[n])
+            say(f"[gpu]   {name} expert {e} ({len(mine)} tokens) {n}: rel Frobenius {err:.3e}")
+            assert err <= TOL[n], (n, e, err)
+
+
 @pytest.mark.parametrize("name", ["bwd_ragged", "bwd_e13_sparse", "bwd_latent_shared"])
 def test_training_forward_and_saved_backward_match_the_plain_calls(name):
     # moe_layer_forward_train gives the grouped forward's y bit for bit, and a backward that
