@@ -41,51 +41,66 @@ __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* counts
   }
 }
 
-__device__ __forceinline__ float block_sum(float v, float* red) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float s = 0.f;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) s += red[w];  // fixed order
-  return s;
-}
-
 // One workgroup per token t. With Y_j the forward's expert output row of pair (t, j):
 //   dg_j = <dy_t, Y_j>,  s_j = sigmoid(logit of e_j),  Z = sum_j s_j,
 //   dz_j = (dg_j - sum_m g_m dg_m) / Z * s_j (1 - s_j),
 //   dYp[pos(t, j)] = bf16(g_j dy_t),  dzp[pos(t, j)] = dz_j.
+// The rows Y_j are read kPairBatch at a time with all their loads in flight, and those dot
+// products are reduced together; each is still summed in a fixed order (per thread along the
+// row, then a butterfly within each wave, then the waves in order).
+constexpr int kPairBatch = 8;
 __global__ __launch_bounds__(256) void bwd_route_kernel(const uint16_t* dy, const uint16_t* Yp,
                                                         const float* logits, const int32_t* idx,
                                                         const float* gates, const int32_t* pos,
                                                         int H, int E, int k, uint16_t* dYp,
                                                         float* dzp) {
-  __shared__ float red[4];
+  constexpr int KB = kPairBatch;
+  __shared__ float red[4][KB];
   __shared__ float dg[kMaxK];
-  const int t = blockIdx.x, tid = threadIdx.x;
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint16_t* dyt = dy + (int64_t)t * H;
   const int nch = H / 8;
-  for (int j = 0; j < k; ++j) {
-    const int r = pos[(int64_t)t * k + j];
-    float part = 0.f;
-    if (r >= 0) {
-      const uint16_t* y = Yp + (int64_t)r * H;
-      for (int c = tid; c < nch; c += 256) {
-        const uint4 a = *(const uint4*)(dyt + c * 8), b = *(const uint4*)(y + c * 8);
-        const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+  for (int j0 = 0; j0 < k; j0 += KB) {
+    int r[KB];
+    float part[KB];
+#pragma unroll
+    for (int q = 0; q < KB; ++q) {
+      r[q] = j0 + q < k ? pos[(int64_t)t * k + j0 + q] : -1;
+      part[q] = 0.f;
+    }
+    for (int c = tid; c < nch; c += 256) {
+      const uint4 a = *(const uint4*)(dyt + c * 8);
+      uint4 b[KB];
+#pragma unroll
+      for (int q = 0; q < KB; ++q)
+        if (r[q] >= 0) b[q] = *(const uint4*)(Yp + (int64_t)r[q] * H + c * 8);
+      const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int q = 0; q < KB; ++q) {
+        if (r[q] < 0) continue;
+        const uint32_t wb[4] = {b[q].x, b[q].y, b[q].z, b[q].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          part += bf16_bits_to_f32(wa[e] & 0xFFFF) * bf16_bits_to_f32(wb[e] & 0xFFFF);
-          part += bf16_bits_to_f32(wa[e] >> 16) * bf16_bits_to_f32(wb[e] >> 16);
+          part[q] += bf16_bits_to_f32(wa[e] & 0xFFFF) * bf16_bits_to_f32(wb[e] & 0xFFFF);
+          part[q] += bf16_bits_to_f32(wa[e] >> 16) * bf16_bits_to_f32(wb[e] >> 16);
         }
       }
     }
-    const float s = block_sum(part, red);
-    if (tid == 0) dg[j] = s;
+#pragma unroll
+    for (int q = 0; q < KB; ++q) {
+      float v = part[q];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+      if (lane == 0) red[wave][q] = v;
+    }
+    __syncthreads();
+    if (tid < KB && j0 + tid < k) {
+      float sum = 0.f;
+      for (int w = 0; w < 4; ++w) sum += red[w][tid];  // fixed order
+      dg[j0 + tid] = sum;
+    }
+    __syncthreads();  // red is reused by the next batch; dg is read below
   }
-  __syncthreads();
   if (tid == 0) {
     float Z = 0.f, gdg = 0.f;
     float sj[kMaxK];
@@ -177,12 +192,16 @@ __global__ __launch_bounds__(256) void router_weight_sum_kernel(const float* par
 }
 
 // dx[t] = dxa[t] + dxb[t] (each optional) + sum_j du[pos(t, j)] (du optional)
-//         + sum_j dzp[pos(t, j)] W_r[e_j], added in that fixed order, fp32.
+//         + sum_j dzp[pos(t, j)] W_r[e_j], added in that fixed order, fp32. The rows of du are
+// read kPairBatch at a time with all their loads in flight.
 __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* dxa, const float* dxb,
                                                      const float* du, const float* dzp,
                                                      const uint16_t* Wr, const int32_t* idx,
                                                      const int32_t* pos, int H, int k, float* dx) {
+  constexpr int KB = kPairBatch;
   const int t = blockIdx.x;
+  const int32_t* post = pos + (int64_t)t * k;
+  const int32_t* idxt = idx + (int64_t)t * k;
   for (int c = threadIdx.x * 4; c < H; c += 1024) {
     float4 a = dxa ? *(const float4*)(dxa + (int64_t)t * H + c) : make_float4(0.f, 0.f, 0.f, 0.f);
     if (dxb) {
@@ -190,18 +209,24 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* dxa, const flo
       a.x += q.x; a.y += q.y; a.z += q.z; a.w += q.w;
     }
     if (du) {
-      for (int j = 0; j < k; ++j) {
-        const int r = pos[(int64_t)t * k + j];
-        if (r < 0) continue;
-        const float4 u = *(const float4*)(du + (int64_t)r * H + c);
-        a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
+      for (int j0 = 0; j0 < k; j0 += KB) {
+        int r[KB];
+        float4 u[KB];
+#pragma unroll
+        for (int q = 0; q < KB; ++q) {
+          r[q] = j0 + q < k ? post[j0 + q] : -1;
+          if (r[q] >= 0) u[q] = *(const float4*)(du + (int64_t)r[q] * H + c);
+        }
+#pragma unroll
+        for (int q = 0; q < KB; ++q)
+          if (r[q] >= 0) { a.x += u[q].x; a.y += u[q].y; a.z += u[q].z; a.w += u[q].w; }
       }
     }
-    for (int j = 0; j < k; ++j) {
-      const int r = pos[(int64_t)t * k + j];
+    for (int j = 0; j < k; ++j) {  // W_r rows are few and stay in cache: one at a time
+      const int r = post[j];
       if (r < 0) continue;
       const float z = dzp[r];
-      const uint2 w = *(const uint2*)(Wr + (int64_t)idx[(int64_t)t * k + j] * H + c);
+      const uint2 w = *(const uint2*)(Wr + (int64_t)idxt[j] * H + c);
       a.x += z * bf16_bits_to_f32(w.x & 0xFFFF);
       a.y += z * bf16_bits_to_f32(w.x >> 16);
       a.z += z * bf16_bits_to_f32(w.y & 0xFFFF);
@@ -212,17 +237,25 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* dxa, const flo
 }
 
 // out[t] = bf16(sum_j du[pos(t, j)]) in j order: the gradient of a token's expert input (the
-// LatentMoE projection u), rows of D.
+// LatentMoE projection u), rows of D. Pair rows are read kPairBatch at a time.
 __global__ __launch_bounds__(256) void pairs_to_tokens_kernel(const float* du, const int32_t* pos,
                                                               int D, int k, uint16_t* out) {
+  constexpr int KB = kPairBatch;
   const int t = blockIdx.x;
+  const int32_t* post = pos + (int64_t)t * k;
   for (int c = threadIdx.x * 4; c < D; c += 1024) {
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      const int r = pos[(int64_t)t * k + j];
-      if (r < 0) continue;
-      const float4 u = *(const float4*)(du + (int64_t)r * D + c);
-      a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
+    for (int j0 = 0; j0 < k; j0 += KB) {
+      int r[KB];
+      float4 u[KB];
+#pragma unroll
+      for (int q = 0; q < KB; ++q) {
+        r[q] = j0 + q < k ? post[j0 + q] : -1;
+        if (r[q] >= 0) u[q] = *(const float4*)(du + (int64_t)r[q] * D + c);
+      }
+#pragma unroll
+      for (int q = 0; q < KB; ++q)
+        if (r[q] >= 0) { a.x += u[q].x; a.y += u[q].y; a.z += u[q].z; a.w += u[q].w; }
     }
     *(uint2*)(out + (int64_t)t * D + c) = make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
   }
