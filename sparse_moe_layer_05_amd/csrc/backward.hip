@@ -152,17 +152,31 @@ __global__ __launch_bounds__(256) void router_weight_chunks_kernel(
   }
   const int p0 = offs[lo] + (q * kTile - koffs[lo]);
   const int p1 = min(p0 + kTile, offs[lo + 1]);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int c = blockIdx.x * 256 + lane * 4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (c < H) {
-    for (int p = p0 + wave; p < p1; p += 4) {
-      const float z = dzp[p];
-      const uint2 v = *(const uint2*)(x + (int64_t)perm[p] * H + c);
-      acc.x += z * bf16_bits_to_f32(v.x & 0xFFFF);
-      acc.y += z * bf16_bits_to_f32(v.x >> 16);
-      acc.z += z * bf16_bits_to_f32(v.y & 0xFFFF);
-      acc.w += z * bf16_bits_to_f32(v.y >> 16);
+    // this wave's rows p0 + wave, p0 + wave + 4, ...: every load in flight, then added in order
+    constexpr int RW = kTile / 4;
+    int src[RW];
+    float z[RW];
+    uint2 v[RW];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const int p = p0 + wave + 4 * i;
+      src[i] = p < p1 ? perm[p] : -1;
+      z[i] = p < p1 ? dzp[p] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+      if (src[i] >= 0) v[i] = *(const uint2*)(x + (int64_t)src[i] * H + c);
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      if (src[i] < 0) continue;
+      acc.x += z[i] * bf16_bits_to_f32(v[i].x & 0xFFFF);
+      acc.y += z[i] * bf16_bits_to_f32(v[i].x >> 16);
+      acc.z += z[i] * bf16_bits_to_f32(v[i].y & 0xFFFF);
+      acc.w += z[i] * bf16_bits_to_f32(v[i].y >> 16);
     }
   }
   acc_w[wave][lane] = acc;
@@ -184,9 +198,15 @@ __global__ __launch_bounds__(256) void router_weight_sum_kernel(const float* par
   const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (c >= H) return;
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int q = koffs[e] / kTile; q < koffs[e + 1] / kTile; ++q) {
-    const float4 u = *(const float4*)(part + (int64_t)q * H + c);
-    s.x += u.x; s.y += u.y; s.z += u.z; s.w += u.w;
+  const int q1 = koffs[e + 1] / kTile;
+  for (int q0 = koffs[e] / kTile; q0 < q1; q0 += 8) {  // 8 chunk sums in flight, added in order
+    float4 u[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (q0 + i < q1) u[i] = *(const float4*)(part + (int64_t)(q0 + i) * H + c);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (q0 + i < q1) { s.x += u[i].x; s.y += u[i].y; s.z += u[i].z; s.w += u[i].w; }
   }
   *(float4*)(dWr + (int64_t)e * H + c) = s;
 }
