@@ -26,19 +26,29 @@ constexpr int kTile = 64;  // pair rows per chunk of the router weight gradient
 // descending count (ties: lower index first), the launch order of the weight-gradient products.
 __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* counts, int G,
                                                            int32_t* koffs, int32_t* order) {
-  for (int g = threadIdx.x; g < G; g += blockDim.x) {
-    const int c = counts[g];
+  // one thread per expert (G <= kMaxE = blockDim.x); counts staged in LDS
+  __shared__ int32_t cnt[kMaxE];
+  __shared__ int32_t scan[kMaxE];
+  const int g = threadIdx.x;
+  const int c = g < G ? counts[g] : 0;
+  if (g < G) cnt[g] = c;
+  __syncthreads();
+  if (g < G) {
     int rank = 0;
-    for (int q = 0; q < G; ++q) rank += counts[q] > c || (counts[q] == c && q < g);
+    for (int q = 0; q < G; ++q) rank += cnt[q] > c || (cnt[q] == c && q < g);
     order[rank] = g;
   }
-  if (threadIdx.x != 0) return;
-  int acc = 0;
-  koffs[0] = 0;
-  for (int g = 0; g < G; ++g) {
-    acc += (counts[g] + kTile - 1) / kTile * kTile;
-    koffs[g + 1] = acc;
+  // inclusive scan of the padded counts (integer sums: exact in any order)
+  scan[g] = g < G ? (c + kTile - 1) / kTile * kTile : 0;
+  __syncthreads();
+  for (int o = 1; o < kMaxE; o <<= 1) {
+    const int add = g >= o ? scan[g - o] : 0;
+    __syncthreads();
+    scan[g] += add;
+    __syncthreads();
   }
+  if (g == 0) koffs[0] = 0;
+  if (g < G) koffs[g + 1] = scan[g];
 }
 
 // One workgroup per token t. With Y_j the forward's expert output row of pair (t, j):
@@ -302,7 +312,8 @@ hipError_t launch_gather_rows(const uint16_t* x, const int32_t* perm, int P, int
 
 hipError_t launch_pad_offsets(const int32_t* counts, int G, int32_t* koffs, int32_t* order,
                               hipStream_t s) {
-  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(1024), 0, s, counts, G, koffs, order);
+  if (G < 1 || G > kMaxE) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(kMaxE), 0, s, counts, G, koffs, order);
   return hipGetLastError();
 }
 
