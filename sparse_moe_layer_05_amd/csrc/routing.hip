@@ -626,8 +626,13 @@ hipError_t launch_topk(const float* logits, int nsplit, const float* b, int T, i
 }
 
 void router_split(int T, int E, int H, int* nsplit, int* kchunk) {
+  // Few output tiles leave most CUs idle: split K so that the launch reaches about 256 tiles
+  // (slices of at least 128 columns) below 128 tiles, about 512 (slices of at least 256 columns)
+  // below 512. The top-k kernel adds the slices' partial logits in slice order.
   const int tiles = cdiv(T, 128) * cdiv(E, 128);
-  const int n = (tiles == 0 || tiles >= 128) ? 1 : std::max(1, std::min(256 / tiles, H / 128));
+  int n = 1;
+  if (tiles > 0 && tiles < 128) n = std::max(1, std::min(256 / tiles, H / 128));
+  else if (tiles >= 128 && tiles < 512) n = std::max(1, std::min(512 / tiles, H / 256));
   const int chunk = cdiv(cdiv(H, n), 64) * 64;   // whole 64-wide K-steps per slice
   *kchunk = chunk;
   *nsplit = cdiv(H, chunk);
