@@ -211,12 +211,16 @@ __device__ __forceinline__ uint64_t build_masks(const int32_t* __restrict__ idx,
   __syncthreads();
   uint64_t valid = 0;  // bit j: pair (t, j) is kept (k <= 64)
   if (t < T) {
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[(int64_t)t * k + j];
-      if ((unsigned)e < (unsigned)E) {
-        const uint32_t bit = 1u << (tid & 31);
-        const uint32_t old = atomicOr(&mask[e * 8 + (tid >> 5)], bit);
-        if (!(old & bit)) valid |= 1ull << j;  // a repeated expert in one token is dropped
+    const uint32_t bit = 1u << (tid & 31);
+    for (int j0 = 0; j0 < k; j0 += 8) {  // a token's slots, 8 loads in flight, in slot order
+      int ev[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ev[i] = j0 + i < k ? idx[(int64_t)t * k + j0 + i] : -1;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if ((unsigned)ev[i] >= (unsigned)E) continue;
+        const uint32_t old = atomicOr(&mask[ev[i] * 8 + (tid >> 5)], bit);
+        if (!(old & bit)) valid |= 1ull << (j0 + i);  // a repeated expert in one token is dropped
       }
     }
   }
@@ -327,15 +331,29 @@ __global__ __launch_bounds__(1024) void dispatch_scan(const int32_t* __restrict_
                                                       DispatchExtras ex) {
   __shared__ int32_t s[4][1024];
   const int e = threadIdx.x;
+  // chunk counts read 8 at a time with their loads in flight
   int tot = 0;
   if (e < E)
-    for (int c = 0; c < nchunks; ++c) tot += ccount[(int64_t)c * E + e];
+    for (int c0 = 0; c0 < nchunks; c0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = c0 + i < nchunks ? ccount[(int64_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) tot += v[i];
+    }
   dispatch_totals(e, E, tot, bm, s, counts, offsets, mt_start, ex);
   if (e < E) {
     int run = s[0][e] - tot;
-    for (int c = 0; c < nchunks; ++c) {
-      cbase[(int64_t)c * E + e] = run;
-      run += ccount[(int64_t)c * E + e];
+    for (int c0 = 0; c0 < nchunks; c0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = c0 + i < nchunks ? ccount[(int64_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (c0 + i >= nchunks) break;
+        cbase[(int64_t)(c0 + i) * E + e] = run;
+        run += v[i];
+      }
     }
   }
 }
@@ -422,17 +440,30 @@ __global__ __launch_bounds__(kDispatchChunk) void dispatch_scatter(
   if (t >= T) return;
   const int w = tid >> 5;
   const uint32_t below = (1u << (tid & 31)) - 1u;
-  for (int j = 0; j < k; ++j) {
-    if (!((valid >> j) & 1ull)) {
-      pos[(int64_t)t * k + j] = -1;
-      continue;
+  for (int j0 = 0; j0 < k; j0 += 8) {  // 8 slots at a time: their loads in flight together
+    int ev[8], base[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = j0 + i;
+      ev[i] = j < k && ((valid >> j) & 1ull) ? idx[(int64_t)t * k + j] : -1;
     }
-    const int e = idx[(int64_t)t * k + j];
-    int rank = __popc(mask[e * 8 + w] & below);
-    for (int q = 0; q < w; ++q) rank += __popc(mask[e * 8 + q]);
-    const int r = cbase[(int64_t)c * E + e] + rank;
-    perm[r] = t;
-    pos[(int64_t)t * k + j] = r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) base[i] = ev[i] >= 0 ? cbase[(int64_t)c * E + ev[i]] : 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = j0 + i;
+      if (j >= k) continue;
+      if (ev[i] < 0) {
+        pos[(int64_t)t * k + j] = -1;
+        continue;
+      }
+      const int e = ev[i];
+      int rank = __popc(mask[e * 8 + w] & below);
+      for (int q = 0; q < w; ++q) rank += __popc(mask[e * 8 + q]);
+      const int r = base[i] + rank;
+      perm[r] = t;
+      pos[(int64_t)t * k + j] = r;
+    }
   }
 }
 
