@@ -63,6 +63,9 @@ CASES = {
     "bwd_all_experts": mi.LayerConfig("bwd_all_experts", T=20, H=256, E=8, k=8, I=64,
                                       I_shared=64),
     "bwd_one_expert": mi.LayerConfig("bwd_one_expert", T=50, H=256, E=1, k=1, I=128),
+    # the largest routing the ABI takes: 1024 experts, 64 per token
+    "bwd_max_routing": mi.LayerConfig("bwd_max_routing", T=150, H=256, E=1024, k=64, I=32,
+                                      I_shared=32),
     # LatentMoE: experts in the latent width, without and with a shared expert
     "bwd_latent": mi.LayerConfig("bwd_latent", T=70, H=256, E=64, k=8, I=64, latent=64),
     "bwd_latent_shared": mi.LayerConfig("bwd_latent_shared", T=33, H=256, E=32, k=4, I=48,

@@ -143,6 +143,9 @@ SMALL = {
     # GEMM epilogue then writes element by element (grouped and decode paths)
     "bf16_e6": mi.LayerConfig("bf16_e6", T=70, H=256, E=6, k=2, I=96, I_shared=64),
     "bf16_e13": mi.LayerConfig("bf16_e13", T=9, H=256, E=13, k=3, I=64),
+    # the largest routing the ABI takes: 1024 experts, 64 per token (about 9 tokens each)
+    "bf16_max_routing": mi.LayerConfig("bf16_max_routing", T=150, H=256, E=1024, k=64, I=32,
+                                       I_shared=32),
     # few tokens and a wide H: the streamed projection into the latent width splits K in four
     "latent_split_small": mi.LayerConfig("latent_split_small", T=20, H=1024, E=16, k=4, I=64,
                                          latent=64, I_shared=32),
@@ -160,7 +163,7 @@ def test_small_layer_all_tokens(name):
 
 @pytest.mark.parametrize("name", ["bf16_ragged", "bf16_no_shared", "latent_small",
                                   "latent_small_shared", "latent_split_small", "bf16_e6",
-                                  "bf16_e13"])
+                                  "bf16_e13", "bf16_max_routing"])
 def test_stream_and_grouped_paths_agree_with_oracle(name):
     inp = mi.make_layer(SMALL[name], seed=2)
     ys, _ = check_full(inp, "stream")
