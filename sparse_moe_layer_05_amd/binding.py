@@ -141,6 +141,52 @@ def expert_dtype_code(x, W_up, s_up=None, W_in=None, expert_dtype=None) -> int:
     return _dtype_code(W_up)
 
 
+def _need(t, shape, what, dtype=None, device=None):
+    if t is None:
+        raise ValueError(f"{what} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{what} has dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{what} is on {t.device}, expected {device}")
+
+
+def check_shapes(desc, x, W_r, b, W_up, W_down, s_up=None, s_down=None, Ws_up=None,
+                 Ws_down=None, W_in=None, W_out=None):
+    """Every tensor must have the shape, dtype and device the descriptor implies: the library
+    only sees pointers, so a mismatch would make it read outside a buffer."""
+    T, H, E, I, Is, L = desc.T, desc.H, desc.E, desc.I, desc.I_shared, desc.latent
+    D = L or H
+    act = x.dtype
+    dev = x.device
+    _need(W_r, (E, H), "W_r", act, dev)
+    _need(b, (E,), "b", torch.float32, dev)
+    ed = desc.expert_dtype
+    if ed in (MOE_F32, MOE_BF16):
+        _need(W_up, (E, I, D), "W_up", act, dev)
+        _need(W_down, (E, D, I), "W_down", act, dev)
+    elif ed == MOE_FP8_E4M3:
+        _need(W_up, (E, I, D), "W_up", W_up.dtype, dev)
+        _need(W_down, (E, D, I), "W_down", W_down.dtype, dev)
+        _need(s_up, (E, I), "s_up", torch.float32, dev)
+        _need(s_down, (E, D), "s_down", torch.float32, dev)
+    else:  # MXFP4 packs two elements per byte, MXFP8 one; one uint8 scale per 32 along K
+        per = 2 if ed == MOE_MXFP4 else 1
+        _need(W_up, (E, I, D // per), "W_up", W_up.dtype, dev)
+        _need(W_down, (E, D, I // per), "W_down", W_down.dtype, dev)
+        _need(s_up, (E, I, D // 32), "s_up", torch.uint8, dev)
+        _need(s_down, (E, D, I // 32), "s_down", torch.uint8, dev)
+    if ed not in (MOE_F32, MOE_BF16) and W_up.element_size() != 1:
+        raise ValueError("8- and 4-bit expert weights are passed as 1-byte tensors")
+    if Is:
+        _need(Ws_up, (Is, H), "Ws_up", act, dev)
+        _need(Ws_down, (H, Is), "Ws_down", act, dev)
+    if L:
+        _need(W_in, (L, H), "W_in", act, dev)
+        _need(W_out, (H, L), "W_out", act, dev)
+
+
 def make_desc(x, W_r, W_up, k, Ws_up=None, W_in=None, path="auto", routing_given=False,
               s_up=None, expert_dtype=None):
     T, H = x.shape
@@ -179,6 +225,10 @@ class Layer:
                  routing_given=False, out=None, expert_dtype=None):
         self.desc = make_desc(x, W_r, W_up, k, Ws_up, W_in, path, routing_given, s_up,
                               expert_dtype)
+        check_shapes(self.desc, x, W_r, b, W_up, W_down, s_up, s_down, Ws_up, Ws_down, W_in,
+                     W_out)
+        if out is not None:
+            _need(out, x.shape, "out", x.dtype, x.device)
         w = MoeWeights()
         w.x, w.W_r, w.b, w.W_up, w.W_down = _p(x), _p(W_r), _p(b), _p(W_up), _p(W_down)
         w.s_up, w.s_down = _p(s_up), _p(s_down)
@@ -211,6 +261,8 @@ class Backward:
     def __init__(self, x, W_r, b, W_up, W_down, k, *, Ws_up=None, Ws_down=None, W_in=None,
                  W_out=None):
         self.desc = make_desc(x, W_r, W_up, k, Ws_up, W_in)
+        check_shapes(self.desc, x, W_r, b, W_up, W_down, Ws_up=Ws_up, Ws_down=Ws_down,
+                     W_in=W_in, W_out=W_out)
         w = MoeWeights()
         w.x, w.W_r, w.b, w.W_up, w.W_down = _p(x), _p(W_r), _p(b), _p(W_up), _p(W_down)
         w.Ws_up, w.Ws_down, w.W_in, w.W_out = _p(Ws_up), _p(Ws_down), _p(W_in), _p(W_out)
@@ -239,13 +291,18 @@ class Backward:
     def forward_train(self, y=None, stream=None):
         """y of the layer (grouped path), keeping what the backward pass reads in the workspace:
         later calls with ``saved=True`` skip the recompute."""
-        y = y if y is not None else torch.empty_like(self._keep[0])
+        x = self._keep[0]
+        if y is None:
+            y = torch.empty_like(x)
+        _need(y, x.shape, "y", x.dtype, x.device)
         rc = lib().moe_layer_forward_train(C.byref(self.desc), C.byref(self.w), _p(y),
                                            _p(self.ws), self.ws_bytes, _stream(stream))
         _check(rc, "moe_layer_forward_train")
         return y
 
     def __call__(self, dy, stream=None, saved=False):
+        x = self._keep[0]
+        _need(dy, x.shape, "dy", x.dtype, x.device)
         d = MoeDesc.from_buffer_copy(self.desc)
         if saved:
             d.flags |= SAVED_IN_WORKSPACE

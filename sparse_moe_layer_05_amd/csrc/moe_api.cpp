@@ -173,6 +173,21 @@ hipError_t side_of(Side** out) {
   return hipSuccess;
 }
 
+// Joins the side stream back into `s` on every exit once work was forked onto it, so that an
+// error return never leaves the caller's stream unordered with work that still writes into the
+// caller's buffers. The success path joins explicitly and sets `done`.
+struct SideJoin {
+  Side* side = nullptr;
+  hipStream_t s = nullptr;
+  bool done = false;
+  ~SideJoin() {
+    if (side && !done) {
+      (void)hipEventRecord(side->join, side->s);
+      (void)hipStreamWaitEvent(s, side->join, 0);
+    }
+  }
+};
+
 // ---------------------------------------------------------------- launch trace (diagnostics)
 struct Trace {
   int cap = 0, n = 0;
@@ -280,9 +295,12 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
   // shared-expert units out in the routed launches instead, which measured faster there.) The
   // per-row e4m3 copy of x does not depend on routing either: it runs first on the side stream.
   Side* side = nullptr;
+  SideJoin join;
   if (stream_path && narrow && Is && !L) {
     MOE_TRY(side_of(&side));
     MOE_TRY(hipEventRecord(side->fork, s));
+    join.side = side;
+    join.s = s;
     MOE_TRY(hipStreamWaitEvent(side->s, side->fork, 0));
     {
       MOE_SPAN_ON("quant_rows:x", side->s);
@@ -504,7 +522,10 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
       S = Sw;
     } else if (Is && stream_path) {
       S = (const float*)Y + (size_t)P * D;
-      if (side) MOE_TRY(hipStreamWaitEvent(s, side->join, 0));  // shared rows of Y are written
+      if (side) {  // shared rows of Y are written
+        MOE_TRY(hipStreamWaitEvent(s, side->join, 0));
+        join.done = true;
+      }
     }
     MOE_SPAN("combine:y");
     MOE_TRY(launch_combine(Y, y_elt, D, S, H, pos, gates, T, D, k, y, act, H, s));

@@ -256,3 +256,34 @@ def test_training_forward_and_saved_flag_validation():
     assert ft(ws_bytes=16) == B.MOE_ERR_WORKSPACE
     assert ft(desc(latent=64, expert_dtype=2)) == B.MOE_ERR_UNSUPPORTED
     assert ft(desc(T=0)) == B.MOE_OK
+
+
+def test_binding_rejects_tensors_that_do_not_match_the_descriptor():
+    # the library sees only pointers: the binding checks shapes, dtypes and devices first
+    import torch
+    bf = torch.bfloat16
+    T, H, E, k, I, Is = 8, 64, 4, 2, 32, 16
+    x = torch.zeros(T, H, dtype=bf)
+    t = dict(W_r=torch.zeros(E, H, dtype=bf), b=torch.zeros(E), W_up=torch.zeros(E, I, H, dtype=bf),
+             W_down=torch.zeros(E, H, I, dtype=bf), Ws_up=torch.zeros(Is, H, dtype=bf),
+             Ws_down=torch.zeros(H, Is, dtype=bf))
+    d = B.make_desc(x, t["W_r"], t["W_up"], k, t["Ws_up"])
+    B.check_shapes(d, x, **t)                                   # consistent: no error
+    bad = [("W_down", torch.zeros(E, I, H, dtype=bf)),          # transposed expert stack
+           ("W_r", torch.zeros(E, H)),                          # fp32 router with bf16 x
+           ("b", torch.zeros(E + 1)),
+           ("Ws_down", torch.zeros(Is, H, dtype=bf)),
+           ("Ws_up", None)]
+    for name, v in bad:
+        with pytest.raises(ValueError):
+            B.check_shapes(d, x, **dict(t, **{name: v}))
+    # 4-bit experts: two elements per byte, one scale byte per 32 along K
+    u8 = torch.uint8
+    mx = dict(W_r=t["W_r"], b=t["b"], W_up=torch.zeros(E, I, H // 2, dtype=u8),
+              W_down=torch.zeros(E, H, I // 2, dtype=u8), s_up=torch.zeros(E, I, H // 32, dtype=u8),
+              s_down=torch.zeros(E, H, I // 32, dtype=u8))
+    dm = B.make_desc(x, mx["W_r"], mx["W_up"], k, s_up=mx["s_up"])
+    assert dm.expert_dtype == B.MOE_MXFP4
+    B.check_shapes(dm, x, **mx)
+    with pytest.raises(ValueError):
+        B.check_shapes(dm, x, **dict(mx, s_down=torch.zeros(E, H, I // 16, dtype=u8)))
