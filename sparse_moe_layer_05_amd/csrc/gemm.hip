@@ -12,7 +12,8 @@
 // order inside a row is XOR-swizzled by choosing which global chunk each lane fetches, so the
 // fragment reads of 16 consecutive rows touch 16 distinct 16-byte bank groups. In a final
 // partial K-step, lanes whose chunk lies beyond K skip the access and their slots are zeroed
-// once the stage has landed. NS stages are in flight: K-step ks + NS - 1 is loaded while K-step
+// once the stage has landed; the padding rows of a partial M-tile skip every access (their
+// products are never stored). NS stages are in flight: K-step ks + NS - 1 is loaded while K-step
 // ks is multiplied.
 // The epilogue stages each wave's accumulators through LDS in 16-row strips so that every lane
 // finishes 8 consecutive columns of a row with 16-byte loads and stores.
@@ -145,9 +146,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < A_GRP; ++i) {
       const int r = (wave + NW * i) * RPI + lrow;
-      const int rr = r < rows ? r : 0;
-      int64_t src = row0 + rr;
-      if (!seg2 && p.a_gather) src = p.a_gather[row0 + rr];
+      if (r >= rows) {  // padding row of a partial tile: no access (its products are discarded)
+        oa[i] = 0xFFFFFFF0u;
+        continue;
+      }
+      int64_t src = row0 + r;
+      if (!seg2 && p.a_gather) src = p.a_gather[row0 + r];
       oa[i] = (uint32_t)(src * (seg2 ? p.lda2 : p.lda) * EB) + cofs;
     }
 #pragma unroll

@@ -159,11 +159,10 @@ void gemm_kt_kernel(KtParams p) {
       col = min(col, p.M - 8);
       ka[i] = kr;
       oa[i] = (uint32_t)(kr * p.lda * 2 + col * 2);
-    } else {
+    } else {  // padding rows of a partial tile take no access (their products are discarded)
       const int r = (wave + NW * i) * 8 + lrow;
-      const int64_t src = row0 + (r < rows ? r : 0);
       ka[i] = 0;
-      oa[i] = (uint32_t)(src * p.lda * 2) + cofs;
+      oa[i] = r < rows ? (uint32_t)((int64_t)(row0 + r) * p.lda * 2) + cofs : 0xFFFFFFF0u;
     }
   }
 #pragma unroll
