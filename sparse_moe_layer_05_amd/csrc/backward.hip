@@ -1,6 +1,6 @@
 // Non-GEMM kernels of the MoE layer's backward pass (bf16 layers): the padded per-expert offsets
 // and launch order, the gradient through the routing gates, the router weight gradient, the sum
-// that forms dx, and the gather of token rows into pair order.
+// that forms dx, and the per-token sum of the LatentMoE experts' input gradient.
 //
 // The gradient is that of the forward of the Nemotron 3 MoE layer ("NVIDIA Nemotron 3: Efficient
 // and Open Intelligence", section 2.2; "Nemotron 3 Nano: Open, Efficient Mixture-of-Experts
@@ -291,24 +291,7 @@ __global__ __launch_bounds__(256) void pairs_to_tokens_kernel(const float* du, c
   }
 }
 
-// Xp[p] = x[perm[p]]: one workgroup per pair row, 16-byte copies.
-__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* x, const int32_t* perm,
-                                                          int H, uint16_t* Xp) {
-  const int p = blockIdx.x;
-  const uint4* src = (const uint4*)(x + (int64_t)perm[p] * H);
-  uint4* dst = (uint4*)(Xp + (int64_t)p * H);
-  for (int c = threadIdx.x; c < H / 8; c += 256) dst[c] = src[c];
-}
-
 }  // namespace
-
-hipError_t launch_gather_rows(const uint16_t* x, const int32_t* perm, int P, int H, uint16_t* Xp,
-                              hipStream_t s) {
-  if (P <= 0) return hipSuccess;
-  if (H % 8) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(P), dim3(256), 0, s, x, perm, H, Xp);
-  return hipGetLastError();
-}
 
 hipError_t launch_pad_offsets(const int32_t* counts, int G, int32_t* koffs, int32_t* order,
                               hipStream_t s) {

@@ -36,8 +36,4 @@ hipError_t launch_bwd_dx(const float* dxa, const float* dxb, const float* du, co
 hipError_t launch_pairs_to_tokens(const float* du, const int32_t* pos, int T, int D, int k,
                                   uint16_t* out, hipStream_t s);
 
-// Xp[p] = x[perm[p]] for the P pair rows (bf16 rows of H, H a multiple of 8).
-hipError_t launch_gather_rows(const uint16_t* x, const int32_t* perm, int P, int H, uint16_t* Xp,
-                              hipStream_t s);
-
 }  // namespace moe

@@ -139,8 +139,10 @@ void gemm_kt_kernel(KtParams p) {
   // Operand resources. K-major operands start at the group's first k row and end after its
   // last, so a load of a row beyond the window reads nothing.
   const uint8_t* Bg = (const uint8_t*)p.B + (int64_t)g * p.b_gstride * 2;
+  const bool gath = p.b_gather != nullptr;  // B rows gathered (K-grouped launches)
   const __amdgpu_buffer_rsrc_t rb =
-      rsrc(Bg + (int64_t)k0 * p.ldb * 2, (int64_t)kc * p.ldb * 2);
+      gath ? rsrc(p.B, (int64_t)p.b_rows * p.ldb * 2)
+           : rsrc(Bg + (int64_t)k0 * p.ldb * 2, (int64_t)kc * p.ldb * 2);
   const __amdgpu_buffer_rsrc_t ra =
       TA ? rsrc((const uint8_t*)p.A + (int64_t)k0 * p.lda * 2, (int64_t)kc * p.lda * 2)
          : rsrc(p.A, (int64_t)p.a_rows * p.lda * 2);
@@ -172,8 +174,17 @@ void gemm_kt_kernel(KtParams p) {
     int col = n0 + ((slot ^ swz_km(kr)) << 3);
     col = min(col, p.N - 8);
     kb[i] = kr;
-    ob[i] = (uint32_t)(kr * p.ldb * 2 + col * 2);
+    ob[i] = gath ? (uint32_t)(col * 2) : (uint32_t)(kr * p.ldb * 2 + col * 2);
   }
+  // gathered B: the source rows of this lane's B loads for the step issued next (loaded one
+  // step ahead; -1 past the window)
+  int grow[B_GRP];
+  auto fetch_rows = [&](int ks) {
+    const int left = kc - ks * KS;
+#pragma unroll
+    for (int i = 0; i < B_GRP; ++i)
+      grow[i] = kb[i] < left ? p.b_gather[k0 + ks * KS + kb[i]] : -1;
+  };
 
   const int nk = cdiv(kc, KS);
   // Issue K-step ks into stage st. Dead lanes (k rows beyond the window; for a K-contiguous A,
@@ -189,11 +200,21 @@ void gemm_kt_kernel(KtParams p) {
           ra, (__attribute__((address_space(3))) void*)(st + (wave + NW * i) * 1024), 16,
           (int)(live ? oa[i] : 0xFFFFFFF0u), sa, 0, 0);
     }
+    if (gath) {
 #pragma unroll
-    for (int i = 0; i < B_GRP; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb, (__attribute__((address_space(3))) void*)(st + SA + (wave + NW * i) * 1024), 16,
-          (int)(kb[i] < left ? ob[i] : 0xFFFFFFF0u), sb, 0, 0);
+      for (int i = 0; i < B_GRP; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (__attribute__((address_space(3))) void*)(st + SA + (wave + NW * i) * 1024), 16,
+            (int)(grow[i] >= 0 ? (uint32_t)grow[i] * (uint32_t)(p.ldb * 2) + ob[i] : 0xFFFFFFF0u),
+            0, 0, 0);
+      if (ks + 1 < nk) fetch_rows(ks + 1);
+    } else {
+#pragma unroll
+      for (int i = 0; i < B_GRP; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (__attribute__((address_space(3))) void*)(st + SA + (wave + NW * i) * 1024), 16,
+            (int)(kb[i] < left ? ob[i] : 0xFFFFFFF0u), sb, 0, 0);
+    }
   };
   auto fix_tail = [&](int ks, uint8_t* st) {
     const int left = kc - ks * KS;
@@ -249,6 +270,7 @@ void gemm_kt_kernel(KtParams p) {
   };
 
   // Two stages: K-step ks + 1 is loaded while K-step ks is multiplied.
+  if (gath && nk > 0) fetch_rows(0);
   if (nk > 0) issue(0, smem);
   for (int ks = 0; ks < nk; ++ks) {
     __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));  // vmcnt(0)
@@ -334,7 +356,9 @@ hipError_t launch_gemm_kt(int ta, int tb, Elt out, Epi epi, const KtParams& p, i
   // operand's K rows, and a K-contiguous A's rows, must span less than 2 GiB.
   constexpr int64_t kLim = ((int64_t)1 << 31) - 1;
   const int64_t krows = p.kgrp ? p.a_rows : p.K;  // K-grouped: the stored rows of both operands
-  if ((int64_t)krows * p.ldb * 2 > kLim || (ta && (int64_t)krows * p.lda * 2 > kLim) ||
+  const int64_t brows = p.b_gather ? p.b_rows : krows;
+  if (p.b_gather && (!p.kgrp || p.b_rows < 1)) return hipErrorInvalidValue;
+  if ((int64_t)brows * p.ldb * 2 > kLim || (ta && (int64_t)krows * p.lda * 2 > kLim) ||
       (!ta && (int64_t)p.a_rows * p.lda * 2 > kLim))
     return hipErrorInvalidValue;
   const int mt = p.kgrp ? p.G * cdiv(p.M, BM) : (p.mt_start ? max_mtiles : cdiv(p.M, BM));

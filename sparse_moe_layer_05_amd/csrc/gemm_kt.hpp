@@ -35,6 +35,10 @@ struct KtParams {
   // [kgrp[g], kgrp[g+1]) of both K-major operands; korder (optional) is the launch order.
   const int32_t* kgrp = nullptr;
   const int32_t* korder = nullptr;
+  // K-grouped launches, optional: stored K row k of B is row b_gather[k] of B (b_rows rows), so
+  // a pair-ordered operand is read straight from the token rows it gathers.
+  const int32_t* b_gather = nullptr;
+  int b_rows = 0;
 };
 
 // ta / tb: 1 when A / B is stored K-major. Provided: (ta, tb, out, epi) in

@@ -565,7 +565,6 @@ struct BwdPlan {
   size_t u = 0, z = 0;                                         // saved (LatentMoE): x W_in^T, z
   size_t dYp = 0, dzp = 0, da = 0, du = 0, das = 0, dxs = 0;   // backward intermediates
   size_t wr_part = 0;                                          // dW_r chunk sums
-  size_t Xp = 0;                                               // expert inputs in pair order
   size_t dacc = 0, dut = 0, dxl = 0;                           // LatentMoE: dz, du per token, dx
   size_t total = 0;
 };
@@ -623,7 +622,6 @@ int32_t make_bwd_plan(const moe_desc_t* d, BwdPlan* out) {
   p.wr_part = take((size_t)(p.Ppad / 64) * H * 4);
   p.da = take(P * I * 2);
   p.du = take(P * D * 4);
-  p.Xp = take(P * D * 2);
   if (Is) {
     p.das = take(T * Is * 2);
     p.dxs = take(T * H * 4);
@@ -879,12 +877,8 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
   }
 
   // (5) routed weight gradients, reduced over each expert's own pair rows (the K window
-  // [offsets[e], offsets[e+1]) of the pair-ordered operands, read as stored), heaviest first
-  uint16_t* Xp = (uint16_t*)at(pl.Xp);
-  {
-    MOE_SPAN("gather_rows:pairs");
-    MOE_TRY(launch_gather_rows((const uint16_t*)(L ? at(pl.u) : w->x), perm, P, D, Xp, s));
-  }
+  // [offsets[e], offsets[e+1]) of the pair-ordered operands, read as stored; the experts'
+  // inputs are read from the token rows through the dispatch permutation), heaviest first
   {
     KtParams g;  // dW_down[e] [D][I] = dY_e^T h_e
     g.A = dYp; g.lda = D; g.B = h; g.ldb = I; g.a_rows = P;
@@ -895,7 +889,8 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
   }
   {
     KtParams g;  // dW_up[e] [I][D] = da_e^T (expert input)_e
-    g.A = da; g.lda = I; g.B = Xp; g.ldb = D; g.a_rows = P;
+    g.A = da; g.lda = I; g.B = L ? at(pl.u) : w->x; g.ldb = D; g.a_rows = P;
+    g.b_gather = perm; g.b_rows = T;
     g.C = gr->dW_up; g.ldc = D; g.c_gstride = (int64_t)I * D;
     g.M = I; g.N = D; g.G = E; g.kgrp = offsets; g.korder = korder;
     MOE_SPAN("gemm_kt_f32out:bwd_routed_wgrad_up");
