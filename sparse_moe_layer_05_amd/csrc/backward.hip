@@ -223,15 +223,21 @@ __global__ __launch_bounds__(256) void router_weight_sum_kernel(const float* par
 
 // dx[t] = dxa[t] + dxb[t] (each optional) + sum_j du[pos(t, j)] (du optional)
 //         + sum_j dzp[pos(t, j)] W_r[e_j], added in that fixed order, fp32. The rows of du are
-// read kPairBatch at a time with all their loads in flight.
-__global__ __launch_bounds__(256) void bwd_dx_kernel(const float* dxa, const float* dxb,
-                                                     const float* du, const float* dzp,
-                                                     const uint16_t* Wr, const int32_t* idx,
-                                                     const int32_t* pos, int H, int k, float* dx) {
+// read kPairBatch at a time with all their loads in flight; the pointers do not alias, so two
+// column chunks' loads can be in flight together.
+__global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ dxa,
+                                                     const float* __restrict__ dxb,
+                                                     const float* __restrict__ du,
+                                                     const float* __restrict__ dzp,
+                                                     const uint16_t* __restrict__ Wr,
+                                                     const int32_t* __restrict__ idx,
+                                                     const int32_t* __restrict__ pos, int H, int k,
+                                                     float* __restrict__ dx) {
   constexpr int KB = kPairBatch;
   const int t = blockIdx.x;
   const int32_t* post = pos + (int64_t)t * k;
   const int32_t* idxt = idx + (int64_t)t * k;
+#pragma unroll 2
   for (int c = threadIdx.x * 4; c < H; c += 1024) {
     float4 a = dxa ? *(const float4*)(dxa + (int64_t)t * H + c) : make_float4(0.f, 0.f, 0.f, 0.f);
     if (dxb) {
@@ -268,11 +274,14 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* dxa, const flo
 
 // out[t] = bf16(sum_j du[pos(t, j)]) in j order: the gradient of a token's expert input (the
 // LatentMoE projection u), rows of D. Pair rows are read kPairBatch at a time.
-__global__ __launch_bounds__(256) void pairs_to_tokens_kernel(const float* du, const int32_t* pos,
-                                                              int D, int k, uint16_t* out) {
+__global__ __launch_bounds__(256) void pairs_to_tokens_kernel(const float* __restrict__ du,
+                                                              const int32_t* __restrict__ pos,
+                                                              int D, int k,
+                                                              uint16_t* __restrict__ out) {
   constexpr int KB = kPairBatch;
   const int t = blockIdx.x;
   const int32_t* post = pos + (int64_t)t * k;
+#pragma unroll 2
   for (int c = threadIdx.x * 4; c < D; c += 1024) {
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j0 = 0; j0 < k; j0 += KB) {
