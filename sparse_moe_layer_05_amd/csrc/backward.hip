@@ -59,11 +59,15 @@ __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* counts
 // products are reduced together; each is still summed in a fixed order (per thread along the
 // row, then a butterfly within each wave, then the waves in order).
 constexpr int kPairBatch = 8;
-__global__ __launch_bounds__(256) void bwd_route_kernel(const uint16_t* dy, const uint16_t* Yp,
-                                                        const float* logits, const int32_t* idx,
-                                                        const float* gates, const int32_t* pos,
-                                                        int H, int E, int k, uint16_t* dYp,
-                                                        float* dzp) {
+__global__ __launch_bounds__(256) void bwd_route_kernel(const uint16_t* __restrict__ dy,
+                                                        const uint16_t* __restrict__ Yp,
+                                                        const float* __restrict__ logits,
+                                                        const int32_t* __restrict__ idx,
+                                                        const float* __restrict__ gates,
+                                                        const int32_t* __restrict__ pos,
+                                                        int H, int E, int k,
+                                                        uint16_t* __restrict__ dYp,
+                                                        float* __restrict__ dzp) {
   constexpr int KB = kPairBatch;
   __shared__ float red[4][KB];
   __shared__ float dg[kMaxK];
@@ -125,19 +129,19 @@ __global__ __launch_bounds__(256) void bwd_route_kernel(const uint16_t* dy, cons
       if (r >= 0) dzp[r] = (dg[j] - gdg) / Z * sj[j] * (1.f - sj[j]);
     }
   }
-  for (int j = 0; j < k; ++j) {
-    const int r = pos[(int64_t)t * k + j];
-    if (r < 0) continue;
-    const float g = gates[(int64_t)t * k + j];
-    uint16_t* o = dYp + (int64_t)r * H;
-    for (int c = tid; c < nch; c += 256) {
-      const uint4 a = *(const uint4*)(dyt + c * 8);
-      const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
+  // rows g_j dy_t: each chunk of dy is loaded once and stored scaled to the token's k rows
+  for (int c = tid; c < nch; c += 256) {
+    const uint4 a = *(const uint4*)(dyt + c * 8);
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
+    for (int j = 0; j < k; ++j) {
+      const int r = pos[(int64_t)t * k + j];
+      if (r < 0) continue;
+      const float g = gates[(int64_t)t * k + j];
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         w[e] = pack_bf16x2(g * bf16_bits_to_f32(wa[e] & 0xFFFF), g * bf16_bits_to_f32(wa[e] >> 16));
-      *(uint4*)(o + c * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+      *(uint4*)(dYp + (int64_t)r * H + c * 8) = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
 }
