@@ -30,8 +30,14 @@
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null stream).
  *   - Return value: MOE_OK (0) or a negative moe_status; nothing is launched on an error found
  *     before launch. MOE_ERR_HIP reports a failed launch (hipGetLastError after enqueueing).
- *   - Thread safety: stateless apart from a per-device properties cache; concurrent calls on
- *     different streams need different workspaces and outputs.
+ *   - State and thread safety: the library keeps, per device and for the life of the process,
+ *     one side stream and three events, created on the first call that needs them (the decode
+ *     path of a layer with a shared expert and 8- or 4-bit experts forks the shared expert onto
+ *     that stream and joins it back before the combine). Calls that use it hold a per-device
+ *     lock while they enqueue, so concurrent host threads may call on different streams; their
+ *     side-stream work then runs one call after another in lock order. Concurrent calls need
+ *     different workspaces and outputs. The launch trace (moe_trace_*) is process-wide and not
+ *     for concurrent calls.
  *   - Dimension rules: H, I, I_shared and latent are multiples of 16; 1 <= k <= E <= 1024,
  *     k <= 64; T >= 0 (T == 0 is a no-op that returns MOE_OK). MOE_MXFP4 / MOE_MXFP8 experts
  *     also need D (H, or latent) and I to be multiples of 32 (else MOE_ERR_INVALID_ARG).
@@ -199,8 +205,9 @@ int32_t moe_bias_update(const int32_t *counts, const float *target, int32_t E, f
  * path bits ignored, MOE_ROUTING_GIVEN not accepted) -- else MOE_ERR_UNSUPPORTED. Without
  * MOE_SAVED_IN_WORKSPACE the call first recomputes the forward's routing and expert activations
  * from x; with it, it reads them from the workspace, where moe_layer_forward_train (same
- * descriptor apart from that flag, same weights and x) left them. Either way it makes transposed
- * copies of the weights in the workspace, and it never overwrites the saved part, so several
+ * descriptor apart from that flag, same weights and x) left them. Either way the weights are
+ * read in place as stored (the products that need them K-major stage them through transposing
+ * LDS reads; nothing is copied), and the call never overwrites the saved part, so several
  * backward calls (e.g. for several dy) may follow one moe_layer_forward_train. Pointers: 16-byte
  * aligned device memory owned by the caller. Workspace: moe_backward_workspace_size bytes.
  * Asynchronous on `stream`; nothing is allocated or synchronised. Results are deterministic (no

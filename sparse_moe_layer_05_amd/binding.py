@@ -123,6 +123,16 @@ def _p(t):
     return t.data_ptr()
 
 
+def _used_on(stream, *tensors):
+    """Tell the caching allocator that `tensors` (allocated on the current stream) are in use on
+    `stream` too, so that their memory is not handed out again before that stream's work ends."""
+    if stream is None:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def _stream(stream):
     s = stream if stream is not None else torch.cuda.current_stream()
     return C.c_void_p(s.cuda_stream)
@@ -341,6 +351,7 @@ def route(b, k, *, logits=None, x=None, W_r=None, stream=None):
     rc = lib().moe_route(_p(logits), _p(x), _p(W_r), _p(b), T, H, E, k, dt, _p(idx), _p(gates),
                          _p(lo), _stream(stream))
     _check(rc, "moe_route")
+    _used_on(stream, idx, gates, lo)
     return idx, gates, (logits if logits is not None else lo)
 
 
@@ -358,6 +369,8 @@ def dispatch(idx, E, stream=None):
     rc = lib().moe_dispatch(_p(idx), T, E, k, _p(counts), _p(offsets), _p(perm), _p(pos), _p(ws),
                             n.value, _stream(stream))
     _check(rc, "moe_dispatch")
+    # the workspace is dropped here while the kernels may still run on `stream`
+    _used_on(stream, ws, counts, offsets, perm, pos)
     return counts, offsets, perm, pos
 
 

@@ -141,9 +141,13 @@ int32_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP
 // the life of the process. The decode path forks the shared expert onto it: that work does not
 // depend on routing, so it overlaps the router, top-k, dispatch and the routed experts, and is
 // joined back before the combine (a fork / join that stream capture also records).
+// The events are re-recorded by every call, so a call holds the device's `mu` from its fork
+// record to its last wait on `ready` / `join`: another thread's call cannot re-record them in
+// between.
 struct Side {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr, ready = nullptr;  // ready: expert inputs quantised
+  std::mutex mu;
 };
 constexpr int kMaxDevices = 64;
 Side g_side[kMaxDevices];
@@ -157,17 +161,19 @@ hipError_t side_of(Side** out) {
   std::lock_guard<std::mutex> lock(g_side_mu);
   Side& sd = g_side[dev];
   if (!sd.s) {
-    Side n;
-    if ((e = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&n.ready, hipEventDisableTiming)) != hipSuccess) {
-      if (n.fork) (void)hipEventDestroy(n.fork);
-      if (n.join) (void)hipEventDestroy(n.join);
-      (void)hipStreamDestroy(n.s);
+    hipStream_t st = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr, ready = nullptr;
+    if ((e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&fork, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&join, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&ready, hipEventDisableTiming)) != hipSuccess) {
+      if (fork) (void)hipEventDestroy(fork);
+      if (join) (void)hipEventDestroy(join);
+      (void)hipStreamDestroy(st);
       return e;
     }
-    sd = n;
+    sd.fork = fork; sd.join = join; sd.ready = ready;
+    sd.s = st;
   }
   *out = &sd;
   return hipSuccess;
@@ -295,9 +301,11 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
   // shared-expert units out in the routed launches instead, which measured faster there.) The
   // per-row e4m3 copy of x does not depend on routing either: it runs first on the side stream.
   Side* side = nullptr;
+  std::unique_lock<std::mutex> side_lock;  // released after `join` below has run
   SideJoin join;
   if (stream_path && narrow && Is && !L) {
     MOE_TRY(side_of(&side));
+    side_lock = std::unique_lock<std::mutex>(side->mu);
     MOE_TRY(hipEventRecord(side->fork, s));
     join.side = side;
     join.s = s;
@@ -579,7 +587,7 @@ int32_t make_bwd_plan(const moe_desc_t* d, BwdPlan* out) {
     return MOE_ERR_INVALID_ARG;
   if (d->flags & MOE_ROUTING_GIVEN) return MOE_ERR_UNSUPPORTED;
   if (d->act_dtype != MOE_BF16 || d->expert_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-  // the pair-ordered rows (g dy, and x or u gathered) are GEMM operands too: under 2 GiB
+  // the pair-ordered rows g dy [P, D] are a GEMM operand too: under 2 GiB
   if ((int64_t)fp.P * fp.D * 2 > ((int64_t)1 << 31) - 1) return MOE_ERR_INVALID_ARG;
   BwdPlan p;
   p.T = fp.T; p.H = fp.H; p.E = fp.E; p.k = fp.k; p.I = fp.I; p.Is = fp.Is; p.P = fp.P;
