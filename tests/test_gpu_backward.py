@@ -189,27 +189,93 @@ def test_backward_full_size(name):
             assert err <= TOL[n], (n, e, err)
 
 
-@pytest.mark.parametrize("name", ["nano_prefill_bf16", "latent_bf16"])
-def test_backward_full_size_with_dy_on_sampled_tokens(name):
-    # Real prefill shapes (the launches the bench times) with dy nonzero on 24 sampled tokens
-    # only. With the selection held fixed, a token's contribution to every gradient is zero
-    # when its dy is, so each gradient is a sum over the sampled tokens that the oracle computes
-    # exactly: dx on every token (exactly zero off the sample), dW_r, the shared expert's and
-    # the latent projections' gradients whole, and the expert stacks on the three experts the
-    # sample uses most; every expert the sample does not use gets exactly zero.
-    cfg = mi.CONFIGS[name]
-    say(f"[gpu] backward full size, dy on 24 tokens: {name} T={cfg.T}")
-    inp = mi.make_layer(cfg, seed=0)
-    rng = np.random.default_rng(17)
-    toks = np.sort(rng.choice(cfg.T, 24, replace=False)).astype(np.int32)
+GROUP_BM = 128   # row height of the grouped launches' M-tiles over the pair rows
+
+
+def tile_cover_tokens(idx, E, T, seed, bm=GROUP_BM):
+    """Tokens whose pair rows meet every (expert, bm-row M-tile) of the grouped launches over
+    the pair rows (rows in the dispatch order of the selection idx), and every bm-row band of T
+    (dense launches over all tokens); a partial tile is met at its last row."""
+    rng = np.random.default_rng(seed)
+    counts, offsets, perm, pos = (a.astype(np.int64) for a in O.dispatch(idx, E))
+    expert_of = np.repeat(np.arange(E), counts)
+    tile_of = (np.arange(offsets[-1]) - offsets[expert_of]) // bm
+    covered, chosen = set(), set()
+    for e in range(E):
+        for mt in range(-(-int(counts[e]) // bm)):
+            if (e, mt) in covered:
+                continue
+            lo = offsets[e] + mt * bm
+            hi = min(lo + bm, offsets[e + 1])
+            t = int(perm[hi - 1 if hi - lo < bm else int(rng.integers(lo, hi))])
+            chosen.add(t)
+            covered.update((int(expert_of[r]), int(tile_of[r])) for r in pos[t])
+    assert len(covered) == int(np.sum(-(-counts // bm)))
+    for b0 in range(0, T, bm):
+        if not any(b0 <= t < b0 + bm for t in chosen):
+            chosen.add(int(rng.integers(b0, min(T, b0 + bm))))
+    return np.array(sorted(chosen), np.int32)
+
+
+def expert_cover_tokens(idx, E, seed):
+    """A few tokens that between them select every expert that has any token."""
+    rng = np.random.default_rng(seed)
+    used = np.zeros(E, bool)
+    chosen = []
+    for e in range(E):
+        if used[e]:
+            continue
+        holders = np.flatnonzero((idx == e).any(axis=1))
+        if holders.size == 0:
+            continue
+        t = int(rng.choice(holders))
+        chosen.append(t)
+        used[idx[t]] = True
+    return np.array(sorted(chosen), np.int32)
+
+
+def dy_on(cfg, toks):
+    """The seeded upstream gradient, kept on `toks` and zero on every other token."""
     on = np.zeros(cfg.T, bool)
     on[toks] = True
     dy = mi.make_grad_output(cfg, seed=0)
     dy = np.where(on[:, None], dy, np.zeros_like(dy))        # bf16 bit pattern 0 is +0.0
-    dy64 = mi.bf16_bits_to_f32(dy).astype(np.float64)
+    return on, dy, mi.bf16_bits_to_f32(dy).astype(np.float64)
+
+
+def expert_stack_errors(inp, idx, dy64, toks, experts, got):
+    """Relative Frobenius errors of the GPU's dW_up / dW_down of each listed expert against the
+    oracle's over the listed tokens: {expert: (tokens, err_up, err_down)} (one thread per
+    expert; each oracle call runs that expert's tokens, and only the errors are kept)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one(e):
+        mine = toks[(idx[toks] == e).any(axis=1)]
+        r = O.backward(inp, idx[mine], dy64[mine], tokens=mine, want=("dW_up", "dW_down"),
+                       expert=int(e))
+        return (len(mine), rel_frob(got["dW_up"][e], r["dW_up"]),
+                rel_frob(got["dW_down"][e], r["dW_down"]))
+    with ThreadPoolExecutor(THREADS) as ex:
+        return dict(zip(experts, ex.map(one, experts)))
+
+
+@pytest.mark.parametrize("name", ["nano_prefill_bf16", "latent_bf16"])
+def test_backward_full_size_with_dy_on_sampled_tokens(name):
+    # Real prefill shapes (the launches the bench times) with dy nonzero only on a token set
+    # that meets every tile of the grouped launches over the pair rows (each expert's M-tiles)
+    # and every band of the dense launches over all tokens. With the selection held fixed, a
+    # token's contribution to every gradient is zero when its dy is, so each gradient is a sum
+    # over the sampled tokens that the oracle computes exactly: dx on every token (exactly zero
+    # off the sample), dW_r, the shared expert's and the latent projections' gradients whole,
+    # and the expert stacks on the three experts the sample uses most.
+    cfg = mi.CONFIGS[name]
+    inp = mi.make_layer(cfg, seed=0)
     dev = moe.to_device(inp)
-    dy_dev = moe.to_device({"dy": dy})["dy"]
     idx, _ = gpu_selection(dev, cfg.k)
+    toks = tile_cover_tokens(idx, cfg.E, cfg.T, seed=17)
+    say(f"[gpu] backward full size, dy on {len(toks)} tile-covering tokens: {name} T={cfg.T}")
+    on, dy, dy64 = dy_on(cfg, toks)
+    dy_dev = moe.to_device({"dy": dy})["dy"]
     check_selection(inp, idx, toks)
     got = grads_of(dev, cfg.k, dy_dev)
     assert not np.any(got["dx"][~on])
@@ -230,6 +296,35 @@ def test_backward_full_size_with_dy_on_sampled_tokens(name):
             err = rel_frob(got[n][e], r[n])
             say(f"[gpu]   {name} expert {e} ({len(mine)} tokens) {n}: rel Frobenius {err:.3e}")
             assert err <= TOL[n], (n, e, err)
+
+
+@pytest.mark.parametrize("name", ["nano_prefill_bf16", "latent_bf16"])
+def test_backward_full_size_every_expert_stack(name):
+    # Real prefill shapes with dy nonzero only on a few tokens that between them select every
+    # expert with any token: each expert's weight gradients are then sums over its sampled
+    # tokens, and every expert's whole dW_up and dW_down (all of its output tiles) is compared
+    # with the oracle; experts no token selects must come out exactly zero.
+    cfg = mi.CONFIGS[name]
+    inp = mi.make_layer(cfg, seed=0)
+    dev = moe.to_device(inp)
+    idx, _ = gpu_selection(dev, cfg.k)
+    toks = expert_cover_tokens(idx, cfg.E, seed=19)
+    say(f"[gpu] backward full size, dy on {len(toks)} expert-covering tokens: {name}")
+    on, dy, dy64 = dy_on(cfg, toks)
+    check_selection(inp, idx, toks)
+    got = grads_of(dev, cfg.k, moe.to_device({"dy": dy})["dy"])
+    used = np.bincount(idx[toks].ravel(), minlength=cfg.E)
+    assert np.array_equal(used > 0, np.bincount(idx.ravel(), minlength=cfg.E) > 0)
+    unused = np.flatnonzero(used == 0)
+    assert not np.any(got["dW_up"][unused]) and not np.any(got["dW_down"][unused])
+    errs = expert_stack_errors(inp, idx, dy64, toks, [int(e) for e in np.flatnonzero(used)],
+                               got)
+    up = max(v[1] for v in errs.values())
+    down = max(v[2] for v in errs.values())
+    say(f"[gpu]   {name}: {len(errs)} experts, worst rel Frobenius dW_up {up:.3e}, "
+        f"dW_down {down:.3e}")
+    for e, (n_tok, eu, ed) in errs.items():
+        assert eu <= TOL["dW_up"] and ed <= TOL["dW_down"], (e, n_tok, eu, ed)
 
 
 @pytest.mark.parametrize("name", ["bwd_ragged", "bwd_e13_sparse", "bwd_latent_shared"])

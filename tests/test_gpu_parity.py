@@ -15,8 +15,9 @@ Bars (from the layer's specification):
     the error it inherits from u and adds its own, sqrt((2 * 0.0255)^2 + 0.0255^2) ~ 0.057 on a
     layer with no shared expert, whose routed part is then the whole output (measured between
     the two oracle modes: 0.040 without a shared expert, 0.017 - 0.020 with one).
-Small layers are checked on every token; the full-size layers on sampled tokens plus whole-T
-routing and dispatch.
+Small layers are checked on every token. The full-size layers are checked on whole-T routing and
+dispatch, and on a token set that meets every tile of every launch (each routed expert's M-tiles,
+each band of the dense launches over all tokens) plus a random sample.
 """
 import dataclasses
 import os
@@ -439,6 +440,45 @@ def sample_tokens(T, n, seed):
     return np.unique(t)
 
 
+GROUP_BM = 128   # row height of the grouped launches' M-tiles (the dispatch builds their list)
+
+
+def tile_cover_tokens(offsets, perm, pos, T, seed, bm=GROUP_BM):
+    """Tokens whose rows meet every tile of the layer's launches at this routing: for every
+    (expert, bm-row M-tile) of the grouped up and down projections (rows in the dispatch order
+    offsets / perm), one token holding a row of it -- the last row when the tile is partial, a
+    seeded random row otherwise -- and one token in every bm-row band of T for the dense
+    launches over all tokens (shared expert, latent projections; their tiles are bm or 2 bm
+    rows high). A checked token is compared on all H columns, so every N-tile of its rows is
+    checked too."""
+    rng = np.random.default_rng(seed)
+    offsets, perm, pos = (np.asarray(a, np.int64) for a in (offsets, perm, pos))
+    counts = np.diff(offsets)
+    E = counts.shape[0]
+    expert_of = np.repeat(np.arange(E), counts)
+    tile_of = np.arange(offsets[-1]) - offsets[expert_of]
+    tile_of //= bm
+    covered = set()
+    chosen = set()
+    for e in range(E):
+        for mt in range(-(-int(counts[e]) // bm)):
+            if (e, mt) in covered:
+                continue
+            lo = offsets[e] + mt * bm
+            hi = min(lo + bm, offsets[e + 1])
+            r = hi - 1 if hi - lo < bm else int(rng.integers(lo, hi))
+            t = int(perm[r])
+            chosen.add(t)
+            for rr in pos[t]:
+                covered.add((int(expert_of[rr]), int(tile_of[rr])))
+    ntiles = int(np.sum(-(-counts // bm)))
+    assert len(covered) == ntiles
+    for b0 in range(0, T, bm):
+        if not any(b0 <= t < b0 + bm for t in chosen):
+            chosen.add(int(rng.integers(b0, min(T, b0 + bm))))
+    return np.array(sorted(chosen), np.int32), ntiles
+
+
 FULL = ["nano_prefill_bf16", "latent_bf16", "nano_fp8"]
 
 
@@ -469,8 +509,10 @@ def test_full_size_layer(name, full_runs):
     c, o, p, q = O.dispatch(rt["idx"], cfg.E)
     assert np.array_equal(c, rt["counts"]) and np.array_equal(o, rt["offsets"])
     assert np.array_equal(p, rt["perm"]) and np.array_equal(q, rt["pos"])
-    toks = sample_tokens(cfg.T, 24, 1)
-    say(f"[gpu] oracle on {len(toks)} sampled tokens of {name}")
+    cover, ntiles = tile_cover_tokens(rt["offsets"], rt["perm"], rt["pos"], cfg.T, seed=1)
+    toks = np.union1d(cover, sample_tokens(cfg.T, 24, 1)).astype(np.int32)
+    say(f"[gpu] oracle on {len(toks)} tokens of {name}: {len(cover)} meet all {ntiles} routed "
+        f"M-tiles and every {GROUP_BM}-token band, plus a random sample")
     ref, nswap = reference(inp, rt["idx"], toks)
     assert np.max(np.abs(rt["logits"][toks] - ref["logits"])) < 1e-4
     err = rel_frob(y[toks], ref["y"])

@@ -205,6 +205,52 @@ def test_route_invariant_to_common_bias_shift():
     np.testing.assert_allclose(g1.sum(1), 1.0, rtol=0, atol=1e-15)
 
 
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_logits_are_x_times_router_transpose(act):
+    # router logits of every token, and of a shuffled token subset with a repeat, against numpy's
+    # matmul of the exactly decoded inputs (a dropped or shifted term of the H sum, a transposed
+    # W_r or a wrong token row would all show)
+    c = cfg(T=29, H=96, E=12, k=3, I=16, act_dtype=act, expert_dtype=act)
+    inp = mi.make_layer(c, seed=21)
+    want = f64(inp, "x") @ f64(inp, "W_r").T
+    np.testing.assert_allclose(O.logits(inp), want, rtol=1e-13, atol=1e-13)
+    toks = np.array([17, 3, 28, 0, 3, 11], np.int32)
+    np.testing.assert_allclose(O.logits(inp, toks), want[toks], rtol=1e-13, atol=1e-13)
+
+
+def test_layer_is_gate_weighted_sum_of_selected_expert_mlps():
+    # generic routing (k of E, distinct gates per token) plus a shared expert, against numpy's
+    # dense squared-ReLU MLPs of the selected experts, on every token and on a token subset
+    c = cfg(T=23, H=48, E=9, k=3, I=24, I_shared=16, act_dtype="bf16", expert_dtype="bf16")
+    inp = mi.make_layer(c, seed=22)
+    r = O.forward(inp)
+    x, Wu, Wd = f64(inp, "x"), f64(inp, "W_up"), f64(inp, "W_down")
+    want = dense_mlp(x, f64(inp, "Ws_up"), f64(inp, "Ws_down"))
+    for t in range(c.T):
+        for j in range(c.k):
+            e = r["idx"][t, j]
+            want[t] += r["gates"][t, j] * dense_mlp(x[t:t + 1], Wu[e], Wd[e])[0]
+    np.testing.assert_allclose(r["y"], want, rtol=1e-12, atol=1e-13)
+    toks = np.array([22, 5, 0, 13], np.int32)
+    rs = O.forward(inp, toks)
+    np.testing.assert_allclose(rs["y"], want[toks], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("latent", [0, 32])
+def test_forward_of_a_token_subset_with_threads_equals_the_whole_call(latent):
+    # the parity tests at full size run the oracle on token subsets split over threads: every
+    # listed token's result must be the whole call's, bit for bit
+    c = cfg(T=41, H=64, E=10, k=4, I=24, I_shared=0 if latent else 16, latent=latent,
+            act_dtype="bf16", expert_dtype="bf16")
+    inp = mi.make_layer(c, seed=23)
+    whole = O.forward(inp)
+    toks = np.array([40, 2, 7, 7, 19, 0, 33, 25, 11], np.int32)
+    for threads in (1, 4):
+        part = O.forward(inp, toks, threads=threads)
+        for key in ("logits", "idx", "gates", "margin", "y"):
+            assert np.array_equal(part[key], whole[key][toks]), (threads, key)
+
+
 # ----------------------------------------------------------------------------- dispatch
 
 @pytest.mark.parametrize("T,E,k", [(1, 4, 1), (37, 8, 3), (64, 16, 2), (200, 128, 6)])
