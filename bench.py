@@ -35,7 +35,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="nano_decode_bf16")
-    ap.add_argument("--also", default="nano_prefill_bf16,latent_decode_bf16,nano_fp8_decode,"
+    ap.add_argument("--also", default="nano_prefill_bf16,latent_bf16,nano_fp8,tiny_f32,"
+                                      "latent_decode_bf16,nano_fp8_decode,"
                                       "nano_mxfp4_decode,nano_mxfp8_decode,latent_mxfp4_decode,"
                                       "latent_fp8_decode,nano_prefill_bf16+backward,"
                                       "latent_bf16+backward",
@@ -183,19 +184,26 @@ def mfma_dtype(kernel, cfg):
 
 # ------------------------------------------------------------------ one workload
 
-def prepare(name, moe, mi, torch, path, shared=None):
+def weights_key(cfg):
+    """Workloads with equal keys draw the same seeded weights (only x and the bias differ)."""
+    return (cfg.H, cfg.E, cfg.I, cfg.I_shared, cfg.latent, cfg.act_dtype, cfg.expert_dtype)
+
+
+def prepare(name, moe, mi, torch, path, cache=None):
     backward = name.endswith("+backward")
     cfg = mi.CONFIGS[name.split("+")[0]]
-    if shared is not None and shared["cfg"].H == cfg.H and shared["cfg"].E == cfg.E and \
-            shared["cfg"].I == cfg.I and shared["cfg"].expert_dtype == cfg.expert_dtype and \
-            shared["cfg"].I_shared == cfg.I_shared and not cfg.latent:
+    key = weights_key(cfg)
+    if cache is not None and key in cache:
+        inp0, dev0 = cache[key]
         inp = mi.make_layer(cfg, 0, tensors={"x", "b"})       # same seeded weights: reuse them
-        dev = dict(shared["dev"])
+        dev = dict(dev0)
         dev.update(moe.to_device(inp))
-        inp = dict(shared["inp"], **{k_: v for k_, v in inp.items()})
+        inp = dict(inp0, **{k_: v for k_, v in inp.items()})
     else:
         inp = mi.make_layer(cfg, 0)
         dev = moe.to_device(inp)
+        if cache is not None:
+            cache[key] = (inp, dev)
     rt = moe.alloc_routing(cfg.T, cfg.E, cfg.k, "cuda")
     if backward:
         # the backward pass of the layer for a seeded upstream gradient dy, as a training step
@@ -298,9 +306,14 @@ def measure(w, moe, torch, steps, warmup, graph):
     # which also waits for the side stream), and steps after the 256 MB Infinity Cache has been
     # overwritten by a 512 MB store, so that no weights stay cached between steps
     dist = step_times(layer, torch, max(steps, 20))
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    cold = step_times(layer, torch, min(max(steps, 10), 30), before=lambda: flush.fill_(1))
-    del flush
+    # eviction by a read-only sweep of 512 MB (written once here, outside the timed steps), so
+    # that no dirty flush lines are written back inside the step that follows
+    flush = torch.zeros(128 << 20, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    cold = step_times(layer, torch, min(max(steps, 10), 30),
+                      before=lambda: torch.sum(flush, dim=0, out=sink))
+    del flush, sink
     pct = lambda a, q: round(float(np.percentile(a, q)), 1)
     extra = {}
     if w.get("backward"):   # the whole pass against the bf16 peak (recompute not counted)
@@ -313,12 +326,56 @@ def measure(w, moe, torch, steps, warmup, graph):
         fwd = step_times(w["train_forward"], torch, max(steps // 2, 10))
         extra = dict(backward_recompute_us=round(float(np.median(rec)), 1),
                      forward_train_us=round(float(np.median(fwd)), 1))
+    step = None
+    if not w.get("backward"):
+        step = step_roofline(cfg, counts, float(np.median(dist)), float(np.median(cold)))
     return dict(ms_per_step=ms_step, tokens_per_s=cfg.T / (ms_step * 1e-3), roofline=roof,
                 kernel_us_per_step=breakdown, touched_experts=int(np.count_nonzero(counts)),
+                step_roofline=step,
                 step_us=dict(median=pct(dist, 50), p10=pct(dist, 10), p90=pct(dist, 90),
                              cold_cache_median=pct(cold, 50),
                              cold_cache_tokens_per_s=round(cfg.T / (np.median(cold) * 1e-6), 1),
                              **extra))
+
+
+def step_work(cfg, counts):
+    """(flops by matrix-core dtype, bytes) of one whole layer call: the router over all E, the
+    selected pairs' expert products, the shared expert and the latent projections; each touched
+    expert's weights, the shared expert, router and projections read once, x read and y written
+    once. 8- and 4-bit experts multiply e4m3 token rows (fp8 rate); the rest runs in the
+    activation dtype."""
+    T, H, E, k, I, Is, L, D = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared, cfg.latent, cfg.D
+    P = T * k
+    ea = 4 if cfg.act_dtype == "f32" else 2
+    ew = {"f32": 4, "bf16": 2, "e4m3": 1, "mxfp8": 1, "mxfp4": 0.5}[cfg.expert_dtype]
+    narrow = cfg.expert_dtype in ("e4m3", "mxfp4", "mxfp8")
+    touched = int(np.count_nonzero(counts))
+    act = "f32" if cfg.act_dtype == "f32" else "bf16"
+    flops = {act: 2 * T * E * H + 4 * T * Is * H + 4 * T * L * H}
+    routed = 4 * P * I * D
+    flops["fp8" if narrow else act] = flops.get("fp8" if narrow else act, 0) + routed
+    scale = 0
+    if cfg.expert_dtype == "e4m3":
+        scale = touched * (I + D) * 4
+    elif cfg.expert_dtype in ("mxfp4", "mxfp8"):
+        scale = touched * 2 * I * D // 32
+    b = touched * 2 * I * D * ew + scale + 2 * Is * H * ea + E * H * ea + 2 * L * H * ea + \
+        2 * T * H * ea
+    return flops, int(b)
+
+
+def step_roofline(cfg, counts, warm_us, cold_us):
+    """The whole step against its roofline: the larger of the HBM time of its algorithmic bytes
+    and the matrix-core time of its flops (each dtype at its own dense peak); frac is that ideal
+    time over the measured median step, warm and after the read-only eviction."""
+    flops, b = step_work(cfg, counts)
+    t_hbm = b / PEAK_HBM
+    t_mfma = sum(f / PEAK_MFMA[dt] for dt, f in flops.items())
+    ideal = max(t_hbm, t_mfma)
+    return dict(bound="hbm" if t_hbm >= t_mfma else "mfma",
+                algorithmic_bytes=b, algorithmic_flops={dt: int(f) for dt, f in flops.items()},
+                ideal_us=round(ideal * 1e6, 1), frac=round(ideal / (warm_us * 1e-6), 4),
+                frac_cold=round(ideal / (cold_us * 1e-6), 4))
 
 
 def step_times(layer, torch, n, before=None):
@@ -380,7 +437,7 @@ def cpu_baseline(w, n_tokens):
     toks = np.linspace(0, cfg.T - 1, n_tokens).astype(np.int32)
     O.build()
     t0 = time.perf_counter()
-    O.forward(inp, toks)
+    O.forward(inp, toks)      # exact weights, one thread
     dt = time.perf_counter() - t0
     model = ""
     try:
@@ -392,7 +449,8 @@ def cpu_baseline(w, n_tokens):
                 cpu_model=model, host_cpus=os.cpu_count(),
                 sample=f"{n_tokens} of the {cfg.T} tokens of {cfg.name} (router over all E, "
                        f"k experts and the shared expert per token), double precision, one "
-                       f"thread, {dt:.1f} s")
+                       f"thread, {dt:.1f} s; tokens are independent, so the rate extrapolates "
+                       f"linearly to the whole batch")
 
 
 def dtype_of(cfg):
@@ -421,7 +479,8 @@ def main():
 
     torch.cuda.set_device(0)
     moe.lib()
-    main_w = prepare(args.config, moe, mi, torch, args.path)
+    cache = {}
+    main_w = prepare(args.config, moe, mi, torch, args.path, cache)
     res = measure(main_w, moe, torch, args.steps, args.warmup, args.graph)
     cfg = main_w["cfg"]
     out = {
@@ -434,13 +493,19 @@ def main():
     }
     extra = {}
     for name in [n for n in args.also.split(",") if n and n != args.config]:
-        w = prepare(name, moe, mi, torch, args.path, shared=main_w)
+        w = prepare(name, moe, mi, torch, args.path, cache)
         r = measure(w, moe, torch, args.steps, args.warmup, args.graph)
         extra[name] = dict(tokens_per_s=round(r["tokens_per_s"], 1), dtype=dtype_of(w["cfg"]),
                            ms_per_step=round(r["ms_per_step"], 4), roofline=r["roofline"],
-                           step_us=r["step_us"], kernel_us_per_step=r["kernel_us_per_step"])
+                           step_roofline=r["step_roofline"], step_us=r["step_us"],
+                           kernel_us_per_step=r["kernel_us_per_step"])
+        if not args.no_cpu_baseline and not w.get("backward"):
+            n = args.cpu_tokens or max(2, min(w["cfg"].T,
+                                              int(ALSO_CPU_S / per_token_seconds(w["cfg"]))))
+            extra[name]["cpu_baseline"] = cpu_baseline(w, n)
         del w
         torch.cuda.empty_cache()
+    out["step_roofline"] = res["step_roofline"]
     out["step_us"] = res["step_us"]
     out["peak_from_clock"] = peak_from_clock()
     out["kernel_us_per_step"] = res["kernel_us_per_step"]
@@ -460,6 +525,9 @@ def main():
         n = args.cpu_tokens or max(4, min(cfg.T, int(15.0 / per_token_seconds(cfg))))
         out["cpu_baseline"] = cpu_baseline(main_w, n)
     print(json.dumps(out), flush=True)
+
+
+ALSO_CPU_S = 4.0    # oracle seconds per extra workload (the headline one gets ~15 s)
 
 
 def per_token_seconds(cfg):
