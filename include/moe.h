@@ -156,6 +156,21 @@ int32_t moe_layer_forward(const moe_desc_t *desc, const moe_weights_t *w, void *
 int32_t latent_moe_forward(const moe_desc_t *desc, const moe_weights_t *w, void *y, void *ws,
                            size_t ws_bytes, moe_routing_t *routing, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): moe_layer_forward, or latent_moe_forward when
+ * desc->latent > 0, with no workspace argument. Its scratch is a library-owned device array of
+ * MOE_STATIC_WORKSPACE_BYTES (64 MiB) per GPU, held until the process ends: enough for decode
+ * calls (a Nano layer at T = 64 needs about 7 MB). A descriptor whose moe_workspace_size exceeds
+ * it returns MOE_ERR_WORKSPACE before anything is launched. The call allocates nothing; its first
+ * call on each device does that device's set-up (looks up the array's address, creates the side
+ * stream of the narrow decode path), so make that first call outside graph capture. Every call
+ * on one GPU shares that GPU's array: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller. Results are those of moe_layer_forward /
+ * latent_moe_forward bit for bit; arguments and other errors as there. */
+#define MOE_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+int32_t moe_layer_forward_static(const moe_desc_t *desc, const moe_weights_t *w, void *y,
+                                 moe_routing_t *routing, void *stream);
+
 /* Router alone (steps logits -> scores -> top-k -> gates). If `logits` is non-NULL it is used as
  * the fp32 router logits [T, E] and x / W_r are ignored; otherwise logits are computed from
  * x [T, H] and W_r [E, H] (dtype `dt`) into `logits_out` [T, E], which is then required.

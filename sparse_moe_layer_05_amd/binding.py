@@ -24,7 +24,7 @@ _PATHS = {"auto": PATH_AUTO, "grouped": PATH_GROUPED, "stream": PATH_STREAM}
 EXPORTS = ("moe_workspace_size", "moe_layer_forward", "latent_moe_forward", "moe_route",
            "moe_dispatch_workspace_size", "moe_dispatch", "moe_bias_update",
            "moe_backward_workspace_size", "moe_layer_forward_train", "moe_layer_backward",
-           "moe_status_str",
+           "moe_layer_forward_static", "moe_status_str",
            "moe_trace_enable",
            "moe_trace_count", "moe_trace_read", "moe_trace_reset")
 
@@ -74,6 +74,8 @@ def lib() -> C.CDLL:
             for fn in (L.moe_layer_forward, L.latent_moe_forward):
                 fn.argtypes = [C.POINTER(MoeDesc), C.POINTER(MoeWeights), vp, vp, sz,
                                C.POINTER(MoeRouting), vp]
+            L.moe_layer_forward_static.argtypes = [C.POINTER(MoeDesc), C.POINTER(MoeWeights),
+                                                   vp, C.POINTER(MoeRouting), vp]
             L.moe_route.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
             L.moe_dispatch_workspace_size.argtypes = [i32, i32, i32, C.POINTER(sz)]
             L.moe_dispatch.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
@@ -232,7 +234,7 @@ class Layer:
 
     def __init__(self, x, W_r, b, W_up, W_down, k, *, s_up=None, s_down=None, Ws_up=None,
                  Ws_down=None, W_in=None, W_out=None, path="auto", routing=None,
-                 routing_given=False, out=None, expert_dtype=None):
+                 routing_given=False, out=None, expert_dtype=None, no_alloc=False):
         self.desc = make_desc(x, W_r, W_up, k, Ws_up, W_in, path, routing_given, s_up,
                               expert_dtype)
         check_shapes(self.desc, x, W_r, b, W_up, W_down, s_up, s_down, Ws_up, Ws_down, W_in,
@@ -246,8 +248,12 @@ class Layer:
         self.w = w
         self._keep = [x, W_r, b, W_up, W_down, s_up, s_down, Ws_up, Ws_down, W_in, W_out]
         self.y = out if out is not None else torch.empty_like(x)
-        self.ws_bytes = workspace_size(self.desc)
-        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=x.device)
+        self.no_alloc = no_alloc
+        if no_alloc:          # moe_layer_forward_static: the library's own per-GPU scratch
+            self.ws_bytes, self.ws = 0, None
+        else:
+            self.ws_bytes = workspace_size(self.desc)
+            self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=x.device)
         self.routing = routing
         self.r = None
         if routing is not None:
@@ -258,8 +264,14 @@ class Layer:
         self.fn = lib().latent_moe_forward if self.desc.latent else lib().moe_layer_forward
 
     def __call__(self, stream=None):
+        r = C.byref(self.r) if self.r is not None else None
+        if self.no_alloc:
+            rc = lib().moe_layer_forward_static(C.byref(self.desc), C.byref(self.w), _p(self.y),
+                                                r, _stream(stream))
+            _check(rc, "moe_layer_forward_static")
+            return self.y
         rc = self.fn(C.byref(self.desc), C.byref(self.w), _p(self.y), _p(self.ws), self.ws_bytes,
-                     C.byref(self.r) if self.r is not None else None, _stream(stream))
+                     r, _stream(stream))
         _check(rc, "latent_moe_forward" if self.desc.latent else "moe_layer_forward")
         return self.y
 

@@ -109,4 +109,12 @@ hipError_t launch_stream(const StreamParams& p, hipStream_t s);
 hipError_t launch_reduce_slabs(const float* part, int S, int T, int N, int64_t ld, void* out,
                                int64_t ldo, int mode, hipStream_t s);
 
+// Size of the per-device library-owned workspace of moe_layer_forward_static
+// (MOE_STATIC_WORKSPACE_BYTES in the C header).
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+
+// Device address and size of that workspace on the current device. The address is looked up
+// once per device (hipGetSymbolAddress) and kept; nothing is allocated.
+hipError_t static_scratch(void** ptr, size_t* bytes);
+
 }  // namespace moe

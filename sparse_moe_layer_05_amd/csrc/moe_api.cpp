@@ -987,6 +987,24 @@ int32_t latent_moe_forward(const moe_desc_t* desc, const moe_weights_t* w, void*
   return forward(desc, w, y, ws, ws_bytes, routing, stream, true);
 }
 
+int32_t moe_layer_forward_static(const moe_desc_t* desc, const moe_weights_t* w, void* y,
+                                 moe_routing_t* routing, void* stream) {
+  if (!desc) return MOE_ERR_INVALID_ARG;
+  Plan pl;
+  const bool latent = desc->latent > 0;
+  int32_t rc = make_plan(desc, latent, &pl);
+  if (rc) return rc;
+  if (pl.total > kStaticScratchBytes) return MOE_ERR_WORKSPACE;
+  // set-up on the first call on a device: the array's device address (looked up once and
+  // kept) and the side stream the narrow decode path forks onto; later calls only read them
+  void* ws = nullptr;
+  size_t bytes = 0;
+  Side* side = nullptr;
+  if (static_scratch(&ws, &bytes) != hipSuccess || side_of(&side) != hipSuccess)
+    return MOE_ERR_HIP;
+  return forward(desc, w, y, ws, bytes, routing, stream, latent);
+}
+
 int32_t moe_route(const float* logits, const void* x, const void* W_r, const float* b, int32_t T,
                   int32_t H, int32_t E, int32_t k, moe_dtype_t dt, int32_t* idx, float* gates,
                   float* logits_out, void* stream) {
