@@ -17,7 +17,12 @@
 // ks is multiplied.
 // The epilogue stages each wave's accumulators through LDS in 16-row strips so that every lane
 // finishes 8 consecutive columns of a row with 16-byte loads and stores.
+// Grouped launches (the routed experts) run persistently: two workgroups per CU walk the tiles of
+// their die's range, and the last K-step of a tile already loads the first K-step of the
+// workgroup's next tile into the stage that step frees, so a tile's first loads overlap the
+// previous tile's last products and epilogue.
 // fp32 layers use a vector-ALU kernel with the same parameters.
+#include <algorithm>
 #include <cmath>
 
 #include "common.hpp"
@@ -46,15 +51,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
 
 template <Elt E> struct EltBytes { static constexpr int v = E == Elt::F32 ? 4 : (E == Elt::BF16 ? 2 : 1); };
 
-// Resolves the tile this workgroup owns. Returns false when the workgroup has no tile.
+// Logical tile L -> its group g, first output row, rows (<= BM) and first column. Grouped
+// launches walk a device-built prefix of per-group M-tiles (mt_start); a group's tiles are
+// N-major with M fastest, so consecutive tiles share a weight panel. Dense launches walk bands of
+// 8 M-tiles, N-major inside a band.
 template <int BM, int BN>
-__device__ __forceinline__ bool tile_of(const GemmParams& p, int& g, int& row0, int& rows,
-                                        int& n0) {
-  const int nN = cdiv(p.N, BN);
-  const int L = xcd_logical_block(blockIdx.x, gridDim.x);
+__device__ __forceinline__ void decode_tile(const GemmParams& p, int nN, int L, int& g, int& row0,
+                                            int& rows, int& n0) {
   if (p.mt_start) {
-    const int total = p.mt_start[p.G] * nN;
-    if (L >= total) return false;
     const int key = L / nN;  // global M-tile index; group g owns [mt_start[g], mt_start[g+1])
     int lo = 0, hi = p.G - 1;
     while (lo < hi) {
@@ -64,14 +68,13 @@ __device__ __forceinline__ bool tile_of(const GemmParams& p, int& g, int& row0, 
     g = lo;
     const int mt_g = p.mt_start[g + 1] - p.mt_start[g];
     const int local = L - p.mt_start[g] * nN;
-    n0 = (local / mt_g) * BN;          // a group's tiles: N-major, M fastest (weight panel reuse)
+    n0 = (local / mt_g) * BN;
     const int mt = local % mt_g;
     row0 = p.offs[g] + mt * BM;
     rows = min(BM, p.offs[g + 1] - row0);
   } else {
     const int nM = cdiv(p.M, BM);
-    if (L >= nM * nN) return false;
-    constexpr int GM = 8;              // bands of 8 M-tiles, N-major inside a band
+    constexpr int GM = 8;
     const int first = (L / (GM * nN)) * GM;
     const int gm = min(GM, nM - first);
     const int within = L - first * nN;
@@ -81,7 +84,179 @@ __device__ __forceinline__ bool tile_of(const GemmParams& p, int& g, int& row0, 
     row0 = m * BM;
     rows = min(BM, p.M - row0);
   }
+}
+
+// Number of logical tiles of a launch (device-side for grouped launches).
+template <int BM, int BN>
+__device__ __forceinline__ int tile_count(const GemmParams& p, int nN) {
+  return p.mt_start ? p.mt_start[p.G] * nN : cdiv(p.M, BM) * nN;
+}
+
+// Resolves the tile this workgroup owns (one tile per workgroup). Returns false when the
+// workgroup has none.
+template <int BM, int BN>
+__device__ __forceinline__ bool tile_of(const GemmParams& p, int& g, int& row0, int& rows,
+                                        int& n0) {
+  const int nN = cdiv(p.N, BN);
+  const int L = xcd_logical_block(blockIdx.x, gridDim.x);
+  if (L >= tile_count<BM, BN>(p, nN)) return false;
+  decode_tile<BM, BN>(p, nN, L, g, row0, rows, n0);
   return rows > 0;
+}
+
+// One K-step of a BM x BN tile on the matrix cores, from the stage at As (A rows, then B rows).
+// Fragments of k-sub s+1 are read from LDS while the MFMAs of k-sub s issue; scheduling fences
+// keep the compiler from hoisting further reads (which would only add registers).
+template <int BM, int BN, int WGM, int WGN, Elt AB, int SL>
+__device__ __forceinline__ void mma_stage(const uint8_t* As,
+                                          f32x16_t (&acc)[BM / WGM / 32][BN / WGN / 32],
+                                          int lane, int wm, int wn) {
+  constexpr int WM = BM / WGM, WN = BN / WGN, MB = WM / 32, NB = WN / 32;
+  const uint8_t* Bs = As + BM * SL;
+  if constexpr (AB == Elt::BF16) {
+    bf16x8_t a[2][MB], b[2][NB];
+    auto rd = [&](int s, int buf) {
+      const int ch = 2 * s + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < MB; ++i) a[buf][i] = *(const bf16x8_t*)(As + slot<SL>(wm * WM + i * 32 + (lane & 31), ch));
+#pragma unroll
+      for (int j = 0; j < NB; ++j) b[buf][j] = *(const bf16x8_t*)(Bs + slot<SL>(wn * WN + j * 32 + (lane & 31), ch));
+    };
+    rd(0, 0);
+    constexpr int NSUB = SL / 32;  // 16-element k-subs per K-step
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      if (s < NSUB - 1) rd(s + 1, (s + 1) & 1);
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    i32x8_t a[2][MB], b[2][NB];
+    auto rd = [&](int s, int buf) {
+      const int ch = 4 * s + 2 * (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int r = wm * WM + i * 32 + (lane & 31);
+        const i32x4_t lo = *(const i32x4_t*)(As + slot<SL>(r, ch));
+        const i32x4_t hi = *(const i32x4_t*)(As + slot<SL>(r, ch + 1));
+        a[buf][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int r = wn * WN + j * 32 + (lane & 31);
+        const i32x4_t lo = *(const i32x4_t*)(Bs + slot<SL>(r, ch));
+        const i32x4_t hi = *(const i32x4_t*)(Bs + slot<SL>(r, ch + 1));
+        b[buf][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    };
+    rd(0, 0);
+    constexpr int NSUB = SL / 64;  // 64-element k-subs per K-step
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      if (s < NSUB - 1) rd(s + 1, (s + 1) & 1);
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[s & 1][i], b[s & 1][j], acc[i][j],
+                                                                       0, 0, 0, 127, 0, 127);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// Epilogue of a tile: acc[i][j][r] is C[wm*WM + i*32 + (r/4)*8 + (lane/32)*4 + r%4]
+// [wn*WN + j*32 + lane%32]. Strip h of m-block i (rows 16h .. 16h+15, registers 8h .. 8h+7) goes
+// through this wave's LDS strip `ep` (16 x (WN+4) floats); then lane l finishes items l, l + 64,
+// ... where item = (row in strip) * (WN/8) + column group.
+template <int BM, int BN, int WGM, int WGN, Elt AB, Elt OUT, Epi EPI>
+__device__ __forceinline__ void store_tile(const GemmParams& p,
+                                           const f32x16_t (&acc)[BM / WGM / 32][BN / WGN / 32],
+                                           float* ep, int g, int row0, int rows, int n0, int lane,
+                                           int wm, int wn) {
+  constexpr int WM = BM / WGM, WN = BN / WGN, MB = WM / 32, NB = WN / 32;
+  constexpr int EPW = WN + 4;            // epilogue strip row (floats)
+  constexpr int CG = WN / 8;             // 8-column groups per strip row
+  constexpr int ITEMS = 16 * CG / 64;    // items per lane per strip
+  static_assert((16 * CG) % 64 == 0, "strip must split evenly over the wave");
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          const int r = 8 * h + rr;
+          const int srow = (rr >> 2) * 8 + (lane >> 5) * 4 + (rr & 3);
+          ep[srow * EPW + j * 32 + (lane & 31)] = acc[i][j][r];
+        }
+#pragma unroll
+      for (int it = 0; it < ITEMS; ++it) {
+        const int item = it * 64 + lane;
+        const int srow = item / CG, cg = item % CG;
+        const int rl = wm * WM + i * 32 + h * 16 + srow;
+        const int col = n0 + wn * WN + cg * 8;
+        const bool ok = rl < rows && col < p.N;
+        const int row = row0 + (rl < rows ? rl : 0);
+        float v[8];
+        const float4 lo = *(const float4*)(ep + srow * EPW + cg * 8);
+        const float4 hi = *(const float4*)(ep + srow * EPW + cg * 8 + 4);
+        v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+        v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+        if (ok) {
+          if constexpr (AB == Elt::FP8) {
+            const int64_t src = p.a_gather ? p.a_gather[row] : (int64_t)row;
+            const float rs = p.a_scale[src];
+            const float* bs = p.b_scale + (int64_t)g * p.N + col;
+            const float4 s0 = *(const float4*)bs, s1 = *(const float4*)(bs + 4);
+            const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] *= rs * sc[q];
+          }
+          if constexpr (EPI == Epi::SqRelu) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = sqrelu(v[q]);
+          }
+          if constexpr (EPI == Epi::SqReluSave) {  // relu(a) kept for the backward pass
+            uint32_t w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              w[q] = pack_bf16x2(fmaxf(v[2 * q], 0.f), fmaxf(v[2 * q + 1], 0.f));
+            *(uint4*)((uint16_t*)p.C2 + (int64_t)row * p.ldc + col) = make_uint4(w[0], w[1], w[2], w[3]);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = sqrelu(v[q]);
+          }
+          // 16-byte stores when the 8 columns lie inside N on an aligned row; else (N or ldc
+          // not a multiple of 8, e.g. router logits of E experts) element by element
+          const bool whole = col + 8 <= p.N && p.ldc % 8 == 0;
+          if constexpr (OUT == Elt::BF16) {
+            uint16_t* o = (uint16_t*)p.C + (int64_t)row * p.ldc + col;
+            if (whole) {
+              uint32_t w[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+              *(uint4*)o = make_uint4(w[0], w[1], w[2], w[3]);
+            } else {
+              for (int q = 0; q < 8 && col + q < p.N; ++q) o[q] = (uint16_t)f32_to_bf16_bits(v[q]);
+            }
+          } else {
+            float* o = (float*)p.C + (int64_t)row * p.ldc + col;
+            if (whole) {
+              *(float4*)o = make_float4(v[0], v[1], v[2], v[3]);
+              *(float4*)(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+            } else {
+              for (int q = 0; q < 8 && col + q < p.N; ++q) o[q] = v[q];
+            }
+          }
+        }
+      }
+    }
+  }
 }
 
 // -------------------------------------------------------------------------------------------
@@ -231,65 +406,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // One K-step on the matrix cores. Fragments of k-sub s+1 are read from LDS while the MFMAs
-  // of k-sub s issue; scheduling fences keep the compiler from hoisting further reads (which
-  // would only add registers).
   auto compute = [&](const uint8_t* As) {
-    const uint8_t* Bs = As + BM * SL;
-    if constexpr (AB == Elt::BF16) {
-      bf16x8_t a[2][MB], b[2][NB];
-      auto rd = [&](int s, int buf) {
-        const int ch = 2 * s + (lane >> 5);
-#pragma unroll
-        for (int i = 0; i < MB; ++i) a[buf][i] = *(const bf16x8_t*)(As + slot<SL>(wm * WM + i * 32 + (lane & 31), ch));
-#pragma unroll
-        for (int j = 0; j < NB; ++j) b[buf][j] = *(const bf16x8_t*)(Bs + slot<SL>(wn * WN + j * 32 + (lane & 31), ch));
-      };
-      rd(0, 0);
-      constexpr int NSUB = SL / 32;  // 16-element k-subs per K-step
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        if (s < NSUB - 1) rd(s + 1, (s + 1) & 1);
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-#pragma unroll
-          for (int j = 0; j < NB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-      i32x8_t a[2][MB], b[2][NB];
-      auto rd = [&](int s, int buf) {
-        const int ch = 4 * s + 2 * (lane >> 5);
-#pragma unroll
-        for (int i = 0; i < MB; ++i) {
-          const int r = wm * WM + i * 32 + (lane & 31);
-          const i32x4_t lo = *(const i32x4_t*)(As + slot<SL>(r, ch));
-          const i32x4_t hi = *(const i32x4_t*)(As + slot<SL>(r, ch + 1));
-          a[buf][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const int r = wn * WN + j * 32 + (lane & 31);
-          const i32x4_t lo = *(const i32x4_t*)(Bs + slot<SL>(r, ch));
-          const i32x4_t hi = *(const i32x4_t*)(Bs + slot<SL>(r, ch + 1));
-          b[buf][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-      };
-      rd(0, 0);
-      constexpr int NSUB = SL / 64;  // 64-element k-subs per K-step
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        if (s < NSUB - 1) rd(s + 1, (s + 1) & 1);
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-#pragma unroll
-          for (int j = 0; j < NB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[s & 1][i], b[s & 1][j], acc[i][j],
-                                                                         0, 0, 0, 127, 0, 127);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+    mma_stage<BM, BN, WGM, WGN, AB, SL>(As, acc, lane, wm, wn);
   };
 
   // Pipeline: K-step ks + NS - 1 is issued while K-step ks is computed. Before computing ks a
@@ -320,87 +438,160 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma(GemmParams p) {
   }
   __syncthreads();  // every wave is done with the stages: the epilogue reuses them
 
-  // ---------------------------------------------------------------- epilogue
-  // acc[i][j][r] is C[wm*WM + i*32 + (r/4)*8 + (lane/32)*4 + r%4][wn*WN + j*32 + lane%32].
-  // Strip h of m-block i (rows 16h .. 16h+15, registers 8h .. 8h+7) goes through LDS; then lane
-  // l finishes items l, l + 64, ... where item = (row in strip) * (WN/8) + column group.
-  float* ep = (float*)smem + wave * 16 * EPW;
-  constexpr int CG = WN / 8;             // 8-column groups per strip row
-  constexpr int ITEMS = 16 * CG / 64;    // items per lane per strip
-  static_assert((16 * CG) % 64 == 0, "strip must split evenly over the wave");
+  store_tile<BM, BN, WGM, WGN, AB, OUT, EPI>(p, acc, (float*)smem + wave * 16 * EPW, g, row0, rows,
+                                            n0, lane, wm, wn);
+}
+
+// -------------------------------------------------------------------------------------------
+// Persistent matrix-core kernel for grouped launches (two stages of 128-byte K-steps, one K
+// segment). Workgroup b runs on die d = b % 8 as the q-th of that die's Qd workgroups; it walks
+// the logical tiles lo + q, lo + q + Qd, ... of its die's contiguous range [lo, hi), so the tiles
+// in flight on a die are neighbours (they share weight and activation panels in that die's L2).
+// During the last K-step of a tile the workgroup loads the first K-step of its next tile into the
+// stage that step frees, and the epilogue stages its strips through the other one.
+// -------------------------------------------------------------------------------------------
+template <int BM, int BN, int WGM, int WGN, Elt AB, Elt OUT, Epi EPI>
+__global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm_mfma_persist(GemmParams p) {  // two workgroups per CU: at most 256 registers per lane
+  static_assert(AB == Elt::BF16 || AB == Elt::FP8, "matrix-core path");
+  constexpr int SL = 128;
+  constexpr int NW = WGM * WGN;
+  constexpr int EB = EltBytes<AB>::v;
+  constexpr int WM = BM / WGM, WN = BN / WGN, MB = WM / 32, NB = WN / 32;
+  constexpr int RPI = 1024 / SL, LPR = SL / 16;
+  constexpr int A_GRP = BM / (RPI * NW), B_GRP = BN / (RPI * NW);
+  constexpr int STAGE = (BM + BN) * SL;
+  constexpr int EPW = WN + 4;
+  static_assert(A_GRP >= 1 && B_GRP >= 1 && MB >= 1 && NB >= 1, "tile too small");
+  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0,
+                "every tile row must be covered by the waves' 1-KB loads");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tiles are whole 32 x 32 blocks");
+  static_assert(NW * 16 * EPW * 4 <= STAGE, "epilogue strips must fit in one stage");
+  static_assert(NW % 2 == 0, "an even wave count keeps the swizzle constant");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+
+  const int nN = cdiv(p.N, BN);
+  const int total = tile_count<BM, BN>(p, nN);
+  const int d = blockIdx.x % kXcds, Qd = gridDim.x / kXcds;
+  const int lo_t = d * cdiv(total, kXcds);
+  const int hi_t = min(total, lo_t + cdiv(total, kXcds));
+  int L = lo_t + (int)blockIdx.x / kXcds;
+  if (L >= hi_t) return;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int lrow = lane / LPR, lpos = lane % LPR;
+  const int cofs = (lpos ^ swz<SL>(wave * RPI + lrow)) << 4;
+  const int kb = p.K * EB;
+  const int nk = cdiv(kb, SL);
+  const int tail = kb % SL;  // bytes of a partial last K-step, 0 when K-steps are whole
+  const __amdgpu_buffer_rsrc_t ra = rsrc(p.A, (int64_t)p.a_rows * p.lda * EB);
+
+  // Operand sources of a tile: the buffer resource of its group's weight panel and this lane's
+  // row offsets (gathered A rows; padding rows of a partial M-tile are pointed out of range).
+  __amdgpu_buffer_rsrc_t rb_c, rb_n;
+  uint32_t oa_c[A_GRP], ob_c[B_GRP], oa_n[A_GRP], ob_n[B_GRP];
+  int g_c, row0_c, rows_c, n0_c, g_n = 0, row0_n = 0, rows_n = 0, n0_n = 0;
+  auto setup = [&](int Lt, __amdgpu_buffer_rsrc_t& rbx, uint32_t* oax, uint32_t* obx, int& gx,
+                   int& row0x, int& rowsx, int& n0x) {
+    decode_tile<BM, BN>(p, nN, Lt, gx, row0x, rowsx, n0x);
+    rbx = rsrc((const uint8_t*)p.B + (int64_t)gx * p.b_gstride * EB, (int64_t)p.N * p.ldb * EB);
 #pragma unroll
-  for (int i = 0; i < MB; ++i) {
+    for (int i = 0; i < A_GRP; ++i) {
+      const int r = (wave + NW * i) * RPI + lrow;
+      if (r >= rowsx) {
+        oax[i] = 0xFFFFFFF0u;
+        continue;
+      }
+      const int64_t src = p.a_gather ? p.a_gather[row0x + r] : (int64_t)(row0x + r);
+      oax[i] = (uint32_t)(src * p.lda * EB) + cofs;
+    }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int i = 0; i < B_GRP; ++i) {
+      const int r = (wave + NW * i) * RPI + lrow;
+      const int n = n0x + r < p.N ? n0x + r : p.N - 1;
+      obx[i] = (uint32_t)((int64_t)n * p.ldb * EB) + cofs;
+    }
+  };
+  // The loads of K-step ks into stage `st`; in a partial last K-step, lanes whose chunk lies
+  // beyond K skip the access (out-of-range offset) and their slots are zeroed after landing.
+  auto issue = [&](__amdgpu_buffer_rsrc_t rbx, const uint32_t* oax, const uint32_t* obx, int ks,
+                   uint8_t* st) {
+    const bool live = !(tail && ks == nk - 1) || cofs < tail;
+    uint8_t* sb = st + BM * SL;
+#pragma unroll
+    for (int i = 0; i < A_GRP; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (__attribute__((address_space(3))) void*)(st + (wave + NW * i) * 1024), 16,
+          (int)(live ? oax[i] : 0xFFFFFFF0u), ks * SL, 0, 0);
+#pragma unroll
+    for (int i = 0; i < B_GRP; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rbx, (__attribute__((address_space(3))) void*)(sb + (wave + NW * i) * 1024), 16,
+          (int)(live ? obx[i] : 0xFFFFFFF0u), ks * SL, 0, 0);
+  };
+  // A workgroup barrier without a memory fence: the fence would also wait for the loads still in
+  // flight into the other stage. Each wave first waits for its own loads of the stage it is about
+  // to read (vmcnt(0): those are the only ones outstanding) and its own LDS operations.
+  auto stage_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8));  // vmcnt(0)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  auto barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  f32x16_t acc[MB][NB];
+  setup(L, rb_c, oa_c, ob_c, g_c, row0_c, rows_c, n0_c);
+  issue(rb_c, oa_c, ob_c, 0, smem);
+  int par = 0;  // stage that holds K-step 0 of the current tile
+  while (true) {
+    const int Ln = L + Qd;
+    const bool has_next = Ln < hi_t;
+    if (has_next) setup(Ln, rb_n, oa_n, ob_n, g_n, row0_n, rows_n, n0_n);
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-          const int r = 8 * h + rr;
-          const int srow = (rr >> 2) * 8 + (lane >> 5) * 4 + (rr & 3);
-          ep[srow * EPW + j * 32 + (lane & 31)] = acc[i][j][r];
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int ks = 0; ks < nk; ++ks) {
+      stage_barrier();
+      uint8_t* st = smem + ((par + ks) & 1) * STAGE;
+      if (tail && ks == nk - 1) {
+        if (cofs >= tail) {
+#pragma unroll
+          for (int i = 0; i < A_GRP; ++i)
+            *(uint4*)(st + (wave + NW * i) * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < B_GRP; ++i)
+            *(uint4*)(st + BM * SL + (wave + NW * i) * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
         }
-#pragma unroll
-      for (int it = 0; it < ITEMS; ++it) {
-        const int item = it * 64 + lane;
-        const int srow = item / CG, cg = item % CG;
-        const int rl = wm * WM + i * 32 + h * 16 + srow;
-        const int col = n0 + wn * WN + cg * 8;
-        const bool ok = rl < rows && col < p.N;
-        const int row = row0 + (rl < rows ? rl : 0);
-        float v[8];
-        const float4 lo = *(const float4*)(ep + srow * EPW + cg * 8);
-        const float4 hi = *(const float4*)(ep + srow * EPW + cg * 8 + 4);
-        v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-        v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-        if (ok) {
-          if constexpr (AB == Elt::FP8) {
-            const int64_t src = p.a_gather ? p.a_gather[row] : (int64_t)row;
-            const float rs = p.a_scale[src];
-            const float* bs = p.b_scale + (int64_t)g * p.N + col;
-            const float4 s0 = *(const float4*)bs, s1 = *(const float4*)(bs + 4);
-            const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-#pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] *= rs * sc[q];
-          }
-          if constexpr (EPI == Epi::SqRelu) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = sqrelu(v[q]);
-          }
-          if constexpr (EPI == Epi::SqReluSave) {  // relu(a) kept for the backward pass
-            uint32_t w[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              w[q] = pack_bf16x2(fmaxf(v[2 * q], 0.f), fmaxf(v[2 * q + 1], 0.f));
-            *(uint4*)((uint16_t*)p.C2 + (int64_t)row * p.ldc + col) = make_uint4(w[0], w[1], w[2], w[3]);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = sqrelu(v[q]);
-          }
-          // 16-byte stores when the 8 columns lie inside N on an aligned row; else (N or ldc
-          // not a multiple of 8, e.g. router logits of E experts) element by element
-          const bool whole = col + 8 <= p.N && p.ldc % 8 == 0;
-          if constexpr (OUT == Elt::BF16) {
-            uint16_t* o = (uint16_t*)p.C + (int64_t)row * p.ldc + col;
-            if (whole) {
-              uint32_t w[4];
-#pragma unroll
-              for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
-              *(uint4*)o = make_uint4(w[0], w[1], w[2], w[3]);
-            } else {
-              for (int q = 0; q < 8 && col + q < p.N; ++q) o[q] = (uint16_t)f32_to_bf16_bits(v[q]);
-            }
-          } else {
-            float* o = (float*)p.C + (int64_t)row * p.ldc + col;
-            if (whole) {
-              *(float4*)o = make_float4(v[0], v[1], v[2], v[3]);
-              *(float4*)(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
-            } else {
-              for (int q = 0; q < 8 && col + q < p.N; ++q) o[q] = v[q];
-            }
-          }
-        }
+        barrier();
       }
+      uint8_t* other = smem + ((par + ks + 1) & 1) * STAGE;
+      if (ks + 1 < nk)
+        issue(rb_c, oa_c, ob_c, ks + 1, other);
+      else if (has_next)
+        issue(rb_n, oa_n, ob_n, 0, other);
+      mma_stage<BM, BN, WGM, WGN, AB, SL>(st, acc, lane, wm, wn);
     }
+    barrier();  // every wave is done with the last stage: the epilogue reuses it
+    store_tile<BM, BN, WGM, WGN, AB, OUT, EPI>(
+        p, acc, (float*)(smem + ((par + nk - 1) & 1) * STAGE) + wave * 16 * EPW, g_c, row0_c,
+        rows_c, n0_c, lane, wm, wn);
+    if (!has_next) break;
+    rb_c = rb_n;
+#pragma unroll
+    for (int i = 0; i < A_GRP; ++i) oa_c[i] = oa_n[i];
+#pragma unroll
+    for (int i = 0; i < B_GRP; ++i) ob_c[i] = ob_n[i];
+    g_c = g_n;
+    row0_c = row0_n;
+    rows_c = rows_n;
+    n0_c = n0_n;
+    par = (par + nk) & 1;
+    L = Ln;
   }
 }
 
@@ -474,6 +665,32 @@ hipError_t run_mfma(const GemmParams& p, int mtiles, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Workgroups of a persistent launch: two per CU (the LDS of two 80 KB stage pairs), rounded down
+// to whole groups of 8 (one per die).
+int persist_grid() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return std::max(kXcds, (2 * cus[dev]) / kXcds * kXcds);
+}
+
+template <int BM, int BN, int WGM, int WGN, Elt AB, Elt OUT, Epi EPI>
+hipError_t run_persist(const GemmParams& p, int mtiles, hipStream_t s) {
+  if (p.K2 > 0 || p.ksplit > 1) return hipErrorInvalidValue;
+  const int tiles = mtiles * cdiv(p.N, BN);
+  if (tiles <= 0) return hipSuccess;
+  const int grid = std::min(cdiv(tiles, kXcds) * kXcds, persist_grid());
+  hipLaunchKernelGGL((gemm_mfma_persist<BM, BN, WGM, WGN, AB, OUT, EPI>), dim3(grid),
+                     dim3(64 * WGM * WGN), 0, s, p);
+  return hipGetLastError();
+}
+
 template <Epi EPI>
 hipError_t run_f32(const GemmParams& p, int mtiles, hipStream_t s) {
   const int tiles = mtiles * cdiv(p.N, 64);
@@ -531,13 +748,14 @@ hipError_t launch_gemm(const GemmKind& k, const GemmParams& p, int max_mtiles, h
     if (k.epi == Epi::SqReluSave && (!p.C2 || k.out != Elt::BF16 || p.N % 8 || p.ldc % 8))
       return hipErrorInvalidValue;
     if (grouped) {
-      // 128 x 192 tiles on 4 waves, two workgroups per CU: the fastest routed shape measured
+      // 128 x 192 tiles on 4 waves, two workgroups per CU: the fastest routed shape measured,
+      // persistent so that each tile's first loads overlap the previous tile's end
       if (k.out == Elt::BF16 && k.epi == Epi::SqRelu)
-        return run_mfma<GB, 192, 2, 2, 2, Elt::BF16, Elt::BF16, Epi::SqRelu>(p, max_mtiles, s);
+        return run_persist<GB, 192, 2, 2, Elt::BF16, Elt::BF16, Epi::SqRelu>(p, max_mtiles, s);
       if (k.out == Elt::BF16 && k.epi == Epi::Store)
-        return run_mfma<GB, 192, 2, 2, 2, Elt::BF16, Elt::BF16, Epi::Store>(p, max_mtiles, s);
+        return run_persist<GB, 192, 2, 2, Elt::BF16, Elt::BF16, Epi::Store>(p, max_mtiles, s);
       if (k.out == Elt::BF16 && k.epi == Epi::SqReluSave)
-        return run_mfma<GB, 192, 2, 2, 2, Elt::BF16, Elt::BF16, Epi::SqReluSave>(p, max_mtiles, s);
+        return run_persist<GB, 192, 2, 2, Elt::BF16, Elt::BF16, Epi::SqReluSave>(p, max_mtiles, s);
       return hipErrorInvalidValue;
     }
     if (k.out == Elt::F32 && k.epi == Epi::Store) return run_dense_bf16<Elt::F32, Epi::Store>(p, s);
@@ -551,9 +769,9 @@ hipError_t launch_gemm(const GemmKind& k, const GemmParams& p, int max_mtiles, h
   if (k.ab == Elt::FP8 && grouped && k.out == Elt::BF16) {
     // the same 128 x 192 / 4-wave shape measured fastest for e4m3 as for bf16
     if (k.epi == Epi::SqRelu)
-      return run_mfma<GB, 192, 2, 2, 2, Elt::FP8, Elt::BF16, Epi::SqRelu>(p, max_mtiles, s);
+      return run_persist<GB, 192, 2, 2, Elt::FP8, Elt::BF16, Epi::SqRelu>(p, max_mtiles, s);
     if (k.epi == Epi::Store)
-      return run_mfma<GB, 192, 2, 2, 2, Elt::FP8, Elt::BF16, Epi::Store>(p, max_mtiles, s);
+      return run_persist<GB, 192, 2, 2, Elt::FP8, Elt::BF16, Epi::Store>(p, max_mtiles, s);
   }
   return hipErrorInvalidValue;
 }
