@@ -21,11 +21,11 @@ namespace moe {
 namespace {
 
 constexpr int BM = 128, BN = 192, NW = 4, WGN = 2, WM = 64, WN = 96, MB = 2, NB = 3;
+constexpr int EPW = WN + 4;             // epilogue strip row (floats)
+constexpr int kBand = 4;
 constexpr int KS = 64;                  // k per stage
 constexpr int SA = BM * KS * 2, SB = BN * KS * 2;
-constexpr int STAGE = SA + SB;          // 40 KB; two stages
-constexpr int EPW = WN + 4;             // epilogue strip row (floats)
-constexpr int kBand = 4;                // N-tiles per band of a K-grouped launch's tile order
+constexpr int STAGE = SA + SB;          // 40 KB; two stages                // N-tiles per band of a K-grouped launch's tile order
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef short v8i16_t __attribute__((ext_vector_type(8)));
@@ -312,7 +312,13 @@ void gemm_kt_kernel(KtParams p) {
           const int row = row0 + rl;
           const float4 lo = *(const float4*)(ep + srow * EPW + cg * CW);
           if constexpr (OUT == Elt::F32) {
-            *(float4*)((float*)Cg + (int64_t)row * p.ldc + col) = lo;
+            float* o = (float*)Cg + (int64_t)row * p.ldc + col;
+            if (p.kgrp) {  // weight gradients: written once, not read again by this pass
+              const f32x4_t v = {lo.x, lo.y, lo.z, lo.w};
+              __builtin_nontemporal_store(v, (f32x4_t*)o);
+            } else {
+              *(float4*)o = lo;
+            }
           } else {
             const float4 hi = *(const float4*)(ep + srow * EPW + cg * CW + 4);
             float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
