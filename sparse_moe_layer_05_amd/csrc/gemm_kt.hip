@@ -22,10 +22,10 @@ namespace {
 
 constexpr int BM = 128, BN = 192, NW = 4, WGN = 2, WM = 64, WN = 96, MB = 2, NB = 3;
 constexpr int EPW = WN + 4;             // epilogue strip row (floats)
-constexpr int kBand = 4;
+constexpr int kBand = 4;                // N-tiles per band of a K-grouped launch's tile order
 constexpr int KS = 64;                  // k per stage
 constexpr int SA = BM * KS * 2, SB = BN * KS * 2;
-constexpr int STAGE = SA + SB;          // 40 KB; two stages                // N-tiles per band of a K-grouped launch's tile order
+constexpr int STAGE = SA + SB;          // 40 KB; two stages
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef short v8i16_t __attribute__((ext_vector_type(8)));
@@ -65,32 +65,42 @@ __device__ __forceinline__ bf16x8_t km_frag(const uint8_t* st, int pitch, int co
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// Tile of block b of a K-grouped launch; false when it has none. The group's K rows are
+// [k0, k0 + kc).
+//   Every die takes an equal, compact share of each group's tiles, the groups in launch order
+// (heaviest first: their tiles cost most). Blocks d, d + 8, d + 16, ... run on die d; its share
+// of a group is a contiguous run of the group's tiles numbered in bands of kBand N-tiles, N
+// fastest, so the die's tiles have few A and B slabs between them and share them through its L2.
+__device__ __forceinline__ bool kgrp_tile(const KtParams& p, int b, int& g, int& row0, int& rows,
+                                          int& n0, int& k0, int& kc) {
+  const int nN = cdiv(p.N, BN), nM = cdiv(p.M, BM);
+  const int per = nM * nN, cs = cdiv(per, kXcds);
+  const int d = b % kXcds, j = b / kXcds;
+  const int slot = j / cs, q = d * cs + j % cs;
+  if (slot >= p.G || q >= per) return false;
+  g = p.korder ? p.korder[slot] : slot;
+  const int band = q / (kBand * nM), within = q - band * kBand * nM;
+  const int nb = min(kBand, nN - band * kBand);
+  n0 = (band * kBand + within % nb) * BN;
+  row0 = (within / nb) * BM;
+  rows = min(BM, p.M - row0);
+  k0 = p.kgrp[g];
+  kc = p.kgrp[g + 1] - k0;
+  return rows > 0;
+}
+
+// Blocks of a K-grouped launch: each die gets ceil(tiles per group / 8) per group.
+inline int kgrp_blocks(const KtParams& p) {
+  return p.G * kXcds * cdiv(cdiv(p.M, BM) * cdiv(p.N, BN), kXcds);
+}
+
 // Tile of this workgroup; false when it has none. kwin: the group's K rows [k0, k0 + kc).
 __device__ __forceinline__ bool kt_tile(const KtParams& p, int& g, int& row0, int& rows, int& n0,
                                         int& k0, int& kc) {
   const int nN = cdiv(p.N, BN), nM = cdiv(p.M, BM);
   k0 = 0;
   kc = p.K;
-  if (p.kgrp) {
-    // Every die takes an equal, compact share of each group's tiles, the groups in launch order
-    // (heaviest first: their tiles cost most). Blocks d, d + 8, d + 16, ... run on die d; its
-    // share of a group is a contiguous run of the group's tiles numbered in bands of kBand
-    // N-tiles, N fastest, so the die's tiles have few A and B slabs between them and share them
-    // through its L2.
-    const int per = nM * nN, cs = cdiv(per, kXcds);
-    const int d = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
-    const int slot = j / cs, q = d * cs + j % cs;
-    if (slot >= p.G || q >= per) return false;
-    g = p.korder ? p.korder[slot] : slot;
-    const int band = q / (kBand * nM), within = q - band * kBand * nM;
-    const int nb = min(kBand, nN - band * kBand);
-    n0 = (band * kBand + within % nb) * BN;
-    row0 = (within / nb) * BM;
-    rows = min(BM, p.M - row0);
-    k0 = p.kgrp[g];
-    kc = p.kgrp[g + 1] - k0;
-    return rows > 0;
-  }
+  if (p.kgrp) return kgrp_tile(p, blockIdx.x, g, row0, rows, n0, k0, kc);
   const int L = xcd_logical_block(blockIdx.x, gridDim.x);
   if (p.mt_start) {
     const int total = p.mt_start[p.G] * nN;
@@ -119,6 +129,101 @@ __device__ __forceinline__ bool kt_tile(const KtParams& p, int& g, int& row0, in
   n0 = (within / gm) * BN;
   rows = min(BM, p.M - row0);
   return rows > 0;
+}
+
+// One K-step of the 128 x 192 tile from the stage at As (A rows, then B rows at As + SA).
+template <int TA>
+__device__ __forceinline__ void kt_mma(const uint8_t* As, f32x16_t (&acc)[MB][NB], int lane,
+                                       int wm, int wn) {
+  const uint8_t* Bs = As + SA;
+  const int lg = lane >> 4, lj = lane & 15;   // 16-lane group and lane in it (K-major reads)
+  bf16x8_t a[2][MB], b[2][NB];
+  auto rd = [&](int s, int buf) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      if constexpr (TA) {
+        a[buf][i] = km_frag(As, BM * 2, wm * WM + i * 32 + 16 * (lg & 1), 16 * s + 8 * (lg >> 1), lj);
+      } else {
+        const int r = wm * WM + i * 32 + (lane & 31);
+        const int ch = 2 * s + (lane >> 5);
+        a[buf][i] = *(const bf16x8_t*)(As + r * 128 + ((ch ^ swz_mk(r)) << 4));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      b[buf][j] = km_frag(Bs, BN * 2, wn * WN + j * 32 + 16 * (lg & 1), 16 * s + 8 * (lg >> 1), lj);
+  };
+  rd(0, 0);
+#pragma unroll
+  for (int s = 0; s < KS / 16; ++s) {
+    if (s < KS / 16 - 1) rd(s + 1, (s + 1) & 1);
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Epilogue (as in the forward GEMM): acc[i][j][r] is C[wm*WM + i*32 + (r/4)*8 + (lane/32)*4 +
+// r%4][wn*WN + j*32 + lane%32]; 16-row strips go through this wave's LDS strip `ep` so each lane
+// finishes CW consecutive columns of a row: 8 for bf16 outputs, 4 for fp32 (16 bytes either way,
+// so that consecutive lanes store consecutive 16-byte chunks of a row). Cg: the group's output.
+// NT: fp32 outputs are weight gradients, written once and not read again by this pass.
+template <Elt OUT, Epi EPI, bool NT>
+__device__ __forceinline__ void kt_store(const KtParams& p, const f32x16_t (&acc)[MB][NB],
+                                         uint8_t* Cg, float* ep, int row0, int rows, int n0,
+                                         int lane, int wm, int wn) {
+  constexpr int CW = OUT == Elt::F32 ? 4 : 8;
+  constexpr int CG = WN / CW, ITEMS = 16 * CG / 64;
+  static_assert((16 * CG) % 64 == 0, "strip must split evenly over the wave");
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          const int srow = (rr >> 2) * 8 + (lane >> 5) * 4 + (rr & 3);
+          ep[srow * EPW + j * 32 + (lane & 31)] = acc[i][j][8 * h + rr];
+        }
+#pragma unroll
+      for (int it = 0; it < ITEMS; ++it) {
+        const int item = it * 64 + lane;
+        const int srow = item / CG, cg = item % CG;
+        const int rl = wm * WM + i * 32 + h * 16 + srow;
+        const int col = n0 + wn * WN + cg * CW;
+        if (rl < rows && col < p.N) {  // N % 8 == 0: a group inside N ends inside it
+          const int row = row0 + rl;
+          const float4 lo = *(const float4*)(ep + srow * EPW + cg * CW);
+          if constexpr (OUT == Elt::F32) {
+            float* o = (float*)Cg + (int64_t)row * p.ldc + col;
+            if constexpr (NT) {
+              const f32x4_t v = {lo.x, lo.y, lo.z, lo.w};
+              __builtin_nontemporal_store(v, (f32x4_t*)o);
+            } else {
+              *(float4*)o = lo;
+            }
+          } else {
+            const float4 hi = *(const float4*)(ep + srow * EPW + cg * CW + 4);
+            float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            if constexpr (EPI == Epi::DSqRelu) {  // d/da relu(a)^2 = 2 relu(a), relu(a) in C2
+              float r[8];
+              unpack8(*(const uint4*)((const uint16_t*)p.C2 + (int64_t)row * p.ldc + col), r);
+#pragma unroll
+              for (int q = 0; q < 8; ++q) v[q] *= 2.f * r[q];
+            }
+            uint32_t w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+            *(uint4*)((uint16_t*)Cg + (int64_t)row * p.ldc + col) = make_uint4(w[0], w[1], w[2], w[3]);
+          }
+        }
+      }
+    }
+  }
 }
 
 template <int TA, int TB, Elt OUT, Epi EPI>
@@ -237,37 +342,7 @@ void gemm_kt_kernel(KtParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int lg = lane >> 4, lj = lane & 15;   // 16-lane group and lane in it (K-major reads)
-  auto compute = [&](const uint8_t* As) {
-    const uint8_t* Bs = As + SA;
-    bf16x8_t a[2][MB], b[2][NB];
-    auto rd = [&](int s, int buf) {
-#pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        if constexpr (TA) {
-          a[buf][i] = km_frag(As, PA, wm * WM + i * 32 + 16 * (lg & 1), 16 * s + 8 * (lg >> 1), lj);
-        } else {
-          const int r = wm * WM + i * 32 + (lane & 31);
-          const int ch = 2 * s + (lane >> 5);
-          a[buf][i] = *(const bf16x8_t*)(As + r * 128 + ((ch ^ swz_mk(r)) << 4));
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-        b[buf][j] = km_frag(Bs, PB, wn * WN + j * 32 + 16 * (lg & 1), 16 * s + 8 * (lg >> 1), lj);
-    };
-    rd(0, 0);
-#pragma unroll
-    for (int s = 0; s < KS / 16; ++s) {
-      if (s < KS / 16 - 1) rd(s + 1, (s + 1) & 1);
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
+  auto compute = [&](const uint8_t* As) { kt_mma<TA>(As, acc, lane, wm, wn); };
 
   // Two stages: K-step ks + 1 is loaded while K-step ks is multiplied.
   if (gath && nk > 0) fetch_rows(0);
@@ -282,70 +357,18 @@ void gemm_kt_kernel(KtParams p) {
   }
   __syncthreads();  // the epilogue reuses the stages
 
-  // Epilogue (as in the forward GEMM): acc[i][j][r] is C[wm*WM + i*32 + (r/4)*8 + (lane/32)*4 +
-  // r%4][wn*WN + j*32 + lane%32]; 16-row strips go through LDS so each lane finishes CW
-  // consecutive columns of a row: 8 for bf16 outputs, 4 for fp32 (16 bytes either way, so that
-  // consecutive lanes store consecutive 16-byte chunks of a row).
   uint8_t* Cg = (uint8_t*)p.C + (p.kgrp ? (int64_t)g * p.c_gstride * (OUT == Elt::F32 ? 4 : 2) : 0);
-  float* ep = (float*)smem + wave * 16 * EPW;
-  constexpr int CW = OUT == Elt::F32 ? 4 : 8;
-  constexpr int CG = WN / CW, ITEMS = 16 * CG / 64;
-  static_assert((16 * CG) % 64 == 0, "strip must split evenly over the wave");
-#pragma unroll
-  for (int i = 0; i < MB; ++i) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-          const int srow = (rr >> 2) * 8 + (lane >> 5) * 4 + (rr & 3);
-          ep[srow * EPW + j * 32 + (lane & 31)] = acc[i][j][8 * h + rr];
-        }
-#pragma unroll
-      for (int it = 0; it < ITEMS; ++it) {
-        const int item = it * 64 + lane;
-        const int srow = item / CG, cg = item % CG;
-        const int rl = wm * WM + i * 32 + h * 16 + srow;
-        const int col = n0 + wn * WN + cg * CW;
-        if (rl < rows && col < p.N) {  // N % 8 == 0: a group inside N ends inside it
-          const int row = row0 + rl;
-          const float4 lo = *(const float4*)(ep + srow * EPW + cg * CW);
-          if constexpr (OUT == Elt::F32) {
-            float* o = (float*)Cg + (int64_t)row * p.ldc + col;
-            if (p.kgrp) {  // weight gradients: written once, not read again by this pass
-              const f32x4_t v = {lo.x, lo.y, lo.z, lo.w};
-              __builtin_nontemporal_store(v, (f32x4_t*)o);
-            } else {
-              *(float4*)o = lo;
-            }
-          } else {
-            const float4 hi = *(const float4*)(ep + srow * EPW + cg * CW + 4);
-            float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            if constexpr (EPI == Epi::DSqRelu) {  // d/da relu(a)^2 = 2 relu(a), relu(a) in C2
-              float r[8];
-              unpack8(*(const uint4*)((const uint16_t*)p.C2 + (int64_t)row * p.ldc + col), r);
-#pragma unroll
-              for (int q = 0; q < 8; ++q) v[q] *= 2.f * r[q];
-            }
-            uint32_t w[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
-            *(uint4*)((uint16_t*)Cg + (int64_t)row * p.ldc + col) = make_uint4(w[0], w[1], w[2], w[3]);
-          }
-        }
-      }
-    }
-  }
+  if (p.kgrp)
+    kt_store<OUT, EPI, true>(p, acc, Cg, (float*)smem + wave * 16 * EPW, row0, rows, n0, lane, wm, wn);
+  else
+    kt_store<OUT, EPI, false>(p, acc, Cg, (float*)smem + wave * 16 * EPW, row0, rows, n0, lane, wm, wn);
 }
 
 template <int TA, int TB, Elt OUT, Epi EPI>
 hipError_t run_kt(const KtParams& p, int mtiles, hipStream_t s) {
   const int nN = cdiv(p.N, BN), tiles = mtiles * nN;
   if (tiles <= 0) return hipSuccess;
-  // K-grouped: each die gets ceil(tiles per group / 8) blocks per group (see kt_tile)
-  const int grid = p.kgrp ? p.G * kXcds * cdiv(cdiv(p.M, BM) * nN, kXcds)
-                          : cdiv(tiles, kXcds) * kXcds;
+  const int grid = p.kgrp ? kgrp_blocks(p) : cdiv(tiles, kXcds) * kXcds;
   hipLaunchKernelGGL((gemm_kt_kernel<TA, TB, OUT, EPI>), dim3(grid), dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }
