@@ -48,10 +48,12 @@ hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int32_t* cou
                            int bm, int32_t* mt_start, const DispatchExtras& ex, hipStream_t s);
 
 // out[t] = S[t] (optional, fp32) + sum_j gates[t, j] * Y[pos[t, j]], in fixed j order, rounded
-// once to out_elt.
+// once to out_elt. S may come as ns fp32 slabs s_slab elements apart (partial sums over ranges
+// of its K), added in slab order first.
 hipError_t launch_combine(const void* Y, Elt y_elt, int64_t ldy, const float* S, int64_t lds,
                           const int32_t* pos, const float* gates, int T, int D, int k, void* out,
-                          Elt out_elt, int64_t ldo, hipStream_t s);
+                          Elt out_elt, int64_t ldo, hipStream_t s, int ns = 1,
+                          int64_t s_slab = 0);
 
 // Per-row e4m3 quantisation of bf16 rows: scale[t] = amax / 448 (1 for a zero row),
 // q[t, :] = e4m3(x * fp32(448 / amax)).

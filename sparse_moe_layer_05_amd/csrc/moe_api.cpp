@@ -30,6 +30,8 @@ struct Plan {
   size_t Y = 0, total = 0;
   int lsplit = 1;    // K ranges of the streamed projection into the latent width (decode)
   size_t xpart = 0;  // its fp32 slabs [lsplit][T][L]
+  int ssplit = 1;    // K ranges of the shared expert's down projection streamed with the routed
+                     // one (decode, bf16): fp32 slabs [ssplit][T][H] after the pair rows of Y
 };
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -125,7 +127,16 @@ int32_t make_plan(const moe_desc_t* d, bool latent_call, Plan* pl) {
   if (p.Is) p.hs = take(Tz * (size_t)p.Is * ea);
   if (p.Is && !p.L && p.path == MOE_PATH_GROUPED) p.S = take(Tz * (size_t)p.H * 4);
   if (p.path == MOE_PATH_STREAM) {
-    const size_t rows = P + ((p.Is && !p.L) ? Tz : 0);
+    // The shared expert's down projection (K = I_s) is dealt out with the routed one (K = I) in
+    // units of 32 rows: cut its K into about I_s / I ranges so that all units are about the same
+    // size and the round-robin deal stays balanced (Nano: 3712 = 2 x 1856).
+    if (p.Is && !p.L && p.ex == Elt::BF16) {
+      int ns = (p.Is + p.I / 2) / p.I;
+      ns = ns < 1 ? 1 : (ns > 4 ? 4 : ns);
+      while (ns > 1 && p.Is % (ns * 8)) --ns;
+      p.ssplit = ns;
+    }
+    const size_t rows = P + ((p.Is && !p.L) ? (size_t)p.ssplit * Tz : 0);
     p.Y = take(rows * (size_t)p.D * 4);
   } else {
     p.Y = take(P * (size_t)p.D * ea);
@@ -457,6 +468,7 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
     if (sh) {
       dn.As = hs; dn.lda_s = Is; dn.Ws = w->Ws_down;
       dn.Ns = H; dn.Ks = Is; dn.Ts = T; dn.out_s = (float*)Y + (size_t)P * D; dn.ldo_s = D;
+      dn.ksplit_s = pl.ssplit;
     }
     dn.store = kStoreF32;
     dn.slice_e = slices; dn.slice_r = slices + max_sl; dn.n_slices = slices + 2 * max_sl;
@@ -536,7 +548,9 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
       }
     }
     MOE_SPAN("combine:y");
-    MOE_TRY(launch_combine(Y, y_elt, D, S, H, pos, gates, T, D, k, y, act, H, s));
+    const int ns = stream_path && S ? pl.ssplit : 1;  // the shared output's K-range slabs
+    MOE_TRY(launch_combine(Y, y_elt, D, S, H, pos, gates, T, D, k, y, act, H, s, ns,
+                           (int64_t)T * H));
   } else {
     void* z = base + pl.z;
     {

@@ -469,10 +469,11 @@ __global__ __launch_bounds__(kDispatchChunk) void dispatch_scatter(
 
 // ---------------------------------------------------------------------------------- combine
 // One workgroup per token; each thread owns 8 consecutive columns (one 16-byte bf16 load or two
-// fp32 loads per source row). Sum order: S (fp32) first, then j = 0..k-1.
+// fp32 loads per source row). Sum order: S (fp32; its ns slabs in order) first, then j = 0..k-1.
 template <Elt YT, Elt OT>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y, int64_t ldy,
                                                       const float* __restrict__ S, int64_t lds,
+                                                      int ns, int64_t s_slab,
                                                       const int32_t* __restrict__ pos,
                                                       const float* __restrict__ gates, int T,
                                                       int D, int k, void* __restrict__ out,
@@ -505,6 +506,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y
       const float4 b = *(const float4*)(S + t * lds + c + 4);
       acc[0] = a.x; acc[1] = a.y; acc[2] = a.z; acc[3] = a.w;
       acc[4] = b.x; acc[5] = b.y; acc[6] = b.z; acc[7] = b.w;
+      for (int q = 1; q < ns; ++q) {
+        const float* Sq = S + q * s_slab + t * lds + c;
+        const float4 e = *(const float4*)Sq, f = *(const float4*)(Sq + 4);
+        acc[0] += e.x; acc[1] += e.y; acc[2] += e.z; acc[3] += e.w;
+        acc[4] += f.x; acc[5] += f.y; acc[6] += f.z; acc[7] += f.w;
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = 0.f;
@@ -692,19 +699,20 @@ hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int32_t* cou
 
 hipError_t launch_combine(const void* Y, Elt y_elt, int64_t ldy, const float* S, int64_t lds,
                           const int32_t* pos, const float* gates, int T, int D, int k, void* out,
-                          Elt out_elt, int64_t ldo, hipStream_t s) {
+                          Elt out_elt, int64_t ldo, hipStream_t s, int ns, int64_t s_slab) {
   if (T <= 0) return hipSuccess;
+  if (ns < 1 || (ns > 1 && !S)) return hipErrorInvalidValue;
   // Many tokens: one workgroup per token. Few tokens (decode): a token's columns are split over
   // workgroups of one wave, 512 columns each, so that enough of them run at once.
   const bool few = T < 1024;
   const int threads = few ? 64 : (D / 8 >= 256 ? 256 : ((D / 8 + 63) / 64) * 64);
   const dim3 grid(T, few ? cdiv(D, 512) : 1), block(threads);
   if (y_elt == Elt::BF16 && out_elt == Elt::BF16)
-    hipLaunchKernelGGL((combine_kernel<Elt::BF16, Elt::BF16>), grid, block, 0, s, Y, ldy, S, lds, pos, gates, T, D, k, out, ldo);
+    hipLaunchKernelGGL((combine_kernel<Elt::BF16, Elt::BF16>), grid, block, 0, s, Y, ldy, S, lds, ns, s_slab, pos, gates, T, D, k, out, ldo);
   else if (y_elt == Elt::F32 && out_elt == Elt::BF16)
-    hipLaunchKernelGGL((combine_kernel<Elt::F32, Elt::BF16>), grid, block, 0, s, Y, ldy, S, lds, pos, gates, T, D, k, out, ldo);
+    hipLaunchKernelGGL((combine_kernel<Elt::F32, Elt::BF16>), grid, block, 0, s, Y, ldy, S, lds, ns, s_slab, pos, gates, T, D, k, out, ldo);
   else if (y_elt == Elt::F32 && out_elt == Elt::F32)
-    hipLaunchKernelGGL((combine_kernel<Elt::F32, Elt::F32>), grid, block, 0, s, Y, ldy, S, lds, pos, gates, T, D, k, out, ldo);
+    hipLaunchKernelGGL((combine_kernel<Elt::F32, Elt::F32>), grid, block, 0, s, Y, ldy, S, lds, ns, s_slab, pos, gates, T, D, k, out, ldo);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

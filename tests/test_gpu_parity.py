@@ -150,6 +150,11 @@ SMALL = {
     # few tokens and a wide H: the streamed projection into the latent width splits K in four
     "latent_split_small": mi.LayerConfig("latent_split_small", T=20, H=1024, E=16, k=4, I=64,
                                          latent=64, I_shared=32),
+    # a shared expert three times as wide as the routed ones: on the decode path its down
+    # projection is streamed in three K ranges (shorter than one batch) whose fp32 slabs the
+    # combine adds
+    "bf16_shared_split": mi.LayerConfig("bf16_shared_split", T=37, H=256, E=16, k=4, I=64,
+                                        I_shared=192),
 }
 MX_ONLY = {"mxfp4_one": dataclasses.replace(SMALL["mxfp4_long"], name="mxfp4_one", T=1)}
 MX_SMALL = ["mxfp4_small", "mxfp8_small", "mxfp4_long", "mxfp8_long", "latent_mxfp4_small",
@@ -164,7 +169,7 @@ def test_small_layer_all_tokens(name):
 
 @pytest.mark.parametrize("name", ["bf16_ragged", "bf16_no_shared", "latent_small",
                                   "latent_small_shared", "latent_split_small", "bf16_e6",
-                                  "bf16_e13", "bf16_max_routing"])
+                                  "bf16_e13", "bf16_max_routing", "bf16_shared_split"])
 def test_stream_and_grouped_paths_agree_with_oracle(name):
     inp = mi.make_layer(SMALL[name], seed=2)
     ys, _ = check_full(inp, "stream")
