@@ -16,71 +16,68 @@ namespace moe {
 namespace {
 
 // ------------------------------------------------------------------------------------ top-k
-// Wave-wide max / min by DPP row shifts and row broadcasts (lane 63 ends with the result over
-// all 64 lanes), then read back from lane 63 as a wave-uniform value. A lane whose DPP source
-// is outside its row (or whose row is masked off) combines with the identity.
+// Order-preserving map of a float's bits to an unsigned integer (larger float, larger integer).
+__device__ __forceinline__ uint32_t okey(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// Wave-wide maximum of a 64-bit value by DPP row shifts and row broadcasts (lane 63 ends with
+// the result over all 64 lanes), then read back from lane 63 as a wave-uniform value. A lane
+// whose DPP source is outside its row (or whose row is masked off) combines with 0, the
+// identity.
 template <int CTRL, int ROWS>
-__device__ __forceinline__ float dpp_max_step(float v) {
-  const float o = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY),
-                                                             __float_as_int(v), CTRL, ROWS, 0xf,
-                                                             false));
-  return fmaxf(v, o);
+__device__ __forceinline__ uint64_t dpp_max_step_u64(uint64_t v) {
+  const uint32_t lo =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWS, 0xf, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROWS, 0xf, false);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > v ? o : v;
 }
-template <int CTRL, int ROWS>
-__device__ __forceinline__ int dpp_min_step(int v) {
-  return min(v, __builtin_amdgcn_update_dpp(0x7FFFFFFF, v, CTRL, ROWS, 0xf, false));
-}
-__device__ __forceinline__ float wave_max(float v) {
-  v = dpp_max_step<0x111, 0xf>(v);  // row_shr:1
-  v = dpp_max_step<0x112, 0xf>(v);  // row_shr:2
-  v = dpp_max_step<0x114, 0xf>(v);  // row_shr:4
-  v = dpp_max_step<0x118, 0xf>(v);  // row_shr:8: lane 15 of each row holds the row's max
-  v = dpp_max_step<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
-  v = dpp_max_step<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-__device__ __forceinline__ int wave_min(int v) {
-  v = dpp_min_step<0x111, 0xf>(v);
-  v = dpp_min_step<0x112, 0xf>(v);
-  v = dpp_min_step<0x114, 0xf>(v);
-  v = dpp_min_step<0x118, 0xf>(v);
-  v = dpp_min_step<0x142, 0xa>(v);
-  v = dpp_min_step<0x143, 0xc>(v);
-  return __builtin_amdgcn_readlane(v, 63);
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_max_step_u64<0x111, 0xf>(v);  // row_shr:1
+  v = dpp_max_step_u64<0x112, 0xf>(v);  // row_shr:2
+  v = dpp_max_step_u64<0x114, 0xf>(v);  // row_shr:4
+  v = dpp_max_step_u64<0x118, 0xf>(v);  // row_shr:8: lane 15 of each row holds the row's max
+  v = dpp_max_step_u64<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step_u64<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // k rounds of selection over the keys of one token; lane l holds experts l, l + 64, ... Each
-// round takes the largest free key (a wave max), then the lowest expert holding it (a wave
-// min: equal keys go to the lower index), and reads that expert's score from its lane. Writes
-// the k experts (descending key) and their gates (scores renormalised over the selection).
+// expert carries one 64-bit value, its key's order-preserving bits above its inverted index, so
+// that one wave-wide maximum per round yields the largest free key and, among equal keys, the
+// lowest expert (a float maximum followed by an index minimum took two reductions a round).
+// Writes the k experts (descending key) and their gates (scores renormalised over the
+// selection).
 template <int NPER>
 __device__ __forceinline__ void select_topk(const float* key, const float* sc, int lane, int E,
                                             int k, int32_t* __restrict__ idx_t,
                                             float* __restrict__ gates_t) {
-  uint32_t taken = 0;
+  uint64_t c[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int e = lane + 64 * i;
+    c[i] = e < E ? ((uint64_t)okey(key[i]) << 32) | (uint32_t)~e : 0;
+  }
   float sum = 0.f, mine = 0.f;
   for (int j = 0; j < k; ++j) {
-    float m = -INFINITY;
+    uint64_t m = 0;
 #pragma unroll
-    for (int i = 0; i < NPER; ++i) {
-      const bool free = !((taken >> i) & 1u) && lane + 64 * i < E;
-      if (free) m = fmaxf(m, key[i]);
-    }
-    m = wave_max(m);
-    int c = 0x7FFFFFFF;
-    float cs = 0.f;
+    for (int i = 0; i < NPER; ++i) m = c[i] > m ? c[i] : m;
+    m = wave_max_u64(m);
+    const int be = (int)~(uint32_t)m;
+    const int slot = be >> 6, owner = be & 63;
+    float v = 0.f;
 #pragma unroll
-    for (int i = NPER - 1; i >= 0; --i) {  // descending i: the lowest matching expert wins
-      const int e = lane + 64 * i;
-      const bool free = !((taken >> i) & 1u) && e < E;
-      if (free && key[i] == m) {
-        c = e;
-        cs = sc[i];
+    for (int i = 0; i < NPER; ++i)
+      if (i == slot) {
+        v = sc[i];
+        if (lane == owner) c[i] = 0;
       }
-    }
-    const int be = wave_min(c);
-    const float bs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), be & 63));
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    const float bs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), owner));
     sum += bs;                       // same order j = 0..k-1 on every lane: deterministic
     if (lane == j) mine = bs;
     if (lane == 0) idx_t[j] = be;
@@ -140,7 +137,7 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
 // s = fp32(1 / (1 + exp(-z))) is evaluated in double so that the rounded score does not depend
 // on a particular single-precision exp; key = s + b is one binary32 addition. Phase 2: wave 0
 // selects; lane l holds experts l, l + 64, ... and k rounds of a wave-wide arg-max over
-// (key desc, expert asc) by butterfly shuffles retire one winner each.
+// (key desc, expert asc) by DPP retire one winner each.
 template <int NPER>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int nsplit,
                                                    const float* __restrict__ bias, int T, int E,
