@@ -7,7 +7,8 @@
 //   K-contiguous rows (A[m][k]): 128 bytes of k per row and stage, 16-byte chunks XOR-swizzled by
 //     (row / 2) % 8, fragments read with ds_read_b128 (as in the forward GEMM);
 //   K-major rows (A[k][m], B[k][n]): 64 rows of k per stage, each holding the tile's 128 or 192
-//     contiguous columns, chunks XOR-swizzled by k % 8. A fragment lane needs 8 consecutive k of
+//     contiguous columns, chunks XOR-swizzled by row (swz_km) so that a transposing read meets
+//     every LDS bank at most as often as its size requires. A fragment lane needs 8 consecutive k of
 //     one column; gfx950's transposing read ds_read_b64_tr_b16 provides them. Within each group
 //     of 16 lanes, lane j of the group reads 8 bytes at row k0 + j / 4, column c0 + 4 (j % 4),
 //     and receives column c0 + j at rows k0 .. k0 + 3 (the lane layout was checked on the chip);
@@ -36,7 +37,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
 }
 
 __device__ __forceinline__ int swz_mk(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int swz_km(int k) { return k & 7; }
+// K-major stages: one transposing read of a 32-lane half-wave takes 32 contiguous bytes of each
+// of 4 consecutive k rows (k0 .. k0 + 3, k0 a multiple of 4) for two 16-lane groups, 4 chunks
+// of 16 bytes per row. The swizzle puts those 4 rows on disjoint banks: rows of 256 bytes (A,
+// 128 columns) all start on bank 0, so row k moves its chunks by (k % 4) groups of four; rows of
+// 384 bytes (B, 192 columns) alternate between banks 0 and 32, so rows 2 and 3 of each four
+// move by one group (chunk ^ 4 stays inside a row of 24 chunks). An XOR keeps it a bijection on
+// each row's chunks.
+template <int PITCH>
+__device__ __forceinline__ int swz_km(int k) {
+  static_assert(PITCH == 256 || PITCH == 384, "K-major rows are 128 or 192 bf16 columns");
+  return PITCH == 256 ? (k & 3) << 2 : ((k >> 1) & 1) << 2;
+}
 
 __device__ __forceinline__ void unpack8(const uint4 q, float* v) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
@@ -47,18 +59,20 @@ __device__ __forceinline__ void unpack8(const uint4 q, float* v) {
   }
 }
 
-// Byte offset of element (k, col) of a K-major stage with `pitch` bytes per row of k.
-__device__ __forceinline__ int km_addr(int k, int col, int pitch) {
-  return k * pitch + (((col >> 3) ^ swz_km(k)) << 4) + ((col & 7) << 1);
+// Byte offset of element (k, col) of a K-major stage with PITCH bytes per row of k.
+template <int PITCH>
+__device__ __forceinline__ int km_addr(int k, int col) {
+  return k * PITCH + (((col >> 3) ^ swz_km<PITCH>(k)) << 4) + ((col & 7) << 1);
 }
 
 // The 8 consecutive k (k0 .. k0 + 7 of this lane's 16-lane group) of one fragment column from a
 // K-major stage: `col0` is the group's first column (a multiple of 16), `j` the lane in its group.
-__device__ __forceinline__ bf16x8_t km_frag(const uint8_t* st, int pitch, int col0, int k0, int j) {
+template <int PITCH>
+__device__ __forceinline__ bf16x8_t km_frag(const uint8_t* st, int col0, int k0, int j) {
   typedef __attribute__((address_space(3))) v4i16_t lds_v4;
   const int col = col0 + 4 * (j & 3);
-  const uint8_t* p0 = st + km_addr(k0 + (j >> 2), col, pitch);
-  const uint8_t* p1 = st + km_addr(k0 + 4 + (j >> 2), col, pitch);
+  const uint8_t* p0 = st + km_addr<PITCH>(k0 + (j >> 2), col);
+  const uint8_t* p1 = st + km_addr<PITCH>(k0 + 4 + (j >> 2), col);
   const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(const void*)p0);
   const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(const void*)p1);
   const v8i16_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -142,7 +156,7 @@ __device__ __forceinline__ void kt_mma(const uint8_t* As, f32x16_t (&acc)[MB][NB
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       if constexpr (TA) {
-        a[buf][i] = km_frag(As, BM * 2, wm * WM + i * 32 + 16 * (lg & 1), 16 * s + 8 * (lg >> 1), lj);
+        a[buf][i] = km_frag<BM * 2>(As, wm * WM + i * 32 + 16 * (lg & 1), 16 * s + 8 * (lg >> 1), lj);
       } else {
         const int r = wm * WM + i * 32 + (lane & 31);
         const int ch = 2 * s + (lane >> 5);
@@ -151,7 +165,7 @@ __device__ __forceinline__ void kt_mma(const uint8_t* As, f32x16_t (&acc)[MB][NB
     }
 #pragma unroll
     for (int j = 0; j < NB; ++j)
-      b[buf][j] = km_frag(Bs, BN * 2, wn * WN + j * 32 + 16 * (lg & 1), 16 * s + 8 * (lg >> 1), lj);
+      b[buf][j] = km_frag<BN * 2>(Bs, wn * WN + j * 32 + 16 * (lg & 1), 16 * s + 8 * (lg >> 1), lj);
   };
   rd(0, 0);
 #pragma unroll
@@ -262,7 +276,7 @@ void gemm_kt_kernel(KtParams p) {
     if constexpr (TA) {
       const int byte = (wave + NW * i) * 1024 + lane * 16;
       const int kr = byte / PA, slot = (byte % PA) >> 4;
-      int col = row0 + (((slot ^ swz_km(kr))) << 3);
+      int col = row0 + ((slot ^ swz_km<PA>(kr)) << 3);
       col = min(col, p.M - 8);
       ka[i] = kr;
       oa[i] = (uint32_t)(kr * p.lda * 2 + col * 2);
@@ -276,7 +290,7 @@ void gemm_kt_kernel(KtParams p) {
   for (int i = 0; i < B_GRP; ++i) {
     const int byte = (wave + NW * i) * 1024 + lane * 16;
     const int kr = byte / PB, slot = (byte % PB) >> 4;
-    int col = n0 + ((slot ^ swz_km(kr)) << 3);
+    int col = n0 + ((slot ^ swz_km<PB>(kr)) << 3);
     col = min(col, p.N - 8);
     kb[i] = kr;
     ob[i] = gath ? (uint32_t)(col * 2) : (uint32_t)(kr * p.ldb * 2 + col * 2);
