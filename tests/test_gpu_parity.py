@@ -558,3 +558,45 @@ def test_graph_replay_matches_eager(name, path):
         torch.cuda.synchronize()
         assert torch.equal(layer.y, want), f"replay {i}"
         del junk
+
+
+@pytest.mark.parametrize("name", ["mxfp4_small", "fp8_small"])
+def test_concurrent_calls_on_two_streams_match_serial_calls(name):
+    # The decode path of a layer with 8-bit or 4-bit experts forks the device's side stream
+    # (shared by every call on that device). Two host threads, each with its own stream,
+    # workspace, inputs and output, call it back to back at the same time: every result must
+    # equal that layer's single-threaded result bit for bit.
+    import threading
+    cfg = SMALL[name]
+    layers = [moe.layer_from(moe.to_device(mi.make_layer(cfg, seed=s)), cfg.k, path="stream")
+              for s in (21, 22)]
+    want = [layer().clone() for layer in layers]
+    torch.cuda.synchronize()
+    assert not torch.equal(want[0], want[1])
+    streams = [torch.cuda.Stream() for _ in layers]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    got = [[], []]
+    start = threading.Barrier(2)
+    errors = []
+
+    def work(i):
+        try:
+            start.wait()
+            with torch.cuda.stream(streams[i]):
+                for _ in range(16):
+                    got[i].append(layers[i](stream=streams[i]).clone())
+        except Exception as e:  # reported in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(2):
+        assert len(got[i]) == 16
+        for j, y in enumerate(got[i]):
+            assert torch.equal(y, want[i]), (i, j)
