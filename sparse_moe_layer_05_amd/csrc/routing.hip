@@ -201,7 +201,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 // Tokens are cut into chunks of 256 (one workgroup each). Inside a chunk, an LDS bitmask per
 // expert records which of the 256 tokens chose it; the popcount of the bits below a token is
 // its stable rank inside the chunk, and chunk bases from a prefix over chunks make the global
-// order "experts ascending, tokens ascending" without any order-deciding atomics.
+// order "experts ascending, tokens ascending" without any order-deciding atomics. The masks are
+// stored word-major, word w of expert e at w * E + e, so that the lanes of a wave, which set
+// bits for unrelated experts, and a sweep over experts spread over the LDS banks (expert-major
+// rows of 8 words put every expert on one of 8 banks).
 __device__ __forceinline__ uint64_t build_masks(const int32_t* __restrict__ idx, int T, int E,
                                                 int k, uint32_t* mask, int t, int tid) {
   for (int i = tid; i < E * 8; i += kDispatchChunk) mask[i] = 0;
@@ -216,7 +219,7 @@ __device__ __forceinline__ uint64_t build_masks(const int32_t* __restrict__ idx,
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         if ((unsigned)ev[i] >= (unsigned)E) continue;
-        const uint32_t old = atomicOr(&mask[ev[i] * 8 + (tid >> 5)], bit);
+        const uint32_t old = atomicOr(&mask[(tid >> 5) * E + ev[i]], bit);
         if (!(old & bit)) valid |= 1ull << (j0 + i);  // a repeated expert in one token is dropped
       }
     }
@@ -234,7 +237,7 @@ __global__ __launch_bounds__(kDispatchChunk) void dispatch_count(const int32_t* 
   for (int e = tid; e < E; e += kDispatchChunk) {
     int n = 0;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) n += __popc(mask[e * 8 + w]);
+    for (int w = 0; w < 8; ++w) n += __popc(mask[w * E + e]);
     ccount[(int64_t)c * E + e] = n;
   }
 }
@@ -360,6 +363,8 @@ __global__ __launch_bounds__(1024) void dispatch_scan(const int32_t* __restrict_
 // most 16). A pair is kept when its expert is in range and no earlier slot of the same token
 // chose that expert (the first occurrence wins, decided without atomics).
 constexpr int kSmallPairs = 16;   // pairs per thread: T*k <= 256*64
+constexpr int kSmallStage = 8;    // slots per token above which the selections go to LDS
+template <bool STAGED>
 __global__ __launch_bounds__(1024) void dispatch_small(const int32_t* __restrict__ idx, int T,
                                                        int E, int k, int bm,
                                                        int32_t* __restrict__ counts,
@@ -370,8 +375,12 @@ __global__ __launch_bounds__(1024) void dispatch_small(const int32_t* __restrict
                                                        DispatchExtras ex) {
   __shared__ uint32_t mask[kMaxE * 8];
   __shared__ int32_t s[4][1024];
+  extern __shared__ int16_t sel[];  // STAGED: the T * k selections, -1 where out of range
   const int tid = threadIdx.x;
   const int P = T * k;
+  // STAGED (many slots per token): the earlier slots of a pair's token are read from LDS
+  // rather than L2; with few slots the loads from L2 measured faster
+  constexpr bool staged = STAGED;
   for (int i = tid; i < E * 8; i += 1024) mask[i] = 0;
   int ex_of[kSmallPairs];
   uint32_t keep = 0;
@@ -379,7 +388,9 @@ __global__ __launch_bounds__(1024) void dispatch_small(const int32_t* __restrict
   for (int c = 0; c < kSmallPairs; ++c) {
     const int pr = tid + 1024 * c;
     ex_of[c] = pr < P ? idx[pr] : -1;
+    if (staged && pr < P) sel[pr] = (int16_t)((unsigned)ex_of[c] < (unsigned)E ? ex_of[c] : -1);
   }
+  __syncthreads();  // mask cleared, selections staged
 #pragma unroll
   for (int c = 0; c < kSmallPairs; ++c) {
     const int pr = tid + 1024 * c;
@@ -387,22 +398,24 @@ __global__ __launch_bounds__(1024) void dispatch_small(const int32_t* __restrict
     if (pr < P && (unsigned)e < (unsigned)E) {
       const int t = pr / k, j = pr - t * k;
       bool dup = false;  // independent loads, no early exit
-      for (int jj = 0; jj < j; ++jj) dup |= idx[(int64_t)t * k + jj] == e;
+      if constexpr (staged)
+        for (int jj = 0; jj < j; ++jj) dup |= sel[t * k + jj] == e;
+      else
+        for (int jj = 0; jj < j; ++jj) dup |= idx[(int64_t)t * k + jj] == e;
       if (!dup) keep |= 1u << c;
     }
   }
-  __syncthreads();  // mask cleared
 #pragma unroll
   for (int c = 0; c < kSmallPairs; ++c)
     if ((keep >> c) & 1u) {
       const int t = (tid + 1024 * c) / k;
-      atomicOr(&mask[ex_of[c] * 8 + (t >> 5)], 1u << (t & 31));
+      atomicOr(&mask[(t >> 5) * E + ex_of[c]], 1u << (t & 31));
     }
   __syncthreads();
   int tot = 0;
   if (tid < E)
 #pragma unroll
-    for (int w = 0; w < 8; ++w) tot += __popc(mask[tid * 8 + w]);
+    for (int w = 0; w < 8; ++w) tot += __popc(mask[w * E + tid]);
   dispatch_totals(tid, E, tot, bm, s, counts, offsets, mt_start, ex);
   // s[0][e] - count[e] is the base of expert e; counts are re-derived from the masks below.
 #pragma unroll
@@ -416,11 +429,11 @@ __global__ __launch_bounds__(1024) void dispatch_small(const int32_t* __restrict
     const int e = ex_of[c];
     const int t = pr / k, w = t >> 5;
     const uint32_t below = (1u << (t & 31)) - 1u;
-    int cnt = 0, rank = __popc(mask[e * 8 + w] & below);
+    int cnt = 0, rank = __popc(mask[w * E + e] & below);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      cnt += __popc(mask[e * 8 + q]);
-      if (q < w) rank += __popc(mask[e * 8 + q]);
+      cnt += __popc(mask[q * E + e]);
+      if (q < w) rank += __popc(mask[q * E + e]);
     }
     const int r = s[0][e] - cnt + rank;
     perm[r] = t;
@@ -455,8 +468,8 @@ __global__ __launch_bounds__(kDispatchChunk) void dispatch_scatter(
         continue;
       }
       const int e = ev[i];
-      int rank = __popc(mask[e * 8 + w] & below);
-      for (int q = 0; q < w; ++q) rank += __popc(mask[e * 8 + q]);
+      int rank = __popc(mask[w * E + e] & below);
+      for (int q = 0; q < w; ++q) rank += __popc(mask[q * E + e]);
       const int r = base[i] + rank;
       perm[r] = t;
       pos[(int64_t)t * k + j] = r;
@@ -678,8 +691,13 @@ hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int32_t* cou
                            int bm, int32_t* mt_start, const DispatchExtras& ex, hipStream_t s) {
   const int nch = (T + kDispatchChunk - 1) / kDispatchChunk;
   if (nch <= 1) {
-    hipLaunchKernelGGL(dispatch_small, dim3(1), dim3(1024), 0, s, idx, T, E, k, bm, counts,
-                       offsets, perm, pos, mt_start, ex);
+    if (k > kSmallStage)
+      hipLaunchKernelGGL(dispatch_small<true>, dim3(1), dim3(1024),
+                         (size_t)T * k * sizeof(int16_t), s, idx, T, E, k, bm, counts, offsets,
+                         perm, pos, mt_start, ex);
+    else
+      hipLaunchKernelGGL(dispatch_small<false>, dim3(1), dim3(1024), 0, s, idx, T, E, k, bm,
+                         counts, offsets, perm, pos, mt_start, ex);
     return hipGetLastError();
   }
   int32_t* ccount = scratch;
