@@ -30,11 +30,13 @@ struct Plan {
   size_t Y = 0, total = 0;
   int lsplit = 1;    // K ranges of the streamed projection into the latent width (decode)
   size_t xpart = 0;  // its fp32 slabs [lsplit][T][L]
-  int ssplit = 1;    // K ranges of the shared expert's down projection streamed with the routed
-                     // one (decode, bf16): fp32 slabs [ssplit][T][H] after the pair rows of Y
+  int ssplit = 1;    // K ranges of the shared expert's down projection on the decode path (plain
+                     // layer): fp32 slabs [ssplit][T][H] after the pair rows of Y
 };
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int kNarrowSharedSplit = 4;
 
 int32_t make_plan(const moe_desc_t* d, bool latent_call, Plan* pl) {
   if (!d) return MOE_ERR_INVALID_ARG;
@@ -130,8 +132,11 @@ int32_t make_plan(const moe_desc_t* d, bool latent_call, Plan* pl) {
     // The shared expert's down projection (K = I_s) is dealt out with the routed one (K = I) in
     // units of 32 rows: cut its K into about I_s / I ranges so that all units are about the same
     // size and the round-robin deal stays balanced (Nano: 3712 = 2 x 1856).
-    if (p.Is && !p.L && p.ex == Elt::BF16) {
-      int ns = (p.Is + p.I / 2) / p.I;
+    // With 8-bit or 4-bit experts the shared expert streams in launches of its own on the side
+    // stream; there four K ranges shorten each wave's chain of dependent batches (I_s / 4 of
+    // K instead of all of it), so that it leaves the routed launches' bandwidth sooner.
+    if (p.Is && !p.L) {
+      int ns = p.ex == Elt::BF16 ? (p.Is + p.I / 2) / p.I : kNarrowSharedSplit;
       ns = ns < 1 ? 1 : (ns > 4 ? 4 : ns);
       while (ns > 1 && p.Is % (ns * 8)) --ns;
       p.ssplit = ns;
@@ -334,7 +339,7 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
     {
       MOE_SPAN_ON("stream:shared_down", side->s);
       MOE_TRY(stream_dense(hs, Is, w->Ws_down, H, Is, T, (float*)Y + (size_t)P * D, D, kStoreF32,
-                           side->s));
+                           side->s, pl.ssplit));
     }
     MOE_TRY(hipEventRecord(side->join, side->s));
   }
