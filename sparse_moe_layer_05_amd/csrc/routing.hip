@@ -561,16 +561,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y
 }
 
 // -------------------------------------------------------------------------------- quantise
-// One workgroup per row: amax by wave shuffles + LDS, then e4m3 codes of x * (448 / amax). A row
-// of up to 256 * 8 * kQuantRegs elements is read once and kept in registers; longer rows are
-// read a second time for the codes.
-constexpr int kQuantRegs = 4;
+// One wave per row, four rows per workgroup: amax by a wave reduction (no barrier), then e4m3
+// codes of x * (448 / amax). A row of up to 64 * 8 * kQuantRegs elements is read once and kept
+// in registers; longer rows are read a second time for the codes. (A workgroup per row spent
+// most of its time on the block reduction's barrier for rows of a few KB.)
+constexpr int kQuantRegs = 8;
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x,
-                                                         int64_t ldx, int H,
+                                                         int64_t ldx, int T, int H,
                                                          uint8_t* __restrict__ q,
                                                          float* __restrict__ scale) {
-  __shared__ float s_max[4];
-  const int t = blockIdx.x, tid = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
   const uint16_t* row = x + (int64_t)t * ldx;
   uint4 keep[kQuantRegs];
   float m = 0.f;
@@ -584,19 +586,17 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
   };
 #pragma unroll
   for (int r = 0; r < kQuantRegs; ++r) {
-    const int c = (r * 256 + tid) * 8;
+    const int c = (r * 64 + lane) * 8;
     keep[r] = c < H ? *(const uint4*)(row + c) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int r = 0; r < kQuantRegs; ++r) amax8(keep[r]);
-  for (int c = (kQuantRegs * 256 + tid) * 8; c < H; c += 256 * 8) amax8(*(const uint4*)(row + c));
+  for (int c = (kQuantRegs * 64 + lane) * 8; c < H; c += 64 * 8) amax8(*(const uint4*)(row + c));
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((tid & 63) == 0) s_max[tid >> 6] = m;
-  __syncthreads();
-  const float amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+  const float amax = m;
   const float inv = amax > 0.f ? 448.f / amax : 1.f;   // codes = e4m3(x * inv)
-  if (tid == 0) scale[t] = amax > 0.f ? amax / 448.f : 1.f;
+  if (lane == 0) scale[t] = amax > 0.f ? amax / 448.f : 1.f;
   auto codes8 = [&](const uint4 v, int c) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t o[2];
@@ -612,10 +612,10 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
   };
 #pragma unroll
   for (int r = 0; r < kQuantRegs; ++r) {
-    const int c = (r * 256 + tid) * 8;
+    const int c = (r * 64 + lane) * 8;
     if (c < H) codes8(keep[r], c);
   }
-  for (int c = (kQuantRegs * 256 + tid) * 8; c < H; c += 256 * 8) codes8(*(const uint4*)(row + c), c);
+  for (int c = (kQuantRegs * 64 + lane) * 8; c < H; c += 64 * 8) codes8(*(const uint4*)(row + c), c);
 }
 
 // One workgroup; thread e handles expert e (loops for E > 1024). The mean-load comparison is done
@@ -736,7 +736,8 @@ hipError_t launch_combine(const void* Y, Elt y_elt, int64_t ldy, const float* S,
 hipError_t launch_quant_rows(const uint16_t* x, int64_t ldx, int T, int H, uint8_t* q,
                              float* scale, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(quant_rows_kernel, dim3(T), dim3(256), 0, s, x, ldx, H, q, scale);
+  hipLaunchKernelGGL(quant_rows_kernel, dim3(cdiv(T, 4)), dim3(256), 0, s, x, ldx, T, H, q,
+                     scale);
   return hipGetLastError();
 }
 
