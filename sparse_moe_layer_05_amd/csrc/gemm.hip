@@ -52,9 +52,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
 template <Elt E> struct EltBytes { static constexpr int v = E == Elt::F32 ? 4 : (E == Elt::BF16 ? 2 : 1); };
 
 // Logical tile L -> its group g, first output row, rows (<= BM) and first column. Grouped
-// launches walk a device-built prefix of per-group M-tiles (mt_start); a group's tiles are
-// N-major with M fastest, so consecutive tiles share a weight panel. Dense launches walk bands of
-// 8 M-tiles, N-major inside a band.
+// launches walk a device-built prefix of per-group M-tiles (mt_start); inside a group, and for
+// dense launches, tiles go in bands of 8 M-tiles, N-major inside a band with M fastest.
 template <int BM, int BN>
 __device__ __forceinline__ void decode_tile(const GemmParams& p, int nN, int L, int& g, int& row0,
                                             int& rows, int& n0) {
@@ -68,8 +67,12 @@ __device__ __forceinline__ void decode_tile(const GemmParams& p, int nN, int L, 
     g = lo;
     const int mt_g = p.mt_start[g + 1] - p.mt_start[g];
     const int local = L - p.mt_start[g] * nN;
-    n0 = (local / mt_g) * BN;
-    const int mt = local % mt_g;
+    constexpr int GB = 8;
+    const int first = (local / (GB * nN)) * GB;
+    const int gm = min(GB, mt_g - first);
+    const int within = local - first * nN;
+    n0 = (within / gm) * BN;
+    const int mt = first + within % gm;
     row0 = p.offs[g] + mt * BM;
     rows = min(BM, p.offs[g + 1] - row0);
   } else {
