@@ -668,6 +668,8 @@ hipError_t run_mfma(const GemmParams& p, int mtiles, hipStream_t s) {
   return hipGetLastError();
 }
 
+}  // namespace
+
 // Workgroups of a persistent launch: two per CU (the LDS of two 80 KB stage pairs), rounded down
 // to whole groups of 8 (one per die).
 int persist_grid() {
@@ -682,6 +684,8 @@ int persist_grid() {
   }
   return std::max(kXcds, (2 * cus[dev]) / kXcds * kXcds);
 }
+
+namespace {
 
 template <int BM, int BN, int WGM, int WGN, Elt AB, Elt OUT, Epi EPI>
 hipError_t run_persist(const GemmParams& p, int mtiles, hipStream_t s) {

@@ -72,4 +72,7 @@ inline int max_group_mtiles(int P, int G, int BM) { return (P + G * (BM - 1)) / 
 hipError_t launch_gemm(const GemmKind& kind, const GemmParams& p, int max_mtiles,
                        hipStream_t stream);
 
+// Workgroups of a persistent launch on the current device: two per CU, a multiple of 8.
+int persist_grid();
+
 }  // namespace moe

@@ -15,6 +15,8 @@
 //     two such reads give the 8 k values.
 // Rows of k beyond a K window (the last step of a group) are skipped by the loads and zeroed in
 // LDS; columns beyond M or N read a valid column instead (their outputs are never stored).
+#include <algorithm>
+
 #include "common.hpp"
 #include "gemm_kt.hpp"
 
@@ -378,6 +380,148 @@ void gemm_kt_kernel(KtParams p) {
     kt_store<OUT, EPI, false>(p, acc, Cg, (float*)smem + wave * 16 * EPW, row0, rows, n0, lane, wm, wn);
 }
 
+// Data gradients of a row-grouped launch (A K-contiguous over the pair rows, B each group's
+// K-major weights), persistent like the forward's grouped GEMMs: two workgroups per CU walk the
+// tiles of each die's contiguous range, and a tile's last K-step loads the next tile's first
+// K-step into the stage it frees, so those loads overlap the last products and the epilogue.
+template <Elt OUT, Epi EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm_kt_rows_persist(KtParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  constexpr int A_GRP = BM / (8 * NW), B_GRP = BN * KS * 2 / 1024 / NW;
+  constexpr int PB = BN * 2;  // K-major pitch of B
+  const int nN = cdiv(p.N, BN);
+  const int total = p.mt_start[p.G] * nN;
+  const int d = blockIdx.x % kXcds, Qd = gridDim.x / kXcds;
+  const int lo_t = d * cdiv(total, kXcds);
+  const int hi_t = min(total, lo_t + cdiv(total, kXcds));
+  int L = lo_t + (int)blockIdx.x / kXcds;
+  if (L >= hi_t) return;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int lrow = lane >> 3, lpos = lane & 7;
+  const int cofs = (lpos ^ swz_mk(wave * 8 + lrow)) << 4;
+  const int K = p.K, nk = cdiv(K, KS);
+  const __amdgpu_buffer_rsrc_t ra = rsrc(p.A, (int64_t)p.a_rows * p.lda * 2);
+  int kb[B_GRP];  // this lane's k row in each of its B loads (the same in every tile)
+#pragma unroll
+  for (int i = 0; i < B_GRP; ++i) kb[i] = ((wave + NW * i) * 1024 + lane * 16) / PB;
+
+  // A tile: its group, rows and columns; its B resource (the group's weights) and this lane's
+  // offsets (padding rows of a partial M-tile point out of range and take no access).
+  __amdgpu_buffer_rsrc_t rb_c, rb_n;
+  uint32_t oa_c[A_GRP], ob_c[B_GRP], oa_n[A_GRP], ob_n[B_GRP];
+  int row0_c, rows_c, n0_c, row0_n = 0, rows_n = 0, n0_n = 0;
+  auto setup = [&](int Lt, __amdgpu_buffer_rsrc_t& rbx, uint32_t* oax, uint32_t* obx, int& row0x,
+                   int& rowsx, int& n0x) {
+    const int key = Lt / nN;
+    int lo = 0, hi = p.G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.mt_start[mid] <= key) lo = mid; else hi = mid - 1;
+    }
+    const int g = lo;
+    const int mt_g = p.mt_start[g + 1] - p.mt_start[g];
+    const int local = Lt - p.mt_start[g] * nN;
+    n0x = (local / mt_g) * BN;
+    row0x = p.offs[g] + (local % mt_g) * BM;
+    rowsx = min(BM, p.offs[g + 1] - row0x);
+    rbx = rsrc((const uint8_t*)p.B + (int64_t)g * p.b_gstride * 2, (int64_t)K * p.ldb * 2);
+#pragma unroll
+    for (int i = 0; i < A_GRP; ++i) {
+      const int r = (wave + NW * i) * 8 + lrow;
+      oax[i] = r < rowsx ? (uint32_t)((int64_t)(row0x + r) * p.lda * 2) + cofs : 0xFFFFFFF0u;
+    }
+#pragma unroll
+    for (int i = 0; i < B_GRP; ++i) {
+      const int slot = (((wave + NW * i) * 1024 + lane * 16) % PB) >> 4;
+      const int col = min(n0x + ((slot ^ swz_km<PB>(kb[i])) << 3), p.N - 8);
+      obx[i] = (uint32_t)(kb[i] * p.ldb * 2 + col * 2);
+    }
+  };
+  // K-step ks of a tile into stage st; chunks beyond K (a partial last step) take an offset
+  // outside the buffers and are zeroed after landing
+  auto issue = [&](__amdgpu_buffer_rsrc_t rbx, const uint32_t* oax, const uint32_t* obx, int ks,
+                   uint8_t* st) {
+    const int left = K - ks * KS;
+#pragma unroll
+    for (int i = 0; i < A_GRP; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (__attribute__((address_space(3))) void*)(st + (wave + NW * i) * 1024), 16,
+          (int)(cofs < left * 2 ? oax[i] : 0xFFFFFFF0u), ks * KS * 2, 0, 0);
+#pragma unroll
+    for (int i = 0; i < B_GRP; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rbx, (__attribute__((address_space(3))) void*)(st + SA + (wave + NW * i) * 1024), 16,
+          (int)(kb[i] < left ? obx[i] : 0xFFFFFFF0u), ks * KS * (int)p.ldb * 2, 0, 0);
+  };
+  // A workgroup barrier without a memory fence (a fence would also wait for the loads in flight
+  // into the other stage); stage_barrier first waits for this wave's own loads of the stage it
+  // is about to read, the only vector memory operations outstanding besides epilogue stores.
+  auto barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  auto stage_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));  // vmcnt(0)
+    barrier();
+  };
+
+  setup(L, rb_c, oa_c, ob_c, row0_c, rows_c, n0_c);
+  issue(rb_c, oa_c, ob_c, 0, smem);
+  f32x16_t acc[MB][NB];
+  int par = 0;  // stage holding K-step 0 of the current tile
+  while (true) {
+    const int Ln = L + Qd;
+    const bool has_next = Ln < hi_t;
+    if (has_next) setup(Ln, rb_n, oa_n, ob_n, row0_n, rows_n, n0_n);
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int ks = 0; ks < nk; ++ks) {
+      stage_barrier();
+      uint8_t* st = smem + ((par + ks) & 1) * STAGE;
+      const int left = K - ks * KS;
+      if (left < KS) {  // uniform: zero the chunks beyond K
+#pragma unroll
+        for (int i = 0; i < A_GRP; ++i)
+          if (cofs >= left * 2)
+            *(uint4*)(st + (wave + NW * i) * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < B_GRP; ++i)
+          if (kb[i] >= left)
+            *(uint4*)(st + SA + (wave + NW * i) * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+        barrier();
+      }
+      uint8_t* other = smem + ((par + ks + 1) & 1) * STAGE;
+      if (ks + 1 < nk)
+        issue(rb_c, oa_c, ob_c, ks + 1, other);
+      else if (has_next)
+        issue(rb_n, oa_n, ob_n, 0, other);
+      kt_mma<0>(st, acc, lane, wm, wn);
+    }
+    barrier();  // every wave is done with the last stage: the epilogue reuses it
+    int el = lane;
+    asm volatile("" : "+v"(el));  // recomputed per tile: its addresses are not kept across tiles
+    kt_store<OUT, EPI, false>(p, acc, (uint8_t*)p.C,
+                              (float*)(smem + ((par + nk - 1) & 1) * STAGE) + wave * 16 * EPW,
+                              row0_c, rows_c, n0_c, el, wm, wn);
+    if (!has_next) break;
+    rb_c = rb_n;
+#pragma unroll
+    for (int i = 0; i < A_GRP; ++i) oa_c[i] = oa_n[i];
+#pragma unroll
+    for (int i = 0; i < B_GRP; ++i) ob_c[i] = ob_n[i];
+    row0_c = row0_n;
+    rows_c = rows_n;
+    n0_c = n0_n;
+    par = (par + nk) & 1;
+    L = Ln;
+  }
+}
+
 template <int TA, int TB, Elt OUT, Epi EPI>
 hipError_t run_kt(const KtParams& p, int mtiles, hipStream_t s) {
   const int nN = cdiv(p.N, BN), tiles = mtiles * nN;
@@ -405,6 +549,19 @@ hipError_t launch_gemm_kt(int ta, int tb, Elt out, Epi epi, const KtParams& p, i
       (!ta && (int64_t)p.a_rows * p.lda * 2 > kLim))
     return hipErrorInvalidValue;
   const int mt = p.kgrp ? p.G * cdiv(p.M, BM) : (p.mt_start ? max_mtiles : cdiv(p.M, BM));
+  if (ta == 0 && p.mt_start && !p.kgrp && p.K > 0 &&
+      ((out == Elt::BF16 && epi == Epi::DSqRelu) || (out == Elt::F32 && epi == Epi::Store))) {
+    // row-grouped data gradients: persistent
+    const int grid = std::min(cdiv(mt * cdiv(p.N, BN), kXcds) * kXcds, persist_grid());
+    if (grid <= 0) return hipSuccess;
+    if (out == Elt::BF16)
+      hipLaunchKernelGGL((gemm_kt_rows_persist<Elt::BF16, Epi::DSqRelu>), dim3(grid), dim3(64 * NW),
+                         0, s, p);
+    else
+      hipLaunchKernelGGL((gemm_kt_rows_persist<Elt::F32, Epi::Store>), dim3(grid), dim3(64 * NW), 0,
+                         s, p);
+    return hipGetLastError();
+  }
   if (ta == 0 && out == Elt::BF16 && epi == Epi::DSqRelu && !p.kgrp)
     return run_kt<0, 1, Elt::BF16, Epi::DSqRelu>(p, mt, s);
   if (ta == 0 && out == Elt::F32 && epi == Epi::Store && !p.kgrp)
