@@ -66,10 +66,12 @@ template <Elt T> struct Fmt;
 // R: blocks of 16 weight rows per unit, sharing the unit's token loads; U(R): steps per batch.
 // bf16 routed launches take two blocks: a unit's token bytes otherwise equal its weight bytes,
 // and two blocks measured 2% faster on the Nano decode step (four slower, from the longer tail
-// of fewer units). Dense launches of the shared slot alone have few units and keep one block.
+// of fewer units). Dense launches of the shared slot alone have few units and keep one block;
+// their batches of 5 steps keep the kernel at 136 registers, so that one of its waves fits on a
+// SIMD beside one of any routed kernel (at most 368 of 512) and the two launches overlap.
 template <> struct Fmt<Elt::BF16> {
   static constexpr int KS = 32, R = 2;            // elements per step, routed row blocks
-  static constexpr int U(int r) { return r == 1 ? 6 : 4; }
+  static constexpr int U(int r) { return r == 1 ? 5 : 4; }
   static constexpr int WH = 4, AB = 2;           // weight half-bytes / token bytes per element
   static constexpr int CW = 1, LW = 16, CWS = 0;
   static constexpr int CA = 1, LA = 16, CAS = 0;
@@ -104,7 +106,8 @@ template <> struct Fmt<Elt::MXFP8> {
   static constexpr int CA = 2, LA = 16, CAS = 64;
 };
 template <Elt T> constexpr bool kBlockScaled = T == Elt::MXFP4 || T == Elt::MXFP8;
-static_assert(Fmt<Elt::MXFP4>::U(4) % 4 == 0 && Fmt<Elt::MXFP4>::KS == 128,
+static_assert(Fmt<Elt::MXFP4>::U(2) % 4 == 0 && Fmt<Elt::MXFP4>::U(4) % 4 == 0 &&
+                  Fmt<Elt::MXFP4>::KS == 128,
               "wide scale loads take a batch's scales 4 steps (16 blocks of 32) at a time");
 constexpr int kMxBlock = 32;  // elements per E8M0 scale
 
@@ -408,12 +411,11 @@ __device__ void run_units(const StreamParams& p, int wave, int nwaves, bool shar
   // the shifted-last-batch path needs every unit's row to span at least one batch
   constexpr int BK = F::U(R) * F::KS;
   const bool full = (nrt == 0 || p.K >= BK) && (nsh == 0 || Kc >= BK);
-  // The four-row-block MXFP4 kernel loads a batch's scales 16 bytes at a time (kWideScale)
-  // when a row's scale count is a multiple of 4: LatentMoE decode 153.5 -> 135.5 us per step
-  // (16 byte loads per batch become 4). Not the others: the two-row-block MXFP4 kernel's wave
-  // must fit on a SIMD beside one of the dense bf16 kernel (360 + 152 of 512 registers) and the
-  // wide path takes 8 more; MXFP8 (two row blocks, 8 byte loads per batch) measured 1.3% slower.
-  if constexpr (T == Elt::MXFP4 && R == 4) {
+  // MXFP4 kernels load a batch's scales 16 bytes at a time (kWideScale) when a row's scale
+  // count is a multiple of 4: a byte load per step and row block becomes one 16-byte load per 4
+  // steps (LatentMoE decode 153.5 -> 135.5 us per step with four row blocks, Nano 198.5 -> 193.1
+  // with two). Not MXFP8 (two row blocks, 8 byte loads per batch): measured 1.3% slower.
+  if constexpr (T == Elt::MXFP4) {
     if (full && (p.K / kMxBlock) % 4 == 0) {
       stream_units<T, R, true, true>(wave, nsh + nrt, nwaves, lane, p.store, resolve);
       return;
