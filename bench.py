@@ -6,7 +6,8 @@
 A step is one full layer call (router GEMM, top-k, dispatch, expert GEMMs / weight streaming,
 shared expert, combine) over one batch of seeded synthetic tokens already resident in HBM. A
 workload named "<config>+backward" times the layer's backward pass instead (reported under
-'also').
+'also'), with fp32 gradients, and beside it the same pass writing the expert weight gradients
+in bf16.
 Prints one JSON line: tokens/s, the dominant kernel's roofline fraction (HIP events around that
 kernel's launches during the timed region, against algorithmic bytes or flops), and the
 double-precision oracle timed on a bounded token sample on the host as the CPU baseline.
@@ -213,9 +214,12 @@ def prepare(name, moe, mi, torch, path, cache=None):
         dy = moe.to_device({"dy": mi.make_grad_output(cfg, 0)})["dy"]
         bw = moe.backward_from(dev, cfg.k)
         bw.forward_train()
+        # the same pass writing the expert weight gradients in bf16 (MOE_WGRAD_BF16)
+        bw16 = moe.backward_from(dev, cfg.k, wgrad_bf16=True)
+        bw16.forward_train()
         return dict(cfg=cfg, inp=inp, dev=dev, rt=rt, layer=lambda: bw(dy, saved=True),
-                    recompute=lambda: bw(dy), train_forward=bw.forward_train, backward=True,
-                    name=name)
+                    recompute=lambda: bw(dy), train_forward=bw.forward_train,
+                    wgrad_bf16=lambda: bw16(dy, saved=True), backward=True, name=name)
     layer = moe.layer_from(dev, cfg.k, path=path, routing=rt)
     return dict(cfg=cfg, inp=inp, dev=dev, rt=rt, layer=layer, name=name)
 
@@ -324,8 +328,12 @@ def measure(w, moe, torch, steps, warmup, graph):
         # training forward that saves them (median single steps)
         rec = step_times(w["recompute"], torch, max(steps // 2, 10))
         fwd = step_times(w["train_forward"], torch, max(steps // 2, 10))
+        wg16 = float(np.median(step_times(w["wgrad_bf16"], torch, max(steps, 20))))
         extra = dict(backward_recompute_us=round(float(np.median(rec)), 1),
-                     forward_train_us=round(float(np.median(fwd)), 1))
+                     forward_train_us=round(float(np.median(fwd)), 1),
+                     backward_wgrad_bf16_us=round(wg16, 1),
+                     backward_wgrad_bf16_frac_of_bf16_peak=round(
+                         backward_flops(cfg) / (wg16 * 1e-6) / PEAK_MFMA["bf16"], 4))
     step = None
     if not w.get("backward"):
         step = step_roofline(cfg, counts, float(np.median(dist)), float(np.median(cold)))

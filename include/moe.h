@@ -98,6 +98,9 @@ typedef enum {
 #define MOE_ROUTING_GIVEN 4u     /* routing->idx and routing->gates are INPUTS: skip the router */
 #define MOE_SAVED_IN_WORKSPACE 8u /* moe_layer_backward only: the workspace holds what
                                     moe_layer_forward_train saved; skip the recompute */
+#define MOE_WGRAD_BF16 16u       /* moe_layer_backward: dW_up, dW_down, dWs_up and dWs_down are
+                                    written in bf16 (moe_layer_forward_train ignores it; the
+                                    inference calls reject it with MOE_ERR_INVALID_ARG) */
 
 typedef struct {
   int32_t T;           /* tokens */
@@ -212,7 +215,9 @@ int32_t moe_bias_update(const int32_t *counts, const float *target, int32_t E, f
  *   expert e_j's output and dY the gradient reaching the experts' gated sum (dy, or for LatentMoE
  *   dy W_out, rounded to bf16). The routing bias b only steers the selection: no gradient.
  * The squared ReLU's derivative is 2 relu(a). Every gradient is written (not accumulated) in
- * fp32, row-major, with D = H (or latent):
+ * fp32, row-major, with D = H (or latent); under MOE_WGRAD_BF16 the expert weight gradients
+ * dW_up, dW_down, dWs_up and dWs_down are written in bf16 instead, each element the fp32 result
+ * rounded to nearest even (the same sums, half the bytes stored):
  *   dx [T, H], dW_r [E, H], dW_up [E, I, D], dW_down [E, D, I], dWs_up [I_s, H], dWs_down [H, I_s]
  *   (when I_shared > 0), dW_in [latent, H] and dW_out [H, latent] (LatentMoE); all required when
  *   they apply.
@@ -230,10 +235,10 @@ int32_t moe_bias_update(const int32_t *counts, const float *target, int32_t E, f
 typedef struct {
   float *dx;
   float *dW_r;
-  float *dW_up;
-  float *dW_down;
-  float *dWs_up;
-  float *dWs_down;
+  void *dW_up;      /* fp32, or bf16 under MOE_WGRAD_BF16; so are the next three */
+  void *dW_down;
+  void *dWs_up;
+  void *dWs_down;
   float *dW_in;     /* LatentMoE only: [latent, H] */
   float *dW_out;    /* LatentMoE only: [H, latent] */
 } moe_grads_t;

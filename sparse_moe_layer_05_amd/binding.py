@@ -19,6 +19,7 @@ _EXPERT_DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_FP8_E4M3, "mxfp4
                   "mxfp8": MOE_MXFP8}
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 PATH_AUTO, PATH_GROUPED, PATH_STREAM, ROUTING_GIVEN, SAVED_IN_WORKSPACE = 0, 1, 2, 4, 8
+WGRAD_BF16 = 16
 _PATHS = {"auto": PATH_AUTO, "grouped": PATH_GROUPED, "stream": PATH_STREAM}
 
 EXPORTS = ("moe_workspace_size", "moe_layer_forward", "latent_moe_forward", "moe_route",
@@ -278,10 +279,11 @@ class Layer:
 
 class Backward:
     """One backward call prepared once (descriptor, weights, gradient outputs in fp32,
-    workspace): ``__call__(dy)`` writes the gradients of sum(dy * y) into ``self.grads``."""
+    workspace): ``__call__(dy)`` writes the gradients of sum(dy * y) into ``self.grads``.
+    ``wgrad_bf16``: the expert weight gradients (dW_up, dW_down, dWs_up, dWs_down) in bf16."""
 
     def __init__(self, x, W_r, b, W_up, W_down, k, *, Ws_up=None, Ws_down=None, W_in=None,
-                 W_out=None):
+                 W_out=None, wgrad_bf16=False):
         self.desc = make_desc(x, W_r, W_up, k, Ws_up, W_in)
         check_shapes(self.desc, x, W_r, b, W_up, W_down, Ws_up=Ws_up, Ws_down=Ws_down,
                      W_in=W_in, W_out=W_out)
@@ -291,12 +293,14 @@ class Backward:
         self.w = w
         self._keep = [x, W_r, b, W_up, W_down, Ws_up, Ws_down, W_in, W_out]
         f32 = dict(dtype=torch.float32, device=x.device)
+        wg = dict(dtype=torch.bfloat16 if wgrad_bf16 else torch.float32, device=x.device)
+        self.wgrad_bf16 = bool(wgrad_bf16)
         self.grads = {"dx": torch.empty(x.shape, **f32), "dW_r": torch.empty(W_r.shape, **f32),
-                      "dW_up": torch.empty(W_up.shape, **f32),
-                      "dW_down": torch.empty(W_down.shape, **f32)}
+                      "dW_up": torch.empty(W_up.shape, **wg),
+                      "dW_down": torch.empty(W_down.shape, **wg)}
         if Ws_up is not None:
-            self.grads["dWs_up"] = torch.empty(Ws_up.shape, **f32)
-            self.grads["dWs_down"] = torch.empty(Ws_down.shape, **f32)
+            self.grads["dWs_up"] = torch.empty(Ws_up.shape, **wg)
+            self.grads["dWs_down"] = torch.empty(Ws_down.shape, **wg)
         if W_in is not None:
             self.grads["dW_in"] = torch.empty(W_in.shape, **f32)
             self.grads["dW_out"] = torch.empty(W_out.shape, **f32)
@@ -328,17 +332,19 @@ class Backward:
         d = MoeDesc.from_buffer_copy(self.desc)
         if saved:
             d.flags |= SAVED_IN_WORKSPACE
+        if self.wgrad_bf16:
+            d.flags |= WGRAD_BF16
         rc = lib().moe_layer_backward(C.byref(d), C.byref(self.w), _p(dy), C.byref(self.g),
                                       _p(self.ws), self.ws_bytes, _stream(stream))
         _check(rc, "moe_layer_backward")
         return self.grads
 
 
-def backward_from(dev: dict, k: int) -> Backward:
-    """A Backward over a ``to_device`` dict."""
+def backward_from(dev: dict, k: int, **kw) -> Backward:
+    """A Backward over a ``to_device`` dict (keywords as for Backward)."""
     return Backward(dev["x"], dev["W_r"], dev["b"], dev["W_up"], dev["W_down"], k,
                     Ws_up=dev.get("Ws_up"), Ws_down=dev.get("Ws_down"), W_in=dev.get("W_in"),
-                    W_out=dev.get("W_out"))
+                    W_out=dev.get("W_out"), **kw)
 
 
 def layer_forward(x, W_r, b, W_up, W_down, k, **kw):

@@ -186,7 +186,8 @@ __device__ __forceinline__ void kt_mma(const uint8_t* As, f32x16_t (&acc)[MB][NB
 // r%4][wn*WN + j*32 + lane%32]; 16-row strips go through this wave's LDS strip `ep` so each lane
 // finishes CW consecutive columns of a row: 8 for bf16 outputs, 4 for fp32 (16 bytes either way,
 // so that consecutive lanes store consecutive 16-byte chunks of a row). Cg: the group's output.
-// NT: fp32 outputs are weight gradients, written once and not read again by this pass.
+// NT: the output is a weight gradient (fp32, or bf16 on request), written once and not read
+// again by this pass.
 template <Elt OUT, Epi EPI, bool NT>
 __device__ __forceinline__ void kt_store(const KtParams& p, const f32x16_t (&acc)[MB][NB],
                                          uint8_t* Cg, float* ep, int row0, int rows, int n0,
@@ -234,7 +235,14 @@ __device__ __forceinline__ void kt_store(const KtParams& p, const f32x16_t (&acc
             uint32_t w[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
-            *(uint4*)((uint16_t*)Cg + (int64_t)row * p.ldc + col) = make_uint4(w[0], w[1], w[2], w[3]);
+            uint16_t* o = (uint16_t*)Cg + (int64_t)row * p.ldc + col;
+            if constexpr (NT) {
+              typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+              const u32x4_t wv = {w[0], w[1], w[2], w[3]};
+              __builtin_nontemporal_store(wv, (u32x4_t*)o);
+            } else {
+              *(uint4*)o = make_uint4(w[0], w[1], w[2], w[3]);
+            }
           }
         }
       }
@@ -570,6 +578,8 @@ hipError_t launch_gemm_kt(int ta, int tb, Elt out, Epi epi, const KtParams& p, i
     return run_kt<0, 1, Elt::BF16, Epi::Store>(p, mt, s);
   if (ta == 1 && out == Elt::F32 && epi == Epi::Store && !p.mt_start)
     return run_kt<1, 1, Elt::F32, Epi::Store>(p, mt, s);
+  if (ta == 1 && out == Elt::BF16 && epi == Epi::Store && !p.mt_start)
+    return run_kt<1, 1, Elt::BF16, Epi::Store>(p, mt, s);
   return hipErrorInvalidValue;
 }
 

@@ -44,7 +44,7 @@ struct KtParams {
 // ta / tb: 1 when A / B is stored K-major. Provided: (ta, tb, out, epi) in
 //   (0, 1, BF16, DSqRelu), (0, 1, F32, Store),
 //   (0, 1, BF16, Store)                         data gradients (dense or row-grouped)
-//   (1, 1, F32, Store)                          weight gradients (dense or K-grouped)
+//   (1, 1, F32, Store), (1, 1, BF16, Store)     weight gradients (dense or K-grouped)
 // N, ldc and the K-major leading dimensions must be multiples of 8, and so must M when A is
 // K-major and K when it is not; each operand must span less than 2 GiB (32-bit offsets).
 // max_mtiles bounds the M-tiles of a row-grouped launch (its grid).

@@ -602,7 +602,7 @@ int32_t make_bwd_plan(const moe_desc_t* d, BwdPlan* out) {
   dd.flags = MOE_PATH_GROUPED;
   int32_t rc = make_plan(&dd, d->latent > 0, &fp);
   if (rc) return rc;
-  if (d->flags & ~(MOE_PATH_MASK | MOE_ROUTING_GIVEN | MOE_SAVED_IN_WORKSPACE))
+  if (d->flags & ~(MOE_PATH_MASK | MOE_ROUTING_GIVEN | MOE_SAVED_IN_WORKSPACE | MOE_WGRAD_BF16))
     return MOE_ERR_INVALID_ARG;
   if (d->flags & MOE_ROUTING_GIVEN) return MOE_ERR_UNSUPPORTED;
   if (d->act_dtype != MOE_BF16 || d->expert_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
@@ -905,14 +905,18 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
 
   // (5) routed weight gradients, reduced over each expert's own pair rows (the K window
   // [offsets[e], offsets[e+1]) of the pair-ordered operands, read as stored; the experts'
-  // inputs are read from the token rows through the dispatch permutation), heaviest first
+  // inputs are read from the token rows through the dispatch permutation), heaviest first.
+  // The expert weight gradients are fp32, or bf16 on request (the same sums, rounded).
+  const bool wg16 = d->flags & MOE_WGRAD_BF16;
+  const Elt wg = wg16 ? Elt::BF16 : Elt::F32;
   {
     KtParams g;  // dW_down[e] [D][I] = dY_e^T h_e
     g.A = dYp; g.lda = D; g.B = h; g.ldb = I; g.a_rows = P;
     g.C = gr->dW_down; g.ldc = I; g.c_gstride = (int64_t)D * I;
     g.M = D; g.N = I; g.G = E; g.kgrp = offsets; g.korder = korder;
-    MOE_SPAN("gemm_kt_f32out:bwd_routed_wgrad_down");
-    MOE_TRY(launch_gemm_kt(1, 1, Elt::F32, Epi::Store, g, 0, s));
+    MOE_SPAN(wg16 ? "gemm_kt_wgrad_bf16:bwd_routed_wgrad_down"
+                  : "gemm_kt_f32out:bwd_routed_wgrad_down");
+    MOE_TRY(launch_gemm_kt(1, 1, wg, Epi::Store, g, 0, s));
   }
   {
     KtParams g;  // dW_up[e] [I][D] = da_e^T (expert input)_e
@@ -920,23 +924,24 @@ int32_t backward(const moe_desc_t* d, const moe_weights_t* w, const void* dy, mo
     g.b_gather = perm; g.b_rows = T;
     g.C = gr->dW_up; g.ldc = D; g.c_gstride = (int64_t)I * D;
     g.M = I; g.N = D; g.G = E; g.kgrp = offsets; g.korder = korder;
-    MOE_SPAN("gemm_kt_f32out:bwd_routed_wgrad_up");
-    MOE_TRY(launch_gemm_kt(1, 1, Elt::F32, Epi::Store, g, 0, s));
+    MOE_SPAN(wg16 ? "gemm_kt_wgrad_bf16:bwd_routed_wgrad_up" : "gemm_kt_f32out:bwd_routed_wgrad_up");
+    MOE_TRY(launch_gemm_kt(1, 1, wg, Epi::Store, g, 0, s));
   }
   // (6) the shared expert's weight gradients over all tokens
   if (Is) {
     {
-      MOE_SPAN("gemm_kt_f32out:bwd_shared_wgrad_down");
+      MOE_SPAN(wg16 ? "gemm_kt_wgrad_bf16:bwd_shared_wgrad_down"
+                    : "gemm_kt_f32out:bwd_shared_wgrad_down");
       KtParams g;  // dWs_down [H][I_s] = dy^T h_s
       g.A = dy; g.lda = H; g.B = hs; g.ldb = Is;
       g.C = gr->dWs_down; g.ldc = Is; g.M = H; g.N = Is; g.K = T;
-      MOE_TRY(launch_gemm_kt(1, 1, Elt::F32, Epi::Store, g, 0, s));
+      MOE_TRY(launch_gemm_kt(1, 1, wg, Epi::Store, g, 0, s));
     }
-    MOE_SPAN("gemm_kt_f32out:bwd_shared_wgrad_up");
+    MOE_SPAN(wg16 ? "gemm_kt_wgrad_bf16:bwd_shared_wgrad_up" : "gemm_kt_f32out:bwd_shared_wgrad_up");
     KtParams g;  // dWs_up [I_s][H] = da_s^T x
     g.A = das; g.lda = Is; g.B = w->x; g.ldb = H;
     g.C = gr->dWs_up; g.ldc = H; g.M = Is; g.N = H; g.K = T;
-    MOE_TRY(launch_gemm_kt(1, 1, Elt::F32, Epi::Store, g, 0, s));
+    MOE_TRY(launch_gemm_kt(1, 1, wg, Epi::Store, g, 0, s));
   }
   return hip_status(hipGetLastError());
 }

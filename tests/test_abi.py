@@ -243,6 +243,11 @@ def test_training_forward_and_saved_flag_validation():
     L = moe.lib()
     assert bwd_ws(desc(flags=B.SAVED_IN_WORKSPACE))[0] == B.MOE_OK
     assert ws_size(desc(flags=B.SAVED_IN_WORKSPACE))[0] == B.MOE_ERR_INVALID_ARG  # forward: no
+    # bf16 weight gradients: a backward flag (same workspace), refused by the inference calls
+    assert bwd_ws(desc(flags=B.WGRAD_BF16)) == bwd_ws(desc())
+    assert bwd_ws(desc(flags=B.WGRAD_BF16 | B.SAVED_IN_WORKSPACE))[0] == B.MOE_OK
+    assert ws_size(desc(flags=B.WGRAD_BF16))[0] == B.MOE_ERR_INVALID_ARG
+    assert bwd_ws(desc(flags=32))[0] == B.MOE_ERR_INVALID_ARG         # unknown bit
     w = B.MoeWeights()
     for n, _ in B.MoeWeights._fields_:
         setattr(w, n, FAKE.value)

@@ -348,3 +348,33 @@ def test_training_forward_and_saved_backward_match_the_plain_calls(name):
         assert torch.equal(first[n], plain[n]), n
         assert torch.equal(second[n], plain[n]), n
 
+
+
+WGRAD = ("dW_up", "dW_down", "dWs_up", "dWs_down")
+
+
+@pytest.mark.parametrize("name", ["bwd_ragged", "bwd_max_routing", "bwd_latent_shared",
+                                  "nano_prefill_bf16"])
+def test_bf16_weight_gradients_are_the_fp32_gradients_rounded(name):
+    # Under MOE_WGRAD_BF16 the expert weight gradients are the same fp32 sums rounded to nearest
+    # even: each equals the fp32 path's rounded by torch, bit for bit, so the parity above holds
+    # for them with one more rounding (relative error at most 2^-9 per element). Every other
+    # gradient is unchanged, with and without the saved activations.
+    cfg = CASES.get(name) or mi.CONFIGS[name]
+    say(f"[gpu] bf16 weight gradients {name}: T={cfg.T} E={cfg.E} I={cfg.I} I_s={cfg.I_shared}")
+    inp = mi.make_layer(cfg, seed=11)
+    dev = moe.to_device(inp)
+    dy_dev = moe.to_device({"dy": mi.make_grad_output(cfg, seed=11)})["dy"]
+    ref = {n: t.clone() for n, t in moe.backward_from(dev, cfg.k)(dy_dev).items()}
+    bw = moe.backward_from(dev, cfg.k, wgrad_bf16=True)
+    plain = {n: t.clone() for n, t in bw(dy_dev).items()}
+    bw.forward_train()
+    saved = bw(dy_dev, saved=True)
+    torch.cuda.synchronize()
+    assert set(plain) == set(ref)
+    for n in ref:
+        want = ref[n].to(torch.bfloat16) if n in WGRAD else ref[n]
+        assert plain[n].dtype == want.dtype, n
+        assert torch.equal(plain[n], want), n
+        assert torch.equal(saved[n], want), n
+    assert any(n in ref for n in WGRAD)
