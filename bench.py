@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--path", default="auto", choices=["auto", "grouped", "stream"])
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-wgrad-bf16", action="store_true",
+                    help="backward workloads: skip the extra timing of the bf16 weight-gradient "
+                         "pass (counter runs then see the fp32 pass alone)")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0: auto)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one device copy of MIB MiB (a known-size reference for "
@@ -190,7 +193,7 @@ def weights_key(cfg):
     return (cfg.H, cfg.E, cfg.I, cfg.I_shared, cfg.latent, cfg.act_dtype, cfg.expert_dtype)
 
 
-def prepare(name, moe, mi, torch, path, cache=None):
+def prepare(name, moe, mi, torch, path, cache=None, wgrad_bf16=True):
     backward = name.endswith("+backward")
     cfg = mi.CONFIGS[name.split("+")[0]]
     key = weights_key(cfg)
@@ -214,12 +217,15 @@ def prepare(name, moe, mi, torch, path, cache=None):
         dy = moe.to_device({"dy": mi.make_grad_output(cfg, 0)})["dy"]
         bw = moe.backward_from(dev, cfg.k)
         bw.forward_train()
-        # the same pass writing the expert weight gradients in bf16 (MOE_WGRAD_BF16)
-        bw16 = moe.backward_from(dev, cfg.k, wgrad_bf16=True)
-        bw16.forward_train()
-        return dict(cfg=cfg, inp=inp, dev=dev, rt=rt, layer=lambda: bw(dy, saved=True),
-                    recompute=lambda: bw(dy), train_forward=bw.forward_train,
-                    wgrad_bf16=lambda: bw16(dy, saved=True), backward=True, name=name)
+        w = dict(cfg=cfg, inp=inp, dev=dev, rt=rt, layer=lambda: bw(dy, saved=True),
+                 recompute=lambda: bw(dy), train_forward=bw.forward_train, backward=True,
+                 name=name)
+        if wgrad_bf16:
+            # the same pass writing the expert weight gradients in bf16 (MOE_WGRAD_BF16)
+            bw16 = moe.backward_from(dev, cfg.k, wgrad_bf16=True)
+            bw16.forward_train()
+            w["wgrad_bf16"] = lambda: bw16(dy, saved=True)
+        return w
     layer = moe.layer_from(dev, cfg.k, path=path, routing=rt)
     return dict(cfg=cfg, inp=inp, dev=dev, rt=rt, layer=layer, name=name)
 
@@ -328,12 +334,13 @@ def measure(w, moe, torch, steps, warmup, graph):
         # training forward that saves them (median single steps)
         rec = step_times(w["recompute"], torch, max(steps // 2, 10))
         fwd = step_times(w["train_forward"], torch, max(steps // 2, 10))
-        wg16 = float(np.median(step_times(w["wgrad_bf16"], torch, max(steps, 20))))
         extra = dict(backward_recompute_us=round(float(np.median(rec)), 1),
-                     forward_train_us=round(float(np.median(fwd)), 1),
-                     backward_wgrad_bf16_us=round(wg16, 1),
-                     backward_wgrad_bf16_frac_of_bf16_peak=round(
-                         backward_flops(cfg) / (wg16 * 1e-6) / PEAK_MFMA["bf16"], 4))
+                     forward_train_us=round(float(np.median(fwd)), 1))
+        if "wgrad_bf16" in w:
+            wg16 = float(np.median(step_times(w["wgrad_bf16"], torch, max(steps, 20))))
+            extra.update(backward_wgrad_bf16_us=round(wg16, 1),
+                         backward_wgrad_bf16_frac_of_bf16_peak=round(
+                             backward_flops(cfg) / (wg16 * 1e-6) / PEAK_MFMA["bf16"], 4))
     step = None
     if not w.get("backward"):
         step = step_roofline(cfg, counts, float(np.median(dist)), float(np.median(cold)))
@@ -488,7 +495,7 @@ def main():
     torch.cuda.set_device(0)
     moe.lib()
     cache = {}
-    main_w = prepare(args.config, moe, mi, torch, args.path, cache)
+    main_w = prepare(args.config, moe, mi, torch, args.path, cache, not args.no_wgrad_bf16)
     res = measure(main_w, moe, torch, args.steps, args.warmup, args.graph)
     cfg = main_w["cfg"]
     out = {
@@ -501,7 +508,7 @@ def main():
     }
     extra = {}
     for name in [n for n in args.also.split(",") if n and n != args.config]:
-        w = prepare(name, moe, mi, torch, args.path, cache)
+        w = prepare(name, moe, mi, torch, args.path, cache, not args.no_wgrad_bf16)
         r = measure(w, moe, torch, args.steps, args.warmup, args.graph)
         extra[name] = dict(tokens_per_s=round(r["tokens_per_s"], 1), dtype=dtype_of(w["cfg"]),
                            ms_per_step=round(r["ms_per_step"], 4), roofline=r["roofline"],
