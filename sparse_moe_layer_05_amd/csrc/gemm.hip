@@ -600,14 +600,31 @@ void gemm_mfma_persist(GemmParams p) {  // two workgroups per CU: at most 256 re
 
 // -------------------------------------------------------------------------------------------
 // Vector-ALU kernel for fp32 layers: 64 x 64 tile, each thread a 4 x 4 block, K-steps of 16.
+// These layers are small, so a K-step's load latency, not its arithmetic, sets the time: the
+// loads of the next kF32Ahead steps are in flight (a ring of registers, refilled as each step
+// is staged) while a step is multiplied, and the LDS stages alternate so that one barrier per
+// step suffices. VEC: every row of A, B (and A2, B2) starts 16-byte aligned and K, K2 are
+// multiples of 4, so a thread's 4 k of a row are one 16-byte load. Loads are branch-free
+// (steps past the end reload the last one, chunks past K are replaced by zeros after landing),
+// so the compiler waits for exactly the step it stages.
 // -------------------------------------------------------------------------------------------
-template <Epi EPI>
+constexpr int kF32Ahead = 8;
+
+template <Epi EPI, bool VEC>
 __global__ __launch_bounds__(256) void gemm_f32(GemmParams p) {
-  constexpr int BM = 64, BN = 64, BK = 16;
-  __shared__ float As[BK][BM + 4];
-  __shared__ float Bs[BK][BN + 4];
+  constexpr int BM = 64, BN = 64, BK = 16, PF = kF32Ahead;
+  static_assert(PF % 2 == 0, "the ring slot's parity is the LDS stage's");
+  __shared__ float As[2][BK][BM + 4];
+  __shared__ float Bs[2][BK][BN + 4];
   int g, row0, rows, n0;
   if (!tile_of<BM, BN>(p, g, row0, rows, n0)) return;
+  if (p.ksplit > 1) {  // this workgroup's K slice (dense Store launches, no second segment)
+    const int k0 = blockIdx.y * p.kchunk;
+    p.K = min(p.kchunk, p.K - k0);
+    p.A = (const float*)p.A + k0;
+    p.B = (const float*)p.B + k0;
+    p.C = (float*)p.C + (int64_t)blockIdx.y * p.M * p.ldc;
+  }
   const int tid = threadIdx.x;
   const int tr = tid / 16, tc = tid % 16;  // thread's 4 x 4 block: rows tr*4.., cols tc*4..
   const int lr = tid >> 2, lk = (tid & 3) * 4;  // loader: row lr, k lk .. lk+3
@@ -615,32 +632,72 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmParams p) {
   const int64_t asrc = p.a_gather ? p.a_gather[row0 + rr] : (int64_t)(row0 + rr);
   const int nn = n0 + lr < p.N ? n0 + lr : p.N - 1;
   const int nk1 = cdiv(p.K, BK), nk = nk1 + cdiv(p.K2, BK);
-  float acc[4][4] = {};
-  for (int ks = 0; ks < nk; ++ks) {
+  const float* a1 = (const float*)p.A + asrc * p.lda;
+  const float* b1 = (const float*)p.B + (int64_t)g * p.b_gstride + (int64_t)nn * p.ldb;
+  const float* a2 = p.K2 > 0 ? (const float*)p.A2 + (int64_t)(row0 + rr) * p.lda2 : a1;
+  const float* b2 = p.K2 > 0 ? (const float*)p.B2 + (int64_t)nn * p.ldb2 : b1;
+  // K-step ks (clamped to the last) of this thread's A and B rows: 4 k each, zero past K
+  auto load = [&](int ks, float4& va, float4& vb) {
+    ks = min(ks, nk - 1);
     const bool seg2 = ks >= nk1;
     const int k0 = (seg2 ? ks - nk1 : ks) * BK + lk;
     const int klim = seg2 ? p.K2 : p.K;
-    const float* ap = seg2 ? (const float*)p.A2 + (int64_t)(row0 + rr) * p.lda2
-                           : (const float*)p.A + asrc * p.lda;
-    const float* bp = seg2 ? (const float*)p.B2 + (int64_t)nn * p.ldb2
-                           : (const float*)p.B + (int64_t)g * p.b_gstride + (int64_t)nn * p.ldb;
+    const float* ap = seg2 ? a2 : a1;
+    const float* bp = seg2 ? b2 : b1;
+    if constexpr (VEC) {
+      const int kc = min(k0, klim - 4);  // K % 4 == 0: the chunk is wholly inside or outside
+      const float4 x = *(const float4*)(ap + kc), y = *(const float4*)(bp + kc);
+      const bool in = k0 < klim;
+      va = in ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+      vb = in ? y : make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+      float x[4], y[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      As[lk + q][lr] = k0 + q < klim ? ap[k0 + q] : 0.f;
-      Bs[lk + q][lr] = k0 + q < klim ? bp[k0 + q] : 0.f;
+      for (int q = 0; q < 4; ++q) {
+        const int kq = min(k0 + q, klim - 1);
+        x[q] = ap[kq];
+        y[q] = bp[kq];
+      }
+      va = make_float4(k0 < klim ? x[0] : 0.f, k0 + 1 < klim ? x[1] : 0.f,
+                       k0 + 2 < klim ? x[2] : 0.f, k0 + 3 < klim ? x[3] : 0.f);
+      vb = make_float4(k0 < klim ? y[0] : 0.f, k0 + 1 < klim ? y[1] : 0.f,
+                       k0 + 2 < klim ? y[2] : 0.f, k0 + 3 < klim ? y[3] : 0.f);
     }
-    __syncthreads();
+  };
+  float acc[4][4] = {};
+  if (nk > 0) {
+    float4 ra[PF], rb[PF];
 #pragma unroll
-    for (int kk = 0; kk < BK; ++kk) {
-      float a[4], b[4];
+    for (int u = 0; u < PF; ++u) load(u, ra[u], rb[u]);
+    for (int ks0 = 0; ks0 < nk; ks0 += PF) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) { a[q] = As[kk][tr * 4 + q]; b[q] = Bs[kk][tc * 4 + q]; }
+      for (int u = 0; u < PF; ++u) {
+        if (ks0 + u >= nk) break;  // uniform
+        const int st = u & 1;      // ks0 is even, so this is the step's parity
+        As[st][lk + 0][lr] = ra[u].x;
+        As[st][lk + 1][lr] = ra[u].y;
+        As[st][lk + 2][lr] = ra[u].z;
+        As[st][lk + 3][lr] = ra[u].w;
+        Bs[st][lk + 0][lr] = rb[u].x;
+        Bs[st][lk + 1][lr] = rb[u].y;
+        Bs[st][lk + 2][lr] = rb[u].z;
+        Bs[st][lk + 3][lr] = rb[u].w;
+        load(ks0 + u + PF, ra[u], rb[u]);
+        // every thread has staged this step, and has finished the step before, which read the
+        // stage the next step writes
+        __syncthreads();
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+        for (int kk = 0; kk < BK; ++kk) {
+          float a[4], b[4];
 #pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(a[x], b[y], acc[x][y]);
+          for (int q = 0; q < 4; ++q) { a[q] = As[st][kk][tr * 4 + q]; b[q] = Bs[st][kk][tc * 4 + q]; }
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(a[x], b[y], acc[x][y]);
+        }
+      }
     }
-    __syncthreads();
   }
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
@@ -703,7 +760,19 @@ hipError_t run_f32(const GemmParams& p, int mtiles, hipStream_t s) {
   const int tiles = mtiles * cdiv(p.N, 64);
   if (tiles <= 0) return hipSuccess;
   const int grid = cdiv(tiles, kXcds) * kXcds;
-  hipLaunchKernelGGL((gemm_f32<EPI>), dim3(grid), dim3(256), 0, s, p);
+  const int ks = p.ksplit > 1 ? p.ksplit : 1;
+  if (ks > 1 && (EPI != Epi::Store || p.mt_start || p.K2 > 0 || p.kchunk <= 0 ||
+                 (int64_t)(ks - 1) * p.kchunk >= p.K || (int64_t)ks * p.kchunk < p.K))
+    return hipErrorInvalidValue;
+  // 16-byte loads when every row of every operand starts 16-byte aligned (and so do K slices)
+  const bool aligned = (((uintptr_t)p.A | (uintptr_t)p.B) & 15) == 0 &&
+                       ((p.lda | p.ldb | p.b_gstride | p.K | (ks > 1 ? p.kchunk : 0)) & 3) == 0 &&
+                       (p.K2 <= 0 || ((((uintptr_t)p.A2 | (uintptr_t)p.B2) & 15) == 0 &&
+                                      ((p.lda2 | p.ldb2 | p.K2) & 3) == 0));
+  if (aligned)
+    hipLaunchKernelGGL((gemm_f32<EPI, true>), dim3(grid, ks), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((gemm_f32<EPI, false>), dim3(grid, ks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

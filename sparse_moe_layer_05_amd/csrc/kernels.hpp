@@ -22,6 +22,8 @@ hipError_t launch_topk(const float* logits, int nsplit, const float* b, int T, i
 // Router K-split for small T: number of K slices (and the slice width) that give the dense
 // router GEMM about one workgroup per CU.
 void router_split(int T, int E, int H, int* nsplit, int* kchunk);
+// The same for the fp32 router (vector-ALU GEMM).
+void router_split_f32(int T, int E, int H, int* nsplit, int* kchunk);
 
 // Dispatch scratch: chunk_counts and chunk_base, each [ceil(T / 256), E] int32.
 inline size_t dispatch_scratch_ints(int T, int E) {

@@ -95,6 +95,7 @@ int32_t make_plan(const moe_desc_t* d, bool latent_call, Plan* pl) {
   };
   const size_t P = (size_t)p.P, Tz = (size_t)p.T, Ez = (size_t)p.E;
   if (p.act == Elt::BF16) router_split(p.T, p.E, p.H, &p.nsplit, &p.kchunk);
+  else router_split_f32(p.T, p.E, p.H, &p.nsplit, &p.kchunk);
   p.logits = take(Tz * Ez * 4);
   if (p.nsplit > 1) p.zpart = take((size_t)p.nsplit * Tz * Ez * 4);
   p.slices = take((2 * (size_t)max_slices(p.P, p.E) + 1) * 4);  // decode slices, their count

@@ -686,6 +686,17 @@ void router_split(int T, int E, int H, int* nsplit, int* kchunk) {
   *nsplit = cdiv(H, chunk);
 }
 
+void router_split_f32(int T, int E, int H, int* nsplit, int* kchunk) {
+  // The fp32 router's 64 x 64 tiles take one K-step of 16 at a time: with few tiles, split K
+  // toward about 256 workgroups, in slices of at least 32 columns (a multiple of 16).
+  const int tiles = cdiv(T, 64) * cdiv(E, 64);
+  int n = 1;
+  if (tiles > 0 && tiles < 256) n = std::max(1, std::min(256 / tiles, H / 32));
+  const int chunk = cdiv(cdiv(H, n), 16) * 16;
+  *kchunk = chunk;
+  *nsplit = cdiv(H, chunk);
+}
+
 hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* scratch,
                            int bm, int32_t* mt_start, const DispatchExtras& ex, hipStream_t s) {
