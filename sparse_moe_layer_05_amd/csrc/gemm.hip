@@ -599,7 +599,8 @@ void gemm_mfma_persist(GemmParams p) {  // two workgroups per CU: at most 256 re
 }
 
 // -------------------------------------------------------------------------------------------
-// Vector-ALU kernel for fp32 layers: 64 x 64 tile, each thread a 4 x 4 block, K-steps of 16.
+// Vector-ALU kernel for fp32 layers: BM x 64 tiles (BM = 64, or 16 for grouped launches whose
+// experts hold few rows), each thread a (BM / 16) x 4 block, K-steps of 16.
 // These layers are small, so a K-step's load latency, not its arithmetic, sets the time: the
 // loads of the next kF32Ahead steps are in flight (a ring of registers, refilled as each step
 // is staged) while a step is multiplied, and the LDS stages alternate so that one barrier per
@@ -610,9 +611,10 @@ void gemm_mfma_persist(GemmParams p) {  // two workgroups per CU: at most 256 re
 // -------------------------------------------------------------------------------------------
 constexpr int kF32Ahead = 8;
 
-template <Epi EPI, bool VEC>
+template <Epi EPI, bool VEC, int BM>
 __global__ __launch_bounds__(256) void gemm_f32(GemmParams p) {
-  constexpr int BM = 64, BN = 64, BK = 16, PF = kF32Ahead;
+  constexpr int BN = 64, BK = 16, PF = kF32Ahead, RM = BM / 16;
+  static_assert(BM == 64 || BM == 16, "tile heights provided");
   static_assert(PF % 2 == 0, "the ring slot's parity is the LDS stage's");
   __shared__ float As[2][BK][BM + 4];
   __shared__ float Bs[2][BK][BN + 4];
@@ -626,9 +628,12 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmParams p) {
     p.C = (float*)p.C + (int64_t)blockIdx.y * p.M * p.ldc;
   }
   const int tid = threadIdx.x;
-  const int tr = tid / 16, tc = tid % 16;  // thread's 4 x 4 block: rows tr*4.., cols tc*4..
-  const int lr = tid >> 2, lk = (tid & 3) * 4;  // loader: row lr, k lk .. lk+3
-  const int rr = lr < rows ? lr : 0;
+  const int tr = tid / 16, tc = tid % 16;  // thread's block: rows tr*RM.., cols tc*4..
+  // loaders: B row lr, A row lr % BM (with BM = 16 all four waves load A's 16 rows, so every
+  // thread issues the same loads; the first wave stages them), k lk .. lk+3
+  const int lr = tid >> 2, la = lr % BM, lk = (tid & 3) * 4;
+  const bool stage_a = tid < BM * 4;
+  const int rr = la < rows ? la : 0;
   const int64_t asrc = p.a_gather ? p.a_gather[row0 + rr] : (int64_t)(row0 + rr);
   const int nn = n0 + lr < p.N ? n0 + lr : p.N - 1;
   const int nk1 = cdiv(p.K, BK), nk = nk1 + cdiv(p.K2, BK);
@@ -664,7 +669,7 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmParams p) {
                        k0 + 2 < klim ? y[2] : 0.f, k0 + 3 < klim ? y[3] : 0.f);
     }
   };
-  float acc[4][4] = {};
+  float acc[RM][4] = {};
   if (nk > 0) {
     float4 ra[PF], rb[PF];
 #pragma unroll
@@ -674,10 +679,12 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmParams p) {
       for (int u = 0; u < PF; ++u) {
         if (ks0 + u >= nk) break;  // uniform
         const int st = u & 1;      // ks0 is even, so this is the step's parity
-        As[st][lk + 0][lr] = ra[u].x;
-        As[st][lk + 1][lr] = ra[u].y;
-        As[st][lk + 2][lr] = ra[u].z;
-        As[st][lk + 3][lr] = ra[u].w;
+        if (stage_a) {             // uniform per wave
+          As[st][lk + 0][la] = ra[u].x;
+          As[st][lk + 1][la] = ra[u].y;
+          As[st][lk + 2][la] = ra[u].z;
+          As[st][lk + 3][la] = ra[u].w;
+        }
         Bs[st][lk + 0][lr] = rb[u].x;
         Bs[st][lk + 1][lr] = rb[u].y;
         Bs[st][lk + 2][lr] = rb[u].z;
@@ -688,11 +695,13 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmParams p) {
         __syncthreads();
 #pragma unroll
         for (int kk = 0; kk < BK; ++kk) {
-          float a[4], b[4];
+          float a[RM], b[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) { a[q] = As[st][kk][tr * 4 + q]; b[q] = Bs[st][kk][tc * 4 + q]; }
+          for (int q = 0; q < RM; ++q) a[q] = As[st][kk][tr * RM + q];
 #pragma unroll
-          for (int x = 0; x < 4; ++x)
+          for (int q = 0; q < 4; ++q) b[q] = Bs[st][kk][tc * 4 + q];
+#pragma unroll
+          for (int x = 0; x < RM; ++x)
 #pragma unroll
             for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(a[x], b[y], acc[x][y]);
         }
@@ -700,8 +709,8 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmParams p) {
     }
   }
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int rl = tr * 4 + x;
+  for (int x = 0; x < RM; ++x) {
+    const int rl = tr * RM + x;
     if (rl >= rows) continue;
     const int row = row0 + rl;
 #pragma unroll
@@ -755,8 +764,8 @@ hipError_t run_persist(const GemmParams& p, int mtiles, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <Epi EPI>
-hipError_t run_f32(const GemmParams& p, int mtiles, hipStream_t s) {
+template <Epi EPI, int BM>
+hipError_t run_f32_bm(const GemmParams& p, int mtiles, hipStream_t s) {
   const int tiles = mtiles * cdiv(p.N, 64);
   if (tiles <= 0) return hipSuccess;
   const int grid = cdiv(tiles, kXcds) * kXcds;
@@ -770,10 +779,18 @@ hipError_t run_f32(const GemmParams& p, int mtiles, hipStream_t s) {
                        (p.K2 <= 0 || ((((uintptr_t)p.A2 | (uintptr_t)p.B2) & 15) == 0 &&
                                       ((p.lda2 | p.ldb2 | p.K2) & 3) == 0));
   if (aligned)
-    hipLaunchKernelGGL((gemm_f32<EPI, true>), dim3(grid, ks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((gemm_f32<EPI, true, BM>), dim3(grid, ks), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((gemm_f32<EPI, false>), dim3(grid, ks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((gemm_f32<EPI, false, BM>), dim3(grid, ks), dim3(256), 0, s, p);
   return hipGetLastError();
+}
+
+// Grouped launches take the tile height their tile list was built with; dense ones 64.
+template <Epi EPI>
+hipError_t run_f32(const GemmParams& p, int mtiles, hipStream_t s) {
+  if (p.mt_start && p.bm == 16) return run_f32_bm<EPI, 16>(p, mtiles, s);
+  if (p.mt_start && p.bm != 0 && p.bm != 64) return hipErrorInvalidValue;
+  return run_f32_bm<EPI, 64>(p, mtiles, s);
 }
 
 // Dense bf16 launch. Candidate tiles (rates measured on the chip with random bf16 data):

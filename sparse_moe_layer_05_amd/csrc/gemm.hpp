@@ -55,6 +55,8 @@ struct GemmParams {
   const int32_t* offs = nullptr;      // [G + 1] row offsets
   const int32_t* mt_start = nullptr;  // [G + 1] prefix of ceil(rows_g / BM)
   int G = 0;
+  // fp32 grouped launches: the M-tile height BM that mt_start counts (16 or 64; 0 means 64)
+  int bm = 0;
 };
 
 struct GemmKind {

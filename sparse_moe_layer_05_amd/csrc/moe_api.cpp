@@ -84,7 +84,8 @@ int32_t make_plan(const moe_desc_t* d, bool latent_call, Plan* pl) {
         E * H * 2 > kOp || I * Dw * 2 > kOp || Is * H * 2 > kOp || L * H * 2 > kOp)
       return MOE_ERR_INVALID_ARG;
   }
-  p.bm = p.act == Elt::F32 ? 64 : kGroupBM;
+  // fp32 grouped launches: 16-row tiles when experts average at most 16 rows, else 64
+  p.bm = p.act == Elt::F32 ? ((int64_t)p.T * p.k <= 16LL * p.E ? 16 : 64) : kGroupBM;
 
   const size_t ea = p.act == Elt::F32 ? 4 : 2;  // activation / intermediate element bytes
   size_t off = 0;
@@ -488,12 +489,12 @@ int32_t forward(const moe_desc_t* d, const moe_weights_t* w, void* y, void* ws, 
     up.lda = D; up.a_rows = T; up.a_gather = perm;
     up.B = w->W_up; up.ldb = D; up.b_gstride = (int64_t)I * D;
     up.C = h; up.ldc = I; up.N = I; up.K = D;
-    up.offs = offsets; up.mt_start = mt_start; up.G = E;
+    up.offs = offsets; up.mt_start = mt_start; up.G = E; up.bm = pl.bm;
     GemmParams dn;
     dn.A = h; dn.lda = I; dn.a_rows = P;
     dn.B = w->W_down; dn.ldb = I; dn.b_gstride = (int64_t)D * I;
     dn.C = Y; dn.ldc = D; dn.N = D; dn.K = I;
-    dn.offs = offsets; dn.mt_start = mt_start; dn.G = E;
+    dn.offs = offsets; dn.mt_start = mt_start; dn.G = E; dn.bm = pl.bm;
     if (pl.ex == Elt::FP8) {
       // e4m3 expert weights: the expert input rows and the h rows are quantised per row to
       // e4m3 (scale = row amax / 448) and both projections run on fp8 matrix cores.

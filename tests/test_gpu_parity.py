@@ -117,6 +117,8 @@ SMALL = {
     "tiny_f32_ragged": mi.CONFIGS["tiny_f32"].with_T(37),
     "tiny_f32_one": mi.CONFIGS["tiny_f32"].with_T(1),
     "tiny_f32_all_experts": dataclasses.replace(mi.CONFIGS["tiny_f32"], k=16, T=20),
+    # about 15 pair rows per expert: the fp32 grouped launches' 16-row tiles, several per expert
+    "tiny_f32_t120": mi.CONFIGS["tiny_f32"].with_T(120),
     "bf16_ragged": mi.LayerConfig("bf16_ragged", T=301, H=272, E=24, k=5, I=144, I_shared=208),
     "bf16_no_shared": mi.LayerConfig("bf16_no_shared", T=130, H=256, E=8, k=3, I=96),
     "latent_small": mi.LayerConfig("latent_small", T=70, H=256, E=64, k=8, I=64, latent=64),
