@@ -48,11 +48,16 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 
 // k rounds of selection over the keys of one token; lane l holds experts l, l + 64, ... Each
 // expert carries one 64-bit value, its key's order-preserving bits above its inverted index, so
-// that one wave-wide maximum per round yields the largest free key and, among equal keys, the
-// lowest expert (a float maximum followed by an index minimum took two reductions a round).
+// that one wave-wide maximum per round yields the largest key and, among equal keys, the lowest
+// expert (a float maximum followed by an index minimum took two reductions a round). The values
+// are distinct, so round j retires the largest value below round j-1's: nothing is cleared and
+// no score is read inside a round, whose cost is one dependent chain. Lane j keeps round j's
+// winner; the scores are fetched afterwards and summed in round order on every lane.
+// TREE: each lane's largest value below the last winner as a tree over its slots (shorter chain;
+// faster with one token per workgroup, slower with four waves of tokens per workgroup).
 // Writes the k experts (descending key) and their gates (scores renormalised over the
 // selection).
-template <int NPER>
+template <int NPER, bool TREE>
 __device__ __forceinline__ void select_topk(const float* key, const float* sc, int lane, int E,
                                             int k, int32_t* __restrict__ idx_t,
                                             float* __restrict__ gates_t) {
@@ -62,27 +67,39 @@ __device__ __forceinline__ void select_topk(const float* key, const float* sc, i
     const int e = lane + 64 * i;
     c[i] = e < E ? ((uint64_t)okey(key[i]) << 32) | (uint32_t)~e : 0;
   }
-  float sum = 0.f, mine = 0.f;
+  uint64_t prev = ~0ull, mine = 0;
   for (int j = 0; j < k; ++j) {
     uint64_t m = 0;
+    if constexpr (TREE) {
+      uint64_t a[NPER];
 #pragma unroll
-    for (int i = 0; i < NPER; ++i) m = c[i] > m ? c[i] : m;
-    m = wave_max_u64(m);
-    const int be = (int)~(uint32_t)m;
-    const int slot = be >> 6, owner = be & 63;
-    float v = 0.f;
+      for (int i = 0; i < NPER; ++i) a[i] = c[i] < prev ? c[i] : 0;
 #pragma unroll
-    for (int i = 0; i < NPER; ++i)
-      if (i == slot) {
-        v = sc[i];
-        if (lane == owner) c[i] = 0;
-      }
-    const float bs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), owner));
-    sum += bs;                       // same order j = 0..k-1 on every lane: deterministic
-    if (lane == j) mine = bs;
-    if (lane == 0) idx_t[j] = be;
+      for (int w = 1; w < NPER; w *= 2)
+#pragma unroll
+        for (int i = 0; i + w < NPER; i += 2 * w) a[i] = a[i + w] > a[i] ? a[i + w] : a[i];
+      m = a[0];
+    } else {
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) m = c[i] < prev && c[i] > m ? c[i] : m;
+    }
+    prev = wave_max_u64(m);
+    if (lane == j) mine = prev;
   }
-  if (lane < k) gates_t[lane] = mine / sum;
+  const int be = (int)~(uint32_t)mine;
+  const int slot = lane < k ? be >> 6 : 0, owner = lane < k ? be & 63 : 0;
+  float bs = 0.f;  // the score lane `owner` holds in slot `slot`
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const float t = __int_as_float(__builtin_amdgcn_ds_bpermute(owner << 2, __float_as_int(sc[i])));
+    bs = slot == i ? t : bs;
+  }
+  float sum = 0.f;  // the same order j = 0..k-1 on every lane: deterministic
+  for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bs), j));
+  if (lane < k) {
+    idx_t[lane] = be;
+    gates_t[lane] = bs / sum;
+  }
 }
 
 // One wave per token, four tokens per workgroup (many tokens): lane l holds experts l, l + 64, ...
@@ -128,7 +145,7 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
       key[i] = -INFINITY;
     }
   }
-  select_topk<NPER>(key, sc, lane, E, k, idx + (int64_t)t * k, gates + (int64_t)t * k);
+  select_topk<NPER, false>(key, sc, lane, E, k, idx + (int64_t)t * k, gates + (int64_t)t * k);
 }
 
 // One workgroup of 256 threads per token. Phase 1: thread i owns experts i, i + 256, ... (EPT of
@@ -194,7 +211,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     key[i] = key_l[lane + 64 * i];
     sc[i] = sc_l[lane + 64 * i];
   }
-  select_topk<NPER>(key, sc, lane, E, k, idx + (int64_t)t * k, gates + (int64_t)t * k);
+  select_topk<NPER, true>(key, sc, lane, E, k, idx + (int64_t)t * k, gates + (int64_t)t * k);
 }
 
 // --------------------------------------------------------------------------------- dispatch
