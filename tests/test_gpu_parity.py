@@ -157,6 +157,10 @@ SMALL = {
     # combine adds
     "bf16_shared_split": mi.LayerConfig("bf16_shared_split", T=37, H=256, E=16, k=4, I=64,
                                         I_shared=192),
+    # H a multiple of 48: the bf16 stream kernel's down launch takes three row blocks per unit
+    # (the routed experts' and the shared expert's rows)
+    "bf16_three_blocks": mi.LayerConfig("bf16_three_blocks", T=40, H=192, E=16, k=4, I=64,
+                                        I_shared=96),
 }
 MX_ONLY = {"mxfp4_one": dataclasses.replace(SMALL["mxfp4_long"], name="mxfp4_one", T=1)}
 MX_SMALL = ["mxfp4_small", "mxfp8_small", "mxfp4_long", "mxfp8_long", "latent_mxfp4_small",
@@ -171,7 +175,8 @@ def test_small_layer_all_tokens(name):
 
 @pytest.mark.parametrize("name", ["bf16_ragged", "bf16_no_shared", "latent_small",
                                   "latent_small_shared", "latent_split_small", "bf16_e6",
-                                  "bf16_e13", "bf16_max_routing", "bf16_shared_split"])
+                                  "bf16_e13", "bf16_max_routing", "bf16_shared_split",
+                                  "bf16_three_blocks"])
 def test_stream_and_grouped_paths_agree_with_oracle(name):
     inp = mi.make_layer(SMALL[name], seed=2)
     ys, _ = check_full(inp, "stream")
