@@ -497,6 +497,8 @@ def main():
     cache = {}
     main_w = prepare(args.config, moe, mi, torch, args.path, cache, not args.no_wgrad_bf16)
     res = measure(main_w, moe, torch, args.steps, args.warmup, args.graph)
+    print(f"[bench] {args.config}: {res['ms_per_step']:.4f} ms per step", file=sys.stderr,
+          flush=True)
     cfg = main_w["cfg"]
     out = {
         "metric": METRIC, "value": round(res["tokens_per_s"], 1), "unit": "tokens/s",
@@ -518,6 +520,7 @@ def main():
             n = args.cpu_tokens or max(2, min(w["cfg"].T,
                                               int(ALSO_CPU_S / per_token_seconds(w["cfg"]))))
             extra[name]["cpu_baseline"] = cpu_baseline(w, n)
+        print(f"[bench] {name}: {r['ms_per_step']:.4f} ms per step", file=sys.stderr, flush=True)
         del w
         torch.cuda.empty_cache()
     out["step_roofline"] = res["step_roofline"]
