@@ -262,7 +262,10 @@ const char *moe_status_str(int32_t code);
  * call whose trace name starts with `filter` (NULL or "" = all) is bracketed by two events
  * recorded on the call's stream, until `capacity` launches are recorded. Trace names are
  * "<kernel>:<role>", e.g. "stream:up", "gemm_bf16_sqrelu:routed_up", "dispatch:all".
- * After synchronising the stream, moe_trace_read(i, name, ms) returns record i. */
+ * The events are timing-only (created with hipEventDisableSystemFence): recording one adds no
+ * cache write-back or invalidate to the stream, so tracing changes the traced work's timing as
+ * little as possible; they order nothing, and a reader must synchronise the stream (or device)
+ * before moe_trace_read(i, name, ms) returns record i. */
 int32_t moe_trace_enable(int32_t capacity, const char *filter);
 int32_t moe_trace_count(void);
 int32_t moe_trace_read(int32_t i, const char **name, float *ms);

@@ -1089,7 +1089,9 @@ int32_t moe_trace_enable(int32_t capacity, const char* filter) {
   g_trace.ev = new hipEvent_t[2 * (size_t)capacity];
   g_trace.names = new const char*[capacity];
   for (int i = 0; i < 2 * capacity; ++i) {
-    if (hipEventCreate(&g_trace.ev[i]) != hipSuccess) {
+    // timing-only events: recording one issues no system-scope fence (no L2 write-back and
+    // invalidate between the traced launches); the reader synchronises the device first
+    if (hipEventCreateWithFlags(&g_trace.ev[i], hipEventDisableSystemFence) != hipSuccess) {
       for (int j = 0; j < i; ++j) (void)hipEventDestroy(g_trace.ev[j]);
       delete[] g_trace.ev;
       delete[] g_trace.names;
