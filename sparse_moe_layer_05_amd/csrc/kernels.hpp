@@ -9,7 +9,16 @@
 
 namespace moe {
 
-constexpr int kDispatchChunk = 256;  // tokens per dispatch workgroup
+// Dispatch of more than kDispatchSmallT tokens runs over chunks of 256, 128 or 64 tokens, one
+// workgroup each. A chunk is halved while it holds more than 2048 (token, slot) pairs and the
+// call keeps at most 128 chunks: many slots per token (LatentMoE's 24) then spread over more
+// workgroups, while the one-workgroup scan still adds few chunk counts per expert.
+constexpr int kDispatchSmallT = 256;   // up to this many tokens: one workgroup does it all
+inline int dispatch_chunk(int T, int k) {
+  int ch = 256;
+  while (ch > 64 && ch * k > 2048 && (T + ch / 2 - 1) / (ch / 2) <= 128) ch /= 2;
+  return ch;
+}
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 64;
 
@@ -25,9 +34,10 @@ void router_split(int T, int E, int H, int* nsplit, int* kchunk);
 // The same for the fp32 router (vector-ALU GEMM).
 void router_split_f32(int T, int E, int H, int* nsplit, int* kchunk);
 
-// Dispatch scratch: chunk_counts and chunk_base, each [ceil(T / 256), E] int32.
-inline size_t dispatch_scratch_ints(int T, int E) {
-  return 2 * (size_t)((T + kDispatchChunk - 1) / kDispatchChunk) * (size_t)E;
+// Dispatch scratch: chunk_counts and chunk_base, each [ceil(T / dispatch_chunk(T, k)), E] int32.
+inline size_t dispatch_scratch_ints(int T, int E, int k) {
+  const int ch = dispatch_chunk(T, k);
+  return 2 * (size_t)((T + ch - 1) / ch) * (size_t)E;
 }
 
 // Extra dispatch product for the decode path: the touched experts cut into slices of at most

@@ -106,7 +106,7 @@ int32_t make_plan(const moe_desc_t* d, bool latent_call, Plan* pl) {
   p.offsets = take((Ez + 1) * 4);
   p.perm = take(P * 4);
   p.pos = take(P * 4);
-  p.dscratch = take(dispatch_scratch_ints(p.T, p.E) * 4);
+  p.dscratch = take(dispatch_scratch_ints(p.T, p.E, p.k) * 4);
   p.mt_start = take((Ez + 1) * 4);
   if (fp8 || mx) {  // per-row e4m3 copies of the expert inputs and of h
     p.xq = take(Tz * (size_t)p.D);
@@ -631,7 +631,7 @@ int32_t make_bwd_plan(const moe_desc_t* d, BwdPlan* out) {
   p.offsets = take((E + 1) * 4);
   p.perm = take(P * 4);
   p.pos = take(P * 4);
-  p.dscratch = take(dispatch_scratch_ints(p.T, p.E) * 4);
+  p.dscratch = take(dispatch_scratch_ints(p.T, p.E, p.k) * 4);
   p.mt_start = take((E + 1) * 4);
   p.koffs = take((E + 1) * 4);
   p.korder = take(E * 4);
@@ -1055,7 +1055,7 @@ int32_t moe_route(const float* logits, const void* x, const void* W_r, const flo
 int32_t moe_dispatch_workspace_size(int32_t T, int32_t E, int32_t k, size_t* bytes) {
   if (!bytes || T < 0 || E < 1 || E > kMaxE || k < 1 || k > E || k > kMaxK)
     return MOE_ERR_INVALID_ARG;
-  *bytes = dispatch_scratch_ints(T, E) * sizeof(int32_t);
+  *bytes = dispatch_scratch_ints(T, E, k) * sizeof(int32_t);
   return MOE_OK;
 }
 

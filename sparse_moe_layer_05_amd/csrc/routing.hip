@@ -215,16 +215,20 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 }
 
 // --------------------------------------------------------------------------------- dispatch
-// Tokens are cut into chunks of 256 (one workgroup each). Inside a chunk, an LDS bitmask per
-// expert records which of the 256 tokens chose it; the popcount of the bits below a token is
-// its stable rank inside the chunk, and chunk bases from a prefix over chunks make the global
-// order "experts ascending, tokens ascending" without any order-deciding atomics. The masks are
-// stored word-major, word w of expert e at w * E + e, so that the lanes of a wave, which set
-// bits for unrelated experts, and a sweep over experts spread over the LDS banks (expert-major
-// rows of 8 words put every expert on one of 8 banks).
+// Tokens are cut into chunks of CH = 256, 128 or 64 (one workgroup each, thread i = token i of
+// the chunk; dispatch_chunk picks CH). Inside a chunk, an LDS bitmask per expert (CH / 32 words) records which of the
+// chunk's tokens chose it; the popcount of the bits below a token is its stable rank inside the
+// chunk, and chunk bases from a prefix over chunks make the global order "experts ascending,
+// tokens ascending" without any order-deciding atomics. The masks are stored word-major, word w
+// of expert e at w * E + e, so that the lanes of a wave, which set bits for unrelated experts,
+// and a sweep over experts spread over the LDS banks (expert-major rows of 8 words put every
+// expert on one of 8 banks). Smaller chunks give more workgroups: LatentMoE prefill (4096
+// tokens, 24 slots each) had 16 workgroups of 256 tokens, now 64 of 64.
+template <int CH>
 __device__ __forceinline__ uint64_t build_masks(const int32_t* __restrict__ idx, int T, int E,
                                                 int k, uint32_t* mask, int t, int tid) {
-  for (int i = tid; i < E * 8; i += kDispatchChunk) mask[i] = 0;
+  constexpr int W = CH / 32;  // mask words per expert
+  for (int i = tid; i < E * W; i += CH) mask[i] = 0;
   __syncthreads();
   uint64_t valid = 0;  // bit j: pair (t, j) is kept (k <= 64)
   if (t < T) {
@@ -245,16 +249,16 @@ __device__ __forceinline__ uint64_t build_masks(const int32_t* __restrict__ idx,
   return valid;
 }
 
-__global__ __launch_bounds__(kDispatchChunk) void dispatch_count(const int32_t* __restrict__ idx,
-                                                                 int T, int E, int k,
-                                                                 int32_t* __restrict__ ccount) {
+template <int CH>
+__global__ __launch_bounds__(CH) void dispatch_count(const int32_t* __restrict__ idx, int T, int E,
+                                                     int k, int32_t* __restrict__ ccount) {
   extern __shared__ uint32_t mask[];
   const int tid = threadIdx.x, c = blockIdx.x;
-  build_masks(idx, T, E, k, mask, c * kDispatchChunk + tid, tid);
-  for (int e = tid; e < E; e += kDispatchChunk) {
+  build_masks<CH>(idx, T, E, k, mask, c * CH + tid, tid);
+  for (int e = tid; e < E; e += CH) {
     int n = 0;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) n += __popc(mask[w * E + e]);
+    for (int w = 0; w < CH / 32; ++w) n += __popc(mask[w * E + e]);
     ccount[(int64_t)c * E + e] = n;
   }
 }
@@ -458,12 +462,15 @@ __global__ __launch_bounds__(1024) void dispatch_small(const int32_t* __restrict
   }
 }
 
-__global__ __launch_bounds__(kDispatchChunk) void dispatch_scatter(
-    const int32_t* __restrict__ idx, int T, int E, int k, const int32_t* __restrict__ cbase,
-    int32_t* __restrict__ perm, int32_t* __restrict__ pos) {
+template <int CH>
+__global__ __launch_bounds__(CH) void dispatch_scatter(const int32_t* __restrict__ idx, int T,
+                                                       int E, int k,
+                                                       const int32_t* __restrict__ cbase,
+                                                       int32_t* __restrict__ perm,
+                                                       int32_t* __restrict__ pos) {
   extern __shared__ uint32_t mask[];
-  const int tid = threadIdx.x, c = blockIdx.x, t = c * kDispatchChunk + tid;
-  const uint64_t valid = build_masks(idx, T, E, k, mask, t, tid);
+  const int tid = threadIdx.x, c = blockIdx.x, t = c * CH + tid;
+  const uint64_t valid = build_masks<CH>(idx, T, E, k, mask, t, tid);
   if (t >= T) return;
   const int w = tid >> 5;
   const uint32_t below = (1u << (tid & 31)) - 1u;
@@ -717,8 +724,7 @@ void router_split_f32(int T, int E, int H, int* nsplit, int* kchunk) {
 hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* scratch,
                            int bm, int32_t* mt_start, const DispatchExtras& ex, hipStream_t s) {
-  const int nch = (T + kDispatchChunk - 1) / kDispatchChunk;
-  if (nch <= 1) {
+  if (T <= kDispatchSmallT) {
     if (k > kSmallStage)
       hipLaunchKernelGGL(dispatch_small<true>, dim3(1), dim3(1024),
                          (size_t)T * k * sizeof(int16_t), s, idx, T, E, k, bm, counts, offsets,
@@ -728,15 +734,22 @@ hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int32_t* cou
                          counts, offsets, perm, pos, mt_start, ex);
     return hipGetLastError();
   }
+  const int ch = dispatch_chunk(T, k), nch = (T + ch - 1) / ch;
   int32_t* ccount = scratch;
   int32_t* cbase = scratch + (size_t)nch * E;
-  const size_t lds = (size_t)E * 8 * sizeof(uint32_t);
-  hipLaunchKernelGGL(dispatch_count, dim3(nch), dim3(kDispatchChunk), lds, s, idx, T, E, k,
-                     ccount);
-  hipLaunchKernelGGL(dispatch_scan, dim3(1), dim3(1024), 0, s, ccount, nch, E, bm, cbase, counts,
-                     offsets, mt_start, ex);
-  hipLaunchKernelGGL(dispatch_scatter, dim3(nch), dim3(kDispatchChunk), lds, s, idx, T, E, k,
-                     cbase, perm, pos);
+  const size_t lds = (size_t)E * (ch / 32) * sizeof(uint32_t);
+  auto run = [&](auto count, auto scatter) {
+    hipLaunchKernelGGL(count, dim3(nch), dim3(ch), lds, s, idx, T, E, k, ccount);
+    hipLaunchKernelGGL(dispatch_scan, dim3(1), dim3(1024), 0, s, ccount, nch, E, bm, cbase,
+                       counts, offsets, mt_start, ex);
+    hipLaunchKernelGGL(scatter, dim3(nch), dim3(ch), lds, s, idx, T, E, k, cbase, perm, pos);
+  };
+  if (ch == 64)
+    run(dispatch_count<64>, dispatch_scatter<64>);
+  else if (ch == 128)
+    run(dispatch_count<128>, dispatch_scatter<128>);
+  else
+    run(dispatch_count<256>, dispatch_scatter<256>);
   return hipGetLastError();
 }
 

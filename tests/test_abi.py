@@ -136,6 +136,8 @@ def test_route_and_dispatch_argument_errors():
     n = C.c_size_t(0)
     assert L.moe_dispatch_workspace_size(300, 16, 2, C.byref(n)) == B.MOE_OK
     assert n.value == 2 * 2 * 16 * 4                             # two [ceil(300/256), E] int tables
+    assert L.moe_dispatch_workspace_size(4096, 512, 24, C.byref(n)) == B.MOE_OK
+    assert n.value == 2 * 64 * 512 * 4                           # 24 slots: chunks of 64 tokens
     assert L.moe_dispatch(FAKE, 300, 16, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None) == \
         B.MOE_ERR_WORKSPACE
     assert L.moe_dispatch(FAKE, 300, 16, 17, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == \

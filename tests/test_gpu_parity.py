@@ -330,7 +330,8 @@ def test_route_from_x_logits_and_tie_band():
 
 
 @pytest.mark.parametrize("T,E,k", [(1, 4, 1), (255, 16, 2), (256, 16, 2), (257, 128, 6),
-                                   (5000, 512, 24), (1000, 1024, 64)])
+                                   (5000, 512, 24), (1000, 1024, 64), (9000, 128, 6),
+                                   (3000, 256, 12)])
 def test_dispatch_is_bit_exact(T, E, k):
     rng = np.random.default_rng(T * 7 + E)
     p = rng.random(E) ** 3 + 1e-3             # skewed popularity, some experts rarely picked
