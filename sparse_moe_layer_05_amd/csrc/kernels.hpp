@@ -16,7 +16,7 @@ namespace moe {
 constexpr int kDispatchSmallT = 256;   // up to this many tokens: one workgroup does it all
 inline int dispatch_chunk(int T, int k) {
   int ch = 256;
-  while (ch > 64 && ch * k > 2048 && (T + ch / 2 - 1) / (ch / 2) <= 128) ch /= 2;
+  while (ch > 64 && ch * k > 2048 && ((int64_t)T + ch / 2 - 1) / (ch / 2) <= 128) ch /= 2;
   return ch;
 }
 constexpr int kMaxE = 1024;
@@ -37,7 +37,7 @@ void router_split_f32(int T, int E, int H, int* nsplit, int* kchunk);
 // Dispatch scratch: chunk_counts and chunk_base, each [ceil(T / dispatch_chunk(T, k)), E] int32.
 inline size_t dispatch_scratch_ints(int T, int E, int k) {
   const int ch = dispatch_chunk(T, k);
-  return 2 * (size_t)((T + ch - 1) / ch) * (size_t)E;
+  return 2 * (size_t)(((int64_t)T + ch - 1) / ch) * (size_t)E;
 }
 
 // Extra dispatch product for the decode path: the touched experts cut into slices of at most

@@ -734,7 +734,7 @@ hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int32_t* cou
                          counts, offsets, perm, pos, mt_start, ex);
     return hipGetLastError();
   }
-  const int ch = dispatch_chunk(T, k), nch = (T + ch - 1) / ch;
+  const int ch = dispatch_chunk(T, k), nch = (int)(((int64_t)T + ch - 1) / ch);
   int32_t* ccount = scratch;
   int32_t* cbase = scratch + (size_t)nch * E;
   const size_t lds = (size_t)E * (ch / 32) * sizeof(uint32_t);
