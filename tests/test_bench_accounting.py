@@ -1,0 +1,105 @@
+"""The benchmark's algorithmic work and traffic bookkeeping, on the CPU.
+
+bench.py reports each workload's roofline fraction as algorithmic bytes or flops over measured
+time. These tests pin that bookkeeping to the work model it states: only the selected (token,
+expert) pairs, each touched expert's weights read once, the shared expert, router and latent
+projections read once, tokens in and out once. They also check that the committed counter
+figures are withdrawn once a kernel's sources change, and that a multi-GPU request is refused.
+"""
+import json
+import os
+import shutil
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import moe_inputs as mi  # noqa: E402
+
+
+def counts_with(E, touched, P):
+    """Expert counts summing to P with exactly `touched` nonzero entries."""
+    c = np.zeros(E, np.int64)
+    c[:touched] = P // touched
+    c[0] += P - c.sum()
+    return c
+
+
+@pytest.mark.parametrize("name", ["nano_decode_bf16", "nano_prefill_bf16", "latent_bf16",
+                                  "latent_decode_bf16", "tiny_f32"])
+def test_step_work_is_the_layer_work_model(name):
+    # F = 2TEH + 4PID + 4T I_s H + 4T l H;  B = touched 2ID w + 2 I_s H a + E H a + 2 l H a + 2 T H a
+    cfg = mi.CONFIGS[name]
+    T, H, E, k, I, Is, L, D = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared, cfg.latent, cfg.D
+    P = T * k
+    a = 4 if cfg.act_dtype == "f32" else 2
+    touched = min(E, 97)
+    flops, b = bench.step_work(cfg, counts_with(E, touched, P))
+    assert sum(flops.values()) == 2 * T * E * H + 4 * P * I * D + 4 * T * Is * H + 4 * T * L * H
+    assert b == touched * 2 * I * D * a + 2 * Is * H * a + E * H * a + 2 * L * H * a + 2 * T * H * a
+
+
+def test_fp8_step_work_counts_weight_bytes_once_with_their_scales():
+    cfg = mi.CONFIGS["nano_fp8"]
+    T, H, E, k, I, Is = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared
+    touched = 120
+    flops, b = bench.step_work(cfg, counts_with(E, touched, T * k))
+    assert flops["fp8"] == 4 * T * k * I * H                    # routed products on fp8 cores
+    assert flops["bf16"] == 2 * T * E * H + 4 * T * Is * H      # router and shared expert in bf16
+    scales = touched * (I + H) * 4                              # fp32 per output channel
+    assert b == touched * 2 * I * H * 1 + scales + 2 * Is * H * 2 + E * H * 2 + 2 * T * H * 2
+
+
+def test_decode_stream_launches_carry_every_weight_byte_once():
+    # the two stream launches of a bf16 decode step (routed experts plus the shared expert dealt
+    # in the same launches) read between them each touched expert's two matrices and the shared
+    # expert's two matrices once
+    cfg = mi.CONFIGS["nano_decode_bf16"]
+    T, H, E, k, I, Is = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared
+    P, touched = T * k, 97
+    counts = counts_with(E, touched, P)
+    f_up, b_up = bench.work_of("stream:up", cfg, counts, stream=True)
+    f_dn, b_dn = bench.work_of("stream:down", cfg, counts, stream=True)
+    weights = touched * 2 * I * H * 2 + 2 * Is * H * 2
+    tokens = (T * H * 2 + P * I * 2 + T * Is * 2) + (P * I * 2 + P * H * 4 + T * Is * 2 + T * H * 4)
+    assert b_up + b_dn == weights + tokens
+    assert f_up + f_dn == 4 * P * I * H + 4 * T * Is * H
+
+
+def test_committed_traffic_is_withdrawn_once_a_source_changes(tmp_path, monkeypatch):
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+        doc = json.load(f)
+    key = "nano_decode_bf16/stream"
+    ent = doc["entries"][key]
+    root = tmp_path / "repo"
+    (root / "profiles").mkdir(parents=True)
+    shutil.copy(os.path.join(ROOT, "profiles", "traffic.json"), root / "profiles")
+    for src in ent["sources"]:
+        (root / os.path.dirname(src)).mkdir(parents=True, exist_ok=True)
+        shutil.copy(os.path.join(ROOT, src), root / src)
+    monkeypatch.setattr(bench, "ROOT", str(root))
+    assert bench.measured_traffic("nano_decode_bf16", "stream") == ent["traffic_bytes_per_launch"]
+    with open(root / ent["sources"][0], "a") as f:
+        f.write("\n// edited\n")
+    assert bench.measured_traffic("nano_decode_bf16", "stream") is None
+    assert bench.measured_traffic("nano_decode_bf16", "no_such_kernel") is None
+
+
+def test_committed_traffic_entries_match_the_current_sources():
+    # every figure bench.py would report was counted on the kernels as they are now
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+        doc = json.load(f)
+    stale = [k for k in doc["entries"] if bench.measured_traffic(*k.split("/")) is None]
+    assert not stale, f"counters taken on other kernel sources: {stale}"
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
