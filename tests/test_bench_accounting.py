@@ -6,6 +6,7 @@ expert) pairs, each touched expert's weights read once, the shared expert, route
 projections read once, tokens in and out once. They also check that the committed counter
 figures are withdrawn once a kernel's sources change, and that a multi-GPU request is refused.
 """
+import hashlib
 import json
 import os
 import shutil
@@ -78,10 +79,14 @@ def test_committed_traffic_is_withdrawn_once_a_source_changes(tmp_path, monkeypa
     ent = doc["entries"][key]
     root = tmp_path / "repo"
     (root / "profiles").mkdir(parents=True)
-    shutil.copy(os.path.join(ROOT, "profiles", "traffic.json"), root / "profiles")
+    h = hashlib.sha256()
     for src in ent["sources"]:
         (root / os.path.dirname(src)).mkdir(parents=True, exist_ok=True)
         shutil.copy(os.path.join(ROOT, src), root / src)
+        h.update((root / src).read_bytes())
+    ent = dict(ent, sha=h.hexdigest()[:16])          # counted on the copied sources
+    with open(root / "profiles" / "traffic.json", "w") as f:
+        json.dump(dict(doc, entries={key: ent}), f)
     monkeypatch.setattr(bench, "ROOT", str(root))
     assert bench.measured_traffic("nano_decode_bf16", "stream") == ent["traffic_bytes_per_launch"]
     with open(root / ent["sources"][0], "a") as f:
