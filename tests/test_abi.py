@@ -138,6 +138,11 @@ def test_route_and_dispatch_argument_errors():
     assert n.value == 2 * 2 * 16 * 4                             # two [ceil(300/256), E] int tables
     assert L.moe_dispatch_workspace_size(4096, 512, 24, C.byref(n)) == B.MOE_OK
     assert n.value == 2 * 64 * 512 * 4                           # 24 slots: chunks of 64 tokens
+    # chunks halve while they hold more than 2048 pairs and the call keeps at most 128 chunks
+    for T, k, chunk in ((16384, 6, 256), (8192, 6, 256), (3000, 12, 128), (1000, 64, 64),
+                        (32768, 24, 256), (9000, 24, 128)):
+        assert L.moe_dispatch_workspace_size(T, 64, k, C.byref(n)) == B.MOE_OK
+        assert n.value == 2 * -(-T // chunk) * 64 * 4, (T, k, chunk)
     assert L.moe_dispatch(FAKE, 300, 16, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None) == \
         B.MOE_ERR_WORKSPACE
     assert L.moe_dispatch(FAKE, 300, 16, 17, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == \
